@@ -1,0 +1,247 @@
+"""CPU oracle of the Llama-family forward pass (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It wraps ``liboracle.so`` (plain C, fp32,
+built from ``oracle.c``) with ctypes and shares no code with the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import build as _build
+
+F32, F16, Q8_0 = 0, 1, 8
+_lib = None
+
+
+class OrcConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("dim", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
+                                               "n_ctx", "rope_dims", "rope_neox")] + [("eps", ctypes.c_float),
+                                                                                      ("rope_base", ctypes.c_float)]
+
+
+class OrcTensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_int32), ("n_dims", ctypes.c_int32),
+                ("ne", ctypes.c_int64 * 2), ("data", ctypes.c_void_p), ("nbytes", ctypes.c_size_t)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_f16_to_f32.restype = f32
+        L.orc_f32_to_f16.argtypes = [f32]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_dequantize.argtypes = [i32, vp, i64, vp]
+        L.orc_quantize_q8_0.argtypes = [vp, i64, vp]
+        L.orc_rmsnorm.argtypes = [vp, vp, vp, i32, f32]
+        L.orc_rmsnorm.restype = None
+        L.orc_matvec.argtypes = [vp, vp, vp, i32, i32]
+        L.orc_matvec.restype = None
+        L.orc_matmul.argtypes = [vp, vp, vp, i32, i32, i32]
+        L.orc_matmul.restype = None
+        L.orc_rope_cos_sin.argtypes = [i32, i32, f32, vp, vp]
+        L.orc_rope_cos_sin.restype = None
+        L.orc_rope.argtypes = [vp, i32, i32, i32, i32, f32, i32]
+        L.orc_rope.restype = None
+        L.orc_silu.argtypes = [f32]
+        L.orc_silu.restype = f32
+        L.orc_argmax.argtypes = [vp, i32]
+        L.orc_argmax.restype = i32
+        L.orc_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp]
+        L.orc_attention.restype = None
+        L.orc_load.argtypes = [ctypes.POINTER(OrcConfig), ctypes.POINTER(OrcTensor), i32, ctypes.POINTER(vp)]
+        L.orc_forward.argtypes = [vp, i32, i32, vp]
+        L.orc_prefill.argtypes = [vp, vp, i32, vp]
+        L.orc_reset.argtypes = [vp]
+        L.orc_reset.restype = None
+        L.orc_kv_len.argtypes = [vp]
+        L.orc_kv_read.argtypes = [vp, i32, i32, vp, vp]
+        L.orc_free.argtypes = [vp]
+        L.orc_free.restype = None
+        L.orc_weights_per_layer.argtypes = [i64, i64, i64]
+        L.orc_weights_per_layer.restype = i64
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+# ---------------------------------------------------------------- operations
+def f16_to_f32(h: int) -> float:
+    return float(np.float32(lib().orc_f16_to_f32(int(h))))
+
+
+def f32_to_f16(x: float) -> int:
+    return int(lib().orc_f32_to_f16(float(np.float32(x))))
+
+
+def dequantize(dtype: int, raw: np.ndarray, n: int) -> np.ndarray:
+    out = np.empty(n, np.float32)
+    rc = lib().orc_dequantize(dtype, _p(np.ascontiguousarray(raw)), n, _p(out))
+    if rc:
+        raise ValueError(f"orc_dequantize: {rc}")
+    return out
+
+
+def quantize_q8_0(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.size // 32 * 34, np.uint8)
+    rc = lib().orc_quantize_q8_0(_p(x), x.size, _p(out))
+    if rc:
+        raise ValueError(f"orc_quantize_q8_0: {rc}")
+    return out
+
+
+def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float32)
+    w = np.ascontiguousarray(w, np.float32)
+    out = np.empty_like(x)
+    lib().orc_rmsnorm(_p(out), _p(x), _p(w), x.size, eps)
+    return out
+
+
+def matvec(w: np.ndarray, x: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    w = np.ascontiguousarray(w, np.float32)
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(rows, np.float32)
+    lib().orc_matvec(_p(out), _p(w), _p(x), rows, cols)
+    return out
+
+
+def matmul(w: np.ndarray, x: np.ndarray, n: int, rows: int, cols: int) -> np.ndarray:
+    w = np.ascontiguousarray(w, np.float32)
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty((n, rows), np.float32)
+    lib().orc_matmul(_p(out), _p(w), _p(x), n, rows, cols)
+    return out
+
+
+def rope_cos_sin(pos: int, rope_dims: int, base: float):
+    c = np.empty(rope_dims // 2, np.float32)
+    s = np.empty(rope_dims // 2, np.float32)
+    lib().orc_rope_cos_sin(pos, rope_dims, base, _p(c), _p(s))
+    return c, s
+
+
+def rope(vec: np.ndarray, n_heads: int, head_dim: int, rope_dims: int, pos: int, base: float, neox: bool) -> np.ndarray:
+    v = np.array(vec, np.float32, copy=True)
+    lib().orc_rope(_p(v), n_heads, head_dim, rope_dims, pos, base, int(neox))
+    return v
+
+
+def silu(z: float) -> float:
+    return float(np.float32(lib().orc_silu(float(np.float32(z)))))
+
+
+def argmax(v: np.ndarray) -> int:
+    v = np.ascontiguousarray(v, np.float32)
+    return int(lib().orc_argmax(_p(v), v.size))
+
+
+def attention(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray, n_heads: int, n_kv_heads: int, head_dim: int,
+              pos: int, want_weights: bool = False):
+    """kcache/vcache: binary16 bits, [>= pos+1][n_kv_heads * head_dim]."""
+    q = np.ascontiguousarray(q, np.float32)
+    kc = np.ascontiguousarray(kcache, np.uint16)
+    vc = np.ascontiguousarray(vcache, np.uint16)
+    out = np.empty(n_heads * head_dim, np.float32)
+    wts = np.empty((n_heads, pos + 1), np.float32) if want_weights else None
+    lib().orc_attention(_p(out), _p(q), _p(kc), _p(vc), n_heads, n_kv_heads, head_dim, pos,
+                        _p(wts) if wts is not None else None)
+    return (out, wts) if want_weights else out
+
+
+def weights_per_layer(dim: int, kv_dim: int, ffn: int) -> int:
+    return int(lib().orc_weights_per_layer(dim, kv_dim, ffn))
+
+
+# --------------------------------------------------------------------- model
+def make_config(cfg) -> OrcConfig:
+    c = OrcConfig()
+    for f in ("dim", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "n_ctx"):
+        setattr(c, f, int(getattr(cfg, f)))
+    c.rope_dims = int(cfg.n_rot)
+    c.rope_neox = int(bool(cfg.rope_neox))
+    c.eps = float(cfg.eps)
+    c.rope_base = float(cfg.rope_base)
+    return c
+
+
+class Model:
+    """The oracle's forward pass over a tensor set (a list of synth.Tensor)."""
+
+    def __init__(self, cfg, tensors: Sequence, config: Optional[OrcConfig] = None):
+        self.cfg = cfg
+        self._keep = list(tensors)
+        arr = (OrcTensor * len(tensors))()
+        self._names = []
+        for i, t in enumerate(tensors):
+            nm = t.name.encode()
+            self._names.append(nm)
+            arr[i].name = nm
+            arr[i].dtype = t.dtype
+            arr[i].n_dims = len(t.ne)
+            arr[i].ne[0] = t.ne[0]
+            arr[i].ne[1] = t.ne[1] if len(t.ne) > 1 else 1
+            arr[i].data = t.data.ctypes.data
+            arr[i].nbytes = t.nbytes
+        self.config = config if config is not None else make_config(cfg)
+        h = ctypes.c_void_p()
+        rc = lib().orc_load(ctypes.byref(self.config), arr, len(tensors), ctypes.byref(h))
+        if rc:
+            raise ValueError(f"orc_load failed: {rc}")
+        self.h = h
+        self.vocab = self.config.vocab
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().orc_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def forward(self, token: int, pos: int) -> np.ndarray:
+        out = np.empty(self.vocab, np.float32)
+        rc = lib().orc_forward(self.h, int(token), int(pos), _p(out))
+        if rc:
+            raise ValueError(f"orc_forward: {rc}")
+        return out
+
+    def prefill(self, tokens) -> np.ndarray:
+        tk = np.ascontiguousarray(tokens, np.int32)
+        out = np.empty(self.vocab, np.float32)
+        rc = lib().orc_prefill(self.h, _p(tk), tk.size, _p(out))
+        if rc:
+            raise ValueError(f"orc_prefill: {rc}")
+        return out
+
+    def reset(self):
+        lib().orc_reset(self.h)
+
+    def kv_len(self) -> int:
+        return int(lib().orc_kv_len(self.h))
+
+    def kv_read(self, layer: int, pos: int):
+        kvd = self.config.n_kv_heads * self.config.head_dim
+        k = np.empty(kvd, np.uint16)
+        v = np.empty(kvd, np.uint16)
+        rc = lib().orc_kv_read(self.h, layer, pos, _p(k), _p(v))
+        if rc:
+            raise ValueError(f"orc_kv_read: {rc}")
+        return k, v

@@ -1,0 +1,568 @@
+/*
+ * CPU oracle for the Llama-family forward pass. TEST INFRASTRUCTURE ONLY: it
+ * is loaded by the tests, by the smoke check and by the bench's CPU-baseline
+ * leg, never by the library it checks, and it shares no code with it.
+ *
+ * It is the plain definition, in the precision the pages fix: the Java engine
+ * of "The Forward Pass in Java" (codeloopback.dev) computes in fp32 `float`,
+ * accumulates the RMSNorm sum of squares in double (Example 4), evaluates cos,
+ * sin and exp in double and rounds them to float (Examples 6, 8, Project 18),
+ * and rounds K and V through binary16 when it stores them (Example 10). Every
+ * dot product is one sequential fp32 sum over the input index (Example 5).
+ * Build flags: -O2 -fno-fast-math -ffp-contract=off, so no multiply-add is
+ * fused (FMA fusion is a named source of divergence in "What a Llama model
+ * computes, and why", section 8).
+ *
+ * OpenMP splits only over independent output rows or heads, so each output is
+ * computed by one thread in a fixed order and the result does not depend on
+ * the thread count ("The Engine", design notes on threading).
+ *
+ * Parity pins: every function here is pinned by tests/test_oracle_pins.py
+ * against values the pages print, closed forms, invariants and brute force.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_F16 1
+#define ORC_Q8_0 8
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_MISSING (-2)
+#define ORC_ERR_SHAPE (-3)
+#define ORC_ERR_DTYPE (-4)
+#define ORC_ERR_SIZE (-5)
+#define ORC_ERR_POS (-6)
+#define ORC_ERR_OOM (-7)
+
+typedef struct {
+    int32_t dim, n_layers, n_heads, n_kv_heads, head_dim, ffn, vocab, n_ctx, rope_dims, rope_neox;
+    float eps, rope_base;
+} orc_config;
+
+typedef struct {
+    const char* name;
+    int32_t dtype;
+    int32_t n_dims;
+    int64_t ne[2];
+    const void* data;
+    size_t nbytes;
+} orc_tensor;
+
+/* ------------------------------------------------------------------------
+ * binary16 <-> binary32, written from IEEE 754-2008 (round to nearest even,
+ * subnormals kept). "Loading GGUF with the FFM API", Example 7 states the
+ * rounding rule; the F16 KV cache of "The Forward Pass in Java", Example 10
+ * stores through it.
+ * ---------------------------------------------------------------------- */
+float orc_f16_to_f32(uint16_t h) {
+    uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+    float f;
+    if (e == 0) {
+        f = ldexpf((float)m, -24); /* zero or subnormal: m * 2^-24, exact in float */
+        uint32_t b;
+        memcpy(&b, &f, 4);
+        b |= sign;
+        memcpy(&f, &b, 4);
+        return f;
+    }
+    uint32_t b;
+    if (e == 31)
+        b = sign | 0x7f800000u | (m << 13);
+    else
+        b = sign | ((e - 15 + 127) << 23) | (m << 13);
+    memcpy(&f, &b, 4);
+    return f;
+}
+
+uint16_t orc_f32_to_f16(float f) {
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);
+    uint32_t ax = x & 0x7fffffffu;
+    if (ax >= 0x7f800000u) return sign | (ax > 0x7f800000u ? 0x7e00u : 0x7c00u); /* NaN stays NaN */
+    int e = (int)(ax >> 23) - 127;                                                /* unbiased exponent */
+    uint32_t sig = (ax & 0x7fffffu) | 0x800000u;                                  /* 24-bit significand */
+    if (ax == 0) return sign;
+    /* Number of low significand bits to drop: 13 in the normal range, more below. */
+    int drop = (e >= -14) ? 13 : 13 + (-14 - e);
+    if (drop > 24) return sign; /* below half of the smallest subnormal */
+    uint32_t kept = sig >> drop;
+    uint32_t rem = sig & ((1u << drop) - 1u), halfway = 1u << (drop - 1);
+    if (rem > halfway || (rem == halfway && (kept & 1u))) kept += 1u;
+    uint32_t h;
+    if (e >= -14)
+        h = ((uint32_t)(e + 15) << 10) + (kept - 0x400u); /* implicit bit removed; a carry bumps the exponent */
+    else
+        h = kept; /* subnormal (a carry to 0x400 is the smallest normal) */
+    if (h >= 0x7c00u) h = 0x7c00u; /* overflow to infinity */
+    return sign | (uint16_t)h;
+}
+
+/* ------------------------------------------------------------------------
+ * Dequantisation to float ("The Forward Pass in Java", Example 2; "Loading
+ * GGUF with the FFM API", Examples 7 and 8): F32 is copied, F16 is converted
+ * per value, a Q8_0 block {fp16 d, int8 qs[32]} decodes to d * qs[j].
+ * ---------------------------------------------------------------------- */
+int orc_dequantize(int32_t dtype, const void* data, int64_t n, float* out) {
+    const uint8_t* p = (const uint8_t*)data;
+    if (dtype == ORC_F32) {
+        memcpy(out, data, (size_t)n * 4);
+        return ORC_OK;
+    }
+    if (dtype == ORC_F16) {
+        for (int64_t i = 0; i < n; i++) {
+            uint16_t h = (uint16_t)(p[2 * i] | (p[2 * i + 1] << 8));
+            out[i] = orc_f16_to_f32(h);
+        }
+        return ORC_OK;
+    }
+    if (dtype == ORC_Q8_0) {
+        if (n % 32) return ORC_ERR_SHAPE;
+        for (int64_t b = 0; b < n / 32; b++) {
+            const uint8_t* blk = p + 34 * b;
+            float d = orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+            for (int j = 0; j < 32; j++) out[32 * b + j] = d * (float)(int8_t)blk[2 + j];
+        }
+        return ORC_OK;
+    }
+    return ORC_ERR_DTYPE;
+}
+
+/* C roundf: halves away from zero ("The Forward Pass in Java", Example 2). */
+static int round_half_away(float v) { return (int)copysign(floor(fabs((double)v) + 0.5), (double)v); }
+
+/*
+ * The reference Q8_0 quantiser of "The Forward Pass in Java", Example 2 and
+ * "Loading GGUF with the FFM API", Example 8: per block of 32, d = amax / 127 in
+ * float, id = 1/d (0 when d = 0), qs = roundf(x * id), d stored as fp16.
+ * Used only to check the pages' worked Q8_0 examples; the workloads draw their
+ * Q8_0 blocks directly.
+ */
+int orc_quantize_q8_0(const float* x, int64_t n, uint8_t* out) {
+    if (n % 32) return ORC_ERR_SHAPE;
+    for (int64_t b = 0; b < n / 32; b++) {
+        float amax = 0.0f;
+        for (int j = 0; j < 32; j++) {
+            float a = fabsf(x[32 * b + j]);
+            if (a > amax) amax = a;
+        }
+        float d = amax / 127.0f;
+        float id = d != 0.0f ? 1.0f / d : 0.0f;
+        uint16_t dh = orc_f32_to_f16(d);
+        out[34 * b] = (uint8_t)(dh & 0xff);
+        out[34 * b + 1] = (uint8_t)(dh >> 8);
+        for (int j = 0; j < 32; j++) out[34 * b + 2 + j] = (uint8_t)(int8_t)round_half_away(x[32 * b + j] * id);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * The operations of the forward pass ("The Forward Pass in Java",
+ * Examples 3-10 and Project 18; "What a Llama model computes, and why",
+ * section 2).
+ * ---------------------------------------------------------------------- */
+
+/* RMSNorm, Example 4: y = x / sqrt(mean(x^2) + eps) * w, with the sum of squares
+ * accumulated in double and the scale rounded to float once. */
+void orc_rmsnorm(float* out, const float* x, const float* w, int32_t n, float eps) {
+    double ss = 0.0;
+    for (int32_t i = 0; i < n; i++) ss += (double)x[i] * x[i];
+    float scale = (float)(1.0 / sqrt(ss / (double)n + (double)eps));
+    for (int32_t i = 0; i < n; i++) out[i] = x[i] * scale * w[i];
+}
+
+/* One sequential fp32 dot product over i ascending (Example 5). */
+static float dot(const float* w, const float* x, int64_t n) {
+    float s = 0.0f;
+    for (int64_t i = 0; i < n; i++) s += w[i] * x[i];
+    return s;
+}
+
+/* Matrix-vector product in GGUF order, Example 5: a tensor with dims
+ * [cols, rows] stores row r at r * cols; out[r] = sum_i w[r*cols + i] * x[i]. */
+void orc_matvec(float* out, const float* w, const float* x, int32_t rows, int32_t cols) {
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < rows; r++) out[r] = dot(w + (int64_t)r * cols, x, cols);
+}
+
+/* The same product for n inputs at once, row-outer: each weight row is read
+ * once and dotted with every input, each dot exactly as orc_matvec computes it
+ * ("What a Llama model computes, and why", section 4: a batch reads each weight
+ * once, and each row of the batched product performs the vector product's
+ * operations). x is [n][cols], out is [n][rows]. */
+void orc_matmul(float* out, const float* w, const float* x, int32_t n, int32_t rows, int32_t cols) {
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < rows; r++)
+        for (int32_t t = 0; t < n; t++) out[(int64_t)t * rows + r] = dot(w + (int64_t)r * cols, x + (int64_t)t * cols, cols);
+}
+
+/* The rotation angles of one position, Example 6: theta_scale = base^(-2/n_rot)
+ * evaluated in double and rounded to float; theta starts at pos and is
+ * multiplied by theta_scale in float once per pair; cos and sin are taken in
+ * double and rounded to float. */
+void orc_rope_cos_sin(int32_t pos, int32_t rope_dims, float base, float* cos_out, float* sin_out) {
+    float theta_scale = (float)pow((double)base, -2.0 / rope_dims);
+    float theta = (float)pos;
+    for (int32_t i = 0; i < rope_dims / 2; i++) {
+        cos_out[i] = (float)cos((double)theta);
+        sin_out[i] = (float)sin((double)theta);
+        theta *= theta_scale;
+    }
+}
+
+/* RoPE, Example 6: rotate pair i of every head by theta_i. Normal layout pairs
+ * (2i, 2i+1); NEOX pairs (i, i + n_rot/2). Dimensions past n_rot are left alone. */
+void orc_rope(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, int32_t pos, float base, int32_t neox) {
+    float* c = (float*)malloc(sizeof(float) * (size_t)(rope_dims / 2 + 1));
+    float* s = (float*)malloc(sizeof(float) * (size_t)(rope_dims / 2 + 1));
+    orc_rope_cos_sin(pos, rope_dims, base, c, s);
+    for (int32_t h = 0; h < n_heads; h++) {
+        for (int32_t i = 0; i < rope_dims / 2; i++) {
+            int32_t a = h * head_dim + (neox ? i : 2 * i);
+            int32_t b = neox ? a + rope_dims / 2 : a + 1;
+            float x0 = vec[a], x1 = vec[b];
+            vec[a] = x0 * c[i] - x1 * s[i];
+            vec[b] = x0 * s[i] + x1 * c[i];
+        }
+    }
+    free(c);
+    free(s);
+}
+
+/* silu(z) = z / (1 + e^-z), Example 8. */
+float orc_silu(float z) { return z / (1.0f + (float)exp(-(double)z)); }
+
+/* Greedy choice, Example 9: the first index of the strict maximum. */
+int32_t orc_argmax(const float* v, int32_t n) {
+    int32_t best = 0;
+    for (int32_t i = 1; i < n; i++)
+        if (v[i] > v[best]) best = i;
+    return best;
+}
+
+/*
+ * Cached grouped-query attention for one token at position pos, Example 7 and
+ * Project 18. The caches hold binary16 bits in the pages' flat layout: row t of
+ * kv head g starts at t * kv_dim + g * head_dim. Query head h reads kv head
+ * h / (n_heads / n_kv_heads). Scores are divided by (float)sqrt(head_dim); the
+ * softmax subtracts the maximum, takes exp in double rounded to float, sums in
+ * float over t ascending; then out_h = sum_t (e_t / sum) * V_t.
+ * `weights`, when not NULL, receives the normalised weights [n_heads][pos+1].
+ */
+void orc_attention(float* out, const float* q, const uint16_t* kcache, const uint16_t* vcache, int32_t n_heads,
+                   int32_t n_kv_heads, int32_t head_dim, int32_t pos, float* weights) {
+    int32_t kv_dim = n_kv_heads * head_dim, group = n_heads / n_kv_heads;
+    float denom = (float)sqrt((double)head_dim);
+    for (int32_t i = 0; i < n_heads * head_dim; i++) out[i] = 0.0f;
+#pragma omp parallel for schedule(static)
+    for (int32_t h = 0; h < n_heads; h++) {
+        float* att = (float*)malloc(sizeof(float) * (size_t)(pos + 1));
+        int32_t kv_off = (h / group) * head_dim;
+        float mx = -INFINITY;
+        for (int32_t t = 0; t <= pos; t++) {
+            float s = 0.0f;
+            for (int32_t i = 0; i < head_dim; i++)
+                s += q[h * head_dim + i] * orc_f16_to_f32(kcache[(int64_t)t * kv_dim + kv_off + i]);
+            att[t] = s / denom;
+            if (att[t] > mx) mx = att[t];
+        }
+        float sum = 0.0f;
+        for (int32_t t = 0; t <= pos; t++) {
+            att[t] = (float)exp((double)(att[t] - mx));
+            sum += att[t];
+        }
+        for (int32_t t = 0; t <= pos; t++) {
+            float a = att[t] / sum;
+            if (weights) weights[(int64_t)h * (pos + 1) + t] = a;
+            for (int32_t i = 0; i < head_dim; i++)
+                out[h * head_dim + i] += a * orc_f16_to_f32(vcache[(int64_t)t * kv_dim + kv_off + i]);
+        }
+        free(att);
+    }
+}
+
+/* ------------------------------------------------------------------------
+ * The model: Project 18's Llama class as plain C ("The Forward Pass in Java",
+ * Example 13) with the prefill batch of "What a Llama model computes, and
+ * why", section 4.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    float *attn_norm, *wq, *wk, *wv, *bq, *bk, *bv, *wo, *ffn_norm, *gate, *up, *down;
+} orc_layer;
+
+typedef struct orc_model {
+    orc_config c;
+    float *tok_embd, *out_norm, *output;
+    int tied;
+    orc_layer* layers;
+    uint16_t *kcache, *vcache; /* [layer][n_ctx][kv_dim] binary16 bits */
+    int32_t len;
+} orc_model;
+
+static const orc_tensor* find(const orc_tensor* ts, int32_t n, const char* name) {
+    for (int32_t i = 0; i < n; i++)
+        if (ts[i].name && strcmp(ts[i].name, name) == 0) return &ts[i];
+    return NULL;
+}
+
+static int64_t need_bytes(int32_t dtype, int64_t n) {
+    if (dtype == ORC_F32) return 4 * n;
+    if (dtype == ORC_F16) return 2 * n;
+    if (dtype == ORC_Q8_0) return n / 32 * 34;
+    return -1;
+}
+
+/* Fetch tensor `name` with dims (ne0[, ne1]) and dequantise it into a new array. */
+static int take(const orc_tensor* ts, int32_t n, const char* name, int64_t ne0, int64_t ne1, int optional,
+                float** out) {
+    const orc_tensor* t = find(ts, n, name);
+    *out = NULL;
+    if (!t) return optional ? ORC_OK : ORC_ERR_MISSING;
+    int dims = ne1 > 0 ? 2 : 1;
+    if (t->n_dims != dims || t->ne[0] != ne0 || (dims == 2 && t->ne[1] != ne1)) return ORC_ERR_SHAPE;
+    if (t->dtype != ORC_F32 && t->dtype != ORC_F16 && t->dtype != ORC_Q8_0) return ORC_ERR_DTYPE;
+    if (t->dtype == ORC_Q8_0 && ne0 % 32) return ORC_ERR_SHAPE;
+    int64_t cnt = ne0 * (dims == 2 ? ne1 : 1);
+    if (!t->data || (int64_t)t->nbytes < need_bytes(t->dtype, cnt)) return ORC_ERR_SIZE;
+    *out = (float*)malloc(sizeof(float) * (size_t)cnt);
+    if (!*out) return ORC_ERR_OOM;
+    return orc_dequantize(t->dtype, t->data, cnt, *out);
+}
+
+void orc_free(orc_model* m);
+
+int orc_load(const orc_config* cfg, const orc_tensor* ts, int32_t n, orc_model** out) {
+    *out = NULL;
+    const orc_config c = *cfg;
+    if (c.dim <= 0 || c.n_layers <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 || c.ffn <= 0 ||
+        c.vocab <= 0 || c.n_ctx <= 0 || c.n_heads % c.n_kv_heads || c.rope_dims <= 0 || c.rope_dims > c.head_dim ||
+        c.rope_dims % 2)
+        return ORC_ERR_ARG;
+    orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
+    m->c = c;
+    m->layers = (orc_layer*)calloc((size_t)c.n_layers, sizeof(orc_layer));
+    int32_t qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    int rc = take(ts, n, "token_embd.weight", c.dim, c.vocab, 0, &m->tok_embd);
+    if (!rc) rc = take(ts, n, "output_norm.weight", c.dim, 0, 0, &m->out_norm);
+    if (!rc) rc = take(ts, n, "output.weight", c.dim, c.vocab, 1, &m->output);
+    if (!rc && !m->output) { /* tied embeddings (Example 9) */
+        m->output = m->tok_embd;
+        m->tied = 1;
+    }
+    char name[128];
+    for (int32_t l = 0; l < c.n_layers && !rc; l++) {
+        orc_layer* L = &m->layers[l];
+#define TAKE(field, suffix, a, b, opt)                                      \
+    if (!rc) {                                                              \
+        snprintf(name, sizeof name, "blk.%d.%s", (int)l, suffix);           \
+        rc = take(ts, n, name, a, b, opt, &L->field);                       \
+    }
+        TAKE(attn_norm, "attn_norm.weight", c.dim, 0, 0)
+        TAKE(wq, "attn_q.weight", c.dim, qd, 0)
+        TAKE(wk, "attn_k.weight", c.dim, kvd, 0)
+        TAKE(wv, "attn_v.weight", c.dim, kvd, 0)
+        TAKE(bq, "attn_q.bias", qd, 0, 1)
+        TAKE(bk, "attn_k.bias", kvd, 0, 1)
+        TAKE(bv, "attn_v.bias", kvd, 0, 1)
+        TAKE(wo, "attn_output.weight", qd, c.dim, 0)
+        TAKE(ffn_norm, "ffn_norm.weight", c.dim, 0, 0)
+        TAKE(gate, "ffn_gate.weight", c.dim, c.ffn, 0)
+        TAKE(up, "ffn_up.weight", c.dim, c.ffn, 0)
+        TAKE(down, "ffn_down.weight", c.ffn, c.dim, 0)
+#undef TAKE
+        if (!rc && !((L->bq && L->bk && L->bv) || (!L->bq && !L->bk && !L->bv))) rc = ORC_ERR_MISSING;
+    }
+    if (!rc) {
+        size_t cache = (size_t)c.n_layers * (size_t)c.n_ctx * (size_t)kvd;
+        m->kcache = (uint16_t*)calloc(cache, 2);
+        m->vcache = (uint16_t*)calloc(cache, 2);
+        if (!m->kcache || !m->vcache) rc = ORC_ERR_OOM;
+    }
+    if (rc) {
+        orc_free(m);
+        return rc;
+    }
+    *out = m;
+    return ORC_OK;
+}
+
+void orc_free(orc_model* m) {
+    if (!m) return;
+    if (m->layers) {
+        for (int32_t l = 0; l < m->c.n_layers; l++) {
+            orc_layer* L = &m->layers[l];
+            float* ps[] = {L->attn_norm, L->wq, L->wk, L->wv, L->bq, L->bk, L->bv, L->wo, L->ffn_norm, L->gate, L->up, L->down};
+            for (size_t i = 0; i < sizeof ps / sizeof ps[0]; i++) free(ps[i]);
+        }
+        free(m->layers);
+    }
+    if (!m->tied) free(m->output);
+    free(m->tok_embd);
+    free(m->out_norm);
+    free(m->kcache);
+    free(m->vcache);
+    free(m);
+}
+
+static void add_bias(float* x, const float* b, int32_t n) {
+    if (b)
+        for (int32_t i = 0; i < n; i++) x[i] += b[i];
+}
+
+/* Store one position's K and V, rounding through binary16 (Example 10). */
+static void store_kv(orc_model* m, int32_t l, int32_t pos, const float* k, const float* v) {
+    int32_t kvd = m->c.n_kv_heads * m->c.head_dim;
+    size_t base = ((size_t)l * (size_t)m->c.n_ctx + (size_t)pos) * (size_t)kvd;
+    for (int32_t i = 0; i < kvd; i++) {
+        m->kcache[base + i] = orc_f32_to_f16(k[i]);
+        m->vcache[base + i] = orc_f32_to_f16(v[i]);
+    }
+}
+
+static const uint16_t* layer_k(const orc_model* m, int32_t l) {
+    return m->kcache + (size_t)l * (size_t)m->c.n_ctx * (size_t)(m->c.n_kv_heads * m->c.head_dim);
+}
+static const uint16_t* layer_v(const orc_model* m, int32_t l) {
+    return m->vcache + (size_t)l * (size_t)m->c.n_ctx * (size_t)(m->c.n_kv_heads * m->c.head_dim);
+}
+
+/*
+ * One token at position pos (Project 18, forward): fills the cache at pos in
+ * every layer and writes the logits. Requires 0 <= pos <= len and pos < n_ctx;
+ * afterwards len = pos + 1.
+ */
+int orc_forward(orc_model* m, int32_t token, int32_t pos, float* logits) {
+    const orc_config c = m->c;
+    if (token < 0 || token >= c.vocab) return ORC_ERR_ARG;
+    if (pos < 0 || pos > m->len || pos >= c.n_ctx) return ORC_ERR_POS;
+    int32_t qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+    float* x = (float*)malloc(sizeof(float) * (size_t)c.dim);
+    float* xb = (float*)malloc(sizeof(float) * (size_t)(c.dim > qd ? c.dim : qd));
+    float* q = (float*)malloc(sizeof(float) * (size_t)qd);
+    float* k = (float*)malloc(sizeof(float) * (size_t)kvd);
+    float* v = (float*)malloc(sizeof(float) * (size_t)kvd);
+    float* heads = (float*)malloc(sizeof(float) * (size_t)qd);
+    float* hb = (float*)malloc(sizeof(float) * (size_t)c.ffn);
+    float* hb2 = (float*)malloc(sizeof(float) * (size_t)c.ffn);
+
+    memcpy(x, m->tok_embd + (int64_t)token * c.dim, sizeof(float) * (size_t)c.dim); /* Example 3 */
+    for (int32_t l = 0; l < c.n_layers; l++) {
+        const orc_layer* w = &m->layers[l];
+        orc_rmsnorm(xb, x, w->attn_norm, c.dim, c.eps);
+        orc_matvec(q, w->wq, xb, qd, c.dim);
+        orc_matvec(k, w->wk, xb, kvd, c.dim);
+        orc_matvec(v, w->wv, xb, kvd, c.dim);
+        add_bias(q, w->bq, qd);
+        add_bias(k, w->bk, kvd);
+        add_bias(v, w->bv, kvd);
+        orc_rope(q, c.n_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox);
+        orc_rope(k, c.n_kv_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox);
+        store_kv(m, l, pos, k, v);
+        orc_attention(heads, q, layer_k(m, l), layer_v(m, l), c.n_heads, c.n_kv_heads, c.head_dim, pos, NULL);
+        orc_matvec(xb, w->wo, heads, c.dim, qd);
+        for (int32_t i = 0; i < c.dim; i++) x[i] += xb[i];
+        orc_rmsnorm(xb, x, w->ffn_norm, c.dim, c.eps);
+        orc_matvec(hb, w->gate, xb, c.ffn, c.dim);
+        orc_matvec(hb2, w->up, xb, c.ffn, c.dim);
+        for (int32_t i = 0; i < c.ffn; i++) hb[i] = orc_silu(hb[i]) * hb2[i];
+        orc_matvec(xb, w->down, hb, c.dim, c.ffn);
+        for (int32_t i = 0; i < c.dim; i++) x[i] += xb[i];
+    }
+    orc_rmsnorm(xb, x, m->out_norm, c.dim, c.eps);
+    orc_matvec(logits, m->output, xb, c.vocab, c.dim);
+    m->len = pos + 1;
+    free(x); free(xb); free(q); free(k); free(v); free(heads); free(hb); free(hb2);
+    return ORC_OK;
+}
+
+/*
+ * Prefill of n tokens at positions len .. len+n-1 ("What a Llama model
+ * computes, and why", section 4): the products run row-outer over the batch,
+ * RMSNorm, RoPE and attention per token, and token i attends cache rows
+ * 0 .. len+i. Each token goes through exactly the operations of orc_forward, so
+ * the logits and cache equal token-by-token decoding bit for bit. The logits
+ * of the last token are written. Afterwards len += n.
+ */
+int orc_prefill(orc_model* m, const int32_t* tokens, int32_t n, float* logits) {
+    const orc_config c = m->c;
+    if (n <= 0) return ORC_ERR_ARG;
+    if ((int64_t)m->len + n > c.n_ctx) return ORC_ERR_POS;
+    for (int32_t i = 0; i < n; i++)
+        if (tokens[i] < 0 || tokens[i] >= c.vocab) return ORC_ERR_ARG;
+    int32_t qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim, len = m->len;
+    int32_t wide = c.dim > qd ? c.dim : qd;
+    float* X = (float*)malloc(sizeof(float) * (size_t)n * (size_t)c.dim);
+    float* XB = (float*)malloc(sizeof(float) * (size_t)n * (size_t)wide);
+    float* Q = (float*)malloc(sizeof(float) * (size_t)n * (size_t)qd);
+    float* K = (float*)malloc(sizeof(float) * (size_t)n * (size_t)kvd);
+    float* V = (float*)malloc(sizeof(float) * (size_t)n * (size_t)kvd);
+    float* HEADS = (float*)malloc(sizeof(float) * (size_t)n * (size_t)qd);
+    float* HB = (float*)malloc(sizeof(float) * (size_t)n * (size_t)c.ffn);
+    float* HB2 = (float*)malloc(sizeof(float) * (size_t)n * (size_t)c.ffn);
+    if (!X || !XB || !Q || !K || !V || !HEADS || !HB || !HB2) {
+        free(X); free(XB); free(Q); free(K); free(V); free(HEADS); free(HB); free(HB2);
+        return ORC_ERR_OOM;
+    }
+    for (int32_t t = 0; t < n; t++)
+        memcpy(X + (int64_t)t * c.dim, m->tok_embd + (int64_t)tokens[t] * c.dim, sizeof(float) * (size_t)c.dim);
+    for (int32_t l = 0; l < c.n_layers; l++) {
+        const orc_layer* w = &m->layers[l];
+        for (int32_t t = 0; t < n; t++) orc_rmsnorm(XB + (int64_t)t * c.dim, X + (int64_t)t * c.dim, w->attn_norm, c.dim, c.eps);
+        orc_matmul(Q, w->wq, XB, n, qd, c.dim);
+        orc_matmul(K, w->wk, XB, n, kvd, c.dim);
+        orc_matmul(V, w->wv, XB, n, kvd, c.dim);
+        for (int32_t t = 0; t < n; t++) {
+            float *q = Q + (int64_t)t * qd, *k = K + (int64_t)t * kvd, *v = V + (int64_t)t * kvd;
+            add_bias(q, w->bq, qd);
+            add_bias(k, w->bk, kvd);
+            add_bias(v, w->bv, kvd);
+            orc_rope(q, c.n_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox);
+            orc_rope(k, c.n_kv_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox);
+            store_kv(m, l, len + t, k, v);
+        }
+        for (int32_t t = 0; t < n; t++)
+            orc_attention(HEADS + (int64_t)t * qd, Q + (int64_t)t * qd, layer_k(m, l), layer_v(m, l), c.n_heads,
+                          c.n_kv_heads, c.head_dim, len + t, NULL);
+        orc_matmul(XB, w->wo, HEADS, n, c.dim, qd);
+        for (int64_t i = 0; i < (int64_t)n * c.dim; i++) X[i] += XB[i];
+        for (int32_t t = 0; t < n; t++) orc_rmsnorm(XB + (int64_t)t * c.dim, X + (int64_t)t * c.dim, w->ffn_norm, c.dim, c.eps);
+        orc_matmul(HB, w->gate, XB, n, c.ffn, c.dim);
+        orc_matmul(HB2, w->up, XB, n, c.ffn, c.dim);
+        for (int64_t i = 0; i < (int64_t)n * c.ffn; i++) HB[i] = orc_silu(HB[i]) * HB2[i];
+        orc_matmul(XB, w->down, HB, n, c.dim, c.ffn);
+        for (int64_t i = 0; i < (int64_t)n * c.dim; i++) X[i] += XB[i];
+    }
+    float* xl = X + (int64_t)(n - 1) * c.dim; /* only the last row's logits */
+    orc_rmsnorm(XB, xl, m->out_norm, c.dim, c.eps);
+    orc_matvec(logits, m->output, XB, c.vocab, c.dim);
+    m->len = len + n;
+    free(X); free(XB); free(Q); free(K); free(V); free(HEADS); free(HB); free(HB2);
+    return ORC_OK;
+}
+
+/* A new sequence: the cache length returns to 0 ("The Engine", reset). */
+void orc_reset(orc_model* m) { m->len = 0; }
+
+int32_t orc_kv_len(const orc_model* m) { return m->len; }
+
+/* Binary16 bits of K and V of one layer at one position, kv_dim values each. */
+int orc_kv_read(const orc_model* m, int32_t layer, int32_t pos, uint16_t* k, uint16_t* v) {
+    if (layer < 0 || layer >= m->c.n_layers || pos < 0 || pos >= m->c.n_ctx) return ORC_ERR_ARG;
+    int32_t kvd = m->c.n_kv_heads * m->c.head_dim;
+    size_t base = ((size_t)layer * (size_t)m->c.n_ctx + (size_t)pos) * (size_t)kvd;
+    memcpy(k, m->kcache + base, (size_t)kvd * 2);
+    memcpy(v, m->vcache + base, (size_t)kvd * 2);
+    return ORC_OK;
+}
+
+/* Size of one layer in weights ("The Forward Pass in Java", Example 1):
+ * 2 d^2 + 2 d kv_dim + 3 d ffn + 2 d (biases not counted). */
+int64_t orc_weights_per_layer(int64_t dim, int64_t kv_dim, int64_t ffn) {
+    return 2 * dim * dim + 2 * dim * kv_dim + 3 * dim * ffn + 2 * dim;
+}

@@ -1,0 +1,66 @@
+"""Shared helpers for the tests: small model configurations and tensor sets."""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+from synth import F16, F32, Q8_0, ModelConfig, Tensor
+
+
+def f32_tensor(name: str, arr: np.ndarray, ne: tuple) -> Tensor:
+    a = np.ascontiguousarray(arr, np.float32).reshape(-1)
+    assert a.size == int(np.prod(ne))
+    return Tensor(name, F32, tuple(ne), a.view(np.uint8))
+
+
+def f16_tensor(name: str, bits: np.ndarray, ne: tuple) -> Tensor:
+    a = np.ascontiguousarray(bits, np.uint16).reshape(-1)
+    return Tensor(name, F16, tuple(ne), a.view(np.uint8))
+
+
+def replace_tensors(ts, **arrays):
+    """Return a copy of tensor set `ts` where each named tensor (dots written as
+    '__' in keyword names) is replaced by an F32 tensor of the given values."""
+    repl = {k.replace("__", "."): v for k, v in arrays.items()}
+    out = []
+    for t in ts:
+        if t.name in repl:
+            out.append(f32_tensor(t.name, repl[t.name], t.ne))
+        else:
+            out.append(t)
+    return out
+
+
+def drop(ts, *names):
+    return [t for t in ts if t.name not in names]
+
+
+# Small models that the oracle runs in milliseconds. Widths are chosen so the
+# GPU kernels see several tiles plus a ragged tail (vocab 1000, ffn 352).
+SMALL = ModelConfig("small-f32", dim=128, n_layers=2, n_heads=4, n_kv_heads=2, head_dim=32, ffn=352, vocab=1000,
+                    n_ctx=96, eps=1e-5, rope_base=10000.0, mat_dtype="f32", embd_dtype="f32", out_dtype="f32",
+                    tied=False, gain_std=0.1, seed=11, prompt_len=7, decode_steps=5)
+SMALL_F16 = SMALL.with_(name="small-f16", mat_dtype="f16", embd_dtype="f16", tied=True, seed=12)
+SMALL_Q8 = SMALL.with_(name="small-q8_0", mat_dtype="q8_0", embd_dtype="f32", tied=True, seed=13)
+SMALL_NEOX_BIAS = SMALL.with_(name="small-neox-bias", rope_neox=True, qkv_bias=True, rope_base=1e6, seed=14)
+SMALL_PARTIAL_ROPE = SMALL.with_(name="small-partial-rope", rope_dims=16, seed=15)
+SMALL_MHA = SMALL.with_(name="small-mha", n_kv_heads=4, seed=16, head_dim=48, dim=192, n_heads=4)
+
+
+def selftest_config(neox: bool) -> ModelConfig:
+    """The synthetic model of Project 18's self-test (width 16, 2 layers)."""
+    return ModelConfig("selftest-" + ("qwen2" if neox else "llama"), dim=16, n_layers=2, n_heads=4, n_kv_heads=2,
+                       head_dim=4, ffn=32, vocab=24, n_ctx=64, eps=1e-5, rope_base=10000.0, rope_neox=neox,
+                       mat_dtype="f32", embd_dtype="f32", out_dtype="f32", tied=False, seed=42)
+
+
+def selftest_tensors(cfg: ModelConfig):
+    """Weights N(0, 1/in), as the self-test draws them; both layouts share them."""
+    out = []
+    for name, dt, ne, kind in synth.tensor_specs(cfg):
+        n = int(np.prod(ne))
+        if kind == "gain":
+            out.append(f32_tensor(name, np.ones(n, np.float32), ne))
+        else:
+            out.append(f32_tensor(name, synth.normal(cfg.seed, name, n, std=1.0 / np.sqrt(ne[0])), ne))
+    return out
