@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the Llama-family forward pass on one MI355X.
+
+Headline workload: the 1B-shape model (16 layers, d 2048, 32/8 heads of 64,
+FFN 8192, vocab 128256) with Q8_0 matrices and a tied F32 embedding, seeded
+random weights; the KV cache is prefilled with 2048 seeded prompt ids, then K
+greedy decode steps run at positions 2048 .. 2048+K-1 (device-side token
+feedback, llm_generate). A step is one token's full forward pass.
+
+The line also reports
+  - roofline: the dominant kernel (the final RMSNorm + vocabulary product +
+    argmax launch, 1.05 GB of F32 weights per launch) timed with HIP events on
+    the stream it runs on; HBM traffic from the committed rocprofv3 counter runs;
+  - prefill: llm_prefill of 512 seeded ids on the Qwen2-style F16 variant;
+  - cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 8]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+F16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+
+
+def algorithmic_step_bytes(cfg, pos):
+    """Bytes one decode step at position pos must move: every weight once, K and
+    V rows 0..pos read, one K/V row written, the embedding row (tied: the table
+    is also the output matrix, read once by the vocabulary product)."""
+    import synth
+
+    total = 0
+    for name, dt, ne, kind in synth.tensor_specs(cfg):
+        n = 1
+        for e in ne:
+            n *= e
+        if name == "token_embd.weight":
+            total += synth.nbytes_of(dt, cfg.dim * cfg.vocab) if cfg.tied else synth.nbytes_of(dt, cfg.dim)
+            continue
+        total += synth.nbytes_of(dt, n)
+    kv_row = 2 * cfg.n_layers * cfg.kv_dim * 2  # K and V, f16
+    total += kv_row * (pos + 1)  # read rows 0..pos (row pos written then read)
+    return total
+
+
+def logits_kernel_bytes(cfg):
+    """Algorithmic bytes of one logits launch: the output matrix, the residual
+    vector and gain in, the logits out."""
+    import synth
+
+    dt = synth.DTYPE_IDS[cfg.embd_dtype] if cfg.tied else synth.DTYPE_IDS[cfg.out_dtype]
+    return synth.nbytes_of(dt, cfg.dim * cfg.vocab) + 2 * cfg.dim * 4 + cfg.vocab * 4
+
+
+def read_traffic():
+    """HBM bytes per launch of the logits kernel from the committed counter runs
+    (profiles/logits_q8_1b_counters.txt), or None when absent."""
+    p = os.path.join(ROOT, "profiles", "logits_q8_1b_counters.txt")
+    if not os.path.exists(p):
+        return None
+    for line in open(p):
+        if line.startswith("traffic_bytes_per_launch:"):
+            try:
+                return float(line.split(":", 1)[1])
+            except ValueError:
+                return None
+    return None
+
+
+def cpu_baseline(cfg, budget_s=20.0):
+    """The oracle, untuned, on a bounded sample of the decode workload: a short
+    prompt prefill (not timed), then decode steps until the time budget."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    ts = synth.make_tensor_set(cfg)
+    m = oracle.Model(cfg, ts)
+    del ts
+    toks = synth.prompt(cfg, 16)
+    logits = m.prefill(toks)
+    pos, n, t0 = 16, 0, time.perf_counter()
+    while True:
+        tok = oracle.argmax(logits)
+        logits = m.forward(tok, pos)
+        pos += 1
+        n += 1
+        if time.perf_counter() - t0 > budget_s or n >= 64:
+            break
+    dt = time.perf_counter() - t0
+    m.close()
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    return {"value": round(n / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} greedy decode steps of the same 1B Q8_0 model at positions 16..{15 + n} after a 16-id "
+                      f"oracle prefill (cache 16 positions instead of 2048; attention is under 3% of the bytes)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--reps", type=int, default=5, help="repetitions of the timed decode run (median)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the decode path has no multi-GPU sharding in this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import llama_family_decode_amd as llm
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    cfg = synth.C4  # 1B shape, Q8_0 matrices, tied F32 embedding
+    ctx_len = 2048
+    t_load = time.perf_counter()
+    ts = synth.make_tensor_set(cfg)
+    model = llm.Model(cfg, ts)
+    del ts
+    prompt = synth.prompt(cfg, ctx_len)
+    nxt = model.prefill(prompt)
+    torch.cuda.synchronize()
+    print(f"# loaded + prefilled {ctx_len} in {time.perf_counter() - t_load:.1f}s", file=sys.stderr, flush=True)
+
+    # warmup (then rewind to the prefilled length)
+    if args.warmup > 0:
+        model.generate(nxt, args.warmup)
+        model.rewind(ctx_len)
+    times = []
+    toks = None
+    for r in range(max(1, args.reps)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = model.generate(nxt, args.steps)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        model.rewind(ctx_len)
+        if toks is None:
+            toks = out
+        else:
+            assert np.array_equal(toks, out), "greedy decode is not deterministic"
+    dt = float(np.median(times))
+    tok_s = args.steps / dt
+    mid_pos = ctx_len + args.steps // 2
+    step_bytes = algorithmic_step_bytes(cfg, mid_pos)
+    print(f"# decode {tok_s:.1f} tok/s ({1e3 * dt / args.steps:.3f} ms/token), step bytes {step_bytes / 1e6:.1f} MB "
+          f"-> {step_bytes * tok_s / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+
+    # dominant kernel: the logits launch, timed with HIP events on its stream
+    ms_logits = model.time_stage(llm.STAGE_LOGITS, 0, 0, 20)
+    lb = logits_kernel_bytes(cfg)
+    achieved = lb / (ms_logits * 1e-3) / 1e9
+    stages = {}
+    for name, st in (("qkv", llm.STAGE_QKV), ("attn", llm.STAGE_ATTN), ("o", llm.STAGE_O),
+                     ("ffn_up", llm.STAGE_FFN_UP), ("down", llm.STAGE_DOWN)):
+        stages[name] = round(model.time_stage(st, 0, mid_pos, 50) * 1e3, 2)
+    stages["logits"] = round(ms_logits * 1e3, 2)
+    print(f"# stage times (us): {stages}", file=sys.stderr, flush=True)
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+
+    prefill = None
+    if not args.no_prefill:
+        c5 = synth.C5
+        ts = synth.make_tensor_set(c5)
+        pm = llm.Model(c5, ts)
+        del ts
+        p5 = synth.prompt(c5, 512)
+        pm.prefill(p5)
+        pm.reset()
+        ptimes = []
+        for _ in range(5):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            pm.prefill(p5)
+            torch.cuda.synchronize()
+            ptimes.append(time.perf_counter() - t0)
+            pm.reset()
+        pt = float(np.median(ptimes))
+        gemm_flop = 2.0 * 512 * c5.n_layers * (
+            c5.dim * (c5.q_dim + 2 * c5.kv_dim) + c5.q_dim * c5.dim + 2 * c5.dim * c5.ffn + c5.ffn * c5.dim)
+        prefill = {"config": c5.name, "tokens": 512, "ms": round(pt * 1e3, 3), "tok_s": round(512 / pt, 1),
+                   "gemm_tflop": round(gemm_flop / 1e12, 4),
+                   "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
+        print(f"# prefill 512: {pt * 1e3:.2f} ms, {512 / pt:.0f} tok/s", file=sys.stderr, flush=True)
+        pm.close()
+        del pm
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg)
+        print(f"# cpu oracle {cpu['value']} tok/s on {cpu['cores']} threads", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "decode tok/s (1B-shape Q8_0, tied F32 embedding, KV cache prefilled to 2048)",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * dt / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q8_0 weights, fp32 arithmetic, f16 KV",
+        "data": "synthetic: seeded random weights and prompt ids",
+        "config": {"workload": "llama-1b-q8_0 decode at positions 2048..2175 after a 2048-id prefill",
+                   "dim": cfg.dim, "layers": cfg.n_layers, "heads": cfg.n_heads, "kv_heads": cfg.n_kv_heads,
+                   "ffn": cfg.ffn, "vocab": cfg.vocab, "ctx": ctx_len, "parallelism": "single GPU"},
+        "step_roofline": {"bytes_per_token": step_bytes, "achieved_GBs": round(step_bytes * tok_s / 1e9, 1),
+                          "peak_GBs": HBM_PEAK_GBS, "frac": round(step_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "k_gemv<F32, NORM, ARGMAX> (final RMSNorm + vocabulary product + argmax)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                     "bytes_per_launch": lb, "ms_per_launch": round(ms_logits, 5)},
+        "stage_us": stages,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

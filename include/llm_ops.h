@@ -1,0 +1,79 @@
+/*
+ * llm_ops.h - per-kernel entry points on a loaded context.
+ *
+ * Each call runs one of the decode step's fused kernels on its own, with the
+ * same kernel, arguments layout and launch configuration the step uses, on
+ * caller-given inputs. They exist so a caller can check or time one stage of
+ * the forward pass in isolation ("The Forward Pass in Java", Example 11 checks
+ * the forward pass tensor by tensor). None of them changes kv_len. All return
+ * LLM_OK or a negative LLM_ERR_* (include/llm.h), validate before any device
+ * work, enqueue on the context's stream, and do not wait for it unless a host
+ * output pointer is given. d_* are device pointers of the sizes named.
+ */
+#ifndef LLM_OPS_H
+#define LLM_OPS_H
+
+#include "llm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Stages of one decode step, in order. */
+#define LLM_STAGE_QKV 0    /* RMSNorm + Q/K/V products + bias + RoPE + F16 KV store */
+#define LLM_STAGE_ATTN 1   /* grouped-query attention over the cache */
+#define LLM_STAGE_O 2      /* output product + residual add */
+#define LLM_STAGE_FFN_UP 3 /* RMSNorm + gate/up products + SwiGLU */
+#define LLM_STAGE_DOWN 4   /* down product + residual add */
+#define LLM_STAGE_LOGITS 5 /* final RMSNorm + vocabulary product + greedy argmax */
+
+/* QKV stage of `layer` at position pos (0 <= pos < n_ctx): h = rmsnorm(d_x)
+ * * attn_norm ("The Forward Pass in Java", Example 4), q|k|v = W h (+ bias),
+ * RoPE at pos on q and k (Example 6); writes rotated q (n_heads*head_dim floats)
+ * to d_q and binary16 k, v to the layer's cache row pos (Example 10).
+ * d_x: dim floats. */
+int llm_op_qkv(llm_ctx* ctx, int32_t layer, int32_t pos, const float* d_x, float* d_q);
+
+/* Attention stage of `layer` for one token at position pos (0 <= pos < n_ctx):
+ * d_q (n_heads*head_dim floats, already rotated) attends cache rows 0..pos
+ * (Example 7); writes n_heads*head_dim floats to d_out. */
+int llm_op_attention(llm_ctx* ctx, int32_t layer, int32_t pos, const float* d_q, float* d_out);
+
+/* Output stage: d_x (dim floats) += W_o d_in (d_in: n_heads*head_dim floats). */
+int llm_op_o(llm_ctx* ctx, int32_t layer, const float* d_in, float* d_x);
+
+/* FFN-up stage: h = rmsnorm(d_x) * ffn_norm; d_u[j] = silu(W_gate h)_j *
+ * (W_up h)_j (Example 8); d_u: ffn floats. */
+int llm_op_ffn_up(llm_ctx* ctx, int32_t layer, const float* d_x, float* d_u);
+
+/* Down stage: d_x (dim floats) += W_down d_u (d_u: ffn floats). */
+int llm_op_down(llm_ctx* ctx, int32_t layer, const float* d_u, float* d_x);
+
+/* Logits stage on residual vector d_x (dim floats): final RMSNorm, the
+ * vocabulary product into the context's logits buffer (and d_logits if not
+ * NULL) and the greedy argmax (Example 9); *h_next (if not NULL) receives it,
+ * after waiting for the stream. */
+int llm_op_logits(llm_ctx* ctx, const float* d_x, float* d_logits, int32_t* h_next);
+
+/* Writes rows pos0 .. pos0+n_pos-1 of `layer`'s K and V caches from host
+ * binary16 bits laid out as the pages' flat cache, [pos][n_kv_heads*head_dim]
+ * (Example 7). Requires pos0 >= 0 and pos0 + n_pos <= n_ctx. Waits. */
+int llm_op_kv_write(llm_ctx* ctx, int32_t layer, int32_t pos0, int32_t n_pos, const uint16_t* h_k,
+                    const uint16_t* h_v);
+
+/* Average device time in milliseconds of one launch of `stage` (LLM_STAGE_*)
+ * of `layer`, over n_launch back-to-back launches bracketed by HIP events on
+ * the context's stream, with the context's own scratch buffers as inputs
+ * (their contents do not affect the time). The attention stage runs at
+ * position pos. Waits. */
+int llm_op_time(llm_ctx* ctx, int32_t stage, int32_t layer, int32_t pos, int32_t n_launch, float* h_ms);
+
+/* Moves the sequence end back: kv_len = len, for 0 <= len <= kv_len ("The
+ * Forward Pass in Java", Example 13: rewritten cache entries give the same
+ * results). */
+int llm_rewind(llm_ctx* ctx, int32_t len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLM_OPS_H */

@@ -1,0 +1,119 @@
+// Internal types shared by the host runtime and the gfx950 kernels of libllm.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace llm {
+
+enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_Q8 = 8 };
+
+// A weight matrix in device layout: `rows` output rows of `cols` inputs.
+//  F32/F16: row r at w + r * cols elements (cols % 32 == 0, so rows are 64/128-byte aligned).
+//  Q8_0:    int8 quants row r at w + r * cols bytes; fp16 scales row r at s + r * cols/32,
+//           scale b of row r belonging to quants [32b, 32b+32).
+struct Mat {
+    int dtype;
+    int rows, cols;
+    const void* w;
+    const uint16_t* s;
+};
+
+// Decode-step state, resident in device memory so that a captured graph can run
+// any step: the kernels read token and pos from here, the argmax writes next.
+struct State {
+    int token;
+    int pos;
+    int next;
+    int nonfinite;
+    int gen_mode;   // 1: the argmax also advances token/pos and appends to gen_out
+    int gen_count;
+    unsigned long long best;  // argmax key of the running step (0 = none yet)
+};
+
+// Per-block partial of the vocabulary argmax (pass 1).
+struct ArgPart {
+    float val;
+    int idx;
+    int nonfinite;
+    int pad;
+};
+
+constexpr int kBlock = 256;  // threads per block for all decode kernels (4 wave64)
+constexpr int kWaves = kBlock / 64;
+constexpr int kMaxCols = 16384;
+constexpr int kMaxHeadDim = 256;
+constexpr int kMaxGroup = 8;  // n_heads / n_kv_heads must be 1, 2, 4 or 8
+constexpr int kAttnChunk = 512;     // positions per online-softmax chunk inside an attention block
+constexpr int kPrefillChunk = 512;  // tokens per prefill batch
+
+// Prologue of a vector product: where the input vector comes from.
+enum Pro : int {
+    PRO_PLAIN = 0,  // x = xin (fp32 vector)
+    PRO_NORM = 1,   // x = rmsnorm(xin) * gain
+    PRO_EMBED = 2,  // x = rmsnorm(E[token]) * gain, and E[token] becomes the residual stream
+};
+// Epilogue of a vector product: what happens to the row results.
+enum Epi : int {
+    EPI_STORE = 0,   // y[r] = acc
+    EPI_RESID = 1,   // y[r] += acc (residual add)
+    EPI_SWIGLU = 2,  // rows (2j, 2j+1) = (gate j, up j): y[j] = silu(gate) * up
+    EPI_QKV = 3,     // bias, RoPE on q and k, q -> y, k and v -> F16 cache at pos
+    EPI_ARGMAX = 4,  // y[r] = acc, plus the greedy argmax over all rows
+};
+
+struct GemvArgs {
+    Mat W;
+    const float* xin;
+    const float* gain;
+    float eps;
+    Mat E;            // embedding table (PRO_EMBED)
+    float* xres;      // PRO_EMBED: the residual stream written by block 0
+    State* st;
+    float* y;
+    const float* bias;  // EPI_QKV: concatenated q|k|v bias or nullptr
+    // EPI_QKV
+    int n_heads, n_kv_heads, head_dim, n_rot, neox, n_ctx;
+    const float2* rope;  // [n_ctx][n_rot/2] (cos, sin)
+    __half* kc;          // this layer's K cache [n_kv_heads][n_ctx][head_dim]
+    __half* vc;
+    // EPI_ARGMAX
+    int* gen_out;
+    int gen_cap;
+};
+
+struct AttnArgs {
+    const float* q;       // [n_q][n_heads*head_dim]
+    const __half* kc;     // this layer's caches [n_kv_heads][n_ctx][head_dim]
+    const __half* vc;
+    float* out;           // fp32 [n_q][n_heads*head_dim]
+    __half* out_h;        // optional f16 copy of the output (prefill MFMA input) or nullptr
+    float* part;          // split partials
+    const State* st;      // decode: P = st->pos + 1
+    int p0;               // prefill: query z is at position p0 + z
+    int n_heads, n_kv_heads, head_dim, n_ctx;
+    int n_split;          // gridDim.x
+    float scale_div;      // scores are divided by this ((float)sqrt(head_dim))
+};
+
+// Launchers (kernels_decode.hip / kernels_prefill.hip).
+hipError_t launch_rope_table(float2* tab, int n_pos, int n_rot, float theta_scale, hipStream_t s);
+hipError_t launch_gemv(int pro, int epi, const GemvArgs& a, int grid, hipStream_t s);
+int gemv_grid(int pro, int epi, int rows);
+hipError_t launch_attn(const AttnArgs& a, int n_q, hipStream_t s);
+hipError_t launch_set_state(State* st, int token, int pos, int gen_mode, hipStream_t s);
+hipError_t launch_argmax_finalize(State* st, int* gen_out, int gen_cap, hipStream_t s);
+
+struct PrefillBufs;
+hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
+                               hipStream_t s);
+// Y[n][rows] op= A[n][K] * W^T, A fp16 (MFMA path for F16/Q8 weights) or fp32 (F32 weights).
+hipError_t launch_gemm(int epi, const Mat& W, const __half* Ah, const float* Af, int n, float* Y, int ldy,
+                       __half* Yh, int ldyh, const float* bias, hipStream_t s);
+hipError_t launch_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int n_kv_heads, int head_dim, int n_rot,
+                               int neox, int n_ctx, const float2* rope, float* Q, __half* kc, __half* vc,
+                               hipStream_t s);
+
+}  // namespace llm

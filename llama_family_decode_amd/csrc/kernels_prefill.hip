@@ -1,0 +1,355 @@
+// Prefill kernels for gfx950: a batch of n tokens at positions p0 .. p0+n-1
+// ("What a Llama model computes, and why", section 4). The vector products
+// become matrix products over the batch, which run on the matrix cores:
+// v_mfma_f32_16x16x32_f16 with the activations rounded to binary16 (as ggml
+// does for F16 weights, section 8) and fp32 accumulation. Q8_0 quants are exact
+// in binary16; each 32-deep product is one Q8_0 block, so its fp32 partial is
+// scaled by that block's fp16 scale before it joins the accumulator. F32
+// weights use an fp32 VALU product instead (no rounding of activations).
+// RMSNorm, RoPE and attention run per token.
+#include "common.h"
+
+#include <math.h>
+
+namespace llm {
+
+// (x0, x1) rotated by the angle whose (cos, sin) is cs, each product rounded
+// separately as the pages' RoPE computes it (no fused multiply-add).
+__device__ __forceinline__ float2 pf_rope_rotate(float x0, float x1, float2 cs) {
+#pragma clang fp contract(off)
+    return make_float2(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x);
+}
+
+__device__ __forceinline__ float pf_h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+__device__ __forceinline__ float pf_silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ------------------------------------------------------------ embedding rows
+__global__ void k_embed_rows(Mat E, const int* tokens, int n, float* X, int dim) {
+    const int row = blockIdx.x;
+    const int64_t t = tokens[row];
+    for (int i = threadIdx.x; i < dim; i += blockDim.x) {
+        float v;
+        if (E.dtype == DT_F32)
+            v = ((const float*)E.w)[t * dim + i];
+        else if (E.dtype == DT_F16)
+            v = pf_h2f(((const uint16_t*)E.w)[t * dim + i]);
+        else
+            v = pf_h2f(E.s[t * (dim / 32) + i / 32]) * (float)((const int8_t*)E.w)[t * dim + i];
+        X[(size_t)row * dim + i] = v;
+    }
+}
+
+hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s) {
+    hipLaunchKernelGGL(k_embed_rows, dim3(n), dim3(256), 0, s, E, tokens, n, X, dim);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ RMSNorm rows
+// y = (x * scale) * g with scale = (float)(1 / sqrt(sum(x^2)/n + eps)), the sum in
+// double ("The Forward Pass in Java", Example 4). Writes fp32 and/or fp16 rows.
+__global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const float* gain, int dim, float eps, float* Yf,
+                                                      __half* Yh) {
+    __shared__ double red[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const float* x = X + (size_t)row * dim;
+    double ss = 0.0;
+    for (int i = tid; i < dim; i += 256) ss += (double)x[i] * (double)x[i];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    const double tot = red[0] + red[1] + red[2] + red[3];
+    const float scale = (float)(1.0 / sqrt(tot / (double)dim + (double)eps));
+    for (int i = tid; i < dim; i += 256) {
+        const float y = x[i] * scale * gain[i];
+        if (Yf) Yf[(size_t)row * dim + i] = y;
+        if (Yh) Yh[(size_t)row * dim + i] = __float2half_rn(y);
+    }
+}
+
+hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(k_rmsnorm_rows, dim3(n), dim3(256), 0, s, X, gain, dim, eps, Yf, Yh);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ MFMA GEMM
+// Y[m][n] (op)= sum_k A[m][k] * W[n][k] for m < M tokens, n < N weight rows.
+// Block tile 128 (m) x 128 (n), K step 32, four waves in a 2 x 2 arrangement,
+// each wave 64 x 64 = 4 x 4 tiles of the 16x16x32 instruction. For that
+// instruction lane l supplies A[l%16][8*(l/16) + j] and B[8*(l/16) + j][l%16]
+// (j < 8) and receives D[4*(l/16) + i][l%16] (i < 4).
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4p __attribute__((ext_vector_type(4)));
+
+constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LD = GB_K + 8;  // LDS row pitch in halfs
+
+template <int DT, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const __half* A, int M, float* Y, int ldy, __half* Yh,
+                                                   int ldyh, const float* bias) {
+    __shared__ __attribute__((aligned(16))) _Float16 As[GB_M * GB_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[GB_N * GB_LD];
+    __shared__ float Ss[GB_N];
+
+    const int N = W.rows, K = W.cols;
+    const int n0 = blockIdx.x * GB_N, m0 = blockIdx.y * GB_M;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // global -> register staging: thread t owns row t/2, k offset 16*(t%2)
+    const int lr = tid >> 1, lk = (tid & 1) * 16;
+    const int am = m0 + lr, bn = n0 + lr;
+    const bool a_ok = am < M, b_ok = bn < N;
+    const _Float16* arow = (const _Float16*)A + (size_t)(a_ok ? am : 0) * K;
+
+    u32x4p ra0, ra1, rb0, rb1;
+    float rs = 0.f;
+    const u32x4p z4 = {0u, 0u, 0u, 0u};
+    const char* bbase = (const char*)W.w + (size_t)(b_ok ? bn : 0) * K * (DT == DT_F16 ? 2 : 1);
+    const uint16_t* sbase = (DT == DT_Q8) ? W.s + (size_t)(b_ok ? bn : 0) * (K / 32) : nullptr;
+
+#define GEMM_GLOAD(k0)                                                                         \
+    do {                                                                                       \
+        ra0 = a_ok ? *(const u32x4p*)(arow + (k0) + lk) : z4;                                  \
+        ra1 = a_ok ? *(const u32x4p*)(arow + (k0) + lk + 8) : z4;                              \
+        if constexpr (DT == DT_F16) {                                                          \
+            const _Float16* brow = (const _Float16*)bbase;                                     \
+            rb0 = b_ok ? __builtin_nontemporal_load((const u32x4p*)(brow + (k0) + lk)) : z4;   \
+            rb1 = b_ok ? __builtin_nontemporal_load((const u32x4p*)(brow + (k0) + lk + 8)) : z4; \
+        } else {                                                                               \
+            rb0 = b_ok ? __builtin_nontemporal_load((const u32x4p*)(bbase + (k0) + lk)) : z4;  \
+            rs = b_ok ? pf_h2f(sbase[(k0) / 32]) : 0.f;                                        \
+        }                                                                                      \
+    } while (0)
+
+    float4v acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+    GEMM_GLOAD(0);
+    for (int k0 = 0; k0 < K; k0 += GB_K) {
+        __syncthreads();
+        *(u32x4p*)(As + lr * GB_LD + lk) = ra0;
+        *(u32x4p*)(As + lr * GB_LD + lk + 8) = ra1;
+        if constexpr (DT == DT_F16) {
+            *(u32x4p*)(Bs + lr * GB_LD + lk) = rb0;
+            *(u32x4p*)(Bs + lr * GB_LD + lk + 8) = rb1;
+        } else {
+            half8 h0, h1;
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int w = (int)rb0[j];
+                const _Float16 q0 = (_Float16)((w << 24) >> 24), q1 = (_Float16)((w << 16) >> 24);
+                const _Float16 q2 = (_Float16)((w << 8) >> 24), q3 = (_Float16)(w >> 24);
+                if (j < 2) {
+                    h0[4 * j] = q0; h0[4 * j + 1] = q1; h0[4 * j + 2] = q2; h0[4 * j + 3] = q3;
+                } else {
+                    h1[4 * j - 8] = q0; h1[4 * j - 7] = q1; h1[4 * j - 6] = q2; h1[4 * j - 5] = q3;
+                }
+            }
+            *(half8*)(Bs + lr * GB_LD + lk) = h0;
+            *(half8*)(Bs + lr * GB_LD + lk + 8) = h1;
+            if ((tid & 1) == 0) Ss[lr] = rs;
+        }
+        __syncthreads();
+        if (k0 + GB_K < K) GEMM_GLOAD(k0 + GB_K);
+        half8 af[4], bf[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) af[i] = *(const half8*)(As + (64 * wm + 16 * i + fr) * GB_LD + fk);
+#pragma unroll
+        for (int j = 0; j < 4; j++) bf[j] = *(const half8*)(Bs + (64 * wn + 16 * j + fr) * GB_LD + fk);
+        if constexpr (DT == DT_F16) {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float sc = Ss[64 * wn + 16 * j + fr];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float4v p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], (float4v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    acc[i][j] += sc * p;
+                }
+            }
+        }
+    }
+#undef GEMM_GLOAD
+
+    // epilogue
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int n = n0 + 64 * wn + 16 * j + fr;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int m = m0 + 64 * wm + 16 * i + (lane >> 4) * 4 + e;
+                const float v = acc[i][j][e];
+                if constexpr (EPI == EPI_SWIGLU) {
+                    const float up = __shfl_xor(v, 1, 64);
+                    if ((fr & 1) == 0 && m < M && n < N) {
+                        const float u = pf_silu(v) * up;
+                        if (Yh) Yh[(size_t)m * ldyh + n / 2] = __float2half_rn(u);
+                        if (Y) Y[(size_t)m * ldy + n / 2] = u;
+                    }
+                } else if (m < M && n < N) {
+                    if constexpr (EPI == EPI_RESID)
+                        Y[(size_t)m * ldy + n] += v;
+                    else
+                        Y[(size_t)m * ldy + n] = bias ? v + bias[n] : v;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ fp32 GEMM (F32 weights)
+constexpr int GF_T = 64, GF_K = 16;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, float* Y, int ldy, __half* Yh,
+                                                  int ldyh, const float* bias) {
+    __shared__ float As[GF_K][GF_T + 4];
+    __shared__ float Bs[GF_K][GF_T + 4];
+    const int N = W.rows, K = W.cols;
+    const int n0 = blockIdx.x * GF_T, m0 = blockIdx.y * GF_T;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const float* Wf = (const float*)W.w;
+    float acc[4][4] = {};
+    // loader: each thread loads 4 consecutive k of one row for A and for B
+    const int lrow = tid >> 2, lk = (tid & 3) * 4;
+    for (int k0 = 0; k0 < K; k0 += GF_K) {
+        const int am = m0 + lrow, bn = n0 + lrow;
+        float4 av = make_float4(0.f, 0.f, 0.f, 0.f), bv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (am < M) av = *(const float4*)(A + (size_t)am * K + k0 + lk);
+        if (bn < N) bv = *(const float4*)(Wf + (size_t)bn * K + k0 + lk);
+        __syncthreads();
+        As[lk + 0][lrow] = av.x; As[lk + 1][lrow] = av.y; As[lk + 2][lrow] = av.z; As[lk + 3][lrow] = av.w;
+        Bs[lk + 0][lrow] = bv.x; Bs[lk + 1][lrow] = bv.y; Bs[lk + 2][lrow] = bv.z; Bs[lk + 3][lrow] = bv.w;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < GF_K; k++) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) a[i] = As[k][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; j++) b[j] = Bs[k][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc[i][j] += a[i] * b[j];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int m = m0 + ty * 4 + i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int n = n0 + tx * 4 + j;
+            if (n >= N) continue;
+            if constexpr (EPI == EPI_SWIGLU) {
+                if ((j & 1) == 0) {
+                    const float u = pf_silu(acc[i][j]) * acc[i][j + 1];
+                    if (Y) Y[(size_t)m * ldy + n / 2] = u;
+                    if (Yh) Yh[(size_t)m * ldyh + n / 2] = __float2half_rn(u);
+                }
+            } else if constexpr (EPI == EPI_RESID) {
+                Y[(size_t)m * ldy + n] += acc[i][j];
+            } else {
+                Y[(size_t)m * ldy + n] = bias ? acc[i][j] + bias[n] : acc[i][j];
+            }
+        }
+    }
+}
+
+template <int EPI>
+static hipError_t gemm_epi(const Mat& W, const __half* Ah, const float* Af, int n, float* Y, int ldy, __half* Yh,
+                           int ldyh, const float* bias, hipStream_t s) {
+    if (W.dtype == DT_F32) {
+        dim3 grid((W.rows + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
+        hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, Af, n, Y, ldy, Yh, ldyh, bias);
+    } else {
+        dim3 grid((W.rows + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M);
+        if (W.dtype == DT_F16)
+            hipLaunchKernelGGL((k_gemm_mfma<DT_F16, EPI>), grid, dim3(256), 0, s, W, Ah, n, Y, ldy, Yh, ldyh, bias);
+        else
+            hipLaunchKernelGGL((k_gemm_mfma<DT_Q8, EPI>), grid, dim3(256), 0, s, W, Ah, n, Y, ldy, Yh, ldyh, bias);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(int epi, const Mat& W, const __half* Ah, const float* Af, int n, float* Y, int ldy, __half* Yh,
+                       int ldyh, const float* bias, hipStream_t s) {
+    switch (epi) {
+        case EPI_STORE: return gemm_epi<EPI_STORE>(W, Ah, Af, n, Y, ldy, Yh, ldyh, bias, s);
+        case EPI_RESID: return gemm_epi<EPI_RESID>(W, Ah, Af, n, Y, ldy, Yh, ldyh, bias, s);
+        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, Ah, Af, n, Y, ldy, Yh, ldyh, bias, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------ RoPE + KV rows
+// Row i of the batch is at position p0 + i. Each thread takes one rotation pair
+// of one row (pairs as in the decode epilogue: (2j, 2j+1) normal, (j, j+n_rot/2)
+// NEOX, "The Forward Pass in Java", Example 6), rotates q and k pairs with the
+// table, writes q to Q and k, v to the F16 cache.
+__global__ void k_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int n_kv_heads, int hd, int n_rot,
+                               int neox, int n_ctx, const float2* rope, float* Q, __half* kc, __half* vc) {
+    const int qd = n_heads * hd, kvd = n_kv_heads * hd, W = qd + 2 * kvd;
+    const int hp = hd / 2, half = n_rot / 2;
+    const int pairs = W / 2;
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n * pairs) return;
+    const int row = idx / pairs, pi = idx % pairs;
+    const int head = pi / hp, j = pi % hp;
+    int ra, rb;
+    if (j < half) {
+        ra = head * hd + (neox ? j : 2 * j);
+        rb = neox ? ra + half : ra + 1;
+    } else {
+        ra = head * hd + n_rot + 2 * (j - half);
+        rb = ra + 1;
+    }
+    const int pos = p0 + row;
+    const float* src = QKV + (size_t)row * W;
+    float va = src[ra], vb = src[rb];
+    if (head < n_heads + n_kv_heads && j < half) {
+        const float2 cs = rope[(size_t)pos * half + j];
+const float2 rv = pf_rope_rotate(va, vb, cs);
+        va = rv.x;
+        vb = rv.y;
+    }
+    if (ra < qd) {
+        Q[(size_t)row * qd + ra] = va;
+        Q[(size_t)row * qd + rb] = vb;
+    } else if (ra < qd + kvd) {
+        const int g = (ra - qd) / hd;
+        __half* r = kc + ((size_t)g * n_ctx + pos) * hd;
+        r[(ra - qd) % hd] = __float2half_rn(va);
+        r[(rb - qd) % hd] = __float2half_rn(vb);
+    } else {
+        const int g = (ra - qd - kvd) / hd;
+        __half* r = vc + ((size_t)g * n_ctx + pos) * hd;
+        r[(ra - qd - kvd) % hd] = __float2half_rn(va);
+        r[(rb - qd - kvd) % hd] = __float2half_rn(vb);
+    }
+}
+
+hipError_t launch_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int n_kv_heads, int head_dim, int n_rot,
+                               int neox, int n_ctx, const float2* rope, float* Q, __half* kc, __half* vc,
+                               hipStream_t s) {
+    const int pairs = (n_heads + 2 * n_kv_heads) * head_dim / 2;
+    const int total = n * pairs;
+    hipLaunchKernelGGL(k_rope_kv_rows, dim3((total + 255) / 256), dim3(256), 0, s, QKV, n, p0, n_heads, n_kv_heads,
+                       head_dim, n_rot, neox, n_ctx, rope, Q, kc, vc);
+    return hipGetLastError();
+}
+
+}  // namespace llm

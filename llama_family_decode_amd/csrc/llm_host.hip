@@ -1,0 +1,884 @@
+// Host runtime of libllm: the C ABI of include/llm.h, tensor-set validation,
+// the weight packer, the KV-cache arenas and the per-token launch graph.
+#include "llm.h"
+#include "llm_ops.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using namespace llm;
+
+namespace {
+
+thread_local std::string g_load_error;
+
+struct LayerW {
+    const float* attn_norm;
+    Mat qkv;
+    const float* bqkv;
+    Mat o;
+    const float* ffn_norm;
+    Mat gu;
+    Mat down;
+};
+
+// 256-byte aligned sub-allocation of an arena; with a null base it only measures.
+struct Arena {
+    char* base = nullptr;
+    size_t off = 0;
+    void* take(size_t bytes) {
+        const size_t o = off;
+        off = (off + bytes + 255) & ~(size_t)255;
+        return base ? base + o : (void*)(uintptr_t)(o + 1);  // non-null placeholder when measuring
+    }
+};
+
+size_t mat_bytes_w(int dtype, int64_t rows, int64_t cols) {
+    return dtype == DT_F32 ? (size_t)(rows * cols * 4) : dtype == DT_F16 ? (size_t)(rows * cols * 2) : (size_t)(rows * cols);
+}
+size_t mat_bytes_s(int dtype, int64_t rows, int64_t cols) { return dtype == DT_Q8 ? (size_t)(rows * (cols / 32) * 2) : 0; }
+
+int64_t src_bytes(int dtype, int64_t n) { return dtype == DT_F32 ? 4 * n : dtype == DT_F16 ? 2 * n : n / 32 * 34; }
+
+struct TensorRef {
+    const llm_tensor* t = nullptr;
+};
+
+struct Validated {
+    const llm_tensor* embd;
+    const llm_tensor* out;  // null when tied
+    const llm_tensor* out_norm;
+    struct L {
+        const llm_tensor *attn_norm, *q, *k, *v, *bq, *bk, *bv, *o, *ffn_norm, *gate, *up, *down;
+    };
+    std::vector<L> layers;
+    bool bias;
+};
+
+const llm_tensor* find(const llm_tensor* ts, int32_t n, const char* name) {
+    for (int32_t i = 0; i < n; i++)
+        if (ts[i].name && strcmp(ts[i].name, name) == 0) return &ts[i];
+    return nullptr;
+}
+
+int check_tensor(const llm_tensor* t, const char* name, int64_t ne0, int64_t ne1, bool matrix, std::string& err) {
+    char buf[256];
+    if (!t) {
+        snprintf(buf, sizeof buf, "missing tensor %s", name);
+        err = buf;
+        return LLM_ERR_MISSING;
+    }
+    const int dims = ne1 > 0 ? 2 : 1;
+    if (t->n_dims != dims || t->ne[0] != ne0 || (dims == 2 && t->ne[1] != ne1)) {
+        snprintf(buf, sizeof buf, "tensor %s has dims [%lld, %lld] (n_dims %d); expected [%lld, %lld]", name,
+                 (long long)t->ne[0], (long long)t->ne[1], t->n_dims, (long long)ne0, (long long)(dims == 2 ? ne1 : 1));
+        err = buf;
+        return LLM_ERR_SHAPE;
+    }
+    if (matrix) {
+        if (t->dtype != DT_F32 && t->dtype != DT_F16 && t->dtype != DT_Q8) {
+            snprintf(buf, sizeof buf, "tensor %s has unsupported type %d", name, t->dtype);
+            err = buf;
+            return LLM_ERR_DTYPE;
+        }
+    } else if (t->dtype != DT_F32) {
+        snprintf(buf, sizeof buf, "tensor %s must be F32 (type %d given)", name, t->dtype);
+        err = buf;
+        return LLM_ERR_DTYPE;
+    }
+    const int64_t n = ne0 * (dims == 2 ? ne1 : 1);
+    if (!t->data || (int64_t)t->nbytes < src_bytes(t->dtype, n)) {
+        snprintf(buf, sizeof buf, "tensor %s: %zu bytes given, %lld needed", name, t->nbytes,
+                 (long long)src_bytes(t->dtype, n));
+        err = buf;
+        return LLM_ERR_SIZE;
+    }
+    return LLM_OK;
+}
+
+int validate(const llm_config* c, const llm_tensor* ts, int32_t n, Validated& V, std::string& err) {
+    if (!c || (!ts && n > 0) || n < 0) {
+        err = "null config or tensor list";
+        return LLM_ERR_ARG;
+    }
+    if (c->dim <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->ffn <= 0 ||
+        c->vocab <= 0 || c->n_ctx <= 0 || c->rope_dims <= 0 || c->rope_dims > c->head_dim || (c->rope_dims & 1) ||
+        c->n_heads % c->n_kv_heads || !(c->eps >= 0.0f) || !(c->rope_base > 0.0f) ||
+        (c->rope_neox != 0 && c->rope_neox != 1)) {
+        err = "invalid config";
+        return LLM_ERR_ARG;
+    }
+    const int G = c->n_heads / c->n_kv_heads;
+    const int64_t qd = (int64_t)c->n_heads * c->head_dim, kvd = (int64_t)c->n_kv_heads * c->head_dim;
+    if (c->head_dim % 8 || c->head_dim > kMaxHeadDim || !(G == 1 || G == 2 || G == 4 || G == 8) || c->dim % 32 ||
+        c->dim > kMaxCols || qd % 32 || qd > kMaxCols || c->ffn % 32 || c->ffn > kMaxCols || c->n_ctx > (1 << 20) ||
+        (int64_t)c->vocab * c->dim > ((int64_t)1 << 40)) {
+        err = "config beyond the supported limits (widths multiple of 32 and <= 16384, head_dim multiple of 8 and <= 256, "
+              "group size 1/2/4/8, n_ctx <= 2^20)";
+        return LLM_ERR_LIMIT;
+    }
+    int rc;
+    V.embd = find(ts, n, "token_embd.weight");
+    if ((rc = check_tensor(V.embd, "token_embd.weight", c->dim, c->vocab, true, err))) return rc;
+    V.out_norm = find(ts, n, "output_norm.weight");
+    if ((rc = check_tensor(V.out_norm, "output_norm.weight", c->dim, 0, false, err))) return rc;
+    V.out = find(ts, n, "output.weight");
+    if (V.out && (rc = check_tensor(V.out, "output.weight", c->dim, c->vocab, true, err))) return rc;
+    V.layers.resize(c->n_layers);
+    char nm[128];
+    int n_bias = 0;
+    for (int l = 0; l < c->n_layers; l++) {
+        Validated::L& L = V.layers[l];
+#define GET(field, suffix, a, b, mat)                                       \
+    snprintf(nm, sizeof nm, "blk.%d.%s", l, suffix);                        \
+    L.field = find(ts, n, nm);                                              \
+    if ((rc = check_tensor(L.field, nm, a, b, mat, err))) return rc;
+        GET(attn_norm, "attn_norm.weight", c->dim, 0, false)
+        GET(q, "attn_q.weight", c->dim, qd, true)
+        GET(k, "attn_k.weight", c->dim, kvd, true)
+        GET(v, "attn_v.weight", c->dim, kvd, true)
+        GET(o, "attn_output.weight", qd, c->dim, true)
+        GET(ffn_norm, "ffn_norm.weight", c->dim, 0, false)
+        GET(gate, "ffn_gate.weight", c->dim, c->ffn, true)
+        GET(up, "ffn_up.weight", c->dim, c->ffn, true)
+        GET(down, "ffn_down.weight", c->ffn, c->dim, true)
+#undef GET
+        snprintf(nm, sizeof nm, "blk.%d.attn_q.bias", l);
+        L.bq = find(ts, n, nm);
+        snprintf(nm, sizeof nm, "blk.%d.attn_k.bias", l);
+        L.bk = find(ts, n, nm);
+        snprintf(nm, sizeof nm, "blk.%d.attn_v.bias", l);
+        L.bv = find(ts, n, nm);
+        const int nb = (L.bq != nullptr) + (L.bk != nullptr) + (L.bv != nullptr);
+        if (nb != 0 && nb != 3) {
+            snprintf(nm, sizeof nm, "layer %d has only some of the q/k/v biases", l);
+            err = nm;
+            return LLM_ERR_MISSING;
+        }
+        if (nb) {
+            if ((rc = check_tensor(L.bq, "attn_q.bias", qd, 0, false, err))) return rc;
+            if ((rc = check_tensor(L.bk, "attn_k.bias", kvd, 0, false, err))) return rc;
+            if ((rc = check_tensor(L.bv, "attn_v.bias", kvd, 0, false, err))) return rc;
+        }
+        n_bias += nb ? 1 : 0;
+        if (L.q->dtype != L.k->dtype || L.q->dtype != L.v->dtype) {
+            snprintf(nm, sizeof nm, "layer %d: attn_q, attn_k and attn_v must share one type", l);
+            err = nm;
+            return LLM_ERR_DTYPE;
+        }
+        if (L.gate->dtype != L.up->dtype) {
+            snprintf(nm, sizeof nm, "layer %d: ffn_gate and ffn_up must share one type", l);
+            err = nm;
+            return LLM_ERR_DTYPE;
+        }
+    }
+    if (n_bias != 0 && n_bias != c->n_layers) {
+        err = "q/k/v biases must be present in every layer or in none";
+        return LLM_ERR_MISSING;
+    }
+    V.bias = n_bias > 0;
+    return LLM_OK;
+}
+
+// Everything a context places in its three arenas.
+struct Layout {
+    // weights
+    Mat embd, out;
+    const float* out_norm;
+    std::vector<LayerW> layers;
+    // kv
+    __half *kc, *vc;
+    size_t kv_layer;  // elements per layer of one cache
+    // scratch
+    State* st;
+    float2* rope;
+    float *x, *q, *ao, *u, *logits, *attn_part;
+    int *gen_out, *ptok;
+    float *X, *Hf, *QKV, *Q, *Of, *Uf;
+    __half *Hh, *Oh, *Uh;
+    int n_split;
+    size_t wbytes, kvbytes, sbytes;
+};
+
+Mat place_mat(Arena& A, int dtype, int rows, int cols) {
+    Mat m;
+    m.dtype = dtype;
+    m.rows = rows;
+    m.cols = cols;
+    m.w = A.take(mat_bytes_w(dtype, rows, cols));
+    m.s = dtype == DT_Q8 ? (const uint16_t*)A.take(mat_bytes_s(dtype, rows, cols)) : nullptr;
+    return m;
+}
+
+int decode_splits(const llm_config* c) {
+    int s = 512 / c->n_kv_heads;
+    if (s < 1) s = 1;
+    if (s > 256) s = 256;
+    return s;
+}
+
+void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, void* sb, Layout& L) {
+    const int qd = c->n_heads * c->head_dim, kvd = c->n_kv_heads * c->head_dim;
+    Arena W;
+    W.base = (char*)wb;
+    L.embd = place_mat(W, V.embd->dtype, c->vocab, c->dim);
+    L.out_norm = (const float*)W.take((size_t)c->dim * 4);
+    L.out = V.out ? place_mat(W, V.out->dtype, c->vocab, c->dim) : L.embd;
+    L.layers.resize(c->n_layers);
+    for (int l = 0; l < c->n_layers; l++) {
+        const Validated::L& S = V.layers[l];
+        LayerW& D = L.layers[l];
+        D.attn_norm = (const float*)W.take((size_t)c->dim * 4);
+        D.qkv = place_mat(W, S.q->dtype, qd + 2 * kvd, c->dim);
+        D.bqkv = V.bias ? (const float*)W.take((size_t)(qd + 2 * kvd) * 4) : nullptr;
+        D.o = place_mat(W, S.o->dtype, c->dim, qd);
+        D.ffn_norm = (const float*)W.take((size_t)c->dim * 4);
+        D.gu = place_mat(W, S.gate->dtype, 2 * c->ffn, c->dim);
+        D.down = place_mat(W, S.down->dtype, c->dim, c->ffn);
+    }
+    L.wbytes = W.off;
+
+    Arena K;
+    K.base = (char*)kb;
+    L.kv_layer = (size_t)c->n_kv_heads * c->n_ctx * c->head_dim;
+    L.kc = (__half*)K.take(L.kv_layer * c->n_layers * 2);
+    L.vc = (__half*)K.take(L.kv_layer * c->n_layers * 2);
+    L.kvbytes = K.off;
+
+    Arena S;
+    S.base = (char*)sb;
+    const int G = c->n_heads / c->n_kv_heads;
+    const int C = kPrefillChunk;
+    L.n_split = decode_splits(c);
+    L.st = (State*)S.take(sizeof(State));
+    L.rope = (float2*)S.take((size_t)c->n_ctx * (c->rope_dims / 2) * sizeof(float2));
+    L.x = (float*)S.take((size_t)c->dim * 4);
+    L.q = (float*)S.take((size_t)qd * 4);
+    L.ao = (float*)S.take((size_t)qd * 4);
+    L.u = (float*)S.take((size_t)c->ffn * 4);
+    L.logits = (float*)S.take((size_t)c->vocab * 4);
+    L.attn_part = (float*)S.take((size_t)L.n_split * c->n_kv_heads * G * (c->head_dim + 2) * 4);
+    L.gen_out = (int*)S.take((size_t)c->n_ctx * 4);
+    L.ptok = (int*)S.take((size_t)C * 4);
+    L.X = (float*)S.take((size_t)C * c->dim * 4);
+    L.Hf = (float*)S.take((size_t)C * c->dim * 4);
+    L.Hh = (__half*)S.take((size_t)C * c->dim * 2);
+    L.QKV = (float*)S.take((size_t)C * (qd + 2 * kvd) * 4);
+    L.Q = (float*)S.take((size_t)C * qd * 4);
+    L.Of = (float*)S.take((size_t)C * qd * 4);
+    L.Oh = (__half*)S.take((size_t)C * qd * 2);
+    L.Uf = (float*)S.take((size_t)C * c->ffn * 4);
+    L.Uh = (__half*)S.take((size_t)C * c->ffn * 2);
+    L.sbytes = S.off;
+}
+
+// Host-side packing of one source matrix into (part of) a device-layout matrix:
+// source row r becomes packed row row0 + r * rstride.
+void pack_rows(const llm_tensor* t, int rows, int cols, int row0, int rstride, std::vector<uint8_t>& w,
+               std::vector<uint16_t>& s) {
+    const uint8_t* src = (const uint8_t*)t->data;
+    if (t->dtype == DT_F32 || t->dtype == DT_F16) {
+        const size_t rb = (size_t)cols * (t->dtype == DT_F32 ? 4 : 2);
+        for (int r = 0; r < rows; r++) memcpy(w.data() + (size_t)(row0 + r * rstride) * rb, src + (size_t)r * rb, rb);
+    } else {
+        const int nb = cols / 32;
+        for (int r = 0; r < rows; r++) {
+            const size_t pr = (size_t)(row0 + r * rstride);
+            for (int b = 0; b < nb; b++) {
+                const uint8_t* blk = src + ((size_t)r * nb + b) * 34;
+                s[pr * nb + b] = (uint16_t)(blk[0] | (blk[1] << 8));
+                memcpy(w.data() + pr * cols + (size_t)b * 32, blk + 2, 32);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+struct llm_ctx {
+    llm_config cfg;
+    int qd, kvd, G;
+    hipStream_t stream;
+    hipStream_t cap = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t gexec = nullptr;
+    bool use_graph = true;
+    void *wbase = nullptr, *kvbase = nullptr, *sbase = nullptr;
+    bool own_w = false, own_kv = false, own_s = false;
+    Layout L;
+    int32_t len = 0;
+    bool poisoned = false;
+    std::string err;
+    int g_qkv, g_o, g_gu, g_down, g_vocab;
+};
+
+namespace {
+
+int fail(llm_ctx* c, int rc, const std::string& msg) {
+    if (c) c->err = msg;
+    return rc;
+}
+
+int dev_fail(llm_ctx* c, hipError_t e, const char* what) {
+    c->poisoned = true;
+    c->err = std::string(what) + ": " + hipGetErrorString(e);
+    return LLM_ERR_DEVICE;
+}
+
+#define HIPCHK(ctx, expr)                                   \
+    do {                                                    \
+        hipError_t e_ = (expr);                             \
+        if (e_ != hipSuccess) return dev_fail(ctx, e_, #expr); \
+    } while (0)
+
+GemvArgs base_args(llm_ctx* c) {
+    GemvArgs a;
+    memset(&a, 0, sizeof a);
+    a.eps = c->cfg.eps;
+    a.st = c->L.st;
+    a.n_heads = c->cfg.n_heads;
+    a.n_kv_heads = c->cfg.n_kv_heads;
+    a.head_dim = c->cfg.head_dim;
+    a.n_rot = c->cfg.rope_dims;
+    a.neox = c->cfg.rope_neox;
+    a.n_ctx = c->cfg.n_ctx;
+    a.rope = c->L.rope;
+    return a;
+}
+
+// Vocabulary product + argmax over residual row `xin` (decode: L.x; prefill: last row of X).
+hipError_t enqueue_logits(llm_ctx* c, const float* xin, hipStream_t s) {
+    GemvArgs a = base_args(c);
+    a.W = c->L.out;
+    a.xin = xin;
+    a.gain = c->L.out_norm;
+    a.y = c->L.logits;
+    a.gen_out = c->L.gen_out;
+    a.gen_cap = c->cfg.n_ctx;
+    hipError_t e = launch_gemv(PRO_NORM, EPI_ARGMAX, a, c->g_vocab, s);
+    if (e != hipSuccess) return e;
+    return launch_argmax_finalize(c->L.st, c->L.gen_out, c->cfg.n_ctx, s);
+}
+
+// The five stages of one layer of the decode step.
+hipError_t stage_qkv(llm_ctx* c, int l, const float* xin, bool embed, float* q, hipStream_t s) {
+    const Layout& L = c->L;
+    const LayerW& W = L.layers[l];
+    GemvArgs a = base_args(c);
+    a.W = W.qkv;
+    a.gain = W.attn_norm;
+    a.y = q;
+    a.bias = W.bqkv;
+    a.kc = L.kc + (size_t)l * L.kv_layer;
+    a.vc = L.vc + (size_t)l * L.kv_layer;
+    if (embed) {
+        a.E = L.embd;
+        a.xres = L.x;
+        return launch_gemv(PRO_EMBED, EPI_QKV, a, c->g_qkv, s);
+    }
+    a.xin = xin;
+    return launch_gemv(PRO_NORM, EPI_QKV, a, c->g_qkv, s);
+}
+
+hipError_t stage_attn(llm_ctx* c, int l, const float* q, float* out, hipStream_t s) {
+    const Layout& L = c->L;
+    const llm_config& cf = c->cfg;
+    AttnArgs t;
+    memset(&t, 0, sizeof t);
+    t.q = q;
+    t.kc = L.kc + (size_t)l * L.kv_layer;
+    t.vc = L.vc + (size_t)l * L.kv_layer;
+    t.out = out;
+    t.part = L.attn_part;
+    t.st = L.st;
+    t.n_heads = cf.n_heads;
+    t.n_kv_heads = cf.n_kv_heads;
+    t.head_dim = cf.head_dim;
+    t.n_ctx = cf.n_ctx;
+    t.n_split = L.n_split;
+    t.scale_div = (float)sqrt((double)cf.head_dim);
+    return launch_attn(t, 1, s);
+}
+
+hipError_t stage_o(llm_ctx* c, int l, const float* in, float* x, hipStream_t s) {
+    GemvArgs o = base_args(c);
+    o.W = c->L.layers[l].o;
+    o.xin = in;
+    o.y = x;
+    return launch_gemv(PRO_PLAIN, EPI_RESID, o, c->g_o, s);
+}
+
+hipError_t stage_ffn_up(llm_ctx* c, int l, const float* x, float* u, hipStream_t s) {
+    GemvArgs g = base_args(c);
+    g.W = c->L.layers[l].gu;
+    g.xin = x;
+    g.gain = c->L.layers[l].ffn_norm;
+    g.y = u;
+    return launch_gemv(PRO_NORM, EPI_SWIGLU, g, c->g_gu, s);
+}
+
+hipError_t stage_down(llm_ctx* c, int l, const float* u, float* x, hipStream_t s) {
+    GemvArgs d = base_args(c);
+    d.W = c->L.layers[l].down;
+    d.xin = u;
+    d.y = x;
+    return launch_gemv(PRO_PLAIN, EPI_RESID, d, c->g_down, s);
+}
+
+// One decode step: 5 launches per layer + the logits launch. Token and position
+// come from the device State.
+hipError_t enqueue_step(llm_ctx* c, hipStream_t s) {
+    const Layout& L = c->L;
+    hipError_t e;
+    for (int l = 0; l < c->cfg.n_layers; l++) {
+        if ((e = stage_qkv(c, l, L.x, l == 0, L.q, s)) != hipSuccess) return e;
+        if ((e = stage_attn(c, l, L.q, L.ao, s)) != hipSuccess) return e;
+        if ((e = stage_o(c, l, L.ao, L.x, s)) != hipSuccess) return e;
+        if ((e = stage_ffn_up(c, l, L.x, L.u, s)) != hipSuccess) return e;
+        if ((e = stage_down(c, l, L.u, L.x, s)) != hipSuccess) return e;
+    }
+    return enqueue_logits(c, L.x, s);
+}
+
+int run_step(llm_ctx* c) {
+    if (c->use_graph) {
+        if (!c->gexec) {
+            HIPCHK(c, hipStreamBeginCapture(c->cap, hipStreamCaptureModeRelaxed));
+            hipError_t e = enqueue_step(c, c->cap);
+            hipGraph_t g = nullptr;
+            hipError_t e2 = hipStreamEndCapture(c->cap, &g);
+            if (e != hipSuccess) return dev_fail(c, e, "enqueue_step (capture)");
+            if (e2 != hipSuccess) return dev_fail(c, e2, "hipStreamEndCapture");
+            c->graph = g;
+            HIPCHK(c, hipGraphInstantiate(&c->gexec, c->graph, nullptr, nullptr, 0));
+        }
+        HIPCHK(c, hipGraphLaunch(c->gexec, c->stream));
+    } else {
+        hipError_t e = enqueue_step(c, c->stream);
+        if (e != hipSuccess) return dev_fail(c, e, "enqueue_step");
+    }
+    return LLM_OK;
+}
+
+int finish(llm_ctx* c, float* d_logits, int32_t* h_next) {
+    if (d_logits)
+        HIPCHK(c, hipMemcpyAsync(d_logits, c->L.logits, (size_t)c->cfg.vocab * 4, hipMemcpyDeviceToDevice, c->stream));
+    if (h_next) {
+        State st;
+        HIPCHK(c, hipMemcpyAsync(&st, c->L.st, sizeof st, hipMemcpyDeviceToHost, c->stream));
+        HIPCHK(c, hipStreamSynchronize(c->stream));
+        *h_next = st.next;
+        if (st.nonfinite) return fail(c, LLM_ERR_NONFINITE, "a logit is NaN or infinite");
+    }
+    return LLM_OK;
+}
+
+int check_ctx(const llm_ctx* c) {
+    if (!c) return LLM_ERR_ARG;
+    if (c->poisoned) return LLM_ERR_DEVICE;
+    return LLM_OK;
+}
+
+void release(llm_ctx* c) {
+    if (!c) return;
+    if (c->gexec) (void)hipGraphExecDestroy(c->gexec);
+    if (c->graph) (void)hipGraphDestroy(c->graph);
+    if (c->cap) (void)hipStreamDestroy(c->cap);
+    if (c->own_w && c->wbase) (void)hipFree(c->wbase);
+    if (c->own_kv && c->kvbase) (void)hipFree(c->kvbase);
+    if (c->own_s && c->sbase) (void)hipFree(c->sbase);
+    delete c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int llm_plan(const llm_config* cfg, const llm_tensor* tensors, int32_t n, size_t* weight_bytes, size_t* kv_bytes,
+             size_t* scratch_bytes) {
+    Validated V;
+    std::string err;
+    int rc = validate(cfg, tensors, n, V, err);
+    if (rc) {
+        g_load_error = err;
+        return rc;
+    }
+    Layout L;
+    make_layout(cfg, V, nullptr, nullptr, nullptr, L);
+    if (weight_bytes) *weight_bytes = L.wbytes;
+    if (kv_bytes) *kv_bytes = L.kvbytes;
+    if (scratch_bytes) *scratch_bytes = L.sbytes;
+    return LLM_OK;
+}
+
+int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n, void* d_weights, void* d_kv,
+                     void* d_scratch, void* hip_stream, llm_ctx** out) {
+    if (!out) return LLM_ERR_ARG;
+    *out = nullptr;
+    Validated V;
+    std::string err;
+    int rc = validate(cfg, tensors, n, V, err);
+    if (rc) {
+        g_load_error = err;
+        return rc;
+    }
+    Layout M;
+    make_layout(cfg, V, nullptr, nullptr, nullptr, M);
+    llm_ctx* c = new llm_ctx();
+    c->cfg = *cfg;
+    c->qd = cfg->n_heads * cfg->head_dim;
+    c->kvd = cfg->n_kv_heads * cfg->head_dim;
+    c->G = cfg->n_heads / cfg->n_kv_heads;
+    c->stream = (hipStream_t)hip_stream;
+    const char* ng = getenv("LLM_NO_GRAPH");
+    c->use_graph = !(ng && ng[0] == '1');
+    auto bail = [&](int code, const std::string& msg) {
+        g_load_error = msg;
+        release(c);
+        return code;
+    };
+    auto alloc = [&](void* given, size_t bytes, void** dst, bool* own) -> bool {
+        if (given) {
+            if ((uintptr_t)given & 255) return false;
+            *dst = given;
+            return true;
+        }
+        if (hipMalloc(dst, bytes ? bytes : 256) != hipSuccess) {
+            *dst = nullptr;
+            return false;
+        }
+        *own = true;
+        return true;
+    };
+    if (!alloc(d_weights, M.wbytes, &c->wbase, &c->own_w) || !alloc(d_kv, M.kvbytes, &c->kvbase, &c->own_kv) ||
+        !alloc(d_scratch, M.sbytes, &c->sbase, &c->own_s))
+        return bail(LLM_ERR_OOM, "device arena allocation failed (or a given arena is not 256-byte aligned)");
+    make_layout(cfg, V, c->wbase, c->kvbase, c->sbase, c->L);
+    Layout& L = c->L;
+    hipStream_t s = c->stream;
+    const int qd = c->qd, kvd = c->kvd;
+
+    // ---- pack and upload the weights
+    auto upload = [&](const void* dst, const void* src, size_t bytes) -> bool {
+        return hipMemcpyAsync((void*)dst, src, bytes, hipMemcpyHostToDevice, s) == hipSuccess &&
+               hipStreamSynchronize(s) == hipSuccess;
+    };
+    auto upload_mat = [&](const Mat& m, std::initializer_list<const llm_tensor*> parts, int mode) -> bool {
+        // mode 0: one tensor; 1: row concatenation; 2: row interleave
+        std::vector<uint8_t> w(mat_bytes_w(m.dtype, m.rows, m.cols));
+        std::vector<uint16_t> sc(m.dtype == DT_Q8 ? (size_t)m.rows * (m.cols / 32) : 0);
+        int row0 = 0, idx = 0;
+        const int np = (int)parts.size();
+        for (const llm_tensor* t : parts) {
+            const int rows = (int)t->ne[1];
+            if (mode == 2)
+                pack_rows(t, rows, m.cols, idx, np, w, sc);
+            else
+                pack_rows(t, rows, m.cols, row0, 1, w, sc);
+            row0 += rows;
+            idx++;
+        }
+        if (!upload(m.w, w.data(), w.size())) return false;
+        if (m.dtype == DT_Q8 && !upload(m.s, sc.data(), sc.size() * 2)) return false;
+        return true;
+    };
+    bool ok = upload_mat(L.embd, {V.embd}, 0) && upload(L.out_norm, V.out_norm->data, (size_t)cfg->dim * 4);
+    if (ok && V.out) ok = upload_mat(L.out, {V.out}, 0);
+    for (int l = 0; ok && l < cfg->n_layers; l++) {
+        const Validated::L& S = V.layers[l];
+        LayerW& D = L.layers[l];
+        ok = upload(D.attn_norm, S.attn_norm->data, (size_t)cfg->dim * 4) && upload_mat(D.qkv, {S.q, S.k, S.v}, 1) &&
+             upload(D.ffn_norm, S.ffn_norm->data, (size_t)cfg->dim * 4) && upload_mat(D.o, {S.o}, 0) &&
+             upload_mat(D.gu, {S.gate, S.up}, 2) && upload_mat(D.down, {S.down}, 0);
+        if (ok && V.bias) {
+            std::vector<float> b((size_t)qd + 2 * kvd);
+            memcpy(b.data(), S.bq->data, (size_t)qd * 4);
+            memcpy(b.data() + qd, S.bk->data, (size_t)kvd * 4);
+            memcpy(b.data() + qd + kvd, S.bv->data, (size_t)kvd * 4);
+            ok = upload(D.bqkv, b.data(), b.size() * 4);
+        }
+    }
+    if (!ok) return bail(LLM_ERR_DEVICE, "weight upload failed");
+
+    // ---- RoPE table and zeroed state
+    const float theta_scale = (float)pow((double)cfg->rope_base, -2.0 / cfg->rope_dims);
+    if (launch_rope_table(L.rope, cfg->n_ctx, cfg->rope_dims, theta_scale, s) != hipSuccess ||
+        hipMemsetAsync(L.st, 0, sizeof(State), s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return bail(LLM_ERR_DEVICE, "initialisation kernels failed");
+
+    c->g_qkv = gemv_grid(PRO_NORM, EPI_QKV, qd + 2 * kvd);
+    c->g_o = gemv_grid(PRO_PLAIN, EPI_RESID, cfg->dim);
+    c->g_gu = gemv_grid(PRO_NORM, EPI_SWIGLU, 2 * cfg->ffn);
+    c->g_down = gemv_grid(PRO_PLAIN, EPI_RESID, cfg->dim);
+    c->g_vocab = gemv_grid(PRO_NORM, EPI_ARGMAX, cfg->vocab);
+
+    if (c->use_graph && hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking) != hipSuccess)
+        return bail(LLM_ERR_DEVICE, "stream creation failed");
+    // One direct step (token 0 at position 0) sets the kernels' launch attributes
+    // before any capture; it only writes cache row 0, which is invalid while len = 0.
+    if (launch_set_state(L.st, 0, 0, 0, s) != hipSuccess || enqueue_step(c, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return bail(LLM_ERR_DEVICE, std::string("first step failed: ") + hipGetErrorString(hipGetLastError()));
+    c->len = 0;
+    *out = c;
+    return LLM_OK;
+}
+
+int llm_decode(llm_ctx* c, int32_t token, int32_t pos, float* d_logits, int32_t* h_next) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    if (token < 0 || token >= c->cfg.vocab) return fail(c, LLM_ERR_TOKEN, "token out of range");
+    if (pos < 0 || pos > c->len || pos >= c->cfg.n_ctx) return fail(c, LLM_ERR_POS, "position out of range");
+    HIPCHK(c, launch_set_state(c->L.st, token, pos, 0, c->stream));
+    if ((rc = run_step(c))) return rc;
+    c->len = pos + 1;
+    return finish(c, d_logits, h_next);
+}
+
+int llm_generate(llm_ctx* c, int32_t token, int32_t n_steps, int32_t* h_tokens) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    if (n_steps <= 0 || !h_tokens) return fail(c, LLM_ERR_ARG, "n_steps must be positive and h_tokens set");
+    if (token < 0 || token >= c->cfg.vocab) return fail(c, LLM_ERR_TOKEN, "token out of range");
+    if ((int64_t)c->len + n_steps > c->cfg.n_ctx) return fail(c, LLM_ERR_CTX_FULL, "generation would pass n_ctx");
+    HIPCHK(c, launch_set_state(c->L.st, token, c->len, 1, c->stream));
+    for (int i = 0; i < n_steps; i++)
+        if ((rc = run_step(c))) return rc;
+    HIPCHK(c, hipMemcpyAsync(h_tokens, c->L.gen_out, (size_t)n_steps * 4, hipMemcpyDeviceToHost, c->stream));
+    State st;
+    HIPCHK(c, hipMemcpyAsync(&st, c->L.st, sizeof st, hipMemcpyDeviceToHost, c->stream));
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    c->len += n_steps;
+    if (st.nonfinite) return fail(c, LLM_ERR_NONFINITE, "a logit is NaN or infinite");
+    return LLM_OK;
+}
+
+int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits, int32_t* h_next) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    if (n <= 0 || !h_tokens) return fail(c, LLM_ERR_ARG, "n must be positive and h_tokens set");
+    for (int i = 0; i < n; i++)
+        if (h_tokens[i] < 0 || h_tokens[i] >= c->cfg.vocab) return fail(c, LLM_ERR_TOKEN, "token out of range");
+    if ((int64_t)c->len + n > c->cfg.n_ctx) return fail(c, LLM_ERR_CTX_FULL, "prefill would pass n_ctx");
+    const llm_config& cf = c->cfg;
+    Layout& L = c->L;
+    hipStream_t s = c->stream;
+    const int qd = c->qd, kvd = c->kvd, qkvd = qd + 2 * kvd;
+    int last = 0;
+    for (int done = 0; done < n; done += kPrefillChunk) {
+        const int m = (n - done) < kPrefillChunk ? (n - done) : kPrefillChunk;
+        const int p0 = c->len;
+        HIPCHK(c, hipMemcpyAsync(L.ptok, h_tokens + done, (size_t)m * 4, hipMemcpyHostToDevice, s));
+        HIPCHK(c, launch_embed_rows(L.embd, L.ptok, m, L.X, cf.dim, s));
+        for (int l = 0; l < cf.n_layers; l++) {
+            const LayerW& W = L.layers[l];
+            __half* kc = L.kc + (size_t)l * L.kv_layer;
+            __half* vc = L.vc + (size_t)l * L.kv_layer;
+            const bool f32_qkv = W.qkv.dtype == DT_F32, f32_o = W.o.dtype == DT_F32;
+            const bool f32_gu = W.gu.dtype == DT_F32, f32_dn = W.down.dtype == DT_F32;
+            HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, f32_qkv ? L.Hf : nullptr,
+                                          f32_qkv ? nullptr : L.Hh, s));
+            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, L.Hh, L.Hf, m, L.QKV, qkvd, nullptr, 0, W.bqkv, s));
+            HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
+                                          cf.rope_neox, cf.n_ctx, L.rope, L.Q, kc, vc, s));
+            AttnArgs t;
+            memset(&t, 0, sizeof t);
+            t.q = L.Q;
+            t.kc = kc;
+            t.vc = vc;
+            t.out = L.Of;
+            t.out_h = f32_o ? nullptr : L.Oh;
+            t.part = L.attn_part;
+                    t.st = nullptr;
+            t.p0 = p0;
+            t.n_heads = cf.n_heads;
+            t.n_kv_heads = cf.n_kv_heads;
+            t.head_dim = cf.head_dim;
+            t.n_ctx = cf.n_ctx;
+            t.n_split = 1;
+            t.scale_div = (float)sqrt((double)cf.head_dim);
+            HIPCHK(c, launch_attn(t, m, s));
+            HIPCHK(c, launch_gemm(EPI_RESID, W.o, L.Oh, L.Of, m, L.X, cf.dim, nullptr, 0, nullptr, s));
+            HIPCHK(c, launch_rmsnorm_rows(L.X, W.ffn_norm, m, cf.dim, cf.eps, f32_gu ? L.Hf : nullptr,
+                                          f32_gu ? nullptr : L.Hh, s));
+            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, L.Hh, L.Hf, m, f32_dn ? L.Uf : nullptr, cf.ffn,
+                                  f32_dn ? nullptr : L.Uh, cf.ffn, nullptr, s));
+            HIPCHK(c, launch_gemm(EPI_RESID, W.down, L.Uh, L.Uf, m, L.X, cf.dim, nullptr, 0, nullptr, s));
+        }
+        c->len += m;
+        last = m;
+    }
+    HIPCHK(c, launch_set_state(L.st, 0, c->len - 1, 0, s));
+    HIPCHK(c, enqueue_logits(c, L.X + (size_t)(last - 1) * cf.dim, s));
+    return finish(c, d_logits, h_next);
+}
+
+int llm_reset(llm_ctx* c) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    c->len = 0;
+    return LLM_OK;
+}
+
+void llm_free(llm_ctx* c) {
+    if (!c) return;
+    if (c->stream) (void)hipStreamSynchronize(c->stream);
+    else (void)hipDeviceSynchronize();
+    release(c);
+}
+
+const char* llm_last_error(const llm_ctx* c) { return c ? c->err.c_str() : g_load_error.c_str(); }
+
+const float* llm_logits(const llm_ctx* c) { return c ? c->L.logits : nullptr; }
+
+int32_t llm_kv_len(const llm_ctx* c) { return c ? c->len : -1; }
+
+int llm_kv_read(const llm_ctx* cc, int32_t layer, int32_t pos, uint16_t* h_k, uint16_t* h_v) {
+    llm_ctx* c = (llm_ctx*)cc;
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    if (layer < 0 || layer >= c->cfg.n_layers || pos < 0 || pos >= c->cfg.n_ctx || !h_k || !h_v)
+        return fail(c, LLM_ERR_ARG, "kv_read: layer/pos out of range or null output");
+    const Layout& L = c->L;
+    const size_t hd = c->cfg.head_dim;
+    const size_t pitch = (size_t)c->cfg.n_ctx * hd * 2;
+    const char* kb = (const char*)(L.kc + (size_t)layer * L.kv_layer + (size_t)pos * hd);
+    const char* vb = (const char*)(L.vc + (size_t)layer * L.kv_layer + (size_t)pos * hd);
+    HIPCHK(c, hipMemcpy2DAsync(h_k, hd * 2, kb, pitch, hd * 2, c->cfg.n_kv_heads, hipMemcpyDeviceToHost, c->stream));
+    HIPCHK(c, hipMemcpy2DAsync(h_v, hd * 2, vb, pitch, hd * 2, c->cfg.n_kv_heads, hipMemcpyDeviceToHost, c->stream));
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    return LLM_OK;
+}
+
+// ------------------------------------------------------------------ llm_ops.h
+namespace {
+int check_layer(llm_ctx* c, int32_t layer) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, LLM_ERR_ARG, "layer out of range");
+    return LLM_OK;
+}
+}  // namespace
+
+int llm_op_qkv(llm_ctx* c, int32_t layer, int32_t pos, const float* d_x, float* d_q) {
+    int rc = check_layer(c, layer);
+    if (rc) return rc;
+    if (pos < 0 || pos >= c->cfg.n_ctx || !d_x || !d_q) return fail(c, LLM_ERR_ARG, "bad position or pointer");
+    HIPCHK(c, launch_set_state(c->L.st, 0, pos, 0, c->stream));
+    HIPCHK(c, stage_qkv(c, layer, d_x, false, d_q, c->stream));
+    return LLM_OK;
+}
+
+int llm_op_attention(llm_ctx* c, int32_t layer, int32_t pos, const float* d_q, float* d_out) {
+    int rc = check_layer(c, layer);
+    if (rc) return rc;
+    if (pos < 0 || pos >= c->cfg.n_ctx || !d_q || !d_out) return fail(c, LLM_ERR_ARG, "bad position or pointer");
+    HIPCHK(c, launch_set_state(c->L.st, 0, pos, 0, c->stream));
+    HIPCHK(c, stage_attn(c, layer, d_q, d_out, c->stream));
+    return LLM_OK;
+}
+
+int llm_op_o(llm_ctx* c, int32_t layer, const float* d_in, float* d_x) {
+    int rc = check_layer(c, layer);
+    if (rc) return rc;
+    if (!d_in || !d_x) return fail(c, LLM_ERR_ARG, "null pointer");
+    HIPCHK(c, stage_o(c, layer, d_in, d_x, c->stream));
+    return LLM_OK;
+}
+
+int llm_op_ffn_up(llm_ctx* c, int32_t layer, const float* d_x, float* d_u) {
+    int rc = check_layer(c, layer);
+    if (rc) return rc;
+    if (!d_x || !d_u) return fail(c, LLM_ERR_ARG, "null pointer");
+    HIPCHK(c, stage_ffn_up(c, layer, d_x, d_u, c->stream));
+    return LLM_OK;
+}
+
+int llm_op_down(llm_ctx* c, int32_t layer, const float* d_u, float* d_x) {
+    int rc = check_layer(c, layer);
+    if (rc) return rc;
+    if (!d_u || !d_x) return fail(c, LLM_ERR_ARG, "null pointer");
+    HIPCHK(c, stage_down(c, layer, d_u, d_x, c->stream));
+    return LLM_OK;
+}
+
+int llm_op_logits(llm_ctx* c, const float* d_x, float* d_logits, int32_t* h_next) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    if (!d_x) return fail(c, LLM_ERR_ARG, "null pointer");
+    HIPCHK(c, launch_set_state(c->L.st, 0, 0, 0, c->stream));
+    HIPCHK(c, enqueue_logits(c, d_x, c->stream));
+    return finish(c, d_logits, h_next);
+}
+
+int llm_op_kv_write(llm_ctx* c, int32_t layer, int32_t pos0, int32_t n_pos, const uint16_t* h_k, const uint16_t* h_v) {
+    int rc = check_layer(c, layer);
+    if (rc) return rc;
+    if (pos0 < 0 || n_pos < 0 || (int64_t)pos0 + n_pos > c->cfg.n_ctx || !h_k || !h_v)
+        return fail(c, LLM_ERR_ARG, "rows out of range or null pointer");
+    if (n_pos == 0) return LLM_OK;
+    const Layout& L = c->L;
+    const size_t hd = c->cfg.head_dim, kvd = (size_t)c->kvd;
+    // the pages' [pos][kv_head*head_dim] rows become head-major [kv_head][pos][head_dim]
+    for (int g = 0; g < c->cfg.n_kv_heads; g++) {
+        char* kd = (char*)(L.kc + (size_t)layer * L.kv_layer + ((size_t)g * c->cfg.n_ctx + pos0) * hd);
+        char* vd = (char*)(L.vc + (size_t)layer * L.kv_layer + ((size_t)g * c->cfg.n_ctx + pos0) * hd);
+        HIPCHK(c, hipMemcpy2DAsync(kd, hd * 2, h_k + g * hd, kvd * 2, hd * 2, n_pos, hipMemcpyHostToDevice, c->stream));
+        HIPCHK(c, hipMemcpy2DAsync(vd, hd * 2, h_v + g * hd, kvd * 2, hd * 2, n_pos, hipMemcpyHostToDevice, c->stream));
+    }
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    return LLM_OK;
+}
+
+int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n_launch, float* h_ms) {
+    int rc = check_layer(c, layer);
+    if (rc) return rc;
+    if (stage < LLM_STAGE_QKV || stage > LLM_STAGE_LOGITS || n_launch <= 0 || !h_ms || pos < 0 || pos >= c->cfg.n_ctx)
+        return fail(c, LLM_ERR_ARG, "bad stage, position, count or pointer");
+    const Layout& L = c->L;
+    hipStream_t s = c->stream;
+    HIPCHK(c, launch_set_state(L.st, 0, pos, 0, s));
+    auto one = [&]() -> hipError_t {
+        switch (stage) {
+            case LLM_STAGE_QKV: return stage_qkv(c, layer, L.x, false, L.q, s);
+            case LLM_STAGE_ATTN: return stage_attn(c, layer, L.q, L.ao, s);
+            case LLM_STAGE_O: return stage_o(c, layer, L.ao, L.x, s);
+            case LLM_STAGE_FFN_UP: return stage_ffn_up(c, layer, L.x, L.u, s);
+            case LLM_STAGE_DOWN: return stage_down(c, layer, L.u, L.x, s);
+            default: return enqueue_logits(c, L.x, s);
+        }
+    };
+    HIPCHK(c, one());  // warm
+    hipEvent_t e0, e1;
+    HIPCHK(c, hipEventCreate(&e0));
+    HIPCHK(c, hipEventCreate(&e1));
+    hipError_t e = hipEventRecord(e0, s);
+    for (int i = 0; e == hipSuccess && i < n_launch; i++) e = one();
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (e != hipSuccess) return dev_fail(c, e, "llm_op_time");
+    *h_ms = ms / (float)n_launch;
+    return LLM_OK;
+}
+
+int llm_rewind(llm_ctx* c, int32_t len) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    if (len < 0 || len > c->len) return fail(c, LLM_ERR_POS, "rewind length beyond kv_len");
+    c->len = len;
+    return LLM_OK;
+}
+
+}  // extern "C"
