@@ -26,6 +26,7 @@ extern "C" {
 #define LLM_STAGE_FFN_UP 3 /* RMSNorm + gate/up products + SwiGLU */
 #define LLM_STAGE_DOWN 4   /* down product + residual add */
 #define LLM_STAGE_LOGITS 5 /* final RMSNorm + vocabulary product + greedy argmax */
+#define LLM_STAGE_STEP 6   /* one whole decode step (token 0 at position pos) */
 
 /* QKV stage of `layer` at position pos (0 <= pos < n_ctx): h = rmsnorm(d_x)
  * * attn_norm ("The Forward Pass in Java", Example 4), q|k|v = W h (+ bias),
@@ -65,8 +66,18 @@ int llm_op_kv_write(llm_ctx* ctx, int32_t layer, int32_t pos0, int32_t n_pos, co
  * of `layer`, over n_launch back-to-back launches bracketed by HIP events on
  * the context's stream, with the context's own scratch buffers as inputs
  * (their contents do not affect the time). The attention stage runs at
- * position pos. Waits. */
+ * position pos. LLM_STAGE_STEP times a whole decode step at position pos
+ * (with layer ignored); it writes cache row pos of every layer. Waits. */
 int llm_op_time(llm_ctx* ctx, int32_t stage, int32_t layer, int32_t pos, int32_t n_launch, float* h_ms);
+
+/* Wall-clock stamps (100 MHz device clock) that block 0 of the last decode-step
+ * launch took at its start and after each of its 5*n_layers + 1 grid barriers:
+ * stamp k+1 - stamp k is the time of phase k (per layer: QKV, attention,
+ * split merge + output, gate/up, down; then the logits). h_out receives
+ * 5*n_layers + 2 values. Available only when the context was loaded with the
+ * environment variable LLM_STEP_TRACE=1 and runs the persistent step kernel;
+ * otherwise LLM_ERR_ARG. Waits. */
+int llm_op_step_trace(llm_ctx* ctx, uint64_t* h_out, int32_t n);
 
 /* Moves the sequence end back: kv_len = len, for 0 <= len <= kv_len ("The
  * Forward Pass in Java", Example 13: rewritten cache entries give the same

@@ -29,7 +29,7 @@ ERRORS = {
 }
 EXPORTS = ["llm_plan", "llm_load_weights", "llm_decode", "llm_prefill", "llm_generate", "llm_reset", "llm_free",
            "llm_last_error", "llm_logits", "llm_kv_len", "llm_kv_read", "llm_op_qkv", "llm_op_attention", "llm_op_o",
-           "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind"]
+           "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind", "llm_op_step_trace"]
 STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_FFN_UP, STAGE_DOWN, STAGE_LOGITS = range(6)
 
 
@@ -93,6 +93,8 @@ def lib():
         L.llm_op_kv_write.argtypes = [vp, i32, i32, i32, vp, vp]
         L.llm_op_time.argtypes = [vp, i32, i32, i32, i32, P(ctypes.c_float)]
         L.llm_rewind.argtypes = [vp, i32]
+        L.llm_op_step_trace.argtypes = [vp, vp, i32]
+        L.llm_op_step_trace.restype = ctypes.c_int
         for f in ("llm_op_qkv", "llm_op_attention", "llm_op_o", "llm_op_ffn_up", "llm_op_down", "llm_op_logits",
                   "llm_op_kv_write", "llm_op_time", "llm_rewind"):
             getattr(L, f).restype = ctypes.c_int
@@ -240,6 +242,12 @@ def llm_op_time(ctx, stage: int, layer: int = 0, pos: int = 0, n_launch: int = 2
     ms = ctypes.c_float()
     _check(lib().llm_op_time(ctx, stage, layer, pos, n_launch, ctypes.byref(ms)), ctx)
     return float(ms.value)
+
+
+def llm_op_step_trace(ctx, n_layers: int) -> np.ndarray:
+    out = np.zeros(5 * n_layers + 2, np.uint64)
+    _check(lib().llm_op_step_trace(ctx, out.ctypes.data, out.size), ctx)
+    return out
 
 
 def llm_rewind(ctx, length: int):

@@ -29,10 +29,12 @@ struct State {
     int nonfinite;
     int gen_mode;   // 1: the argmax also advances token/pos and appends to gen_out
     int gen_count;
+    int epoch;      // launches of the persistent step kernel so far
+    int abort;      // set when a grid barrier wait exceeded its spin limit
     unsigned long long best;  // argmax key of the running step (0 = none yet)
 };
 
-// Per-block partial of the vocabulary argmax (pass 1).
+// Per-block partial of the vocabulary argmax: (max, first index, non-finite seen).
 struct ArgPart {
     float val;
     int idx;
@@ -40,12 +42,57 @@ struct ArgPart {
     int pad;
 };
 
+// One layer's weights in device layout.
+struct LayerW {
+    const float* attn_norm;
+    Mat qkv;            // rows: q | k | v
+    const float* bqkv;  // q | k | v bias or nullptr
+    Mat o;
+    const float* ffn_norm;
+    Mat gu;             // rows interleaved: gate j at 2j, up j at 2j+1
+    Mat down;
+};
+
+// Arguments of the persistent decode-step kernel. Every activation buffer is
+// versioned (one copy per layer, or per residual update), so within a launch
+// each address is written once, before any block reads it.
+struct StepArgs {
+    const LayerW* layers;  // device array of n_layers descriptors
+    int n_layers;
+    Mat embd, out;
+    const float* out_norm;
+    __half* kc;
+    __half* vc;
+    long long kv_layer;  // elements of one layer of one cache
+    const float2* rope;
+    State* st;
+    unsigned long long* bar;  // [kBarGroups] group counters then the global one, 256 bytes apart
+    float* xv;      // residual versions [2 n_layers + 1][xstride]
+    float* qkv;     // q | k | v after bias and RoPE, per layer [n_layers][qkv_stride]
+    float* ao;      // attention output per layer [n_layers][ao_stride]
+    float* part;    // attention split partials per layer [n_layers][part_stride]
+    float* u;       // SwiGLU output per layer [n_layers][u_stride]
+    float* logits;  // [vocab]
+    int* gen_out;
+    int gen_cap;
+    long long xstride, qkv_stride, ao_stride, part_stride, u_stride;
+    unsigned long long* trace;  // nullptr, or wall-clock stamps of block 0 after each barrier
+    int dim, n_heads, n_kv_heads, head_dim, n_rot, neox, n_ctx, ffn, vocab, n_split;
+    float eps, scale_div;
+};
+
+constexpr int kStepMaxSplit = 16;  // attention splits of the persistent step kernel
+constexpr int kStepPhases = 5;     // grid barriers per layer of the persistent step kernel
+constexpr int kBarGroup = 16;    // blocks per first-level barrier counter
+constexpr int kBarGroups = 64;   // capacity of first-level counters (grid <= 1024)
+constexpr int kBarStride = 32;   // u64 elements between counters (256 bytes)
+
 constexpr int kBlock = 256;  // threads per block for all decode kernels (4 wave64)
 constexpr int kWaves = kBlock / 64;
 constexpr int kMaxCols = 16384;
 constexpr int kMaxHeadDim = 256;
 constexpr int kMaxGroup = 8;  // n_heads / n_kv_heads must be 1, 2, 4 or 8
-constexpr int kAttnChunk = 512;     // positions per online-softmax chunk inside an attention block
+constexpr int kMaxSplit = 256;      // position splits of the decode attention
 constexpr int kPrefillChunk = 512;  // tokens per prefill batch
 
 // Prologue of a vector product: where the input vector comes from.
@@ -104,6 +151,10 @@ int gemv_grid(int pro, int epi, int rows);
 hipError_t launch_attn(const AttnArgs& a, int n_q, hipStream_t s);
 hipError_t launch_set_state(State* st, int token, int pos, int gen_mode, hipStream_t s);
 hipError_t launch_argmax_finalize(State* st, int* gen_out, int gen_cap, hipStream_t s);
+// Persistent step kernel: blocks that can be co-resident (0 if it cannot run)
+// and the launch of one step.
+int step_grid(const StepArgs& a, int* lds_bytes);
+hipError_t launch_step(const StepArgs& a, int grid, int lds_bytes, hipStream_t s);
 
 struct PrefillBufs;
 hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s);

@@ -16,91 +16,9 @@
 // are bank-conflict free) and Q8_0 quants are dequantised in registers. All
 // reductions are in a fixed order (no float atomics), so results are
 // deterministic run to run.
-#include "common.h"
-
-#include <math.h>
+#include "device_common.h"
 
 namespace llm {
-
-// (x0, x1) rotated by the angle whose (cos, sin) is cs, each product rounded
-// separately as the pages' RoPE computes it (no fused multiply-add).
-__device__ __forceinline__ float2 rope_rotate(float x0, float x1, float2 cs) {
-#pragma clang fp contract(off)
-    return make_float2(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x);
-}
-
-// ------------------------------------------------------------------ helpers
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-__device__ __forceinline__ float h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
-
-// Elements per 16-byte chunk of a weight row.
-template <int DT>
-struct VecW {
-    static constexpr int VE = DT == DT_F32 ? 4 : (DT == DT_F16 ? 8 : 16);
-    static constexpr int SEG = VE * 64;  // elements read by one wave-wide 16-byte load
-};
-
-// Position of input element e in the LDS copy. Lane l's chunk c = 64*seg + l
-// covers elements VE*c .. VE*c+VE-1; those are stored as VE/4 float4 pieces at
-// seg*SEG + k*256 + 4*l, so each of the lane's ds_read_b128 hits consecutive
-// 16-byte slots across the wave.
-template <int DT>
-__device__ __forceinline__ int swz(int e) {
-    if constexpr (DT == DT_F32) {
-        return e;
-    } else {
-        constexpr int VE = VecW<DT>::VE, SEG = VecW<DT>::SEG;
-        int seg = e / SEG, w = e % SEG;
-        int l = w / VE, k = (w % VE) >> 2, m = w & 3;
-        return seg * SEG + k * 256 + 4 * l + m;
-    }
-}
-
-template <int DT>
-__host__ __device__ constexpr int lds_floats(int K) {
-    return ((K + VecW<DT>::SEG - 1) / VecW<DT>::SEG) * VecW<DT>::SEG;
-}
-
-// Element i of row `row` of an F32/F16/Q8_0 matrix, as float (embedding gather).
-__device__ __forceinline__ float mat_elem(const Mat& M, int64_t row, int i) {
-    if (M.dtype == DT_F32) return ((const float*)M.w)[row * M.cols + i];
-    if (M.dtype == DT_F16) return h2f(((const uint16_t*)M.w)[row * M.cols + i]);
-    const int8_t* q = (const int8_t*)M.w;
-    float d = h2f(M.s[row * (M.cols / 32) + i / 32]);
-    return d * (float)q[row * M.cols + i];
-}
-
-// Block-wide sum of doubles, fixed order; every thread gets the result.
-__device__ __forceinline__ double block_sum_d(double v, double* red) {
-    v = wave_sum_d(v);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; w++) t += red[w];
-    return t;
-}
 
 // Stage the product's input vector in LDS (swizzled for weight type DT).
 //   PRO_PLAIN: x = xin.   PRO_NORM: x = rmsnorm(xin) * gain.
@@ -137,76 +55,10 @@ __device__ void stage_input(const GemvArgs& a, float* xs, double* red) {
     __syncthreads();
 }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Raw 16-byte chunk c of row r, loaded with the non-temporal hint (weights are
-// streamed once per token).
-template <int DT>
-__device__ __forceinline__ u32x4 load_chunk(const Mat& W, int r, int c) {
-    const char* base;
-    if constexpr (DT == DT_F32)
-        base = (const char*)W.w + ((size_t)r * W.cols) * 4;
-    else if constexpr (DT == DT_F16)
-        base = (const char*)W.w + ((size_t)r * W.cols) * 2;
-    else
-        base = (const char*)W.w + (size_t)r * W.cols;
-    return __builtin_nontemporal_load((const u32x4*)base + c);
-}
-
-// Partial dot of one chunk with the staged input.
-template <int DT>
-__device__ __forceinline__ float chunk_dot(u32x4 raw, const float* xs, int c) {
-    const int lane = c & 63, seg = c >> 6;
-    if constexpr (DT == DT_F32) {
-        const float4 x = *(const float4*)(xs + 4 * c);
-        float s = __uint_as_float(raw.x) * x.x;
-        s += __uint_as_float(raw.y) * x.y;
-        s += __uint_as_float(raw.z) * x.z;
-        s += __uint_as_float(raw.w) * x.w;
-        return s;
-    } else if constexpr (DT == DT_F16) {
-        const float* b = xs + seg * 512 + 4 * lane;
-        const float4 x0 = *(const float4*)(b);
-        const float4 x1 = *(const float4*)(b + 256);
-        const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
-        float w[8];
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            w[2 * k] = h2f((uint16_t)(u[k] & 0xffffu));
-            w[2 * k + 1] = h2f((uint16_t)(u[k] >> 16));
-        }
-        float s = w[0] * x0.x;
-        s += w[1] * x0.y;
-        s += w[2] * x0.z;
-        s += w[3] * x0.w;
-        s += w[4] * x1.x;
-        s += w[5] * x1.y;
-        s += w[6] * x1.z;
-        s += w[7] * x1.w;
-        return s;
-    } else {
-        const float* b = xs + seg * 1024 + 4 * lane;
-        const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const float4 x = *(const float4*)(b + 256 * k);
-            const int w = (int)u[k];
-            const float q0 = (float)((w << 24) >> 24), q1 = (float)((w << 16) >> 24);
-            const float q2 = (float)((w << 8) >> 24), q3 = (float)(w >> 24);
-            s0 += q0 * x.x;
-            s1 += q1 * x.y;
-            s0 += q2 * x.z;
-            s1 += q3 * x.w;
-        }
-        return s0 + s1;
-    }
-}
-
 // Rows per wave for each epilogue.
 template <int EPI>
 struct RowsPer {
-    static constexpr int NR = (EPI == EPI_QKV || EPI == EPI_RESID) ? 2 : 4;
+    static constexpr int NR = (EPI == EPI_QKV || EPI == EPI_RESID) ? LLM_GEMV_NR_SMALL : LLM_GEMV_NR_BIG;
 };
 
 template <int EPI>
@@ -245,18 +97,6 @@ __device__ __forceinline__ void group_rows(const GemvArgs& a, int g, int* rows) 
     }
 }
 
-// Order-preserving 64-bit key of (value, index): a larger value wins, and for
-// equal values the smaller index wins, so the maximum key is the first index of
-// the strict maximum ("The Forward Pass in Java", Example 9). -0 is taken as +0.
-__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
-    const uint32_t b = __float_as_uint(v + 0.0f);
-    const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return ((unsigned long long)o << 32) | (unsigned long long)(0xffffffffu - (uint32_t)idx);
-}
-
-// fp32 -> binary16 with round to nearest even (the hardware conversion).
-__device__ __forceinline__ __half f2h(float v) { return __float2half_rn(v); }
-
 template <int DT, int PRO, int EPI>
 __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
     extern __shared__ float xs[];
@@ -264,39 +104,42 @@ __global__ __launch_bounds__(kBlock) void k_gemv(GemvArgs a) {
     __shared__ ArgPart wbest[kWaves];
     constexpr int NR = RowsPer<EPI>::NR;
     constexpr int VE = VecW<DT>::VE;
-    constexpr int U = (DT == DT_F32) ? 4 : 2;  // chunks per lane loaded before use
-
-    stage_input<DT, PRO>(a, xs, red);
+    // chunks per lane whose loads are in flight together (a Q8_0 row of 8192 is 8)
+    constexpr int U = (DT == DT_Q8 && NR == LLM_GEMV_NR_SMALL) ? LLM_GEMV_U_Q8 : LLM_GEMV_U;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int K = a.W.cols, R = a.W.rows;
     const int nch = K / VE;
     const int ng = n_groups<EPI>(a);
+    const int g0 = blockIdx.x * kWaves + wave;
     float best = -INFINITY;
     int best_i = 0x7fffffff, nonfinite = 0;
 
-    for (int g = blockIdx.x * kWaves + wave; g < ng; g += gridDim.x * kWaves) {
-        int rows[NR];
-        group_rows<EPI>(a, g, rows);
-        int lrow[NR];
+    u32x4 raw[U][NR];
+    float sc[U][NR];
+    int rows[NR], lrow[NR];
+    // Rows and first batch of weight loads of this wave's first group, issued
+    // before the input vector is staged: weights do not depend on it.
+    if (g0 < ng) {
+        group_rows<EPI>(a, g0, rows);
 #pragma unroll
         for (int i = 0; i < NR; i++) lrow[i] = rows[i] < R ? rows[i] : R - 1;
+        load_batch<DT, NR, U>(a.W, lrow, lane, nch, raw, sc);
+    }
+
+    stage_input<DT, PRO>(a, xs, red);
+
+    for (int g = g0; g < ng; g += gridDim.x * kWaves) {
+        if (g != g0) {
+            group_rows<EPI>(a, g, rows);
+#pragma unroll
+            for (int i = 0; i < NR; i++) lrow[i] = rows[i] < R ? rows[i] : R - 1;
+        }
         float acc[NR];
 #pragma unroll
         for (int i = 0; i < NR; i++) acc[i] = 0.f;
         for (int c0 = lane; c0 < nch; c0 += 64 * U) {
-            u32x4 raw[U][NR];
-            float sc[U][NR];
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int c = c0 + 64 * u;
-                const int cc = c < nch ? c : c0;
-#pragma unroll
-                for (int i = 0; i < NR; i++) {
-                    raw[u][i] = load_chunk<DT>(a.W, lrow[i], cc);
-                    if constexpr (DT == DT_Q8) sc[u][i] = h2f(a.W.s[(size_t)lrow[i] * (K / 32) + cc / 2]);
-                }
-            }
+            if (g != g0 || c0 != lane) load_batch<DT, NR, U>(a.W, lrow, c0, nch, raw, sc);
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int c = c0 + 64 * u;
@@ -429,10 +272,10 @@ static hipError_t launch_dt(const GemvArgs& a, int grid, hipStream_t s) {
 
 int gemv_grid(int pro, int epi, int rows) {
     (void)pro;
-    const int nr = (epi == EPI_QKV || epi == EPI_RESID) ? 2 : 4;
+    const int nr = (epi == EPI_QKV || epi == EPI_RESID) ? LLM_GEMV_NR_SMALL : LLM_GEMV_NR_BIG;
     const int groups = (rows + nr - 1) / nr;
     int blocks = (groups + kWaves - 1) / kWaves;
-    const int cap = 2048;
+    const int cap = LLM_GEMV_GRID_CAP;
     return blocks < cap ? blocks : cap;
 }
 
@@ -513,13 +356,13 @@ hipError_t launch_set_state(State* st, int token, int pos, int gen_mode, hipStre
 // query heads of one KV head, so every K and V row is read once. The positions
 // 0..P-1 are split across gridDim.x blocks; within a block they are processed
 // in chunks with an online softmax (running max m, sum l, unnormalised output
-// o). Scores are divided by sqrt(head_dim). The last block of a KV head to
-// finish merges the splits: M = max m_s, L = sum l_s e^(m_s - M),
-// out = sum o_s e^(m_s - M) / L.
+// o). Scores are divided by sqrt(head_dim). k_attn_combine merges the splits:
+// M = max m_s, L = sum l_s e^(m_s - M), out = sum o_s e^(m_s - M) / L.
 //
 // Thread layout: LPP lanes share one position, each lane holding 8 consecutive
 // dimensions (one 16-byte load of a K or V row); PPI = 256/LPP positions per
-// step.
+// step, and a chunk is kAttnSteps steps, whose K and V loads are all issued
+// before any of them is used.
 template <int G>
 __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     extern __shared__ float sm[];
@@ -536,22 +379,24 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     const int t_begin = s * CH, t_end = min(P, t_begin + CH);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int LPP = 1;
-    while (LPP * 8 < hd) LPP <<= 1;
+    const int LPP = attn_lpp(hd);
     const int PPI = kBlock / LPP;
+    const int CHUNK = PPI * kAttnSteps;
     const int sub = tid % LPP, pg = tid / LPP;
     const bool dim_ok = sub * 8 < hd;
 
-    float* sc = sm;                         // [G][kAttnChunk] scores, then weights
-    float* wred = sm + G * kAttnChunk;      // [kWaves][G][hd] output reduction
+    float* sc = sm;                     // [G][CHUNK] scores, then weights
+    float* wred = sm + G * CHUNK;       // [kWaves][G][hd] output reduction
 
     const int qd = a.n_heads * hd;
     const float* qz = a.q + (size_t)z * qd;
     float qv[G][8];
+#pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
         for (int i = 0; i < 8; i++) qv[h][i] = dim_ok ? qz[(g * G + h) * hd + sub * 8 + i] : 0.f;
     float acc[G][8];
+#pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
         for (int i = 0; i < 8; i++) acc[h][i] = 0.f;
@@ -560,51 +405,47 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         l_run[tid] = 0.f;
     }
 
-    const __half* kbase = a.kc + (size_t)g * a.n_ctx * hd;
-    const __half* vbase = a.vc + (size_t)g * a.n_ctx * hd;
+    const __half* kbase = a.kc + (size_t)g * a.n_ctx * hd + sub * 8;
+    const __half* vbase = a.vc + (size_t)g * a.n_ctx * hd + sub * 8;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
 
-    for (int c0 = t_begin; c0 < t_end; c0 += kAttnChunk) {
-        const int cn = min(kAttnChunk, t_end - c0);
-        __syncthreads();
+    for (int c0 = t_begin; c0 < t_end; c0 += CHUNK) {
+        const int cn = min(CHUNK, t_end - c0);
+        u32x4 kr[kAttnSteps], vr[kAttnSteps];
+#pragma unroll
+        for (int i = 0; i < kAttnSteps; i++) {
+            const int t = pg + i * PPI;
+            const bool ok = dim_ok && t < cn;
+            kr[i] = ok ? *(const u32x4*)(kbase + (size_t)(c0 + t) * hd) : z4;
+            vr[i] = ok ? *(const u32x4*)(vbase + (size_t)(c0 + t) * hd) : z4;
+        }
         // scores
-        for (int tt = pg; tt < ((cn + PPI - 1) / PPI) * PPI; tt += PPI) {
-            const bool ok = tt < cn;
-            float part[G];
-            for (int h = 0; h < G; h++) part[h] = 0.f;
-            if (ok && dim_ok) {
-                const uint4 raw = *(const uint4*)(kbase + (size_t)(c0 + tt) * hd + sub * 8);
-                const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
-                float kf[8];
 #pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    kf[2 * k] = h2f((uint16_t)(u[k] & 0xffffu));
-                    kf[2 * k + 1] = h2f((uint16_t)(u[k] >> 16));
-                }
-                for (int h = 0; h < G; h++) {
-                    float d = 0.f;
+        for (int i = 0; i < kAttnSteps; i++) {
+            const int t = pg + i * PPI;
+            float kf[8];
+            unpack8(kr[i], kf);
 #pragma unroll
-                    for (int i = 0; i < 8; i++) d += qv[h][i] * kf[i];
-                    part[h] = d;
-                }
-            }
             for (int h = 0; h < G; h++) {
-                float d = part[h];
+                float d = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; j++) d += qv[h][j] * kf[j];
                 for (int o = 1; o < LPP; o <<= 1) d += __shfl_xor(d, o, 64);
-                if (sub == 0 && ok) sc[h * kAttnChunk + tt] = d / a.scale_div;
+                if (sub == 0 && t < cn) sc[h * CHUNK + t] = d / a.scale_div;
             }
         }
         __syncthreads();
         // chunk max, running max, weights and their sum (one wave per head)
         for (int h = wave; h < G; h += kWaves) {
             float mx = -INFINITY;
-            for (int t = lane; t < cn; t += 64) mx = fmaxf(mx, sc[h * kAttnChunk + t]);
+            for (int t = lane; t < cn; t += 64) mx = fmaxf(mx, sc[h * CHUNK + t]);
             mx = wave_max(mx);
             const float m_old = m_run[h];
             const float m_new = fmaxf(m_old, mx);
             float ls = 0.f;
             for (int t = lane; t < cn; t += 64) {
-                const float e = expf(sc[h * kAttnChunk + t] - m_new);
-                sc[h * kAttnChunk + t] = e;
+                const float e = expf(sc[h * CHUNK + t] - m_new);
+                sc[h * CHUNK + t] = e;
                 ls += e;
             }
             ls = wave_sum(ls);
@@ -617,30 +458,30 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         }
         __syncthreads();
         // weighted values
+#pragma unroll
         for (int h = 0; h < G; h++) {
             const float al = alpha[h];
 #pragma unroll
             for (int i = 0; i < 8; i++) acc[h][i] *= al;
         }
-        if (dim_ok) {
-            for (int tt = pg; tt < cn; tt += PPI) {
-                const uint4 raw = *(const uint4*)(vbase + (size_t)(c0 + tt) * hd + sub * 8);
-                const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < kAttnSteps; i++) {
+            const int t = pg + i * PPI;
+            if (dim_ok && t < cn) {
                 float vf[8];
+                unpack8(vr[i], vf);
 #pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    vf[2 * k] = h2f((uint16_t)(u[k] & 0xffffu));
-                    vf[2 * k + 1] = h2f((uint16_t)(u[k] >> 16));
-                }
                 for (int h = 0; h < G; h++) {
-                    const float w = sc[h * kAttnChunk + tt];
+                    const float w = sc[h * CHUNK + t];
 #pragma unroll
-                    for (int i = 0; i < 8; i++) acc[h][i] += w * vf[i];
+                    for (int j = 0; j < 8; j++) acc[h][j] += w * vf[j];
                 }
             }
         }
+        __syncthreads();
     }
     // reduce the per-thread outputs over the positions each lane group took
+#pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
         for (int i = 0; i < 8; i++) {
@@ -648,8 +489,8 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
             for (int o = LPP; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
             acc[h][i] = v;
         }
-    __syncthreads();
     if (lane < LPP && dim_ok)
+#pragma unroll
         for (int h = 0; h < G; h++)
 #pragma unroll
             for (int i = 0; i < 8; i++) wred[(wave * G + h) * hd + sub * 8 + i] = acc[h][i];
@@ -687,9 +528,12 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 // Merge of the position splits of one KV head's G query heads: M = max m_s,
 // L = sum l_s e^(m_s - M), out = sum o_s e^(m_s - M) / L, splits in order.
 // When a single split was active the attention kernel wrote out itself.
+template <int G>
 __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
+    __shared__ float wj[kMaxSplit * G];
+    __shared__ float Ls[G];
     const int g = blockIdx.x, z = blockIdx.y;
-    const int hd = a.head_dim, G = a.n_heads / a.n_kv_heads;
+    const int hd = a.head_dim;
     const int P = a.st ? a.st->pos + 1 : a.p0 + z + 1;
     const int S = a.n_split;
     int CH = (P + S - 1) / S;
@@ -697,20 +541,32 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
     const int n_active = (P + CH - 1) / CH;
     if (n_active == 1) return;
     const int stride = hd + 2, GH = G * hd, qd = a.n_heads * hd;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* parts = a.part + (((size_t)z * a.n_kv_heads + g) * S) * (size_t)(G * stride);
-    float* outz = a.out + (size_t)z * qd + (size_t)g * GH;
-    for (int e = threadIdx.x; e < GH; e += kBlock) {
-        const int h = e / hd, d = e % hd;
+    // split maxima and sums, one wave per head
+    for (int h = wave; h < G; h += kWaves) {
         float M = -INFINITY;
-        for (int j = 0; j < n_active; j++) M = fmaxf(M, parts[(size_t)j * G * stride + h * stride]);
-        float L = 0.f, O = 0.f;
-        for (int j = 0; j < n_active; j++) {
+        for (int j = lane; j < n_active; j += 64) M = fmaxf(M, parts[(size_t)j * G * stride + h * stride]);
+        M = wave_max(M);
+        float L = 0.f;
+        for (int j = lane; j < n_active; j += 64) {
             const float* pj = parts + (size_t)j * G * stride + h * stride;
             const float f = expf(pj[0] - M);
+            wj[j * G + h] = f;
             L += pj[1] * f;
-            O += pj[2 + d] * f;
         }
-        const float r = O / L;
+        L = wave_sum(L);
+        if (lane == 0) Ls[h] = L;
+    }
+    __syncthreads();
+    float* outz = a.out + (size_t)z * qd + (size_t)g * GH;
+    for (int e = tid; e < GH; e += kBlock) {
+        const int h = e / hd, d = e % hd;
+        const float* po = parts + h * stride + 2 + d;
+        float O = 0.f;
+#pragma unroll 8
+        for (int j = 0; j < n_active; j++) O += wj[j * G + h] * po[(size_t)j * G * stride];
+        const float r = O / Ls[h];
         outz[e] = r;
         if (a.out_h) a.out_h[(size_t)z * qd + (size_t)g * GH + e] = f2h(r);
     }
@@ -718,7 +574,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
 
 template <int G>
 static hipError_t launch_attn_g(const AttnArgs& a, int n_q, hipStream_t s) {
-    const size_t lds = ((size_t)G * kAttnChunk + (size_t)kWaves * G * a.head_dim) * sizeof(float);
+    const size_t lds = ((size_t)G * attn_chunk(a.head_dim) + (size_t)kWaves * G * a.head_dim) * sizeof(float);
     static bool attr_done = false;
     if (!attr_done) {
         hipError_t e = hipFuncSetAttribute((const void*)k_attn<G>, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
@@ -728,7 +584,7 @@ static hipError_t launch_attn_g(const AttnArgs& a, int n_q, hipStream_t s) {
     hipLaunchKernelGGL((k_attn<G>), dim3(a.n_split, a.n_kv_heads, n_q), dim3(kBlock), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
-    hipLaunchKernelGGL(k_attn_combine, dim3(a.n_kv_heads, n_q), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_attn_combine<G>), dim3(a.n_kv_heads, n_q), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 

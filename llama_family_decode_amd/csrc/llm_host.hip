@@ -19,16 +19,6 @@ namespace {
 
 thread_local std::string g_load_error;
 
-struct LayerW {
-    const float* attn_norm;
-    Mat qkv;
-    const float* bqkv;
-    Mat o;
-    const float* ffn_norm;
-    Mat gu;
-    Mat down;
-};
-
 // 256-byte aligned sub-allocation of an arena; with a null base it only measures.
 struct Arena {
     char* base = nullptr;
@@ -201,6 +191,12 @@ struct Layout {
     float2* rope;
     float *x, *q, *ao, *u, *logits, *attn_part;
     int *gen_out, *ptok;
+    LayerW* dlayers;  // device copy of the layer table (persistent step kernel)
+    // versioned activations of the persistent step kernel (strides padded to 256 bytes)
+    float *sx, *sqkv, *sao, *spart, *su;
+    long long xstride, qkv_stride, ao_stride, part_stride, u_stride;
+    unsigned long long* sbar;
+    unsigned long long* strace;
     float *X, *Hf, *QKV, *Q, *Of, *Uf;
     __half *Hh, *Oh, *Uh;
     int n_split;
@@ -264,7 +260,21 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.ao = (float*)S.take((size_t)qd * 4);
     L.u = (float*)S.take((size_t)c->ffn * 4);
     L.logits = (float*)S.take((size_t)c->vocab * 4);
-    L.attn_part = (float*)S.take((size_t)L.n_split * c->n_kv_heads * G * (c->head_dim + 2) * 4);
+    L.attn_part = (float*)S.take((size_t)kMaxSplit * c->n_kv_heads * G * (c->head_dim + 2) * 4);
+    L.dlayers = (LayerW*)S.take((size_t)c->n_layers * sizeof(LayerW));
+    auto pad64 = [](long long n) { return (n + 63) / 64 * 64; };
+    L.xstride = pad64(c->dim);
+    L.qkv_stride = pad64(qd + 2 * kvd);
+    L.ao_stride = pad64(qd);
+    L.part_stride = pad64((long long)kStepMaxSplit * c->n_kv_heads * G * (c->head_dim + 2));
+    L.u_stride = pad64(c->ffn);
+    L.sx = (float*)S.take((size_t)(2 * c->n_layers + 1) * L.xstride * 4);
+    L.sqkv = (float*)S.take((size_t)c->n_layers * L.qkv_stride * 4);
+    L.sao = (float*)S.take((size_t)c->n_layers * L.ao_stride * 4);
+    L.spart = (float*)S.take((size_t)c->n_layers * L.part_stride * 4);
+    L.su = (float*)S.take((size_t)c->n_layers * L.u_stride * 4);
+    L.sbar = (unsigned long long*)S.take((size_t)(kBarGroups + 1) * kBarStride * 8);
+    L.strace = (unsigned long long*)S.take((size_t)(kStepPhases * c->n_layers + 2) * 8);
     L.gen_out = (int*)S.take((size_t)c->n_ctx * 4);
     L.ptok = (int*)S.take((size_t)C * 4);
     L.X = (float*)S.take((size_t)C * c->dim * 4);
@@ -317,6 +327,9 @@ struct llm_ctx {
     bool poisoned = false;
     std::string err;
     int g_qkv, g_o, g_gu, g_down, g_vocab;
+    bool use_step = false;  // persistent step kernel (else the launch graph)
+    int step_grid = 0, step_lds = 0;
+    StepArgs step;
 };
 
 namespace {
@@ -448,6 +461,10 @@ hipError_t enqueue_step(llm_ctx* c, hipStream_t s) {
 }
 
 int run_step(llm_ctx* c) {
+    if (c->use_step) {
+        HIPCHK(c, launch_step(c->step, c->step_grid, c->step_lds, c->stream));
+        return LLM_OK;
+    }
     if (c->use_graph) {
         if (!c->gexec) {
             HIPCHK(c, hipStreamBeginCapture(c->cap, hipStreamCaptureModeRelaxed));
@@ -475,6 +492,10 @@ int finish(llm_ctx* c, float* d_logits, int32_t* h_next) {
         HIPCHK(c, hipMemcpyAsync(&st, c->L.st, sizeof st, hipMemcpyDeviceToHost, c->stream));
         HIPCHK(c, hipStreamSynchronize(c->stream));
         *h_next = st.next;
+        if (st.abort) {
+            c->poisoned = true;
+            return fail(c, LLM_ERR_DEVICE, "a grid barrier of the step kernel timed out");
+        }
         if (st.nonfinite) return fail(c, LLM_ERR_NONFINITE, "a logit is NaN or infinite");
     }
     return LLM_OK;
@@ -611,6 +632,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
     const float theta_scale = (float)pow((double)cfg->rope_base, -2.0 / cfg->rope_dims);
     if (launch_rope_table(L.rope, cfg->n_ctx, cfg->rope_dims, theta_scale, s) != hipSuccess ||
         hipMemsetAsync(L.st, 0, sizeof(State), s) != hipSuccess ||
+        hipMemsetAsync(L.sbar, 0, (size_t)(kBarGroups + 1) * kBarStride * 8, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
         return bail(LLM_ERR_DEVICE, "initialisation kernels failed");
 
@@ -620,6 +642,59 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
     c->g_down = gemv_grid(PRO_PLAIN, EPI_RESID, cfg->dim);
     c->g_vocab = gemv_grid(PRO_NORM, EPI_ARGMAX, cfg->vocab);
 
+    // persistent step kernel
+    {
+        StepArgs& A = c->step;
+        memset(&A, 0, sizeof A);
+        A.layers = L.dlayers;
+        A.n_layers = cfg->n_layers;
+        A.embd = L.embd;
+        A.out = L.out;
+        A.out_norm = L.out_norm;
+        A.kc = L.kc;
+        A.vc = L.vc;
+        A.kv_layer = (long long)L.kv_layer;
+        A.rope = L.rope;
+        A.st = L.st;
+        A.bar = L.sbar;
+        A.xv = L.sx;
+        A.qkv = L.sqkv;
+        A.ao = L.sao;
+        A.part = L.spart;
+        A.u = L.su;
+        A.xstride = L.xstride;
+        A.qkv_stride = L.qkv_stride;
+        A.ao_stride = L.ao_stride;
+        A.part_stride = L.part_stride;
+        A.u_stride = L.u_stride;
+        A.logits = L.logits;
+        const char* tr = getenv("LLM_STEP_TRACE");
+        A.trace = (tr && tr[0] == '1') ? L.strace : nullptr;
+        A.gen_out = L.gen_out;
+        A.gen_cap = cfg->n_ctx;
+        A.dim = cfg->dim;
+        A.n_heads = cfg->n_heads;
+        A.n_kv_heads = cfg->n_kv_heads;
+        A.head_dim = cfg->head_dim;
+        A.n_rot = cfg->rope_dims;
+        A.neox = cfg->rope_neox;
+        A.n_ctx = cfg->n_ctx;
+        A.ffn = cfg->ffn;
+        A.vocab = cfg->vocab;
+        A.eps = cfg->eps;
+        A.scale_div = (float)sqrt((double)cfg->head_dim);
+        if (!upload(L.dlayers, L.layers.data(), L.layers.size() * sizeof(LayerW)))
+            return bail(LLM_ERR_DEVICE, "layer table upload failed");
+        const char* sk = getenv("LLM_STEP");
+        const bool want = sk && strcmp(sk, "persistent") == 0;
+        c->step_grid = want ? step_grid(A, &c->step_lds) : 0;
+        if (c->step_grid >= cfg->n_kv_heads && c->step_grid <= kBarGroup * kBarGroups) {
+            int S = c->step_grid / cfg->n_kv_heads;
+            A.n_split = S < kMaxSplit ? S : kMaxSplit;
+            c->use_step = true;
+        }
+    }
+
     if (c->use_graph && hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking) != hipSuccess)
         return bail(LLM_ERR_DEVICE, "stream creation failed");
     // One direct step (token 0 at position 0) sets the kernels' launch attributes
@@ -627,6 +702,17 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
     if (launch_set_state(L.st, 0, 0, 0, s) != hipSuccess || enqueue_step(c, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
         return bail(LLM_ERR_DEVICE, std::string("first step failed: ") + hipGetErrorString(hipGetLastError()));
+    if (c->use_step) {
+        if (launch_set_state(L.st, 0, 0, 0, s) != hipSuccess ||
+            launch_step(c->step, c->step_grid, c->step_lds, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+            (void)hipGetLastError();
+            c->use_step = false;  // cooperative launch unavailable: the launch graph runs the steps
+        } else {
+            State st;
+            if (hipMemcpy(&st, L.st, sizeof st, hipMemcpyDeviceToHost) != hipSuccess || st.abort)
+                return bail(LLM_ERR_DEVICE, "step kernel failed its first run");
+        }
+    }
     c->len = 0;
     *out = c;
     return LLM_OK;
@@ -657,6 +743,10 @@ int llm_generate(llm_ctx* c, int32_t token, int32_t n_steps, int32_t* h_tokens) 
     HIPCHK(c, hipMemcpyAsync(&st, c->L.st, sizeof st, hipMemcpyDeviceToHost, c->stream));
     HIPCHK(c, hipStreamSynchronize(c->stream));
     c->len += n_steps;
+    if (st.abort) {
+        c->poisoned = true;
+        return fail(c, LLM_ERR_DEVICE, "a grid barrier of the step kernel timed out");
+    }
     if (st.nonfinite) return fail(c, LLM_ERR_NONFINITE, "a logit is NaN or infinite");
     return LLM_OK;
 }
@@ -841,7 +931,7 @@ int llm_op_kv_write(llm_ctx* c, int32_t layer, int32_t pos0, int32_t n_pos, cons
 int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n_launch, float* h_ms) {
     int rc = check_layer(c, layer);
     if (rc) return rc;
-    if (stage < LLM_STAGE_QKV || stage > LLM_STAGE_LOGITS || n_launch <= 0 || !h_ms || pos < 0 || pos >= c->cfg.n_ctx)
+    if (stage < LLM_STAGE_QKV || stage > LLM_STAGE_STEP || n_launch <= 0 || !h_ms || pos < 0 || pos >= c->cfg.n_ctx)
         return fail(c, LLM_ERR_ARG, "bad stage, position, count or pointer");
     const Layout& L = c->L;
     hipStream_t s = c->stream;
@@ -853,6 +943,12 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
             case LLM_STAGE_O: return stage_o(c, layer, L.ao, L.x, s);
             case LLM_STAGE_FFN_UP: return stage_ffn_up(c, layer, L.x, L.u, s);
             case LLM_STAGE_DOWN: return stage_down(c, layer, L.u, L.x, s);
+            case LLM_STAGE_STEP:
+                if (c->use_step) {
+                    hipError_t e = launch_set_state(L.st, 0, pos, 0, s);
+                    return e != hipSuccess ? e : launch_step(c->step, c->step_grid, c->step_lds, s);
+                }
+                return enqueue_step(c, s);
             default: return enqueue_logits(c, L.x, s);
         }
     };
@@ -870,6 +966,17 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
     (void)hipEventDestroy(e1);
     if (e != hipSuccess) return dev_fail(c, e, "llm_op_time");
     *h_ms = ms / (float)n_launch;
+    return LLM_OK;
+}
+
+int llm_op_step_trace(llm_ctx* c, uint64_t* h_out, int32_t n) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    const int total = kStepPhases * c->cfg.n_layers + 2;
+    if (!h_out || n < total) return fail(c, LLM_ERR_ARG, "output too small");
+    if (!c->use_step || !c->step.trace) return fail(c, LLM_ERR_ARG, "step trace is off (set LLM_STEP_TRACE=1 before loading)");
+    HIPCHK(c, hipMemcpyAsync(h_out, c->L.strace, (size_t)total * 8, hipMemcpyDeviceToHost, c->stream));
+    HIPCHK(c, hipStreamSynchronize(c->stream));
     return LLM_OK;
 }
 
