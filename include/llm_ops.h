@@ -70,8 +70,17 @@ int llm_op_kv_write(llm_ctx* ctx, int32_t layer, int32_t pos0, int32_t n_pos, co
  * (with layer ignored); it writes cache row pos of every layer. Waits. */
 int llm_op_time(llm_ctx* ctx, int32_t stage, int32_t layer, int32_t pos, int32_t n_launch, float* h_ms);
 
+/* Which kernel runs the context's decode steps: 1 for the persistent step
+ * kernel (one cooperative launch per token), 0 for the captured launch graph
+ * (six launches per layer plus the logits). The persistent kernel is used
+ * when the environment variable LLM_STEP is "persistent" at load time, the
+ * device can co-schedule one block per compute unit, all layer matrices
+ * share one weight type and G*head_dim (G = n_heads/n_kv_heads) is a multiple
+ * of 32. Returns the kind, or a negative LLM_ERR_* for a NULL context. */
+int llm_op_step_kind(llm_ctx* ctx);
+
 /* Wall-clock stamps (100 MHz device clock) that block 0 of the last decode-step
- * launch took at its start and after each of its 5*n_layers + 1 grid barriers:
+ * launch took at its start and after each of its 5*n_layers + 1 barriers:
  * stamp k+1 - stamp k is the time of phase k (per layer: QKV, attention,
  * split merge + output, gate/up, down; then the logits). h_out receives
  * 5*n_layers + 2 values. Available only when the context was loaded with the

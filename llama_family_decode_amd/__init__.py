@@ -29,7 +29,8 @@ ERRORS = {
 }
 EXPORTS = ["llm_plan", "llm_load_weights", "llm_decode", "llm_prefill", "llm_generate", "llm_reset", "llm_free",
            "llm_last_error", "llm_logits", "llm_kv_len", "llm_kv_read", "llm_op_qkv", "llm_op_attention", "llm_op_o",
-           "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind", "llm_op_step_trace"]
+           "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind", "llm_op_step_trace",
+           "llm_op_step_kind"]
 STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_FFN_UP, STAGE_DOWN, STAGE_LOGITS = range(6)
 
 
@@ -95,6 +96,8 @@ def lib():
         L.llm_rewind.argtypes = [vp, i32]
         L.llm_op_step_trace.argtypes = [vp, vp, i32]
         L.llm_op_step_trace.restype = ctypes.c_int
+        L.llm_op_step_kind.argtypes = [vp]
+        L.llm_op_step_kind.restype = ctypes.c_int
         for f in ("llm_op_qkv", "llm_op_attention", "llm_op_o", "llm_op_ffn_up", "llm_op_down", "llm_op_logits",
                   "llm_op_kv_write", "llm_op_time", "llm_rewind"):
             getattr(L, f).restype = ctypes.c_int
@@ -242,6 +245,14 @@ def llm_op_time(ctx, stage: int, layer: int = 0, pos: int = 0, n_launch: int = 2
     ms = ctypes.c_float()
     _check(lib().llm_op_time(ctx, stage, layer, pos, n_launch, ctypes.byref(ms)), ctx)
     return float(ms.value)
+
+
+def llm_op_step_kind(ctx) -> int:
+    """1 if the persistent step kernel runs the context's decode steps, 0 for the launch graph."""
+    r = lib().llm_op_step_kind(ctx)
+    if r < 0:
+        raise LlmError(r, "llm_op_step_kind")
+    return r
 
 
 def llm_op_step_trace(ctx, n_layers: int) -> np.ndarray:

@@ -53,9 +53,9 @@ struct LayerW {
     Mat down;
 };
 
-// Arguments of the persistent decode-step kernel. Every activation buffer is
-// versioned (one copy per layer, or per residual update), so within a launch
-// each address is written once, before any block reads it.
+// Arguments of the persistent decode-step kernel. Activations that cross
+// blocks live in buffers with one copy per layer, so within a launch each
+// address is written once, before any block reads it.
 struct StepArgs {
     const LayerW* layers;  // device array of n_layers descriptors
     int n_layers;
@@ -66,26 +66,27 @@ struct StepArgs {
     long long kv_layer;  // elements of one layer of one cache
     const float2* rope;
     State* st;
-    unsigned long long* bar;  // [kBarGroups] group counters then the global one, 256 bytes apart
-    float* xv;      // residual versions [2 n_layers + 1][xstride]
+    unsigned long long* bar;  // barrier counters, kBarStride u64 apart
     float* qkv;     // q | k | v after bias and RoPE, per layer [n_layers][qkv_stride]
-    float* ao;      // attention output per layer [n_layers][ao_stride]
     float* part;    // attention split partials per layer [n_layers][part_stride]
+    float* po;      // output-product partial sums per layer and group [n_layers][kStepGroups][pstride]
+    float* pd;      // down-product partial sums, same layout
     float* u;       // SwiGLU output per layer [n_layers][u_stride]
     float* logits;  // [vocab]
     int* gen_out;
     int gen_cap;
-    long long xstride, qkv_stride, ao_stride, part_stride, u_stride;
+    long long qkv_stride, part_stride, u_stride, pstride;
     unsigned long long* trace;  // nullptr, or wall-clock stamps of block 0 after each barrier
-    int dim, n_heads, n_kv_heads, head_dim, n_rot, neox, n_ctx, ffn, vocab, n_split;
+    int dim, n_heads, n_kv_heads, head_dim, n_rot, neox, n_ctx, ffn, vocab;
+    int lds_xr, lds_xs, lds_wsp;  // LDS regions (floats)
     float eps, scale_div;
 };
 
-constexpr int kStepMaxSplit = 16;  // attention splits of the persistent step kernel
-constexpr int kStepPhases = 5;     // grid barriers per layer of the persistent step kernel
-constexpr int kBarGroup = 16;    // blocks per first-level barrier counter
-constexpr int kBarGroups = 64;   // capacity of first-level counters (grid <= 1024)
-constexpr int kBarStride = 32;   // u64 elements between counters (256 bytes)
+constexpr int kStepGroups = 8;     // block groups of the persistent step kernel (one per XCD)
+constexpr int kStepMaxSplit = 64;  // attention splits per KV head of the persistent step kernel
+constexpr int kStepPhases = 5;     // barriers per layer of the persistent step kernel
+constexpr int kBarSlots = 2 * kStepGroups;  // barrier counters
+constexpr int kBarStride = 32;     // u64 elements between counters (256 bytes)
 
 constexpr int kBlock = 256;  // threads per block for all decode kernels (4 wave64)
 constexpr int kWaves = kBlock / 64;
@@ -151,10 +152,11 @@ int gemv_grid(int pro, int epi, int rows);
 hipError_t launch_attn(const AttnArgs& a, int n_q, hipStream_t s);
 hipError_t launch_set_state(State* st, int token, int pos, int gen_mode, hipStream_t s);
 hipError_t launch_argmax_finalize(State* st, int* gen_out, int gen_cap, hipStream_t s);
-// Persistent step kernel: blocks that can be co-resident (0 if it cannot run)
-// and the launch of one step.
-int step_grid(const StepArgs& a, int* lds_bytes);
-hipError_t launch_step(const StepArgs& a, int grid, int lds_bytes, hipStream_t s);
+// Persistent step kernel for layer weights of type dtype: the grid (0 if the
+// shape or the device does not allow it; also fills the LDS plan of a) and the
+// launch of one step.
+int step_grid(StepArgs& a, int dtype, int* lds_bytes);
+hipError_t launch_step(const StepArgs& a, int dtype, int grid, int lds_bytes, hipStream_t s);
 
 struct PrefillBufs;
 hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s);

@@ -1,24 +1,43 @@
-// Persistent decode-step kernel for gfx950: one launch runs one token's whole
-// forward pass ("The Forward Pass in Java", Project 18 forward(); "What a Llama
-// model computes, and why", section 2) as a sequence of phases separated by
-// grid-wide barriers, one 512-thread block per compute unit:
-//   per layer: QKV (RMSNorm + products + bias + RoPE + F16 KV store) |
-//   attention splits | split merge + output product + residual |
-//   RMSNorm + gate/up + SwiGLU | down product + residual;
-//   then RMSNorm + vocabulary product + argmax, and the token feedback.
-// All blocks are co-resident (cooperative launch). Activations that cross
-// blocks are written with agent-scope atomic stores, which reach the point of
-// coherence of all the chip's L2 caches without writing back or invalidating
-// any of them. Every activation buffer is versioned (one copy per layer, or
-// per residual update), so within a launch an address is written once and
-// read only after the barrier that follows the write: no cache can hold a
-// stale copy of it (caches are invalidated at kernel start), and readers use
-// ordinary cached, vectorised loads. A barrier counts arrivals in two levels,
-// kBarGroup blocks per first-level counter and the last arrival of a group
-// bumping the global counter; counters are never reset, so barrier j (counted
-// over all launches) waits for the global count j * groups. Every wait is
-// bounded: past the spin limit the block raises the abort flag, every later
-// wait returns at once, and the host reports a device error.
+// Persistent decode-step kernel for gfx950: one cooperative launch runs one
+// token's whole forward pass ("The Forward Pass in Java", Project 18
+// forward(); "What a Llama model computes, and why", section 2), one 512-thread
+// block per compute unit.
+//
+// The grid is split into 8 groups of blocks (block b in group b % 8, which is
+// how the dispatcher deals blocks to the chip's 8 XCDs, so a group shares one
+// L2). The groups split every layer the way tensor-parallel devices would:
+// group x owns a contiguous share of the KV heads (with their query heads) and
+// a contiguous share of the FFN hidden units. Per layer:
+//   QKV    every block normalises its own copy of the residual; the group
+//          computes the q/k/v rows of its heads (+ bias, RoPE, F16 KV store)
+//   | group barrier |
+//   ATTN   the group's blocks split the cached positions of its KV heads
+//   | group barrier |
+//   O      every block of the group merges the splits, then the group computes
+//          the output product over its heads' columns: a partial sum of W_o o
+//   | all-group barrier |
+//   GU     every block adds the 8 partial sums to its residual copy (fixed
+//          order), normalises; the group computes gate/up of its hidden units
+//          and SwiGLU
+//   | group barrier |
+//   DOWN   the group computes W_down u over its hidden units: a partial sum
+//   | all-group barrier |, after which every block adds the partials.
+// Then every block takes a share of the vocabulary rows (final RMSNorm,
+// product, argmax), and a last all-group barrier precedes the token feedback.
+//
+// Memory ordering. Values that cross blocks are written with agent-scope
+// atomic stores (they reach the coherence point of all L2 caches without
+// flushing any cache) into buffers with one copy per layer, so within a launch
+// an address is written once and read only after the barrier that follows the
+// write; readers then use ordinary cached loads (caches are invalidated at
+// kernel start, and no cache line is shared between two buffers). A barrier
+// arrival is an atomic add without return, issued only after the block's
+// stores have completed. The weights of the next phase do not depend on any
+// activation, so each wave issues their loads right after the arrival: they
+// stream from HBM while the barrier completes. Counters are never reset:
+// barrier j (counted over all launches) waits for j arrivals per group block.
+// Every wait is bounded: past the spin limit a block raises the abort flag,
+// later waits return at once, and the host reports a device error.
 #include "device_common.h"
 
 namespace llm {
@@ -26,31 +45,112 @@ namespace llm {
 constexpr int kSpinLimit = 4 << 20;
 constexpr int kSB = 512;       // threads per block
 constexpr int kSW = kSB / 64;  // waves per block
+constexpr int kNG = kStepGroups;
+constexpr int kPF = 16;        // 16-byte weight chunks a lane holds per batch
+
+typedef unsigned long long u64;
 
 __device__ __forceinline__ void stc(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ u64 ldc(u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ void arrive(u64* p) {
+    (void)__hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this wave's stores (and loads) have completed; also a compiler
+// barrier, so no memory access moves across it.
+__device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void pin() { asm volatile("" ::: "memory"); }
+// The lane index, opaque to the optimiser: address arithmetic derived from it
+// is redone at each use instead of being hoisted out of the layer loop (where
+// the same values for every layer would stay live in registers).
+__device__ __forceinline__ int lane_id() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+}
+__device__ __forceinline__ int thread_id() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+// Loads through global-address-space pointers: weights and activations live in
+// device memory, and global (not flat) loads count only against the vector
+// memory counter, so LDS waits never wait for weight loads in flight.
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const uint16_t g_u16;
+typedef __attribute__((address_space(1))) const float g_f32;
+__device__ __forceinline__ u32x4 ld_nt(const void* p) { return __builtin_nontemporal_load((g_u32x4*)p); }
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(g_u32x4*)p; }
+__device__ __forceinline__ uint32_t ld_u16(const uint16_t* p) { return *(g_u16*)p; }
+__device__ __forceinline__ float ldf(const float* p) { return *(g_f32*)p; }
+__device__ __forceinline__ float4 ldf4(const float* p) {
+    const u32x4 v = ld16(p);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
 
-// Barrier number `j` (counted over all launches) of the grid.
-__device__ void grid_sync(State* st, unsigned long long* bar, unsigned long long j) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+// A wave-uniform value made opaque the same way (kept in a scalar register).
+__device__ __forceinline__ int opaque_s(int v) {
+    v = __builtin_amdgcn_readfirstlane(v);
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+__device__ __forceinline__ bool aborted(State* st) {
+    return __hip_atomic_load(&st->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+}
+__device__ __forceinline__ void raise_abort(State* st) {
+    __hip_atomic_store(&st->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counter slots (kBarStride u64 apart): group barrier counters 0..7, all-group
+// arrival counters 8..15.
+__device__ __forceinline__ u64* lcount(const StepArgs& a, int x) { return a.bar + (size_t)x * kBarStride; }
+__device__ __forceinline__ u64* gcount(const StepArgs& a, int x) { return a.bar + (size_t)(kNG + x) * kBarStride; }
+
+// Group barrier, first half: all stores of the block have completed (every
+// wave ran wait_mem), then one arrival.
+__device__ __forceinline__ void group_arrive(const StepArgs& a, int x) {
     __syncthreads();
+    if (threadIdx.x == 0) arrive(lcount(a, x));
+}
+__device__ __forceinline__ void all_arrive(const StepArgs& a, int x) {
+    __syncthreads();
+    if (threadIdx.x == 0) arrive(gcount(a, x));
+}
+// Second half: wait for `target` arrivals on the group's counter.
+__device__ __forceinline__ void group_wait(const StepArgs& a, int x, u64 target) {
     if (threadIdx.x == 0) {
-        const int grp = blockIdx.x / kBarGroup, ngrp = (gridDim.x + kBarGroup - 1) / kBarGroup;
-        const int gsize = min(kBarGroup, (int)gridDim.x - grp * kBarGroup);
-        unsigned long long* gc = bar + (size_t)grp * kBarStride;
-        unsigned long long* top = bar + (size_t)kBarGroups * kBarStride;
-        const unsigned long long prev = __hip_atomic_fetch_add(gc, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev + 1 == j * (unsigned long long)gsize)
-            __hip_atomic_fetch_add(top, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long target = j * (unsigned long long)ngrp;
+        u64* c = lcount(a, x);
         int spins = 0;
-        while (__hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        while (ldc(c) < target) {
             __builtin_amdgcn_s_sleep(1);
             if ((++spins & 63) == 0) {
-                if (__hip_atomic_load(&st->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+                if (aborted(a.st)) break;
                 if (spins > kSpinLimit) {
-                    __hip_atomic_store(&st->abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    raise_abort(a.st);
+                    break;
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+// Wait until every group's counter reached `target`: lane i of wave 0 polls
+// group i's counter, all 8 in one load.
+__device__ __forceinline__ void all_wait(const StepArgs& a, u64 target) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        u64* c = gcount(a, lane & (kNG - 1));
+        int spins = 0;
+        while (true) {
+            const u64 v = lane < kNG ? ldc(c) : target;
+            if (__all(v >= target)) break;
+            __builtin_amdgcn_s_sleep(1);
+            if ((++spins & 63) == 0) {
+                if (aborted(a.st)) break;
+                if (spins > kSpinLimit) {
+                    if (lane == 0) raise_abort(a.st);
                     break;
                 }
             }
@@ -72,400 +172,672 @@ __device__ __forceinline__ double block_sum_s(double v, double* red) {
     return t;
 }
 
-// Stage the input vector of a product in LDS (swizzled for weight type DT).
-//   MODE 0: x = src.  MODE 1: x = rmsnorm(src) * gain ("The Forward Pass in
-//   Java", Example 4: sum of squares in double, scale rounded to float once).
-//   MODE 2: x = rmsnorm(E[tok]) * gain, and block 0 writes E[tok] to xres.
-template <int DT, int MODE>
-__device__ void stage_c(const float* src, const Mat* E, int tok, float* xres, const float* gain, float eps, int K,
-                        float* xs, double* red) {
-    const int tid = threadIdx.x;
+// xs (swizzled for weight type DT) = rmsnorm(xr) * gain over K elements
+// ("The Forward Pass in Java", Example 4: sum of squares in double, the scale
+// rounded to float once, then x * scale * gain).
+template <int DT>
+__device__ __forceinline__ void stage_norm(const float* xr, const float* gain, float eps, int K, float* xs, double* red) {
+    const int tid = thread_id();
     double ss = 0.0;
     for (int i = 4 * tid; i < K; i += 4 * kSB) {
-        float4 v;
-        if constexpr (MODE == 2) {
-            v = make_float4(mat_elem(*E, tok, i), mat_elem(*E, tok, i + 1), mat_elem(*E, tok, i + 2),
-                            mat_elem(*E, tok, i + 3));
-            if (blockIdx.x == 0) {
-                stc(xres + i, v.x);
-                stc(xres + i + 1, v.y);
-                stc(xres + i + 2, v.z);
-                stc(xres + i + 3, v.w);
-            }
-        } else {
-            v = *(const float4*)(src + i);
-        }
-        if constexpr (MODE != 0)
-            ss += (double)v.x * (double)v.x + (double)v.y * (double)v.y + (double)v.z * (double)v.z +
-                  (double)v.w * (double)v.w;
-        *(float4*)(xs + swz<DT>(i)) = v;  // the swizzle keeps runs of 4 together
+        const float4 v = *(const float4*)(xr + i);
+        ss += (double)v.x * (double)v.x + (double)v.y * (double)v.y + (double)v.z * (double)v.z +
+              (double)v.w * (double)v.w;
     }
-    if constexpr (MODE != 0) {
-        const double tot = block_sum_s(ss, red);
-        const float scale = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
-        for (int i = tid; i < K; i += kSB) {
-            const int j = swz<DT>(i);
-            xs[j] = xs[j] * scale * gain[i];
-        }
+    const double tot = block_sum_s(ss, red);
+    const float scale = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
+    for (int i = tid; i < K; i += kSB) xs[swz<DT>(i)] = xr[i] * scale * ldf(gain + i);
+    __syncthreads();
+}
+
+// xs (swizzled) = src[0..K), K a multiple of 4.
+template <int DT>
+__device__ __forceinline__ void stage_copy(const float* src, int K, float* xs) {
+    for (int i = 4 * thread_id(); i < K; i += 4 * kSB) *(float4*)(xs + swz<DT>(i)) = ldf4(src + i);
+    __syncthreads();
+}
+
+// xr[i] += sum over the groups that contributed of P[g][i], groups in order.
+__device__ __forceinline__ void add_partials(float* xr, const float* P, long long pstride, int dim, unsigned gmask) {
+    for (int i = 4 * thread_id(); i < dim; i += 4 * kSB) {
+        float4 p[kNG];
+#pragma unroll
+        for (int g = 0; g < kNG; g++)
+            p[g] = (gmask >> g) & 1 ? ldf4(P + g * pstride + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 v = *(const float4*)(xr + i);
+#pragma unroll
+        for (int g = 0; g < kNG; g++)
+            if ((gmask >> g) & 1) {
+                v.x += p[g].x;
+                v.y += p[g].y;
+                v.z += p[g].z;
+                v.w += p[g].w;
+            }
+        *(float4*)(xr + i) = v;
     }
     __syncthreads();
 }
 
-// acc[i] = row rows[i] of W dotted with the staged input (wave-wide sum).
-template <int DT, int NR, int U>
-__device__ __forceinline__ void gemv_group(const Mat& W, const int* rows, const float* xs, float (&acc)[NR]) {
-    constexpr int VE = VecW<DT>::VE;
-    const int lane = threadIdx.x & 63;
-    const int nch = W.cols / VE;
-    int lrow[NR];
-#pragma unroll
-    for (int i = 0; i < NR; i++) {
-        lrow[i] = rows[i] < W.rows ? rows[i] : W.rows - 1;
-        acc[i] = 0.f;
+// ------------------------------------------------------ row-parallel products
+// A column window of a weight matrix: row r's window starts at w + r*ld
+// elements; Q8_0 scales of the window start at s + r*(ld/32).
+struct Win {
+    const char* w;
+    const uint16_t* s;
+    long long ld;
+    int nch;  // 16-byte chunks per row in the window
+};
+
+template <int DT>
+__device__ __forceinline__ Win make_win(const Mat& M, int col0, int ncols) {
+    constexpr int ES = DT == DT_F32 ? 4 : (DT == DT_F16 ? 2 : 1);
+    Win v;
+    v.w = (const char*)M.w + (size_t)col0 * ES;
+    v.s = DT == DT_Q8 ? M.s + col0 / 32 : nullptr;
+    v.ld = M.cols;
+    v.nch = ncols / VecW<DT>::VE;
+    return v;
+}
+
+// One wave's rows [r0, r1) of a product. A row is read by lpr lanes (a power
+// of two, 64 unless the window is short), so rpi = 64 / lpr rows share one
+// wave-wide load. The wave walks slots: slot k covers row group k / ncb (rpi
+// rows) and column batch k % ncb, in which lane l reads chunk l % lpr + lpr *
+// batch of row l / lpr of the group. A lane holds kPF slots at a time.
+struct WRows {
+    Win W;
+    int r0, r1;
+    int lpr, lsh, rpi, ncb, nslots;
+};
+
+__device__ __forceinline__ WRows wave_rows(int n, int nwaves, int wv, int nch, bool pairs) {
+    WRows w;
+    w.lpr = 64;
+    w.lsh = 6;
+    if (nch < 64) {
+        w.lpr = 1;
+        w.lsh = 0;
+        while (w.lpr < nch) {
+            w.lpr <<= 1;
+            w.lsh++;
+        }
     }
-    for (int c0 = lane; c0 < nch; c0 += 64 * U) {
-        u32x4 raw[U][NR];
-        float sc[U][NR];
-        load_batch<DT, NR, U>(W, lrow, c0, nch, raw, sc);
+    w.rpi = 64 >> w.lsh;
+    w.ncb = nch > 0 ? (nch + w.lpr - 1) >> w.lsh : 1;
+    const int unit = pairs ? 2 * w.rpi : w.rpi;
+    int per = (n + nwaves - 1) / nwaves;
+    per = (per + unit - 1) / unit * unit;
+    w.r0 = wv * per;
+    w.r1 = min(n, w.r0 + per);
+    if (nch <= 0 || w.r1 < w.r0) w.r1 = w.r0;
+    w.nslots = (w.r1 - w.r0 + w.rpi - 1) / w.rpi * w.ncb;
+    return w;
+}
+
+struct PF {
+    u32x4 q[kPF];
+    uint32_t s[kPF];  // raw binary16 scales (Q8_0)
+};
+
+// A wave with no rows still redefines its buffer, so that no older contents
+// stay live across the phases in between.
+__device__ __forceinline__ void pf_clear(PF& pf) {
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int c = c0 + 64 * u;
-            if (c < nch) {
+    for (int i = 0; i < kPF; i++) {
+        pf.q[i] = (u32x4){0u, 0u, 0u, 0u};
+        pf.s[i] = 0u;
+    }
+}
+
+// Issues the loads of slots k0 .. k0 + kPF - 1 into pf. Addresses past the
+// rows, slots or window are clamped to valid ones; wdot ignores their values.
+// Nothing here waits for the data. rmap (or nullptr) maps wave rows to matrix
+// rows, else matrix row = roff + row.
+template <int DT>
+__device__ __forceinline__ void wload(const WRows& w, const int* rmap, int roff, int k0, PF& pf) {
+    constexpr int ES = DT == DT_F32 ? 4 : (DT == DT_F16 ? 2 : 1);
+    if (w.nslots == 0) {
+        pf_clear(pf);
+        return;
+    }
+    const int lane = lane_id(), sub = lane >> w.lsh, cl = lane & (w.lpr - 1);
+    k0 = opaque_s(k0);
+    int g = k0 / w.ncb, cb = k0 - g * w.ncb;
 #pragma unroll
-                for (int i = 0; i < NR; i++) {
-                    const float p = chunk_dot<DT>(raw[u][i], xs, c);
-                    if constexpr (DT == DT_Q8)
-                        acc[i] += sc[u][i] * p;
-                    else
-                        acc[i] += p;
+    for (int k = 0; k < kPF; k++) {
+        int row = w.r0 + g * w.rpi + sub;
+        row = row < w.r1 ? row : w.r1 - 1;
+        const long long ar = rmap ? rmap[row] : roff + row;
+        int c = cl + (cb << w.lsh);
+        c = c < w.W.nch ? c : w.W.nch - 1;
+        pf.q[k] = ld_nt(w.W.w + (ar * w.W.ld * ES + (long long)c * 16));
+        if constexpr (DT == DT_Q8) pf.s[k] = ld_u16(w.W.s + (ar * (w.W.ld / 32) + (c >> 1)));
+        if (++cb == w.ncb) {
+            cb = 0;
+            ++g;
+        }
+    }
+}
+
+// Kinds of what a product's rows become.
+enum StepEmit : int {
+    EM_PART = 0,    // P[row] = value (a partial sum of a K-split product)
+    EM_QKV = 1,     // RoPE pairs of q/k/v: bias, rotation, qkv buffer, F16 cache
+    EM_SWIGLU = 2,  // gate/up pairs: u[row / 2] = silu(gate) * up
+    EM_ARGMAX = 3,  // vocabulary rows: logits and the running first maximum
+};
+
+struct EmitArgs {
+    float* out;
+    const float* bias;
+    const float2* cs;  // (cos, sin) of this step's position, pair j at cs[j] (LDS)
+    __half* kc;
+    __half* vc;
+    int pos, n_ctx, hd, qd, kvd, half, n_rot, neox;
+};
+
+// q/k/v pair (matrix rows ra < rb): bias, RoPE at pos on q and k ("The Forward
+// Pass in Java", Example 6), q|k|v -> qkv buffer, k and v -> binary16 cache
+// row pos (Example 10).
+__device__ __forceinline__ void emit_qkv(const EmitArgs& e, int ra, int rb, float va, float vb) {
+    const int kind = ra < e.qd ? 0 : (ra < e.qd + e.kvd ? 1 : 2);
+    const int base = kind == 0 ? 0 : (kind == 1 ? e.qd : e.qd + e.kvd);
+    const int head = (ra - base) / e.hd, d = ra - base - head * e.hd;
+    if (e.bias) {
+        va += ldf(e.bias + ra);
+        vb += ldf(e.bias + rb);
+    }
+    if (kind < 2 && d < e.n_rot) {
+        const int j = e.neox ? d : d >> 1;
+        const float2 r = rope_rotate(va, vb, e.cs[j]);
+        va = r.x;
+        vb = r.y;
+    }
+    stc(e.out + ra, va);
+    stc(e.out + rb, vb);
+    if (kind > 0) {
+        __half* row = (kind == 1 ? e.kc : e.vc) + ((size_t)head * e.n_ctx + e.pos) * e.hd;
+        row[d] = f2h(va);
+        row[rb - base - head * e.hd] = f2h(vb);
+    }
+}
+
+// One batch of kPF slots starting at slot k0: dot products with the staged
+// input xs, summed over the lane's column batches of a row group (acc carries
+// a group into the next batch) and then over the group's lpr lanes, then
+// emitted. FULL: every slot, row and chunk of the batch is in range.
+template <int DT, int EM, bool FULL>
+__device__ __forceinline__ void wbatch(const WRows& w, const int* rmap, int roff, const float* xs, const PF& pf,
+                                       int k0, int lane, int sub, int cl, const EmitArgs& ea, float& acc,
+                                       float& pend, float& best, int& best_i, int& nonfinite) {
+    int g = k0 / w.ncb, cb = k0 - g * w.ncb;
+#pragma unroll
+    for (int k = 0; k < kPF; k++) {
+        const int row = w.r0 + g * w.rpi + sub;
+        const int c = cl + (cb << w.lsh);
+        if (FULL || (row < w.r1 && c < w.W.nch && k0 + k < w.nslots)) {
+            const float p = chunk_dot<DT>(pf.q[k], xs, c);
+            if constexpr (DT == DT_Q8)
+                acc += h2f((uint16_t)pf.s[k]) * p;
+            else
+                acc += p;
+        }
+        if (cb == w.ncb - 1 && (FULL || k0 + k < w.nslots)) {  // the group's rows are complete
+            float v = acc;
+            acc = 0.f;
+            for (int o = w.lpr >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+            if constexpr (EM == EM_QKV || EM == EM_SWIGLU) {
+                if (w.rpi == 1) {
+                    if (lane == 0) {
+                        if ((row & 1) == 0) {
+                            pend = v;
+                        } else if constexpr (EM == EM_QKV) {
+                            emit_qkv(ea, rmap[row - 1], rmap[row], pend, v);
+                        } else {
+                            stc(ea.out + (row >> 1), silu(pend) * v);
+                        }
+                    }
+                } else {
+                    const float other = __shfl_down(v, w.lpr, 64);
+                    if (cl == 0 && (sub & 1) == 0 && row < w.r1) {
+                        if constexpr (EM == EM_QKV)
+                            emit_qkv(ea, rmap[row], rmap[row + 1], v, other);
+                        else
+                            stc(ea.out + (row >> 1), silu(v) * other);
+                    }
+                }
+            } else if (cl == 0 && (FULL || row < w.r1)) {
+                if constexpr (EM == EM_PART) {
+                    stc(ea.out + row, v);
+                } else {
+                    const int r = roff + row;
+                    ea.out[r] = v;
+                    if (!isfinite(v)) nonfinite = 1;
+                    if (v > best) {  // a lane's rows arrive in increasing order
+                        best = v;
+                        best_i = r;
+                    }
                 }
             }
         }
+        if (++cb == w.ncb) {
+            cb = 0;
+            ++g;
+        }
     }
-#pragma unroll
-    for (int i = 0; i < NR; i++) acc[i] = wave_sum(acc[i]);
 }
 
-// Attention splits of this step: S splits of CH positions (a multiple of 16)
-// for P = pos + 1 cached positions.
-__device__ __forceinline__ void attn_splits(int P, int& S, int& CH) {
-    S = (P + 255) / 256;
+// Lane that holds slot s (0..15) after wave_reduce16.
+__device__ __forceinline__ int slot_lane(int s) {
+    return ((s >> 3) & 1) << 5 | ((s >> 2) & 1) << 4 | ((s >> 1) & 1) << 3 | (s & 1) << 2;
+}
+
+// Sums each of the 16 values v[s] over the 64 lanes of the wave in 17
+// exchanges (a transposed butterfly: every step keeps half of the values and
+// sends the other half); lane l ends with the total of slot s(l) =
+// 8*l5 + 4*l4 + 2*l3 + l2 (lk = bit k of l), so lanes slot_lane(s) .. +3 hold
+// slot s. The totals are sums of the same terms as a plain butterfly, in a
+// fixed order.
+__device__ __forceinline__ float wave_reduce16(const float (&v)[16], int lane) {
+    float t8[8], t4[4], t2[2];
+    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float send = h5 ? v[i] : v[i + 8], keep = h5 ? v[i + 8] : v[i];
+        t8[i] = keep + __shfl_xor(send, 32, 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float send = h4 ? t8[i] : t8[i + 4], keep = h4 ? t8[i + 4] : t8[i];
+        t4[i] = keep + __shfl_xor(send, 16, 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const float send = h3 ? t4[i] : t4[i + 2], keep = h3 ? t4[i + 2] : t4[i];
+        t2[i] = keep + __shfl_xor(send, 8, 64);
+    }
+    const float send = h2 ? t2[0] : t2[1], keep = h2 ? t2[1] : t2[0];
+    float t = keep + __shfl_xor(send, 4, 64);
+    t += __shfl_xor(t, 2, 64);
+    t += __shfl_xor(t, 1, 64);
+    return t;
+}
+
+// One batch of kPF = 16 slots for rows read by whole waves (lpr = 64) whose
+// window is a whole number of 64-chunk batches, ncb in {1, 2, 4, 8}: a batch
+// then holds 16 / ncb whole rows, an even number. Lane partials of each row
+// accumulate over its ncb slots, one transposed butterfly sums all rows over
+// the wave, and the lanes emit the rows in parallel.
+template <int DT, int EM>
+__device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int roff, const float* xs, const PF& pf,
+                                            int k0, int lane, const EmitArgs& ea, float& best, int& best_i,
+                                            int& nonfinite) {
+    static_assert(kPF == 16, "wave_reduce16 takes 16 slots");
+    float rv[16];
+    float acc = 0.f;
+    int cb = 0;
+#pragma unroll
+    for (int k = 0; k < kPF; k++) {
+        rv[k] = 0.f;
+        if (k0 + k < w.nslots) {
+            const int c = lane + (cb << 6);
+            const float p = chunk_dot<DT>(pf.q[k], xs, c);
+            if constexpr (DT == DT_Q8)
+                acc += h2f((uint16_t)pf.s[k]) * p;
+            else
+                acc += p;
+            if (cb == w.ncb - 1) {
+                rv[k] = acc;
+                acc = 0.f;
+            }
+        }
+        if (++cb == w.ncb) cb = 0;
+    }
+    const float t = wave_reduce16(rv, lane);
+    const int s = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+    const int row = w.r0 + (k0 + s) / w.ncb;  // the row that ends at slot s
+    const bool end = (lane & 3) == 0 && (s & (w.ncb - 1)) == w.ncb - 1 && k0 + s < w.nslots;
+    if constexpr (EM == EM_QKV || EM == EM_SWIGLU) {
+        // rows 2i and 2i+1: the odd row ends ncb slots later
+        const float other = __shfl(t, slot_lane((s + w.ncb) & 15), 64);
+        if (end && ((row - w.r0) & 1) == 0) {
+            if constexpr (EM == EM_QKV)
+                emit_qkv(ea, rmap[row], rmap[row + 1], t, other);
+            else
+                stc(ea.out + (row >> 1), silu(t) * other);
+        }
+    } else if (end) {
+        if constexpr (EM == EM_PART) {
+            stc(ea.out + row, t);
+        } else {
+            const int r = roff + row;
+            ea.out[r] = t;
+            if (!isfinite(t)) nonfinite = 1;
+            if (t > best) {  // a lane's rows arrive in increasing order
+                best = t;
+                best_i = r;
+            }
+        }
+    }
+}
+
+// The wave's rows. If `prefetched`, pf already holds the first kPF slots
+// (issued by wload before the barrier). For pairs, wave ranges start at even
+// rows.
+template <int DT, int EM>
+__device__ __forceinline__ void wrun(const WRows& w, const int* rmap, int roff, const float* xs, PF& pf,
+                                     bool prefetched, const EmitArgs& ea, float& best, int& best_i, int& nonfinite) {
+    if (w.nslots == 0) return;
+    const int lane = lane_id(), sub = lane >> w.lsh, cl = lane & (w.lpr - 1);
+    const bool fast = w.lpr == 64 && (w.W.nch & 63) == 0 && w.ncb <= 8 && (w.ncb & (w.ncb - 1)) == 0;
+    float acc = 0.f, pend = 0.f;
+    for (int k0 = 0; k0 < w.nslots; k0 += kPF) {
+        if (!prefetched || k0 > 0) wload<DT>(w, rmap, roff, k0, pf);
+        const int k0s = opaque_s(k0);
+        if (fast)
+            wbatch_fast<DT, EM>(w, rmap, roff, xs, pf, k0s, lane, ea, best, best_i, nonfinite);
+        else
+            wbatch<DT, EM, false>(w, rmap, roff, xs, pf, k0s, lane, sub, cl, ea, acc, pend, best, best_i, nonfinite);
+    }
+}
+
+// ------------------------------------------------------------------ attention
+// Splits of the P = pos + 1 cached positions of one KV head: S splits of CH
+// positions (the last one shorter), S chosen so that the group's items (its KV
+// heads times S) cover its blocks, with at least 16 positions per split.
+__device__ __forceinline__ void attn_splits(int P, int bg, int n_kv_heads, int& S, int& CH) {
+    const int nh_max = (n_kv_heads + kNG - 1) / kNG;
+    S = bg / nh_max;
+    const int smax = (P + 15) / 16;
+    if (S > smax) S = smax;
     if (S > kStepMaxSplit) S = kStepMaxSplit;
+    if (S < 1) S = 1;
     CH = (P + S - 1) / S;
-    CH = (CH + 15) & ~15;
     S = (P + CH - 1) / CH;
 }
 
-// ------------------------------------------------------------------ phases
-template <int DT>
-__device__ void phase_qkv(const StepArgs& a, const LayerW& L, int layer, int pos, int tok, const float* xin,
-                          float* x0, float* qkv, float* xs, double* red) {
-    if (layer == 0)
-        stage_c<DT, 2>(nullptr, &a.embd, tok, x0, L.attn_norm, a.eps, a.dim, xs, red);
-    else
-        stage_c<DT, 1>(xin, nullptr, 0, nullptr, L.attn_norm, a.eps, a.dim, xs, red);
-    const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * kSW + (threadIdx.x >> 6), nw = gridDim.x * kSW;
-    const int hd = a.head_dim, hp = hd / 2, half = a.n_rot / 2;
-    const int qd = a.n_heads * hd, kvd = a.n_kv_heads * hd;
-    const int npairs = (qd + 2 * kvd) / 2;
-    __half* kc = a.kc + (size_t)layer * a.kv_layer;
-    __half* vc = a.vc + (size_t)layer * a.kv_layer;
-    constexpr int U = DT == DT_Q8 ? 8 : 4;
-    for (int pi = gw; pi < npairs; pi += nw) {
-        const int head = pi / hp, j = pi % hp;
-        int rows[2];
-        if (j < half) {
-            rows[0] = head * hd + (a.neox ? j : 2 * j);
-            rows[1] = a.neox ? rows[0] + half : rows[0] + 1;
-        } else {
-            rows[0] = head * hd + a.n_rot + 2 * (j - half);
-            rows[1] = rows[0] + 1;
-        }
-        float acc[2];
-        gemv_group<DT, 2, U>(L.qkv, rows, xs, acc);
-        if (lane == 0) {
-            const int ra = rows[0], rb = rows[1];
-            float va = acc[0], vb = acc[1];
-            if (L.bqkv) {
-                va += L.bqkv[ra];
-                vb += L.bqkv[rb];
-            }
-            if (head < a.n_heads + a.n_kv_heads && j < half) {
-                const float2 rv = rope_rotate(va, vb, a.rope[(size_t)pos * half + j]);
-                va = rv.x;
-                vb = rv.y;
-            }
-            stc(qkv + ra, va);
-            stc(qkv + rb, vb);
-            if (ra >= qd) {
-                const bool isk = ra < qd + kvd;
-                const int off = ra - qd - (isk ? 0 : kvd), offb = rb - qd - (isk ? 0 : kvd);
-                const int g = off / hd;
-                __half* row = (isk ? kc : vc) + ((size_t)g * a.n_ctx + pos) * hd;
-                row[off % hd] = f2h(va);
-                row[offb % hd] = f2h(vb);
-            }
-        }
+// Loads of the K and V rows a thread needs for positions c0 + pg + i*PPI of KV
+// head g; rows past the split are clamped to row pos (their values are not
+// used; row pos itself is substituted from the q|k|v buffer).
+__device__ __forceinline__ void attn_kv_load(const StepArgs& a, int layer, int g, int c0, int pos,
+                                             u32x4 (&kr)[kAttnSteps], u32x4 (&vr)[kAttnSteps]) {
+    const int hd = a.head_dim, LPP = attn_lpp(hd), PPI = kSB / LPP;
+    const int tid = thread_id(), sub = tid % LPP, pg = tid / LPP;
+    const int sub8 = sub * 8 < hd ? sub * 8 : 0;
+    const __half* kb = a.kc + (size_t)layer * a.kv_layer + (size_t)g * a.n_ctx * hd + sub8;
+    const __half* vb = a.vc + (size_t)layer * a.kv_layer + (size_t)g * a.n_ctx * hd + sub8;
+#pragma unroll
+    for (int i = 0; i < kAttnSteps; i++) {
+        const int t = min(c0 + pg + i * PPI, pos);
+        kr[i] = ld16(kb + (size_t)t * hd);
+        vr[i] = ld16(vb + (size_t)t * hd);
     }
 }
 
-// Attention splits (see k_attn): item = kv_head * S + split writes that split's
-// (m, l, unnormalised o) for the G query heads of its KV head. Row `pos` is
-// taken from the q|k|v buffer of this step, rounded to binary16 as stored.
-template <int G>
-__device__ void phase_attn(const StepArgs& a, int layer, int pos, const float* qkv, float* part, float* sm,
-                           float* m_run, float* l_run, float* alpha) {
-    const int hd = a.head_dim, P = pos + 1;
-    int S, CH;
-    attn_splits(P, S, CH);
+// The block's items (KV head g, split s) of the group: scaled scores, softmax
+// and the weighted sum of V over the split's positions ("The Forward Pass in
+// Java", Example 7), kept as (running max m, sum l, unnormalised o) per query
+// head of g and written to part[((g*S + s)*G + h)*(hd + 2)]: m, l, o[hd]. The
+// G query heads of g are taken GC at a time.
+template <int GC>
+__device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos, const float* qkv, float* part,
+                                           int hlo, int nh, int S, int CH, int rk, int bg,
+                                           u32x4 (&kr)[kAttnSteps], u32x4 (&vr)[kAttnSteps], float* sm,
+                                           float* m_run, float* l_run, float* alpha) {
+    const int hd = a.head_dim, P = pos + 1, G = a.n_heads / a.n_kv_heads;
     const int qd = a.n_heads * hd, kvd = a.n_kv_heads * hd;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
     const int LPP = attn_lpp(hd), PPI = kSB / LPP, CHUNK = PPI * kAttnSteps;
     const int sub = tid % LPP, pg = tid / LPP;
     const bool dim_ok = sub * 8 < hd;
-    float* sc = sm;                   // [G][CHUNK]
-    float* wred = sm + G * CHUNK;     // [kSW][G][hd]
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    const int sub8 = dim_ok ? sub * 8 : 0;
+    float* sc = sm;                 // [GC][CHUNK]
+    float* wred = sm + GC * CHUNK;  // [kSW][GC][hd]
+    bool have = true;               // the first chunk of the first item is prefetched
 
-    for (int item = blockIdx.x; item < a.n_kv_heads * S; item += gridDim.x) {
-        const int g = item / S, s = item % S;
+    for (int item = rk; item < nh * S; item += bg) {
+        const int g = hlo + item / S, s = item % S;
         const int t_begin = s * CH, t_end = min(P, t_begin + CH);
-        float qv[G][8], acc[G][8];
-#pragma unroll
-        for (int h = 0; h < G; h++)
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                qv[h][i] = dim_ok ? qkv[(g * G + h) * hd + sub * 8 + i] : 0.f;
-                acc[h][i] = 0.f;
-            }
-        __syncthreads();
-        if (tid < G) {
-            m_run[tid] = -INFINITY;
-            l_run[tid] = 0.f;
+        // this step's K and V row (the split that holds pos), rounded to
+        // binary16 as the cache stores them, loaded once per item
+        u32x4 kpos = {0u, 0u, 0u, 0u}, vpos = {0u, 0u, 0u, 0u};
+        if (pos >= t_begin && pos < t_end) {
+            const float4 k0 = ldf4(qkv + qd + g * hd + sub8), k1 = ldf4(qkv + qd + g * hd + sub8 + 4);
+            const float4 v0 = ldf4(qkv + qd + kvd + g * hd + sub8), v1 = ldf4(qkv + qd + kvd + g * hd + sub8 + 4);
+            auto pk = [](float lo, float hi) {
+                return (uint32_t)__half_as_ushort(f2h(lo)) | ((uint32_t)__half_as_ushort(f2h(hi)) << 16);
+            };
+            kpos = (u32x4){pk(k0.x, k0.y), pk(k0.z, k0.w), pk(k1.x, k1.y), pk(k1.z, k1.w)};
+            vpos = (u32x4){pk(v0.x, v0.y), pk(v0.z, v0.w), pk(v1.x, v1.y), pk(v1.z, v1.w)};
         }
-        const __half* kbase = a.kc + (size_t)layer * a.kv_layer + (size_t)g * a.n_ctx * hd + sub * 8;
-        const __half* vbase = a.vc + (size_t)layer * a.kv_layer + (size_t)g * a.n_ctx * hd + sub * 8;
-        for (int c0 = t_begin; c0 < t_end; c0 += CHUNK) {
-            const int cn = min(CHUNK, t_end - c0);
-            u32x4 kr[kAttnSteps], vr[kAttnSteps];
+        for (int h0 = 0; h0 < G; h0 += GC) {
+            float qv[GC][8], acc[GC][8];
 #pragma unroll
-            for (int i = 0; i < kAttnSteps; i++) {
-                const int t = pg + i * PPI;
-                const bool ok = dim_ok && t < cn;
-                if (ok && c0 + t == pos) {
-                    uint32_t kw[4], vw[4];
+            for (int h = 0; h < GC; h++) {
+                const float4 a0 = ldf4(qkv + ((g * G + h0 + h) * hd + sub8));
+                const float4 a1 = ldf4(qkv + ((g * G + h0 + h) * hd + sub8 + 4));
+                const float f = dim_ok ? 1.f : 0.f;
+                qv[h][0] = a0.x * f;
+                qv[h][1] = a0.y * f;
+                qv[h][2] = a0.z * f;
+                qv[h][3] = a0.w * f;
+                qv[h][4] = a1.x * f;
+                qv[h][5] = a1.y * f;
+                qv[h][6] = a1.z * f;
+                qv[h][7] = a1.w * f;
 #pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const float* kp = qkv + qd + g * hd + sub * 8 + 2 * q;
-                        const float* vp = qkv + qd + kvd + g * hd + sub * 8 + 2 * q;
-                        kw[q] = (uint32_t)__half_as_ushort(f2h(kp[0])) | ((uint32_t)__half_as_ushort(f2h(kp[1])) << 16);
-                        vw[q] = (uint32_t)__half_as_ushort(f2h(vp[0])) | ((uint32_t)__half_as_ushort(f2h(vp[1])) << 16);
-                    }
-                    kr[i] = (u32x4){kw[0], kw[1], kw[2], kw[3]};
-                    vr[i] = (u32x4){vw[0], vw[1], vw[2], vw[3]};
-                } else {
-                    kr[i] = ok ? *(const u32x4*)(kbase + (size_t)(c0 + t) * hd) : z4;
-                    vr[i] = ok ? *(const u32x4*)(vbase + (size_t)(c0 + t) * hd) : z4;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < kAttnSteps; i++) {
-                const int t = pg + i * PPI;
-                float kf[8];
-                unpack8(kr[i], kf);
-#pragma unroll
-                for (int h = 0; h < G; h++) {
-                    float d = 0.f;
-#pragma unroll
-                    for (int j = 0; j < 8; j++) d += qv[h][j] * kf[j];
-                    for (int o = 1; o < LPP; o <<= 1) d += __shfl_xor(d, o, 64);
-                    if (sub == 0 && t < cn) sc[h * CHUNK + t] = d / a.scale_div;
-                }
+                for (int i = 0; i < 8; i++) acc[h][i] = 0.f;
             }
             __syncthreads();
-            for (int h = wave; h < G; h += kSW) {
-                float mx = -INFINITY;
-                for (int t = lane; t < cn; t += 64) mx = fmaxf(mx, sc[h * CHUNK + t]);
-                mx = wave_max(mx);
-                const float m_old = m_run[h];
-                const float m_new = fmaxf(m_old, mx);
-                float ls = 0.f;
-                for (int t = lane; t < cn; t += 64) {
-                    const float e = expf(sc[h * CHUNK + t] - m_new);
-                    sc[h * CHUNK + t] = e;
-                    ls += e;
-                }
-                ls = wave_sum(ls);
-                if (lane == 0) {
-                    const float al = (m_old == -INFINITY) ? 0.f : expf(m_old - m_new);
-                    alpha[h] = al;
-                    l_run[h] = l_run[h] * al + ls;
-                    m_run[h] = m_new;
-                }
+            if (tid < GC) {
+                m_run[tid] = -INFINITY;
+                l_run[tid] = 0.f;
             }
-            __syncthreads();
+            for (int c0 = t_begin; c0 < t_end; c0 += CHUNK) {
+                const int cn = min(CHUNK, t_end - c0);
+                if (!have) attn_kv_load(a, layer, g, c0, pos, kr, vr);
+                have = false;
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                const float al = alpha[h];
-#pragma unroll
-                for (int i = 0; i < 8; i++) acc[h][i] *= al;
-            }
-#pragma unroll
-            for (int i = 0; i < kAttnSteps; i++) {
-                const int t = pg + i * PPI;
-                if (dim_ok && t < cn) {
-                    float vf[8];
-                    unpack8(vr[i], vf);
-#pragma unroll
-                    for (int h = 0; h < G; h++) {
-                        const float w = sc[h * CHUNK + t];
-#pragma unroll
-                        for (int j = 0; j < 8; j++) acc[h][j] += w * vf[j];
+                for (int i = 0; i < kAttnSteps; i++) {
+                    const int t = pg + i * PPI;
+                    if (t < cn && c0 + t == pos) {
+                        kr[i] = kpos;
+                        vr[i] = vpos;
                     }
                 }
+#pragma unroll
+                for (int i = 0; i < kAttnSteps; i++) {
+                    const int t = pg + i * PPI;
+                    float kf[8];
+                    unpack8(kr[i], kf);
+#pragma unroll
+                    for (int h = 0; h < GC; h++) {
+                        float d = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 8; j++) d += qv[h][j] * kf[j];
+                        for (int o = 1; o < LPP; o <<= 1) d += __shfl_xor(d, o, 64);
+                        if (sub == 0 && t < cn) sc[h * CHUNK + t] = d / a.scale_div;
+                    }
+                }
+                __syncthreads();
+                for (int h = wave; h < GC; h += kSW) {
+                    float mx = -INFINITY;
+                    for (int t = lane; t < cn; t += 64) mx = fmaxf(mx, sc[h * CHUNK + t]);
+                    mx = wave_max(mx);
+                    const float m_old = m_run[h];
+                    const float m_new = fmaxf(m_old, mx);
+                    float ls = 0.f;
+                    for (int t = lane; t < cn; t += 64) {
+                        const float e = expf(sc[h * CHUNK + t] - m_new);
+                        sc[h * CHUNK + t] = e;
+                        ls += e;
+                    }
+                    ls = wave_sum(ls);
+                    if (lane == 0) {
+                        const float al = (m_old == -INFINITY) ? 0.f : expf(m_old - m_new);
+                        alpha[h] = al;
+                        l_run[h] = l_run[h] * al + ls;
+                        m_run[h] = m_new;
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int h = 0; h < GC; h++) {
+                    const float al = alpha[h];
+#pragma unroll
+                    for (int i = 0; i < 8; i++) acc[h][i] *= al;
+                }
+#pragma unroll
+                for (int i = 0; i < kAttnSteps; i++) {
+                    const int t = pg + i * PPI;
+                    if (dim_ok && t < cn) {
+                        float vf[8];
+                        unpack8(vr[i], vf);
+#pragma unroll
+                        for (int h = 0; h < GC; h++) {
+                            const float wgt = sc[h * CHUNK + t];
+#pragma unroll
+                            for (int j = 0; j < 8; j++) acc[h][j] += wgt * vf[j];
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+            if (h0 + GC < G) have = false;  // the next pass reloads K and V
+#pragma unroll
+            for (int h = 0; h < GC; h++)
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    float v = acc[h][i];
+                    for (int o = LPP; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+                    acc[h][i] = v;
+                }
+            if (lane < LPP && dim_ok)
+#pragma unroll
+                for (int h = 0; h < GC; h++)
+#pragma unroll
+                    for (int i = 0; i < 8; i++) wred[(wave * GC + h) * hd + sub8 + i] = acc[h][i];
+            __syncthreads();
+            const int GH = GC * hd, stride = hd + 2;
+            float* mypart = part + (((size_t)g * S + s) * G + h0) * (size_t)stride;
+            for (int e = tid; e < GH; e += kSB) {
+                float o = 0.f;
+#pragma unroll
+                for (int w = 0; w < kSW; w++) o += wred[w * GH + e];
+                stc(mypart + (e / hd) * stride + 2 + (e % hd), o);
+            }
+            if (tid < GC) {
+                stc(mypart + tid * stride, m_run[tid]);
+                stc(mypart + tid * stride + 1, l_run[tid]);
             }
             __syncthreads();
         }
-#pragma unroll
-        for (int h = 0; h < G; h++)
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                float v = acc[h][i];
-                for (int o = LPP; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-                acc[h][i] = v;
-            }
-        if (lane < LPP && dim_ok)
-#pragma unroll
-            for (int h = 0; h < G; h++)
-#pragma unroll
-                for (int i = 0; i < 8; i++) wred[(wave * G + h) * hd + sub * 8 + i] = acc[h][i];
-        __syncthreads();
-        const int GH = G * hd, stride = hd + 2;
-        float* mypart = part + ((size_t)g * S + s) * (size_t)(G * stride);
-        for (int e = tid; e < GH; e += kSB) {
-            float o = 0.f;
-#pragma unroll
-            for (int w = 0; w < kSW; w++) o += wred[w * GH + e];
-            stc(mypart + (e / hd) * stride + 2 + (e % hd), o);
-        }
-        if (tid < G) {
-            stc(mypart + tid * stride, m_run[tid]);
-            stc(mypart + tid * stride + 1, l_run[tid]);
-        }
-        __syncthreads();
     }
 }
 
-// Output stage: every block merges the attention splits of all heads into the
-// staged input (M = max m_s, L = sum l_s e^(m_s - M), o = sum o_s e^(m_s - M) /
-// L, splits in order), then x_mid[r] = x_in[r] + W_o o for its rows.
-template <int DT, int G>
-__device__ void phase_o(const StepArgs& a, const LayerW& L, int pos, const float* part, const float* xprev,
-                        float* xnext, float* xs, float* wsp) {
-    const int hd = a.head_dim, H = a.n_heads, qd = H * hd, stride = hd + 2;
-    int S, CH;
-    attn_splits(pos + 1, S, CH);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // per (head, split) weights e^(m_s - M) / L into wsp[h * S + s]
-    for (int h = wave; h < H; h += kSW) {
-        const int g = h / G, hl = h % G;
+// Merge of the splits of the group's query heads into xs (swizzled for DT,
+// element hl*hd + d for local head hl): with M = max_s m_s and L = sum_s l_s
+// e^(m_s - M), o = sum_s o_s e^(m_s - M) / L.
+template <int DT>
+__device__ __forceinline__ void merge_splits(const StepArgs& a, const float* part, int hlo, int nh, int S, float* xs, float* wsp,
+                             float* ored) {
+    const int hd = a.head_dim, G = a.n_heads / a.n_kv_heads, stride = hd + 2;
+    const int NHL = nh * G, E = NHL * hd;
+    const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
+    // o loads first (they do not depend on the weights), then the weights
+    const int nsl = E <= kSB ? kSB / E : 1;
+    const int e = E <= kSB ? tid % E : tid, sl = E <= kSB ? tid / E : 0;
+    constexpr int kU = 16;
+    float ov[kU];
+    int hl = 0, d = 0;
+    const float* po = part;
+    const bool act = E <= kSB && sl < nsl;
+    if (act) {
+        hl = e / hd;
+        d = e - hl * hd;
+        const int g = hlo + hl / G, h = hl % G;
+        po = part + ((size_t)g * S * G + h) * stride + 2 + d;
+#pragma unroll
+        for (int i = 0; i < kU; i++) {
+            const int s = sl + i * nsl;
+            ov[i] = s < S ? ldf(po + (size_t)s * G * stride) : 0.f;
+        }
+    }
+    for (int h2 = wave; h2 < NHL; h2 += kSW) {
+        const int g = hlo + h2 / G, h = h2 % G;
         float m = -INFINITY, l = 0.f;
         if (lane < S) {
-            const float* pj = part + ((size_t)g * S + lane) * (size_t)(G * stride) + hl * stride;
-            m = pj[0];
-            l = pj[1];
+            const float* pj = part + (((size_t)g * S + lane) * G + h) * stride;
+            m = ldf(pj);
+            l = ldf(pj + 1);
         }
         const float M = wave_max(m);
         const float f = lane < S ? expf(m - M) : 0.f;
         const float Lh = wave_sum(l * f);
-        if (lane < S) wsp[h * S + lane] = f / Lh;
+        if (lane < S) wsp[h2 * S + lane] = f / Lh;
     }
     __syncthreads();
-    for (int e = tid; e < qd; e += kSB) {
-        const int h = e / hd, d = e % hd, g = h / G, hl = h % G;
-        const float* po = part + (size_t)g * S * (size_t)(G * stride) + hl * stride + 2 + d;
-        float o = 0.f;
-        for (int s = 0; s < S; s++) o += wsp[h * S + s] * po[(size_t)s * G * stride];
-        xs[swz<DT>(e)] = o;
-    }
-    __syncthreads();
-    const int gw = blockIdx.x * kSW + wave, nw = gridDim.x * kSW;
-    constexpr int U = DT == DT_Q8 ? 8 : 4;
-    for (int r = gw; r < L.o.rows; r += nw) {
-        const int rows[1] = {r};
-        float acc[1];
-        gemv_group<DT, 1, U>(L.o, rows, xs, acc);
-        if (lane == 0) stc(xnext + r, xprev[r] + acc[0]);
-    }
-}
-
-// x_out[r] = x_mid[r] + W_down u for the block's rows.
-template <int DT>
-__device__ void phase_down(const StepArgs& a, const Mat& W, const float* u, const float* xprev, float* xnext,
-                           float* xs, double* red) {
-    stage_c<DT, 0>(u, nullptr, 0, nullptr, nullptr, 0.f, W.cols, xs, red);
-    const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * kSW + (threadIdx.x >> 6), nw = gridDim.x * kSW;
-    constexpr int U = DT == DT_Q8 ? 8 : 4;
-    for (int r = gw; r < W.rows; r += nw) {
-        const int rows[1] = {r};
-        float acc[1];
-        gemv_group<DT, 1, U>(W, rows, xs, acc);
-        if (lane == 0) stc(xnext + r, xprev[r] + acc[0]);
-    }
-}
-
-template <int DT>
-__device__ void phase_gateup(const StepArgs& a, const LayerW& L, const float* xin, float* u, float* xs, double* red) {
-    stage_c<DT, 1>(xin, nullptr, 0, nullptr, L.ffn_norm, a.eps, a.dim, xs, red);
-    const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * kSW + (threadIdx.x >> 6), nw = gridDim.x * kSW;
-    const int ng = L.gu.rows / 4;
-    for (int g = gw; g < ng; g += nw) {
-        const int rows[4] = {4 * g, 4 * g + 1, 4 * g + 2, 4 * g + 3};
-        float acc[4];
-        gemv_group<DT, 4, 4>(L.gu, rows, xs, acc);
-        if (lane == 0) {
-            stc(u + 2 * g, silu(acc[0]) * acc[1]);
-            stc(u + 2 * g + 1, silu(acc[2]) * acc[3]);
-        }
-    }
-}
-
-template <int DT>
-__device__ void phase_logits(const StepArgs& a, const float* xin, float* xs, double* red, ArgPart* wbest) {
-    stage_c<DT, 1>(xin, nullptr, 0, nullptr, a.out_norm, a.eps, a.dim, xs, red);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int gw = blockIdx.x * kSW + wave, nw = gridDim.x * kSW;
-    const int R = a.out.rows, ng = (R + 3) / 4;
-    float best = -INFINITY;
-    int best_i = 0x7fffffff, nonfinite = 0;
-    for (int g = gw; g < ng; g += nw) {
-        const int rows[4] = {4 * g, 4 * g + 1, 4 * g + 2, 4 * g + 3};
-        float acc[4];
-        gemv_group<DT, 4, 4>(a.out, rows, xs, acc);
-        if (lane == 0) {
+    if (E <= kSB) {
+        if (act) {
+            float o = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (rows[i] < R) {
-                    const float v = acc[i];
-                    a.logits[rows[i]] = v;
-                    if (!isfinite(v)) nonfinite = 1;
-                    if (v > best) {  // rows arrive in increasing order: ties keep the first
-                        best = v;
-                        best_i = rows[i];
-                    }
-                }
+            for (int i = 0; i < kU; i++) {
+                const int s = sl + i * nsl;
+                if (s < S) o += wsp[hl * S + s] * ov[i];
             }
+            for (int s = sl + kU * nsl; s < S; s += nsl) o += wsp[hl * S + s] * ldf(po + (size_t)s * G * stride);
+            ored[sl * E + e] = o;
+        }
+        __syncthreads();
+        if (tid < E) {
+            float o = 0.f;
+            for (int k = 0; k < nsl; k++) o += ored[k * E + tid];
+            xs[swz<DT>(tid)] = o;
+        }
+    } else {
+        for (int e2 = tid; e2 < E; e2 += kSB) {
+            const int hl2 = e2 / hd, d2 = e2 - hl2 * hd;
+            const int g = hlo + hl2 / G, h = hl2 % G;
+            const float* p2 = part + ((size_t)g * S * G + h) * stride + 2 + d2;
+            float o = 0.f;
+            for (int s = 0; s < S; s++) o += wsp[hl2 * S + s] * ldf(p2 + (size_t)s * G * stride);
+            xs[swz<DT>(e2)] = o;
         }
     }
-    if (lane == 0) wbest[wave] = ArgPart{best, best_i, nonfinite, 0};
+    __syncthreads();
+}
+
+// --------------------------------------------------------------------- logits
+template <int DT>
+__device__ __forceinline__ void logits_phase(const StepArgs& a, const float* xr, float* xs, double* red,
+                                             ArgPart* wbest) {
+    stage_norm<DT>(xr, a.out_norm, a.eps, a.dim, xs, red);
+    const int lane = thread_id() & 63, wave = thread_id() >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(blockIdx.x * kSW + wave);
+    WRows w = wave_rows(a.out.rows, gridDim.x * kSW, wv, a.dim / VecW<DT>::VE, false);
+    w.W = make_win<DT>(a.out, 0, a.dim);
+    EmitArgs ea{};
+    ea.out = a.logits;
+    float best = -INFINITY;
+    int bi = 0x7fffffff, nf = 0;
+    PF pf;
+    wrun<DT, EM_ARGMAX>(w, nullptr, 0, xs, pf, false, ea, best, bi, nf);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ob > best || (ob == best && oi < bi)) {
+            best = ob;
+            bi = oi;
+        }
+    }
+    const int anynf = __any(nf);
+    if (lane == 0) wbest[wave] = ArgPart{best, bi, anynf, 0};
     __syncthreads();
     if (threadIdx.x == 0) {
         ArgPart b = wbest[0];
-        for (int w = 1; w < kSW; w++) {
-            const ArgPart o = wbest[w];
+        for (int k = 1; k < kSW; k++) {
+            const ArgPart o = wbest[k];
             if (o.val > b.val || (o.val == b.val && o.idx < b.idx)) {
                 b.val = o.val;
                 b.idx = o.idx;
@@ -477,7 +849,8 @@ __device__ void phase_logits(const StepArgs& a, const float* xin, float* xs, dou
     }
 }
 
-template <int G>
+// --------------------------------------------------------------------- kernel
+template <int DT>
 __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     extern __shared__ float sm[];
     __shared__ double red[kSW];
@@ -486,54 +859,188 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
 
     State* st = a.st;
     const int pos = st->pos, tok = st->token, epoch = st->epoch;
-    const unsigned long long nb = (unsigned long long)kStepPhases * a.n_layers + 1;
-    unsigned long long bar = (unsigned long long)epoch * nb;
-    int phase = 0;
-    if (a.trace && blockIdx.x == 0 && threadIdx.x == 0) a.trace[0] = wall_clock64();
-#define STEP_SYNC()                                                                          \
-    do {                                                                                     \
-        grid_sync(st, a.bar, ++bar);                                                         \
-        ++phase;                                                                             \
-        if (a.trace && blockIdx.x == 0 && threadIdx.x == 0) a.trace[phase] = wall_clock64(); \
-    } while (0)
-#define BY_DTYPE(M, CALL)                 \
-    switch ((M).dtype) {                  \
-        case DT_F32: CALL(DT_F32); break; \
-        case DT_F16: CALL(DT_F16); break; \
-        default: CALL(DT_Q8); break;      \
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int x = blockIdx.x % kNG, rk = blockIdx.x / kNG, bg = gridDim.x / kNG;
+    const int gwv = __builtin_amdgcn_readfirstlane(rk * kSW + wave), GW = bg * kSW;
+    const int hd = a.head_dim, G = a.n_heads / a.n_kv_heads;
+    const int qd = a.n_heads * hd, kvd = a.n_kv_heads * hd;
+    const int hlo = x * a.n_kv_heads / kNG, nh = (x + 1) * a.n_kv_heads / kNG - hlo;
+    const int nbk = a.ffn / 32, flo = x * nbk / kNG * 32, nf = (x + 1) * nbk / kNG * 32 - flo;
+    unsigned hmask = 0, fmask = 0;  // groups that own heads / hidden units
+    for (int g = 0; g < kNG; g++) {
+        if ((g + 1) * a.n_kv_heads / kNG > g * a.n_kv_heads / kNG) hmask |= 1u << g;
+        if ((g + 1) * nbk / kNG > g * nbk / kNG) fmask |= 1u << g;
     }
+    int S, CH;
+    attn_splits(pos + 1, bg, a.n_kv_heads, S, CH);
+    constexpr int VE = VecW<DT>::VE;
 
-    // LDS: the staged input vector; the output stage keeps its split weights
-    // past the largest attention output it stages.
-    float* wsp = sm + lds_floats<DT_Q8>(a.n_heads * a.head_dim);
+    float* xr = sm;                        // this block's copy of the residual stream
+    float* xs = sm + a.lds_xr;             // staged product input, or attention scratch
+    float* wsp = xs + a.lds_xs;            // split weights of the merge
+    float* ored = wsp + a.lds_wsp;         // merge partial sums [kSB]
+    float2* cs = (float2*)(ored + kSB);    // RoPE (cos, sin) of this position, kMaxHeadDim/2 pairs
+    int* qmap = (int*)(cs + kMaxHeadDim / 2);  // the group's q/k/v rows in RoPE-pair order
+
+    const unsigned long long nloc = 3ull * a.n_layers, ncro = 2ull * a.n_layers + 1;
+    unsigned long long jl = (unsigned long long)epoch * nloc, jc = (unsigned long long)epoch * ncro;
+    int phase = 0;
+    const bool tr = a.trace && blockIdx.x == 0 && tid == 0;
+    if (tr) a.trace[0] = wall_clock64();
+#define STAMP()                                  \
+    do {                                         \
+        ++phase;                                 \
+        if (tr) a.trace[phase] = wall_clock64(); \
+    } while (0)
+
+    // Rows 2p, 2p+1 of the group's q/k/v share are the two rows RoPE pair p
+    // rotates together ("The Forward Pass in Java", Example 6: (2j, 2j+1) in
+    // the normal layout, (j, j + n_rot/2) in the NEOX one; dimensions past
+    // n_rot pair up unrotated). Pairs run over the group's KV heads, each as
+    // its G query heads, then its key and its value head.
+    const int n_qkv = nh * (G + 2) * hd, half = a.n_rot / 2;
+    for (int p = tid; p < n_qkv / 2; p += kSB) {
+        const int hp = hd / 2, hh = p / hp, j = p - hh * hp;
+        const int i = hh / (G + 2), sub = hh - i * (G + 2), kvh = hlo + i;
+        const int base = sub < G ? (kvh * G + sub) * hd : (sub == G ? qd + kvh * hd : qd + kvd + kvh * hd);
+        int ra, rb;
+        if (j < half) {
+            ra = base + (a.neox ? j : 2 * j);
+            rb = a.neox ? ra + half : ra + 1;
+        } else {
+            ra = base + a.n_rot + 2 * (j - half);
+            rb = ra + 1;
+        }
+        qmap[2 * p] = ra;
+        qmap[2 * p + 1] = rb;
+    }
+    for (int i = tid; i < a.dim; i += kSB) xr[i] = mat_elem(a.embd, tok, i);
+    for (int j = tid; j < half; j += kSB) {
+        const float* c = (const float*)(a.rope + ((size_t)pos * half + j));
+        cs[j] = make_float2(ldf(c), ldf(c + 1));
+    }
+    __syncthreads();
+
+    WRows wq = wave_rows(n_qkv, GW, gwv, a.dim / VE, true);
+    WRows wo = wave_rows(nh > 0 ? a.dim : 0, GW, gwv, nh * G * hd / VE, false);
+    WRows wg = wave_rows(2 * nf, GW, gwv, a.dim / VE, true);
+    WRows wd = wave_rows(nf > 0 ? a.dim : 0, GW, gwv, nf / VE, false);
+    EmitArgs ea{};
+    ea.cs = cs;
+    ea.pos = pos;
+    ea.n_ctx = a.n_ctx;
+    ea.hd = hd;
+    ea.qd = qd;
+    ea.kvd = kvd;
+    ea.half = half;
+    ea.n_rot = a.n_rot;
+    ea.neox = a.neox;
+    float best = 0.f;
+    int bi = 0, nfin = 0;
+
+    PF pf;
+    u32x4 kr[kAttnSteps], vr[kAttnSteps];
+    LayerW L = a.layers[0];
+    wq.W = make_win<DT>(L.qkv, 0, a.dim);
+    wload<DT>(wq, qmap, 0, 0, pf);
+    pin();
+
     for (int l = 0; l < a.n_layers; l++) {
-        const LayerW L = a.layers[l];
-        const float* x_in = a.xv + (size_t)(2 * l) * a.xstride;  // residual entering the layer
-        float* x_mid = a.xv + (size_t)(2 * l + 1) * a.xstride;   // after attention
-        float* x_out = a.xv + (size_t)(2 * l + 2) * a.xstride;   // after the FFN
         float* qkv = a.qkv + (size_t)l * a.qkv_stride;
         float* part = a.part + (size_t)l * a.part_stride;
         float* u = a.u + (size_t)l * a.u_stride;
-#define QKV(D) phase_qkv<D>(a, L, l, pos, tok, x_in, a.xv, qkv, sm, red)
-        BY_DTYPE(L.qkv, QKV)
-        STEP_SYNC();
-        phase_attn<G>(a, l, pos, qkv, part, sm, m_run, l_run, alpha);
-        STEP_SYNC();
-#define OPROJ(D) phase_o<D, G>(a, L, pos, part, x_in, x_mid, sm, wsp)
-        BY_DTYPE(L.o, OPROJ)
-        STEP_SYNC();
-#define GATEUP(D) phase_gateup<D>(a, L, x_mid, u, sm, red)
-        BY_DTYPE(L.gu, GATEUP)
-        STEP_SYNC();
-#define DOWN(D) phase_down<D>(a, L.down, u, x_mid, x_out, sm, red)
-        BY_DTYPE(L.down, DOWN)
-        STEP_SYNC();
+        float* po = a.po + (size_t)l * kNG * a.pstride;
+        float* pd = a.pd + (size_t)l * kNG * a.pstride;
+
+        // ---- QKV
+        stage_norm<DT>(xr, L.attn_norm, a.eps, a.dim, xs, red);
+        ea.out = qkv;
+        ea.bias = L.bqkv;
+        ea.kc = a.kc + (size_t)l * a.kv_layer;
+        ea.vc = a.vc + (size_t)l * a.kv_layer;
+        wrun<DT, EM_QKV>(wq, qmap, 0, xs, pf, true, ea, best, bi, nfin);
+        wait_mem();
+        group_arrive(a, x);
+        if (rk < nh * S) {
+            attn_kv_load(a, l, hlo + rk / S, (rk % S) * CH, pos, kr, vr);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kAttnSteps; i++) kr[i] = vr[i] = (u32x4){0u, 0u, 0u, 0u};
+        }
+        pin();
+        group_wait(a, x, ++jl * bg);
+        STAMP();
+
+        // ---- attention
+        switch (G) {
+            case 1: attn_items<1>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+            case 2: attn_items<2>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+            default: attn_items<4>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+        }
+        wait_mem();
+        group_arrive(a, x);
+        wo.W = make_win<DT>(L.o, hlo * G * hd, nh * G * hd);
+        wload<DT>(wo, nullptr, 0, 0, pf);
+        pin();
+        group_wait(a, x, ++jl * bg);
+        STAMP();
+
+        // ---- split merge + output product (partial over the group's heads)
+        if (nh > 0) {
+            merge_splits<DT>(a, part, hlo, nh, S, xs, wsp, ored);
+            ea.out = po + (size_t)x * a.pstride;
+            wrun<DT, EM_PART>(wo, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
+        }
+        wait_mem();
+        all_arrive(a, x);
+        wg.W = make_win<DT>(L.gu, 0, a.dim);
+        wload<DT>(wg, nullptr, 2 * flo, 0, pf);
+        pin();
+        all_wait(a, ++jc * bg);
+        STAMP();
+
+        // ---- residual, RMSNorm, gate/up + SwiGLU
+        add_partials(xr, po, a.pstride, a.dim, hmask);
+        stage_norm<DT>(xr, L.ffn_norm, a.eps, a.dim, xs, red);
+        ea.out = u + flo;
+        wrun<DT, EM_SWIGLU>(wg, nullptr, 2 * flo, xs, pf, true, ea, best, bi, nfin);
+        wait_mem();
+        group_arrive(a, x);
+        wd.W = make_win<DT>(L.down, flo, nf);
+        wload<DT>(wd, nullptr, 0, 0, pf);
+        pin();
+        group_wait(a, x, ++jl * bg);
+        STAMP();
+
+        // ---- down product (partial over the group's hidden units)
+        if (nf > 0) {
+            stage_copy<DT>(u + flo, nf, xs);
+            ea.out = pd + (size_t)x * a.pstride;
+            wrun<DT, EM_PART>(wd, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
+        }
+        wait_mem();
+        all_arrive(a, x);
+        if (l + 1 < a.n_layers) {
+            L = a.layers[l + 1];
+            wq.W = make_win<DT>(L.qkv, 0, a.dim);
+            wload<DT>(wq, qmap, 0, 0, pf);
+        }
+        pin();
+        all_wait(a, ++jc * bg);
+        STAMP();
+        add_partials(xr, pd, a.pstride, a.dim, fmask);
     }
-    const float* x_last = a.xv + (size_t)(2 * a.n_layers) * a.xstride;
-#define LOGITS(D) phase_logits<D>(a, x_last, sm, red, wbest)
-    BY_DTYPE(a.out, LOGITS)
-    STEP_SYNC();
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+
+    switch (a.out.dtype) {
+        case DT_F32: logits_phase<DT_F32>(a, xr, xs, red, wbest); break;
+        case DT_F16: logits_phase<DT_F16>(a, xr, xs, red, wbest); break;
+        default: logits_phase<DT_Q8>(a, xr, xs, red, wbest); break;
+    }
+    wait_mem();
+    all_arrive(a, x);
+    all_wait(a, ++jc * bg);
+    STAMP();
+    if (blockIdx.x == 0 && tid == 0) {
         const unsigned long long k = __hip_atomic_load(&st->best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int next = k ? (int)(0xffffffffu - (uint32_t)(k & 0xffffffffull)) : 0;
         st->next = next;
@@ -547,71 +1054,74 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         __hip_atomic_store(&st->best, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         st->epoch = epoch + 1;
     }
-#undef STEP_SYNC
-#undef BY_DTYPE
-#undef QKV
-#undef OPROJ
-#undef GATEUP
-#undef DOWN
-#undef LOGITS
+#undef STAMP
 }
 
-static int step_lds_bytes(const StepArgs& a) {
-    int maxk = a.dim;
-    if (a.n_heads * a.head_dim > maxk) maxk = a.n_heads * a.head_dim;
-    if (a.ffn > maxk) maxk = a.ffn;
-    const int G = a.n_heads / a.n_kv_heads;
-    int f = lds_floats<DT_Q8>(maxk);  // the largest swizzle round-up of the three types
-    const int att = G * (kSB / attn_lpp(a.head_dim)) * kAttnSteps + kSW * G * a.head_dim;
-    const int ost = lds_floats<DT_Q8>(a.n_heads * a.head_dim) + a.n_heads * kStepMaxSplit;  // staged o + split weights
-    if (att > f) f = att;
-    if (ost > f) f = ost;
-    return f * (int)sizeof(float);
+
+// ------------------------------------------------------------------- host side
+// LDS sizes (floats) of the step kernel's regions for this shape, or false if
+// the shape is outside what the kernel handles.
+bool step_lds_plan(StepArgs& a, int dtype, int* lds_bytes) {
+    const int G = a.n_heads / a.n_kv_heads, hd = a.head_dim;
+    if (a.ffn % 32 || a.dim % 32 || (G * hd) % 32 || hd % 8 || hd > kMaxHeadDim) return false;
+    const int nh_max = (a.n_kv_heads + kNG - 1) / kNG;
+    const int nbk = a.ffn / 32, nf_max = ((nbk + kNG - 1) / kNG) * 32;
+    auto lds_any = [](int K) {
+        int m = lds_floats<DT_F32>(K);
+        if (lds_floats<DT_F16>(K) > m) m = lds_floats<DT_F16>(K);
+        if (lds_floats<DT_Q8>(K) > m) m = lds_floats<DT_Q8>(K);
+        return m;
+    };
+    (void)dtype;
+    int xs = lds_any(a.dim);
+    if (lds_any(nh_max * G * hd) > xs) xs = lds_any(nh_max * G * hd);
+    if (lds_any(nf_max) > xs) xs = lds_any(nf_max);
+    const int GC = G < 4 ? G : 4;
+    const int att = GC * (kSB / attn_lpp(hd)) * kAttnSteps + kSW * GC * hd;
+    if (att > xs) xs = att;
+    a.lds_xr = (a.dim + 63) / 64 * 64;
+    a.lds_xs = (xs + 63) / 64 * 64;
+    a.lds_wsp = (nh_max * G * kStepMaxSplit + 63) / 64 * 64;
+    const int qmap = nh_max * (G + 2) * hd;  // ints
+    const int total = a.lds_xr + a.lds_xs + a.lds_wsp + kSB + kMaxHeadDim + qmap;
+    *lds_bytes = total * (int)sizeof(float);
+    return *lds_bytes <= 150 * 1024;
 }
 
-template <int G>
-static int step_grid_g(const StepArgs& a, int lds) {
-    static bool attr_done = false;
-    if (!attr_done) {
-        if (hipFuncSetAttribute((const void*)k_step<G>, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+template <int DT>
+static int step_grid_t(int lds) {
+    static int attr_for = -1;
+    if (attr_for != lds) {
+        if (hipFuncSetAttribute((const void*)k_step<DT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
             return 0;
-        attr_done = true;
+        attr_for = lds;
     }
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_step<G>, kSB, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_step<DT>, kSB, lds) != hipSuccess)
         return 0;
-    return per_cu >= 1 ? cus : 0;
+    const int grid = cus / kNG * kNG;
+    return per_cu >= 1 && grid >= kNG ? grid : 0;
 }
 
-int step_grid(const StepArgs& a, int* lds_bytes) {
-    const int lds = step_lds_bytes(a);
-    *lds_bytes = lds;
-    switch (a.n_heads / a.n_kv_heads) {
-        case 1: return step_grid_g<1>(a, lds);
-        case 2: return step_grid_g<2>(a, lds);
-        case 4: return step_grid_g<4>(a, lds);
-        case 8: return step_grid_g<8>(a, lds);
+int step_grid(StepArgs& a, int dtype, int* lds_bytes) {
+    if (!step_lds_plan(a, dtype, lds_bytes)) return 0;
+    switch (dtype) {
+        case DT_F32: return step_grid_t<DT_F32>(*lds_bytes);
+        case DT_F16: return step_grid_t<DT_F16>(*lds_bytes);
+        case DT_Q8: return step_grid_t<DT_Q8>(*lds_bytes);
     }
     return 0;
 }
 
-template <int G>
-static hipError_t launch_step_g(const StepArgs& a, int grid, int lds, hipStream_t s) {
+hipError_t launch_step(const StepArgs& a, int dtype, int grid, int lds, hipStream_t s) {
     StepArgs arg = a;
     void* params[] = {&arg};
-    return hipLaunchCooperativeKernel((const void*)k_step<G>, dim3(grid), dim3(kSB), params, (unsigned)lds, s);
-}
-
-hipError_t launch_step(const StepArgs& a, int grid, int lds, hipStream_t s) {
-    switch (a.n_heads / a.n_kv_heads) {
-        case 1: return launch_step_g<1>(a, grid, lds, s);
-        case 2: return launch_step_g<2>(a, grid, lds, s);
-        case 4: return launch_step_g<4>(a, grid, lds, s);
-        case 8: return launch_step_g<8>(a, grid, lds, s);
-    }
-    return hipErrorInvalidValue;
+    const void* fn = dtype == DT_F32 ? (const void*)k_step<DT_F32>
+                     : dtype == DT_F16 ? (const void*)k_step<DT_F16>
+                                       : (const void*)k_step<DT_Q8>;
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kSB), params, (unsigned)lds, s);
 }
 
 }  // namespace llm

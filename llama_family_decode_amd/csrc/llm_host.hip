@@ -192,9 +192,9 @@ struct Layout {
     float *x, *q, *ao, *u, *logits, *attn_part;
     int *gen_out, *ptok;
     LayerW* dlayers;  // device copy of the layer table (persistent step kernel)
-    // versioned activations of the persistent step kernel (strides padded to 256 bytes)
-    float *sx, *sqkv, *sao, *spart, *su;
-    long long xstride, qkv_stride, ao_stride, part_stride, u_stride;
+    // per-layer activations of the persistent step kernel (strides padded to 256 bytes)
+    float *sqkv, *spart, *spo, *spd, *su;
+    long long qkv_stride, part_stride, u_stride, pstride;
     unsigned long long* sbar;
     unsigned long long* strace;
     float *X, *Hf, *QKV, *Q, *Of, *Uf;
@@ -263,17 +263,16 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.attn_part = (float*)S.take((size_t)kMaxSplit * c->n_kv_heads * G * (c->head_dim + 2) * 4);
     L.dlayers = (LayerW*)S.take((size_t)c->n_layers * sizeof(LayerW));
     auto pad64 = [](long long n) { return (n + 63) / 64 * 64; };
-    L.xstride = pad64(c->dim);
     L.qkv_stride = pad64(qd + 2 * kvd);
-    L.ao_stride = pad64(qd);
     L.part_stride = pad64((long long)kStepMaxSplit * c->n_kv_heads * G * (c->head_dim + 2));
     L.u_stride = pad64(c->ffn);
-    L.sx = (float*)S.take((size_t)(2 * c->n_layers + 1) * L.xstride * 4);
+    L.pstride = pad64(c->dim);
     L.sqkv = (float*)S.take((size_t)c->n_layers * L.qkv_stride * 4);
-    L.sao = (float*)S.take((size_t)c->n_layers * L.ao_stride * 4);
     L.spart = (float*)S.take((size_t)c->n_layers * L.part_stride * 4);
+    L.spo = (float*)S.take((size_t)c->n_layers * kStepGroups * L.pstride * 4);
+    L.spd = (float*)S.take((size_t)c->n_layers * kStepGroups * L.pstride * 4);
     L.su = (float*)S.take((size_t)c->n_layers * L.u_stride * 4);
-    L.sbar = (unsigned long long*)S.take((size_t)(kBarGroups + 1) * kBarStride * 8);
+    L.sbar = (unsigned long long*)S.take((size_t)kBarSlots * kBarStride * 8);
     L.strace = (unsigned long long*)S.take((size_t)(kStepPhases * c->n_layers + 2) * 8);
     L.gen_out = (int*)S.take((size_t)c->n_ctx * 4);
     L.ptok = (int*)S.take((size_t)C * 4);
@@ -328,7 +327,7 @@ struct llm_ctx {
     std::string err;
     int g_qkv, g_o, g_gu, g_down, g_vocab;
     bool use_step = false;  // persistent step kernel (else the launch graph)
-    int step_grid = 0, step_lds = 0;
+    int step_grid = 0, step_lds = 0, step_dtype = 0;
     StepArgs step;
 };
 
@@ -462,7 +461,7 @@ hipError_t enqueue_step(llm_ctx* c, hipStream_t s) {
 
 int run_step(llm_ctx* c) {
     if (c->use_step) {
-        HIPCHK(c, launch_step(c->step, c->step_grid, c->step_lds, c->stream));
+        HIPCHK(c, launch_step(c->step, c->step_dtype, c->step_grid, c->step_lds, c->stream));
         return LLM_OK;
     }
     if (c->use_graph) {
@@ -632,7 +631,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
     const float theta_scale = (float)pow((double)cfg->rope_base, -2.0 / cfg->rope_dims);
     if (launch_rope_table(L.rope, cfg->n_ctx, cfg->rope_dims, theta_scale, s) != hipSuccess ||
         hipMemsetAsync(L.st, 0, sizeof(State), s) != hipSuccess ||
-        hipMemsetAsync(L.sbar, 0, (size_t)(kBarGroups + 1) * kBarStride * 8, s) != hipSuccess ||
+        hipMemsetAsync(L.sbar, 0, (size_t)kBarSlots * kBarStride * 8, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
         return bail(LLM_ERR_DEVICE, "initialisation kernels failed");
 
@@ -657,16 +656,15 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         A.rope = L.rope;
         A.st = L.st;
         A.bar = L.sbar;
-        A.xv = L.sx;
         A.qkv = L.sqkv;
-        A.ao = L.sao;
         A.part = L.spart;
+        A.po = L.spo;
+        A.pd = L.spd;
         A.u = L.su;
-        A.xstride = L.xstride;
         A.qkv_stride = L.qkv_stride;
-        A.ao_stride = L.ao_stride;
         A.part_stride = L.part_stride;
         A.u_stride = L.u_stride;
+        A.pstride = L.pstride;
         A.logits = L.logits;
         const char* tr = getenv("LLM_STEP_TRACE");
         A.trace = (tr && tr[0] == '1') ? L.strace : nullptr;
@@ -685,14 +683,16 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         A.scale_div = (float)sqrt((double)cfg->head_dim);
         if (!upload(L.dlayers, L.layers.data(), L.layers.size() * sizeof(LayerW)))
             return bail(LLM_ERR_DEVICE, "layer table upload failed");
+        // The persistent kernel needs one weight type for all layer matrices.
+        const int dt = L.layers[0].qkv.dtype;
+        bool same = true;
+        for (const LayerW& w : L.layers)
+            same = same && w.qkv.dtype == dt && w.o.dtype == dt && w.gu.dtype == dt && w.down.dtype == dt;
         const char* sk = getenv("LLM_STEP");
         const bool want = sk && strcmp(sk, "persistent") == 0;
-        c->step_grid = want ? step_grid(A, &c->step_lds) : 0;
-        if (c->step_grid >= cfg->n_kv_heads && c->step_grid <= kBarGroup * kBarGroups) {
-            int S = c->step_grid / cfg->n_kv_heads;
-            A.n_split = S < kMaxSplit ? S : kMaxSplit;
-            c->use_step = true;
-        }
+        c->step_dtype = dt;
+        c->step_grid = want && same ? step_grid(A, dt, &c->step_lds) : 0;
+        c->use_step = c->step_grid > 0;
     }
 
     if (c->use_graph && hipStreamCreateWithFlags(&c->cap, hipStreamNonBlocking) != hipSuccess)
@@ -704,7 +704,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         return bail(LLM_ERR_DEVICE, std::string("first step failed: ") + hipGetErrorString(hipGetLastError()));
     if (c->use_step) {
         if (launch_set_state(L.st, 0, 0, 0, s) != hipSuccess ||
-            launch_step(c->step, c->step_grid, c->step_lds, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+            launch_step(c->step, c->step_dtype, c->step_grid, c->step_lds, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
             (void)hipGetLastError();
             c->use_step = false;  // cooperative launch unavailable: the launch graph runs the steps
         } else {
@@ -946,7 +946,7 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
             case LLM_STAGE_STEP:
                 if (c->use_step) {
                     hipError_t e = launch_set_state(L.st, 0, pos, 0, s);
-                    return e != hipSuccess ? e : launch_step(c->step, c->step_grid, c->step_lds, s);
+                    return e != hipSuccess ? e : launch_step(c->step, c->step_dtype, c->step_grid, c->step_lds, s);
                 }
                 return enqueue_step(c, s);
             default: return enqueue_logits(c, L.x, s);
@@ -967,6 +967,12 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
     if (e != hipSuccess) return dev_fail(c, e, "llm_op_time");
     *h_ms = ms / (float)n_launch;
     return LLM_OK;
+}
+
+int llm_op_step_kind(llm_ctx* c) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    return c->use_step ? 1 : 0;
 }
 
 int llm_op_step_trace(llm_ctx* c, uint64_t* h_out, int32_t n) {
