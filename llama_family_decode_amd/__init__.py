@@ -248,7 +248,7 @@ def llm_op_time(ctx, stage: int, layer: int = 0, pos: int = 0, n_launch: int = 2
 
 
 def llm_op_step_kind(ctx) -> int:
-    """1 if the persistent step kernel runs the context's decode steps, 0 for the launch graph."""
+    """0: launch graph; 1: persistent step kernel; 2: persistent step kernel compiled for this shape."""
     r = lib().llm_op_step_kind(ctx)
     if r < 0:
         raise LlmError(r, "llm_op_step_kind")

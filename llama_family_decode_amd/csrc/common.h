@@ -153,10 +153,11 @@ hipError_t launch_attn(const AttnArgs& a, int n_q, hipStream_t s);
 hipError_t launch_set_state(State* st, int token, int pos, int gen_mode, hipStream_t s);
 hipError_t launch_argmax_finalize(State* st, int* gen_out, int gen_cap, hipStream_t s);
 // Persistent step kernel for layer weights of type dtype: the grid (0 if the
-// shape or the device does not allow it; also fills the LDS plan of a) and the
-// launch of one step.
-int step_grid(StepArgs& a, int dtype, int* lds_bytes);
-hipError_t launch_step(const StepArgs& a, int dtype, int grid, int lds_bytes, hipStream_t s);
+// shape or the device does not allow it; also fills the LDS plan of a), the
+// kernel chosen (*special: one compiled for this shape), and the launch of one
+// step.
+int step_grid(StepArgs& a, int dtype, int* lds_bytes, const void** fn, bool* special);
+hipError_t launch_step(const StepArgs& a, const void* fn, int grid, int lds_bytes, hipStream_t s);
 
 struct PrefillBufs;
 hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s);

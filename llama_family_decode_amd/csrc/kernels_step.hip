@@ -47,8 +47,17 @@ constexpr int kSB = 512;       // threads per block
 constexpr int kSW = kSB / 64;  // waves per block
 constexpr int kNG = kStepGroups;
 constexpr int kPF = 16;        // 16-byte weight chunks a lane holds per batch
+constexpr int kStepAttn = 2;   // position steps of 64 threads-groups per attention chunk
 
 typedef unsigned long long u64;
+
+// Compile-time geometry of one product phase: rows read by 2^L lanes, N column
+// batches per row; Geo<0, 0> leaves both to the run-time shape.
+template <int L_, int N_>
+struct Geo {
+    static constexpr int L = L_, N = N_;
+};
+using GeoRT = Geo<0, 0>;
 
 __device__ __forceinline__ void stc(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -157,6 +166,98 @@ __device__ __forceinline__ void all_wait(const StepArgs& a, u64 target) {
         }
     }
     __syncthreads();
+}
+
+// Value of lane l ^ M, for a compile-time M: DPP quad permutes for 1 and 2,
+// swizzles (within 32 lanes) for 4, 8 and 16, the gfx950 half swap for 32.
+// None of them goes through an LDS address computation as a bpermute does.
+template <int M>
+__device__ __forceinline__ uint32_t xshfl_u(uint32_t v) {
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    } else if constexpr (M == 4 || M == 8 || M == 16) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));    // bitmask mode, xor M
+    } else {
+        static_assert(M == 32, "xor offset");
+        // swaps lanes 32..63 of the first operand with lanes 0..31 of the second
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (threadIdx.x & 32) ? r[0] : r[1];
+    }
+}
+template <int M>
+__device__ __forceinline__ float xshfl(float v) { return __uint_as_float(xshfl_u<M>(__float_as_uint(v))); }
+template <int M>
+__device__ __forceinline__ int xshfl(int v) { return (int)xshfl_u<M>((uint32_t)v); }
+template <int M>
+__device__ __forceinline__ double xshfl(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = xshfl_u<M>((uint32_t)b), hi = xshfl_u<M>((uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Sum / max over all 64 lanes (every lane gets the result), in the same
+// butterfly order as a plain xor reduction from offset 32 down to 1.
+template <class T>
+__device__ __forceinline__ T xsum64(T v) {
+    v += xshfl<32>(v);
+    v += xshfl<16>(v);
+    v += xshfl<8>(v);
+    v += xshfl<4>(v);
+    v += xshfl<2>(v);
+    v += xshfl<1>(v);
+    return v;
+}
+__device__ __forceinline__ float xmax64(float v) {
+    v = fmaxf(v, xshfl<32>(v));
+    v = fmaxf(v, xshfl<16>(v));
+    v = fmaxf(v, xshfl<8>(v));
+    v = fmaxf(v, xshfl<4>(v));
+    v = fmaxf(v, xshfl<2>(v));
+    v = fmaxf(v, xshfl<1>(v));
+    return v;
+}
+
+// v summed over lanes that differ in the bits of [lo, hi) (powers of two),
+// from the low offsets up, with uniform conditions.
+__device__ __forceinline__ float lane_sum(float v, int lo, int hi) {
+    if (lo <= 1 && 1 < hi) v += xshfl<1>(v);
+    if (lo <= 2 && 2 < hi) v += xshfl<2>(v);
+    if (lo <= 4 && 4 < hi) v += xshfl<4>(v);
+    if (lo <= 8 && 8 < hi) v += xshfl<8>(v);
+    if (lo <= 16 && 16 < hi) v += xshfl<16>(v);
+    if (lo <= 32 && 32 < hi) v += xshfl<32>(v);
+    return v;
+}
+// Each of the N values summed over lanes that differ in the bits of [lo, hi):
+// every step is applied to all N values before the next, so the exchanges of
+// independent values overlap.
+template <int N>
+__device__ __forceinline__ void lanes_sum_all(float* v, int lo, int hi) {
+#define LSA_STEP(M)                                          \
+    if (lo <= (M) && (M) < hi) {                             \
+        _Pragma("unroll") for (int i = 0; i < N; i++) v[i] += xshfl<M>(v[i]); \
+    }
+    LSA_STEP(1)
+    LSA_STEP(2)
+    LSA_STEP(4)
+    LSA_STEP(8)
+    LSA_STEP(16)
+    LSA_STEP(32)
+#undef LSA_STEP
+}
+
+// The same from the high offsets down (the order of a reduction over a row's
+// lpr lanes).
+__device__ __forceinline__ float lane_sum_down(float v, int lpr) {
+    if (lpr > 32) v += xshfl<32>(v);
+    if (lpr > 16) v += xshfl<16>(v);
+    if (lpr > 8) v += xshfl<8>(v);
+    if (lpr > 4) v += xshfl<4>(v);
+    if (lpr > 2) v += xshfl<2>(v);
+    if (lpr > 1) v += xshfl<1>(v);
+    return v;
 }
 
 // Block-wide sum of doubles in a fixed order; every thread gets the result.
@@ -427,79 +528,88 @@ __device__ __forceinline__ void wbatch(const WRows& w, const int* rmap, int roff
     }
 }
 
-// Lane that holds slot s (0..15) after wave_reduce16.
+// Lane (within its group of 2^LSH lanes) that holds slot s after
+// seg_reduce16<LSH>: slot bit 3-j sits at lane bit LSH-1-j.
+template <int LSH>
 __device__ __forceinline__ int slot_lane(int s) {
-    return ((s >> 3) & 1) << 5 | ((s >> 2) & 1) << 4 | ((s >> 1) & 1) << 3 | (s & 1) << 2;
+    return ((s >> 3) & 1) << (LSH - 1) | ((s >> 2) & 1) << (LSH - 2) | ((s >> 1) & 1) << (LSH - 3) |
+           (s & 1) << (LSH - 4);
 }
 
-// Sums each of the 16 values v[s] over the 64 lanes of the wave in 17
-// exchanges (a transposed butterfly: every step keeps half of the values and
-// sends the other half); lane l ends with the total of slot s(l) =
-// 8*l5 + 4*l4 + 2*l3 + l2 (lk = bit k of l), so lanes slot_lane(s) .. +3 hold
-// slot s. The totals are sums of the same terms as a plain butterfly, in a
-// fixed order.
-__device__ __forceinline__ float wave_reduce16(const float (&v)[16], int lane) {
-    float t8[8], t4[4], t2[2];
-    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
+// One halving step of the transposed butterfly: lanes with bit M set keep the
+// upper half of the values, the others the lower half; each sends the half it
+// drops to lane ^ M and adds what it receives.
+template <int M, int N>
+__device__ __forceinline__ void halve(const float (&in)[2 * N], float (&out)[N], int lane) {
+    const bool up = lane & M;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const float send = h5 ? v[i] : v[i + 8], keep = h5 ? v[i + 8] : v[i];
-        t8[i] = keep + __shfl_xor(send, 32, 64);
+    for (int i = 0; i < N; i++) {
+        const float send = up ? in[i] : in[i + N], keep = up ? in[i + N] : in[i];
+        out[i] = keep + __shfl_xor(send, M, 64);
     }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float send = h4 ? t8[i] : t8[i + 4], keep = h4 ? t8[i + 4] : t8[i];
-        t4[i] = keep + __shfl_xor(send, 16, 64);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const float send = h3 ? t4[i] : t4[i + 2], keep = h3 ? t4[i + 2] : t4[i];
-        t2[i] = keep + __shfl_xor(send, 8, 64);
-    }
-    const float send = h2 ? t2[0] : t2[1], keep = h2 ? t2[1] : t2[0];
-    float t = keep + __shfl_xor(send, 4, 64);
-    t += __shfl_xor(t, 2, 64);
-    t += __shfl_xor(t, 1, 64);
+}
+
+// Sums each of 16 values over every group of 2^LSH lanes (LSH = 4, 5 or 6)
+// in 15 + (LSH - 4) exchanges: four halving steps, then plain butterfly
+// steps. Lane l ends with the group total of slot slot(l), replicated over the
+// 2^(LSH-4) lanes that differ only in the low bits.
+template <int LSH>
+__device__ __forceinline__ float seg_reduce16(const float (&v)[16], int lane) {
+    constexpr int L = 1 << LSH;
+    float t8[8], t4[4], t2[2], t1[1];
+    halve<L / 2, 8>(v, t8, lane);
+    halve<L / 4, 4>(t8, t4, lane);
+    halve<L / 8, 2>(t4, t2, lane);
+    halve<L / 16, 1>(t2, t1, lane);
+    float t = t1[0];
+    if constexpr (L / 32 >= 1) t += __shfl_xor(t, L / 32, 64);
+    if constexpr (L / 64 >= 1) t += __shfl_xor(t, L / 64, 64);
     return t;
 }
 
-// One batch of kPF = 16 slots for rows read by whole waves (lpr = 64) whose
-// window is a whole number of 64-chunk batches, ncb in {1, 2, 4, 8}: a batch
-// then holds 16 / ncb whole rows, an even number. Lane partials of each row
+// One batch of kPF = 16 slots in the dense case: rows read by 2^LSH lanes
+// (LSH = 4, 5, 6), every chunk of the window in range (nch a multiple of the
+// row's lanes), whole row groups, and for LSH = 6 ncb in {1, 2, 4, 8} so a
+// batch holds whole rows (an even number). Lane partials of each row
 // accumulate over its ncb slots, one transposed butterfly sums all rows over
-// the wave, and the lanes emit the rows in parallel.
-template <int DT, int EM>
+// their lanes, and the lanes emit the rows in parallel.
+template <int DT, int EM, int LSH, int NCB>
 __device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int roff, const float* xs, const PF& pf,
                                             int k0, int lane, const EmitArgs& ea, float& best, int& best_i,
                                             int& nonfinite) {
-    static_assert(kPF == 16, "wave_reduce16 takes 16 slots");
+    static_assert(kPF == 16, "seg_reduce16 takes 16 slots");
+    constexpr int L = 1 << LSH, RPI = 64 / L;
+    const int ncb = NCB ? NCB : w.ncb;  // a power of two dividing kPF; k0 is a multiple of kPF
+    const int sub = lane >> LSH, cl = lane & (L - 1);
     float rv[16];
     float acc = 0.f;
-    int cb = 0;
 #pragma unroll
     for (int k = 0; k < kPF; k++) {
+        const int cb = k & (ncb - 1);
         rv[k] = 0.f;
         if (k0 + k < w.nslots) {
-            const int c = lane + (cb << 6);
+            const int c = cl + (cb << LSH);
             const float p = chunk_dot<DT>(pf.q[k], xs, c);
             if constexpr (DT == DT_Q8)
                 acc += h2f((uint16_t)pf.s[k]) * p;
             else
                 acc += p;
-            if (cb == w.ncb - 1) {
+            if (cb == ncb - 1) {
                 rv[k] = acc;
                 acc = 0.f;
             }
         }
-        if (++cb == w.ncb) cb = 0;
     }
-    const float t = wave_reduce16(rv, lane);
-    const int s = ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
-    const int row = w.r0 + (k0 + s) / w.ncb;  // the row that ends at slot s
-    const bool end = (lane & 3) == 0 && (s & (w.ncb - 1)) == w.ncb - 1 && k0 + s < w.nslots;
+    const float t = seg_reduce16<LSH>(rv, cl);
+    const int s = ((cl >> (LSH - 1)) & 1) * 8 + ((cl >> (LSH - 2)) & 1) * 4 + ((cl >> (LSH - 3)) & 1) * 2 +
+                  ((cl >> (LSH - 4)) & 1);
+    const int row = w.r0 + (k0 + s) / ncb * RPI + sub;  // the row that ends at slot s
+    const bool end = (cl & (L / 16 - 1)) == 0 && (s & (ncb - 1)) == ncb - 1 && k0 + s < w.nslots;
     if constexpr (EM == EM_QKV || EM == EM_SWIGLU) {
-        // rows 2i and 2i+1: the odd row ends ncb slots later
-        const float other = __shfl(t, slot_lane((s + w.ncb) & 15), 64);
+        // rows 2i and 2i+1: the odd row ends ncb slots later (whole-wave rows)
+        // or sits in the next group of lanes (shorter rows)
+        const int src = RPI == 1 ? slot_lane<LSH>((s + ncb) & 15) : (lane + L) & 63;
+        const float other = __shfl(t, src, 64);
         if (end && ((row - w.r0) & 1) == 0) {
             if constexpr (EM == EM_QKV)
                 emit_qkv(ea, rmap[row], rmap[row + 1], t, other);
@@ -524,18 +634,32 @@ __device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int
 // The wave's rows. If `prefetched`, pf already holds the first kPF slots
 // (issued by wload before the barrier). For pairs, wave ranges start at even
 // rows.
-template <int DT, int EM>
+template <int DT, int EM, class GEO = GeoRT>
 __device__ __forceinline__ void wrun(const WRows& w, const int* rmap, int roff, const float* xs, PF& pf,
                                      bool prefetched, const EmitArgs& ea, float& best, int& best_i, int& nonfinite) {
     if (w.nslots == 0) return;
+    if constexpr (GEO::L > 0) {  // the shape is known to be dense with this geometry
+        const int lane = lane_id();
+        for (int k0 = 0; k0 < w.nslots; k0 += kPF) {
+            if (!prefetched || k0 > 0) wload<DT>(w, rmap, roff, k0, pf);
+            wbatch_fast<DT, EM, GEO::L, GEO::N>(w, rmap, roff, xs, pf, opaque_s(k0), lane, ea, best, best_i,
+                                                nonfinite);
+        }
+        return;
+    }
     const int lane = lane_id(), sub = lane >> w.lsh, cl = lane & (w.lpr - 1);
-    const bool fast = w.lpr == 64 && (w.W.nch & 63) == 0 && w.ncb <= 8 && (w.ncb & (w.ncb - 1)) == 0;
+    const bool dense = w.lsh >= 4 && (w.W.nch & (w.lpr - 1)) == 0 && (w.r1 - w.r0) % w.rpi == 0 && w.ncb <= 8 &&
+                       (w.ncb & (w.ncb - 1)) == 0;
     float acc = 0.f, pend = 0.f;
     for (int k0 = 0; k0 < w.nslots; k0 += kPF) {
         if (!prefetched || k0 > 0) wload<DT>(w, rmap, roff, k0, pf);
         const int k0s = opaque_s(k0);
-        if (fast)
-            wbatch_fast<DT, EM>(w, rmap, roff, xs, pf, k0s, lane, ea, best, best_i, nonfinite);
+        if (dense && w.lsh == 6)
+            wbatch_fast<DT, EM, 6, 0>(w, rmap, roff, xs, pf, k0s, lane, ea, best, best_i, nonfinite);
+        else if (dense && w.lsh == 5)
+            wbatch_fast<DT, EM, 5, 0>(w, rmap, roff, xs, pf, k0s, lane, ea, best, best_i, nonfinite);
+        else if (dense)
+            wbatch_fast<DT, EM, 4, 0>(w, rmap, roff, xs, pf, k0s, lane, ea, best, best_i, nonfinite);
         else
             wbatch<DT, EM, false>(w, rmap, roff, xs, pf, k0s, lane, sub, cl, ea, acc, pend, best, best_i, nonfinite);
     }
@@ -560,14 +684,14 @@ __device__ __forceinline__ void attn_splits(int P, int bg, int n_kv_heads, int& 
 // head g; rows past the split are clamped to row pos (their values are not
 // used; row pos itself is substituted from the q|k|v buffer).
 __device__ __forceinline__ void attn_kv_load(const StepArgs& a, int layer, int g, int c0, int pos,
-                                             u32x4 (&kr)[kAttnSteps], u32x4 (&vr)[kAttnSteps]) {
+                                             u32x4 (&kr)[kStepAttn], u32x4 (&vr)[kStepAttn]) {
     const int hd = a.head_dim, LPP = attn_lpp(hd), PPI = kSB / LPP;
     const int tid = thread_id(), sub = tid % LPP, pg = tid / LPP;
     const int sub8 = sub * 8 < hd ? sub * 8 : 0;
     const __half* kb = a.kc + (size_t)layer * a.kv_layer + (size_t)g * a.n_ctx * hd + sub8;
     const __half* vb = a.vc + (size_t)layer * a.kv_layer + (size_t)g * a.n_ctx * hd + sub8;
 #pragma unroll
-    for (int i = 0; i < kAttnSteps; i++) {
+    for (int i = 0; i < kStepAttn; i++) {
         const int t = min(c0 + pg + i * PPI, pos);
         kr[i] = ld16(kb + (size_t)t * hd);
         vr[i] = ld16(vb + (size_t)t * hd);
@@ -582,12 +706,12 @@ __device__ __forceinline__ void attn_kv_load(const StepArgs& a, int layer, int g
 template <int GC>
 __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos, const float* qkv, float* part,
                                            int hlo, int nh, int S, int CH, int rk, int bg,
-                                           u32x4 (&kr)[kAttnSteps], u32x4 (&vr)[kAttnSteps], float* sm,
+                                           u32x4 (&kr)[kStepAttn], u32x4 (&vr)[kStepAttn], float* sm,
                                            float* m_run, float* l_run, float* alpha) {
     const int hd = a.head_dim, P = pos + 1, G = a.n_heads / a.n_kv_heads;
     const int qd = a.n_heads * hd, kvd = a.n_kv_heads * hd;
     const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
-    const int LPP = attn_lpp(hd), PPI = kSB / LPP, CHUNK = PPI * kAttnSteps;
+    const int LPP = attn_lpp(hd), PPI = kSB / LPP, CHUNK = PPI * kStepAttn;
     const int sub = tid % LPP, pg = tid / LPP;
     const bool dim_ok = sub * 8 < hd;
     const int sub8 = dim_ok ? sub * 8 : 0;
@@ -638,26 +762,36 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                 if (!have) attn_kv_load(a, layer, g, c0, pos, kr, vr);
                 have = false;
 #pragma unroll
-                for (int i = 0; i < kAttnSteps; i++) {
+                for (int i = 0; i < kStepAttn; i++) {
                     const int t = pg + i * PPI;
                     if (t < cn && c0 + t == pos) {
                         kr[i] = kpos;
                         vr[i] = vpos;
                     }
                 }
+                // scores: each lane's partial dot over its 8 dimensions, then
+                // the sums over the LPP lanes of a position, every step
+                // applied to all of the block's values at once
+                float d[kStepAttn][GC];
 #pragma unroll
-                for (int i = 0; i < kAttnSteps; i++) {
-                    const int t = pg + i * PPI;
+                for (int i = 0; i < kStepAttn; i++) {
                     float kf[8];
                     unpack8(kr[i], kf);
 #pragma unroll
                     for (int h = 0; h < GC; h++) {
-                        float d = 0.f;
+                        float v = 0.f;
 #pragma unroll
-                        for (int j = 0; j < 8; j++) d += qv[h][j] * kf[j];
-                        for (int o = 1; o < LPP; o <<= 1) d += __shfl_xor(d, o, 64);
-                        if (sub == 0 && t < cn) sc[h * CHUNK + t] = d / a.scale_div;
+                        for (int j = 0; j < 8; j++) v += qv[h][j] * kf[j];
+                        d[i][h] = v;
                     }
+                }
+                lanes_sum_all<kStepAttn * GC>(&d[0][0], 1, LPP);
+#pragma unroll
+                for (int i = 0; i < kStepAttn; i++) {
+                    const int t = pg + i * PPI;
+#pragma unroll
+                    for (int h = 0; h < GC; h++)
+                        if (sub == 0 && t < cn) sc[h * CHUNK + t] = d[i][h] / a.scale_div;
                 }
                 __syncthreads();
                 for (int h = wave; h < GC; h += kSW) {
@@ -688,7 +822,7 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                     for (int i = 0; i < 8; i++) acc[h][i] *= al;
                 }
 #pragma unroll
-                for (int i = 0; i < kAttnSteps; i++) {
+                for (int i = 0; i < kStepAttn; i++) {
                     const int t = pg + i * PPI;
                     if (dim_ok && t < cn) {
                         float vf[8];
@@ -704,14 +838,7 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                 __syncthreads();
             }
             if (h0 + GC < G) have = false;  // the next pass reloads K and V
-#pragma unroll
-            for (int h = 0; h < GC; h++)
-#pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    float v = acc[h][i];
-                    for (int o = LPP; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-                    acc[h][i] = v;
-                }
+            lanes_sum_all<GC * 8>(&acc[0][0], LPP, 64);
             if (lane < LPP && dim_ok)
 #pragma unroll
                 for (int h = 0; h < GC; h++)
@@ -808,7 +935,7 @@ __device__ __forceinline__ void merge_splits(const StepArgs& a, const float* par
 }
 
 // --------------------------------------------------------------------- logits
-template <int DT>
+template <int DT, class GEO = GeoRT>
 __device__ __forceinline__ void logits_phase(const StepArgs& a, const float* xr, float* xs, double* red,
                                              ArgPart* wbest) {
     stage_norm<DT>(xr, a.out_norm, a.eps, a.dim, xs, red);
@@ -821,7 +948,7 @@ __device__ __forceinline__ void logits_phase(const StepArgs& a, const float* xr,
     float best = -INFINITY;
     int bi = 0x7fffffff, nf = 0;
     PF pf;
-    wrun<DT, EM_ARGMAX>(w, nullptr, 0, xs, pf, false, ea, best, bi, nf);
+    wrun<DT, EM_ARGMAX, GEO>(w, nullptr, 0, xs, pf, false, ea, best, bi, nf);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const float ob = __shfl_xor(best, o, 64);
@@ -850,7 +977,11 @@ __device__ __forceinline__ void logits_phase(const StepArgs& a, const float* xr,
 }
 
 // --------------------------------------------------------------------- kernel
-template <int DT>
+// DT: layer weight type. The remaining parameters specialise the kernel for
+// one shape (ODT: output matrix type, GA: query heads per attention pass, then
+// the geometry of the QKV, output, gate/up, down and vocabulary products);
+// ODT = -1, GA = 0 and GeoRT take everything from the run-time shape.
+template <int DT, int ODT, int GA, class GQ, class GO, class GG, class GD, class GL>
 __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     extern __shared__ float sm[];
     __shared__ double red[kSW];
@@ -939,10 +1070,18 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     int bi = 0, nfin = 0;
 
     PF pf;
-    u32x4 kr[kAttnSteps], vr[kAttnSteps];
-    LayerW L = a.layers[0];
-    wq.W = make_win<DT>(L.qkv, 0, a.dim);
+    u32x4 kr[kStepAttn], vr[kStepAttn];
+#define KV_PREFETCH(layer)                                                                  \
+    do {                                                                                    \
+        if (rk < nh * S) {                                                                  \
+            attn_kv_load(a, (layer), hlo + rk / S, (rk % S) * CH, pos, kr, vr);              \
+        } else {                                                                            \
+            for (int i_ = 0; i_ < kStepAttn; i_++) kr[i_] = vr[i_] = (u32x4){0u, 0u, 0u, 0u}; \
+        }                                                                                   \
+    } while (0)
+    wq.W = make_win<DT>(a.layers[0].qkv, 0, a.dim);
     wload<DT>(wq, qmap, 0, 0, pf);
+    KV_PREFETCH(0);
     pin();
 
     for (int l = 0; l < a.n_layers; l++) {
@@ -953,33 +1092,30 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         float* pd = a.pd + (size_t)l * kNG * a.pstride;
 
         // ---- QKV
-        stage_norm<DT>(xr, L.attn_norm, a.eps, a.dim, xs, red);
+        stage_norm<DT>(xr, a.layers[l].attn_norm, a.eps, a.dim, xs, red);
         ea.out = qkv;
-        ea.bias = L.bqkv;
+        ea.bias = a.layers[l].bqkv;
         ea.kc = a.kc + (size_t)l * a.kv_layer;
         ea.vc = a.vc + (size_t)l * a.kv_layer;
-        wrun<DT, EM_QKV>(wq, qmap, 0, xs, pf, true, ea, best, bi, nfin);
+        wrun<DT, EM_QKV, GQ>(wq, qmap, 0, xs, pf, true, ea, best, bi, nfin);
         wait_mem();
         group_arrive(a, x);
-        if (rk < nh * S) {
-            attn_kv_load(a, l, hlo + rk / S, (rk % S) * CH, pos, kr, vr);
-        } else {
-#pragma unroll
-            for (int i = 0; i < kAttnSteps; i++) kr[i] = vr[i] = (u32x4){0u, 0u, 0u, 0u};
-        }
-        pin();
         group_wait(a, x, ++jl * bg);
         STAMP();
 
         // ---- attention
-        switch (G) {
-            case 1: attn_items<1>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
-            case 2: attn_items<2>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
-            default: attn_items<4>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+        if constexpr (GA > 0) {
+            attn_items<GA>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha);
+        } else {
+            switch (G) {
+                case 1: attn_items<1>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+                case 2: attn_items<2>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+                default: attn_items<4>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+            }
         }
         wait_mem();
         group_arrive(a, x);
-        wo.W = make_win<DT>(L.o, hlo * G * hd, nh * G * hd);
+        wo.W = make_win<DT>(a.layers[l].o, hlo * G * hd, nh * G * hd);
         wload<DT>(wo, nullptr, 0, 0, pf);
         pin();
         group_wait(a, x, ++jl * bg);
@@ -989,11 +1125,11 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         if (nh > 0) {
             merge_splits<DT>(a, part, hlo, nh, S, xs, wsp, ored);
             ea.out = po + (size_t)x * a.pstride;
-            wrun<DT, EM_PART>(wo, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
+            wrun<DT, EM_PART, GO>(wo, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
         }
         wait_mem();
         all_arrive(a, x);
-        wg.W = make_win<DT>(L.gu, 0, a.dim);
+        wg.W = make_win<DT>(a.layers[l].gu, 0, a.dim);
         wload<DT>(wg, nullptr, 2 * flo, 0, pf);
         pin();
         all_wait(a, ++jc * bg);
@@ -1001,12 +1137,12 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
 
         // ---- residual, RMSNorm, gate/up + SwiGLU
         add_partials(xr, po, a.pstride, a.dim, hmask);
-        stage_norm<DT>(xr, L.ffn_norm, a.eps, a.dim, xs, red);
+        stage_norm<DT>(xr, a.layers[l].ffn_norm, a.eps, a.dim, xs, red);
         ea.out = u + flo;
-        wrun<DT, EM_SWIGLU>(wg, nullptr, 2 * flo, xs, pf, true, ea, best, bi, nfin);
+        wrun<DT, EM_SWIGLU, GG>(wg, nullptr, 2 * flo, xs, pf, true, ea, best, bi, nfin);
         wait_mem();
         group_arrive(a, x);
-        wd.W = make_win<DT>(L.down, flo, nf);
+        wd.W = make_win<DT>(a.layers[l].down, flo, nf);
         wload<DT>(wd, nullptr, 0, 0, pf);
         pin();
         group_wait(a, x, ++jl * bg);
@@ -1016,14 +1152,14 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         if (nf > 0) {
             stage_copy<DT>(u + flo, nf, xs);
             ea.out = pd + (size_t)x * a.pstride;
-            wrun<DT, EM_PART>(wd, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
+            wrun<DT, EM_PART, GD>(wd, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
         }
         wait_mem();
         all_arrive(a, x);
         if (l + 1 < a.n_layers) {
-            L = a.layers[l + 1];
-            wq.W = make_win<DT>(L.qkv, 0, a.dim);
+            wq.W = make_win<DT>(a.layers[l + 1].qkv, 0, a.dim);
             wload<DT>(wq, qmap, 0, 0, pf);
+            KV_PREFETCH(l + 1);
         }
         pin();
         all_wait(a, ++jc * bg);
@@ -1031,10 +1167,14 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         add_partials(xr, pd, a.pstride, a.dim, fmask);
     }
 
-    switch (a.out.dtype) {
-        case DT_F32: logits_phase<DT_F32>(a, xr, xs, red, wbest); break;
-        case DT_F16: logits_phase<DT_F16>(a, xr, xs, red, wbest); break;
-        default: logits_phase<DT_Q8>(a, xr, xs, red, wbest); break;
+    if constexpr (ODT >= 0) {
+        logits_phase<ODT, GL>(a, xr, xs, red, wbest);
+    } else {
+        switch (a.out.dtype) {
+            case DT_F32: logits_phase<DT_F32>(a, xr, xs, red, wbest); break;
+            case DT_F16: logits_phase<DT_F16>(a, xr, xs, red, wbest); break;
+            default: logits_phase<DT_Q8>(a, xr, xs, red, wbest); break;
+        }
     }
     wait_mem();
     all_arrive(a, x);
@@ -1077,7 +1217,7 @@ bool step_lds_plan(StepArgs& a, int dtype, int* lds_bytes) {
     if (lds_any(nh_max * G * hd) > xs) xs = lds_any(nh_max * G * hd);
     if (lds_any(nf_max) > xs) xs = lds_any(nf_max);
     const int GC = G < 4 ? G : 4;
-    const int att = GC * (kSB / attn_lpp(hd)) * kAttnSteps + kSW * GC * hd;
+    const int att = GC * (kSB / attn_lpp(hd)) * kStepAttn + kSW * GC * hd;
     if (att > xs) xs = att;
     a.lds_xr = (a.dim + 63) / 64 * 64;
     a.lds_xs = (xs + 63) / 64 * 64;
@@ -1088,39 +1228,90 @@ bool step_lds_plan(StepArgs& a, int dtype, int* lds_bytes) {
     return *lds_bytes <= 150 * 1024;
 }
 
-template <int DT>
-static int step_grid_t(int lds) {
-    static int attr_for = -1;
-    if (attr_for != lds) {
-        if (hipFuncSetAttribute((const void*)k_step<DT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-            return 0;
-        attr_for = lds;
+// A specialisation: weight types, query heads per attention pass and the
+// (lanes-per-row shift, column batches) of the five products.
+struct StepSpec {
+    int dt, odt, ga, geo[5][2];
+    const void* fn;
+};
+
+static const StepSpec kSpecs[] = {
+    // 2048-wide Q8_0 layers, 4 query heads per KV head of 64, 8192 FFN units, F32 vocabulary rows
+    {DT_Q8, DT_F32, 4, {{6, 2}, {4, 1}, {6, 2}, {6, 1}, {6, 8}},
+     (const void*)k_step<DT_Q8, DT_F32, 4, Geo<6, 2>, Geo<4, 1>, Geo<6, 2>, Geo<6, 1>, Geo<6, 8>>},
+    // the same shape with F16 layers and F16 vocabulary rows
+    {DT_F16, DT_F16, 4, {{6, 4}, {5, 1}, {6, 4}, {6, 2}, {6, 4}},
+     (const void*)k_step<DT_F16, DT_F16, 4, Geo<6, 4>, Geo<5, 1>, Geo<6, 4>, Geo<6, 2>, Geo<6, 4>>},
+};
+
+// The geometry wave_rows gives a product of n rows over a window of nch
+// chunks, and whether it is dense (every wave range a whole number of row
+// groups, every chunk in range, a power-of-two number of column batches <= 8).
+static bool host_geo(int n, int nch, int* lsh, int* ncb) {
+    int lpr = 64, sh = 6;
+    if (nch < 64) {
+        lpr = 1;
+        sh = 0;
+        while (lpr < nch) {
+            lpr <<= 1;
+            sh++;
+        }
     }
+    *lsh = sh;
+    *ncb = (nch + lpr - 1) / lpr;
+    const int rpi = 64 / lpr;
+    return sh >= 4 && nch % lpr == 0 && n % rpi == 0 && *ncb <= 8 && (*ncb & (*ncb - 1)) == 0;
+}
+
+static const void* pick_kernel(const StepArgs& a, int dtype, bool* special) {
+    *special = false;
+    const int G = a.n_heads / a.n_kv_heads, hd = a.head_dim;
+    auto ve = [](int dt) { return dt == DT_F32 ? 4 : (dt == DT_F16 ? 8 : 16); };
+    const int nh_max = (a.n_kv_heads + kNG - 1) / kNG, nh_min = a.n_kv_heads / kNG;
+    const int nbk = a.ffn / 32;
+    const bool even = nh_max == nh_min && nbk % kNG == 0;  // every group owns the same share
+    int g[5][2];
+    bool dense = even;
+    if (even) {
+        const int nf = nbk / kNG * 32;
+        dense = host_geo(nh_max * (G + 2) * hd, a.dim / ve(dtype), &g[0][0], &g[0][1]) &&
+                host_geo(a.dim, nh_max * G * hd / ve(dtype), &g[1][0], &g[1][1]) &&
+                host_geo(2 * nf, a.dim / ve(dtype), &g[2][0], &g[2][1]) &&
+                host_geo(a.dim, nf / ve(dtype), &g[3][0], &g[3][1]) &&
+                host_geo(a.out.rows, a.dim / ve(a.out.dtype), &g[4][0], &g[4][1]) && g[0][0] == 6 && g[2][0] == 6;
+    }
+    if (dense)
+        for (const StepSpec& sp : kSpecs) {
+            if (sp.dt != dtype || sp.odt != a.out.dtype || (sp.ga != (G < 4 ? G : 4))) continue;
+            bool same = true;
+            for (int i = 0; i < 5; i++) same = same && sp.geo[i][0] == g[i][0] && sp.geo[i][1] == g[i][1];
+            if (same) {
+                *special = true;
+                return sp.fn;
+            }
+        }
+    switch (dtype) {
+        case DT_F32: return (const void*)k_step<DT_F32, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT>;
+        case DT_F16: return (const void*)k_step<DT_F16, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT>;
+        default: return (const void*)k_step<DT_Q8, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT>;
+    }
+}
+
+int step_grid(StepArgs& a, int dtype, int* lds_bytes, const void** fn, bool* special) {
+    if (!step_lds_plan(a, dtype, lds_bytes)) return 0;
+    *fn = pick_kernel(a, dtype, special);
+    if (hipFuncSetAttribute(*fn, hipFuncAttributeMaxDynamicSharedMemorySize, *lds_bytes) != hipSuccess) return 0;
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_step<DT>, kSB, lds) != hipSuccess)
-        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, *fn, kSB, *lds_bytes) != hipSuccess) return 0;
     const int grid = cus / kNG * kNG;
     return per_cu >= 1 && grid >= kNG ? grid : 0;
 }
 
-int step_grid(StepArgs& a, int dtype, int* lds_bytes) {
-    if (!step_lds_plan(a, dtype, lds_bytes)) return 0;
-    switch (dtype) {
-        case DT_F32: return step_grid_t<DT_F32>(*lds_bytes);
-        case DT_F16: return step_grid_t<DT_F16>(*lds_bytes);
-        case DT_Q8: return step_grid_t<DT_Q8>(*lds_bytes);
-    }
-    return 0;
-}
-
-hipError_t launch_step(const StepArgs& a, int dtype, int grid, int lds, hipStream_t s) {
+hipError_t launch_step(const StepArgs& a, const void* fn, int grid, int lds, hipStream_t s) {
     StepArgs arg = a;
     void* params[] = {&arg};
-    const void* fn = dtype == DT_F32 ? (const void*)k_step<DT_F32>
-                     : dtype == DT_F16 ? (const void*)k_step<DT_F16>
-                                       : (const void*)k_step<DT_Q8>;
     return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kSB), params, (unsigned)lds, s);
 }
 

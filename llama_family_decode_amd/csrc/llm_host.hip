@@ -327,7 +327,9 @@ struct llm_ctx {
     std::string err;
     int g_qkv, g_o, g_gu, g_down, g_vocab;
     bool use_step = false;  // persistent step kernel (else the launch graph)
-    int step_grid = 0, step_lds = 0, step_dtype = 0;
+    int step_grid = 0, step_lds = 0;
+    const void* step_fn = nullptr;
+    bool step_special = false;  // a step kernel compiled for this shape
     StepArgs step;
 };
 
@@ -461,7 +463,7 @@ hipError_t enqueue_step(llm_ctx* c, hipStream_t s) {
 
 int run_step(llm_ctx* c) {
     if (c->use_step) {
-        HIPCHK(c, launch_step(c->step, c->step_dtype, c->step_grid, c->step_lds, c->stream));
+        HIPCHK(c, launch_step(c->step, c->step_fn, c->step_grid, c->step_lds, c->stream));
         return LLM_OK;
     }
     if (c->use_graph) {
@@ -690,8 +692,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
             same = same && w.qkv.dtype == dt && w.o.dtype == dt && w.gu.dtype == dt && w.down.dtype == dt;
         const char* sk = getenv("LLM_STEP");
         const bool want = sk && strcmp(sk, "persistent") == 0;
-        c->step_dtype = dt;
-        c->step_grid = want && same ? step_grid(A, dt, &c->step_lds) : 0;
+        c->step_grid = want && same ? step_grid(A, dt, &c->step_lds, &c->step_fn, &c->step_special) : 0;
         c->use_step = c->step_grid > 0;
     }
 
@@ -704,7 +705,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         return bail(LLM_ERR_DEVICE, std::string("first step failed: ") + hipGetErrorString(hipGetLastError()));
     if (c->use_step) {
         if (launch_set_state(L.st, 0, 0, 0, s) != hipSuccess ||
-            launch_step(c->step, c->step_dtype, c->step_grid, c->step_lds, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+            launch_step(c->step, c->step_fn, c->step_grid, c->step_lds, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
             (void)hipGetLastError();
             c->use_step = false;  // cooperative launch unavailable: the launch graph runs the steps
         } else {
@@ -946,7 +947,7 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
             case LLM_STAGE_STEP:
                 if (c->use_step) {
                     hipError_t e = launch_set_state(L.st, 0, pos, 0, s);
-                    return e != hipSuccess ? e : launch_step(c->step, c->step_dtype, c->step_grid, c->step_lds, s);
+                    return e != hipSuccess ? e : launch_step(c->step, c->step_fn, c->step_grid, c->step_lds, s);
                 }
                 return enqueue_step(c, s);
             default: return enqueue_logits(c, L.x, s);
@@ -972,7 +973,7 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
 int llm_op_step_kind(llm_ctx* c) {
     int rc = check_ctx(c);
     if (rc) return rc;
-    return c->use_step ? 1 : 0;
+    return c->use_step ? (c->step_special ? 2 : 1) : 0;
 }
 
 int llm_op_step_trace(llm_ctx* c, uint64_t* h_out, int32_t n) {

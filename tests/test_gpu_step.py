@@ -55,9 +55,10 @@ def test_step_after_prefill(cfg):
 
 
 def test_step_two_attention_chunks():
-    # 8300 cached positions over 32 splits: 260 per split, more than the 256
-    # positions one pass of a block covers at head_dim 64.
-    cfg = SMALL.with_(name="small-long", n_heads=2, n_kv_heads=1, head_dim=64, n_ctx=8400, seed=24)
+    # 8300 cached positions over 32 splits: 260 per split, more than the 128
+    # positions one pass of a block covers at head_dim 64; four query heads
+    # per KV head, as in the 1B shape.
+    cfg = SMALL.with_(name="small-long", dim=256, n_heads=4, n_kv_heads=1, head_dim=64, n_ctx=8400, seed=24)
     run_decode(cfg, n_prompt=8300, n_steps=3, prefill_gpu=True, prefill_ref=True)
 
 
@@ -67,13 +68,15 @@ def test_step_config2_workload():
 
 
 def test_step_1b_q8_shape():
+    # the benchmark shape runs the kernel compiled for it (kind 2)
     cfg = synth.C4.with_(n_ctx=160)
-    load(cfg).close()
+    load(cfg, kind=2).close()
     run_decode(cfg, n_prompt=20, n_steps=4)
 
 
 def test_step_1b_f16_shape():
     cfg = synth.C3.with_(n_ctx=160)
+    load(cfg, kind=2).close()
     run_decode(cfg, n_prompt=12, n_steps=3)
 
 
