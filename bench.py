@@ -7,10 +7,12 @@ random weights; the KV cache is prefilled with 2048 seeded prompt ids, then K
 greedy decode steps run at positions 2048 .. 2048+K-1 (device-side token
 feedback, llm_generate). A step is one token's full forward pass.
 
-The line also reports
-  - roofline: the dominant kernel (the final RMSNorm + vocabulary product +
-    argmax launch, 1.05 GB of F32 weights per launch) timed with HIP events on
-    the stream it runs on; HBM traffic from the committed rocprofv3 counter runs;
+Decode runs the persistent step kernel (one cooperative launch per token,
+compiled for this shape). The line also reports
+  - roofline: that kernel, the only one a decode step launches, timed with HIP
+    events on the context's stream; its algorithmic bytes are the step's
+    (every weight once, the K/V rows 0..pos, the new K/V row); HBM traffic
+    from the committed rocprofv3 counter runs;
   - prefill: llm_prefill of 512 seeded ids on the Qwen2-style F16 variant;
   - cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
@@ -49,19 +51,10 @@ def algorithmic_step_bytes(cfg, pos):
     return total
 
 
-def logits_kernel_bytes(cfg):
-    """Algorithmic bytes of one logits launch: the output matrix, the residual
-    vector and gain in, the logits out."""
-    import synth
-
-    dt = synth.DTYPE_IDS[cfg.embd_dtype] if cfg.tied else synth.DTYPE_IDS[cfg.out_dtype]
-    return synth.nbytes_of(dt, cfg.dim * cfg.vocab) + 2 * cfg.dim * 4 + cfg.vocab * 4
-
-
 def read_traffic():
-    """HBM bytes per launch of the logits kernel from the committed counter runs
-    (profiles/logits_q8_1b_counters.txt), or None when absent."""
-    p = os.path.join(ROOT, "profiles", "logits_q8_1b_counters.txt")
+    """HBM bytes per launch of the step kernel from the committed counter runs
+    (profiles/step_q8_1b_ctx2048_counters.txt), or None when absent."""
+    p = os.path.join(ROOT, "profiles", "step_q8_1b_ctx2048_counters.txt")
     if not os.path.exists(p):
         return None
     for line in open(p):
@@ -110,6 +103,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of the timed decode run (median)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run 5 device-to-device copies of this many bytes (the reference kernel that scales "
+                         "the HBM counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path has no multi-GPU sharding in this build "
@@ -124,6 +120,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copied {args.copy_bytes} bytes 5 times", file=sys.stderr)
+        return
     cfg = synth.C4  # 1B shape, Q8_0 matrices, tied F32 embedding
     ctx_len = 2048
     t_load = time.perf_counter()
@@ -159,16 +163,15 @@ def main():
     print(f"# decode {tok_s:.1f} tok/s ({1e3 * dt / args.steps:.3f} ms/token), step bytes {step_bytes / 1e6:.1f} MB "
           f"-> {step_bytes * tok_s / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
 
-    # dominant kernel: the logits launch, timed with HIP events on its stream
-    ms_logits = model.time_stage(llm.STAGE_LOGITS, 0, 0, 20)
-    lb = logits_kernel_bytes(cfg)
-    achieved = lb / (ms_logits * 1e-3) / 1e9
-    stages = {}
-    for name, st in (("qkv", llm.STAGE_QKV), ("attn", llm.STAGE_ATTN), ("o", llm.STAGE_O),
-                     ("ffn_up", llm.STAGE_FFN_UP), ("down", llm.STAGE_DOWN)):
-        stages[name] = round(model.time_stage(st, 0, mid_pos, 50) * 1e3, 2)
-    stages["logits"] = round(ms_logits * 1e3, 2)
-    print(f"# stage times (us): {stages}", file=sys.stderr, flush=True)
+    # the dominant (only) decode kernel, timed with HIP events on its stream
+    kind = llm.llm_op_step_kind(model.ctx)
+    ms_step = model.time_stage(llm.STAGE_STEP, 0, mid_pos, 50)
+    achieved = step_bytes / (ms_step * 1e-3) / 1e9
+    kernel = {2: "k_step (persistent decode step compiled for this shape: whole forward pass of one token)",
+              1: "k_step (persistent decode step: whole forward pass of one token)",
+              0: "launch graph of the decode step"}[kind]
+    print(f"# step kernel {ms_step * 1e3:.1f} us per launch -> {achieved:.0f} GB/s", file=sys.stderr, flush=True)
+    model.rewind(ctx_len)
     model.close()
     del model
     torch.cuda.empty_cache()
@@ -224,11 +227,9 @@ def main():
                    "ffn": cfg.ffn, "vocab": cfg.vocab, "ctx": ctx_len, "parallelism": "single GPU"},
         "step_roofline": {"bytes_per_token": step_bytes, "achieved_GBs": round(step_bytes * tok_s / 1e9, 1),
                           "peak_GBs": HBM_PEAK_GBS, "frac": round(step_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "k_gemv<F32, NORM, ARGMAX> (final RMSNorm + vocabulary product + argmax)",
-                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
-                     "bytes_per_launch": lb, "ms_per_launch": round(ms_logits, 5)},
-        "stage_us": stages,
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                     "bytes_per_launch": step_bytes, "ms_per_launch": round(ms_step, 5), "position": mid_pos},
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

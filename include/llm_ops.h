@@ -67,7 +67,9 @@ int llm_op_kv_write(llm_ctx* ctx, int32_t layer, int32_t pos0, int32_t n_pos, co
  * the context's stream, with the context's own scratch buffers as inputs
  * (their contents do not affect the time). The attention stage runs at
  * position pos. LLM_STAGE_STEP times a whole decode step at position pos
- * (with layer ignored); it writes cache row pos of every layer. Waits. */
+ * (with layer ignored; on the persistent path one launch of the step kernel,
+ * the state being set once before the timed launches); it writes cache row
+ * pos of every layer. Waits. */
 int llm_op_time(llm_ctx* ctx, int32_t stage, int32_t layer, int32_t pos, int32_t n_launch, float* h_ms);
 
 /* Which kernel runs the context's decode steps: 0 for the captured launch
@@ -76,8 +78,8 @@ int llm_op_time(llm_ctx* ctx, int32_t stage, int32_t layer, int32_t pos, int32_t
  * compiled for the model's shape (the 2048-wide, 64-dim-head, 4-query-heads-
  * per-KV-head shape with 8192 FFN units: Q8_0 layers with F32 vocabulary
  * rows, or F16 layers with F16 vocabulary rows). The persistent kernel is used
- * when the environment variable LLM_STEP is "persistent" at load time, the
- * device can co-schedule one block per compute unit, all layer matrices
+ * unless the environment variable LLM_STEP is "graph" at load time, provided
+ * the device can co-schedule one block per compute unit, all layer matrices
  * share one weight type and G*head_dim (G = n_heads/n_kv_heads) is a multiple
  * of 32. Returns the kind, or a negative LLM_ERR_* for a NULL context. */
 int llm_op_step_kind(llm_ctx* ctx);

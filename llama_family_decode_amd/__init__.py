@@ -31,7 +31,7 @@ EXPORTS = ["llm_plan", "llm_load_weights", "llm_decode", "llm_prefill", "llm_gen
            "llm_last_error", "llm_logits", "llm_kv_len", "llm_kv_read", "llm_op_qkv", "llm_op_attention", "llm_op_o",
            "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind", "llm_op_step_trace",
            "llm_op_step_kind"]
-STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_FFN_UP, STAGE_DOWN, STAGE_LOGITS = range(6)
+STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_FFN_UP, STAGE_DOWN, STAGE_LOGITS, STAGE_STEP = range(7)
 
 
 class LlmError(RuntimeError):

@@ -691,7 +691,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         for (const LayerW& w : L.layers)
             same = same && w.qkv.dtype == dt && w.o.dtype == dt && w.gu.dtype == dt && w.down.dtype == dt;
         const char* sk = getenv("LLM_STEP");
-        const bool want = sk && strcmp(sk, "persistent") == 0;
+        const bool want = !(sk && strcmp(sk, "graph") == 0);
         c->step_grid = want && same ? step_grid(A, dt, &c->step_lds, &c->step_fn, &c->step_special) : 0;
         c->use_step = c->step_grid > 0;
     }
@@ -937,6 +937,8 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
     const Layout& L = c->L;
     hipStream_t s = c->stream;
     HIPCHK(c, launch_set_state(L.st, 0, pos, 0, s));
+    // the persistent kernel reads token and position from the state: with the
+    // feedback off every launch recomputes the same step
     auto one = [&]() -> hipError_t {
         switch (stage) {
             case LLM_STAGE_QKV: return stage_qkv(c, layer, L.x, false, L.q, s);
@@ -945,10 +947,7 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
             case LLM_STAGE_FFN_UP: return stage_ffn_up(c, layer, L.x, L.u, s);
             case LLM_STAGE_DOWN: return stage_down(c, layer, L.u, L.x, s);
             case LLM_STAGE_STEP:
-                if (c->use_step) {
-                    hipError_t e = launch_set_state(L.st, 0, pos, 0, s);
-                    return e != hipSuccess ? e : launch_step(c->step, c->step_fn, c->step_grid, c->step_lds, s);
-                }
+                if (c->use_step) return launch_step(c->step, c->step_fn, c->step_grid, c->step_lds, s);
                 return enqueue_step(c, s);
             default: return enqueue_logits(c, L.x, s);
         }

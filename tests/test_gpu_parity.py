@@ -1,6 +1,9 @@
 """Parity of the HIP forward pass with the CPU oracle (needs an MI355X).
 
-Both sides get the same seeded tensor set and prompt. Decode is teacher-forced
+These tests load every context with LLM_STEP=graph: decode steps run as the
+captured launch graph (the persistent step kernel has its own suite in
+test_gpu_step.py), prefill as the batched MFMA path. Both sides get the same
+seeded tensor set and prompt. Decode is teacher-forced
 with the oracle's own greedy tokens. Per step the test checks:
   - max |logit_gpu - logit_oracle| <= 1e-3 for F32 weights, 2e-2 for F16/Q8_0;
   - the GPU's next token is the first index of the strict maximum of the GPU
@@ -22,6 +25,13 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import llama_family_decode_amd as llm
+
+
+@pytest.fixture(autouse=True)
+def graph_path(request, monkeypatch):
+    # helpers imported by test_gpu_step.py run under that file's own fixture
+    if request.module.__name__.endswith("test_gpu_parity"):
+        monkeypatch.setenv("LLM_STEP", "graph")
 
 
 def tol(cfg):
