@@ -1,11 +1,14 @@
 // Prefill kernels for gfx950: a batch of n tokens at positions p0 .. p0+n-1
 // ("What a Llama model computes, and why", section 4). The vector products
 // become matrix products over the batch, which run on the matrix cores:
-// v_mfma_f32_16x16x32_f16 with the activations rounded to binary16 (as ggml
-// does for F16 weights, section 8) and fp32 accumulation. Q8_0 quants are exact
-// in binary16; each 32-deep product is one Q8_0 block, so its fp32 partial is
-// scaled by that block's fp16 scale before it joins the accumulator. F32
-// weights use an fp32 VALU product instead (no rounding of activations).
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation. F16 weights and Q8_0 quants
+// are exact in binary16; each fp32 activation enters as the sum of two
+// binary16 numbers (hi = f16(x), lo = f16(x - hi)), two products per tile, so
+// the result matches fp32 activations to about 2^-22 relative: rounding the
+// activations themselves to binary16 grows through the layers past the
+// decode tolerance. Each 32-deep product is one Q8_0 block, so its fp32
+// partial is scaled by that block's fp16 scale before it joins the
+// accumulator. F32 weights use an fp32 VALU product.
 // RMSNorm, RoPE and attention run per token.
 #include "common.h"
 
@@ -46,9 +49,8 @@ hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, i
 
 // ------------------------------------------------------------ RMSNorm rows
 // y = (x * scale) * g with scale = (float)(1 / sqrt(sum(x^2)/n + eps)), the sum in
-// double ("The Forward Pass in Java", Example 4). Writes fp32 and/or fp16 rows.
-__global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const float* gain, int dim, float eps, float* Yf,
-                                                      __half* Yh) {
+// double ("The Forward Pass in Java", Example 4).
+__global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const float* gain, int dim, float eps, float* Yf) {
     __shared__ double red[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     const float* x = X + (size_t)row * dim;
@@ -61,15 +63,13 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const floa
     const double tot = red[0] + red[1] + red[2] + red[3];
     const float scale = (float)(1.0 / sqrt(tot / (double)dim + (double)eps));
     for (int i = tid; i < dim; i += 256) {
-        const float y = x[i] * scale * gain[i];
-        if (Yf) Yf[(size_t)row * dim + i] = y;
-        if (Yh) Yh[(size_t)row * dim + i] = __float2half_rn(y);
+        Yf[(size_t)row * dim + i] = x[i] * scale * gain[i];
     }
 }
 
-hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
+hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf,
                                hipStream_t s) {
-    hipLaunchKernelGGL(k_rmsnorm_rows, dim3(n), dim3(256), 0, s, X, gain, dim, eps, Yf, Yh);
+    hipLaunchKernelGGL(k_rmsnorm_rows, dim3(n), dim3(256), 0, s, X, gain, dim, eps, Yf);
     return hipGetLastError();
 }
 
@@ -86,9 +86,11 @@ typedef unsigned int u32x4p __attribute__((ext_vector_type(4)));
 constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LD = GB_K + 8;  // LDS row pitch in halfs
 
 template <int DT, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const __half* A, int M, float* Y, int ldy, __half* Yh,
-                                                   int ldyh, const float* bias) {
-    __shared__ __attribute__((aligned(16))) _Float16 As[GB_M * GB_LD];
+__global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M, float* Y, int ldy, const float* bias) {
+    // activations as hi + lo binary16 pairs (hi = f16(x), lo = f16(x - hi)),
+    // so the products see x to about 2^-22 relative instead of 2^-11
+    __shared__ __attribute__((aligned(16))) _Float16 Ah[GB_M * GB_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 Al[GB_M * GB_LD];
     __shared__ __attribute__((aligned(16))) _Float16 Bs[GB_N * GB_LD];
     __shared__ float Ss[GB_N];
 
@@ -101,18 +103,22 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const __half* A, int M
     const int lr = tid >> 1, lk = (tid & 1) * 16;
     const int am = m0 + lr, bn = n0 + lr;
     const bool a_ok = am < M, b_ok = bn < N;
-    const _Float16* arow = (const _Float16*)A + (size_t)(a_ok ? am : 0) * K;
+    const float* arow = A + (size_t)(a_ok ? am : 0) * K;
 
-    u32x4p ra0, ra1, rb0, rb1;
+    float4 ra0, ra1, ra2, ra3;
+    u32x4p rb0, rb1;
     float rs = 0.f;
     const u32x4p z4 = {0u, 0u, 0u, 0u};
+    const float4 zf = make_float4(0.f, 0.f, 0.f, 0.f);
     const char* bbase = (const char*)W.w + (size_t)(b_ok ? bn : 0) * K * (DT == DT_F16 ? 2 : 1);
     const uint16_t* sbase = (DT == DT_Q8) ? W.s + (size_t)(b_ok ? bn : 0) * (K / 32) : nullptr;
 
 #define GEMM_GLOAD(k0)                                                                         \
     do {                                                                                       \
-        ra0 = a_ok ? *(const u32x4p*)(arow + (k0) + lk) : z4;                                  \
-        ra1 = a_ok ? *(const u32x4p*)(arow + (k0) + lk + 8) : z4;                              \
+        ra0 = a_ok ? *(const float4*)(arow + (k0) + lk) : zf;                                  \
+        ra1 = a_ok ? *(const float4*)(arow + (k0) + lk + 4) : zf;                              \
+        ra2 = a_ok ? *(const float4*)(arow + (k0) + lk + 8) : zf;                              \
+        ra3 = a_ok ? *(const float4*)(arow + (k0) + lk + 12) : zf;                             \
         if constexpr (DT == DT_F16) {                                                          \
             const _Float16* brow = (const _Float16*)bbase;                                     \
             rb0 = b_ok ? __builtin_nontemporal_load((const u32x4p*)(brow + (k0) + lk)) : z4;   \
@@ -133,8 +139,25 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const __half* A, int M
     GEMM_GLOAD(0);
     for (int k0 = 0; k0 < K; k0 += GB_K) {
         __syncthreads();
-        *(u32x4p*)(As + lr * GB_LD + lk) = ra0;
-        *(u32x4p*)(As + lr * GB_LD + lk + 8) = ra1;
+        {
+            half8 h0, h1, l0, l1;
+#define SPLIT(H, L, I, V)                             \
+    do {                                              \
+        const float v_ = (V);                         \
+        const _Float16 t_ = (_Float16)v_;             \
+        H[I] = t_;                                    \
+        L[I] = (_Float16)(v_ - (float)t_);            \
+    } while (0)
+            SPLIT(h0, l0, 0, ra0.x); SPLIT(h0, l0, 1, ra0.y); SPLIT(h0, l0, 2, ra0.z); SPLIT(h0, l0, 3, ra0.w);
+            SPLIT(h0, l0, 4, ra1.x); SPLIT(h0, l0, 5, ra1.y); SPLIT(h0, l0, 6, ra1.z); SPLIT(h0, l0, 7, ra1.w);
+            SPLIT(h1, l1, 0, ra2.x); SPLIT(h1, l1, 1, ra2.y); SPLIT(h1, l1, 2, ra2.z); SPLIT(h1, l1, 3, ra2.w);
+            SPLIT(h1, l1, 4, ra3.x); SPLIT(h1, l1, 5, ra3.y); SPLIT(h1, l1, 6, ra3.z); SPLIT(h1, l1, 7, ra3.w);
+#undef SPLIT
+            *(half8*)(Ah + lr * GB_LD + lk) = h0;
+            *(half8*)(Ah + lr * GB_LD + lk + 8) = h1;
+            *(half8*)(Al + lr * GB_LD + lk) = l0;
+            *(half8*)(Al + lr * GB_LD + lk + 8) = l1;
+        }
         if constexpr (DT == DT_F16) {
             *(u32x4p*)(Bs + lr * GB_LD + lk) = rb0;
             *(u32x4p*)(Bs + lr * GB_LD + lk + 8) = rb1;
@@ -157,23 +180,30 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const __half* A, int M
         }
         __syncthreads();
         if (k0 + GB_K < K) GEMM_GLOAD(k0 + GB_K);
-        half8 af[4], bf[4];
+        half8 ah[4], al[4], bf[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) af[i] = *(const half8*)(As + (64 * wm + 16 * i + fr) * GB_LD + fk);
+        for (int i = 0; i < 4; i++) {
+            ah[i] = *(const half8*)(Ah + (64 * wm + 16 * i + fr) * GB_LD + fk);
+            al[i] = *(const half8*)(Al + (64 * wm + 16 * i + fr) * GB_LD + fk);
+        }
 #pragma unroll
         for (int j = 0; j < 4; j++) bf[j] = *(const half8*)(Bs + (64 * wn + 16 * j + fr) * GB_LD + fk);
         if constexpr (DT == DT_F16) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; j++) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bf[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], bf[j], acc[i][j], 0, 0, 0);
+                }
         } else {
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const float sc = Ss[64 * wn + 16 * j + fr];
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const float4v p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], (float4v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    float4v p = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bf[j], (float4v){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], bf[j], p, 0, 0, 0);
                     acc[i][j] += sc * p;
                 }
             }
@@ -193,11 +223,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const __half* A, int M
                 const float v = acc[i][j][e];
                 if constexpr (EPI == EPI_SWIGLU) {
                     const float up = __shfl_xor(v, 1, 64);
-                    if ((fr & 1) == 0 && m < M && n < N) {
-                        const float u = pf_silu(v) * up;
-                        if (Yh) Yh[(size_t)m * ldyh + n / 2] = __float2half_rn(u);
-                        if (Y) Y[(size_t)m * ldy + n / 2] = u;
-                    }
+                    if ((fr & 1) == 0 && m < M && n < N) Y[(size_t)m * ldy + n / 2] = pf_silu(v) * up;
                 } else if (m < M && n < N) {
                     if constexpr (EPI == EPI_RESID)
                         Y[(size_t)m * ldy + n] += v;
@@ -213,8 +239,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const __half* A, int M
 constexpr int GF_T = 64, GF_K = 16;
 
 template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, float* Y, int ldy, __half* Yh,
-                                                  int ldyh, const float* bias) {
+__global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, float* Y, int ldy, const float* bias) {
     __shared__ float As[GF_K][GF_T + 4];
     __shared__ float Bs[GF_K][GF_T + 4];
     const int N = W.rows, K = W.cols;
@@ -256,9 +281,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, 
             if (n >= N) continue;
             if constexpr (EPI == EPI_SWIGLU) {
                 if ((j & 1) == 0) {
-                    const float u = pf_silu(acc[i][j]) * acc[i][j + 1];
-                    if (Y) Y[(size_t)m * ldy + n / 2] = u;
-                    if (Yh) Yh[(size_t)m * ldyh + n / 2] = __float2half_rn(u);
+                    Y[(size_t)m * ldy + n / 2] = pf_silu(acc[i][j]) * acc[i][j + 1];
                 }
             } else if constexpr (EPI == EPI_RESID) {
                 Y[(size_t)m * ldy + n] += acc[i][j];
@@ -270,27 +293,26 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, 
 }
 
 template <int EPI>
-static hipError_t gemm_epi(const Mat& W, const __half* Ah, const float* Af, int n, float* Y, int ldy, __half* Yh,
-                           int ldyh, const float* bias, hipStream_t s) {
+static hipError_t gemm_epi(const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias, hipStream_t s) {
     if (W.dtype == DT_F32) {
         dim3 grid((W.rows + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
-        hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, Af, n, Y, ldy, Yh, ldyh, bias);
+        hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias);
     } else {
         dim3 grid((W.rows + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M);
         if (W.dtype == DT_F16)
-            hipLaunchKernelGGL((k_gemm_mfma<DT_F16, EPI>), grid, dim3(256), 0, s, W, Ah, n, Y, ldy, Yh, ldyh, bias);
+            hipLaunchKernelGGL((k_gemm_mfma<DT_F16, EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias);
         else
-            hipLaunchKernelGGL((k_gemm_mfma<DT_Q8, EPI>), grid, dim3(256), 0, s, W, Ah, n, Y, ldy, Yh, ldyh, bias);
+            hipLaunchKernelGGL((k_gemm_mfma<DT_Q8, EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int epi, const Mat& W, const __half* Ah, const float* Af, int n, float* Y, int ldy, __half* Yh,
-                       int ldyh, const float* bias, hipStream_t s) {
+hipError_t launch_gemm(int epi, const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias,
+                       hipStream_t s) {
     switch (epi) {
-        case EPI_STORE: return gemm_epi<EPI_STORE>(W, Ah, Af, n, Y, ldy, Yh, ldyh, bias, s);
-        case EPI_RESID: return gemm_epi<EPI_RESID>(W, Ah, Af, n, Y, ldy, Yh, ldyh, bias, s);
-        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, Ah, Af, n, Y, ldy, Yh, ldyh, bias, s);
+        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, s);
+        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, s);
+        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, s);
     }
     return hipErrorInvalidValue;
 }

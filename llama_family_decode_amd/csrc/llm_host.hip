@@ -198,7 +198,6 @@ struct Layout {
     unsigned long long* sbar;
     unsigned long long* strace;
     float *X, *Hf, *QKV, *Q, *Of, *Uf;
-    __half *Hh, *Oh, *Uh;
     int n_split;
     size_t wbytes, kvbytes, sbytes;
 };
@@ -278,13 +277,10 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.ptok = (int*)S.take((size_t)C * 4);
     L.X = (float*)S.take((size_t)C * c->dim * 4);
     L.Hf = (float*)S.take((size_t)C * c->dim * 4);
-    L.Hh = (__half*)S.take((size_t)C * c->dim * 2);
     L.QKV = (float*)S.take((size_t)C * (qd + 2 * kvd) * 4);
     L.Q = (float*)S.take((size_t)C * qd * 4);
     L.Of = (float*)S.take((size_t)C * qd * 4);
-    L.Oh = (__half*)S.take((size_t)C * qd * 2);
     L.Uf = (float*)S.take((size_t)C * c->ffn * 4);
-    L.Uh = (__half*)S.take((size_t)C * c->ffn * 2);
     L.sbytes = S.off;
 }
 
@@ -773,11 +769,8 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
             const LayerW& W = L.layers[l];
             __half* kc = L.kc + (size_t)l * L.kv_layer;
             __half* vc = L.vc + (size_t)l * L.kv_layer;
-            const bool f32_qkv = W.qkv.dtype == DT_F32, f32_o = W.o.dtype == DT_F32;
-            const bool f32_gu = W.gu.dtype == DT_F32, f32_dn = W.down.dtype == DT_F32;
-            HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, f32_qkv ? L.Hf : nullptr,
-                                          f32_qkv ? nullptr : L.Hh, s));
-            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, L.Hh, L.Hf, m, L.QKV, qkvd, nullptr, 0, W.bqkv, s));
+            HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, s));
+            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, L.Hf, m, L.QKV, qkvd, W.bqkv, s));
             HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
                                           cf.rope_neox, cf.n_ctx, L.rope, L.Q, kc, vc, s));
             AttnArgs t;
@@ -786,9 +779,9 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
             t.kc = kc;
             t.vc = vc;
             t.out = L.Of;
-            t.out_h = f32_o ? nullptr : L.Oh;
+            t.out_h = nullptr;
             t.part = L.attn_part;
-                    t.st = nullptr;
+            t.st = nullptr;
             t.p0 = p0;
             t.n_heads = cf.n_heads;
             t.n_kv_heads = cf.n_kv_heads;
@@ -797,12 +790,10 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
             t.n_split = 1;
             t.scale_div = (float)sqrt((double)cf.head_dim);
             HIPCHK(c, launch_attn(t, m, s));
-            HIPCHK(c, launch_gemm(EPI_RESID, W.o, L.Oh, L.Of, m, L.X, cf.dim, nullptr, 0, nullptr, s));
-            HIPCHK(c, launch_rmsnorm_rows(L.X, W.ffn_norm, m, cf.dim, cf.eps, f32_gu ? L.Hf : nullptr,
-                                          f32_gu ? nullptr : L.Hh, s));
-            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, L.Hh, L.Hf, m, f32_dn ? L.Uf : nullptr, cf.ffn,
-                                  f32_dn ? nullptr : L.Uh, cf.ffn, nullptr, s));
-            HIPCHK(c, launch_gemm(EPI_RESID, W.down, L.Uh, L.Uf, m, L.X, cf.dim, nullptr, 0, nullptr, s));
+            HIPCHK(c, launch_gemm(EPI_RESID, W.o, L.Of, m, L.X, cf.dim, nullptr, s));
+            HIPCHK(c, launch_rmsnorm_rows(L.X, W.ffn_norm, m, cf.dim, cf.eps, L.Hf, s));
+            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, L.Hf, m, L.Uf, cf.ffn, nullptr, s));
+            HIPCHK(c, launch_gemm(EPI_RESID, W.down, L.Uf, m, L.X, cf.dim, nullptr, s));
         }
         c->len += m;
         last = m;

@@ -156,6 +156,20 @@ def test_prefill_spans_chunks_and_ragged_tail():
     run_decode(cfg, n_prompt=1100, n_steps=3, prefill_gpu=True, prefill_ref=True)
 
 
+def test_prefill_1b_q8_shape():
+    # the headline model's shape: 16 layers of Q8_0 weights whose synthetic
+    # scales make activations grow, where binary16 prefill inputs would drift
+    # past the tolerance; prefill then decode, both against the oracle
+    cfg = synth.C4.with_(n_ctx=160)
+    run_decode(cfg, n_prompt=40, n_steps=3, prefill_gpu=True, prefill_ref=True)
+
+
+def test_prefill_1b_f16_neox_bias_shape():
+    # the prefill workload's model (NEOX RoPE, q/k/v bias, F16 weights, tied)
+    cfg = synth.C5.with_(n_ctx=160)
+    run_decode(cfg, n_prompt=40, n_steps=2, prefill_gpu=True, prefill_ref=True)
+
+
 def test_config1_llama2c_workload():
     cfg = synth.C1
     run_decode(cfg, n_prompt=cfg.prompt_len, n_steps=cfg.decode_steps)
