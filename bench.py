@@ -95,6 +95,37 @@ def cpu_baseline(cfg, budget_s=20.0):
                       f"oracle prefill (cache 16 positions instead of 2048; attention is under 3% of the bytes)"}
 
 
+def measure_prefill(llm, synth, np, torch, reps=5):
+    """llm_prefill of 512 seeded ids on the Qwen2-style F16 1B model from an
+    empty cache, median of `reps`; MFMA fraction = algorithmic GEMM FLOPs /
+    time / F16 dense peak."""
+    c5 = synth.C5
+    ts = synth.make_tensor_set(c5)
+    pm = llm.Model(c5, ts)
+    del ts
+    p5 = synth.prompt(c5, 512)
+    pm.prefill(p5)
+    pm.reset()
+    ptimes = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        pm.prefill(p5)
+        torch.cuda.synchronize()
+        ptimes.append(time.perf_counter() - t0)
+        pm.reset()
+    pt = float(np.median(ptimes))
+    gemm_flop = 2.0 * 512 * c5.n_layers * (
+        c5.dim * (c5.q_dim + 2 * c5.kv_dim) + c5.q_dim * c5.dim + 2 * c5.dim * c5.ffn + c5.ffn * c5.dim)
+    pm.close()
+    del pm
+    torch.cuda.empty_cache()
+    print(f"# prefill 512: {pt * 1e3:.2f} ms, {512 / pt:.0f} tok/s", file=sys.stderr, flush=True)
+    return {"config": c5.name, "tokens": 512, "ms": round(pt * 1e3, 3), "tok_s": round(512 / pt, 1),
+            "gemm_tflop": round(gemm_flop / 1e12, 4),
+            "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +134,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of the timed decode run (median)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the prefill measurement (512 ids, Qwen2-style F16 1B) and print it as JSON")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 5 device-to-device copies of this many bytes (the reference kernel that scales "
                          "the HBM counters) and exit")
@@ -127,6 +160,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(f"# copied {args.copy_bytes} bytes 5 times", file=sys.stderr)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": measure_prefill(llm, synth, np, torch)}))
         return
     cfg = synth.C4  # 1B shape, Q8_0 matrices, tied F32 embedding
     ctx_len = 2048
@@ -178,31 +214,7 @@ def main():
 
     prefill = None
     if not args.no_prefill:
-        c5 = synth.C5
-        ts = synth.make_tensor_set(c5)
-        pm = llm.Model(c5, ts)
-        del ts
-        p5 = synth.prompt(c5, 512)
-        pm.prefill(p5)
-        pm.reset()
-        ptimes = []
-        for _ in range(5):
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            pm.prefill(p5)
-            torch.cuda.synchronize()
-            ptimes.append(time.perf_counter() - t0)
-            pm.reset()
-        pt = float(np.median(ptimes))
-        gemm_flop = 2.0 * 512 * c5.n_layers * (
-            c5.dim * (c5.q_dim + 2 * c5.kv_dim) + c5.q_dim * c5.dim + 2 * c5.dim * c5.ffn + c5.ffn * c5.dim)
-        prefill = {"config": c5.name, "tokens": 512, "ms": round(pt * 1e3, 3), "tok_s": round(512 / pt, 1),
-                   "gemm_tflop": round(gemm_flop / 1e12, 4),
-                   "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
-        print(f"# prefill 512: {pt * 1e3:.2f} ms, {512 / pt:.0f} tok/s", file=sys.stderr, flush=True)
-        pm.close()
-        del pm
-        torch.cuda.empty_cache()
+        prefill = measure_prefill(llm, synth, np, torch)
 
     cpu = None
     if not args.no_cpu:

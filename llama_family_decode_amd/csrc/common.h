@@ -163,9 +163,9 @@ struct PrefillBufs;
 hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, hipStream_t s);
 // Y[n][rows] op= A[n][K] * W^T with fp32 activations A (MFMA path for F16/Q8
-// weights, VALU path for F32).
-hipError_t launch_gemm(int epi, const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias,
-                       hipStream_t s);
+// weights, VALU path for F32); ws (ws_floats floats) holds split-K partials.
+hipError_t launch_gemm(int epi, const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias, float* ws,
+                       size_t ws_floats, hipStream_t s);
 hipError_t launch_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int n_kv_heads, int head_dim, int n_rot,
                                int neox, int n_ctx, const float2* rope, float* Q, __half* kc, __half* vc,
                                hipStream_t s);

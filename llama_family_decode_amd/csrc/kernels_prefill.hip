@@ -85,8 +85,11 @@ typedef unsigned int u32x4p __attribute__((ext_vector_type(4)));
 
 constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LD = GB_K + 8;  // LDS row pitch in halfs
 
+// Split K: block z of gridDim.z takes K columns [z*kz, (z+1)*kz); with P set
+// it stores its raw partial sums to P[z][m][n] (ld N) instead of applying EPI.
 template <int DT, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M, float* Y, int ldy, const float* bias) {
+__global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M, float* Y, int ldy, const float* bias,
+                                                   int kz, float* P) {
     // activations as hi + lo binary16 pairs (hi = f16(x), lo = f16(x - hi)),
     // so the products see x to about 2^-22 relative instead of 2^-11
     __shared__ __attribute__((aligned(16))) _Float16 Ah[GB_M * GB_LD];
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M,
     __shared__ __attribute__((aligned(16))) _Float16 Bs[GB_N * GB_LD];
     __shared__ float Ss[GB_N];
 
-    const int N = W.rows, K = W.cols;
+    const int N = W.rows, K = W.cols, kb = blockIdx.z * kz;
     const int n0 = blockIdx.x * GB_N, m0 = blockIdx.y * GB_M;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -103,15 +106,15 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M,
     const int lr = tid >> 1, lk = (tid & 1) * 16;
     const int am = m0 + lr, bn = n0 + lr;
     const bool a_ok = am < M, b_ok = bn < N;
-    const float* arow = A + (size_t)(a_ok ? am : 0) * K;
+    const float* arow = A + (size_t)(a_ok ? am : 0) * K + kb;
 
     float4 ra0, ra1, ra2, ra3;
     u32x4p rb0, rb1;
     float rs = 0.f;
     const u32x4p z4 = {0u, 0u, 0u, 0u};
     const float4 zf = make_float4(0.f, 0.f, 0.f, 0.f);
-    const char* bbase = (const char*)W.w + (size_t)(b_ok ? bn : 0) * K * (DT == DT_F16 ? 2 : 1);
-    const uint16_t* sbase = (DT == DT_Q8) ? W.s + (size_t)(b_ok ? bn : 0) * (K / 32) : nullptr;
+    const char* bbase = (const char*)W.w + ((size_t)(b_ok ? bn : 0) * K + kb) * (DT == DT_F16 ? 2 : 1);
+    const uint16_t* sbase = (DT == DT_Q8) ? W.s + (size_t)(b_ok ? bn : 0) * (K / 32) + kb / 32 : nullptr;
 
 #define GEMM_GLOAD(k0)                                                                         \
     do {                                                                                       \
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M,
 
     const int fr = lane & 15, fk = (lane >> 4) * 8;
     GEMM_GLOAD(0);
-    for (int k0 = 0; k0 < K; k0 += GB_K) {
+    for (int k0 = 0; k0 < kz; k0 += GB_K) {
         __syncthreads();
         {
             half8 h0, h1, l0, l1;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M,
             if ((tid & 1) == 0) Ss[lr] = rs;
         }
         __syncthreads();
-        if (k0 + GB_K < K) GEMM_GLOAD(k0 + GB_K);
+        if (k0 + GB_K < kz) GEMM_GLOAD(k0 + GB_K);
         half8 ah[4], al[4], bf[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -221,7 +224,9 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M,
             for (int e = 0; e < 4; e++) {
                 const int m = m0 + 64 * wm + 16 * i + (lane >> 4) * 4 + e;
                 const float v = acc[i][j][e];
-                if constexpr (EPI == EPI_SWIGLU) {
+                if (P) {
+                    if (m < M && n < N) P[((size_t)blockIdx.z * M + m) * N + n] = v;
+                } else if constexpr (EPI == EPI_SWIGLU) {
                     const float up = __shfl_xor(v, 1, 64);
                     if ((fr & 1) == 0 && m < M && n < N) Y[(size_t)m * ldy + n / 2] = pf_silu(v) * up;
                 } else if (m < M && n < N) {
@@ -292,27 +297,73 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, 
     }
 }
 
+// Sum of the S split-K partials P[z][m][n] in z order, then the epilogue.
 template <int EPI>
-static hipError_t gemm_epi(const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias, hipStream_t s) {
+__global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, int ldy, const float* bias) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t MN = (size_t)M * N;
+    if constexpr (EPI == EPI_SWIGLU) {
+        if (2 * i >= MN) return;
+        const size_t m = 2 * i / N, n = 2 * i % N;
+        float g = 0.f, u = 0.f;
+        for (int z = 0; z < S; z++) {
+            g += P[z * MN + 2 * i];
+            u += P[z * MN + 2 * i + 1];
+        }
+        Y[m * ldy + n / 2] = pf_silu(g) * u;
+    } else {
+        if (i >= MN) return;
+        const size_t m = i / N, n = i % N;
+        float v = 0.f;
+        for (int z = 0; z < S; z++) v += P[z * MN + i];
+        if constexpr (EPI == EPI_RESID)
+            Y[m * ldy + n] += v;
+        else
+            Y[m * ldy + n] = bias ? v + bias[n] : v;
+    }
+}
+
+// Splits of K for an M x N product on the MFMA path: enough blocks to cover
+// the compute units, each split at least 256 deep and a multiple of 32.
+static int gemm_splits(int M, int N, int K, size_t ws_floats) {
+    const int tiles = ((N + GB_N - 1) / GB_N) * ((M + GB_M - 1) / GB_M);
+    int S = 1;
+    while (tiles * S < 256 && S < 4 && (K / (2 * S)) % GB_K == 0 && K / (2 * S) >= 256 &&
+           (size_t)2 * S * M * N <= ws_floats)
+        S *= 2;
+    return S;
+}
+
+template <int EPI>
+static hipError_t gemm_epi(const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias, float* ws,
+                           size_t ws_floats, hipStream_t s) {
     if (W.dtype == DT_F32) {
         dim3 grid((W.rows + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
         hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias);
-    } else {
-        dim3 grid((W.rows + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M);
-        if (W.dtype == DT_F16)
-            hipLaunchKernelGGL((k_gemm_mfma<DT_F16, EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias);
-        else
-            hipLaunchKernelGGL((k_gemm_mfma<DT_Q8, EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias);
+        return hipGetLastError();
     }
+    const int S = gemm_splits(n, W.rows, W.cols, ws_floats);
+    const int kz = W.cols / S;
+    float* P = S > 1 ? ws : nullptr;
+    dim3 grid((W.rows + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M, S);
+    if (W.dtype == DT_F16)
+        hipLaunchKernelGGL((k_gemm_mfma<DT_F16, EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias, kz, P);
+    else
+        hipLaunchKernelGGL((k_gemm_mfma<DT_Q8, EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias, kz, P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    const size_t items = EPI == EPI_SWIGLU ? (size_t)n * W.rows / 2 : (size_t)n * W.rows;
+    hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, ws, S, n,
+                       W.rows, Y, ldy, bias);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int epi, const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias,
-                       hipStream_t s) {
+hipError_t launch_gemm(int epi, const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias, float* ws,
+                       size_t ws_floats, hipStream_t s) {
     switch (epi) {
-        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, s);
-        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, s);
-        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, s);
+        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, ws, ws_floats, s);
+        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, ws, ws_floats, s);
+        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, ws, ws_floats, s);
     }
     return hipErrorInvalidValue;
 }

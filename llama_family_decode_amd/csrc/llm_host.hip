@@ -197,7 +197,8 @@ struct Layout {
     long long qkv_stride, part_stride, u_stride, pstride;
     unsigned long long* sbar;
     unsigned long long* strace;
-    float *X, *Hf, *QKV, *Q, *Of, *Uf;
+    float *X, *Hf, *QKV, *Q, *Of, *Uf, *ws;
+    size_t ws_floats;
     int n_split;
     size_t wbytes, kvbytes, sbytes;
 };
@@ -281,6 +282,9 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.Q = (float*)S.take((size_t)C * qd * 4);
     L.Of = (float*)S.take((size_t)C * qd * 4);
     L.Uf = (float*)S.take((size_t)C * c->ffn * 4);
+    // split-K partials of the prefill products with at most max(q|k|v, dim) rows
+    L.ws_floats = (size_t)4 * C * (qd + 2 * kvd > c->dim ? qd + 2 * kvd : c->dim);
+    L.ws = (float*)S.take(L.ws_floats * 4);
     L.sbytes = S.off;
 }
 
@@ -770,7 +774,7 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
             __half* kc = L.kc + (size_t)l * L.kv_layer;
             __half* vc = L.vc + (size_t)l * L.kv_layer;
             HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, s));
-            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, L.Hf, m, L.QKV, qkvd, W.bqkv, s));
+            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, L.Hf, m, L.QKV, qkvd, W.bqkv, L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
                                           cf.rope_neox, cf.n_ctx, L.rope, L.Q, kc, vc, s));
             AttnArgs t;
@@ -790,10 +794,10 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
             t.n_split = 1;
             t.scale_div = (float)sqrt((double)cf.head_dim);
             HIPCHK(c, launch_attn(t, m, s));
-            HIPCHK(c, launch_gemm(EPI_RESID, W.o, L.Of, m, L.X, cf.dim, nullptr, s));
+            HIPCHK(c, launch_gemm(EPI_RESID, W.o, L.Of, m, L.X, cf.dim, nullptr, L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rmsnorm_rows(L.X, W.ffn_norm, m, cf.dim, cf.eps, L.Hf, s));
-            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, L.Hf, m, L.Uf, cf.ffn, nullptr, s));
-            HIPCHK(c, launch_gemm(EPI_RESID, W.down, L.Uf, m, L.X, cf.dim, nullptr, s));
+            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, L.Hf, m, L.Uf, cf.ffn, nullptr, L.ws, L.ws_floats, s));
+            HIPCHK(c, launch_gemm(EPI_RESID, W.down, L.Uf, m, L.X, cf.dim, nullptr, L.ws, L.ws_floats, s));
         }
         c->len += m;
         last = m;
