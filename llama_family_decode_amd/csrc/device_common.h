@@ -114,21 +114,36 @@ __device__ __forceinline__ u32x4 load_chunk(const Mat& W, int r, int c) {
 #endif
 }
 
-// Partial dot of one chunk with the staged input.
+// The staged-input values that multiply one 16-byte weight chunk c (VE
+// floats, as VE/4 float4 pieces of the swizzled LDS copy).
 template <int DT>
-__device__ __forceinline__ float chunk_dot(u32x4 raw, const float* xs, int c) {
-    const int lane = c & 63, seg = c >> 6;
+struct XChunk {
+    float4 v[VecW<DT>::VE / 4];
+};
+
+template <int DT>
+__device__ __forceinline__ XChunk<DT> xchunk_load(const float* xs, int c) {
+    XChunk<DT> x;
     if constexpr (DT == DT_F32) {
-        const float4 x = *(const float4*)(xs + 4 * c);
-        float s = __uint_as_float(raw.x) * x.x;
-        s += __uint_as_float(raw.y) * x.y;
-        s += __uint_as_float(raw.z) * x.z;
-        s += __uint_as_float(raw.w) * x.w;
+        x.v[0] = *(const float4*)(xs + 4 * c);
+    } else {
+        const float* b = xs + (c >> 6) * VecW<DT>::SEG + 4 * (c & 63);
+#pragma unroll
+        for (int k = 0; k < VecW<DT>::VE / 4; k++) x.v[k] = *(const float4*)(b + 256 * k);
+    }
+    return x;
+}
+
+// Partial dot of one chunk with its input values.
+template <int DT>
+__device__ __forceinline__ float chunk_dot_x(u32x4 raw, const XChunk<DT>& x) {
+    if constexpr (DT == DT_F32) {
+        float s = __uint_as_float(raw.x) * x.v[0].x;
+        s += __uint_as_float(raw.y) * x.v[0].y;
+        s += __uint_as_float(raw.z) * x.v[0].z;
+        s += __uint_as_float(raw.w) * x.v[0].w;
         return s;
     } else if constexpr (DT == DT_F16) {
-        const float* b = xs + seg * 512 + 4 * lane;
-        const float4 x0 = *(const float4*)(b);
-        const float4 x1 = *(const float4*)(b + 256);
         const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
         float w[8];
 #pragma unroll
@@ -136,32 +151,36 @@ __device__ __forceinline__ float chunk_dot(u32x4 raw, const float* xs, int c) {
             w[2 * k] = h2f((uint16_t)(u[k] & 0xffffu));
             w[2 * k + 1] = h2f((uint16_t)(u[k] >> 16));
         }
-        float s = w[0] * x0.x;
-        s += w[1] * x0.y;
-        s += w[2] * x0.z;
-        s += w[3] * x0.w;
-        s += w[4] * x1.x;
-        s += w[5] * x1.y;
-        s += w[6] * x1.z;
-        s += w[7] * x1.w;
+        float s = w[0] * x.v[0].x;
+        s += w[1] * x.v[0].y;
+        s += w[2] * x.v[0].z;
+        s += w[3] * x.v[0].w;
+        s += w[4] * x.v[1].x;
+        s += w[5] * x.v[1].y;
+        s += w[6] * x.v[1].z;
+        s += w[7] * x.v[1].w;
         return s;
     } else {
-        const float* b = xs + seg * 1024 + 4 * lane;
         const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            const float4 x = *(const float4*)(b + 256 * k);
             const int w = (int)u[k];
             const float q0 = (float)((w << 24) >> 24), q1 = (float)((w << 16) >> 24);
             const float q2 = (float)((w << 8) >> 24), q3 = (float)(w >> 24);
-            s0 += q0 * x.x;
-            s1 += q1 * x.y;
-            s0 += q2 * x.z;
-            s1 += q3 * x.w;
+            s0 += q0 * x.v[k].x;
+            s1 += q1 * x.v[k].y;
+            s0 += q2 * x.v[k].z;
+            s1 += q3 * x.v[k].w;
         }
         return s0 + s1;
     }
+}
+
+// Partial dot of one chunk with the staged input.
+template <int DT>
+__device__ __forceinline__ float chunk_dot(u32x4 raw, const float* xs, int c) {
+    return chunk_dot_x<DT>(raw, xchunk_load<DT>(xs, c));
 }
 
 // Order-preserving 64-bit key of (value, index): a larger value wins, and for

@@ -262,7 +262,7 @@ __device__ __forceinline__ float lane_sum_down(float v, int lpr) {
 
 // Block-wide sum of doubles in a fixed order; every thread gets the result.
 __device__ __forceinline__ double block_sum_s(double v, double* red) {
-    v = wave_sum_d(v);
+    v = xsum64(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     __syncthreads();
     if (lane == 0) red[wave] = v;
@@ -276,8 +276,21 @@ __device__ __forceinline__ double block_sum_s(double v, double* red) {
 // xs (swizzled for weight type DT) = rmsnorm(xr) * gain over K elements
 // ("The Forward Pass in Java", Example 4: sum of squares in double, the scale
 // rounded to float once, then x * scale * gain).
+// The gain elements tid + j*kSB (j < kGainPF) of the next RMSNorm, loaded
+// ahead of the barrier that precedes it.
+constexpr int kGainPF = 4;
+struct GainPF {
+    float g[kGainPF];
+};
+__device__ __forceinline__ void gain_load(GainPF& gp, const float* gain, int K) {
+    const int tid = thread_id();
+#pragma unroll
+    for (int j = 0; j < kGainPF; j++) gp.g[j] = tid + j * kSB < K ? ldf(gain + tid + j * kSB) : 0.f;
+}
+
 template <int DT>
-__device__ __forceinline__ void stage_norm(const float* xr, const float* gain, float eps, int K, float* xs, double* red) {
+__device__ __forceinline__ void stage_norm(const float* xr, const float* gain, const GainPF& gp, float eps, int K,
+                                           float* xs, double* red) {
     const int tid = thread_id();
     double ss = 0.0;
     for (int i = 4 * tid; i < K; i += 4 * kSB) {
@@ -287,7 +300,12 @@ __device__ __forceinline__ void stage_norm(const float* xr, const float* gain, f
     }
     const double tot = block_sum_s(ss, red);
     const float scale = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
-    for (int i = tid; i < K; i += kSB) xs[swz<DT>(i)] = xr[i] * scale * ldf(gain + i);
+#pragma unroll
+    for (int j = 0; j < kGainPF; j++) {
+        const int i = tid + j * kSB;
+        if (i < K) xs[swz<DT>(i)] = xr[i] * scale * gp.g[j];
+    }
+    for (int i = tid + kGainPF * kSB; i < K; i += kSB) xs[swz<DT>(i)] = xr[i] * scale * ldf(gain + i);
     __syncthreads();
 }
 
@@ -582,21 +600,48 @@ __device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int
     const int ncb = NCB ? NCB : w.ncb;  // a power of two dividing kPF; k0 is a multiple of kPF
     const int sub = lane >> LSH, cl = lane & (L - 1);
     float rv[16];
-    float acc = 0.f;
+    if constexpr (NCB > 0) {
+        // column batch outer, rows inner: the input chunk of a batch is read
+        // from LDS once for all the batch's rows; each row still sums its
+        // batches in order
+        constexpr int NR = kPF / NCB;
+        float acc[NR];
 #pragma unroll
-    for (int k = 0; k < kPF; k++) {
-        const int cb = k & (ncb - 1);
-        rv[k] = 0.f;
-        if (k0 + k < w.nslots) {
-            const int c = cl + (cb << LSH);
-            const float p = chunk_dot<DT>(pf.q[k], xs, c);
-            if constexpr (DT == DT_Q8)
-                acc += h2f((uint16_t)pf.s[k]) * p;
-            else
-                acc += p;
-            if (cb == ncb - 1) {
-                rv[k] = acc;
-                acc = 0.f;
+        for (int r = 0; r < NR; r++) acc[r] = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NCB; cb++) {
+            const XChunk<DT> xc = xchunk_load<DT>(xs, cl + (cb << LSH));
+#pragma unroll
+            for (int r = 0; r < NR; r++) {
+                const int k = r * NCB + cb;
+                if (k0 + k < w.nslots) {
+                    const float p = chunk_dot_x<DT>(pf.q[k], xc);
+                    if constexpr (DT == DT_Q8)
+                        acc[r] += h2f((uint16_t)pf.s[k]) * p;
+                    else
+                        acc[r] += p;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kPF; k++) rv[k] = (k % NCB == NCB - 1 && k0 + k < w.nslots) ? acc[k / NCB] : 0.f;
+    } else {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < kPF; k++) {
+            const int cb = k & (ncb - 1);
+            rv[k] = 0.f;
+            if (k0 + k < w.nslots) {
+                const int c = cl + (cb << LSH);
+                const float p = chunk_dot<DT>(pf.q[k], xs, c);
+                if constexpr (DT == DT_Q8)
+                    acc += h2f((uint16_t)pf.s[k]) * p;
+                else
+                    acc += p;
+                if (cb == ncb - 1) {
+                    rv[k] = acc;
+                    acc = 0.f;
+                }
             }
         }
     }
@@ -797,7 +842,7 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                 for (int h = wave; h < GC; h += kSW) {
                     float mx = -INFINITY;
                     for (int t = lane; t < cn; t += 64) mx = fmaxf(mx, sc[h * CHUNK + t]);
-                    mx = wave_max(mx);
+                    mx = xmax64(mx);
                     const float m_old = m_run[h];
                     const float m_new = fmaxf(m_old, mx);
                     float ls = 0.f;
@@ -806,7 +851,7 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                         sc[h * CHUNK + t] = e;
                         ls += e;
                     }
-                    ls = wave_sum(ls);
+                    ls = xsum64(ls);
                     if (lane == 0) {
                         const float al = (m_old == -INFINITY) ? 0.f : expf(m_old - m_new);
                         alpha[h] = al;
@@ -898,9 +943,9 @@ __device__ __forceinline__ void merge_splits(const StepArgs& a, const float* par
             m = ldf(pj);
             l = ldf(pj + 1);
         }
-        const float M = wave_max(m);
+        const float M = xmax64(m);
         const float f = lane < S ? expf(m - M) : 0.f;
-        const float Lh = wave_sum(l * f);
+        const float Lh = xsum64(l * f);
         if (lane < S) wsp[h2 * S + lane] = f / Lh;
     }
     __syncthreads();
@@ -936,9 +981,9 @@ __device__ __forceinline__ void merge_splits(const StepArgs& a, const float* par
 
 // --------------------------------------------------------------------- logits
 template <int DT, class GEO = GeoRT>
-__device__ __forceinline__ void logits_phase(const StepArgs& a, const float* xr, float* xs, double* red,
-                                             ArgPart* wbest) {
-    stage_norm<DT>(xr, a.out_norm, a.eps, a.dim, xs, red);
+__device__ __forceinline__ void logits_phase(const StepArgs& a, const float* xr, const GainPF& gp, float* xs,
+                                             double* red, ArgPart* wbest) {
+    stage_norm<DT>(xr, a.out_norm, gp, a.eps, a.dim, xs, red);
     const int lane = thread_id() & 63, wave = thread_id() >> 6;
     const int wv = __builtin_amdgcn_readfirstlane(blockIdx.x * kSW + wave);
     WRows w = wave_rows(a.out.rows, gridDim.x * kSW, wv, a.dim / VecW<DT>::VE, false);
@@ -1070,6 +1115,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     int bi = 0, nfin = 0;
 
     PF pf;
+    GainPF gp;
     u32x4 kr[kStepAttn], vr[kStepAttn];
 #define KV_PREFETCH(layer)                                                                  \
     do {                                                                                    \
@@ -1079,6 +1125,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
             for (int i_ = 0; i_ < kStepAttn; i_++) kr[i_] = vr[i_] = (u32x4){0u, 0u, 0u, 0u}; \
         }                                                                                   \
     } while (0)
+    gain_load(gp, a.layers[0].attn_norm, a.dim);
     wq.W = make_win<DT>(a.layers[0].qkv, 0, a.dim);
     wload<DT>(wq, qmap, 0, 0, pf);
     KV_PREFETCH(0);
@@ -1092,7 +1139,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         float* pd = a.pd + (size_t)l * kNG * a.pstride;
 
         // ---- QKV
-        stage_norm<DT>(xr, a.layers[l].attn_norm, a.eps, a.dim, xs, red);
+        stage_norm<DT>(xr, a.layers[l].attn_norm, gp, a.eps, a.dim, xs, red);
         ea.out = qkv;
         ea.bias = a.layers[l].bqkv;
         ea.kc = a.kc + (size_t)l * a.kv_layer;
@@ -1129,6 +1176,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         }
         wait_mem();
         all_arrive(a, x);
+        gain_load(gp, a.layers[l].ffn_norm, a.dim);
         wg.W = make_win<DT>(a.layers[l].gu, 0, a.dim);
         wload<DT>(wg, nullptr, 2 * flo, 0, pf);
         pin();
@@ -1137,7 +1185,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
 
         // ---- residual, RMSNorm, gate/up + SwiGLU
         add_partials(xr, po, a.pstride, a.dim, hmask);
-        stage_norm<DT>(xr, a.layers[l].ffn_norm, a.eps, a.dim, xs, red);
+        stage_norm<DT>(xr, a.layers[l].ffn_norm, gp, a.eps, a.dim, xs, red);
         ea.out = u + flo;
         wrun<DT, EM_SWIGLU, GG>(wg, nullptr, 2 * flo, xs, pf, true, ea, best, bi, nfin);
         wait_mem();
@@ -1157,9 +1205,12 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         wait_mem();
         all_arrive(a, x);
         if (l + 1 < a.n_layers) {
+            gain_load(gp, a.layers[l + 1].attn_norm, a.dim);
             wq.W = make_win<DT>(a.layers[l + 1].qkv, 0, a.dim);
             wload<DT>(wq, qmap, 0, 0, pf);
             KV_PREFETCH(l + 1);
+        } else {
+            gain_load(gp, a.out_norm, a.dim);
         }
         pin();
         all_wait(a, ++jc * bg);
@@ -1168,12 +1219,12 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     }
 
     if constexpr (ODT >= 0) {
-        logits_phase<ODT, GL>(a, xr, xs, red, wbest);
+        logits_phase<ODT, GL>(a, xr, gp, xs, red, wbest);
     } else {
         switch (a.out.dtype) {
-            case DT_F32: logits_phase<DT_F32>(a, xr, xs, red, wbest); break;
-            case DT_F16: logits_phase<DT_F16>(a, xr, xs, red, wbest); break;
-            default: logits_phase<DT_Q8>(a, xr, xs, red, wbest); break;
+            case DT_F32: logits_phase<DT_F32>(a, xr, gp, xs, red, wbest); break;
+            case DT_F16: logits_phase<DT_F16>(a, xr, gp, xs, red, wbest); break;
+            default: logits_phase<DT_Q8>(a, xr, gp, xs, red, wbest); break;
         }
     }
     wait_mem();
