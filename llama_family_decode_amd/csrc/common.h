@@ -161,11 +161,25 @@ hipError_t launch_step(const StepArgs& a, const void* fn, int grid, int lds_byte
 
 struct PrefillBufs;
 hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s);
-hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, hipStream_t s);
-// Y[n][rows] op= A[n][K] * W^T with fp32 activations A (MFMA path for F16/Q8
-// weights, VALU path for F32); ws (ws_floats floats) holds split-K partials.
-hipError_t launch_gemm(int epi, const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias, float* ws,
-                       size_t ws_floats, hipStream_t s);
+// Yf = rmsnorm(X) * gain per row; with Yh set also the binary16 hi/lo pair of
+// each output (Yh = f16(y), Yl = f16(y - Yh)), the matrix-core input form.
+hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
+                               __half* Yl, hipStream_t s);
+// H = f16(X), L = f16(X - H) elementwise over n values.
+hipError_t launch_split_hl(const float* X, size_t n, __half* H, __half* L, hipStream_t s);
+// Activations of a prefill product: fp32 rows (ld K) and, for F16 weights,
+// their binary16 hi/lo planes (same layout).
+struct GemmA {
+    const float* f;
+    const __half* h;
+    const __half* l;
+};
+// Y[n][rows] op= A[n][K] * W^T: F16 weights on the matrix cores with the
+// hi/lo activation planes, Q8_0 on the matrix cores splitting the fp32 rows,
+// F32 on the vector ALUs. SwiGLU also writes its output's hi/lo planes when
+// Yh is set. ws (ws_floats floats) holds split-K partials.
+hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
+                       __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s);
 hipError_t launch_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int n_kv_heads, int head_dim, int n_rot,
                                int neox, int n_ctx, const float2* rope, float* Q, __half* kc, __half* vc,
                                hipStream_t s);

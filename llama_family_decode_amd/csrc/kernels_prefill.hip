@@ -50,7 +50,8 @@ hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, i
 // ------------------------------------------------------------ RMSNorm rows
 // y = (x * scale) * g with scale = (float)(1 / sqrt(sum(x^2)/n + eps)), the sum in
 // double ("The Forward Pass in Java", Example 4).
-__global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const float* gain, int dim, float eps, float* Yf) {
+__global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const float* gain, int dim, float eps, float* Yf,
+                                                      __half* Yh, __half* Yl) {
     __shared__ double red[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     const float* x = X + (size_t)row * dim;
@@ -63,14 +64,46 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const floa
     const double tot = red[0] + red[1] + red[2] + red[3];
     const float scale = (float)(1.0 / sqrt(tot / (double)dim + (double)eps));
     for (int i = tid; i < dim; i += 256) {
-        Yf[(size_t)row * dim + i] = x[i] * scale * gain[i];
+        const float y = x[i] * scale * gain[i];
+        Yf[(size_t)row * dim + i] = y;
+        if (Yh) {
+            const __half h = __float2half_rn(y);
+            Yh[(size_t)row * dim + i] = h;
+            Yl[(size_t)row * dim + i] = __float2half_rn(y - __half2float(h));
+        }
     }
 }
 
-hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf,
-                               hipStream_t s) {
-    hipLaunchKernelGGL(k_rmsnorm_rows, dim3(n), dim3(256), 0, s, X, gain, dim, eps, Yf);
+hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
+                               __half* Yl, hipStream_t s) {
+    hipLaunchKernelGGL(k_rmsnorm_rows, dim3(n), dim3(256), 0, s, X, gain, dim, eps, Yf, Yh, Yl);
     return hipGetLastError();
+}
+
+__global__ void k_split_hl(const float* X, size_t n, __half* H, __half* L) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float v = X[i];
+    const __half h = __float2half_rn(v);
+    H[i] = h;
+    L[i] = __float2half_rn(v - __half2float(h));
+}
+
+hipError_t launch_split_hl(const float* X, size_t n, __half* H, __half* L, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_split_hl, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, X, n, H, L);
+    return hipGetLastError();
+}
+
+// u = silu(gate) * up at Y[i], and its hi/lo pair when Yh is set.
+__device__ __forceinline__ void store_swiglu(float* Y, __half* Yh, __half* Yl, size_t i, float gate, float up) {
+    const float u = pf_silu(gate) * up;
+    Y[i] = u;
+    if (Yh) {
+        const __half h = __float2half_rn(u);
+        Yh[i] = h;
+        Yl[i] = __float2half_rn(u - __half2float(h));
+    }
 }
 
 // ------------------------------------------------------------ MFMA GEMM
@@ -89,7 +122,7 @@ constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LD = GB_K + 8;  // LDS row p
 // it stores its raw partial sums to P[z][m][n] (ld N) instead of applying EPI.
 template <int DT, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M, float* Y, int ldy, const float* bias,
-                                                   int kz, float* P) {
+                                                   __half* Yh, __half* Yl, int kz, float* P) {
     // activations as hi + lo binary16 pairs (hi = f16(x), lo = f16(x - hi)),
     // so the products see x to about 2^-22 relative instead of 2^-11
     __shared__ __attribute__((aligned(16))) _Float16 Ah[GB_M * GB_LD];
@@ -228,7 +261,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M,
                     if (m < M && n < N) P[((size_t)blockIdx.z * M + m) * N + n] = v;
                 } else if constexpr (EPI == EPI_SWIGLU) {
                     const float up = __shfl_xor(v, 1, 64);
-                    if ((fr & 1) == 0 && m < M && n < N) Y[(size_t)m * ldy + n / 2] = pf_silu(v) * up;
+                    if ((fr & 1) == 0 && m < M && n < N) store_swiglu(Y, Yh, Yl, (size_t)m * ldy + n / 2, v, up);
                 } else if (m < M && n < N) {
                     if constexpr (EPI == EPI_RESID)
                         Y[(size_t)m * ldy + n] += v;
@@ -244,7 +277,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M,
 constexpr int GF_T = 64, GF_K = 16;
 
 template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, float* Y, int ldy, const float* bias) {
+__global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, float* Y, int ldy, const float* bias,
+                                                  __half* Yh, __half* Yl) {
     __shared__ float As[GF_K][GF_T + 4];
     __shared__ float Bs[GF_K][GF_T + 4];
     const int N = W.rows, K = W.cols;
@@ -285,9 +319,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, 
             const int n = n0 + tx * 4 + j;
             if (n >= N) continue;
             if constexpr (EPI == EPI_SWIGLU) {
-                if ((j & 1) == 0) {
-                    Y[(size_t)m * ldy + n / 2] = pf_silu(acc[i][j]) * acc[i][j + 1];
-                }
+                if ((j & 1) == 0) store_swiglu(Y, Yh, Yl, (size_t)m * ldy + n / 2, acc[i][j], acc[i][j + 1]);
             } else if constexpr (EPI == EPI_RESID) {
                 Y[(size_t)m * ldy + n] += acc[i][j];
             } else {
@@ -299,7 +331,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, 
 
 // Sum of the S split-K partials P[z][m][n] in z order, then the epilogue.
 template <int EPI>
-__global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, int ldy, const float* bias) {
+__global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, int ldy, const float* bias, __half* Yh,
+                                __half* Yl) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t MN = (size_t)M * N;
     if constexpr (EPI == EPI_SWIGLU) {
@@ -310,7 +343,7 @@ __global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, i
             g += P[z * MN + 2 * i];
             u += P[z * MN + 2 * i + 1];
         }
-        Y[m * ldy + n / 2] = pf_silu(g) * u;
+        store_swiglu(Y, Yh, Yl, m * ldy + n / 2, g, u);
     } else {
         if (i >= MN) return;
         const size_t m = i / N, n = i % N;
@@ -323,47 +356,176 @@ __global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, i
     }
 }
 
-// Splits of K for an M x N product on the MFMA path: enough blocks to cover
-// the compute units, each split at least 256 deep and a multiple of 32.
-static int gemm_splits(int M, int N, int K, size_t ws_floats) {
-    const int tiles = ((N + GB_N - 1) / GB_N) * ((M + GB_M - 1) / GB_M);
+// ------------------------------------------------------------ MFMA GEMM, F16 weights
+// The same product with the activations' hi/lo planes read from memory (made
+// once by the kernel that produces the activations) and every operand tile
+// moved global -> LDS by the DMA path (global_load_lds_dwordx4) through a
+// four-stage ring, so three K steps are in flight while one is multiplied.
+// Block tile 128 (m) x 256 (n), K step 32; four waves in a 2 x 2 arrangement,
+// each 64 x 128 = 4 x 8 tiles of the 16x16x32 instruction. A stage holds 16
+// groups of 16 rows x 64 bytes (A hi, A lo: 8 groups each; W: 16 groups), one
+// 1 KB DMA each; within a group, row r's 16-byte chunk c sits in slot
+// 4r + (c ^ ((r >> 2) & 3)), so the fragment reads of 16 lanes hit 16
+// different bank groups.
+constexpr int HL_M = 128, HL_N = 256, HL_K = 32, HL_ST = 4, HL_STAGE = 32768;
+
+__device__ __forceinline__ int hl_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_hl(Mat W, const __half* Ah, const __half* Al, int M, int kz, int nm,
+                                                 int nn, float* Y, int ldy, const float* bias, __half* Yh, __half* Yl,
+                                                 float* P) {
+    __shared__ __attribute__((aligned(1024))) char lds[HL_ST * HL_STAGE];
+    const int N = W.rows, K = W.cols;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // tiles that share a weight tile are dealt to one XCD (block b runs on
+    // XCD b % 8) and start together, so that tile is fetched into one L2
+    int q = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) q = (q & 7) * (nb >> 3) + (q >> 3);
+    const int mt = q % nm, nt = (q / nm) % nn;
+    const int z = blockIdx.y;
+    const int m0 = mt * HL_M, n0 = nt * HL_N, kb = z * kz;
+
+    // this wave's eight DMA sources: wave 0 A hi, 1 A lo, 2 and 3 W
+    const __half* src[8];
+    {
+        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            if (wave < 2) {
+                const int row = min(m0 + 16 * i + r, M - 1);
+                src[i] = (wave == 0 ? Ah : Al) + (size_t)row * K + kb + 8 * c;
+            } else {
+                const int row = min(n0 + 16 * (i + 8 * (wave - 2)) + r, N - 1);
+                src[i] = (const __half*)W.w + (size_t)row * K + kb + 8 * c;
+            }
+        }
+    }
+    auto issue = [&](int ks) {
+        char* dst = lds + (ks % HL_ST) * HL_STAGE + wave * 8192;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + ks * HL_K),
+                                             (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+    };
+
+    const int wm = wave >> 1, wn = wave & 1;
+    const int fslot = hl_slot(lane & 15, lane >> 4) * 16;
+    float4v acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc[i][j] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+    const int nk = kz / HL_K;
+    for (int p = 0; p < HL_ST - 1 && p < nk; p++) issue(p);
+    for (int ks = 0; ks < nk; ks++) {
+        // this wave's DMAs of stage ks are done (later stages may still be in
+        // flight) and its LDS reads of the previous step have returned; then
+        // every wave's are
+        const int pend = min(HL_ST - 2, nk - 1 - ks);
+        if (pend >= 2)
+            asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if (pend == 1)
+            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // the ring slot of step ks - 1 is free now
+        if (ks + HL_ST - 1 < nk) issue(ks + HL_ST - 1);
+        const char* st = lds + (ks % HL_ST) * HL_STAGE;
+        half8 ah[4], al[4], bf[8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            ah[i] = *(const half8*)(st + (4 * wm + i) * 1024 + fslot);
+            al[i] = *(const half8*)(st + 8192 + (4 * wm + i) * 1024 + fslot);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; j++) bf[j] = *(const half8*)(st + 16384 + (8 * wn + j) * 1024 + fslot);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bf[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], bf[j], acc[i][j], 0, 0, 0);
+            }
+    }
+
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int n = n0 + 128 * wn + 16 * j + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int m = m0 + 64 * wm + 16 * i + (lane >> 4) * 4 + e;
+                const float v = acc[i][j][e];
+                if (P) {
+                    if (m < M && n < N) P[((size_t)z * M + m) * N + n] = v;
+                } else if constexpr (EPI == EPI_SWIGLU) {
+                    const float up = __shfl_xor(v, 1, 64);
+                    if ((lane & 1) == 0 && m < M && n < N) store_swiglu(Y, Yh, Yl, (size_t)m * ldy + n / 2, v, up);
+                } else if (m < M && n < N) {
+                    if constexpr (EPI == EPI_RESID)
+                        Y[(size_t)m * ldy + n] += v;
+                    else
+                        Y[(size_t)m * ldy + n] = bias ? v + bias[n] : v;
+                }
+            }
+        }
+    }
+}
+
+// Splits of K for an M x N product on tiles of tm x tn: enough blocks to cover
+// the compute units, each split at least 256 deep and a multiple of 32, the
+// partials within ws_floats.
+static int gemm_splits(int M, int N, int K, int tm, int tn, int smax, size_t ws_floats) {
+    const int tiles = ((N + tn - 1) / tn) * ((M + tm - 1) / tm);
     int S = 1;
-    while (tiles * S < 256 && S < 4 && (K / (2 * S)) % GB_K == 0 && K / (2 * S) >= 256 &&
+    while (tiles * S < 256 && 2 * S <= smax && (K / (2 * S)) % 32 == 0 && K / (2 * S) >= 256 &&
            (size_t)2 * S * M * N <= ws_floats)
         S *= 2;
     return S;
 }
 
 template <int EPI>
-static hipError_t gemm_epi(const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias, float* ws,
-                           size_t ws_floats, hipStream_t s) {
+static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias, __half* Yh,
+                           __half* Yl, float* ws, size_t ws_floats, hipStream_t s) {
+    const int N = W.rows, K = W.cols;
+    int S = 1;
     if (W.dtype == DT_F32) {
-        dim3 grid((W.rows + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
-        hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias);
-        return hipGetLastError();
+        dim3 grid((N + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
+        hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl);
+    } else if (W.dtype == DT_F16 && A.h && K % HL_K == 0) {
+        S = gemm_splits(n, N, K, HL_M, HL_N, 8, ws_floats);
+        const int nm = (n + HL_M - 1) / HL_M, nn = (N + HL_N - 1) / HL_N;
+        hipLaunchKernelGGL((k_gemm_hl<EPI>), dim3(nm * nn, S), dim3(256), 0, s, W, (const __half*)A.h,
+                           (const __half*)A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr);
+    } else {
+        S = gemm_splits(n, N, K, GB_M, GB_N, 4, ws_floats);
+        dim3 grid((N + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M, S);
+        float* P = S > 1 ? ws : nullptr;
+        if (W.dtype == DT_F16)
+            hipLaunchKernelGGL((k_gemm_mfma<DT_F16, EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl,
+                               K / S, P);
+        else
+            hipLaunchKernelGGL((k_gemm_mfma<DT_Q8, EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl,
+                               K / S, P);
     }
-    const int S = gemm_splits(n, W.rows, W.cols, ws_floats);
-    const int kz = W.cols / S;
-    float* P = S > 1 ? ws : nullptr;
-    dim3 grid((W.rows + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M, S);
-    if (W.dtype == DT_F16)
-        hipLaunchKernelGGL((k_gemm_mfma<DT_F16, EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias, kz, P);
-    else
-        hipLaunchKernelGGL((k_gemm_mfma<DT_Q8, EPI>), grid, dim3(256), 0, s, W, A, n, Y, ldy, bias, kz, P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
-    const size_t items = EPI == EPI_SWIGLU ? (size_t)n * W.rows / 2 : (size_t)n * W.rows;
-    hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, ws, S, n,
-                       W.rows, Y, ldy, bias);
+    const size_t items = EPI == EPI_SWIGLU ? (size_t)n * N / 2 : (size_t)n * N;
+    hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, ws, S, n, N, Y,
+                       ldy, bias, Yh, Yl);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int epi, const Mat& W, const float* A, int n, float* Y, int ldy, const float* bias, float* ws,
-                       size_t ws_floats, hipStream_t s) {
+hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
+                       __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s) {
     switch (epi) {
-        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, ws, ws_floats, s);
-        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, ws, ws_floats, s);
-        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, ws, ws_floats, s);
+        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s);
+        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s);
+        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s);
     }
     return hipErrorInvalidValue;
 }

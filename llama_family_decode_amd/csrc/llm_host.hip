@@ -198,6 +198,7 @@ struct Layout {
     unsigned long long* sbar;
     unsigned long long* strace;
     float *X, *Hf, *QKV, *Q, *Of, *Uf, *ws;
+    __half *Hh, *Hl, *Oh, *Ol, *Uh, *Ul;  // binary16 hi/lo planes of Hf, Of, Uf
     size_t ws_floats;
     int n_split;
     size_t wbytes, kvbytes, sbytes;
@@ -282,8 +283,15 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.Q = (float*)S.take((size_t)C * qd * 4);
     L.Of = (float*)S.take((size_t)C * qd * 4);
     L.Uf = (float*)S.take((size_t)C * c->ffn * 4);
-    // split-K partials of the prefill products with at most max(q|k|v, dim) rows
-    L.ws_floats = (size_t)4 * C * (qd + 2 * kvd > c->dim ? qd + 2 * kvd : c->dim);
+    L.Hh = (__half*)S.take((size_t)C * c->dim * 2);
+    L.Hl = (__half*)S.take((size_t)C * c->dim * 2);
+    L.Oh = (__half*)S.take((size_t)C * qd * 2);
+    L.Ol = (__half*)S.take((size_t)C * qd * 2);
+    L.Uh = (__half*)S.take((size_t)C * c->ffn * 2);
+    L.Ul = (__half*)S.take((size_t)C * c->ffn * 2);
+    // split-K partials (up to 8 splits) of the prefill products with at most
+    // max(q|k|v, dim) rows
+    L.ws_floats = (size_t)8 * C * (qd + 2 * kvd > c->dim ? qd + 2 * kvd : c->dim);
     L.ws = (float*)S.take(L.ws_floats * 4);
     L.sbytes = S.off;
 }
@@ -773,8 +781,9 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
             const LayerW& W = L.layers[l];
             __half* kc = L.kc + (size_t)l * L.kv_layer;
             __half* vc = L.vc + (size_t)l * L.kv_layer;
-            HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, s));
-            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, L.Hf, m, L.QKV, qkvd, W.bqkv, L.ws, L.ws_floats, s));
+            HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, GemmA{L.Hf, L.Hh, L.Hl}, m, L.QKV, qkvd, W.bqkv, nullptr, nullptr,
+                                  L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
                                           cf.rope_neox, cf.n_ctx, L.rope, L.Q, kc, vc, s));
             AttnArgs t;
@@ -794,10 +803,14 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
             t.n_split = 1;
             t.scale_div = (float)sqrt((double)cf.head_dim);
             HIPCHK(c, launch_attn(t, m, s));
-            HIPCHK(c, launch_gemm(EPI_RESID, W.o, L.Of, m, L.X, cf.dim, nullptr, L.ws, L.ws_floats, s));
-            HIPCHK(c, launch_rmsnorm_rows(L.X, W.ffn_norm, m, cf.dim, cf.eps, L.Hf, s));
-            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, L.Hf, m, L.Uf, cf.ffn, nullptr, L.ws, L.ws_floats, s));
-            HIPCHK(c, launch_gemm(EPI_RESID, W.down, L.Uf, m, L.X, cf.dim, nullptr, L.ws, L.ws_floats, s));
+            if (W.o.dtype == DT_F16) HIPCHK(c, launch_split_hl(L.Of, (size_t)m * qd, L.Oh, L.Ol, s));
+            HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{L.Of, L.Oh, L.Ol}, m, L.X, cf.dim, nullptr, nullptr, nullptr,
+                                  L.ws, L.ws_floats, s));
+            HIPCHK(c, launch_rmsnorm_rows(L.X, W.ffn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, L.Hl}, m, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
+                                  L.ws, L.ws_floats, s));
+            HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, L.Ul}, m, L.X, cf.dim, nullptr, nullptr,
+                                  nullptr, L.ws, L.ws_floats, s));
         }
         c->len += m;
         last = m;
