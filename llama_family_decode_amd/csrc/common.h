@@ -167,6 +167,12 @@ hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim
                                __half* Yl, hipStream_t s);
 // H = f16(X), L = f16(X - H) elementwise over n values.
 hipError_t launch_split_hl(const float* X, size_t n, __half* H, __half* L, hipStream_t s);
+// Causal prefill attention of n_q queries at positions p0 .. p0+n_q-1 on the
+// matrix cores (head_dim 64 only; hipErrorInvalidValue otherwise): out as
+// fp32 rows [n_q][n_heads*64] and their binary16 hi/lo planes.
+hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
+                                    __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
+                                    int n_ctx, float scale_div, hipStream_t s);
 // Activations of a prefill product: fp32 rows (ld K) and, for F16 weights,
 // their binary16 hi/lo planes (same layout).
 struct GemmA {

@@ -530,6 +530,195 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
     return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------------ causal attention on the matrix cores
+// Prefill attention for head_dim 64 ("The Forward Pass in Java", Example 7,
+// over the batch as in "What a Llama model computes, and why", section 4):
+// query z at position p0 + z attends cache rows 0 .. p0 + z of its KV head.
+// A block takes 64 (token, head) rows that share KV head g: row r is token
+// z0 + r / G, query head g*G + r % G; wave w owns rows 16w .. 16w+15. Cache
+// rows stream through LDS 64 positions at a time (K as stored, V transposed);
+// per chunk each wave forms its 16 x 64 scores with the 16x16x32 instruction
+// (q as a hi/lo binary16 pair, K exact), divides them by sqrt(head_dim),
+// masks positions past each row's own, updates the running max m and sum l
+// of the online softmax, and adds P V (P as a hi/lo pair, V exact) to its
+// 16 x 64 output, rescaled by e^(m_old - m_new). The result o / l goes out
+// as fp32 rows and as their hi/lo planes (the output product's input).
+constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72, PA_PLD = 68;
+
+__global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc,
+                                                           float* out, __half* out_h, __half* out_l, int n_q, int p0,
+                                                           int n_heads, int n_kv_heads, int n_ctx, float scale_div) {
+    constexpr int hd = 64;
+    __shared__ __attribute__((aligned(16))) __half Ks[PA_CH * PA_LD];   // [position][dim]
+    __shared__ __attribute__((aligned(16))) __half Vt[hd * PA_LD];      // [dim][position]
+    __shared__ __attribute__((aligned(16))) float Ps[4][16 * PA_PLD];   // per wave [row][position]
+    const int G = n_heads / n_kv_heads, TB = PA_ROWS / G;
+    const int g = blockIdx.y, z0 = blockIdx.x * TB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qd = n_heads * hd;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    // q fragments of this lane's row (row lr of the wave) as hi/lo pairs
+    const int ra = 16 * wave + lr;
+    const int za = min(z0 + ra / G, n_q - 1), ha = g * G + ra % G;
+    half8 qh[2], ql[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+        const float* qp = Q + (size_t)za * qd + ha * hd + 32 * ks + 8 * lq;
+        const float4 a0 = *(const float4*)qp, a1 = *(const float4*)(qp + 4);
+        const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const _Float16 h = (_Float16)v[j];
+            qh[ks][j] = h;
+            ql[ks][j] = (_Float16)(v[j] - (float)h);
+        }
+    }
+    // the four rows whose scores and outputs this lane holds: 4*lq + i
+    int rpos[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) rpos[i] = p0 + z0 + (16 * wave + 4 * lq + i) / G;
+    float m_run[4], l_run[4];
+    float4v o[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        m_run[i] = -INFINITY;
+        l_run[i] = 0.f;
+        o[i] = (float4v){0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int last = p0 + min(z0 + TB, n_q) - 1;  // the block's last position
+    const int nch = last / PA_CH + 1;
+    const __half* kbase = kc + (size_t)g * n_ctx * hd;
+    const __half* vbase = vc + (size_t)g * n_ctx * hd;
+    // loader: thread t moves position t/8 (+32) dims 8*(t%8) .. +8 of K and V
+    const int lp = tid >> 3, ld8 = (tid & 7) * 8;
+    const u32x4p z4 = {0u, 0u, 0u, 0u};
+    u32x4p kr[2], vr[2];
+    auto load = [&](int c0) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int t = c0 + lp + 32 * u;
+            const bool ok = t <= last;  // rows past the block's last position are never written yet
+            kr[u] = ok ? *(const u32x4p*)(kbase + (size_t)t * hd + ld8) : z4;
+            vr[u] = ok ? *(const u32x4p*)(vbase + (size_t)t * hd + ld8) : z4;
+        }
+    };
+    load(0);
+    float* P = Ps[wave];
+    for (int c = 0; c < nch; c++) {
+        const int c0 = c * PA_CH;
+        __syncthreads();  // the previous chunk's K, V and P reads are done
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            *(u32x4p*)(Ks + (lp + 32 * u) * PA_LD + ld8) = kr[u];
+            const __half* vh = (const __half*)&vr[u];
+#pragma unroll
+            for (int j = 0; j < 8; j++) Vt[(ld8 + j) * PA_LD + lp + 32 * u] = vh[j];
+        }
+        __syncthreads();
+        if (c + 1 < nch) load(c0 + PA_CH);
+
+        // scores of this wave's 16 rows over the chunk: tile pt covers
+        // positions c0 + 16 pt .. +15
+        float4v sc[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; pt++) {
+            sc[pt] = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++) {
+                const half8 kf = *(const half8*)(Ks + (16 * pt + lr) * PA_LD + 32 * ks + 8 * lq);
+                sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[ks], kf, sc[pt], 0, 0, 0);
+                sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], kf, sc[pt], 0, 0, 0);
+            }
+        }
+        // online softmax per row; a row's 64 scores sit in the 16 lanes with
+        // the same lq, four tiles each
+        float alpha[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int pt = 0; pt < 4; pt++) {
+                const int t = c0 + 16 * pt + lr;
+                const float v = t <= rpos[i] ? sc[pt][i] / scale_div : -INFINITY;
+                sc[pt][i] = v;
+                mx = fmaxf(mx, v);
+            }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            const float m_new = fmaxf(m_run[i], mx);
+            alpha[i] = m_run[i] == -INFINITY ? 0.f : expf(m_run[i] - m_new);
+            float ls = 0.f;
+#pragma unroll
+            for (int pt = 0; pt < 4; pt++) {
+                const float e = sc[pt][i] == -INFINITY ? 0.f : expf(sc[pt][i] - m_new);
+                sc[pt][i] = e;
+                ls += e;
+            }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) ls += __shfl_xor(ls, off, 64);
+            l_run[i] = l_run[i] * alpha[i] + ls;
+            m_run[i] = m_new;
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; pt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) P[(4 * lq + i) * PA_PLD + 16 * pt + lr] = sc[pt][i];
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) o[dt][i] *= alpha[i];
+        // o += P V over the chunk's 64 positions (two 32-deep steps)
+#pragma unroll
+        for (int ps = 0; ps < 2; ps++) {
+            const float4 p0v = *(const float4*)(P + lr * PA_PLD + 32 * ps + 8 * lq);
+            const float4 p1v = *(const float4*)(P + lr * PA_PLD + 32 * ps + 8 * lq + 4);
+            const float pv[8] = {p0v.x, p0v.y, p0v.z, p0v.w, p1v.x, p1v.y, p1v.z, p1v.w};
+            half8 ph, pl;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const _Float16 h = (_Float16)pv[j];
+                ph[j] = h;
+                pl[j] = (_Float16)(pv[j] - (float)h);
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) {
+                const half8 vf = *(const half8*)(Vt + (16 * dt + lr) * PA_LD + 32 * ps + 8 * lq);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vf, o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vf, o[dt], 0, 0, 0);
+            }
+        }
+    }
+    // out[z][h*64 + d] = o / l for the lane's rows 4 lq + i, dims 16 dt + lr
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int r = 16 * wave + 4 * lq + i, z = z0 + r / G, h = g * G + r % G;
+        if (z >= n_q) continue;
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) {
+            const float v = o[dt][i] / l_run[i];
+            const size_t e = (size_t)z * qd + h * hd + 16 * dt + lr;
+            out[e] = v;
+            const __half hh = __float2half_rn(v);
+            out_h[e] = hh;
+            out_l[e] = __float2half_rn(v - __half2float(hh));
+        }
+    }
+}
+
+hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
+                                    __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
+                                    int n_ctx, float scale_div, hipStream_t s) {
+    const int G = n_kv_heads > 0 ? n_heads / n_kv_heads : 0;
+    if (head_dim != 64 || G < 1 || G > PA_ROWS || PA_ROWS % G || n_heads % n_kv_heads || n_q <= 0)
+        return hipErrorInvalidValue;
+    const int TB = PA_ROWS / G;
+    hipLaunchKernelGGL(k_attn_prefill_mfma, dim3((n_q + TB - 1) / TB, n_kv_heads), dim3(256), 0, s, Q, kc, vc, out,
+                       out_h, out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ RoPE + KV rows
 // Row i of the batch is at position p0 + i. Each thread takes one rotation pair
 // of one row (pairs as in the decode epilogue: (2j, 2j+1) normal, (j, j+n_rot/2)
@@ -557,7 +746,7 @@ __global__ void k_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int
     float va = src[ra], vb = src[rb];
     if (head < n_heads + n_kv_heads && j < half) {
         const float2 cs = rope[(size_t)pos * half + j];
-const float2 rv = pf_rope_rotate(va, vb, cs);
+        const float2 rv = pf_rope_rotate(va, vb, cs);
         va = rv.x;
         vb = rv.y;
     }

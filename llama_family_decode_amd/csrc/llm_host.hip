@@ -802,8 +802,13 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
             t.n_ctx = cf.n_ctx;
             t.n_split = 1;
             t.scale_div = (float)sqrt((double)cf.head_dim);
-            HIPCHK(c, launch_attn(t, m, s));
-            if (W.o.dtype == DT_F16) HIPCHK(c, launch_split_hl(L.Of, (size_t)m * qd, L.Oh, L.Ol, s));
+            if (cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0) {
+                HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, L.Oh, L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
+                                                   cf.head_dim, cf.n_ctx, t.scale_div, s));
+            } else {
+                HIPCHK(c, launch_attn(t, m, s));
+                if (W.o.dtype == DT_F16) HIPCHK(c, launch_split_hl(L.Of, (size_t)m * qd, L.Oh, L.Ol, s));
+            }
             HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{L.Of, L.Oh, L.Ol}, m, L.X, cf.dim, nullptr, nullptr, nullptr,
                                   L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rmsnorm_rows(L.X, W.ffn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
