@@ -18,7 +18,23 @@ struct Mat {
     int rows, cols;
     const void* w;
     const uint16_t* s;
+    const void* wt;  // F16 only: the prefill products' tiled copy (or nullptr)
 };
+
+// Tiled binary16 layout of the prefill products' operands: rows in tiles of
+// TM (128 for activations, 256 for weights), K in steps of 32; tile t, step
+// ks, 16-row group g is one contiguous 1 KB piece at ((t*nk + ks)*(TM/16) + g)
+// KB, nk = K/32, whose 16-byte slot 4r + (c ^ swz(r)) holds row r's elements
+// 8c .. 8c+7 of the step, swz(r) = ((r >> 1) ^ (r >> 3)) & 3 (the LDS order of
+// the product kernel, so one DMA moves one piece).
+constexpr int kTileA = 128, kTileW = 256;
+__host__ __device__ inline int tile_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__host__ __device__ inline size_t tile_off(int m, int k, int K, int TM) {
+    const int nk = K >> 5, t = m / TM, rr = m - t * TM, g = rr >> 4, r = rr & 15;
+    const int ks = k >> 5, c = (k >> 3) & 3, e = k & 7;
+    return (((size_t)t * nk + ks) * (TM >> 4) + g) * 512 + (size_t)(4 * r + (c ^ tile_swz(r))) * 8 + e;
+}
+inline size_t tiled_w_bytes(int rows, int cols) { return (size_t)((rows + kTileW - 1) / kTileW) * kTileW * cols * 2; }
 
 // Decode-step state, resident in device memory so that a captured graph can run
 // any step: the kernels read token and pos from here, the argmax writes next.
@@ -162,19 +178,22 @@ hipError_t launch_step(const StepArgs& a, const void* fn, int grid, int lds_byte
 struct PrefillBufs;
 hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s);
 // Yf = rmsnorm(X) * gain per row; with Yh set also the binary16 hi/lo pair of
-// each output (Yh = f16(y), Yl = f16(y - Yh)), the matrix-core input form.
+// each output (Yh = f16(y), Yl = f16(y - Yh)) in the tiled layout, the
+// matrix-core input form.
 hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
                                __half* Yl, hipStream_t s);
-// H = f16(X), L = f16(X - H) elementwise over n values.
-hipError_t launch_split_hl(const float* X, size_t n, __half* H, __half* L, hipStream_t s);
+// H, L = the tiled binary16 hi/lo planes of the n x K fp32 rows X.
+hipError_t launch_split_hl(const float* X, int n, int K, __half* H, __half* L, hipStream_t s);
+// The tiled copy of an F16 matrix (rows padded with zeros to a multiple of 256).
+hipError_t launch_tile_w(const Mat& W, void* dst, hipStream_t s);
 // Causal prefill attention of n_q queries at positions p0 .. p0+n_q-1 on the
 // matrix cores (head_dim 64 only; hipErrorInvalidValue otherwise): out as
-// fp32 rows [n_q][n_heads*64] and their binary16 hi/lo planes.
+// fp32 rows [n_q][n_heads*64] and their tiled binary16 hi/lo planes.
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
                                     int n_ctx, float scale_div, hipStream_t s);
 // Activations of a prefill product: fp32 rows (ld K) and, for F16 weights,
-// their binary16 hi/lo planes (same layout).
+// their binary16 hi/lo planes (tiled layout).
 struct GemmA {
     const float* f;
     const __half* h;

@@ -68,8 +68,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const floa
         Yf[(size_t)row * dim + i] = y;
         if (Yh) {
             const __half h = __float2half_rn(y);
-            Yh[(size_t)row * dim + i] = h;
-            Yl[(size_t)row * dim + i] = __float2half_rn(y - __half2float(h));
+            const size_t t = tile_off(row, i, dim, kTileA);
+            Yh[t] = h;
+            Yl[t] = __float2half_rn(y - __half2float(h));
         }
     }
 }
@@ -80,29 +81,56 @@ hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim
     return hipGetLastError();
 }
 
-__global__ void k_split_hl(const float* X, size_t n, __half* H, __half* L) {
+__global__ void k_split_hl(const float* X, int n, int K, __half* H, __half* L) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
+    if (i >= (size_t)n * K) return;
+    const int m = (int)(i / K), k = (int)(i % K);
     const float v = X[i];
     const __half h = __float2half_rn(v);
-    H[i] = h;
-    L[i] = __float2half_rn(v - __half2float(h));
+    const size_t t = tile_off(m, k, K, kTileA);
+    H[t] = h;
+    L[t] = __float2half_rn(v - __half2float(h));
 }
 
-hipError_t launch_split_hl(const float* X, size_t n, __half* H, __half* L, hipStream_t s) {
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_split_hl, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, X, n, H, L);
+hipError_t launch_split_hl(const float* X, int n, int K, __half* H, __half* L, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const size_t total = (size_t)n * K;
+    hipLaunchKernelGGL(k_split_hl, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, X, n, K, H, L);
     return hipGetLastError();
 }
 
-// u = silu(gate) * up at Y[i], and its hi/lo pair when Yh is set.
-__device__ __forceinline__ void store_swiglu(float* Y, __half* Yh, __half* Yl, size_t i, float gate, float up) {
+// One 16-byte piece (8 elements) of the tiled copy per thread; rows past the
+// matrix become zeros.
+__global__ void k_tile_w(const __half* W, int rows, int cols, int rows_pad, __half* T) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int cpr = cols >> 3;
+    if (i >= (size_t)rows_pad * cpr) return;
+    const int n = (int)(i / cpr), k = (int)(i % cpr) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (n < rows) v = *(const uint4*)(W + (size_t)n * cols + k);
+    *(uint4*)(T + tile_off(n, k, cols, kTileW)) = v;
+}
+
+hipError_t launch_tile_w(const Mat& W, void* dst, hipStream_t s) {
+    if (W.dtype != DT_F16 || W.cols % 32) return hipErrorInvalidValue;
+    const int rows_pad = (W.rows + kTileW - 1) / kTileW * kTileW;
+    const size_t total = (size_t)rows_pad * (W.cols / 8);
+    hipLaunchKernelGGL(k_tile_w, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, (const __half*)W.w, W.rows,
+                       W.cols, rows_pad, (__half*)dst);
+    return hipGetLastError();
+}
+
+// u = silu(gate) * up at Y[m*ldy + j], and its hi/lo pair (tiled, K = ldy)
+// when Yh is set.
+__device__ __forceinline__ void store_swiglu(float* Y, __half* Yh, __half* Yl, int m, int j, int ldy, float gate,
+                                             float up) {
     const float u = pf_silu(gate) * up;
-    Y[i] = u;
+    Y[(size_t)m * ldy + j] = u;
     if (Yh) {
         const __half h = __float2half_rn(u);
-        Yh[i] = h;
-        Yl[i] = __float2half_rn(u - __half2float(h));
+        const size_t t = tile_off(m, j, ldy, kTileA);
+        Yh[t] = h;
+        Yl[t] = __float2half_rn(u - __half2float(h));
     }
 }
 
@@ -114,6 +142,7 @@ __device__ __forceinline__ void store_swiglu(float* Y, __half* Yh, __half* Yl, s
 // (j < 8) and receives D[4*(l/16) + i][l%16] (i < 4).
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4p __attribute__((ext_vector_type(4)));
 
 constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LD = GB_K + 8;  // LDS row pitch in halfs
@@ -261,7 +290,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M,
                     if (m < M && n < N) P[((size_t)blockIdx.z * M + m) * N + n] = v;
                 } else if constexpr (EPI == EPI_SWIGLU) {
                     const float up = __shfl_xor(v, 1, 64);
-                    if ((fr & 1) == 0 && m < M && n < N) store_swiglu(Y, Yh, Yl, (size_t)m * ldy + n / 2, v, up);
+                    if ((fr & 1) == 0 && m < M && n < N) store_swiglu(Y, Yh, Yl, m, n / 2, ldy, v, up);
                 } else if (m < M && n < N) {
                     if constexpr (EPI == EPI_RESID)
                         Y[(size_t)m * ldy + n] += v;
@@ -319,7 +348,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, 
             const int n = n0 + tx * 4 + j;
             if (n >= N) continue;
             if constexpr (EPI == EPI_SWIGLU) {
-                if ((j & 1) == 0) store_swiglu(Y, Yh, Yl, (size_t)m * ldy + n / 2, acc[i][j], acc[i][j + 1]);
+                if ((j & 1) == 0) store_swiglu(Y, Yh, Yl, m, n / 2, ldy, acc[i][j], acc[i][j + 1]);
             } else if constexpr (EPI == EPI_RESID) {
                 Y[(size_t)m * ldy + n] += acc[i][j];
             } else {
@@ -343,7 +372,7 @@ __global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, i
             g += P[z * MN + 2 * i];
             u += P[z * MN + 2 * i + 1];
         }
-        store_swiglu(Y, Yh, Yl, m * ldy + n / 2, g, u);
+        store_swiglu(Y, Yh, Yl, (int)m, (int)(n / 2), ldy, g, u);
     } else {
         if (i >= MN) return;
         const size_t m = i / N, n = i % N;
@@ -361,20 +390,28 @@ __global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, i
 // once by the kernel that produces the activations) and every operand tile
 // moved global -> LDS by the DMA path (global_load_lds_dwordx4) through a
 // four-stage ring, so three K steps are in flight while one is multiplied.
-// Block tile 128 (m) x 256 (n), K step 32; four waves in a 2 x 2 arrangement,
-// each 64 x 128 = 4 x 8 tiles of the 16x16x32 instruction. A stage holds 16
-// groups of 16 rows x 64 bytes (A hi, A lo: 8 groups each; W: 16 groups), one
-// 1 KB DMA each; within a group, row r's 16-byte chunk c sits in slot
-// 4r + (c ^ ((r >> 2) & 3)), so the fragment reads of 16 lanes hit 16
-// different bank groups.
+// Block tile 128 (m) x 256 (n), K step 32, eight waves in a 2 x 4
+// arrangement, each 64 x 64 = 2 x 2 tiles of the 32x32x16 instruction. A stage
+// holds 32 groups of 16 rows x 64 bytes (A hi, A lo: 8 groups each; W: 16
+// groups), one 1 KB DMA each; within a group, row r's 16-byte chunk c sits in slot
+// 4r + (c ^ (((r >> 1) ^ (r >> 3)) & 3)), so the fragment reads of any 8
+// consecutive lanes hit 8 different 16-byte bank groups of a 128-byte bank
+// row, and those of any 16 lanes 16 different groups of a 256-byte row.
 constexpr int HL_M = 128, HL_N = 256, HL_K = 32, HL_ST = 4, HL_STAGE = 32768;
 
-__device__ __forceinline__ int hl_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+__device__ __forceinline__ int hl_slot(int r, int c) { return 4 * r + (c ^ tile_swz(r)); }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_hl(Mat W, const __half* Ah, const __half* Al, int M, int kz, int nm,
-                                                 int nn, float* Y, int ldy, const float* bias, __half* Yh, __half* Yl,
-                                                 float* P) {
+#ifndef LLM_HL_WAVES
+#define LLM_HL_WAVES 8
+#endif
+template <int EPI, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, const __half* Al, int M, int kz, int nm,
+                                                     int nn, float* Y, int ldy, const float* bias, __half* Yh,
+                                                     __half* Yl, float* P) {
+    // NW waves in a 2 x NW/2 arrangement; wave tile 64 x (256 / (NW/2)) as
+    // 2 x NJ tiles of the 32x32x16 instruction (on gfx950 it moves twice the
+    // operands per cycle of the 16x16x32 one)
+    constexpr int WN = NW / 2, NJ = HL_N / WN / 32, ND = 32 / NW;
     __shared__ __attribute__((aligned(1024))) char lds[HL_ST * HL_STAGE];
     const int N = W.rows, K = W.cols;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -387,84 +424,142 @@ __global__ __launch_bounds__(256) void k_gemm_hl(Mat W, const __half* Ah, const 
     const int z = blockIdx.y;
     const int m0 = mt * HL_M, n0 = nt * HL_N, kb = z * kz;
 
-    // this wave's eight DMA sources: wave 0 A hi, 1 A lo, 2 and 3 W
-    const __half* src[8];
+    // this wave's ND DMA sources: the stage's 32 groups of 16 rows are A hi
+    // (groups 0-7), A lo (8-15) and W (16-31), ND consecutive groups a wave;
+    // in the tiled layout each is one contiguous 1 KB piece, lane l's 16 bytes
+    // at 16 l, already in LDS slot order
+    const __half* src[ND];
+    // a K step advances 8 (A) or 16 (W) pieces; a wave's groups are all of one kind
+    const size_t kstep = wave * ND < 16 ? 8 * 512 : 16 * 512;
     {
-        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+        const int nkK = K / HL_K, kbs = kb / HL_K;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            if (wave < 2) {
-                const int row = min(m0 + 16 * i + r, M - 1);
-                src[i] = (wave == 0 ? Ah : Al) + (size_t)row * K + kb + 8 * c;
-            } else {
-                const int row = min(n0 + 16 * (i + 8 * (wave - 2)) + r, N - 1);
-                src[i] = (const __half*)W.w + (size_t)row * K + kb + 8 * c;
-            }
+        for (int i = 0; i < ND; i++) {
+            const int grp = wave * ND + i;
+            if (grp < 16)
+                src[i] = (grp < 8 ? Ah : Al) + (((size_t)mt * nkK + kbs) * 8 + (grp & 7)) * 512 + lane * 8;
+            else
+                src[i] = (const __half*)W.wt + (((size_t)nt * nkK + kbs) * 16 + (grp - 16)) * 512 + lane * 8;
         }
     }
+    const int nk = kz / HL_K;
     auto issue = [&](int ks) {
-        char* dst = lds + (ks % HL_ST) * HL_STAGE + wave * 8192;
+        char* dst = lds + (ks % HL_ST) * HL_STAGE + wave * ND * 1024;
 #pragma unroll
-        for (int i = 0; i < 8; i++)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + ks * HL_K),
+        for (int i = 0; i < ND; i++)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + kstep * ks),
                                              (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
     };
 
-    const int wm = wave >> 1, wn = wave & 1;
-    const int fslot = hl_slot(lane & 15, lane >> 4) * 16;
-    float4v acc[4][8];
+    // For 32x32x16 lane l supplies A[l%32][8*(l/32) + j] and B[8*(l/32) + j][l%32]
+    // (j < 8) and receives D[8*(r/4) + 4*(l/32) + r%4][l%32] (r < 16). A
+    // 32-row tile spans two 16-row LDS groups; K half kh of a 32-deep step is
+    // chunks 2kh and 2kh+1 of each row.
+    const int wm = wave / WN, wn = wave % WN;
+    const int fgrp = ((lane >> 4) & 1) * 1024;
+    const int fslot0 = hl_slot(lane & 15, lane >> 5) * 16 + fgrp;
+    const int fslot1 = hl_slot(lane & 15, 2 + (lane >> 5)) * 16 + fgrp;
+    float16v acc[2][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int j = 0; j < 8; j++) acc[i][j] = (float4v){0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
 
-    const int nk = kz / HL_K;
-    for (int p = 0; p < HL_ST - 1 && p < nk; p++) issue(p);
-    for (int ks = 0; ks < nk; ks++) {
-        // this wave's DMAs of stage ks are done (later stages may still be in
-        // flight) and its LDS reads of the previous step have returned; then
-        // every wave's are
-        const int pend = min(HL_ST - 2, nk - 1 - ks);
-        if (pend >= 2)
-            asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else if (pend == 1)
-            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // Waits until at most `pend` later stages of this wave's DMAs are in
+    // flight and its LDS reads have returned, then for every wave.
+    auto wait_bar = [&](int pend) {
+        // s_waitcnt immediates (vmcnt n, lgkmcnt 0, expcnt unconstrained); as
+        // builtins the compiler's own wait bookkeeping sees them
+        const int n = pend * ND;
+        asm volatile("" ::: "memory");
+        if (n >= 24)
+            __builtin_amdgcn_s_waitcnt(0x4078);
+        else if (n >= 16)
+            __builtin_amdgcn_s_waitcnt(0x4070);
+        else if (n >= 12)
+            __builtin_amdgcn_s_waitcnt(0x007C);
+        else if (n >= 8)
+            __builtin_amdgcn_s_waitcnt(0x0078);
+        else if (n >= 4)
+            __builtin_amdgcn_s_waitcnt(0x0074);
         else
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // the ring slot of step ks - 1 is free now
-        if (ks + HL_ST - 1 < nk) issue(ks + HL_ST - 1);
+            __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    struct Frag {
+        half8 ah[2][2], al[2][2], bf[NJ][2];  // [tile][K half]
+    };
+    auto fread = [&](int ks, Frag& F) {
         const char* st = lds + (ks % HL_ST) * HL_STAGE;
-        half8 ah[4], al[4], bf[8];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            ah[i] = *(const half8*)(st + (4 * wm + i) * 1024 + fslot);
-            al[i] = *(const half8*)(st + 8192 + (4 * wm + i) * 1024 + fslot);
+        for (int i = 0; i < 2; i++) {
+            const char* a = st + (4 * wm + 2 * i) * 1024;
+            F.ah[i][0] = *(const half8*)(a + fslot0);
+            F.ah[i][1] = *(const half8*)(a + fslot1);
+            F.al[i][0] = *(const half8*)(a + 8192 + fslot0);
+            F.al[i][1] = *(const half8*)(a + 8192 + fslot1);
         }
 #pragma unroll
-        for (int j = 0; j < 8; j++) bf[j] = *(const half8*)(st + 16384 + (8 * wn + j) * 1024 + fslot);
+        for (int j = 0; j < NJ; j++) {
+            const char* b = st + 16384 + (2 * NJ * wn + 2 * j) * 1024;
+            F.bf[j][0] = *(const half8*)(b + fslot0);
+            F.bf[j][1] = *(const half8*)(b + fslot1);
+        }
+    };
+    auto fmma = [&](const Frag& F) {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int kh = 0; kh < 2; kh++)
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bf[j], acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], bf[j], acc[i][j], 0, 0, 0);
-            }
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < NJ; j++) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.ah[i][kh], F.bf[j][kh], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.al[i][kh], F.bf[j][kh], acc[i][j], 0, 0, 0);
+                }
+    };
+    // Stage s lives in ring slot s % HL_ST. The fragments of step ks are read
+    // during step ks - 1, so while step ks multiplies, the slots hold steps
+    // ks+1 (landed) .. ks+HL_ST (in flight).
+    for (int p = 0; p < HL_ST && p < nk; p++) issue(p);
+    wait_bar(min(HL_ST - 1, nk - 1));
+    Frag F0, F1;
+    fread(0, F0);
+    // One K step: wait for the next step's stage (the last step re-reads its
+    // own), refill the slot this step was read from, read the next fragments,
+    // multiply the current ones. No branch guards the reads or the products,
+    // so the compiler keeps one register assignment and a partial LDS wait.
+    auto step = [&](int ks, Frag& cur, Frag& nxt) {
+        wait_bar(min(HL_ST - 2, max(nk - 2 - ks, 0)));
+        if (ks + HL_ST < nk) issue(ks + HL_ST);
+        fread(min(ks + 1, nk - 1), nxt);
+        // keep the reads ahead of the products, so LDS and the matrix cores
+        // work at the same time
+        __builtin_amdgcn_sched_barrier(0);
+        fmma(cur);
+    };
+    for (int ks = 0; ks + 1 < nk; ks += 2) {
+        step(ks, F0, F1);
+        step(ks + 1, F1, F0);
     }
+    if (nk & 1) step(nk - 1, F0, F1);
 
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int n = n0 + 128 * wn + 16 * j + (lane & 15);
+    for (int j = 0; j < NJ; j++) {
+        const int n = n0 + 32 * NJ * wn + 32 * j + (lane & 31);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 2; i++) {
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int m = m0 + 64 * wm + 16 * i + (lane >> 4) * 4 + e;
+            for (int e = 0; e < 16; e++) {
+                const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 const float v = acc[i][j][e];
                 if (P) {
                     if (m < M && n < N) P[((size_t)z * M + m) * N + n] = v;
                 } else if constexpr (EPI == EPI_SWIGLU) {
                     const float up = __shfl_xor(v, 1, 64);
-                    if ((lane & 1) == 0 && m < M && n < N) store_swiglu(Y, Yh, Yl, (size_t)m * ldy + n / 2, v, up);
+                    if ((lane & 1) == 0 && m < M && n < N) store_swiglu(Y, Yh, Yl, m, n / 2, ldy, v, up);
                 } else if (m < M && n < N) {
                     if constexpr (EPI == EPI_RESID)
                         Y[(size_t)m * ldy + n] += v;
@@ -496,10 +591,11 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
     if (W.dtype == DT_F32) {
         dim3 grid((N + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
         hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl);
-    } else if (W.dtype == DT_F16 && A.h && K % HL_K == 0) {
+    } else if (W.dtype == DT_F16 && W.wt && A.h && K % HL_K == 0) {
         S = gemm_splits(n, N, K, HL_M, HL_N, 8, ws_floats);
         const int nm = (n + HL_M - 1) / HL_M, nn = (N + HL_N - 1) / HL_N;
-        hipLaunchKernelGGL((k_gemm_hl<EPI>), dim3(nm * nn, S), dim3(256), 0, s, W, (const __half*)A.h,
+        hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES), 0, s, W,
+                           (const __half*)A.h,
                            (const __half*)A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr);
     } else {
         S = gemm_splits(n, N, K, GB_M, GB_N, 4, ws_floats);
@@ -698,11 +794,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
 #pragma unroll
         for (int dt = 0; dt < 4; dt++) {
             const float v = o[dt][i] / l_run[i];
-            const size_t e = (size_t)z * qd + h * hd + 16 * dt + lr;
-            out[e] = v;
+            const int col = h * hd + 16 * dt + lr;
+            out[(size_t)z * qd + col] = v;
             const __half hh = __float2half_rn(v);
-            out_h[e] = hh;
-            out_l[e] = __float2half_rn(v - __half2float(hh));
+            const size_t t = tile_off(z, col, qd, kTileA);
+            out_h[t] = hh;
+            out_l[t] = __float2half_rn(v - __half2float(hh));
         }
     }
 }

@@ -211,7 +211,13 @@ Mat place_mat(Arena& A, int dtype, int rows, int cols) {
     m.cols = cols;
     m.w = A.take(mat_bytes_w(dtype, rows, cols));
     m.s = dtype == DT_Q8 ? (const uint16_t*)A.take(mat_bytes_s(dtype, rows, cols)) : nullptr;
+    m.wt = nullptr;
     return m;
+}
+
+// Layer matrices in F16 also get the tiled copy the prefill products read.
+void place_tiled(Arena& A, Mat& m) {
+    if (m.dtype == DT_F16 && m.cols % 32 == 0) m.wt = A.take(tiled_w_bytes(m.rows, m.cols));
 }
 
 int decode_splits(const llm_config* c) {
@@ -239,6 +245,10 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
         D.ffn_norm = (const float*)W.take((size_t)c->dim * 4);
         D.gu = place_mat(W, S.gate->dtype, 2 * c->ffn, c->dim);
         D.down = place_mat(W, S.down->dtype, c->dim, c->ffn);
+        place_tiled(W, D.qkv);
+        place_tiled(W, D.o);
+        place_tiled(W, D.gu);
+        place_tiled(W, D.down);
     }
     L.wbytes = W.off;
 
@@ -635,6 +645,11 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
             ok = upload(D.bqkv, b.data(), b.size() * 4);
         }
     }
+    for (int l = 0; ok && l < cfg->n_layers; l++) {
+        const LayerW& D = L.layers[l];
+        for (const Mat* m : {&D.qkv, &D.o, &D.gu, &D.down})
+            if (m->wt) ok = ok && launch_tile_w(*m, (void*)m->wt, s) == hipSuccess;
+    }
     if (!ok) return bail(LLM_ERR_DEVICE, "weight upload failed");
 
     // ---- RoPE table and zeroed state
@@ -807,7 +822,7 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
                                                    cf.head_dim, cf.n_ctx, t.scale_div, s));
             } else {
                 HIPCHK(c, launch_attn(t, m, s));
-                if (W.o.dtype == DT_F16) HIPCHK(c, launch_split_hl(L.Of, (size_t)m * qd, L.Oh, L.Ol, s));
+                if (W.o.dtype == DT_F16) HIPCHK(c, launch_split_hl(L.Of, m, qd, L.Oh, L.Ol, s));
             }
             HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{L.Of, L.Oh, L.Ol}, m, L.X, cf.dim, nullptr, nullptr, nullptr,
                                   L.ws, L.ws_floats, s));
