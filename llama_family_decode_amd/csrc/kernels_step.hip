@@ -408,8 +408,9 @@ __device__ __forceinline__ void pf_clear(PF& pf) {
     }
 }
 
-// Issues the loads of slots k0 .. k0 + kPF - 1 into pf. Addresses past the
-// rows, slots or window are clamped to valid ones; wdot ignores their values.
+// Issues the loads of slots k0 .. k0 + kPF - 1 (those below nslots) into pf.
+// Rows and chunks past the window are clamped to valid ones; wdot ignores
+// their values.
 // Nothing here waits for the data. rmap (or nullptr) maps wave rows to matrix
 // rows, else matrix row = roff + row.
 template <int DT>
@@ -424,13 +425,18 @@ __device__ __forceinline__ void wload(const WRows& w, const int* rmap, int roff,
     int g = k0 / w.ncb, cb = k0 - g * w.ncb;
 #pragma unroll
     for (int k = 0; k < kPF; k++) {
-        int row = w.r0 + g * w.rpi + sub;
-        row = row < w.r1 ? row : w.r1 - 1;
-        const long long ar = rmap ? rmap[row] : roff + row;
-        int c = cl + (cb << w.lsh);
-        c = c < w.W.nch ? c : w.W.nch - 1;
-        pf.q[k] = ld_nt(w.W.w + (ar * w.W.ld * ES + (long long)c * 16));
-        if constexpr (DT == DT_Q8) pf.s[k] = ld_u16(w.W.s + (ar * (w.W.ld / 32) + (c >> 1)));
+        if (k0 + k < w.nslots) {  // wave-uniform; slots past the wave's rows load nothing
+            int row = w.r0 + g * w.rpi + sub;
+            row = row < w.r1 ? row : w.r1 - 1;
+            const long long ar = rmap ? rmap[row] : roff + row;
+            int c = cl + (cb << w.lsh);
+            c = c < w.W.nch ? c : w.W.nch - 1;
+            pf.q[k] = ld_nt(w.W.w + (ar * w.W.ld * ES + (long long)c * 16));
+            if constexpr (DT == DT_Q8) pf.s[k] = ld_u16(w.W.s + (ar * (w.W.ld / 32) + (c >> 1)));
+        } else {
+            pf.q[k] = (u32x4){0u, 0u, 0u, 0u};
+            pf.s[k] = 0u;
+        }
         if (++cb == w.ncb) {
             cb = 0;
             ++g;
