@@ -95,6 +95,7 @@ struct StepArgs {
     unsigned long long* trace;  // nullptr, or wall-clock stamps of block 0 after each barrier
     int dim, n_heads, n_kv_heads, head_dim, n_rot, neox, n_ctx, ffn, vocab;
     int lds_xr, lds_xs, lds_wsp;  // LDS regions (floats)
+    int lds_lw;                   // LDS offset (floats) of the copy of the layer table
     float eps, scale_div;
 };
 

@@ -42,6 +42,7 @@
 
 namespace llm {
 
+static_assert(sizeof(LayerW) % 8 == 0, "the layer table is copied in 8-byte words");
 constexpr int kSpinLimit = 4 << 20;
 constexpr int kSB = 512;       // threads per block
 constexpr int kSW = kSB / 64;  // waves per block
@@ -1063,6 +1064,11 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     float* ored = wsp + a.lds_wsp;         // merge partial sums [kSB]
     float2* cs = (float2*)(ored + kSB);    // RoPE (cos, sin) of this position, kMaxHeadDim/2 pairs
     int* qmap = (int*)(cs + kMaxHeadDim / 2);  // the group's q/k/v rows in RoPE-pair order
+    // the layer descriptors, copied once, so that the address of a phase's
+    // weights is an LDS read rather than a dependent load from device memory
+    LayerW* lw = (LayerW*)(sm + a.lds_lw);
+    for (int i = tid; i < a.n_layers * (int)(sizeof(LayerW) / 8); i += kSB)
+        ((unsigned long long*)lw)[i] = ((const unsigned long long*)a.layers)[i];
 
     const unsigned long long nloc = 3ull * a.n_layers, ncro = 2ull * a.n_layers + 1;
     unsigned long long jl = (unsigned long long)epoch * nloc, jc = (unsigned long long)epoch * ncro;
@@ -1131,8 +1137,8 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
             for (int i_ = 0; i_ < kStepAttn; i_++) kr[i_] = vr[i_] = (u32x4){0u, 0u, 0u, 0u}; \
         }                                                                                   \
     } while (0)
-    gain_load(gp, a.layers[0].attn_norm, a.dim);
-    wq.W = make_win<DT>(a.layers[0].qkv, 0, a.dim);
+    gain_load(gp, lw[0].attn_norm, a.dim);
+    wq.W = make_win<DT>(lw[0].qkv, 0, a.dim);
     wload<DT>(wq, qmap, 0, 0, pf);
     KV_PREFETCH(0);
     pin();
@@ -1145,9 +1151,9 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         float* pd = a.pd + (size_t)l * kNG * a.pstride;
 
         // ---- QKV
-        stage_norm<DT>(xr, a.layers[l].attn_norm, gp, a.eps, a.dim, xs, red);
+        stage_norm<DT>(xr, lw[l].attn_norm, gp, a.eps, a.dim, xs, red);
         ea.out = qkv;
-        ea.bias = a.layers[l].bqkv;
+        ea.bias = lw[l].bqkv;
         ea.kc = a.kc + (size_t)l * a.kv_layer;
         ea.vc = a.vc + (size_t)l * a.kv_layer;
         wrun<DT, EM_QKV, GQ>(wq, qmap, 0, xs, pf, true, ea, best, bi, nfin);
@@ -1168,7 +1174,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         }
         wait_mem();
         group_arrive(a, x);
-        wo.W = make_win<DT>(a.layers[l].o, hlo * G * hd, nh * G * hd);
+        wo.W = make_win<DT>(lw[l].o, hlo * G * hd, nh * G * hd);
         wload<DT>(wo, nullptr, 0, 0, pf);
         pin();
         group_wait(a, x, ++jl * bg);
@@ -1182,8 +1188,8 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         }
         wait_mem();
         all_arrive(a, x);
-        gain_load(gp, a.layers[l].ffn_norm, a.dim);
-        wg.W = make_win<DT>(a.layers[l].gu, 0, a.dim);
+        gain_load(gp, lw[l].ffn_norm, a.dim);
+        wg.W = make_win<DT>(lw[l].gu, 0, a.dim);
         wload<DT>(wg, nullptr, 2 * flo, 0, pf);
         pin();
         all_wait(a, ++jc * bg);
@@ -1191,12 +1197,12 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
 
         // ---- residual, RMSNorm, gate/up + SwiGLU
         add_partials(xr, po, a.pstride, a.dim, hmask);
-        stage_norm<DT>(xr, a.layers[l].ffn_norm, gp, a.eps, a.dim, xs, red);
+        stage_norm<DT>(xr, lw[l].ffn_norm, gp, a.eps, a.dim, xs, red);
         ea.out = u + flo;
         wrun<DT, EM_SWIGLU, GG>(wg, nullptr, 2 * flo, xs, pf, true, ea, best, bi, nfin);
         wait_mem();
         group_arrive(a, x);
-        wd.W = make_win<DT>(a.layers[l].down, flo, nf);
+        wd.W = make_win<DT>(lw[l].down, flo, nf);
         wload<DT>(wd, nullptr, 0, 0, pf);
         pin();
         group_wait(a, x, ++jl * bg);
@@ -1211,8 +1217,8 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         wait_mem();
         all_arrive(a, x);
         if (l + 1 < a.n_layers) {
-            gain_load(gp, a.layers[l + 1].attn_norm, a.dim);
-            wq.W = make_win<DT>(a.layers[l + 1].qkv, 0, a.dim);
+            gain_load(gp, lw[l + 1].attn_norm, a.dim);
+            wq.W = make_win<DT>(lw[l + 1].qkv, 0, a.dim);
             wload<DT>(wq, qmap, 0, 0, pf);
             KV_PREFETCH(l + 1);
         } else {
@@ -1280,7 +1286,10 @@ bool step_lds_plan(StepArgs& a, int dtype, int* lds_bytes) {
     a.lds_xs = (xs + 63) / 64 * 64;
     a.lds_wsp = (nh_max * G * kStepMaxSplit + 63) / 64 * 64;
     const int qmap = nh_max * (G + 2) * hd;  // ints
-    const int total = a.lds_xr + a.lds_xs + a.lds_wsp + kSB + kMaxHeadDim + qmap;
+    int total = a.lds_xr + a.lds_xs + a.lds_wsp + kSB + kMaxHeadDim + qmap;
+    total = (total + 1) & ~1;  // 8-byte alignment for the layer table
+    a.lds_lw = total;
+    total += a.n_layers * (int)(sizeof(LayerW) / 4);
     *lds_bytes = total * (int)sizeof(float);
     return *lds_bytes <= 150 * 1024;
 }
