@@ -1,0 +1,166 @@
+"""Full-size checks in the launch configuration bench.py times (needs an MI355X).
+
+The oracle cannot run the whole 1B model through a 2048-position prompt in a
+test's time, so at these sizes the checks are outputs the oracle computes one
+at a time, plus properties that hold at any size:
+  - layer-0 K and V rows at sampled positions depend only on that position's
+    token, so the oracle computes them directly (RMSNorm, the K/V products,
+    bias, RoPE, binary16 rounding; "The Forward Pass in Java", Examples 4, 5,
+    6 and 10): rows the decode path wrote agree within 2 binary16 ulps, rows
+    the matrix-core prefill wrote within the logit tolerance of the head rms;
+  - the greedy token is the first index of the strict maximum of the GPU's own
+    logits, bit for bit ("The Forward Pass in Java", Example 9);
+  - the KV length is the prompt plus the decoded steps;
+  - the decode path bench.py times (the shape-compiled persistent kernel) and
+    the launch-graph path (separate kernels) agree within the logit tolerance
+    on every teacher-forced step, and a second run repeats bit for bit;
+  - the 512-token matrix-core prefill agrees with the same tokens decoded one
+    at a time, within the logit tolerance.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from test_gpu_parity import f16_ulp_diff, first_max, tol
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import llama_family_decode_amd as llm
+
+
+def _tensors_by_name(ts):
+    return {t.name: t for t in ts}
+
+
+def _row(t, dim, row):
+    """Row `row` of a [rows][dim] tensor, dequantized to fp32 by the oracle."""
+    if t.dtype == 8:  # Q8_0: 34 bytes per block of 32
+        nb = dim // 32 * 34
+        raw = t.data[row * nb:(row + 1) * nb]
+    else:
+        es = 4 if t.dtype == 0 else 2
+        raw = t.data[row * dim * es:(row + 1) * dim * es]
+    return oracle.dequantize(t.dtype, raw, dim)
+
+
+def layer0_kv_oracle(cfg, T, token, pos):
+    """Binary16 bits of layer 0's K and V rows for `token` at `pos`."""
+    x = _row(T["token_embd.weight"], cfg.dim, int(token))
+    h = oracle.rmsnorm(x, oracle.dequantize(0, T["blk.0.attn_norm.weight"].data, cfg.dim), cfg.eps)
+    kvd = cfg.kv_dim
+    out = []
+    for name, bias_name in (("blk.0.attn_k.weight", "blk.0.attn_k.bias"), ("blk.0.attn_v.weight", "blk.0.attn_v.bias")):
+        t = T[name]
+        w = oracle.dequantize(t.dtype, t.data, kvd * cfg.dim)
+        v = oracle.matvec(w, h, kvd, cfg.dim)
+        if bias_name in T:
+            v = v + oracle.dequantize(0, T[bias_name].data, kvd)
+        if name.endswith("attn_k.weight"):
+            v = oracle.rope(v, cfg.n_kv_heads, cfg.head_dim, cfg.n_rot, pos, cfg.rope_base, cfg.rope_neox)
+        out.append(np.array([oracle.f32_to_f16(float(e)) for e in v], np.uint16))
+    return out
+
+
+def check_layer0_kv(cfg, T, model, tokens_at, max_ulps):
+    """Layer-0 K/V rows against the oracle's. Rows written by the decode path
+    see fp32 activations on both sides and may differ only by binary16
+    rounding flips (max_ulps = 2). Rows written by the matrix-core prefill
+    (max_ulps None) are held to the logit tolerance relative to the head's rms,
+    plus 2 ulps, as the parity suite holds every layer."""
+    worst = 0.0
+    for pos, tok in tokens_at:
+        kg, vg = model.kv_read(0, pos)
+        ko, vo = layer0_kv_oracle(cfg, T, tok, pos)
+        for g, o in ((kg, ko), (vg, vo)):
+            if max_ulps is not None:
+                worst = max(worst, float(f16_ulp_diff(g, o, cfg.head_dim).max()))
+            else:
+                a = g.view(np.float16).astype(np.float64).reshape(-1, cfg.head_dim)
+                b = o.view(np.float16).astype(np.float64).reshape(-1, cfg.head_dim)
+                rms = np.sqrt(np.mean(b * b, axis=1, keepdims=True)) + 1e-30
+                ulp = np.spacing(np.maximum(np.abs(a), np.abs(b)).astype(np.float16)).astype(np.float64)
+                worst = max(worst, float(((np.abs(a - b) - 2 * ulp) / rms).max()))
+    if max_ulps is not None:
+        assert worst <= max_ulps, f"layer-0 KV differs from the oracle by {worst} binary16 ulps"
+    else:
+        assert worst <= tol(cfg), f"layer-0 KV differs from the oracle by {worst:.3e} of the head rms"
+    return worst
+
+
+def test_c4_decode_at_2048_in_the_benchmarked_kernel(monkeypatch):
+    cfg = synth.C4  # 1B shape, Q8_0 layers, tied F32 embedding, n_ctx 8320
+    ts = synth.make_tensor_set(cfg)
+    T = _tensors_by_name(ts)
+    toks = synth.prompt(cfg, 2048)
+    n_steps = 6
+
+    def run(kind_env):
+        monkeypatch.setenv("LLM_STEP", kind_env)
+        m = llm.Model(cfg, ts)
+        nxt = m.prefill(toks)
+        feed, logits, nexts = [], [], []
+        t, pos = nxt, len(toks)
+        for _ in range(n_steps):
+            feed.append((pos, int(t)))
+            n2 = m.decode(int(t), pos)
+            logits.append(m.logits())
+            nexts.append(n2)
+            t, pos = n2, pos + 1
+        return m, feed, logits, nexts
+
+    step, feed, lg_step, nx_step = run("persistent")
+    assert llm.llm_op_step_kind(step.ctx) == 2, "the benchmark shape must run the shape-compiled step kernel"
+    assert step.kv_len() == len(toks) + n_steps
+    for lg, nx in zip(lg_step, nx_step):
+        assert np.all(np.isfinite(lg))
+        assert nx == first_max(lg)
+    w0 = check_layer0_kv(cfg, T, step, feed, 2.0)
+    wp = check_layer0_kv(cfg, T, step, [(0, toks[0]), (1024, toks[1024]), (2047, toks[2047])], None)
+
+    # the independent launch-graph path, teacher-forced with the same tokens
+    monkeypatch.setenv("LLM_STEP", "graph")
+    g = llm.Model(cfg, ts)
+    assert llm.llm_op_step_kind(g.ctx) == 0
+    g.prefill(toks)
+    worst = 0.0
+    for (pos, tok), lg in zip(feed, lg_step):
+        g.decode(tok, pos)
+        worst = max(worst, float(np.max(np.abs(g.logits().astype(np.float64) - lg))))
+    assert worst <= tol(cfg), f"persistent vs graph: max |dlogit| {worst:.3e}"
+    g.close()
+
+    # a second persistent run repeats bit for bit
+    step.close()
+    again, _, lg2, nx2 = run("persistent")
+    assert nx2 == nx_step
+    for a, b in zip(lg_step, lg2):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    again.close()
+    print(f"[C4 ctx 2048] layer-0 KV: decode rows {w0} ulps, prefill rows {wp:.2e} rms; persistent vs graph "
+          f"{worst:.3e}", flush=True)
+
+
+def test_c5_prefill_512_against_decode_and_oracle(monkeypatch):
+    cfg = synth.C5  # Qwen2-style 1B, F16, NEOX RoPE, QKV bias
+    ts = synth.make_tensor_set(cfg)
+    T = _tensors_by_name(ts)
+    toks = synth.prompt(cfg, 512)
+    monkeypatch.setenv("LLM_STEP", "persistent")
+    pre = llm.Model(cfg, ts)
+    nxt = pre.prefill(toks)
+    lp = pre.logits()
+    assert pre.kv_len() == 512
+    assert np.all(np.isfinite(lp)) and nxt == first_max(lp)
+    w0 = check_layer0_kv(cfg, T, pre, [(p, toks[p]) for p in (0, 1, 127, 128, 255, 256, 383, 511)], None)
+    dec = llm.Model(cfg, ts)
+    for p, t in enumerate(toks):
+        dec.decode(int(t), p)
+    ld = dec.logits()
+    err = float(np.max(np.abs(lp.astype(np.float64) - ld)))
+    assert err <= tol(cfg), f"prefill vs token-by-token decode: max |dlogit| {err:.3e}"
+    pre.close()
+    dec.close()
+    print(f"[C5 prefill 512] layer-0 KV {w0:.2e} rms, prefill vs decode {err:.3e}", flush=True)
