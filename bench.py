@@ -14,6 +14,8 @@ compiled for this shape). The line also reports
     (every weight once, the K/V rows 0..pos, the new K/V row); HBM traffic
     from the committed rocprofv3 counter runs;
   - prefill: llm_prefill of 512 seeded ids on the Qwen2-style F16 variant;
+  - decode_reports: the same decode with F16 matrices at context 2048, and
+    with Q8_0 at context 8192 (attention a larger share of the bytes);
   - cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 8]
@@ -126,6 +128,37 @@ def measure_prefill(llm, synth, np, torch, reps=5):
             "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
 
 
+def measure_decode_report(llm, synth, np, torch, cfg, ctx_len, steps=64, reps=3):
+    """A reported (not headline) decode workload: llm_prefill of ctx_len seeded
+    ids, then `steps` greedy steps by llm_generate, median of `reps`."""
+    ts = synth.make_tensor_set(cfg)
+    m = llm.Model(cfg, ts)
+    del ts
+    nxt = m.prefill(synth.prompt(cfg, ctx_len))
+    m.generate(nxt, 4)
+    m.rewind(ctx_len)
+    times = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        m.generate(nxt, steps)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        m.rewind(ctx_len)
+    kind = llm.llm_op_step_kind(m.ctx)
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    dt = float(np.median(times))
+    tok_s = steps / dt
+    b = algorithmic_step_bytes(cfg, ctx_len + steps // 2)
+    print(f"# report {cfg.name} ctx {ctx_len}: {tok_s:.1f} tok/s, {b * tok_s / 1e9:.0f} GB/s", file=sys.stderr,
+          flush=True)
+    return {"config": cfg.name, "ctx": ctx_len, "steps": steps, "tok_s": round(tok_s, 1),
+            "ms_per_token": round(1e3 * dt / steps, 4), "bytes_per_token": b,
+            "hbm_frac": round(b * tok_s / 1e9 / HBM_PEAK_GBS, 4), "step_kind": kind}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +167,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of the timed decode run (median)")
+    ap.add_argument("--no-reports", action="store_true",
+                    help="skip the reported decode workloads (F16 1B at ctx 2048, Q8_0 1B at ctx 8192)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill measurement (512 ids, Qwen2-style F16 1B) and print it as JSON")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -216,6 +251,11 @@ def main():
     if not args.no_prefill:
         prefill = measure_prefill(llm, synth, np, torch)
 
+    reports = None
+    if not args.no_reports:
+        reports = [measure_decode_report(llm, synth, np, torch, synth.C3, 2048),
+                   measure_decode_report(llm, synth, np, torch, synth.C4_LONG, 8192)]
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg)
@@ -243,6 +283,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
                      "bytes_per_launch": step_bytes, "ms_per_launch": round(ms_step, 5), "position": mid_pos},
         "prefill": prefill,
+        "decode_reports": reports,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
