@@ -14,8 +14,9 @@ compiled for this shape). The line also reports
     (every weight once, the K/V rows 0..pos, the new K/V row); HBM traffic
     from the committed rocprofv3 counter runs;
   - prefill: llm_prefill of 512 seeded ids on the Qwen2-style F16 variant;
-  - decode_reports: the same decode with F16 matrices at context 2048, and
-    with Q8_0 at context 8192 (attention a larger share of the bytes);
+  - decode_reports: the same decode with F16 matrices at context 2048, with
+    Q8_0 at context 8192 (attention a larger share of the bytes), and with
+    Llama 3's RoPE frequency factors (rope_freqs.weight);
   - cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 8]
@@ -44,6 +45,8 @@ def algorithmic_step_bytes(cfg, pos):
         n = 1
         for e in ne:
             n *= e
+        if name == "rope_freqs.weight":  # consumed at load into the RoPE table
+            continue
         if name == "token_embd.weight":
             total += synth.nbytes_of(dt, cfg.dim * cfg.vocab) if cfg.tied else synth.nbytes_of(dt, cfg.dim)
             continue
@@ -168,7 +171,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--reps", type=int, default=5, help="repetitions of the timed decode run (median)")
     ap.add_argument("--no-reports", action="store_true",
-                    help="skip the reported decode workloads (F16 1B at ctx 2048, Q8_0 1B at ctx 8192)")
+                    help="skip the reported decode workloads (F16 1B at ctx 2048, Q8_0 1B at ctx 8192, "
+                         "Q8_0 1B with RoPE frequency factors)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill measurement (512 ids, Qwen2-style F16 1B) and print it as JSON")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -254,7 +258,9 @@ def main():
     reports = None
     if not args.no_reports:
         reports = [measure_decode_report(llm, synth, np, torch, synth.C3, 2048),
-                   measure_decode_report(llm, synth, np, torch, synth.C4_LONG, 8192)]
+                   measure_decode_report(llm, synth, np, torch, synth.C4_LONG, 8192),
+                   measure_decode_report(llm, synth, np, torch,
+                                         synth.C4.with_(name="llama-1b-q8_0-rope-freqs", rope_freq_factors=True), 2048)]
 
     cpu = None
     if not args.no_cpu:

@@ -103,8 +103,12 @@ int llm_plan(const llm_config* cfg, const llm_tensor* tensors, int32_t n_tensors
  * ffn_down.weight [ffn, dim]. Optional: output.weight [dim, vocab] (absent means
  * the output product reuses token_embd, "tied embeddings", Example 9) and
  * blk.l.attn_{q,k,v}.bias (all three or none; added after the product and
- * before RoPE, Project 18). Matrices may be F32, F16 or Q8_0 (q, k and v share
- * one type, as do gate and up); norm gains and biases are F32.
+ * before RoPE, Project 18), and rope_freqs.weight [rope_dims/2]: one divisor
+ * per RoPE pair, pair i's angle theta_i becomes theta_i / f_i (Llama 3's
+ * frequency factors, "What a Llama model computes, and why", sections 2.4 and
+ * 6); its values must be finite and positive (LLM_ERR_ARG from
+ * llm_load_weights otherwise). Matrices may be F32, F16 or Q8_0 (q, k and v
+ * share one type, as do gate and up); norm gains, biases and divisors are F32.
  *
  * Limits (LLM_ERR_LIMIT): every matrix width (`in`) is a multiple of 32 and at
  * most 16384; head_dim is a multiple of 8 and at most 256; n_heads/n_kv_heads

@@ -294,19 +294,22 @@ hipError_t launch_gemv(int pro, int epi, const GemvArgs& a, int grid, hipStream_
 // Row p holds (cos, sin) of theta_i for i < n_rot/2 ("The Forward Pass in Java",
 // Example 6): theta starts at (float)p and is multiplied by theta_scale in float
 // once per pair; cos and sin are evaluated in double and rounded to float.
-__global__ void k_rope_table(float2* tab, int n_pos, int half, float theta_scale) {
+__global__ void k_rope_table(float2* tab, int n_pos, int half, float theta_scale, const float* freq) {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= n_pos) return;
     float theta = (float)p;
     for (int i = 0; i < half; i++) {
-        tab[(size_t)p * half + i] = make_float2((float)cos((double)theta), (float)sin((double)theta));
+        // Llama 3 frequency factors divide pair i's angle ("What a Llama model
+        // computes, and why", sections 2.4 and 6)
+        const float angle = freq ? theta / freq[i] : theta;
+        tab[(size_t)p * half + i] = make_float2((float)cos((double)angle), (float)sin((double)angle));
         theta = theta * theta_scale;
     }
 }
 
-hipError_t launch_rope_table(float2* tab, int n_pos, int n_rot, float theta_scale, hipStream_t s) {
+hipError_t launch_rope_table(float2* tab, int n_pos, int n_rot, float theta_scale, const float* freq, hipStream_t s) {
     const int half = n_rot / 2;
-    hipLaunchKernelGGL(k_rope_table, dim3((n_pos + 255) / 256), dim3(256), 0, s, tab, n_pos, half, theta_scale);
+    hipLaunchKernelGGL(k_rope_table, dim3((n_pos + 255) / 256), dim3(256), 0, s, tab, n_pos, half, theta_scale, freq);
     return hipGetLastError();
 }
 

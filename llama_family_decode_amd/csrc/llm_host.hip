@@ -45,6 +45,7 @@ struct Validated {
     const llm_tensor* embd;
     const llm_tensor* out;  // null when tied
     const llm_tensor* out_norm;
+    const llm_tensor* rope_freqs;  // optional per-pair RoPE divisors
     struct L {
         const llm_tensor *attn_norm, *q, *k, *v, *bq, *bk, *bv, *o, *ffn_norm, *gate, *up, *down;
     };
@@ -121,6 +122,9 @@ int validate(const llm_config* c, const llm_tensor* ts, int32_t n, Validated& V,
     if ((rc = check_tensor(V.out_norm, "output_norm.weight", c->dim, 0, false, err))) return rc;
     V.out = find(ts, n, "output.weight");
     if (V.out && (rc = check_tensor(V.out, "output.weight", c->dim, c->vocab, true, err))) return rc;
+    V.rope_freqs = find(ts, n, "rope_freqs.weight");
+    if (V.rope_freqs && (rc = check_tensor(V.rope_freqs, "rope_freqs.weight", c->rope_dims / 2, 0, false, err)))
+        return rc;
     V.layers.resize(c->n_layers);
     char nm[128];
     int n_bias = 0;
@@ -189,6 +193,7 @@ struct Layout {
     // scratch
     State* st;
     float2* rope;
+    const float* rope_freqs;  // device copy of rope_freqs.weight or nullptr
     float *x, *q, *ao, *u, *logits, *attn_part;
     int *gen_out, *ptok;
     LayerW* dlayers;  // device copy of the layer table (persistent step kernel)
@@ -234,6 +239,7 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.embd = place_mat(W, V.embd->dtype, c->vocab, c->dim);
     L.out_norm = (const float*)W.take((size_t)c->dim * 4);
     L.out = V.out ? place_mat(W, V.out->dtype, c->vocab, c->dim) : L.embd;
+    L.rope_freqs = V.rope_freqs ? (const float*)W.take((size_t)(c->rope_dims / 2) * 4) : nullptr;
     L.layers.resize(c->n_layers);
     for (int l = 0; l < c->n_layers; l++) {
         const Validated::L& S = V.layers[l];
@@ -569,6 +575,14 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         g_load_error = err;
         return rc;
     }
+    if (V.rope_freqs) {  // values are read only here (llm_plan may see placeholder data)
+        const float* f = (const float*)V.rope_freqs->data;
+        for (int i = 0; i < cfg->rope_dims / 2; i++)
+            if (!(f[i] > 0.f) || !isfinite(f[i])) {
+                g_load_error = "rope_freqs.weight must hold finite positive divisors";
+                return LLM_ERR_ARG;
+            }
+    }
     Layout M;
     make_layout(cfg, V, nullptr, nullptr, nullptr, M);
     llm_ctx* c = new llm_ctx();
@@ -630,6 +644,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         return true;
     };
     bool ok = upload_mat(L.embd, {V.embd}, 0) && upload(L.out_norm, V.out_norm->data, (size_t)cfg->dim * 4);
+    if (ok && V.rope_freqs) ok = upload(L.rope_freqs, V.rope_freqs->data, (size_t)(cfg->rope_dims / 2) * 4);
     if (ok && V.out) ok = upload_mat(L.out, {V.out}, 0);
     for (int l = 0; ok && l < cfg->n_layers; l++) {
         const Validated::L& S = V.layers[l];
@@ -654,7 +669,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
 
     // ---- RoPE table and zeroed state
     const float theta_scale = (float)pow((double)cfg->rope_base, -2.0 / cfg->rope_dims);
-    if (launch_rope_table(L.rope, cfg->n_ctx, cfg->rope_dims, theta_scale, s) != hipSuccess ||
+    if (launch_rope_table(L.rope, cfg->n_ctx, cfg->rope_dims, theta_scale, L.rope_freqs, s) != hipSuccess ||
         hipMemsetAsync(L.st, 0, sizeof(State), s) != hipSuccess ||
         hipMemsetAsync(L.sbar, 0, (size_t)kBarSlots * kBarStride * 8, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)

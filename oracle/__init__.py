@@ -52,6 +52,10 @@ def lib():
         L.orc_rope_cos_sin.restype = None
         L.orc_rope.argtypes = [vp, i32, i32, i32, i32, f32, i32]
         L.orc_rope.restype = None
+        L.orc_rope_cos_sin_ff.argtypes = [i32, i32, f32, vp, vp, vp]
+        L.orc_rope_cos_sin_ff.restype = None
+        L.orc_rope_ff.argtypes = [vp, i32, i32, i32, i32, f32, i32, vp]
+        L.orc_rope_ff.restype = None
         L.orc_silu.argtypes = [f32]
         L.orc_silu.restype = f32
         L.orc_argmax.argtypes = [vp, i32]
@@ -128,16 +132,20 @@ def matmul(w: np.ndarray, x: np.ndarray, n: int, rows: int, cols: int) -> np.nda
     return out
 
 
-def rope_cos_sin(pos: int, rope_dims: int, base: float):
+def rope_cos_sin(pos: int, rope_dims: int, base: float, freq=None):
+    """(cos, sin) of each pair's angle at pos; freq: optional per-pair divisors."""
     c = np.empty(rope_dims // 2, np.float32)
     s = np.empty(rope_dims // 2, np.float32)
-    lib().orc_rope_cos_sin(pos, rope_dims, base, _p(c), _p(s))
+    f = None if freq is None else np.ascontiguousarray(freq, np.float32)
+    lib().orc_rope_cos_sin_ff(pos, rope_dims, base, None if f is None else _p(f), _p(c), _p(s))
     return c, s
 
 
-def rope(vec: np.ndarray, n_heads: int, head_dim: int, rope_dims: int, pos: int, base: float, neox: bool) -> np.ndarray:
+def rope(vec: np.ndarray, n_heads: int, head_dim: int, rope_dims: int, pos: int, base: float, neox: bool,
+         freq=None) -> np.ndarray:
     v = np.array(vec, np.float32, copy=True)
-    lib().orc_rope(_p(v), n_heads, head_dim, rope_dims, pos, base, int(neox))
+    f = None if freq is None else np.ascontiguousarray(freq, np.float32)
+    lib().orc_rope_ff(_p(v), n_heads, head_dim, rope_dims, pos, base, int(neox), None if f is None else _p(f))
     return v
 
 

@@ -205,23 +205,33 @@ void orc_matmul(float* out, const float* w, const float* x, int32_t n, int32_t r
 /* The rotation angles of one position, Example 6: theta_scale = base^(-2/n_rot)
  * evaluated in double and rounded to float; theta starts at pos and is
  * multiplied by theta_scale in float once per pair; cos and sin are taken in
- * double and rounded to float. */
-void orc_rope_cos_sin(int32_t pos, int32_t rope_dims, float base, float* cos_out, float* sin_out) {
+ * double and rounded to float. With frequency factors ("What a Llama model
+ * computes, and why", sections 2.4 and 6: theta_i = p base^(-2i/n) / f_i, one
+ * divisor per pair from rope_freqs.weight) pair i's angle is that theta
+ * divided by freq[i] in float; freq NULL means every f_i = 1. */
+void orc_rope_cos_sin_ff(int32_t pos, int32_t rope_dims, float base, const float* freq, float* cos_out,
+                         float* sin_out) {
     float theta_scale = (float)pow((double)base, -2.0 / rope_dims);
     float theta = (float)pos;
     for (int32_t i = 0; i < rope_dims / 2; i++) {
-        cos_out[i] = (float)cos((double)theta);
-        sin_out[i] = (float)sin((double)theta);
+        const float angle = freq ? theta / freq[i] : theta;
+        cos_out[i] = (float)cos((double)angle);
+        sin_out[i] = (float)sin((double)angle);
         theta *= theta_scale;
     }
 }
 
+void orc_rope_cos_sin(int32_t pos, int32_t rope_dims, float base, float* cos_out, float* sin_out) {
+    orc_rope_cos_sin_ff(pos, rope_dims, base, NULL, cos_out, sin_out);
+}
+
 /* RoPE, Example 6: rotate pair i of every head by theta_i. Normal layout pairs
  * (2i, 2i+1); NEOX pairs (i, i + n_rot/2). Dimensions past n_rot are left alone. */
-void orc_rope(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, int32_t pos, float base, int32_t neox) {
+void orc_rope_ff(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, int32_t pos, float base,
+                 int32_t neox, const float* freq) {
     float* c = (float*)malloc(sizeof(float) * (size_t)(rope_dims / 2 + 1));
     float* s = (float*)malloc(sizeof(float) * (size_t)(rope_dims / 2 + 1));
-    orc_rope_cos_sin(pos, rope_dims, base, c, s);
+    orc_rope_cos_sin_ff(pos, rope_dims, base, freq, c, s);
     for (int32_t h = 0; h < n_heads; h++) {
         for (int32_t i = 0; i < rope_dims / 2; i++) {
             int32_t a = h * head_dim + (neox ? i : 2 * i);
@@ -233,6 +243,10 @@ void orc_rope(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, 
     }
     free(c);
     free(s);
+}
+
+void orc_rope(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, int32_t pos, float base, int32_t neox) {
+    orc_rope_ff(vec, n_heads, head_dim, rope_dims, pos, base, neox, NULL);
 }
 
 /* silu(z) = z / (1 + e^-z), Example 8. */
@@ -299,6 +313,7 @@ typedef struct {
 typedef struct orc_model {
     orc_config c;
     float *tok_embd, *out_norm, *output;
+    float* rope_freqs; /* optional per-pair divisors (rope_freqs.weight) or NULL */
     int tied;
     orc_layer* layers;
     uint16_t *kcache, *vcache; /* [layer][n_ctx][kv_dim] binary16 bits */
@@ -351,6 +366,7 @@ int orc_load(const orc_config* cfg, const orc_tensor* ts, int32_t n, orc_model**
     int rc = take(ts, n, "token_embd.weight", c.dim, c.vocab, 0, &m->tok_embd);
     if (!rc) rc = take(ts, n, "output_norm.weight", c.dim, 0, 0, &m->out_norm);
     if (!rc) rc = take(ts, n, "output.weight", c.dim, c.vocab, 1, &m->output);
+    if (!rc) rc = take(ts, n, "rope_freqs.weight", c.rope_dims / 2, 0, 1, &m->rope_freqs);
     if (!rc && !m->output) { /* tied embeddings (Example 9) */
         m->output = m->tok_embd;
         m->tied = 1;
@@ -405,6 +421,7 @@ void orc_free(orc_model* m) {
     if (!m->tied) free(m->output);
     free(m->tok_embd);
     free(m->out_norm);
+    free(m->rope_freqs);
     free(m->kcache);
     free(m->vcache);
     free(m);
@@ -461,8 +478,8 @@ int orc_forward(orc_model* m, int32_t token, int32_t pos, float* logits) {
         add_bias(q, w->bq, qd);
         add_bias(k, w->bk, kvd);
         add_bias(v, w->bv, kvd);
-        orc_rope(q, c.n_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox);
-        orc_rope(k, c.n_kv_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox);
+        orc_rope_ff(q, c.n_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs);
+        orc_rope_ff(k, c.n_kv_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs);
         store_kv(m, l, pos, k, v);
         orc_attention(heads, q, layer_k(m, l), layer_v(m, l), c.n_heads, c.n_kv_heads, c.head_dim, pos, NULL);
         orc_matvec(xb, w->wo, heads, c.dim, qd);
@@ -522,8 +539,8 @@ int orc_prefill(orc_model* m, const int32_t* tokens, int32_t n, float* logits) {
             add_bias(q, w->bq, qd);
             add_bias(k, w->bk, kvd);
             add_bias(v, w->bv, kvd);
-            orc_rope(q, c.n_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox);
-            orc_rope(k, c.n_kv_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox);
+            orc_rope_ff(q, c.n_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox, m->rope_freqs);
+            orc_rope_ff(k, c.n_kv_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox, m->rope_freqs);
             store_kv(m, l, len + t, k, v);
         }
         for (int32_t t = 0; t < n; t++)

@@ -74,6 +74,7 @@ class ModelConfig:
     out_dtype: str = "f32"  # output.weight when untied
     tied: bool = False
     qkv_bias: bool = False
+    rope_freq_factors: bool = False  # a rope_freqs.weight tensor (one divisor per RoPE pair)
     weight_std: float = 0.02
     q8_scale_std: float = 0.002
     gain_std: float = 0.0  # norm gains are 1 + N(0, gain_std); 0 gives exactly 1.0
@@ -140,6 +141,8 @@ def tensor_specs(cfg: ModelConfig):
             (p + "ffn_down.weight", md, (f, d), "matrix"),
         ]
     out.append(("output_norm.weight", F32, (d,), "gain"))
+    if cfg.rope_freq_factors:
+        out.append(("rope_freqs.weight", F32, (cfg.n_rot // 2,), "rope_freqs"))
     if not cfg.tied:
         out.append(("output.weight", DTYPE_IDS[cfg.out_dtype], (d, cfg.vocab), "matrix"))
     return out
@@ -177,7 +180,15 @@ def gen_tensor(seed: int, name: str, dtype: int, ne: tuple, kind: str, cfg: Opti
     n = int(np.prod(ne))
     sid = fnv1a64(name)
     std = cfg.weight_std if cfg is not None else 0.02
-    if kind == "gain":
+    if kind == "rope_freqs":
+        # Llama-3-style divisors: 1 for the fastest quarter of the pairs, 32 for
+        # the slowest quarter, a linear ramp between (synthetic input data)
+        assert dtype == F32
+        i = np.arange(n, dtype=np.float64)
+        lo, hi = n / 4.0, 3.0 * n / 4.0
+        t = np.clip((i - lo) / max(hi - lo, 1.0), 0.0, 1.0)
+        raw = (1.0 + 31.0 * t).astype(np.float32).view(np.uint8)
+    elif kind == "gain":
         assert dtype == F32
         arr = np.empty(n, np.float32)
         gstd = cfg.gain_std if cfg is not None else 0.0

@@ -45,6 +45,7 @@ SMALL_Q8 = SMALL.with_(name="small-q8_0", mat_dtype="q8_0", embd_dtype="f32", ti
 SMALL_NEOX_BIAS = SMALL.with_(name="small-neox-bias", rope_neox=True, qkv_bias=True, rope_base=1e6, seed=14)
 SMALL_PARTIAL_ROPE = SMALL.with_(name="small-partial-rope", rope_dims=16, seed=15)
 SMALL_MHA = SMALL.with_(name="small-mha", n_kv_heads=4, seed=16, head_dim=48, dim=192, n_heads=4)
+SMALL_FREQS = SMALL.with_(name="small-rope-freqs", rope_freq_factors=True, rope_base=500000.0, seed=17)
 
 
 def selftest_config(neox: bool) -> ModelConfig:

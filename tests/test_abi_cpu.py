@@ -92,10 +92,11 @@ def test_plan_1b_q8_sizes():
     assert k == 2 * 16 * 8 * 8320 * 64 * 2
 
 
-@pytest.mark.parametrize("case", ["missing", "shape", "dtype_norm", "size", "bias_partial", "mixed_qkv"])
+@pytest.mark.parametrize("case", ["missing", "shape", "dtype_norm", "size", "bias_partial", "mixed_qkv", "freqs_shape"])
 def test_plan_rejects_bad_tensor_sets(case):
     ts = synth.make_tensor_set(SMALL)
-    want = {"missing": -4, "shape": -2, "dtype_norm": -3, "size": -5, "bias_partial": -4, "mixed_qkv": -3}[case]
+    want = {"missing": -4, "shape": -2, "dtype_norm": -3, "size": -5, "bias_partial": -4, "mixed_qkv": -3,
+            "freqs_shape": -2}[case]
     if case == "missing":
         ts = drop(ts, "blk.1.ffn_down.weight")
     elif case == "shape":
@@ -108,6 +109,8 @@ def test_plan_rejects_bad_tensor_sets(case):
         ts = [synth.Tensor(t.name, t.dtype, t.ne, t.data[:-4]) if t.name == "blk.0.ffn_up.weight" else t for t in ts]
     elif case == "bias_partial":
         ts = ts + [f32_tensor("blk.0.attn_q.bias", np.zeros(SMALL.q_dim, np.float32), (SMALL.q_dim,))]
+    elif case == "freqs_shape":  # one divisor per pair: n_rot / 2 values
+        ts = ts + [f32_tensor("rope_freqs.weight", np.ones(SMALL.n_rot, np.float32), (SMALL.n_rot,))]
     elif case == "mixed_qkv":
         ts = [synth.gen_tensor(9, t.name, synth.F16, t.ne, "matrix", SMALL) if t.name == "blk.0.attn_v.weight" else t
               for t in ts]
@@ -146,6 +149,22 @@ def test_load_validates_before_device_work():
     rc = llm.lib().llm_load_weights(ctypes.byref(c), arr, len(ts), None, None, None, None, ctypes.byref(h))
     assert rc == -4 and not h.value
     assert "output_norm" in llm.llm_last_error()
+
+
+@pytest.mark.parametrize("bad", [0.0, -1.0, float("inf"), float("nan")])
+def test_load_rejects_bad_rope_divisors(bad):
+    cfg = SMALL.with_(rope_freq_factors=True)
+    ts = synth.make_tensor_set(cfg)
+    f = np.ones(cfg.n_rot // 2, np.float32)
+    f[3] = bad
+    ts = [f32_tensor(t.name, f, t.ne) if t.name == "rope_freqs.weight" else t for t in ts]
+    assert plan_rc(cfg, ts) == 0  # llm_plan checks shapes only
+    c = llm.make_config(cfg)
+    arr, keep = llm.make_tensors(ts)
+    h = ctypes.c_void_p(123)
+    rc = llm.lib().llm_load_weights(ctypes.byref(c), arr, len(ts), None, None, None, None, ctypes.byref(h))
+    assert rc == -1 and not h.value
+    assert "rope_freqs" in llm.llm_last_error()
 
 
 def test_null_context_calls():

@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import SMALL, SMALL_F16, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8
+from helpers import SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -138,7 +138,7 @@ def run_decode(cfg, n_prompt, n_steps, prefill_gpu=False, prefill_ref=False):
     return worst
 
 
-SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA]
+SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA, SMALL_FREQS]
 
 
 @pytest.mark.parametrize("cfg", SMALLS, ids=lambda c: c.name)
@@ -167,6 +167,13 @@ def test_prefill_1b_q8_shape():
 def test_prefill_1b_f16_neox_bias_shape():
     # the prefill workload's model (NEOX RoPE, q/k/v bias, F16 weights, tied)
     cfg = synth.C5.with_(n_ctx=160)
+    run_decode(cfg, n_prompt=40, n_steps=2, prefill_gpu=True, prefill_ref=True)
+
+
+def test_prefill_1b_f16_rope_freqs_shape():
+    # Llama 3's frequency factors (rope_freqs.weight) on the 1B F16 shape:
+    # matrix-core prefill, then launch-graph decode, both against the oracle
+    cfg = synth.C3.with_(n_ctx=160, rope_freq_factors=True)
     run_decode(cfg, n_prompt=40, n_steps=2, prefill_gpu=True, prefill_ref=True)
 
 

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import SMALL, SMALL_F16, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8
+from helpers import SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8
 from test_gpu_parity import check_step, run_decode, tol
 
 torch = pytest.importorskip("torch")
@@ -40,7 +40,7 @@ def load(cfg, ts=None, kind=1):
 G8 = SMALL.with_(name="small-g8", dim=256, n_heads=8, n_kv_heads=1, head_dim=32, seed=21)
 KV16 = SMALL.with_(name="small-kv16", dim=512, n_heads=16, n_kv_heads=16, head_dim=32, ffn=320, seed=22)
 SHORT_ROWS_Q8 = SMALL_Q8.with_(name="small-q8-g1", n_heads=2, n_kv_heads=2, head_dim=64, seed=23)
-STEP_SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, G8, KV16, SHORT_ROWS_Q8]
+STEP_SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, G8, KV16, SHORT_ROWS_Q8, SMALL_FREQS]
 
 
 @pytest.mark.parametrize("cfg", STEP_SMALLS, ids=lambda c: c.name)
@@ -70,6 +70,13 @@ def test_step_config2_workload():
 def test_step_1b_q8_shape():
     # the benchmark shape runs the kernel compiled for it (kind 2)
     cfg = synth.C4.with_(n_ctx=160)
+    load(cfg, kind=2).close()
+    run_decode(cfg, n_prompt=20, n_steps=4)
+
+
+def test_step_1b_q8_rope_freqs_shape():
+    # the benchmark kernel (kind 2) with Llama 3's frequency factors in the table
+    cfg = synth.C4.with_(n_ctx=160, rope_freq_factors=True)
     load(cfg, kind=2).close()
     run_decode(cfg, n_prompt=20, n_steps=4)
 

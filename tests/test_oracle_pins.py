@@ -166,6 +166,86 @@ def test_rope_dot_depends_on_position_difference(neox):
         assert abs(d - ref) <= 2e-5 * (np.linalg.norm(q) * np.linalg.norm(k))
 
 
+# ------------------------------------------------------------ RoPE frequency factors
+# "What a Llama model computes, and why", sections 2.4 and 6: theta_i = p *
+# base^(-2i/n) / f_i, one divisor per pair from rope_freqs.weight; factor 1
+# keeps a pair's angle, the slow pairs are slowed by the scaling factor.
+def _ramp(n):
+    i = np.arange(n, dtype=np.float64)
+    return (1.0 + 31.0 * np.clip((i - n / 4) / (n / 2), 0.0, 1.0)).astype(np.float32)
+
+
+def test_rope_factor_one_keeps_the_angle_bit_exact():
+    for pos in (0, 1, 77, 4097):
+        c0, s0 = oracle.rope_cos_sin(pos, 64, 500000.0)
+        c1, s1 = oracle.rope_cos_sin(pos, 64, 500000.0, np.ones(32, np.float32))
+        assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32))
+        assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+
+
+def test_rope_factor_angles_closed_form():
+    # small positions keep every angle below pi, so atan2 recovers it; the
+    # reference is the formula in double, independent of the float recurrence
+    f = _ramp(32)
+    for pos in (1, 2, 3):
+        c, s = oracle.rope_cos_sin(pos, 64, 500000.0, f)
+        got = np.arctan2(s.astype(np.float64), c.astype(np.float64))
+        want = pos * 500000.0 ** (-2.0 * np.arange(32) / 64) / f.astype(np.float64)
+        np.testing.assert_allclose(got, want, rtol=2e-6, atol=1e-9)
+
+
+def test_rope_factor_slows_a_pair_by_its_divisor():
+    # a pair with divisor 32 turns at position 32 p as the undivided pair does at p
+    f = np.full(32, 32.0, np.float32)
+    for p in (1, 5, 40):
+        c32, s32 = oracle.rope_cos_sin(32 * p, 64, 10000.0, f)
+        c1, s1 = oracle.rope_cos_sin(p, 64, 10000.0)
+        np.testing.assert_allclose(c32, c1, atol=2e-5)
+        np.testing.assert_allclose(s32, s1, atol=2e-5)
+
+
+@pytest.mark.parametrize("neox", [False, True])
+def test_rope_factor_dot_depends_on_position_difference(neox):
+    q = synth.normal(19, "q", 64)
+    k = synth.normal(19, "k", 64)
+    f = _ramp(32)
+    ref = None
+    for shift in (0, 1, 17, 300):
+        qa = oracle.rope(q, 1, 64, 64, 40 + shift, 500000.0, neox, f).astype(np.float64)
+        kb = oracle.rope(k, 1, 64, 64, 13 + shift, 500000.0, neox, f).astype(np.float64)
+        d = float(qa @ kb)
+        ref = d if ref is None else ref
+        assert abs(d - ref) <= 2e-5 * (np.linalg.norm(q) * np.linalg.norm(k))
+
+
+def test_model_with_unit_factors_equals_model_without():
+    cfg = SMALL.with_(name="small-unit-freqs")
+    ts = synth.make_tensor_set(cfg)
+    ones = synth.Tensor("rope_freqs.weight", synth.F32, (cfg.n_rot // 2,),
+                        np.ones(cfg.n_rot // 2, np.float32).view(np.uint8))
+    a, b = oracle.Model(cfg, ts), oracle.Model(cfg, ts + [ones])
+    toks = synth.prompt(cfg, 5)
+    for p, t in enumerate(toks):
+        la, lb = a.forward(int(t), p), b.forward(int(t), p)
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    a.close()
+    b.close()
+
+
+def test_model_reads_the_factors():
+    cfg = SMALL.with_(name="small-freqs", rope_freq_factors=True)
+    ts = synth.make_tensor_set(cfg)
+    plain = [t for t in ts if t.name != "rope_freqs.weight"]
+    a, b = oracle.Model(cfg, ts), oracle.Model(cfg, plain)
+    toks = synth.prompt(cfg, 6)
+    diff = 0.0
+    for p, t in enumerate(toks):
+        diff = max(diff, float(np.max(np.abs(a.forward(int(t), p) - b.forward(int(t), p)))))
+    assert diff > 1e-4  # pairs past the first quarter turn slower, so the logits move
+    a.close()
+    b.close()
+
+
 # ------------------------------------------------------------ silu / SwiGLU
 def test_silu_printed_values():
     g = golden("swiglu.json")["silu"]
