@@ -65,6 +65,8 @@ def lib():
         L.orc_load.argtypes = [ctypes.POINTER(OrcConfig), ctypes.POINTER(OrcTensor), i32, ctypes.POINTER(vp)]
         L.orc_forward.argtypes = [vp, i32, i32, vp]
         L.orc_prefill.argtypes = [vp, vp, i32, vp]
+        L.orc_prefill_rows.argtypes = [vp, vp, i32, vp, i32, vp]
+        L.orc_prefill_rows.restype = ctypes.c_int
         L.orc_reset.argtypes = [vp]
         L.orc_reset.restype = None
         L.orc_kv_len.argtypes = [vp]
@@ -237,6 +239,16 @@ class Model:
         rc = lib().orc_prefill(self.h, _p(tk), tk.size, _p(out))
         if rc:
             raise ValueError(f"orc_prefill: {rc}")
+        return out
+
+    def prefill_rows(self, tokens, rows) -> np.ndarray:
+        """Prefill, returning the logits of the batch rows `rows` ([len(rows), vocab])."""
+        tk = np.ascontiguousarray(tokens, np.int32)
+        rw = np.ascontiguousarray(rows, np.int32)
+        out = np.empty((rw.size, self.vocab), np.float32)
+        rc = lib().orc_prefill_rows(self.h, _p(tk), tk.size, _p(rw), rw.size, _p(out))
+        if rc:
+            raise ValueError(f"orc_prefill_rows: {rc}")
         return out
 
     def reset(self):

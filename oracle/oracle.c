@@ -506,9 +506,14 @@ int orc_forward(orc_model* m, int32_t token, int32_t pos, float* logits) {
  * the logits and cache equal token-by-token decoding bit for bit. The logits
  * of the last token are written. Afterwards len += n.
  */
-int orc_prefill(orc_model* m, const int32_t* tokens, int32_t n, float* logits) {
+/* Logits of the batch rows rows[0..n_rows) (indices into tokens) into
+ * out[r * vocab], after the same row-outer pass ("What a Llama model computes,
+ * and why", section 4: every row of a prompt has its own next-token logits). */
+int orc_prefill_rows(orc_model* m, const int32_t* tokens, int32_t n, const int32_t* rows, int32_t n_rows, float* out) {
     const orc_config c = m->c;
-    if (n <= 0) return ORC_ERR_ARG;
+    if (n <= 0 || n_rows <= 0) return ORC_ERR_ARG;
+    for (int32_t r = 0; r < n_rows; r++)
+        if (rows[r] < 0 || rows[r] >= n) return ORC_ERR_ARG;
     if ((int64_t)m->len + n > c.n_ctx) return ORC_ERR_POS;
     for (int32_t i = 0; i < n; i++)
         if (tokens[i] < 0 || tokens[i] >= c.vocab) return ORC_ERR_ARG;
@@ -555,12 +560,20 @@ int orc_prefill(orc_model* m, const int32_t* tokens, int32_t n, float* logits) {
         orc_matmul(XB, w->down, HB, n, c.dim, c.ffn);
         for (int64_t i = 0; i < (int64_t)n * c.dim; i++) X[i] += XB[i];
     }
-    float* xl = X + (int64_t)(n - 1) * c.dim; /* only the last row's logits */
-    orc_rmsnorm(XB, xl, m->out_norm, c.dim, c.eps);
-    orc_matvec(logits, m->output, XB, c.vocab, c.dim);
+    for (int32_t r = 0; r < n_rows; r++) {
+        orc_rmsnorm(XB, X + (int64_t)rows[r] * c.dim, m->out_norm, c.dim, c.eps);
+        orc_matvec(out + (int64_t)r * c.vocab, m->output, XB, c.vocab, c.dim);
+    }
     m->len = len + n;
     free(X); free(XB); free(Q); free(K); free(V); free(HEADS); free(HB); free(HB2);
     return ORC_OK;
+}
+
+/* The last row's logits only (the next token after the prompt). */
+int orc_prefill(orc_model* m, const int32_t* tokens, int32_t n, float* logits) {
+    if (n <= 0) return ORC_ERR_ARG;
+    const int32_t last = n - 1;
+    return orc_prefill_rows(m, tokens, n, &last, 1, logits);
 }
 
 /* A new sequence: the cache length returns to 0 ("The Engine", reset). */

@@ -548,6 +548,29 @@ def test_prefill_equals_token_by_token_bit_exact(cfg):
     assert np.array_equal(a.forward(3, len(toks)), b.forward(3, len(toks)))
 
 
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_Q8], ids=lambda c: c.name)
+def test_prefill_rows_equal_token_by_token_logits_bit_exact(cfg):
+    # every prompt row has its own next-token logits ("What a Llama model
+    # computes, and why", section 4); the batch pass gives each row the logits
+    # a token-by-token pass gives it, bit for bit, in any row order
+    ts = synth.make_tensor_set(cfg)
+    toks = synth.prompt(cfg, 9)
+    a, b = oracle.Model(cfg, ts), oracle.Model(cfg, ts)
+    want = np.stack([a.forward(int(t), p) for p, t in enumerate(toks)])
+    rows = [8, 0, 3, 3, 5]
+    got = b.prefill_rows(toks, rows)
+    for r, g in zip(rows, got):
+        assert np.array_equal(g.view(np.uint32), want[r].view(np.uint32))
+    assert b.kv_len() == len(toks)
+    c = oracle.Model(cfg, ts)
+    assert np.array_equal(c.prefill(toks).view(np.uint32), want[-1].view(np.uint32))
+    with pytest.raises(ValueError):
+        c.prefill_rows(toks, [len(toks)])
+    a.close()
+    b.close()
+    c.close()
+
+
 def test_reset_and_rewind():
     cfg = SMALL
     ts = synth.make_tensor_set(cfg)
