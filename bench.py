@@ -102,8 +102,9 @@ def cpu_baseline(cfg, budget_s=20.0):
 
 def measure_prefill(llm, synth, np, torch, reps=5):
     """llm_prefill of 512 seeded ids on the Qwen2-style F16 1B model from an
-    empty cache, median of `reps`; MFMA fraction = algorithmic GEMM FLOPs /
-    time / F16 dense peak."""
+    empty cache, median of `reps`, and llm_prefill_rows of the same ids with
+    every row's logits; MFMA fraction = algorithmic GEMM FLOPs / time / F16
+    dense peak."""
     c5 = synth.C5
     ts = synth.make_tensor_set(c5)
     pm = llm.Model(c5, ts)
@@ -120,15 +121,33 @@ def measure_prefill(llm, synth, np, torch, reps=5):
         ptimes.append(time.perf_counter() - t0)
         pm.reset()
     pt = float(np.median(ptimes))
-    gemm_flop = 2.0 * 512 * c5.n_layers * (
-        c5.dim * (c5.q_dim + 2 * c5.kv_dim) + c5.q_dim * c5.dim + 2 * c5.dim * c5.ffn + c5.ffn * c5.dim)
+    # the same prompt with the logits of every row (llm_prefill_rows)
+    out = torch.empty((512, c5.vocab), dtype=torch.float32, device="cuda")
+    rtimes = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        llm.llm_prefill_rows(pm.ctx, p5, None, out.data_ptr())
+        torch.cuda.synchronize()
+        rtimes.append(time.perf_counter() - t0)
+        pm.reset()
+    rt = float(np.median(rtimes))
+    # GEMM FLOPs the pass needs: the last layer's output product and FFN run
+    # on the one row whose logits are read (on all 512 for every row's logits)
+    qkv = c5.dim * (c5.q_dim + 2 * c5.kv_dim)
+    rest = c5.q_dim * c5.dim + 3 * c5.dim * c5.ffn
+    gemm_flop = 2.0 * (512 * c5.n_layers * qkv + 512 * (c5.n_layers - 1) * rest + rest)
+    rows_flop = 2.0 * 512 * (c5.n_layers * (qkv + rest) + c5.vocab * c5.dim)
     pm.close()
-    del pm
+    del pm, out
     torch.cuda.empty_cache()
-    print(f"# prefill 512: {pt * 1e3:.2f} ms, {512 / pt:.0f} tok/s", file=sys.stderr, flush=True)
+    print(f"# prefill 512: {pt * 1e3:.2f} ms, {512 / pt:.0f} tok/s; with all 512 logit rows {rt * 1e3:.2f} ms",
+          file=sys.stderr, flush=True)
     return {"config": c5.name, "tokens": 512, "ms": round(pt * 1e3, 3), "tok_s": round(512 / pt, 1),
             "gemm_tflop": round(gemm_flop / 1e12, 4),
-            "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
+            "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+            "all_rows_ms": round(rt * 1e3, 3), "all_rows_gemm_tflop": round(rows_flop / 1e12, 4),
+            "all_rows_mfma_frac": round(rows_flop / rt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
 
 
 def measure_decode_report(llm, synth, np, torch, cfg, ctx_len, steps=64, reps=3):

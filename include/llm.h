@@ -148,6 +148,24 @@ int llm_decode(llm_ctx* ctx, int32_t token, int32_t pos, float* d_logits, int32_
 int llm_prefill(llm_ctx* ctx, const int32_t* h_tokens, int32_t n, float* d_logits, int32_t* h_next);
 
 /*
+ * Prefill with chosen output rows ("What a Llama model computes, and why",
+ * section 4: the last layer only needs the rows whose logits are read). Same
+ * tokens, positions, K/V writes, requirements and kv_len update as llm_prefill,
+ * and the last layer's output product and FFN run only on the chosen rows.
+ * h_rows (host, n_rows entries) lists prompt rows in 0..n-1, in any order,
+ * repeats allowed; 1 <= n_rows <= n_ctx. h_rows NULL with n_rows == n asks for
+ * every row in order. Output j, the logits of prompt row h_rows[j] (vocab
+ * floats, before any softmax), goes to d_logits + j*vocab: d_logits is a
+ * caller-owned device buffer of n_rows*vocab floats. Any bad argument returns
+ * LLM_ERR_ARG (tokens: LLM_ERR_TOKEN; capacity: LLM_ERR_CTX_FULL) before any
+ * device work, with kv_len unchanged. The call only enqueues work on the
+ * context's stream; the context's own logits buffer (llm_logits) is not
+ * written.
+ */
+int llm_prefill_rows(llm_ctx* ctx, const int32_t* h_tokens, int32_t n, const int32_t* h_rows, int32_t n_rows,
+                     float* d_logits);
+
+/*
  * Greedy generation without host round trips ("The Forward Pass in Java",
  * Example 12's loop with the greedy choice of Example 9): decodes `token` at
  * position kv_len, then n_steps-1 more steps, each feeding the previous step's

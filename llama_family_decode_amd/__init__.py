@@ -27,7 +27,7 @@ ERRORS = {
     -6: "LLM_ERR_TOKEN", -7: "LLM_ERR_POS", -8: "LLM_ERR_CTX_FULL", -9: "LLM_ERR_NONFINITE", -10: "LLM_ERR_DEVICE",
     -11: "LLM_ERR_OOM", -12: "LLM_ERR_LIMIT",
 }
-EXPORTS = ["llm_plan", "llm_load_weights", "llm_decode", "llm_prefill", "llm_generate", "llm_reset", "llm_free",
+EXPORTS = ["llm_plan", "llm_load_weights", "llm_decode", "llm_prefill", "llm_prefill_rows", "llm_generate", "llm_reset", "llm_free",
            "llm_last_error", "llm_logits", "llm_kv_len", "llm_kv_read", "llm_op_qkv", "llm_op_attention", "llm_op_o",
            "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind", "llm_op_step_trace",
            "llm_op_step_kind"]
@@ -71,6 +71,8 @@ def lib():
         L.llm_decode.restype = ctypes.c_int
         L.llm_prefill.argtypes = [vp, vp, i32, vp, P(i32)]
         L.llm_prefill.restype = ctypes.c_int
+        L.llm_prefill_rows.argtypes = [vp, vp, i32, vp, i32, vp]
+        L.llm_prefill_rows.restype = ctypes.c_int
         L.llm_generate.argtypes = [vp, i32, i32, vp]
         L.llm_generate.restype = ctypes.c_int
         L.llm_reset.argtypes = [vp]
@@ -177,6 +179,19 @@ def llm_prefill(ctx, tokens, d_logits: Optional[int] = None, want_next: bool = T
     rc = lib().llm_prefill(ctx, tk.ctypes.data, tk.size, d_logits, ctypes.byref(nxt) if want_next else None)
     _check(rc, ctx)
     return int(nxt.value) if want_next else None
+
+
+def llm_prefill_rows(ctx, tokens, rows, d_logits: int):
+    """Prefill `tokens`; the logits of prompt rows `rows` (None: every row) go
+    to the device buffer d_logits, [len(rows)][vocab] fp32. Enqueue only."""
+    tk = np.ascontiguousarray(tokens, np.int32)
+    if rows is None:
+        rc = lib().llm_prefill_rows(ctx, tk.ctypes.data, tk.size, None, tk.size, d_logits)
+    else:
+        rw = np.ascontiguousarray(rows, np.int32)
+        rc = lib().llm_prefill_rows(ctx, tk.ctypes.data, tk.size, rw.ctypes.data if rw.size else None, rw.size,
+                                    d_logits)
+    _check(rc, ctx)
 
 
 def llm_generate(ctx, token: int, n_steps: int) -> np.ndarray:
@@ -306,6 +321,15 @@ class Model:
 
     def prefill(self, tokens, want_next: bool = True, copy_logits: bool = True):
         return llm_prefill(self.ctx, tokens, self.logits_buf.data_ptr() if copy_logits else None, want_next)
+
+    def prefill_rows(self, tokens, rows=None) -> np.ndarray:
+        """Prefill and return the logits of the chosen prompt rows (all rows
+        if None) as a [len(rows), vocab] array."""
+        n_out = len(tokens) if rows is None else len(rows)
+        out = torch.empty((max(n_out, 1), self.vocab), dtype=torch.float32, device=self.device)
+        llm_prefill_rows(self.ctx, tokens, rows, out.data_ptr())
+        torch.cuda.synchronize(self.device)
+        return out[:n_out].cpu().numpy()
 
     def generate(self, token: int, n_steps: int) -> np.ndarray:
         return llm_generate(self.ctx, token, n_steps)

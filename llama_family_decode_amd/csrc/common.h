@@ -185,6 +185,8 @@ hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, i
 // matrix-core input form.
 hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
                                __half* Yl, hipStream_t s);
+// dst[j][0..K) = src[idx[j]][0..K) for j < k (fp32 rows).
+hipError_t launch_gather_rows(const float* src, int K, const int* idx, int k, float* dst, hipStream_t s);
 // H, L = the tiled binary16 hi/lo planes of the n x K fp32 rows X.
 hipError_t launch_split_hl(const float* X, int n, int K, __half* H, __half* L, hipStream_t s);
 // The tiled copy of an F16 matrix (rows padded with zeros to a multiple of 256).
@@ -205,9 +207,11 @@ struct GemmA {
 // Y[n][rows] op= A[n][K] * W^T: F16 weights on the matrix cores with the
 // hi/lo activation planes, Q8_0 on the matrix cores splitting the fp32 rows,
 // F32 on the vector ALUs. SwiGLU also writes its output's hi/lo planes when
-// Yh is set. ws (ws_floats floats) holds split-K partials.
+// Yh is set. ws (ws_floats floats) holds split-K partials. A plain store may
+// scatter its rows: with ymap (device, n entries) row m goes to Y row ymap[m].
 hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
-                       __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s);
+                       __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s,
+                       const int* ymap = nullptr);
 hipError_t launch_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int n_kv_heads, int head_dim, int n_rot,
                                int neox, int n_ctx, const float2* rope, float* Q, __half* kc, __half* vc,
                                hipStream_t s);

@@ -81,6 +81,18 @@ hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim
     return hipGetLastError();
 }
 
+__global__ void k_gather_rows(const float* src, int K, const int* idx, float* dst) {
+    const int j = blockIdx.x;
+    const float* a = src + (size_t)idx[j] * K;
+    for (int i = threadIdx.x; i < K; i += blockDim.x) dst[(size_t)j * K + i] = a[i];
+}
+
+hipError_t launch_gather_rows(const float* src, int K, const int* idx, int k, float* dst, hipStream_t s) {
+    if (k <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gather_rows, dim3(k), dim3(256), 0, s, src, K, idx, dst);
+    return hipGetLastError();
+}
+
 __global__ void k_split_hl(const float* X, int n, int K, __half* H, __half* L) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (size_t)n * K) return;
@@ -120,6 +132,9 @@ hipError_t launch_tile_w(const Mat& W, void* dst, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Output row of product row m: ymap[m] when a row map is given (stores only).
+__device__ __forceinline__ int out_row(const int* ymap, int m) { return ymap ? ymap[m] : m; }
+
 // u = silu(gate) * up at Y[m*ldy + j], and its hi/lo pair (tiled, K = ldy)
 // when Yh is set.
 __device__ __forceinline__ void store_swiglu(float* Y, __half* Yh, __half* Yl, int m, int j, int ldy, float gate,
@@ -151,7 +166,7 @@ constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_LD = GB_K + 8;  // LDS row p
 // it stores its raw partial sums to P[z][m][n] (ld N) instead of applying EPI.
 template <int DT, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M, float* Y, int ldy, const float* bias,
-                                                   __half* Yh, __half* Yl, int kz, float* P) {
+                                                   __half* Yh, __half* Yl, int kz, float* P, const int* ymap) {
     // activations as hi + lo binary16 pairs (hi = f16(x), lo = f16(x - hi)),
     // so the products see x to about 2^-22 relative instead of 2^-11
     __shared__ __attribute__((aligned(16))) _Float16 Ah[GB_M * GB_LD];
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(Mat W, const float* A, int M,
                     if constexpr (EPI == EPI_RESID)
                         Y[(size_t)m * ldy + n] += v;
                     else
-                        Y[(size_t)m * ldy + n] = bias ? v + bias[n] : v;
+                        Y[(size_t)out_row(ymap, m) * ldy + n] = bias ? v + bias[n] : v;
                 }
             }
         }
@@ -307,7 +322,7 @@ constexpr int GF_T = 64, GF_K = 16;
 
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, float* Y, int ldy, const float* bias,
-                                                  __half* Yh, __half* Yl) {
+                                                  __half* Yh, __half* Yl, const int* ymap) {
     __shared__ float As[GF_K][GF_T + 4];
     __shared__ float Bs[GF_K][GF_T + 4];
     const int N = W.rows, K = W.cols;
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, 
             } else if constexpr (EPI == EPI_RESID) {
                 Y[(size_t)m * ldy + n] += acc[i][j];
             } else {
-                Y[(size_t)m * ldy + n] = bias ? acc[i][j] + bias[n] : acc[i][j];
+                Y[(size_t)out_row(ymap, m) * ldy + n] = bias ? acc[i][j] + bias[n] : acc[i][j];
             }
         }
     }
@@ -361,7 +376,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(Mat W, const float* A, int M, 
 // Sum of the S split-K partials P[z][m][n] in z order, then the epilogue.
 template <int EPI>
 __global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, int ldy, const float* bias, __half* Yh,
-                                __half* Yl) {
+                                __half* Yl, const int* ymap) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t MN = (size_t)M * N;
     if constexpr (EPI == EPI_SWIGLU) {
@@ -381,7 +396,7 @@ __global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, i
         if constexpr (EPI == EPI_RESID)
             Y[m * ldy + n] += v;
         else
-            Y[m * ldy + n] = bias ? v + bias[n] : v;
+            Y[(size_t)out_row(ymap, (int)m) * ldy + n] = bias ? v + bias[n] : v;
     }
 }
 
@@ -407,7 +422,7 @@ __device__ __forceinline__ int hl_slot(int r, int c) { return 4 * r + (c ^ tile_
 template <int EPI, int NW>
 __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, const __half* Al, int M, int kz, int nm,
                                                      int nn, float* Y, int ldy, const float* bias, __half* Yh,
-                                                     __half* Yl, float* P) {
+                                                     __half* Yl, float* P, const int* ymap) {
     // NW waves in a 2 x NW/2 arrangement; wave tile 64 x (256 / (NW/2)) as
     // 2 x NJ tiles of the 32x32x16 instruction (on gfx950 it moves twice the
     // operands per cycle of the 16x16x32 one)
@@ -564,7 +579,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
                     if constexpr (EPI == EPI_RESID)
                         Y[(size_t)m * ldy + n] += v;
                     else
-                        Y[(size_t)m * ldy + n] = bias ? v + bias[n] : v;
+                        Y[(size_t)out_row(ymap, m) * ldy + n] = bias ? v + bias[n] : v;
                 }
             }
         }
@@ -585,43 +600,44 @@ static int gemm_splits(int M, int N, int K, int tm, int tn, int smax, size_t ws_
 
 template <int EPI>
 static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias, __half* Yh,
-                           __half* Yl, float* ws, size_t ws_floats, hipStream_t s) {
+                           __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap) {
     const int N = W.rows, K = W.cols;
     int S = 1;
     if (W.dtype == DT_F32) {
         dim3 grid((N + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
-        hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl);
+        hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl, ymap);
     } else if (W.dtype == DT_F16 && W.wt && A.h && K % HL_K == 0) {
         S = gemm_splits(n, N, K, HL_M, HL_N, 8, ws_floats);
         const int nm = (n + HL_M - 1) / HL_M, nn = (N + HL_N - 1) / HL_N;
         hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES), 0, s, W,
                            (const __half*)A.h,
-                           (const __half*)A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr);
+                           (const __half*)A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr, ymap);
     } else {
         S = gemm_splits(n, N, K, GB_M, GB_N, 4, ws_floats);
         dim3 grid((N + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M, S);
         float* P = S > 1 ? ws : nullptr;
         if (W.dtype == DT_F16)
             hipLaunchKernelGGL((k_gemm_mfma<DT_F16, EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl,
-                               K / S, P);
+                               K / S, P, ymap);
         else
             hipLaunchKernelGGL((k_gemm_mfma<DT_Q8, EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl,
-                               K / S, P);
+                               K / S, P, ymap);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     const size_t items = EPI == EPI_SWIGLU ? (size_t)n * N / 2 : (size_t)n * N;
     hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, ws, S, n, N, Y,
-                       ldy, bias, Yh, Yl);
+                       ldy, bias, Yh, Yl, ymap);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
-                       __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s) {
+                       __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap) {
+    if (ymap && epi != EPI_STORE) return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s);
-        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s);
-        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s);
+        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap);
+        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap);
+        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap);
     }
     return hipErrorInvalidValue;
 }

@@ -204,6 +204,9 @@ struct Layout {
     unsigned long long* strace;
     float *X, *Hf, *QKV, *Q, *Of, *Uf, *ws;
     __half *Hh, *Hl, *Oh, *Ol, *Uh, *Ul;  // binary16 hi/lo planes of Hf, Of, Uf
+    float* Xc;                            // the wanted rows' residuals (last prefill layer)
+    int* sel;                             // prompt rows whose logits are wanted (chunk-relative)
+    int* selo;                            // and their output rows
     size_t ws_floats;
     int n_split;
     size_t wbytes, kvbytes, sbytes;
@@ -239,6 +242,7 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.embd = place_mat(W, V.embd->dtype, c->vocab, c->dim);
     L.out_norm = (const float*)W.take((size_t)c->dim * 4);
     L.out = V.out ? place_mat(W, V.out->dtype, c->vocab, c->dim) : L.embd;
+    place_tiled(W, L.out);  // for the batched vocabulary product of chosen prompt rows
     L.rope_freqs = V.rope_freqs ? (const float*)W.take((size_t)(c->rope_dims / 2) * 4) : nullptr;
     L.layers.resize(c->n_layers);
     for (int l = 0; l < c->n_layers; l++) {
@@ -304,6 +308,9 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.Oh = (__half*)S.take((size_t)C * qd * 2);
     L.Ol = (__half*)S.take((size_t)C * qd * 2);
     L.Uh = (__half*)S.take((size_t)C * c->ffn * 2);
+    L.Xc = (float*)S.take((size_t)C * c->dim * 4);
+    L.sel = (int*)S.take((size_t)c->n_ctx * 4);
+    L.selo = (int*)S.take((size_t)c->n_ctx * 4);
     L.Ul = (__half*)S.take((size_t)C * c->ffn * 2);
     // split-K partials (up to 8 splits) of the prefill products with at most
     // max(q|k|v, dim) rows
@@ -355,6 +362,7 @@ struct llm_ctx {
     const void* step_fn = nullptr;
     bool step_special = false;  // a step kernel compiled for this shape
     StepArgs step;
+    std::vector<int32_t> sel_out, sel_row;  // wanted prefill rows (host copies stay alive for the async upload)
 };
 
 namespace {
@@ -665,6 +673,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         for (const Mat* m : {&D.qkv, &D.o, &D.gu, &D.down})
             if (m->wt) ok = ok && launch_tile_w(*m, (void*)m->wt, s) == hipSuccess;
     }
+    if (ok && L.out.wt) ok = launch_tile_w(L.out, (void*)L.out.wt, s) == hipSuccess;
     if (!ok) return bail(LLM_ERR_DEVICE, "weight upload failed");
 
     // ---- RoPE table and zeroed state
@@ -790,25 +799,48 @@ int llm_generate(llm_ctx* c, int32_t token, int32_t n_steps, int32_t* h_tokens) 
     return LLM_OK;
 }
 
-int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits, int32_t* h_next) {
-    int rc = check_ctx(c);
-    if (rc) return rc;
-    if (n <= 0 || !h_tokens) return fail(c, LLM_ERR_ARG, "n must be positive and h_tokens set");
-    for (int i = 0; i < n; i++)
-        if (h_tokens[i] < 0 || h_tokens[i] >= c->cfg.vocab) return fail(c, LLM_ERR_TOKEN, "token out of range");
-    if ((int64_t)c->len + n > c->cfg.n_ctx) return fail(c, LLM_ERR_CTX_FULL, "prefill would pass n_ctx");
+// The batched prompt pass ("What a Llama model computes, and why", section 4)
+// over chunks of kPrefillChunk rows. The last layer's output product and FFN
+// run only on the rows whose logits are wanted (every row still writes its
+// K/V): the chunk's wanted rows are gathered into a compact batch first.
+// rows_out: for each wanted row, in output order, its index in the prompt;
+// with d_rows the logits of output j go to d_rows[j*vocab] (vocabulary
+// product over the compact batch), else exactly one row (the last) is wanted
+// and goes through the decode vocabulary kernel and argmax.
+static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const std::vector<int32_t>& rows_out,
+                        float* d_rows) {
     const llm_config& cf = c->cfg;
     Layout& L = c->L;
     hipStream_t s = c->stream;
     const int qd = c->qd, kvd = c->kvd, qkvd = qd + 2 * kvd;
-    int last = 0;
+    const int nr = (int)rows_out.size();
+    // the wanted rows grouped by chunk, output order kept within a chunk:
+    // c->sel_out[p] = output index, c->sel_row[p] = prompt row
+    c->sel_out.clear();
+    c->sel_row.clear();
+    std::vector<int> chunk_begin;
     for (int done = 0; done < n; done += kPrefillChunk) {
+        chunk_begin.push_back((int)c->sel_out.size());
+        const int end = done + kPrefillChunk < n ? done + kPrefillChunk : n;
+        for (int j = 0; j < nr; j++)
+            if (rows_out[j] >= done && rows_out[j] < end) {
+                c->sel_out.push_back(j);
+                c->sel_row.push_back(rows_out[j] - done);
+            }
+    }
+    chunk_begin.push_back((int)c->sel_out.size());
+    HIPCHK(c, hipMemcpyAsync(L.sel, c->sel_row.data(), (size_t)nr * 4, hipMemcpyHostToDevice, s));
+    if (d_rows) HIPCHK(c, hipMemcpyAsync(L.selo, c->sel_out.data(), (size_t)nr * 4, hipMemcpyHostToDevice, s));
+    int ci = 0;
+    for (int done = 0; done < n; done += kPrefillChunk, ci++) {
         const int m = (n - done) < kPrefillChunk ? (n - done) : kPrefillChunk;
         const int p0 = c->len;
+        const int sb = chunk_begin[ci], k = chunk_begin[ci + 1] - sb;  // wanted rows of this chunk
         HIPCHK(c, hipMemcpyAsync(L.ptok, h_tokens + done, (size_t)m * 4, hipMemcpyHostToDevice, s));
         HIPCHK(c, launch_embed_rows(L.embd, L.ptok, m, L.X, cf.dim, s));
         for (int l = 0; l < cf.n_layers; l++) {
             const LayerW& W = L.layers[l];
+            const bool last = l == cf.n_layers - 1;
             __half* kc = L.kc + (size_t)l * L.kv_layer;
             __half* vc = L.vc + (size_t)l * L.kv_layer;
             HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
@@ -832,27 +864,83 @@ int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits,
             t.n_ctx = cf.n_ctx;
             t.n_split = 1;
             t.scale_div = (float)sqrt((double)cf.head_dim);
-            if (cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0) {
+            const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0;
+            if (mfma_attn)
                 HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, L.Oh, L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
                                                    cf.head_dim, cf.n_ctx, t.scale_div, s));
-            } else {
+            else
                 HIPCHK(c, launch_attn(t, m, s));
-                if (W.o.dtype == DT_F16) HIPCHK(c, launch_split_hl(L.Of, m, qd, L.Oh, L.Ol, s));
+            int mr = m;
+            const float* of = L.Of;
+            float* X = L.X;
+            if (last) {
+                if (k == 0) break;  // no wanted row here: the K/V rows were all the last layer owed
+                // gather the wanted rows' attention outputs and residuals
+                HIPCHK(c, launch_gather_rows(L.Of, qd, L.sel + sb, k, L.Q, s));
+                HIPCHK(c, launch_gather_rows(L.X, cf.dim, L.sel + sb, k, L.Xc, s));
+                mr = k;
+                of = L.Q;
+                X = L.Xc;
             }
-            HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{L.Of, L.Oh, L.Ol}, m, L.X, cf.dim, nullptr, nullptr, nullptr,
+            if (W.o.dtype == DT_F16 && (last || !mfma_attn)) HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
+            HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, L.Ol}, mr, X, cf.dim, nullptr, nullptr, nullptr,
                                   L.ws, L.ws_floats, s));
-            HIPCHK(c, launch_rmsnorm_rows(L.X, W.ffn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, L.Hl}, m, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
+            HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, L.Hl}, mr, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
                                   L.ws, L.ws_floats, s));
-            HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, L.Ul}, m, L.X, cf.dim, nullptr, nullptr,
+            HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, L.Ul}, mr, X, cf.dim, nullptr, nullptr,
                                   nullptr, L.ws, L.ws_floats, s));
         }
         c->len += m;
-        last = m;
+        if (k > 0 && d_rows) {
+            // final RMSNorm of the compact rows, then one vocabulary product
+            // whose rows land at their output indices
+            HIPCHK(c, launch_rmsnorm_rows(L.Xc, L.out_norm, k, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, L.Hl}, k, d_rows, cf.vocab, nullptr, nullptr,
+                                  nullptr, L.ws, L.ws_floats, s, L.selo + sb));
+        } else if (k > 0) {
+            HIPCHK(c, launch_set_state(L.st, 0, c->len - 1, 0, s));
+            HIPCHK(c, enqueue_logits(c, L.Xc, s));
+        }
     }
-    HIPCHK(c, launch_set_state(L.st, 0, c->len - 1, 0, s));
-    HIPCHK(c, enqueue_logits(c, L.X + (size_t)(last - 1) * cf.dim, s));
+    return LLM_OK;
+}
+
+static int check_prompt(llm_ctx* c, const int32_t* h_tokens, int32_t n) {
+    if (n <= 0 || !h_tokens) return fail(c, LLM_ERR_ARG, "n must be positive and h_tokens set");
+    for (int i = 0; i < n; i++)
+        if (h_tokens[i] < 0 || h_tokens[i] >= c->cfg.vocab) return fail(c, LLM_ERR_TOKEN, "token out of range");
+    if ((int64_t)c->len + n > c->cfg.n_ctx) return fail(c, LLM_ERR_CTX_FULL, "prefill would pass n_ctx");
+    return LLM_OK;
+}
+
+int llm_prefill(llm_ctx* c, const int32_t* h_tokens, int32_t n, float* d_logits, int32_t* h_next) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    if ((rc = check_prompt(c, h_tokens, n))) return rc;
+    const std::vector<int32_t> last{n - 1};
+    if ((rc = prefill_pass(c, h_tokens, n, last, nullptr))) return rc;
     return finish(c, d_logits, h_next);
+}
+
+int llm_prefill_rows(llm_ctx* c, const int32_t* h_tokens, int32_t n, const int32_t* h_rows, int32_t n_rows,
+                     float* d_logits) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    if ((rc = check_prompt(c, h_tokens, n))) return rc;
+    if (!d_logits) return fail(c, LLM_ERR_ARG, "d_logits must be set");
+    std::vector<int32_t> rows;
+    if (h_rows) {
+        if (n_rows <= 0 || n_rows > c->cfg.n_ctx) return fail(c, LLM_ERR_ARG, "n_rows must be in 1..n_ctx");
+        rows.assign(h_rows, h_rows + n_rows);
+        for (int32_t r : rows)
+            if (r < 0 || r >= n) return fail(c, LLM_ERR_ARG, "a row index is outside the prompt");
+    } else {
+        if (n_rows != n) return fail(c, LLM_ERR_ARG, "with h_rows NULL, n_rows must equal n");
+        rows.resize(n);
+        for (int32_t i = 0; i < n; i++) rows[i] = i;
+    }
+    return prefill_pass(c, h_tokens, n, rows, d_logits);
 }
 
 int llm_reset(llm_ctx* c) {
