@@ -20,8 +20,9 @@ _lib = None
 
 class OrcConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("dim", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
-                                               "n_ctx", "rope_dims", "rope_neox")] + [("eps", ctypes.c_float),
-                                                                                      ("rope_base", ctypes.c_float)]
+                                               "n_ctx", "rope_dims", "rope_neox")] + [
+        ("eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_window", ctypes.c_int32),
+        ("attn_sinks", ctypes.c_int32), ("attn_temp_scale", ctypes.c_float), ("attn_temp_len", ctypes.c_int32)]
 
 
 class OrcTensor(ctypes.Structure):
@@ -62,6 +63,12 @@ def lib():
         L.orc_argmax.restype = i32
         L.orc_attention.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp]
         L.orc_attention.restype = None
+        L.orc_attention_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+        L.orc_attention_ex.restype = None
+        L.orc_attn_temp.argtypes = [i32, f32, i32]
+        L.orc_attn_temp.restype = f32
+        L.orc_attends.argtypes = [i32, i32, i32, i32]
+        L.orc_attends.restype = ctypes.c_int
         L.orc_load.argtypes = [ctypes.POINTER(OrcConfig), ctypes.POINTER(OrcTensor), i32, ctypes.POINTER(vp)]
         L.orc_forward.argtypes = [vp, i32, i32, vp]
         L.orc_prefill.argtypes = [vp, vp, i32, vp]
@@ -161,16 +168,31 @@ def argmax(v: np.ndarray) -> int:
 
 
 def attention(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray, n_heads: int, n_kv_heads: int, head_dim: int,
-              pos: int, want_weights: bool = False):
-    """kcache/vcache: binary16 bits, [>= pos+1][n_kv_heads * head_dim]."""
+              pos: int, want_weights: bool = False, window: int = 0, sinks: int = 0, temp_scale: float = 0.0,
+              temp_len: int = 0):
+    """kcache/vcache: binary16 bits, [>= pos+1][n_kv_heads * head_dim]. window /
+    sinks: the attended rows (0: all rows up to pos); temp_scale / temp_len:
+    the attention temperature (0: none)."""
     q = np.ascontiguousarray(q, np.float32)
     kc = np.ascontiguousarray(kcache, np.uint16)
     vc = np.ascontiguousarray(vcache, np.uint16)
     out = np.empty(n_heads * head_dim, np.float32)
     wts = np.empty((n_heads, pos + 1), np.float32) if want_weights else None
-    lib().orc_attention(_p(out), _p(q), _p(kc), _p(vc), n_heads, n_kv_heads, head_dim, pos,
-                        _p(wts) if wts is not None else None)
+    if window == 0 and sinks == 0 and temp_scale == 0.0:
+        lib().orc_attention(_p(out), _p(q), _p(kc), _p(vc), n_heads, n_kv_heads, head_dim, pos,
+                            _p(wts) if wts is not None else None)
+    else:
+        lib().orc_attention_ex(_p(out), _p(q), _p(kc), _p(vc), n_heads, n_kv_heads, head_dim, pos, window, sinks,
+                               temp_scale, temp_len, _p(wts) if wts is not None else None)
     return (out, wts) if want_weights else out
+
+
+def attn_temp(pos: int, temp_scale: float, temp_len: int) -> float:
+    return float(lib().orc_attn_temp(pos, temp_scale, temp_len))
+
+
+def attends(t: int, pos: int, window: int, sinks: int) -> bool:
+    return bool(lib().orc_attends(t, pos, window, sinks))
 
 
 def weights_per_layer(dim: int, kv_dim: int, ffn: int) -> int:
@@ -186,6 +208,10 @@ def make_config(cfg) -> OrcConfig:
     c.rope_neox = int(bool(cfg.rope_neox))
     c.eps = float(cfg.eps)
     c.rope_base = float(cfg.rope_base)
+    c.attn_window = int(getattr(cfg, "attn_window", 0))
+    c.attn_sinks = int(getattr(cfg, "attn_sinks", 0))
+    c.attn_temp_scale = float(getattr(cfg, "attn_temp_scale", 0.0))
+    c.attn_temp_len = int(getattr(cfg, "attn_temp_len", 0))
     return c
 
 

@@ -39,9 +39,16 @@
 #define ORC_ERR_POS (-6)
 #define ORC_ERR_OOM (-7)
 
+/* attn_window / attn_sinks: "The Engine", its built-in attentions sliding:N
+ * and sink:s,w (0 = the full causal span); attn_temp_scale / attn_temp_len:
+ * "What a Llama model computes, and why", section 6, Mistral 3's attention
+ * temperature (beta and the original context; beta 0 = none). */
 typedef struct {
     int32_t dim, n_layers, n_heads, n_kv_heads, head_dim, ffn, vocab, n_ctx, rope_dims, rope_neox;
     float eps, rope_base;
+    int32_t attn_window, attn_sinks;
+    float attn_temp_scale;
+    int32_t attn_temp_len;
 } orc_config;
 
 typedef struct {
@@ -269,36 +276,74 @@ int32_t orc_argmax(const float* v, int32_t n) {
  * float over t ascending; then out_h = sum_t (e_t / sum) * V_t.
  * `weights`, when not NULL, receives the normalised weights [n_heads][pos+1].
  */
-void orc_attention(float* out, const float* q, const uint16_t* kcache, const uint16_t* vcache, int32_t n_heads,
-                   int32_t n_kv_heads, int32_t head_dim, int32_t pos, float* weights) {
+/* Mistral 3's attention temperature ("What a Llama model computes, and why",
+ * section 6, the family table and the temperature section): the query at
+ * position pos is scaled by 1 + beta * ln(floor(pos / len) + 1), exactly 1
+ * below len. Evaluated in double, rounded to float. beta 0: no temperature. */
+float orc_attn_temp(int32_t pos, float beta, int32_t len) {
+    if (beta == 0.0f || len <= 0) return 1.0f;
+    return (float)(1.0 + (double)beta * log((double)(pos / len) + 1.0));
+}
+
+/* Whether cache row t is attended by the query at position pos: every row up
+ * to pos for the full causal span (window 0); with window w > 0 only the last
+ * w rows (pos - w < t <= pos, sliding:N of "The Engine"), plus the first
+ * `sinks` rows (sink:s,w, the sinks-plus-window eviction). */
+int orc_attends(int32_t t, int32_t pos, int32_t window, int32_t sinks) {
+    if (t < 0 || t > pos) return 0;
+    if (window <= 0) return 1;
+    return t > pos - window || t < sinks;
+}
+
+/* Scaled dot-product attention of one token over the F16 cache ("The Forward
+ * Pass in Java", Example 7): q scaled by the temperature, scores q.k /
+ * sqrt(head_dim) over the attended rows, softmax, weighted sum of V. Query
+ * head h reads KV head h / (n_heads / n_kv_heads). weights (optional) gets
+ * [n_heads][pos + 1] probabilities, 0 for rows not attended. */
+void orc_attention_ex(float* out, const float* q, const uint16_t* kcache, const uint16_t* vcache, int32_t n_heads,
+                      int32_t n_kv_heads, int32_t head_dim, int32_t pos, int32_t window, int32_t sinks,
+                      float temp_scale, int32_t temp_len, float* weights) {
     int32_t kv_dim = n_kv_heads * head_dim, group = n_heads / n_kv_heads;
     float denom = (float)sqrt((double)head_dim);
+    float tau = orc_attn_temp(pos, temp_scale, temp_len);
     for (int32_t i = 0; i < n_heads * head_dim; i++) out[i] = 0.0f;
 #pragma omp parallel for schedule(static)
     for (int32_t h = 0; h < n_heads; h++) {
         float* att = (float*)malloc(sizeof(float) * (size_t)(pos + 1));
+        float* qs = (float*)malloc(sizeof(float) * (size_t)head_dim);
         int32_t kv_off = (h / group) * head_dim;
+        for (int32_t i = 0; i < head_dim; i++) qs[i] = tau * q[h * head_dim + i];
         float mx = -INFINITY;
         for (int32_t t = 0; t <= pos; t++) {
+            if (!orc_attends(t, pos, window, sinks)) continue;
             float s = 0.0f;
-            for (int32_t i = 0; i < head_dim; i++)
-                s += q[h * head_dim + i] * orc_f16_to_f32(kcache[(int64_t)t * kv_dim + kv_off + i]);
+            for (int32_t i = 0; i < head_dim; i++) s += qs[i] * orc_f16_to_f32(kcache[(int64_t)t * kv_dim + kv_off + i]);
             att[t] = s / denom;
             if (att[t] > mx) mx = att[t];
         }
         float sum = 0.0f;
         for (int32_t t = 0; t <= pos; t++) {
+            if (!orc_attends(t, pos, window, sinks)) continue;
             att[t] = (float)exp((double)(att[t] - mx));
             sum += att[t];
         }
         for (int32_t t = 0; t <= pos; t++) {
-            float a = att[t] / sum;
+            int on = orc_attends(t, pos, window, sinks);
+            float a = on ? att[t] / sum : 0.0f;
             if (weights) weights[(int64_t)h * (pos + 1) + t] = a;
+            if (!on) continue;
             for (int32_t i = 0; i < head_dim; i++)
                 out[h * head_dim + i] += a * orc_f16_to_f32(vcache[(int64_t)t * kv_dim + kv_off + i]);
         }
+        free(qs);
         free(att);
     }
+}
+
+/* The full causal span without temperature. */
+void orc_attention(float* out, const float* q, const uint16_t* kcache, const uint16_t* vcache, int32_t n_heads,
+                   int32_t n_kv_heads, int32_t head_dim, int32_t pos, float* weights) {
+    orc_attention_ex(out, q, kcache, vcache, n_heads, n_kv_heads, head_dim, pos, 0, 0, 0.0f, 0, weights);
 }
 
 /* ------------------------------------------------------------------------
@@ -357,7 +402,8 @@ int orc_load(const orc_config* cfg, const orc_tensor* ts, int32_t n, orc_model**
     const orc_config c = *cfg;
     if (c.dim <= 0 || c.n_layers <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 || c.ffn <= 0 ||
         c.vocab <= 0 || c.n_ctx <= 0 || c.n_heads % c.n_kv_heads || c.rope_dims <= 0 || c.rope_dims > c.head_dim ||
-        c.rope_dims % 2)
+        c.rope_dims % 2 || c.attn_window < 0 || c.attn_sinks < 0 || (c.attn_sinks > 0 && c.attn_window == 0) ||
+        !(c.attn_temp_scale >= 0.0f && c.attn_temp_scale < INFINITY) || (c.attn_temp_scale > 0.0f && c.attn_temp_len <= 0))
         return ORC_ERR_ARG;
     orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
     m->c = c;
@@ -481,7 +527,8 @@ int orc_forward(orc_model* m, int32_t token, int32_t pos, float* logits) {
         orc_rope_ff(q, c.n_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs);
         orc_rope_ff(k, c.n_kv_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs);
         store_kv(m, l, pos, k, v);
-        orc_attention(heads, q, layer_k(m, l), layer_v(m, l), c.n_heads, c.n_kv_heads, c.head_dim, pos, NULL);
+        orc_attention_ex(heads, q, layer_k(m, l), layer_v(m, l), c.n_heads, c.n_kv_heads, c.head_dim, pos,
+                         c.attn_window, c.attn_sinks, c.attn_temp_scale, c.attn_temp_len, NULL);
         orc_matvec(xb, w->wo, heads, c.dim, qd);
         for (int32_t i = 0; i < c.dim; i++) x[i] += xb[i];
         orc_rmsnorm(xb, x, w->ffn_norm, c.dim, c.eps);
@@ -549,8 +596,9 @@ int orc_prefill_rows(orc_model* m, const int32_t* tokens, int32_t n, const int32
             store_kv(m, l, len + t, k, v);
         }
         for (int32_t t = 0; t < n; t++)
-            orc_attention(HEADS + (int64_t)t * qd, Q + (int64_t)t * qd, layer_k(m, l), layer_v(m, l), c.n_heads,
-                          c.n_kv_heads, c.head_dim, len + t, NULL);
+            orc_attention_ex(HEADS + (int64_t)t * qd, Q + (int64_t)t * qd, layer_k(m, l), layer_v(m, l), c.n_heads,
+                             c.n_kv_heads, c.head_dim, len + t, c.attn_window, c.attn_sinks, c.attn_temp_scale,
+                             c.attn_temp_len, NULL);
         orc_matmul(XB, w->wo, HEADS, n, c.dim, qd);
         for (int64_t i = 0; i < (int64_t)n * c.dim; i++) X[i] += XB[i];
         for (int32_t t = 0; t < n; t++) orc_rmsnorm(XB + (int64_t)t * c.dim, X + (int64_t)t * c.dim, w->ffn_norm, c.dim, c.eps);

@@ -75,6 +75,10 @@ class ModelConfig:
     tied: bool = False
     qkv_bias: bool = False
     rope_freq_factors: bool = False  # a rope_freqs.weight tensor (one divisor per RoPE pair)
+    attn_window: int = 0  # attend only the last attn_window positions (0: all)
+    attn_sinks: int = 0  # ... plus the first attn_sinks positions (with a window)
+    attn_temp_scale: float = 0.0  # query scaled by 1 + scale * ln(floor(pos / attn_temp_len) + 1)
+    attn_temp_len: int = 16384
     weight_std: float = 0.02
     q8_scale_std: float = 0.002
     gain_std: float = 0.0  # norm gains are 1 + N(0, gain_std); 0 gives exactly 1.0

@@ -46,6 +46,13 @@ SMALL_NEOX_BIAS = SMALL.with_(name="small-neox-bias", rope_neox=True, qkv_bias=T
 SMALL_PARTIAL_ROPE = SMALL.with_(name="small-partial-rope", rope_dims=16, seed=15)
 SMALL_MHA = SMALL.with_(name="small-mha", n_kv_heads=4, seed=16, head_dim=48, dim=192, n_heads=4)
 SMALL_FREQS = SMALL.with_(name="small-rope-freqs", rope_freq_factors=True, rope_base=500000.0, seed=17)
+# attention spans and temperature ("The Engine": sliding:N, sink:s,w; Mistral 3's
+# temperature with a short original context so that small runs cross it)
+SMALL_WINDOW = SMALL_Q8.with_(name="small-window", attn_window=5, seed=18)
+SMALL_SINKS = SMALL_F16.with_(name="small-sinks", attn_window=4, attn_sinks=2, seed=19)
+SMALL_TEMP = SMALL.with_(name="small-temp", attn_temp_scale=0.1, attn_temp_len=4, seed=20)
+SMALL_SPAN_ALL = SMALL_NEOX_BIAS.with_(name="small-window-sinks-temp", attn_window=6, attn_sinks=3,
+                                      attn_temp_scale=0.5, attn_temp_len=3, seed=21)
 
 
 def selftest_config(neox: bool) -> ModelConfig:

@@ -13,8 +13,8 @@ import pytest
 import oracle
 import synth
 from conftest import golden
-from helpers import (SMALL, SMALL_F16, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8, drop, f32_tensor,
-                     replace_tensors, selftest_config, selftest_tensors)
+from helpers import (SMALL, SMALL_F16, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8, SMALL_SPAN_ALL, drop,
+                     f32_tensor, replace_tensors, selftest_config, selftest_tensors)
 
 
 def f32(x):
@@ -349,6 +349,103 @@ def test_attention_reads_only_positions_up_to_pos():
     assert np.array_equal(a, oracle.attention(q, kb2, vb2, H, KVH, hd, 5))
 
 
+# ------------------------------------------------------------ attention spans and temperature
+# "The Engine" names sliding:N (the last N positions) and sink:s,w (the first s
+# positions plus the last w); "What a Llama model computes, and why", section
+# 6, gives Mistral 3's query scale 1 + 0.1 ln(floor(p / 16384) + 1).
+def _span_inputs(seed, H=4, KVH=2, hd=16, P=16):
+    kvd = KVH * hd
+    q = synth.normal(seed, "q", H * hd) * 2
+    kb = _f16_bits(synth.normal(seed, "k", P * kvd)).reshape(P, kvd)
+    vb = _f16_bits(synth.normal(seed, "v", P * kvd)).reshape(P, kvd)
+    return q, kb, vb, H, KVH, hd, P
+
+
+def test_window_covering_the_span_is_full_attention_bit_exact():
+    q, kb, vb, H, KVH, hd, P = _span_inputs(30)
+    for pos in (0, 5, P - 1):
+        full = oracle.attention(q, kb, vb, H, KVH, hd, pos)
+        for w, s in ((pos + 1, 0), (P + 7, 0), (2, pos + 1), (1, pos)):
+            got = oracle.attention(q, kb, vb, H, KVH, hd, pos, window=w, sinks=s)
+            assert np.array_equal(got.view(np.uint32), full.view(np.uint32)), (pos, w, s)
+
+
+def test_window_of_one_returns_the_current_value_row():
+    q, kb, vb, H, KVH, hd, P = _span_inputs(31)
+    for pos in (0, 7, P - 1):
+        out = oracle.attention(q, kb, vb, H, KVH, hd, pos, window=1, temp_scale=0.3, temp_len=2)
+        vv = _f16_vals(vb[pos])
+        for h in range(H):
+            g = h // (H // KVH)
+            assert np.array_equal(out[h * hd:(h + 1) * hd], vv[g * hd:(g + 1) * hd])
+
+
+@pytest.mark.parametrize("window,sinks", [(3, 0), (3, 2), (4, 1), (2, 5), (6, 3)])
+def test_span_equals_full_attention_over_the_kept_rows(window, sinks):
+    # the masked attention at pos is the plain attention over a cache that
+    # holds only the kept rows, in order: the first `sinks` rows and the last
+    # `window` rows up to pos
+    q, kb, vb, H, KVH, hd, P = _span_inputs(32)
+    for pos in range(P):
+        keep = sorted(set(range(min(sinks, pos + 1))) | set(range(max(0, pos - window + 1), pos + 1)))
+        got, w = oracle.attention(q, kb, vb, H, KVH, hd, pos, want_weights=True, window=window, sinks=sinks)
+        want = oracle.attention(q, kb[keep], vb[keep], H, KVH, hd, len(keep) - 1)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), pos
+        off = [t for t in range(pos + 1) if t not in keep]
+        assert not np.any(w[:, off])
+        np.testing.assert_allclose(w.astype(np.float64).sum(1), 1.0, atol=2e-6)
+        assert [oracle.attends(t, pos, window, sinks) for t in range(P)] == [t in keep for t in range(P)]
+
+
+def test_temperature_closed_form():
+    for p in (0, 1, 16383):
+        assert oracle.attn_temp(p, 0.1, 16384) == 1.0
+    assert oracle.attn_temp(16384, 0.1, 16384) == np.float32(1 + 0.1 * math.log(2))
+    assert oracle.attn_temp(32767, 0.1, 16384) == np.float32(1 + 0.1 * math.log(2))
+    assert oracle.attn_temp(32768, 0.1, 16384) == np.float32(1 + 0.1 * math.log(3))
+    assert oracle.attn_temp(10 ** 6, 0.0, 16384) == 1.0
+
+
+def test_temperature_scales_the_query():
+    q, kb, vb, H, KVH, hd, P = _span_inputs(33)
+    pos = P - 1  # floor(15 / 5) + 1 = 4
+    tau = np.float32(1 + 0.25 * math.log(4))
+    got = oracle.attention(q, kb, vb, H, KVH, hd, pos, temp_scale=0.25, temp_len=5)
+    want = oracle.attention((q * tau).astype(np.float32), kb, vb, H, KVH, hd, pos)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    below = oracle.attention(q, kb, vb, H, KVH, hd, 4, temp_scale=0.25, temp_len=5)
+    assert np.array_equal(below, oracle.attention(q, kb, vb, H, KVH, hd, 4))
+
+
+def test_model_span_and_temperature_switch_on_where_the_pages_say():
+    # a window of W changes nothing before position W and changes the logits
+    # from there on; a temperature changes nothing before its original
+    # context; neither changes anything when it covers the whole cache
+    base = SMALL_Q8.with_(n_ctx=24)
+    ts = synth.make_tensor_set(base)
+    toks = synth.prompt(base, 14)
+    ref = oracle.Model(base, ts)
+    want = [ref.forward(int(t), p) for p, t in enumerate(toks)]
+    for cfg, first_change in ((base.with_(attn_window=6), 6), (base.with_(attn_window=6, attn_sinks=2), 8),
+                              (base.with_(attn_temp_scale=0.1, attn_temp_len=9), 9),
+                              (base.with_(attn_window=24, attn_sinks=3, attn_temp_scale=0.1, attn_temp_len=24), None)):
+        m = oracle.Model(cfg, ts)
+        got = [m.forward(int(t), p) for p, t in enumerate(toks)]
+        for p in range(len(toks)):
+            same = np.array_equal(got[p].view(np.uint32), want[p].view(np.uint32))
+            assert same == (first_change is None or p < first_change), (cfg, p)
+        m.close()
+    ref.close()
+
+
+def test_bad_span_configs_are_rejected():
+    ts = synth.make_tensor_set(SMALL)
+    for kw in (dict(attn_window=-1), dict(attn_sinks=2), dict(attn_sinks=-1, attn_window=3),
+               dict(attn_temp_scale=-0.1), dict(attn_temp_scale=float("inf")), dict(attn_temp_scale=0.1, attn_temp_len=0)):
+        with pytest.raises(Exception):
+            oracle.Model(SMALL.with_(**kw), ts)
+
+
 # ------------------------------------------------------------ binary16
 def test_f16_printed_values():
     g = golden("f16_values.json")
@@ -548,7 +645,7 @@ def test_prefill_equals_token_by_token_bit_exact(cfg):
     assert np.array_equal(a.forward(3, len(toks)), b.forward(3, len(toks)))
 
 
-@pytest.mark.parametrize("cfg", [SMALL, SMALL_Q8], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_Q8, SMALL_SPAN_ALL], ids=lambda c: c.name)
 def test_prefill_rows_equal_token_by_token_logits_bit_exact(cfg):
     # every prompt row has its own next-token logits ("What a Llama model
     # computes, and why", section 4); the batch pass gives each row the logits
