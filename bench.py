@@ -15,8 +15,9 @@ compiled for this shape). The line also reports
     from the committed rocprofv3 counter runs;
   - prefill: llm_prefill of 512 seeded ids on the Qwen2-style F16 variant;
   - decode_reports: the same decode with F16 matrices at context 2048, with
-    Q8_0 at context 8192 (attention a larger share of the bytes), and with
-    Llama 3's RoPE frequency factors (rope_freqs.weight);
+    Q8_0 at context 8192 (attention a larger share of the bytes), with
+    Llama 3's RoPE frequency factors (rope_freqs.weight), and at context 8192
+    with a 1024-row sliding window plus 4 sink rows;
   - cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 8]
@@ -34,10 +35,21 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 
 
+def span_rows(cfg, pos):
+    """Cache rows the query at pos attends: 0..pos, or with a window w the last
+    w rows plus the sink rows below them."""
+    w = getattr(cfg, "attn_window", 0)
+    if w <= 0:
+        return pos + 1
+    lo = max(0, pos - w + 1)
+    return min(getattr(cfg, "attn_sinks", 0), lo) + pos - lo + 1
+
+
 def algorithmic_step_bytes(cfg, pos):
-    """Bytes one decode step at position pos must move: every weight once, K and
-    V rows 0..pos read, one K/V row written, the embedding row (tied: the table
-    is also the output matrix, read once by the vocabulary product)."""
+    """Bytes one decode step at position pos must move: every weight once, the
+    attended K and V rows read (0..pos, or the window and sinks), one K/V row
+    written, the embedding row (tied: the table is also the output matrix,
+    read once by the vocabulary product)."""
     import synth
 
     total = 0
@@ -52,7 +64,7 @@ def algorithmic_step_bytes(cfg, pos):
             continue
         total += synth.nbytes_of(dt, n)
     kv_row = 2 * cfg.n_layers * cfg.kv_dim * 2  # K and V, f16
-    total += kv_row * (pos + 1)  # read rows 0..pos (row pos written then read)
+    total += kv_row * span_rows(cfg, pos)  # attended rows (row pos written then read)
     return total
 
 
@@ -279,7 +291,10 @@ def main():
         reports = [measure_decode_report(llm, synth, np, torch, synth.C3, 2048),
                    measure_decode_report(llm, synth, np, torch, synth.C4_LONG, 8192),
                    measure_decode_report(llm, synth, np, torch,
-                                         synth.C4.with_(name="llama-1b-q8_0-rope-freqs", rope_freq_factors=True), 2048)]
+                                         synth.C4.with_(name="llama-1b-q8_0-rope-freqs", rope_freq_factors=True), 2048),
+                   measure_decode_report(llm, synth, np, torch,
+                                         synth.C4_LONG.with_(name="llama-1b-q8_0-window1024-sinks4", attn_window=1024,
+                                                             attn_sinks=4), 8192)]
 
     cpu = None
     if not args.no_cpu:

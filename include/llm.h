@@ -76,10 +76,23 @@ typedef struct {
  * rope_dims (n_rot) is the number of rotated dimensions of each head, even,
  * <= head_dim; rope_neox selects NEOX pairs (i, i + n_rot/2) instead of the
  * normal pairs (2i, 2i+1) (Example 6). n_ctx is the KV-cache capacity in
- * positions. eps is the RMSNorm epsilon, rope_base the RoPE frequency base. */
+ * positions. eps is the RMSNorm epsilon, rope_base the RoPE frequency base.
+ *
+ * Attention span ("The Engine", its sliding:N and sink:s,w attentions): with
+ * attn_window = 0 the query at position p attends rows 0..p; with
+ * attn_window = w > 0 only rows p-w+1..p, plus rows 0..attn_sinks-1
+ * (attn_sinks > 0 needs a window). The cache still holds every position.
+ * Attention temperature ("What a Llama model computes, and why", section 6,
+ * Mistral 3): the query at position p is scaled by
+ * 1 + attn_temp_scale * ln(floor(p / attn_temp_len) + 1); attn_temp_scale 0
+ * turns it off, Mistral 3 uses 0.1 and 16384. Zero-filled fields give the
+ * plain causal attention. */
 typedef struct {
     int32_t dim, n_layers, n_heads, n_kv_heads, head_dim, ffn, vocab, n_ctx, rope_dims, rope_neox;
     float eps, rope_base;
+    int32_t attn_window, attn_sinks;
+    float attn_temp_scale;
+    int32_t attn_temp_len;
 } llm_config;
 
 /*

@@ -47,8 +47,9 @@ class llm_tensor(ctypes.Structure):
 
 class llm_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("dim", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
-                                               "n_ctx", "rope_dims", "rope_neox")] + [("eps", ctypes.c_float),
-                                                                                      ("rope_base", ctypes.c_float)]
+                                               "n_ctx", "rope_dims", "rope_neox")] + [
+        ("eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_window", ctypes.c_int32),
+        ("attn_sinks", ctypes.c_int32), ("attn_temp_scale", ctypes.c_float), ("attn_temp_len", ctypes.c_int32)]
 
 
 _lib = None
@@ -117,6 +118,10 @@ def make_config(cfg) -> llm_config:
     c.rope_neox = int(bool(cfg.rope_neox))
     c.eps = float(cfg.eps)
     c.rope_base = float(cfg.rope_base)
+    c.attn_window = int(getattr(cfg, "attn_window", 0))
+    c.attn_sinks = int(getattr(cfg, "attn_sinks", 0))
+    c.attn_temp_scale = float(getattr(cfg, "attn_temp_scale", 0.0))
+    c.attn_temp_len = int(getattr(cfg, "attn_temp_len", 0))
     return c
 
 

@@ -36,6 +36,36 @@ __host__ __device__ inline size_t tile_off(int m, int k, int K, int TM) {
 }
 inline size_t tiled_w_bytes(int rows, int cols) { return (size_t)((rows + kTileW - 1) / kTileW) * kTileW * cols * 2; }
 
+// Attention span and temperature of the config: the query at position p
+// attends rows p-window+1..p plus rows 0..sinks-1 (window 0: rows 0..p), with
+// q scaled by 1 + temp_scale * ln(floor(p / temp_len) + 1) (temp_scale 0: 1).
+struct SpanCfg {
+    int window, sinks;
+    float temp_scale;
+    int temp_len;
+};
+// The attended rows of position pos as n indices: index j is row j for
+// j < ns (sinks below the window), row lo + (j - ns) after; the last index is
+// always row pos.
+struct Span {
+    int n, ns, lo;
+};
+__host__ __device__ inline Span attn_span(const SpanCfg& c, int pos) {
+    if (c.window <= 0) return Span{pos + 1, 0, 0};
+    const int lo = pos - c.window + 1 > 0 ? pos - c.window + 1 : 0;
+    const int ns = c.sinks < lo ? c.sinks : lo;
+    return Span{ns + pos - lo + 1, ns, lo};
+}
+__host__ __device__ inline int span_row(const Span& s, int j) { return j < s.ns ? j : s.lo + (j - s.ns); }
+__host__ __device__ inline bool span_has(const SpanCfg& c, int t, int pos) {
+    return t <= pos && (c.window <= 0 || t > pos - c.window || t < c.sinks);
+}
+// The query scale, evaluated in double and rounded to float.
+__host__ __device__ inline float attn_temp(const SpanCfg& c, int pos) {
+    if (c.temp_scale == 0.0f || c.temp_len <= 0) return 1.0f;
+    return (float)(1.0 + (double)c.temp_scale * log((double)(pos / c.temp_len) + 1.0));
+}
+
 // Decode-step state, resident in device memory so that a captured graph can run
 // any step: the kernels read token and pos from here, the argmax writes next.
 struct State {
@@ -97,6 +127,7 @@ struct StepArgs {
     int lds_xr, lds_xs, lds_wsp;  // LDS regions (floats)
     int lds_lw;                   // LDS offset (floats) of the copy of the layer table
     float eps, scale_div;
+    SpanCfg span;
 };
 
 constexpr int kStepGroups = 8;     // block groups of the persistent step kernel (one per XCD)
@@ -160,6 +191,7 @@ struct AttnArgs {
     int n_heads, n_kv_heads, head_dim, n_ctx;
     int n_split;          // gridDim.x
     float scale_div;      // scores are divided by this ((float)sqrt(head_dim))
+    SpanCfg span;
 };
 
 // Launchers (kernels_decode.hip / kernels_prefill.hip).
@@ -196,7 +228,7 @@ hipError_t launch_tile_w(const Mat& W, void* dst, hipStream_t s);
 // fp32 rows [n_q][n_heads*64] and their tiled binary16 hi/lo planes.
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
-                                    int n_ctx, float scale_div, hipStream_t s);
+                                    int n_ctx, float scale_div, const SpanCfg& span, hipStream_t s);
 // Activations of a prefill product: fp32 rows (ld K) and, for F16 weights,
 // their binary16 hi/lo planes (tiled layout).
 struct GemmA {

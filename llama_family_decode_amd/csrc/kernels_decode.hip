@@ -361,6 +361,9 @@ hipError_t launch_set_state(State* st, int token, int pos, int gen_mode, hipStre
 // in chunks with an online softmax (running max m, sum l, unnormalised output
 // o). Scores are divided by sqrt(head_dim). k_attn_combine merges the splits:
 // M = max m_s, L = sum l_s e^(m_s - M), out = sum o_s e^(m_s - M) / L.
+// The attended rows are the span of the query's position (all rows up to it,
+// or a window plus sinks, "The Engine"), taken as a dense index range, and
+// q is scaled by the attention temperature of that position.
 //
 // Thread layout: LPP lanes share one position, each lane holding 8 consecutive
 // dimensions (one 16-byte load of a K or V row); PPI = 256/LPP positions per
@@ -373,7 +376,9 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 
     const int s = blockIdx.x, g = blockIdx.y, z = blockIdx.z;
     const int hd = a.head_dim;
-    const int P = a.st ? a.st->pos + 1 : a.p0 + z + 1;
+    const int qpos = a.st ? a.st->pos : a.p0 + z;
+    const Span span = attn_span(a.span, qpos);
+    const int P = span.n;
     const int S = a.n_split;
     int CH = (P + S - 1) / S;
     CH = (CH + 15) & ~15;
@@ -393,11 +398,12 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 
     const int qd = a.n_heads * hd;
     const float* qz = a.q + (size_t)z * qd;
+    const float tau = attn_temp(a.span, qpos);
     float qv[G][8];
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
-        for (int i = 0; i < 8; i++) qv[h][i] = dim_ok ? qz[(g * G + h) * hd + sub * 8 + i] : 0.f;
+        for (int i = 0; i < 8; i++) qv[h][i] = dim_ok ? tau * qz[(g * G + h) * hd + sub * 8 + i] : 0.f;
     float acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; h++)
@@ -419,8 +425,9 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
         for (int i = 0; i < kAttnSteps; i++) {
             const int t = pg + i * PPI;
             const bool ok = dim_ok && t < cn;
-            kr[i] = ok ? *(const u32x4*)(kbase + (size_t)(c0 + t) * hd) : z4;
-            vr[i] = ok ? *(const u32x4*)(vbase + (size_t)(c0 + t) * hd) : z4;
+            const size_t row = (size_t)span_row(span, c0 + t);
+            kr[i] = ok ? *(const u32x4*)(kbase + row * hd) : z4;
+            vr[i] = ok ? *(const u32x4*)(vbase + row * hd) : z4;
         }
         // scores
 #pragma unroll
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
     __shared__ float Ls[G];
     const int g = blockIdx.x, z = blockIdx.y;
     const int hd = a.head_dim;
-    const int P = a.st ? a.st->pos + 1 : a.p0 + z + 1;
+    const int P = attn_span(a.span, a.st ? a.st->pos : a.p0 + z).n;
     const int S = a.n_split;
     int CH = (P + S - 1) / S;
     CH = (CH + 15) & ~15;

@@ -655,11 +655,15 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // of the online softmax, and adds P V (P as a hi/lo pair, V exact) to its
 // 16 x 64 output, rescaled by e^(m_old - m_new). The result o / l goes out
 // as fp32 rows and as their hi/lo planes (the output product's input).
+// With an attention span (a window plus sinks) each row masks the positions
+// outside its own span, and chunks outside every row's span are skipped; q
+// is scaled by its position's attention temperature before the split.
 constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72, PA_PLD = 68;
 
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc,
                                                            float* out, __half* out_h, __half* out_l, int n_q, int p0,
-                                                           int n_heads, int n_kv_heads, int n_ctx, float scale_div) {
+                                                           int n_heads, int n_kv_heads, int n_ctx, float scale_div,
+                                                           SpanCfg span) {
     constexpr int hd = 64;
     __shared__ __attribute__((aligned(16))) __half Ks[PA_CH * PA_LD];   // [position][dim]
     __shared__ __attribute__((aligned(16))) __half Vt[hd * PA_LD];      // [dim][position]
@@ -674,11 +678,13 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
     const int ra = 16 * wave + lr;
     const int za = min(z0 + ra / G, n_q - 1), ha = g * G + ra % G;
     half8 qh[2], ql[2];
+    const float tau = attn_temp(span, p0 + za);
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
         const float* qp = Q + (size_t)za * qd + ha * hd + 32 * ks + 8 * lq;
         const float4 a0 = *(const float4*)qp, a1 = *(const float4*)(qp + 4);
-        const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float v[8] = {tau * a0.x, tau * a0.y, tau * a0.z, tau * a0.w,
+                            tau * a1.x, tau * a1.y, tau * a1.z, tau * a1.w};
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const _Float16 h = (_Float16)v[j];
@@ -701,6 +707,17 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
 
     const int last = p0 + min(z0 + TB, n_q) - 1;  // the block's last position
     const int nch = last / PA_CH + 1;
+    // chunks in use: with a window, the sink chunks (below the first row's
+    // window) and then the chunks from the first row's window start on;
+    // virtual chunk v is chunk v for v < nA, cB + (v - nA) after
+    int nA = 0, cB = 0;
+    if (span.window > 0) {
+        const int lo = max(0, p0 + z0 - span.window + 1);
+        cB = lo / PA_CH;
+        nA = min((span.sinks + PA_CH - 1) / PA_CH, cB);
+    }
+    const int nv = nA + nch - cB;
+    auto chunk_of = [&](int v) { return v < nA ? v : cB + (v - nA); };
     const __half* kbase = kc + (size_t)g * n_ctx * hd;
     const __half* vbase = vc + (size_t)g * n_ctx * hd;
     // loader: thread t moves position t/8 (+32) dims 8*(t%8) .. +8 of K and V
@@ -716,10 +733,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             vr[u] = ok ? *(const u32x4p*)(vbase + (size_t)t * hd + ld8) : z4;
         }
     };
-    load(0);
+    load(chunk_of(0) * PA_CH);
     float* P = Ps[wave];
-    for (int c = 0; c < nch; c++) {
-        const int c0 = c * PA_CH;
+    for (int v = 0; v < nv; v++) {
+        const int c0 = chunk_of(v) * PA_CH;
         __syncthreads();  // the previous chunk's K, V and P reads are done
 #pragma unroll
         for (int u = 0; u < 2; u++) {
@@ -729,7 +746,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             for (int j = 0; j < 8; j++) Vt[(ld8 + j) * PA_LD + lp + 32 * u] = vh[j];
         }
         __syncthreads();
-        if (c + 1 < nch) load(c0 + PA_CH);
+        if (v + 1 < nv) load(chunk_of(v + 1) * PA_CH);
 
         // scores of this wave's 16 rows over the chunk: tile pt covers
         // positions c0 + 16 pt .. +15
@@ -753,9 +770,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
 #pragma unroll
             for (int pt = 0; pt < 4; pt++) {
                 const int t = c0 + 16 * pt + lr;
-                const float v = t <= rpos[i] ? sc[pt][i] / scale_div : -INFINITY;
-                sc[pt][i] = v;
-                mx = fmaxf(mx, v);
+                const float s = span_has(span, t, rpos[i]) ? sc[pt][i] / scale_div : -INFINITY;
+                sc[pt][i] = s;
+                mx = fmaxf(mx, s);
             }
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
@@ -822,13 +839,13 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
 
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
-                                    int n_ctx, float scale_div, hipStream_t s) {
+                                    int n_ctx, float scale_div, const SpanCfg& span, hipStream_t s) {
     const int G = n_kv_heads > 0 ? n_heads / n_kv_heads : 0;
     if (head_dim != 64 || G < 1 || G > PA_ROWS || PA_ROWS % G || n_heads % n_kv_heads || n_q <= 0)
         return hipErrorInvalidValue;
     const int TB = PA_ROWS / G;
     hipLaunchKernelGGL(k_attn_prefill_mfma, dim3((n_q + TB - 1) / TB, n_kv_heads), dim3(256), 0, s, Q, kc, vc, out,
-                       out_h, out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div);
+                       out_h, out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div, span);
     return hipGetLastError();
 }
 

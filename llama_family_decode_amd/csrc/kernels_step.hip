@@ -718,7 +718,7 @@ __device__ __forceinline__ void wrun(const WRows& w, const int* rmap, int roff, 
 }
 
 // ------------------------------------------------------------------ attention
-// Splits of the P = pos + 1 cached positions of one KV head: S splits of CH
+// Splits of the P attended rows (the span of pos) of one KV head: S splits of CH
 // positions (the last one shorter), S chosen so that the group's items (its KV
 // heads times S) cover its blocks, with at least 16 positions per split.
 __device__ __forceinline__ void attn_splits(int P, int bg, int n_kv_heads, int& S, int& CH) {
@@ -732,10 +732,10 @@ __device__ __forceinline__ void attn_splits(int P, int bg, int n_kv_heads, int& 
     S = (P + CH - 1) / CH;
 }
 
-// Loads of the K and V rows a thread needs for positions c0 + pg + i*PPI of KV
-// head g; rows past the split are clamped to row pos (their values are not
-// used; row pos itself is substituted from the q|k|v buffer).
-__device__ __forceinline__ void attn_kv_load(const StepArgs& a, int layer, int g, int c0, int pos,
+// Loads of the K and V rows a thread needs for span indices c0 + pg + i*PPI
+// of KV head g; indices past the split are clamped to the last (row pos: its
+// values are not used, row pos itself is substituted from the q|k|v buffer).
+__device__ __forceinline__ void attn_kv_load(const StepArgs& a, int layer, int g, int c0, const Span& span,
                                              u32x4 (&kr)[kStepAttn], u32x4 (&vr)[kStepAttn]) {
     const int hd = a.head_dim, LPP = attn_lpp(hd), PPI = kSB / LPP;
     const int tid = thread_id(), sub = tid % LPP, pg = tid / LPP;
@@ -744,7 +744,7 @@ __device__ __forceinline__ void attn_kv_load(const StepArgs& a, int layer, int g
     const __half* vb = a.vc + (size_t)layer * a.kv_layer + (size_t)g * a.n_ctx * hd + sub8;
 #pragma unroll
     for (int i = 0; i < kStepAttn; i++) {
-        const int t = min(c0 + pg + i * PPI, pos);
+        const int t = span_row(span, min(c0 + pg + i * PPI, span.n - 1));
         kr[i] = ld16(kb + (size_t)t * hd);
         vr[i] = ld16(vb + (size_t)t * hd);
     }
@@ -754,13 +754,16 @@ __device__ __forceinline__ void attn_kv_load(const StepArgs& a, int layer, int g
 // and the weighted sum of V over the split's positions ("The Forward Pass in
 // Java", Example 7), kept as (running max m, sum l, unnormalised o) per query
 // head of g and written to part[((g*S + s)*G + h)*(hd + 2)]: m, l, o[hd]. The
-// G query heads of g are taken GC at a time.
+// G query heads of g are taken GC at a time. Splits run over the span's
+// indices (span_row gives the cache row); q is scaled by the attention
+// temperature of pos.
 template <int GC>
-__device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos, const float* qkv, float* part,
-                                           int hlo, int nh, int S, int CH, int rk, int bg,
+__device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos, const Span& span, const float* qkv,
+                                           float* part, int hlo, int nh, int S, int CH, int rk, int bg,
                                            u32x4 (&kr)[kStepAttn], u32x4 (&vr)[kStepAttn], float* sm,
                                            float* m_run, float* l_run, float* alpha) {
-    const int hd = a.head_dim, P = pos + 1, G = a.n_heads / a.n_kv_heads;
+    const int hd = a.head_dim, P = span.n, G = a.n_heads / a.n_kv_heads;
+    const float tau = attn_temp(a.span, pos);
     const int qd = a.n_heads * hd, kvd = a.n_kv_heads * hd;
     const int tid = thread_id(), lane = tid & 63, wave = tid >> 6;
     const int LPP = attn_lpp(hd), PPI = kSB / LPP, CHUNK = PPI * kStepAttn;
@@ -777,7 +780,7 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
         // this step's K and V row (the split that holds pos), rounded to
         // binary16 as the cache stores them, loaded once per item
         u32x4 kpos = {0u, 0u, 0u, 0u}, vpos = {0u, 0u, 0u, 0u};
-        if (pos >= t_begin && pos < t_end) {
+        if (P - 1 >= t_begin && P - 1 < t_end) {
             const float4 k0 = ldf4(qkv + qd + g * hd + sub8), k1 = ldf4(qkv + qd + g * hd + sub8 + 4);
             const float4 v0 = ldf4(qkv + qd + kvd + g * hd + sub8), v1 = ldf4(qkv + qd + kvd + g * hd + sub8 + 4);
             auto pk = [](float lo, float hi) {
@@ -792,7 +795,7 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
             for (int h = 0; h < GC; h++) {
                 const float4 a0 = ldf4(qkv + ((g * G + h0 + h) * hd + sub8));
                 const float4 a1 = ldf4(qkv + ((g * G + h0 + h) * hd + sub8 + 4));
-                const float f = dim_ok ? 1.f : 0.f;
+                const float f = dim_ok ? tau : 0.f;
                 qv[h][0] = a0.x * f;
                 qv[h][1] = a0.y * f;
                 qv[h][2] = a0.z * f;
@@ -811,12 +814,12 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
             }
             for (int c0 = t_begin; c0 < t_end; c0 += CHUNK) {
                 const int cn = min(CHUNK, t_end - c0);
-                if (!have) attn_kv_load(a, layer, g, c0, pos, kr, vr);
+                if (!have) attn_kv_load(a, layer, g, c0, span, kr, vr);
                 have = false;
 #pragma unroll
                 for (int i = 0; i < kStepAttn; i++) {
                     const int t = pg + i * PPI;
-                    if (t < cn && c0 + t == pos) {
+                    if (t < cn && c0 + t == P - 1) {
                         kr[i] = kpos;
                         vr[i] = vpos;
                     }
@@ -1054,8 +1057,9 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         if ((g + 1) * a.n_kv_heads / kNG > g * a.n_kv_heads / kNG) hmask |= 1u << g;
         if ((g + 1) * nbk / kNG > g * nbk / kNG) fmask |= 1u << g;
     }
+    const Span span = attn_span(a.span, pos);
     int S, CH;
-    attn_splits(pos + 1, bg, a.n_kv_heads, S, CH);
+    attn_splits(span.n, bg, a.n_kv_heads, S, CH);
     constexpr int VE = VecW<DT>::VE;
 
     float* xr = sm;                        // this block's copy of the residual stream
@@ -1132,7 +1136,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
 #define KV_PREFETCH(layer)                                                                  \
     do {                                                                                    \
         if (rk < nh * S) {                                                                  \
-            attn_kv_load(a, (layer), hlo + rk / S, (rk % S) * CH, pos, kr, vr);              \
+            attn_kv_load(a, (layer), hlo + rk / S, (rk % S) * CH, span, kr, vr);             \
         } else {                                                                            \
             for (int i_ = 0; i_ < kStepAttn; i_++) kr[i_] = vr[i_] = (u32x4){0u, 0u, 0u, 0u}; \
         }                                                                                   \
@@ -1164,12 +1168,12 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
 
         // ---- attention
         if constexpr (GA > 0) {
-            attn_items<GA>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha);
+            attn_items<GA>(a, l, pos, span, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha);
         } else {
             switch (G) {
-                case 1: attn_items<1>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
-                case 2: attn_items<2>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
-                default: attn_items<4>(a, l, pos, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+                case 1: attn_items<1>(a, l, pos, span, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+                case 2: attn_items<2>(a, l, pos, span, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+                default: attn_items<4>(a, l, pos, span, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
             }
         }
         wait_mem();

@@ -94,6 +94,8 @@ int check_tensor(const llm_tensor* t, const char* name, int64_t ne0, int64_t ne1
     return LLM_OK;
 }
 
+SpanCfg span_cfg(const llm_config& c) { return SpanCfg{c.attn_window, c.attn_sinks, c.attn_temp_scale, c.attn_temp_len}; }
+
 int validate(const llm_config* c, const llm_tensor* ts, int32_t n, Validated& V, std::string& err) {
     if (!c || (!ts && n > 0) || n < 0) {
         err = "null config or tensor list";
@@ -104,6 +106,12 @@ int validate(const llm_config* c, const llm_tensor* ts, int32_t n, Validated& V,
         c->n_heads % c->n_kv_heads || !(c->eps >= 0.0f) || !(c->rope_base > 0.0f) ||
         (c->rope_neox != 0 && c->rope_neox != 1)) {
         err = "invalid config";
+        return LLM_ERR_ARG;
+    }
+    if (c->attn_window < 0 || c->attn_sinks < 0 || (c->attn_sinks > 0 && c->attn_window == 0) ||
+        !(c->attn_temp_scale >= 0.0f && c->attn_temp_scale < INFINITY) ||
+        (c->attn_temp_scale > 0.0f && c->attn_temp_len <= 0)) {
+        err = "invalid attention span or temperature";
         return LLM_ERR_ARG;
     }
     const int G = c->n_heads / c->n_kv_heads;
@@ -450,6 +458,7 @@ hipError_t stage_attn(llm_ctx* c, int l, const float* q, float* out, hipStream_t
     t.n_ctx = cf.n_ctx;
     t.n_split = L.n_split;
     t.scale_div = (float)sqrt((double)cf.head_dim);
+    t.span = span_cfg(cf);
     return launch_attn(t, 1, s);
 }
 
@@ -730,6 +739,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         A.vocab = cfg->vocab;
         A.eps = cfg->eps;
         A.scale_div = (float)sqrt((double)cfg->head_dim);
+        A.span = span_cfg(*cfg);
         if (!upload(L.dlayers, L.layers.data(), L.layers.size() * sizeof(LayerW)))
             return bail(LLM_ERR_DEVICE, "layer table upload failed");
         // The persistent kernel needs one weight type for all layer matrices.
@@ -864,10 +874,11 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             t.n_ctx = cf.n_ctx;
             t.n_split = 1;
             t.scale_div = (float)sqrt((double)cf.head_dim);
+            t.span = span_cfg(cf);
             const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0;
             if (mfma_attn)
                 HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, L.Oh, L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
-                                                   cf.head_dim, cf.n_ctx, t.scale_div, s));
+                                                   cf.head_dim, cf.n_ctx, t.scale_div, t.span, s));
             else
                 HIPCHK(c, launch_attn(t, m, s));
             int mr = m;

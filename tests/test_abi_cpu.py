@@ -124,12 +124,22 @@ def test_plan_rejects_bad_tensor_sets(case):
     ("n_kv_heads", 3, -1),    # 4 % 3 != 0
     ("vocab", 0, -1),
     ("n_ctx", 0, -1),
+    ("attn_window", -1, -1),
+    ("attn_sinks", 2, -1),          # sinks need a window
+    ("attn_temp_scale", -0.1, -1),
+    ("attn_temp_scale", float("nan"), -1),
 ])
 def test_plan_rejects_bad_configs(field, value, want):
     ts = synth.make_tensor_set(SMALL)
     c = llm.make_config(SMALL)
     setattr(c, field, value)
     assert plan_rc(SMALL, ts, c) == want
+
+
+def test_plan_accepts_spans_and_rejects_a_temperature_without_length():
+    ts = synth.make_tensor_set(SMALL)
+    assert plan_rc(SMALL.with_(attn_window=8, attn_sinks=4, attn_temp_scale=0.1), ts) == 0
+    assert plan_rc(SMALL.with_(attn_temp_scale=0.1, attn_temp_len=0), ts) == -1
 
 
 def test_limits_are_reported():

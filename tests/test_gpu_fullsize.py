@@ -15,7 +15,9 @@ at a time, plus properties that hold at any size:
     the launch-graph path (separate kernels) agree within the logit tolerance
     on every teacher-forced step, and a second run repeats bit for bit;
   - the 512-token matrix-core prefill agrees with the same tokens decoded one
-    at a time, within the logit tolerance.
+    at a time, within the logit tolerance;
+  - with a sliding window plus sink rows, the step reads exactly the rows of
+    its span: overwriting any other cache row changes no logit bit.
 """
 import numpy as np
 import pytest
@@ -164,3 +166,71 @@ def test_c5_prefill_512_against_decode_and_oracle(monkeypatch):
     pre.close()
     dec.close()
     print(f"[C5 prefill 512] layer-0 KV {w0:.2e} rms, prefill vs decode {err:.3e}", flush=True)
+
+
+def test_c4_window_and_sinks_read_exactly_their_rows_at_ctx_4096(monkeypatch):
+    # a 1024-row window plus 4 sink rows at position 4096 in the benchmarked
+    # kernel ("The Engine", sink:s,w). Layer 0's cache is rewritten so that
+    # every row has the current position's K (equal scores, so any row that
+    # is read gets weight 1/(rows read)) and its own random V. Then a new V in
+    # a row of the span (the window's first row, a sink row) changes the
+    # logits, and a new V anywhere else (the row just below the window, the
+    # first row above the sinks, every row in between, also in the last
+    # layer) leaves them bit for bit the same. The launch graph agrees within
+    # the logit tolerance.
+    cfg = synth.C4.with_(attn_window=1024, attn_sinks=4)
+    ts = synth.make_tensor_set(cfg)
+    toks = synth.prompt(cfg, 4096)
+    monkeypatch.setenv("LLM_STEP", "persistent")
+    m = llm.Model(cfg, ts)
+    assert llm.llm_op_step_kind(m.ctx) == 2
+    tok = int(m.prefill(toks))
+    pos = len(toks)
+    lo = pos - 1024 + 1  # first window row
+    kvd = cfg.kv_dim
+    rng = np.random.default_rng(7)
+
+    def garbage(n):
+        return rng.normal(0, 1, n * kvd).astype(np.float16).view(np.uint16).reshape(n, kvd)
+
+    def step():
+        m.rewind(pos)
+        m.decode(tok, pos)
+        return m.logits()
+
+    step()  # writes row pos
+    k_pos, _ = m.kv_read(0, pos)
+    llm.llm_op_kv_write(m.ctx, 0, 0, np.tile(k_pos, (pos, 1)), garbage(pos), kvd)
+    base = step()
+    assert np.all(np.isfinite(base))
+
+    def same_after(layer, row, n=1):
+        k = np.tile(k_pos, (n, 1)) if layer == 0 else garbage(n)
+        llm.llm_op_kv_write(m.ctx, layer, row, k, garbage(n), kvd)
+        return np.array_equal(step().view(np.uint32), base.view(np.uint32))
+
+    assert same_after(0, lo - 1), "the row below the window was read"
+    assert same_after(0, 4), "the first row above the sinks was read"
+    assert same_after(0, 5, lo - 6), "rows between the sinks and the window were read"
+    assert same_after(cfg.n_layers - 1, 4, lo - 5), "last layer: rows outside the span were read"
+    assert not same_after(0, lo), "the window's first row was not read"
+    base = step()
+    assert not same_after(0, 2), "a sink row was not read"
+    base = step()
+    assert not same_after(0, pos - 1), "the row before the current one was not read"
+    m.close()
+
+    monkeypatch.setenv("LLM_STEP", "graph")
+    g = llm.Model(cfg, ts)
+    g.prefill(toks)
+    g.decode(tok, pos)
+    lg = g.logits()
+    g.close()
+    monkeypatch.setenv("LLM_STEP", "persistent")
+    p2 = llm.Model(cfg, ts)
+    p2.prefill(toks)
+    p2.decode(tok, pos)
+    err = float(np.max(np.abs(lg.astype(np.float64) - p2.logits())))
+    p2.close()
+    assert err <= tol(cfg), f"persistent vs graph with a window: {err:.3e}"
+    print(f"[C4 window 1024 + 4 sinks at 4096] persistent vs graph {err:.3e}", flush=True)

@@ -18,7 +18,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8
+from helpers import (SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8,
+                     SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -138,7 +139,8 @@ def run_decode(cfg, n_prompt, n_steps, prefill_gpu=False, prefill_ref=False):
     return worst
 
 
-SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA, SMALL_FREQS]
+SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA, SMALL_FREQS, SMALL_WINDOW,
+          SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL]
 
 
 @pytest.mark.parametrize("cfg", SMALLS, ids=lambda c: c.name)
@@ -151,8 +153,10 @@ def test_prefill_small(cfg):
     run_decode(cfg, n_prompt=13, n_steps=4, prefill_gpu=True, prefill_ref=True)
 
 
-def test_prefill_spans_chunks_and_ragged_tail():
-    cfg = SMALL_Q8.with_(n_ctx=1200)
+@pytest.mark.parametrize("cfg", [SMALL_Q8, SMALL_SPAN_ALL.with_(attn_window=300, attn_temp_len=400)],
+                         ids=lambda c: c.name)
+def test_prefill_spans_chunks_and_ragged_tail(cfg):
+    cfg = cfg.with_(n_ctx=1200)
     run_decode(cfg, n_prompt=1100, n_steps=3, prefill_gpu=True, prefill_ref=True)
 
 
@@ -175,6 +179,13 @@ def test_prefill_1b_f16_rope_freqs_shape():
     # matrix-core prefill, then launch-graph decode, both against the oracle
     cfg = synth.C3.with_(n_ctx=160, rope_freq_factors=True)
     run_decode(cfg, n_prompt=40, n_steps=2, prefill_gpu=True, prefill_ref=True)
+
+
+def test_prefill_1b_f16_window_sinks_temperature():
+    # matrix-core prefill attention with per-row spans: the last blocks, whose
+    # first row's window starts past chunk 1, skip it and keep the sink chunk
+    cfg = synth.C5.with_(n_ctx=256, attn_window=40, attn_sinks=5, attn_temp_scale=0.1, attn_temp_len=64)
+    run_decode(cfg, n_prompt=200, n_steps=2, prefill_gpu=True, prefill_ref=True)
 
 
 def test_config1_llama2c_workload():

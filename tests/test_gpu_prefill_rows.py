@@ -14,7 +14,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8
+from helpers import (SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8,
+                     SMALL_SPAN_ALL)
 from test_gpu_parity import check_kv, check_step, first_max, tol, top2_gap
 
 torch = pytest.importorskip("torch")
@@ -74,7 +75,7 @@ def run_rows(cfg, n_prompt, rows, n_steps=2, split=None):
     return worst
 
 
-SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA, SMALL_FREQS]
+SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA, SMALL_FREQS, SMALL_SPAN_ALL]
 
 
 @pytest.mark.parametrize("cfg", SMALLS, ids=lambda c: c.name)
