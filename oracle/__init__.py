@@ -22,7 +22,14 @@ class OrcConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("dim", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
                                                "n_ctx", "rope_dims", "rope_neox")] + [
         ("eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_window", ctypes.c_int32),
-        ("attn_sinks", ctypes.c_int32), ("attn_temp_scale", ctypes.c_float), ("attn_temp_len", ctypes.c_int32)]
+        ("attn_sinks", ctypes.c_int32), ("attn_temp_scale", ctypes.c_float), ("attn_temp_len", ctypes.c_int32),
+        ("yarn_factor", ctypes.c_float), ("yarn_orig_ctx", ctypes.c_int32), ("yarn_beta_fast", ctypes.c_float),
+        ("yarn_beta_slow", ctypes.c_float)]
+
+
+class OrcYarn(ctypes.Structure):
+    _fields_ = [("factor", ctypes.c_float), ("orig_ctx", ctypes.c_int32), ("beta_fast", ctypes.c_float),
+                ("beta_slow", ctypes.c_float)]
 
 
 class OrcTensor(ctypes.Structure):
@@ -57,6 +64,12 @@ def lib():
         L.orc_rope_cos_sin_ff.restype = None
         L.orc_rope_ff.argtypes = [vp, i32, i32, i32, i32, f32, i32, vp]
         L.orc_rope_ff.restype = None
+        L.orc_rope_cos_sin_y.argtypes = [i32, i32, f32, vp, vp, vp, vp]
+        L.orc_rope_cos_sin_y.restype = None
+        L.orc_rope_y.argtypes = [vp, i32, i32, i32, i32, f32, i32, vp, vp]
+        L.orc_rope_y.restype = None
+        L.orc_yarn_ramp.argtypes = [vp, i32, i32, f32]
+        L.orc_yarn_ramp.restype = ctypes.c_double
         L.orc_silu.argtypes = [f32]
         L.orc_silu.restype = f32
         L.orc_argmax.argtypes = [vp, i32]
@@ -141,21 +154,41 @@ def matmul(w: np.ndarray, x: np.ndarray, n: int, rows: int, cols: int) -> np.nda
     return out
 
 
-def rope_cos_sin(pos: int, rope_dims: int, base: float, freq=None):
-    """(cos, sin) of each pair's angle at pos; freq: optional per-pair divisors."""
+def _yarn(yarn):
+    """yarn: None or (factor, orig_ctx, beta_fast, beta_slow)."""
+    return None if yarn is None else OrcYarn(float(yarn[0]), int(yarn[1]), float(yarn[2]), float(yarn[3]))
+
+
+def rope_cos_sin(pos: int, rope_dims: int, base: float, freq=None, yarn=None):
+    """(cos, sin) of each pair's angle at pos; freq: optional per-pair divisors;
+    yarn: optional (factor, orig_ctx, beta_fast, beta_slow)."""
     c = np.empty(rope_dims // 2, np.float32)
     s = np.empty(rope_dims // 2, np.float32)
     f = None if freq is None else np.ascontiguousarray(freq, np.float32)
-    lib().orc_rope_cos_sin_ff(pos, rope_dims, base, None if f is None else _p(f), _p(c), _p(s))
+    y = _yarn(yarn)
+    if y is None:
+        lib().orc_rope_cos_sin_ff(pos, rope_dims, base, None if f is None else _p(f), _p(c), _p(s))
+    else:
+        lib().orc_rope_cos_sin_y(pos, rope_dims, base, None if f is None else _p(f), ctypes.byref(y), _p(c), _p(s))
     return c, s
 
 
 def rope(vec: np.ndarray, n_heads: int, head_dim: int, rope_dims: int, pos: int, base: float, neox: bool,
-         freq=None) -> np.ndarray:
+         freq=None, yarn=None) -> np.ndarray:
     v = np.array(vec, np.float32, copy=True)
     f = None if freq is None else np.ascontiguousarray(freq, np.float32)
-    lib().orc_rope_ff(_p(v), n_heads, head_dim, rope_dims, pos, base, int(neox), None if f is None else _p(f))
+    y = _yarn(yarn)
+    if y is None:
+        lib().orc_rope_ff(_p(v), n_heads, head_dim, rope_dims, pos, base, int(neox), None if f is None else _p(f))
+    else:
+        lib().orc_rope_y(_p(v), n_heads, head_dim, rope_dims, pos, base, int(neox), None if f is None else _p(f),
+                         ctypes.byref(y))
     return v
+
+
+def yarn_ramp(yarn, i: int, rope_dims: int, base: float) -> float:
+    y = _yarn(yarn)
+    return float(lib().orc_yarn_ramp(ctypes.byref(y), i, rope_dims, base))
 
 
 def silu(z: float) -> float:
@@ -212,6 +245,10 @@ def make_config(cfg) -> OrcConfig:
     c.attn_sinks = int(getattr(cfg, "attn_sinks", 0))
     c.attn_temp_scale = float(getattr(cfg, "attn_temp_scale", 0.0))
     c.attn_temp_len = int(getattr(cfg, "attn_temp_len", 0))
+    c.yarn_factor = float(getattr(cfg, "yarn_factor", 0.0))
+    c.yarn_orig_ctx = int(getattr(cfg, "yarn_orig_ctx", 0))
+    c.yarn_beta_fast = float(getattr(cfg, "yarn_beta_fast", 32.0))
+    c.yarn_beta_slow = float(getattr(cfg, "yarn_beta_slow", 1.0))
     return c
 
 

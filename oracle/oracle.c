@@ -49,6 +49,11 @@ typedef struct {
     int32_t attn_window, attn_sinks;
     float attn_temp_scale;
     int32_t attn_temp_len;
+    /* YaRN ("What a Llama model computes, and why", section 6; Peng et al.,
+     * 2023): scale factor (0 = off), original context, ramp ends */
+    float yarn_factor;
+    int32_t yarn_orig_ctx;
+    float yarn_beta_fast, yarn_beta_slow;
 } orc_config;
 
 typedef struct {
@@ -216,16 +221,49 @@ void orc_matmul(float* out, const float* w, const float* x, int32_t n, int32_t r
  * computes, and why", sections 2.4 and 6: theta_i = p base^(-2i/n) / f_i, one
  * divisor per pair from rope_freqs.weight) pair i's angle is that theta
  * divided by freq[i] in float; freq NULL means every f_i = 1. */
-void orc_rope_cos_sin_ff(int32_t pos, int32_t rope_dims, float base, const float* freq, float* cos_out,
-                         float* sin_out) {
+/* YaRN's per-pair angle change and its attention rescaling, as the YaRN paper
+ * (Peng et al., 2023) defines them and "What a Llama model computes, and
+ * why", section 6, describes them: pair i, of base frequency
+ * theta_i = base^(-2i/n) radians per position, completes r = L theta_i / (2 pi)
+ * turns over the original context L. The ramp g(r) is 0 below beta_slow, 1
+ * above beta_fast and linear in between; the angle a becomes
+ * (1 - g) a / s + g a (fast pairs keep theirs, slow pairs are interpolated by
+ * the factor s), evaluated in double and rounded to float. Both q and k are
+ * scaled by m = 1 + 0.1 ln s (so the logits by m^2), folded into cos and sin. */
+typedef struct {
+    float factor;
+    int32_t orig_ctx;
+    float beta_fast, beta_slow;
+} orc_yarn;
+
+double orc_yarn_ramp(const orc_yarn* y, int32_t i, int32_t rope_dims, float base) {
+    const double theta = pow((double)base, -2.0 * i / rope_dims);
+    const double r = (double)y->orig_ctx * theta / 6.283185307179586476925286766559;
+    if (r < y->beta_slow) return 0.0;
+    if (r > y->beta_fast) return 1.0;
+    return (r - y->beta_slow) / ((double)y->beta_fast - y->beta_slow);
+}
+
+void orc_rope_cos_sin_y(int32_t pos, int32_t rope_dims, float base, const float* freq, const orc_yarn* y,
+                        float* cos_out, float* sin_out) {
     float theta_scale = (float)pow((double)base, -2.0 / rope_dims);
     float theta = (float)pos;
+    const double m = y ? 1.0 + 0.1 * log((double)y->factor) : 1.0;
     for (int32_t i = 0; i < rope_dims / 2; i++) {
-        const float angle = freq ? theta / freq[i] : theta;
-        cos_out[i] = (float)cos((double)angle);
-        sin_out[i] = (float)sin((double)angle);
+        float angle = freq ? theta / freq[i] : theta;
+        if (y) {
+            const double g = orc_yarn_ramp(y, i, rope_dims, base);
+            angle = (float)((1.0 - g) * ((double)angle / y->factor) + g * (double)angle);
+        }
+        cos_out[i] = (float)(m * cos((double)angle));
+        sin_out[i] = (float)(m * sin((double)angle));
         theta *= theta_scale;
     }
+}
+
+void orc_rope_cos_sin_ff(int32_t pos, int32_t rope_dims, float base, const float* freq, float* cos_out,
+                         float* sin_out) {
+    orc_rope_cos_sin_y(pos, rope_dims, base, freq, NULL, cos_out, sin_out);
 }
 
 void orc_rope_cos_sin(int32_t pos, int32_t rope_dims, float base, float* cos_out, float* sin_out) {
@@ -234,11 +272,11 @@ void orc_rope_cos_sin(int32_t pos, int32_t rope_dims, float base, float* cos_out
 
 /* RoPE, Example 6: rotate pair i of every head by theta_i. Normal layout pairs
  * (2i, 2i+1); NEOX pairs (i, i + n_rot/2). Dimensions past n_rot are left alone. */
-void orc_rope_ff(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, int32_t pos, float base,
-                 int32_t neox, const float* freq) {
+void orc_rope_y(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, int32_t pos, float base,
+                int32_t neox, const float* freq, const orc_yarn* y) {
     float* c = (float*)malloc(sizeof(float) * (size_t)(rope_dims / 2 + 1));
     float* s = (float*)malloc(sizeof(float) * (size_t)(rope_dims / 2 + 1));
-    orc_rope_cos_sin_ff(pos, rope_dims, base, freq, c, s);
+    orc_rope_cos_sin_y(pos, rope_dims, base, freq, y, c, s);
     for (int32_t h = 0; h < n_heads; h++) {
         for (int32_t i = 0; i < rope_dims / 2; i++) {
             int32_t a = h * head_dim + (neox ? i : 2 * i);
@@ -250,6 +288,11 @@ void orc_rope_ff(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dim
     }
     free(c);
     free(s);
+}
+
+void orc_rope_ff(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, int32_t pos, float base,
+                 int32_t neox, const float* freq) {
+    orc_rope_y(vec, n_heads, head_dim, rope_dims, pos, base, neox, freq, NULL);
 }
 
 void orc_rope(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, int32_t pos, float base, int32_t neox) {
@@ -359,6 +402,8 @@ typedef struct orc_model {
     orc_config c;
     float *tok_embd, *out_norm, *output;
     float* rope_freqs; /* optional per-pair divisors (rope_freqs.weight) or NULL */
+    orc_yarn yarn;
+    const orc_yarn* yarn_on; /* &yarn, or NULL without YaRN */
     int tied;
     orc_layer* layers;
     uint16_t *kcache, *vcache; /* [layer][n_ctx][kv_dim] binary16 bits */
@@ -403,10 +448,20 @@ int orc_load(const orc_config* cfg, const orc_tensor* ts, int32_t n, orc_model**
     if (c.dim <= 0 || c.n_layers <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 || c.ffn <= 0 ||
         c.vocab <= 0 || c.n_ctx <= 0 || c.n_heads % c.n_kv_heads || c.rope_dims <= 0 || c.rope_dims > c.head_dim ||
         c.rope_dims % 2 || c.attn_window < 0 || c.attn_sinks < 0 || (c.attn_sinks > 0 && c.attn_window == 0) ||
-        !(c.attn_temp_scale >= 0.0f && c.attn_temp_scale < INFINITY) || (c.attn_temp_scale > 0.0f && c.attn_temp_len <= 0))
+        !(c.attn_temp_scale >= 0.0f && c.attn_temp_scale < INFINITY) || (c.attn_temp_scale > 0.0f && c.attn_temp_len <= 0) ||
+        !(c.yarn_factor == 0.0f || (c.yarn_factor >= 1.0f && c.yarn_factor < INFINITY && c.yarn_orig_ctx > 0 &&
+                                    c.yarn_beta_slow >= 0.0f && c.yarn_beta_fast > c.yarn_beta_slow &&
+                                    c.yarn_beta_fast < INFINITY)))
         return ORC_ERR_ARG;
     orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
     m->c = c;
+    if (c.yarn_factor > 0.0f) {
+        m->yarn.factor = c.yarn_factor;
+        m->yarn.orig_ctx = c.yarn_orig_ctx;
+        m->yarn.beta_fast = c.yarn_beta_fast;
+        m->yarn.beta_slow = c.yarn_beta_slow;
+        m->yarn_on = &m->yarn;
+    }
     m->layers = (orc_layer*)calloc((size_t)c.n_layers, sizeof(orc_layer));
     int32_t qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
     int rc = take(ts, n, "token_embd.weight", c.dim, c.vocab, 0, &m->tok_embd);
@@ -524,8 +579,8 @@ int orc_forward(orc_model* m, int32_t token, int32_t pos, float* logits) {
         add_bias(q, w->bq, qd);
         add_bias(k, w->bk, kvd);
         add_bias(v, w->bv, kvd);
-        orc_rope_ff(q, c.n_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs);
-        orc_rope_ff(k, c.n_kv_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs);
+        orc_rope_y(q, c.n_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs, m->yarn_on);
+        orc_rope_y(k, c.n_kv_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs, m->yarn_on);
         store_kv(m, l, pos, k, v);
         orc_attention_ex(heads, q, layer_k(m, l), layer_v(m, l), c.n_heads, c.n_kv_heads, c.head_dim, pos,
                          c.attn_window, c.attn_sinks, c.attn_temp_scale, c.attn_temp_len, NULL);
@@ -591,8 +646,8 @@ int orc_prefill_rows(orc_model* m, const int32_t* tokens, int32_t n, const int32
             add_bias(q, w->bq, qd);
             add_bias(k, w->bk, kvd);
             add_bias(v, w->bv, kvd);
-            orc_rope_ff(q, c.n_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox, m->rope_freqs);
-            orc_rope_ff(k, c.n_kv_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox, m->rope_freqs);
+            orc_rope_y(q, c.n_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox, m->rope_freqs, m->yarn_on);
+            orc_rope_y(k, c.n_kv_heads, c.head_dim, c.rope_dims, len + t, c.rope_base, c.rope_neox, m->rope_freqs, m->yarn_on);
             store_kv(m, l, len + t, k, v);
         }
         for (int32_t t = 0; t < n; t++)

@@ -79,6 +79,10 @@ class ModelConfig:
     attn_sinks: int = 0  # ... plus the first attn_sinks positions (with a window)
     attn_temp_scale: float = 0.0  # query scaled by 1 + scale * ln(floor(pos / attn_temp_len) + 1)
     attn_temp_len: int = 16384
+    yarn_factor: float = 0.0  # YaRN context scale factor (0: off)
+    yarn_orig_ctx: int = 0  # the original context YaRN's ramp is measured against
+    yarn_beta_fast: float = 32.0  # pairs with more turns than this over it keep their angle
+    yarn_beta_slow: float = 1.0  # pairs with fewer turns are interpolated by the factor
     weight_std: float = 0.02
     q8_scale_std: float = 0.002
     gain_std: float = 0.0  # norm gains are 1 + N(0, gain_std); 0 gives exactly 1.0

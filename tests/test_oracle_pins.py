@@ -246,6 +246,88 @@ def test_model_reads_the_factors():
     b.close()
 
 
+# ------------------------------------------------------------ YaRN
+# "What a Llama model computes, and why", section 6 names YaRN (Ministral 3:
+# factor 16); the ramp and the rescale follow the YaRN paper (Peng et al.,
+# 2023). The 64-dim, base 1e6, original-context 16384 case below has
+# r_i = 16384 * 1e6^(-i/32) / (2 pi) turns per pair: above 32 up to pair 10,
+# below 1 from pair 19, r_11 = 22.59 in between.
+YARN16 = (16.0, 16384, 32.0, 1.0)
+M16 = 1 + 0.1 * math.log(16)  # 1.2772588722...
+
+
+def _ulps32(a, b):
+    a = np.asarray(a, np.float32).astype(np.float64)
+    b = np.asarray(b, np.float32).astype(np.float64)
+    return np.abs(a - b) / np.spacing(np.maximum(np.abs(a), np.abs(b)).astype(np.float32)).astype(np.float64)
+
+
+def test_yarn_ramp_closed_form():
+    g = [oracle.yarn_ramp(YARN16, i, 64, 1e6) for i in range(32)]
+    assert g[:11] == [1.0] * 11 and g[19:] == [0.0] * 13
+    assert abs(g[11] - (22.59 - 1) / 31) < 1e-3
+    assert all(x > y for x, y in zip(g[11:19], g[12:20]))
+
+
+def test_yarn_factor_one_is_plain_rope_bit_exact():
+    for pos in (0, 1, 777, 16000):
+        c0, s0 = oracle.rope_cos_sin(pos, 64, 1e6)
+        c1, s1 = oracle.rope_cos_sin(pos, 64, 1e6, yarn=(1.0, 16384, 32.0, 1.0))
+        assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32))
+        assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+
+
+def test_yarn_fast_pairs_keep_their_angle_and_slow_pairs_are_interpolated():
+    # fast pairs: m times the plain cos/sin at the same position; slow pairs at
+    # position 16 q: m times the plain cos/sin at position q (the float angle
+    # recurrence scales exactly by the power of two 16)
+    for q in (1, 5, 300, 1000):
+        p = 16 * q
+        cy, sy = oracle.rope_cos_sin(p, 64, 1e6, yarn=YARN16)
+        cp, sp = oracle.rope_cos_sin(p, 64, 1e6)
+        cq, sq = oracle.rope_cos_sin(q, 64, 1e6)
+        assert _ulps32(cy[:11], np.float32(M16 * cp[:11].astype(np.float64))).max() <= 1
+        assert _ulps32(sy[:11], np.float32(M16 * sp[:11].astype(np.float64))).max() <= 1
+        assert _ulps32(cy[19:], np.float32(M16 * cq[19:].astype(np.float64))).max() <= 1
+        assert _ulps32(sy[19:], np.float32(M16 * sq[19:].astype(np.float64))).max() <= 1
+        # every pair keeps norm m
+        np.testing.assert_allclose(np.hypot(cy.astype(np.float64), sy), M16, rtol=1e-6)
+
+
+@pytest.mark.parametrize("neox", [False, True])
+def test_yarn_dot_depends_on_position_difference(neox):
+    q = synth.normal(40, "q", 2 * 64)
+    k = synth.normal(40, "k", 2 * 64)
+    dots = []
+    for p in (0, 37, 900):
+        qr = oracle.rope(q, 2, 64, 64, p + 5, 1e6, neox, yarn=YARN16)
+        kr = oracle.rope(k, 2, 64, 64, p, 1e6, neox, yarn=YARN16)
+        dots.append(float(np.dot(qr.astype(np.float64), kr)))
+    np.testing.assert_allclose(dots, dots[0], rtol=2e-4)
+    plain = float(np.dot(oracle.rope(q, 2, 64, 64, 5, 1e6, neox).astype(np.float64),
+                         oracle.rope(k, 2, 64, 64, 0, 1e6, neox)))
+    assert abs(dots[0]) > 0 and abs(dots[0] - plain) > 1e-3  # the logits are rescaled (m^2) and slow pairs turn slower
+
+
+def test_model_yarn_factor_one_equals_plain_and_model_reads_yarn():
+    ts = synth.make_tensor_set(SMALL)
+    toks = synth.prompt(SMALL, 6)
+    ref = oracle.Model(SMALL, ts)
+    want = [ref.forward(int(t), p) for p, t in enumerate(toks)]
+    one = oracle.Model(SMALL.with_(yarn_factor=1.0, yarn_orig_ctx=8), ts)
+    got = [one.forward(int(t), p) for p, t in enumerate(toks)]
+    assert all(np.array_equal(a.view(np.uint32), b.view(np.uint32)) for a, b in zip(got, want))
+    y = oracle.Model(SMALL.with_(yarn_factor=4.0, yarn_orig_ctx=8), ts)
+    diff = max(float(np.max(np.abs(y.forward(int(t), p) - w))) for (p, t), w in zip(enumerate(toks), want))
+    assert diff > 1e-4
+    for m in (ref, one, y):
+        m.close()
+    for kw in (dict(yarn_factor=0.5, yarn_orig_ctx=8), dict(yarn_factor=4.0), dict(yarn_factor=4.0, yarn_orig_ctx=8,
+                                                                                 yarn_beta_fast=1.0)):
+        with pytest.raises(Exception):
+            oracle.Model(SMALL.with_(**kw), ts)
+
+
 # ------------------------------------------------------------ silu / SwiGLU
 def test_silu_printed_values():
     g = golden("swiglu.json")["silu"]
