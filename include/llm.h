@@ -86,13 +86,24 @@ typedef struct {
  * Mistral 3): the query at position p is scaled by
  * 1 + attn_temp_scale * ln(floor(p / attn_temp_len) + 1); attn_temp_scale 0
  * turns it off, Mistral 3 uses 0.1 and 16384. Zero-filled fields give the
- * plain causal attention. */
+ * plain causal attention.
+ *
+ * YaRN ("What a Llama model computes, and why", section 6; the YaRN paper,
+ * Peng et al., 2023): with yarn_factor s >= 1 (0 = off), pair i of base
+ * frequency theta_i = rope_base^(-2i/rope_dims) completes
+ * r = yarn_orig_ctx * theta_i / (2 pi) turns over the original context; a
+ * ramp g(r), 0 below yarn_beta_slow and 1 above yarn_beta_fast (linear in
+ * between; Ministral 3 uses 1 and 32), turns the angle a into
+ * (1 - g) a / s + g a, and q and k are scaled by 1 + 0.1 ln s. */
 typedef struct {
     int32_t dim, n_layers, n_heads, n_kv_heads, head_dim, ffn, vocab, n_ctx, rope_dims, rope_neox;
     float eps, rope_base;
     int32_t attn_window, attn_sinks;
     float attn_temp_scale;
     int32_t attn_temp_len;
+    float yarn_factor;
+    int32_t yarn_orig_ctx;
+    float yarn_beta_fast, yarn_beta_slow;
 } llm_config;
 
 /*

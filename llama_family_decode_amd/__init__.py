@@ -49,7 +49,9 @@ class llm_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("dim", "n_layers", "n_heads", "n_kv_heads", "head_dim", "ffn", "vocab",
                                                "n_ctx", "rope_dims", "rope_neox")] + [
         ("eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_window", ctypes.c_int32),
-        ("attn_sinks", ctypes.c_int32), ("attn_temp_scale", ctypes.c_float), ("attn_temp_len", ctypes.c_int32)]
+        ("attn_sinks", ctypes.c_int32), ("attn_temp_scale", ctypes.c_float), ("attn_temp_len", ctypes.c_int32),
+        ("yarn_factor", ctypes.c_float), ("yarn_orig_ctx", ctypes.c_int32), ("yarn_beta_fast", ctypes.c_float),
+        ("yarn_beta_slow", ctypes.c_float)]
 
 
 _lib = None
@@ -122,6 +124,10 @@ def make_config(cfg) -> llm_config:
     c.attn_sinks = int(getattr(cfg, "attn_sinks", 0))
     c.attn_temp_scale = float(getattr(cfg, "attn_temp_scale", 0.0))
     c.attn_temp_len = int(getattr(cfg, "attn_temp_len", 0))
+    c.yarn_factor = float(getattr(cfg, "yarn_factor", 0.0))
+    c.yarn_orig_ctx = int(getattr(cfg, "yarn_orig_ctx", 0))
+    c.yarn_beta_fast = float(getattr(cfg, "yarn_beta_fast", 32.0))
+    c.yarn_beta_slow = float(getattr(cfg, "yarn_beta_slow", 1.0))
     return c
 
 

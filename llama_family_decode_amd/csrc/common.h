@@ -194,10 +194,18 @@ struct AttnArgs {
     SpanCfg span;
 };
 
+// YaRN parameters (factor 0: off).
+struct YarnCfg {
+    float factor;
+    int orig_ctx;
+    float beta_fast, beta_slow;
+};
+
 // Launchers (kernels_decode.hip / kernels_prefill.hip).
 // (cos, sin) of every (position, pair) angle; freq (n_rot/2 divisors, or
-// nullptr) divides each pair's angle.
-hipError_t launch_rope_table(float2* tab, int n_pos, int n_rot, float theta_scale, const float* freq, hipStream_t s);
+// nullptr) divides each pair's angle; YaRN (if on) remaps it and scales both.
+hipError_t launch_rope_table(float2* tab, int n_pos, int n_rot, float base, const float* freq, const YarnCfg& yarn,
+                             hipStream_t s);
 hipError_t launch_gemv(int pro, int epi, const GemvArgs& a, int grid, hipStream_t s);
 int gemv_grid(int pro, int epi, int rows);
 hipError_t launch_attn(const AttnArgs& a, int n_q, hipStream_t s);

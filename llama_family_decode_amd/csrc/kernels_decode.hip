@@ -292,24 +292,42 @@ hipError_t launch_gemv(int pro, int epi, const GemvArgs& a, int grid, hipStream_
 
 // ------------------------------------------------------------------ RoPE table
 // Row p holds (cos, sin) of theta_i for i < n_rot/2 ("The Forward Pass in Java",
-// Example 6): theta starts at (float)p and is multiplied by theta_scale in float
-// once per pair; cos and sin are evaluated in double and rounded to float.
-__global__ void k_rope_table(float2* tab, int n_pos, int half, float theta_scale, const float* freq) {
+// Example 6): theta starts at (float)p and is multiplied by theta_scale =
+// base^(-2/n_rot) (double, rounded to float) in float once per pair; cos and
+// sin are evaluated in double and rounded to float.
+// Llama 3 frequency factors divide pair i's angle ("What a Llama model
+// computes, and why", sections 2.4 and 6). YaRN (the YaRN paper, Peng et al.,
+// 2023, named in section 6) mixes the angle a into (1 - g) a / s + g a, g the
+// ramp of the pair's turns r = L base^(-2i/n_rot) / (2 pi) over the original
+// context L (0 below beta_slow, 1 above beta_fast), in double, and scales cos
+// and sin by 1 + 0.1 ln s.
+__global__ void k_rope_table(float2* tab, int n_pos, int half, float theta_scale, float base, const float* freq,
+                             YarnCfg y) {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= n_pos) return;
+    const int n_rot = 2 * half;
+    const bool yarn = y.factor > 0.0f;
+    const double m = yarn ? 1.0 + 0.1 * log((double)y.factor) : 1.0;
     float theta = (float)p;
     for (int i = 0; i < half; i++) {
-        // Llama 3 frequency factors divide pair i's angle ("What a Llama model
-        // computes, and why", sections 2.4 and 6)
-        const float angle = freq ? theta / freq[i] : theta;
-        tab[(size_t)p * half + i] = make_float2((float)cos((double)angle), (float)sin((double)angle));
+        float angle = freq ? theta / freq[i] : theta;
+        if (yarn) {
+            const double r = (double)y.orig_ctx * pow((double)base, -2.0 * i / n_rot) / 6.283185307179586476925286766559;
+            const double g = r < y.beta_slow ? 0.0 : r > y.beta_fast ? 1.0
+                                                 : (r - y.beta_slow) / ((double)y.beta_fast - y.beta_slow);
+            angle = (float)((1.0 - g) * ((double)angle / y.factor) + g * (double)angle);
+        }
+        tab[(size_t)p * half + i] = make_float2((float)(m * cos((double)angle)), (float)(m * sin((double)angle)));
         theta = theta * theta_scale;
     }
 }
 
-hipError_t launch_rope_table(float2* tab, int n_pos, int n_rot, float theta_scale, const float* freq, hipStream_t s) {
+hipError_t launch_rope_table(float2* tab, int n_pos, int n_rot, float base, const float* freq, const YarnCfg& yarn,
+                             hipStream_t s) {
     const int half = n_rot / 2;
-    hipLaunchKernelGGL(k_rope_table, dim3((n_pos + 255) / 256), dim3(256), 0, s, tab, n_pos, half, theta_scale, freq);
+    const float theta_scale = (float)pow((double)base, -2.0 / n_rot);  // on the host, as the angle recurrence's start
+    hipLaunchKernelGGL(k_rope_table, dim3((n_pos + 255) / 256), dim3(256), 0, s, tab, n_pos, half, theta_scale, base,
+                       freq, yarn);
     return hipGetLastError();
 }
 

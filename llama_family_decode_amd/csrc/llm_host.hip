@@ -114,6 +114,12 @@ int validate(const llm_config* c, const llm_tensor* ts, int32_t n, Validated& V,
         err = "invalid attention span or temperature";
         return LLM_ERR_ARG;
     }
+    if (!(c->yarn_factor == 0.0f ||
+          (c->yarn_factor >= 1.0f && c->yarn_factor < INFINITY && c->yarn_orig_ctx > 0 && c->yarn_beta_slow >= 0.0f &&
+           c->yarn_beta_fast > c->yarn_beta_slow && c->yarn_beta_fast < INFINITY))) {
+        err = "invalid YaRN parameters";
+        return LLM_ERR_ARG;
+    }
     const int G = c->n_heads / c->n_kv_heads;
     const int64_t qd = (int64_t)c->n_heads * c->head_dim, kvd = (int64_t)c->n_kv_heads * c->head_dim;
     if (c->head_dim % 8 || c->head_dim > kMaxHeadDim || !(G == 1 || G == 2 || G == 4 || G == 8) || c->dim % 32 ||
@@ -686,8 +692,8 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
     if (!ok) return bail(LLM_ERR_DEVICE, "weight upload failed");
 
     // ---- RoPE table and zeroed state
-    const float theta_scale = (float)pow((double)cfg->rope_base, -2.0 / cfg->rope_dims);
-    if (launch_rope_table(L.rope, cfg->n_ctx, cfg->rope_dims, theta_scale, L.rope_freqs, s) != hipSuccess ||
+    const YarnCfg yarn{cfg->yarn_factor, cfg->yarn_orig_ctx, cfg->yarn_beta_fast, cfg->yarn_beta_slow};
+    if (launch_rope_table(L.rope, cfg->n_ctx, cfg->rope_dims, cfg->rope_base, L.rope_freqs, yarn, s) != hipSuccess ||
         hipMemsetAsync(L.st, 0, sizeof(State), s) != hipSuccess ||
         hipMemsetAsync(L.sbar, 0, (size_t)kBarSlots * kBarStride * 8, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)

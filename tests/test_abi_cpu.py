@@ -128,6 +128,8 @@ def test_plan_rejects_bad_tensor_sets(case):
     ("attn_sinks", 2, -1),          # sinks need a window
     ("attn_temp_scale", -0.1, -1),
     ("attn_temp_scale", float("nan"), -1),
+    ("yarn_factor", 0.5, -1),        # YaRN factors start at 1
+    ("yarn_factor", 4.0, -1),        # ... and need the original context
 ])
 def test_plan_rejects_bad_configs(field, value, want):
     ts = synth.make_tensor_set(SMALL)

@@ -19,7 +19,7 @@ import pytest
 import oracle
 import synth
 from helpers import (SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8,
-                     SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW)
+                     SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW, SMALL_YARN)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -140,7 +140,7 @@ def run_decode(cfg, n_prompt, n_steps, prefill_gpu=False, prefill_ref=False):
 
 
 SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA, SMALL_FREQS, SMALL_WINDOW,
-          SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL]
+          SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL, SMALL_YARN]
 
 
 @pytest.mark.parametrize("cfg", SMALLS, ids=lambda c: c.name)
@@ -178,6 +178,13 @@ def test_prefill_1b_f16_rope_freqs_shape():
     # Llama 3's frequency factors (rope_freqs.weight) on the 1B F16 shape:
     # matrix-core prefill, then launch-graph decode, both against the oracle
     cfg = synth.C3.with_(n_ctx=160, rope_freq_factors=True)
+    run_decode(cfg, n_prompt=40, n_steps=2, prefill_gpu=True, prefill_ref=True)
+
+
+def test_prefill_1b_f16_yarn_shape():
+    # Ministral 3's YaRN factor 16 on the 1B F16 shape (original context 16384,
+    # ramp 1..32): matrix-core prefill, then launch-graph decode
+    cfg = synth.C3.with_(n_ctx=160, yarn_factor=16.0, yarn_orig_ctx=16384, rope_base=1e6)
     run_decode(cfg, n_prompt=40, n_steps=2, prefill_gpu=True, prefill_ref=True)
 
 

@@ -16,7 +16,7 @@ import pytest
 import oracle
 import synth
 from helpers import (SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8,
-                     SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW)
+                     SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW, SMALL_YARN)
 from test_gpu_parity import check_step, run_decode, tol
 
 torch = pytest.importorskip("torch")
@@ -42,7 +42,7 @@ G8 = SMALL.with_(name="small-g8", dim=256, n_heads=8, n_kv_heads=1, head_dim=32,
 KV16 = SMALL.with_(name="small-kv16", dim=512, n_heads=16, n_kv_heads=16, head_dim=32, ffn=320, seed=22)
 SHORT_ROWS_Q8 = SMALL_Q8.with_(name="small-q8-g1", n_heads=2, n_kv_heads=2, head_dim=64, seed=23)
 STEP_SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, G8, KV16, SHORT_ROWS_Q8, SMALL_FREQS,
-               SMALL_WINDOW, SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL]
+               SMALL_WINDOW, SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL, SMALL_YARN]
 
 
 @pytest.mark.parametrize("cfg", STEP_SMALLS, ids=lambda c: c.name)
@@ -89,6 +89,13 @@ def test_step_1b_q8_window_sinks_temperature():
     cfg = synth.C4.with_(n_ctx=200, attn_window=70, attn_sinks=3, attn_temp_scale=0.1, attn_temp_len=64)
     load(cfg, kind=2).close()
     run_decode(cfg, n_prompt=150, n_steps=4, prefill_gpu=True, prefill_ref=True)
+
+
+def test_step_1b_q8_yarn_shape():
+    # the benchmark kernel (kind 2) reading a YaRN table (factor 16)
+    cfg = synth.C4.with_(n_ctx=160, yarn_factor=16.0, yarn_orig_ctx=16384)
+    load(cfg, kind=2).close()
+    run_decode(cfg, n_prompt=20, n_steps=4)
 
 
 def test_step_1b_f16_shape():
