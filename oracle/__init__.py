@@ -24,7 +24,7 @@ class OrcConfig(ctypes.Structure):
         ("eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_window", ctypes.c_int32),
         ("attn_sinks", ctypes.c_int32), ("attn_temp_scale", ctypes.c_float), ("attn_temp_len", ctypes.c_int32),
         ("yarn_factor", ctypes.c_float), ("yarn_orig_ctx", ctypes.c_int32), ("yarn_beta_fast", ctypes.c_float),
-        ("yarn_beta_slow", ctypes.c_float)]
+        ("yarn_beta_slow", ctypes.c_float), ("numerics", ctypes.c_int32)]
 
 
 class OrcYarn(ctypes.Structure):
@@ -78,6 +78,10 @@ def lib():
         L.orc_attention.restype = None
         L.orc_attention_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
         L.orc_attention_ex.restype = None
+        L.orc_attention_nx.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+        L.orc_attention_nx.restype = None
+        L.orc_round_input.argtypes = [vp, i64, i32]
+        L.orc_round_input.restype = ctypes.c_int
         L.orc_attn_temp.argtypes = [i32, f32, i32]
         L.orc_attn_temp.restype = f32
         L.orc_attends.argtypes = [i32, i32, i32, i32]
@@ -202,7 +206,7 @@ def argmax(v: np.ndarray) -> int:
 
 def attention(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray, n_heads: int, n_kv_heads: int, head_dim: int,
               pos: int, want_weights: bool = False, window: int = 0, sinks: int = 0, temp_scale: float = 0.0,
-              temp_len: int = 0):
+              temp_len: int = 0, round16: bool = False):
     """kcache/vcache: binary16 bits, [>= pos+1][n_kv_heads * head_dim]. window /
     sinks: the attended rows (0: all rows up to pos); temp_scale / temp_len:
     the attention temperature (0: none)."""
@@ -211,13 +215,25 @@ def attention(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray, n_heads: in
     vc = np.ascontiguousarray(vcache, np.uint16)
     out = np.empty(n_heads * head_dim, np.float32)
     wts = np.empty((n_heads, pos + 1), np.float32) if want_weights else None
-    if window == 0 and sinks == 0 and temp_scale == 0.0:
+    if round16:
+        lib().orc_attention_nx(_p(out), _p(q), _p(kc), _p(vc), n_heads, n_kv_heads, head_dim, pos, window, sinks,
+                               temp_scale, temp_len, 1, _p(wts) if wts is not None else None)
+    elif window == 0 and sinks == 0 and temp_scale == 0.0:
         lib().orc_attention(_p(out), _p(q), _p(kc), _p(vc), n_heads, n_kv_heads, head_dim, pos,
                             _p(wts) if wts is not None else None)
     else:
         lib().orc_attention_ex(_p(out), _p(q), _p(kc), _p(vc), n_heads, n_kv_heads, head_dim, pos, window, sinks,
                                temp_scale, temp_len, _p(wts) if wts is not None else None)
     return (out, wts) if want_weights else out
+
+
+def round_input(x: np.ndarray, dtype: int) -> np.ndarray:
+    """A product's input as llama.cpp rounds it for weights of type dtype."""
+    v = np.array(x, np.float32, copy=True)
+    rc = lib().orc_round_input(_p(v), v.size, dtype)
+    if rc:
+        raise ValueError(f"orc_round_input: {rc}")
+    return v
 
 
 def attn_temp(pos: int, temp_scale: float, temp_len: int) -> float:
@@ -249,6 +265,7 @@ def make_config(cfg) -> OrcConfig:
     c.yarn_orig_ctx = int(getattr(cfg, "yarn_orig_ctx", 0))
     c.yarn_beta_fast = float(getattr(cfg, "yarn_beta_fast", 32.0))
     c.yarn_beta_slow = float(getattr(cfg, "yarn_beta_slow", 1.0))
+    c.numerics = int(getattr(cfg, "numerics", 0))
     return c
 
 

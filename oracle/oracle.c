@@ -54,6 +54,9 @@ typedef struct {
     float yarn_factor;
     int32_t yarn_orig_ctx;
     float yarn_beta_fast, yarn_beta_slow;
+    /* 0: float activations (the Java engine); 1: llama.cpp's rounding points
+     * ("What a Llama model computes, and why", section 8) */
+    int32_t numerics;
 } orc_config;
 
 typedef struct {
@@ -170,6 +173,26 @@ int orc_quantize_q8_0(const float* x, int64_t n, uint8_t* out) {
         out[34 * b] = (uint8_t)(dh & 0xff);
         out[34 * b + 1] = (uint8_t)(dh >> 8);
         for (int j = 0; j < 32; j++) out[34 * b + 2 + j] = (uint8_t)(int8_t)round_half_away(x[32 * b + j] * id);
+    }
+    return ORC_OK;
+}
+
+/* llama.cpp's rounding of a matrix product's input ("What a Llama model
+ * computes, and why", section 8): for Q8_0 weights each block of 32 is
+ * quantized as orc_quantize_q8_0 does (Example 8's quantizer) and the product
+ * sees the block's binary16 scale times its code; for F16 weights the input is
+ * rounded to binary16; F32 weights see it unchanged. In place, n values. */
+int orc_round_input(float* x, int64_t n, int32_t dtype) {
+    if (dtype == ORC_F16) {
+        for (int64_t i = 0; i < n; i++) x[i] = orc_f16_to_f32(orc_f32_to_f16(x[i]));
+        return ORC_OK;
+    }
+    if (dtype != ORC_Q8_0) return ORC_OK;
+    if (n % 32) return ORC_ERR_SHAPE;
+    uint8_t blk[34];
+    for (int64_t b = 0; b < n / 32; b++) {
+        orc_quantize_q8_0(x + 32 * b, 32, blk);
+        orc_dequantize(ORC_Q8_0, blk, 32, x + 32 * b);
     }
     return ORC_OK;
 }
@@ -343,9 +366,13 @@ int orc_attends(int32_t t, int32_t pos, int32_t window, int32_t sinks) {
  * sqrt(head_dim) over the attended rows, softmax, weighted sum of V. Query
  * head h reads KV head h / (n_heads / n_kv_heads). weights (optional) gets
  * [n_heads][pos + 1] probabilities, 0 for rows not attended. */
-void orc_attention_ex(float* out, const float* q, const uint16_t* kcache, const uint16_t* vcache, int32_t n_heads,
+/* round16 (llama.cpp's rounding points, "What a Llama model computes, and
+ * why", section 8): the scaled query is rounded to binary16 before q.k, and
+ * each probability, after the softmax's division, before it weights V; weights
+ * then receives the rounded probabilities. */
+void orc_attention_nx(float* out, const float* q, const uint16_t* kcache, const uint16_t* vcache, int32_t n_heads,
                       int32_t n_kv_heads, int32_t head_dim, int32_t pos, int32_t window, int32_t sinks,
-                      float temp_scale, int32_t temp_len, float* weights) {
+                      float temp_scale, int32_t temp_len, int32_t round16, float* weights) {
     int32_t kv_dim = n_kv_heads * head_dim, group = n_heads / n_kv_heads;
     float denom = (float)sqrt((double)head_dim);
     float tau = orc_attn_temp(pos, temp_scale, temp_len);
@@ -356,6 +383,8 @@ void orc_attention_ex(float* out, const float* q, const uint16_t* kcache, const 
         float* qs = (float*)malloc(sizeof(float) * (size_t)head_dim);
         int32_t kv_off = (h / group) * head_dim;
         for (int32_t i = 0; i < head_dim; i++) qs[i] = tau * q[h * head_dim + i];
+        if (round16)
+            for (int32_t i = 0; i < head_dim; i++) qs[i] = orc_f16_to_f32(orc_f32_to_f16(qs[i]));
         float mx = -INFINITY;
         for (int32_t t = 0; t <= pos; t++) {
             if (!orc_attends(t, pos, window, sinks)) continue;
@@ -373,6 +402,7 @@ void orc_attention_ex(float* out, const float* q, const uint16_t* kcache, const 
         for (int32_t t = 0; t <= pos; t++) {
             int on = orc_attends(t, pos, window, sinks);
             float a = on ? att[t] / sum : 0.0f;
+            if (round16) a = orc_f16_to_f32(orc_f32_to_f16(a));
             if (weights) weights[(int64_t)h * (pos + 1) + t] = a;
             if (!on) continue;
             for (int32_t i = 0; i < head_dim; i++)
@@ -381,6 +411,13 @@ void orc_attention_ex(float* out, const float* q, const uint16_t* kcache, const 
         free(qs);
         free(att);
     }
+}
+
+void orc_attention_ex(float* out, const float* q, const uint16_t* kcache, const uint16_t* vcache, int32_t n_heads,
+                      int32_t n_kv_heads, int32_t head_dim, int32_t pos, int32_t window, int32_t sinks,
+                      float temp_scale, int32_t temp_len, float* weights) {
+    orc_attention_nx(out, q, kcache, vcache, n_heads, n_kv_heads, head_dim, pos, window, sinks, temp_scale, temp_len, 0,
+                     weights);
 }
 
 /* The full causal span without temperature. */
@@ -396,6 +433,7 @@ void orc_attention(float* out, const float* q, const uint16_t* kcache, const uin
  * ---------------------------------------------------------------------- */
 typedef struct {
     float *attn_norm, *wq, *wk, *wv, *bq, *bk, *bv, *wo, *ffn_norm, *gate, *up, *down;
+    int32_t dt_q, dt_k, dt_v, dt_o, dt_gate, dt_up, dt_down; /* stored types of the matrices */
 } orc_layer;
 
 typedef struct orc_model {
@@ -405,6 +443,7 @@ typedef struct orc_model {
     orc_yarn yarn;
     const orc_yarn* yarn_on; /* &yarn, or NULL without YaRN */
     int tied;
+    int32_t dt_out; /* stored type of the output (or tied embedding) matrix */
     orc_layer* layers;
     uint16_t *kcache, *vcache; /* [layer][n_ctx][kv_dim] binary16 bits */
     int32_t len;
@@ -415,6 +454,8 @@ static const orc_tensor* find(const orc_tensor* ts, int32_t n, const char* name)
         if (ts[i].name && strcmp(ts[i].name, name) == 0) return &ts[i];
     return NULL;
 }
+
+static int32_t last_dtype; /* stored type of the tensor take() read last (load is single-threaded) */
 
 static int64_t need_bytes(int32_t dtype, int64_t n) {
     if (dtype == ORC_F32) return 4 * n;
@@ -428,6 +469,7 @@ static int take(const orc_tensor* ts, int32_t n, const char* name, int64_t ne0, 
                 float** out) {
     const orc_tensor* t = find(ts, n, name);
     *out = NULL;
+    if (t) last_dtype = t->dtype;
     if (!t) return optional ? ORC_OK : ORC_ERR_MISSING;
     int dims = ne1 > 0 ? 2 : 1;
     if (t->n_dims != dims || t->ne[0] != ne0 || (dims == 2 && t->ne[1] != ne1)) return ORC_ERR_SHAPE;
@@ -451,7 +493,7 @@ int orc_load(const orc_config* cfg, const orc_tensor* ts, int32_t n, orc_model**
         !(c.attn_temp_scale >= 0.0f && c.attn_temp_scale < INFINITY) || (c.attn_temp_scale > 0.0f && c.attn_temp_len <= 0) ||
         !(c.yarn_factor == 0.0f || (c.yarn_factor >= 1.0f && c.yarn_factor < INFINITY && c.yarn_orig_ctx > 0 &&
                                     c.yarn_beta_slow >= 0.0f && c.yarn_beta_fast > c.yarn_beta_slow &&
-                                    c.yarn_beta_fast < INFINITY)))
+                                    c.yarn_beta_fast < INFINITY)) || (c.numerics != 0 && c.numerics != 1))
         return ORC_ERR_ARG;
     orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
     m->c = c;
@@ -466,7 +508,9 @@ int orc_load(const orc_config* cfg, const orc_tensor* ts, int32_t n, orc_model**
     int32_t qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
     int rc = take(ts, n, "token_embd.weight", c.dim, c.vocab, 0, &m->tok_embd);
     if (!rc) rc = take(ts, n, "output_norm.weight", c.dim, 0, 0, &m->out_norm);
+    m->dt_out = last_dtype; /* the embedding's, unless an output matrix follows */
     if (!rc) rc = take(ts, n, "output.weight", c.dim, c.vocab, 1, &m->output);
+    if (!rc && m->output) m->dt_out = last_dtype;
     if (!rc) rc = take(ts, n, "rope_freqs.weight", c.rope_dims / 2, 0, 1, &m->rope_freqs);
     if (!rc && !m->output) { /* tied embeddings (Example 9) */
         m->output = m->tok_embd;
@@ -482,16 +526,23 @@ int orc_load(const orc_config* cfg, const orc_tensor* ts, int32_t n, orc_model**
     }
         TAKE(attn_norm, "attn_norm.weight", c.dim, 0, 0)
         TAKE(wq, "attn_q.weight", c.dim, qd, 0)
+        L->dt_q = last_dtype;
         TAKE(wk, "attn_k.weight", c.dim, kvd, 0)
+        L->dt_k = last_dtype;
         TAKE(wv, "attn_v.weight", c.dim, kvd, 0)
+        L->dt_v = last_dtype;
         TAKE(bq, "attn_q.bias", qd, 0, 1)
         TAKE(bk, "attn_k.bias", kvd, 0, 1)
         TAKE(bv, "attn_v.bias", kvd, 0, 1)
         TAKE(wo, "attn_output.weight", qd, c.dim, 0)
+        L->dt_o = last_dtype;
         TAKE(ffn_norm, "ffn_norm.weight", c.dim, 0, 0)
         TAKE(gate, "ffn_gate.weight", c.dim, c.ffn, 0)
+        L->dt_gate = last_dtype;
         TAKE(up, "ffn_up.weight", c.dim, c.ffn, 0)
+        L->dt_up = last_dtype;
         TAKE(down, "ffn_down.weight", c.ffn, c.dim, 0)
+        L->dt_down = last_dtype;
 #undef TAKE
         if (!rc && !((L->bq && L->bk && L->bv) || (!L->bq && !L->bk && !L->bv))) rc = ORC_ERR_MISSING;
     }
@@ -550,6 +601,19 @@ static const uint16_t* layer_v(const orc_model* m, int32_t l) {
     return m->vcache + (size_t)l * (size_t)m->c.n_ctx * (size_t)(m->c.n_kv_heads * m->c.head_dim);
 }
 
+/* out[t][rows] = W x_t for the n inputs x (n x cols), with x rounded for W's
+ * stored type first when the model uses llama.cpp's rounding points; tmp has
+ * room for n x cols floats. */
+static void product(const orc_model* m, float* out, const float* w, int32_t dt, const float* x, int32_t n, int32_t rows,
+                    int32_t cols, float* tmp) {
+    if (m->c.numerics && dt != ORC_F32) {
+        memcpy(tmp, x, sizeof(float) * (size_t)n * (size_t)cols);
+        for (int32_t t = 0; t < n; t++) orc_round_input(tmp + (int64_t)t * cols, cols, dt);
+        x = tmp;
+    }
+    orc_matmul(out, w, x, n, rows, cols);
+}
+
 /*
  * One token at position pos (Project 18, forward): fills the cache at pos in
  * every layer and writes the logits. Requires 0 <= pos <= len and pos < n_ctx;
@@ -568,35 +632,38 @@ int orc_forward(orc_model* m, int32_t token, int32_t pos, float* logits) {
     float* heads = (float*)malloc(sizeof(float) * (size_t)qd);
     float* hb = (float*)malloc(sizeof(float) * (size_t)c.ffn);
     float* hb2 = (float*)malloc(sizeof(float) * (size_t)c.ffn);
+    int32_t widest = c.ffn > c.dim ? c.ffn : c.dim;
+    if (qd > widest) widest = qd;
+    float* tmp = (float*)malloc(sizeof(float) * (size_t)widest);
 
     memcpy(x, m->tok_embd + (int64_t)token * c.dim, sizeof(float) * (size_t)c.dim); /* Example 3 */
     for (int32_t l = 0; l < c.n_layers; l++) {
         const orc_layer* w = &m->layers[l];
         orc_rmsnorm(xb, x, w->attn_norm, c.dim, c.eps);
-        orc_matvec(q, w->wq, xb, qd, c.dim);
-        orc_matvec(k, w->wk, xb, kvd, c.dim);
-        orc_matvec(v, w->wv, xb, kvd, c.dim);
+        product(m, q, w->wq, w->dt_q, xb, 1, qd, c.dim, tmp);
+        product(m, k, w->wk, w->dt_k, xb, 1, kvd, c.dim, tmp);
+        product(m, v, w->wv, w->dt_v, xb, 1, kvd, c.dim, tmp);
         add_bias(q, w->bq, qd);
         add_bias(k, w->bk, kvd);
         add_bias(v, w->bv, kvd);
         orc_rope_y(q, c.n_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs, m->yarn_on);
         orc_rope_y(k, c.n_kv_heads, c.head_dim, c.rope_dims, pos, c.rope_base, c.rope_neox, m->rope_freqs, m->yarn_on);
         store_kv(m, l, pos, k, v);
-        orc_attention_ex(heads, q, layer_k(m, l), layer_v(m, l), c.n_heads, c.n_kv_heads, c.head_dim, pos,
-                         c.attn_window, c.attn_sinks, c.attn_temp_scale, c.attn_temp_len, NULL);
-        orc_matvec(xb, w->wo, heads, c.dim, qd);
+        orc_attention_nx(heads, q, layer_k(m, l), layer_v(m, l), c.n_heads, c.n_kv_heads, c.head_dim, pos,
+                         c.attn_window, c.attn_sinks, c.attn_temp_scale, c.attn_temp_len, c.numerics, NULL);
+        product(m, xb, w->wo, w->dt_o, heads, 1, c.dim, qd, tmp);
         for (int32_t i = 0; i < c.dim; i++) x[i] += xb[i];
         orc_rmsnorm(xb, x, w->ffn_norm, c.dim, c.eps);
-        orc_matvec(hb, w->gate, xb, c.ffn, c.dim);
-        orc_matvec(hb2, w->up, xb, c.ffn, c.dim);
+        product(m, hb, w->gate, w->dt_gate, xb, 1, c.ffn, c.dim, tmp);
+        product(m, hb2, w->up, w->dt_up, xb, 1, c.ffn, c.dim, tmp);
         for (int32_t i = 0; i < c.ffn; i++) hb[i] = orc_silu(hb[i]) * hb2[i];
-        orc_matvec(xb, w->down, hb, c.dim, c.ffn);
+        product(m, xb, w->down, w->dt_down, hb, 1, c.dim, c.ffn, tmp);
         for (int32_t i = 0; i < c.dim; i++) x[i] += xb[i];
     }
     orc_rmsnorm(xb, x, m->out_norm, c.dim, c.eps);
-    orc_matvec(logits, m->output, xb, c.vocab, c.dim);
+    product(m, logits, m->output, m->dt_out, xb, 1, c.vocab, c.dim, tmp);
     m->len = pos + 1;
-    free(x); free(xb); free(q); free(k); free(v); free(heads); free(hb); free(hb2);
+    free(x); free(xb); free(q); free(k); free(v); free(heads); free(hb); free(hb2); free(tmp);
     return ORC_OK;
 }
 
@@ -629,8 +696,10 @@ int orc_prefill_rows(orc_model* m, const int32_t* tokens, int32_t n, const int32
     float* HEADS = (float*)malloc(sizeof(float) * (size_t)n * (size_t)qd);
     float* HB = (float*)malloc(sizeof(float) * (size_t)n * (size_t)c.ffn);
     float* HB2 = (float*)malloc(sizeof(float) * (size_t)n * (size_t)c.ffn);
-    if (!X || !XB || !Q || !K || !V || !HEADS || !HB || !HB2) {
-        free(X); free(XB); free(Q); free(K); free(V); free(HEADS); free(HB); free(HB2);
+    int32_t widest = c.ffn > wide ? c.ffn : wide;
+    float* TMP = (float*)malloc(sizeof(float) * (size_t)n * (size_t)widest);
+    if (!X || !XB || !Q || !K || !V || !HEADS || !HB || !HB2 || !TMP) {
+        free(X); free(XB); free(Q); free(K); free(V); free(HEADS); free(HB); free(HB2); free(TMP);
         return ORC_ERR_OOM;
     }
     for (int32_t t = 0; t < n; t++)
@@ -638,9 +707,9 @@ int orc_prefill_rows(orc_model* m, const int32_t* tokens, int32_t n, const int32
     for (int32_t l = 0; l < c.n_layers; l++) {
         const orc_layer* w = &m->layers[l];
         for (int32_t t = 0; t < n; t++) orc_rmsnorm(XB + (int64_t)t * c.dim, X + (int64_t)t * c.dim, w->attn_norm, c.dim, c.eps);
-        orc_matmul(Q, w->wq, XB, n, qd, c.dim);
-        orc_matmul(K, w->wk, XB, n, kvd, c.dim);
-        orc_matmul(V, w->wv, XB, n, kvd, c.dim);
+        product(m, Q, w->wq, w->dt_q, XB, n, qd, c.dim, TMP);
+        product(m, K, w->wk, w->dt_k, XB, n, kvd, c.dim, TMP);
+        product(m, V, w->wv, w->dt_v, XB, n, kvd, c.dim, TMP);
         for (int32_t t = 0; t < n; t++) {
             float *q = Q + (int64_t)t * qd, *k = K + (int64_t)t * kvd, *v = V + (int64_t)t * kvd;
             add_bias(q, w->bq, qd);
@@ -651,24 +720,24 @@ int orc_prefill_rows(orc_model* m, const int32_t* tokens, int32_t n, const int32
             store_kv(m, l, len + t, k, v);
         }
         for (int32_t t = 0; t < n; t++)
-            orc_attention_ex(HEADS + (int64_t)t * qd, Q + (int64_t)t * qd, layer_k(m, l), layer_v(m, l), c.n_heads,
+            orc_attention_nx(HEADS + (int64_t)t * qd, Q + (int64_t)t * qd, layer_k(m, l), layer_v(m, l), c.n_heads,
                              c.n_kv_heads, c.head_dim, len + t, c.attn_window, c.attn_sinks, c.attn_temp_scale,
-                             c.attn_temp_len, NULL);
-        orc_matmul(XB, w->wo, HEADS, n, c.dim, qd);
+                             c.attn_temp_len, c.numerics, NULL);
+        product(m, XB, w->wo, w->dt_o, HEADS, n, c.dim, qd, TMP);
         for (int64_t i = 0; i < (int64_t)n * c.dim; i++) X[i] += XB[i];
         for (int32_t t = 0; t < n; t++) orc_rmsnorm(XB + (int64_t)t * c.dim, X + (int64_t)t * c.dim, w->ffn_norm, c.dim, c.eps);
-        orc_matmul(HB, w->gate, XB, n, c.ffn, c.dim);
-        orc_matmul(HB2, w->up, XB, n, c.ffn, c.dim);
+        product(m, HB, w->gate, w->dt_gate, XB, n, c.ffn, c.dim, TMP);
+        product(m, HB2, w->up, w->dt_up, XB, n, c.ffn, c.dim, TMP);
         for (int64_t i = 0; i < (int64_t)n * c.ffn; i++) HB[i] = orc_silu(HB[i]) * HB2[i];
-        orc_matmul(XB, w->down, HB, n, c.dim, c.ffn);
+        product(m, XB, w->down, w->dt_down, HB, n, c.dim, c.ffn, TMP);
         for (int64_t i = 0; i < (int64_t)n * c.dim; i++) X[i] += XB[i];
     }
     for (int32_t r = 0; r < n_rows; r++) {
         orc_rmsnorm(XB, X + (int64_t)rows[r] * c.dim, m->out_norm, c.dim, c.eps);
-        orc_matvec(out + (int64_t)r * c.vocab, m->output, XB, c.vocab, c.dim);
+        product(m, out + (int64_t)r * c.vocab, m->output, m->dt_out, XB, 1, c.vocab, c.dim, TMP);
     }
     m->len = len + n;
-    free(X); free(XB); free(Q); free(K); free(V); free(HEADS); free(HB); free(HB2);
+    free(X); free(XB); free(Q); free(K); free(V); free(HEADS); free(HB); free(HB2); free(TMP);
     return ORC_OK;
 }
 

@@ -83,6 +83,7 @@ class ModelConfig:
     yarn_orig_ctx: int = 0  # the original context YaRN's ramp is measured against
     yarn_beta_fast: float = 32.0  # pairs with more turns than this over it keep their angle
     yarn_beta_slow: float = 1.0  # pairs with fewer turns are interpolated by the factor
+    numerics: int = 0  # 0: float activations; 1: llama.cpp's rounding points
     weight_std: float = 0.02
     q8_scale_std: float = 0.002
     gain_std: float = 0.0  # norm gains are 1 + N(0, gain_std); 0 gives exactly 1.0

@@ -328,6 +328,93 @@ def test_model_yarn_factor_one_equals_plain_and_model_reads_yarn():
             oracle.Model(SMALL.with_(**kw), ts)
 
 
+# ------------------------------------------------------------ llama.cpp's rounding points
+# "What a Llama model computes, and why", section 8: a quantized product's input
+# is rounded to Q8_0 before the integer dot, an F16 product's input to binary16,
+# q to binary16 before q.k, and the probabilities to binary16 before they
+# weight V (numerics = 1).
+def _q8_fields(raw):
+    blocks = raw.reshape(-1, 34)
+    d = np.array([oracle.f16_to_f32(int(b[0]) | (int(b[1]) << 8)) for b in blocks], np.float64)
+    return d, blocks[:, 2:].view(np.int8).astype(np.int64)
+
+
+def test_rounded_q8_input_is_its_quantized_blocks():
+    x = synth.normal(41, "x", 256) * np.float32(3)
+    x[40] = np.float32(-7.5)  # a block whose largest magnitude is negative
+    y = oracle.round_input(x, 8)
+    d, q = _q8_fields(oracle.quantize_q8_0(x))
+    np.testing.assert_array_equal(y, (d[:, None] * q).astype(np.float32).reshape(-1))
+    assert np.all(np.abs(q) <= 127) and np.all(np.abs(q).max(1) == 127)
+    # within half a step of the block's scale (plus the scale's binary16 rounding)
+    amax = np.abs(x.reshape(-1, 32)).max(1).astype(np.float64)
+    bound = d / 2 + 127 * np.abs(d - amax / 127) + 1e-9
+    assert np.all(np.abs(y.reshape(-1, 32) - x.reshape(-1, 32)) <= bound[:, None])
+
+
+def test_rounded_f16_input_is_the_library_conversion_and_f32_is_untouched():
+    x = synth.normal(42, "x", 512) * np.float32(50)
+    np.testing.assert_array_equal(oracle.round_input(x, 1), x.astype(np.float16).astype(np.float32))
+    np.testing.assert_array_equal(oracle.round_input(x, 0), x)
+
+
+def test_q8_product_of_rounded_input_is_the_integer_dot():
+    # the product of the dequantized weights with the rounded input equals the
+    # integer formulation sum_b d_w d_x sum_j q_w q_x within fp32 summation error
+    rows, cols = 7, 96
+    w = synth.normal(43, "w", rows * cols) * np.float32(0.5)
+    x = synth.normal(43, "x", cols) * np.float32(2)
+    wraw = oracle.quantize_q8_0(w)
+    wd = oracle.dequantize(8, wraw, rows * cols)
+    got = oracle.matvec(wd, oracle.round_input(x, 8), rows, cols)
+    dw, qw = _q8_fields(wraw)
+    dx, qx = _q8_fields(oracle.quantize_q8_0(x))
+    nb = cols // 32
+    for r in range(rows):
+        exact = sum(dw[r * nb + b] * dx[b] * int(np.dot(qw[r * nb + b], qx[b])) for b in range(nb))
+        scale = sum(abs(dw[r * nb + b] * dx[b]) * int(np.abs(qw[r * nb + b]) @ np.abs(qx[b])) for b in range(nb))
+        assert abs(got[r] - exact) <= 1e-6 * scale
+
+
+def test_rounded_attention_brute_force():
+    q, kb, vb, H, KVH, hd, P = _span_inputs(44)
+    for pos in (0, 6, P - 1):
+        out, w = oracle.attention(q, kb, vb, H, KVH, hd, pos, want_weights=True, round16=True)
+        K = _f16_vals(kb[:pos + 1].reshape(-1)).reshape(pos + 1, KVH, hd).astype(np.float64)
+        V = _f16_vals(vb[:pos + 1].reshape(-1)).reshape(pos + 1, KVH, hd).astype(np.float64)
+        Q = q.astype(np.float16).astype(np.float64).reshape(H, hd)
+        for h in range(H):
+            g = h // (H // KVH)
+            sc = K[:, g] @ Q[h] / math.sqrt(hd)
+            a = np.exp(sc - sc.max())
+            a = (a / a.sum()).astype(np.float16).astype(np.float64)
+            np.testing.assert_allclose(w[h], a, rtol=1e-3, atol=1e-7)  # probabilities on the binary16 grid
+            assert np.array_equal(w[h].astype(np.float16).astype(np.float32), w[h])
+            np.testing.assert_allclose(out[h * hd:(h + 1) * hd], w[h].astype(np.float64) @ V[:, g], rtol=1e-5,
+                                       atol=1e-6)
+        plain = oracle.attention(q, kb, vb, H, KVH, hd, pos)
+        if pos > 0:
+            assert not np.array_equal(plain, out)
+
+
+@pytest.mark.parametrize("cfg", [SMALL, SMALL_F16, SMALL_Q8], ids=lambda c: c.name)
+def test_llamacpp_numerics_prefill_rows_equal_token_by_token_bit_exact(cfg):
+    cfg = cfg.with_(numerics=1)
+    ts = synth.make_tensor_set(cfg)
+    toks = synth.prompt(cfg, 9)
+    a, b = oracle.Model(cfg, ts), oracle.Model(cfg, ts)
+    want = np.stack([a.forward(int(t), p) for p, t in enumerate(toks)])
+    got = b.prefill_rows(toks, [8, 0, 4])
+    for r, g in zip([8, 0, 4], got):
+        assert np.array_equal(g.view(np.uint32), want[r].view(np.uint32))
+    plain = oracle.Model(cfg.with_(numerics=0), ts)
+    base = np.stack([plain.forward(int(t), p) for p, t in enumerate(toks)])
+    diff = float(np.max(np.abs(base - want)))
+    assert 0 < diff < 0.5, diff  # the rounding moves the logits, a little
+    for m in (a, b, plain):
+        m.close()
+
+
 # ------------------------------------------------------------ silu / SwiGLU
 def test_silu_printed_values():
     g = golden("swiglu.json")["silu"]
