@@ -13,11 +13,13 @@ compiled for this shape). The line also reports
     events on the context's stream; its algorithmic bytes are the step's
     (every weight once, the K/V rows 0..pos, the new K/V row); HBM traffic
     from the committed rocprofv3 counter runs;
-  - prefill: llm_prefill of 512 seeded ids on the Qwen2-style F16 variant;
+  - prefill: llm_prefill of 512 seeded ids on the Qwen2-style F16 variant
+    (also with every row's logits, and with llama.cpp's rounding points);
   - decode_reports: the same decode with F16 matrices at context 2048, with
     Q8_0 at context 8192 (attention a larger share of the bytes), with
-    Llama 3's RoPE frequency factors (rope_freqs.weight), and at context 8192
-    with a 1024-row sliding window plus 4 sink rows;
+    Llama 3's RoPE frequency factors (rope_freqs.weight), at context 8192
+    with a 1024-row sliding window plus 4 sink rows, and with llama.cpp's
+    rounding points (on the launch graph);
   - cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 8]
@@ -153,13 +155,33 @@ def measure_prefill(llm, synth, np, torch, reps=5):
     pm.close()
     del pm, out
     torch.cuda.empty_cache()
-    print(f"# prefill 512: {pt * 1e3:.2f} ms, {512 / pt:.0f} tok/s; with all 512 logit rows {rt * 1e3:.2f} ms",
-          file=sys.stderr, flush=True)
+    # the same prompt with llama.cpp's rounding points (numerics 1)
+    c5n = c5.with_(numerics=1)
+    ts = synth.make_tensor_set(c5n)
+    pn = llm.Model(c5n, ts)
+    del ts
+    pn.prefill(p5)
+    pn.reset()
+    ntimes = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        pn.prefill(p5)
+        torch.cuda.synchronize()
+        ntimes.append(time.perf_counter() - t0)
+        pn.reset()
+    nt = float(np.median(ntimes))
+    pn.close()
+    del pn
+    torch.cuda.empty_cache()
+    print(f"# prefill 512: {pt * 1e3:.2f} ms, {512 / pt:.0f} tok/s; with all 512 logit rows {rt * 1e3:.2f} ms; "
+          f"with llama.cpp's rounding points {nt * 1e3:.2f} ms", file=sys.stderr, flush=True)
     return {"config": c5.name, "tokens": 512, "ms": round(pt * 1e3, 3), "tok_s": round(512 / pt, 1),
             "gemm_tflop": round(gemm_flop / 1e12, 4),
             "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
             "all_rows_ms": round(rt * 1e3, 3), "all_rows_gemm_tflop": round(rows_flop / 1e12, 4),
-            "all_rows_mfma_frac": round(rows_flop / rt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
+            "all_rows_mfma_frac": round(rows_flop / rt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+            "llamacpp_numerics_ms": round(nt * 1e3, 3), "llamacpp_numerics_tok_s": round(512 / nt, 1)}
 
 
 def measure_decode_report(llm, synth, np, torch, cfg, ctx_len, steps=64, reps=3):
@@ -294,7 +316,9 @@ def main():
                                          synth.C4.with_(name="llama-1b-q8_0-rope-freqs", rope_freq_factors=True), 2048),
                    measure_decode_report(llm, synth, np, torch,
                                          synth.C4_LONG.with_(name="llama-1b-q8_0-window1024-sinks4", attn_window=1024,
-                                                             attn_sinks=4), 8192)]
+                                                             attn_sinks=4), 8192),
+                   measure_decode_report(llm, synth, np, torch,
+                                         synth.C4.with_(name="llama-1b-q8_0-llamacpp-numerics", numerics=1), 2048)]
 
     cpu = None
     if not args.no_cpu:

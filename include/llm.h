@@ -94,7 +94,14 @@ typedef struct {
  * r = yarn_orig_ctx * theta_i / (2 pi) turns over the original context; a
  * ramp g(r), 0 below yarn_beta_slow and 1 above yarn_beta_fast (linear in
  * between; Ministral 3 uses 1 and 32), turns the angle a into
- * (1 - g) a / s + g a, and q and k are scaled by 1 + 0.1 ln s. */
+ * (1 - g) a / s + g a, and q and k are scaled by 1 + 0.1 ln s.
+ *
+ * numerics: 0 computes with float activations (the Java engine's numerics);
+ * 1 rounds where llama.cpp rounds ("What a Llama model computes, and why",
+ * section 8): a Q8_0 product's input to Q8_0 blocks (Example 8's quantizer),
+ * an F16 product's input to binary16, q to binary16 before q.k, and the
+ * softmax probabilities to binary16 before they weight V. Mode 1 decodes on
+ * the launch graph (the persistent step kernel computes mode 0 only). */
 typedef struct {
     int32_t dim, n_layers, n_heads, n_kv_heads, head_dim, ffn, vocab, n_ctx, rope_dims, rope_neox;
     float eps, rope_base;
@@ -104,6 +111,7 @@ typedef struct {
     float yarn_factor;
     int32_t yarn_orig_ctx;
     float yarn_beta_fast, yarn_beta_slow;
+    int32_t numerics;
 } llm_config;
 
 /*

@@ -51,7 +51,7 @@ class llm_config(ctypes.Structure):
         ("eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("attn_window", ctypes.c_int32),
         ("attn_sinks", ctypes.c_int32), ("attn_temp_scale", ctypes.c_float), ("attn_temp_len", ctypes.c_int32),
         ("yarn_factor", ctypes.c_float), ("yarn_orig_ctx", ctypes.c_int32), ("yarn_beta_fast", ctypes.c_float),
-        ("yarn_beta_slow", ctypes.c_float)]
+        ("yarn_beta_slow", ctypes.c_float), ("numerics", ctypes.c_int32)]
 
 
 _lib = None
@@ -128,6 +128,7 @@ def make_config(cfg) -> llm_config:
     c.yarn_orig_ctx = int(getattr(cfg, "yarn_orig_ctx", 0))
     c.yarn_beta_fast = float(getattr(cfg, "yarn_beta_fast", 32.0))
     c.yarn_beta_slow = float(getattr(cfg, "yarn_beta_slow", 1.0))
+    c.numerics = int(getattr(cfg, "numerics", 0))
     return c
 
 

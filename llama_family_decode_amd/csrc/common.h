@@ -60,6 +60,22 @@ __host__ __device__ inline int span_row(const Span& s, int j) { return j < s.ns 
 __host__ __device__ inline bool span_has(const SpanCfg& c, int t, int pos) {
     return t <= pos && (c.window <= 0 || t > pos - c.window || t < c.sinks);
 }
+// v rounded to binary16 and back
+__device__ __forceinline__ float round16(float v) { return __half2float(__float2half_rn(v)); }
+
+// llama.cpp's rounding of 32 consecutive product inputs for Q8_0 weights
+// ("What a Llama model computes, and why", section 8, with the Q8_0 quantizer
+// of "The Forward Pass in Java", Example 8): d = amax / 127 and its inverse in
+// float, codes roundf(x / d) (halves away from zero), values f16(d) * code.
+__device__ __forceinline__ void q8_round32(float (&v)[32]) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
+    const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f, dh = round16(d);
+#pragma unroll
+    for (int j = 0; j < 32; j++) v[j] = dh * roundf(v[j] * id);
+}
+
 // The query scale, evaluated in double and rounded to float.
 __host__ __device__ inline float attn_temp(const SpanCfg& c, int pos) {
     if (c.temp_scale == 0.0f || c.temp_len <= 0) return 1.0f;
@@ -177,6 +193,7 @@ struct GemvArgs {
     // EPI_ARGMAX
     int* gen_out;
     int gen_cap;
+    int n3;  // llama.cpp's rounding points: round the staged input for W's type
 };
 
 struct AttnArgs {
@@ -192,6 +209,11 @@ struct AttnArgs {
     int n_split;          // gridDim.x
     float scale_div;      // scores are divided by this ((float)sqrt(head_dim))
     SpanCfg span;
+    // llama.cpp's rounding points (q and the probabilities to binary16) run as
+    // passes: 1 = split maxima and sums only, 2 = the weighted sum of V with
+    // probabilities f16(e^(s - M) / L) from stats ([n_q][n_heads][2]: M, L)
+    int n3;
+    float* stats;
 };
 
 // YaRN parameters (factor 0: off).
@@ -229,6 +251,10 @@ hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim
 hipError_t launch_gather_rows(const float* src, int K, const int* idx, int k, float* dst, hipStream_t s);
 // H, L = the tiled binary16 hi/lo planes of the n x K fp32 rows X.
 hipError_t launch_split_hl(const float* X, int n, int K, __half* H, __half* L, hipStream_t s);
+// llama.cpp's rounding of the n x K fp32 product inputs X for weights of type
+// dtype (Q8_0: each 32-block to its quantized values; F16: to binary16), in
+// place; H, L (if set) get the rounded rows' tiled hi/lo planes.
+hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __half* L, hipStream_t s);
 // The tiled copy of an F16 matrix (rows padded with zeros to a multiple of 256).
 hipError_t launch_tile_w(const Mat& W, void* dst, hipStream_t s);
 // Causal prefill attention of n_q queries at positions p0 .. p0+n_q-1 on the

@@ -52,6 +52,24 @@ __device__ void stage_input(const GemvArgs& a, float* xs, double* red) {
             xs[j] = xs[j] * scale * a.gain[i];
         }
     }
+    if constexpr (DT != DT_F32) {
+        if (a.n3) {  // llama.cpp's rounding of the product's input for this weight type
+            __syncthreads();
+            for (int b = tid; b < K / 32; b += kBlock) {
+                float v[32];
+#pragma unroll
+                for (int j = 0; j < 32; j++) v[j] = xs[swz<DT>(32 * b + j)];
+                if constexpr (DT == DT_Q8) {
+                    q8_round32(v);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 32; j++) v[j] = round16(v[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < 32; j++) xs[swz<DT>(32 * b + j)] = v[j];
+            }
+        }
+    }
     __syncthreads();
 }
 
@@ -421,7 +439,10 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
-        for (int i = 0; i < 8; i++) qv[h][i] = dim_ok ? tau * qz[(g * G + h) * hd + sub * 8 + i] : 0.f;
+        for (int i = 0; i < 8; i++) {
+            const float v = dim_ok ? tau * qz[(g * G + h) * hd + sub * 8 + i] : 0.f;
+            qv[h][i] = a.n3 ? round16(v) : v;
+        }
     float acc[G][8];
 #pragma unroll
     for (int h = 0; h < G; h++)
@@ -463,6 +484,16 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
             }
         }
         __syncthreads();
+        if (a.n3 == 2) {
+            // probabilities from the whole span's max M and sum L, rounded
+            // to binary16 before they weight V
+            for (int h = wave; h < G; h += kWaves) {
+                const float* mz = a.stats + ((size_t)z * a.n_heads + g * G + h) * 2;
+                const float M = mz[0], L = mz[1];
+                for (int t = lane; t < cn; t += 64) sc[h * CHUNK + t] = round16(expf(sc[h * CHUNK + t] - M) / L);
+                if (lane == 0) alpha[h] = 1.f;
+            }
+        } else
         // chunk max, running max, weights and their sum (one wave per head)
         for (int h = wave; h < G; h += kWaves) {
             float mx = -INFINITY;
@@ -495,7 +526,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < kAttnSteps; i++) {
             const int t = pg + i * PPI;
-            if (dim_ok && t < cn) {
+            if (dim_ok && t < cn && a.n3 != 1) {
                 float vf[8];
                 unpack8(vr[i], vf);
 #pragma unroll
@@ -527,12 +558,12 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     const int GH = G * hd;
     float* outz = a.out + (size_t)z * qd + (size_t)g * G * hd;
     __half* outhz = a.out_h ? a.out_h + (size_t)z * qd + (size_t)g * G * hd : nullptr;
-    if (n_active == 1) {
+    if (n_active == 1 && a.n3 != 1) {
         for (int e = tid; e < GH; e += kBlock) {
             float o = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; w++) o += wred[w * GH + e];
-            const float r = o / l_run[e / hd];
+            const float r = a.n3 == 2 ? o : o / l_run[e / hd];
             outz[e] = r;
             if (outhz) outhz[e] = f2h(r);
         }
@@ -600,6 +631,55 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(AttnArgs a) {
     }
 }
 
+// The rounded-probability passes (llama.cpp's rounding points): after pass 1,
+// each head's span maximum M = max m_s and sum L = sum l_s e^(m_s - M) over its
+// splits, in split order, go to stats.
+template <int G>
+__global__ __launch_bounds__(64 * G) void k_attn_stats(AttnArgs a) {
+    const int g = blockIdx.x, z = blockIdx.y, h = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int P = attn_span(a.span, a.st ? a.st->pos : a.p0 + z).n;
+    const int S = a.n_split;
+    int CH = (P + S - 1) / S;
+    CH = (CH + 15) & ~15;
+    const int n_active = (P + CH - 1) / CH;
+    const int stride = a.head_dim + 2;
+    const float* parts = a.part + (((size_t)z * a.n_kv_heads + g) * S) * (size_t)(G * stride) + h * stride;
+    float M = -INFINITY;
+    for (int j = lane; j < n_active; j += 64) M = fmaxf(M, parts[(size_t)j * G * stride]);
+    M = wave_max(M);
+    float L = 0.f;
+    if (lane == 0)
+        for (int j = 0; j < n_active; j++) L += parts[(size_t)j * G * stride + 1] * expf(parts[(size_t)j * G * stride] - M);
+    if (lane == 0) {
+        float* st = a.stats + ((size_t)z * a.n_heads + g * G + h) * 2;
+        st[0] = M;
+        st[1] = L;
+    }
+}
+
+// After pass 2 with several active splits: out = sum of the splits' outputs,
+// in split order.
+template <int G>
+__global__ __launch_bounds__(kBlock) void k_attn_sum(AttnArgs a) {
+    const int g = blockIdx.x, z = blockIdx.y;
+    const int hd = a.head_dim;
+    const int P = attn_span(a.span, a.st ? a.st->pos : a.p0 + z).n;
+    const int S = a.n_split;
+    int CH = (P + S - 1) / S;
+    CH = (CH + 15) & ~15;
+    const int n_active = (P + CH - 1) / CH;
+    if (n_active == 1) return;
+    const int stride = hd + 2, GH = G * hd, qd = a.n_heads * hd;
+    const float* parts = a.part + (((size_t)z * a.n_kv_heads + g) * S) * (size_t)(G * stride);
+    for (int e = threadIdx.x; e < GH; e += kBlock) {
+        const float* po = parts + (e / hd) * stride + 2 + e % hd;
+        float O = 0.f;
+        for (int j = 0; j < n_active; j++) O += po[(size_t)j * G * stride];
+        a.out[(size_t)z * qd + (size_t)g * GH + e] = O;
+        if (a.out_h) a.out_h[(size_t)z * qd + (size_t)g * GH + e] = f2h(O);
+    }
+}
+
 template <int G>
 static hipError_t launch_attn_g(const AttnArgs& a, int n_q, hipStream_t s) {
     const size_t lds = ((size_t)G * attn_chunk(a.head_dim) + (size_t)kWaves * G * a.head_dim) * sizeof(float);
@@ -608,6 +688,18 @@ static hipError_t launch_attn_g(const AttnArgs& a, int n_q, hipStream_t s) {
         hipError_t e = hipFuncSetAttribute((const void*)k_attn<G>, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
         if (e != hipSuccess) return e;
         attr_done = true;
+    }
+    if (a.n3) {
+        AttnArgs p = a;
+        p.n3 = 1;  // split maxima and sums
+        hipLaunchKernelGGL((k_attn<G>), dim3(a.n_split, a.n_kv_heads, n_q), dim3(kBlock), lds, s, p);
+        hipLaunchKernelGGL((k_attn_stats<G>), dim3(a.n_kv_heads, n_q), dim3(64 * G), 0, s, p);
+        p.n3 = 2;  // the weighted sum with the rounded probabilities
+        hipLaunchKernelGGL((k_attn<G>), dim3(a.n_split, a.n_kv_heads, n_q), dim3(kBlock), lds, s, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.n_split == 1) return e;
+        hipLaunchKernelGGL((k_attn_sum<G>), dim3(a.n_kv_heads, n_q), dim3(kBlock), 0, s, p);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((k_attn<G>), dim3(a.n_split, a.n_kv_heads, n_q), dim3(kBlock), lds, s, a);
     hipError_t e = hipGetLastError();

@@ -81,6 +81,39 @@ hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim
     return hipGetLastError();
 }
 
+__global__ void k_round_rows(float* X, int K, int dtype, __half* H, __half* L) {
+    const int row = blockIdx.x;
+    float* x = X + (size_t)row * K;
+    for (int b = threadIdx.x; b < K / 32; b += blockDim.x) {
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 32; j++) v[j] = x[32 * b + j];
+        if (dtype == DT_Q8) {
+            q8_round32(v);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 32; j++) v[j] = round16(v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            x[32 * b + j] = v[j];
+            if (H) {
+                const __half h = __float2half_rn(v[j]);
+                const size_t t = tile_off(row, 32 * b + j, K, kTileA);
+                H[t] = h;
+                L[t] = __float2half_rn(v[j] - __half2float(h));
+            }
+        }
+    }
+}
+
+hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __half* L, hipStream_t s) {
+    if (dtype == DT_F32 || n <= 0) return hipSuccess;
+    if (K % 32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_round_rows, dim3(n), dim3(64), 0, s, X, K, dtype, H, L);
+    return hipGetLastError();
+}
+
 __global__ void k_gather_rows(const float* src, int K, const int* idx, float* dst) {
     const int j = blockIdx.x;
     const float* a = src + (size_t)idx[j] * K;

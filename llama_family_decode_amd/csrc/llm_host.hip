@@ -114,6 +114,10 @@ int validate(const llm_config* c, const llm_tensor* ts, int32_t n, Validated& V,
         err = "invalid attention span or temperature";
         return LLM_ERR_ARG;
     }
+    if (c->numerics != 0 && c->numerics != 1) {
+        err = "numerics must be 0 or 1";
+        return LLM_ERR_ARG;
+    }
     if (!(c->yarn_factor == 0.0f ||
           (c->yarn_factor >= 1.0f && c->yarn_factor < INFINITY && c->yarn_orig_ctx > 0 && c->yarn_beta_slow >= 0.0f &&
            c->yarn_beta_fast > c->yarn_beta_slow && c->yarn_beta_fast < INFINITY))) {
@@ -219,6 +223,7 @@ struct Layout {
     float *X, *Hf, *QKV, *Q, *Of, *Uf, *ws;
     __half *Hh, *Hl, *Oh, *Ol, *Uh, *Ul;  // binary16 hi/lo planes of Hf, Of, Uf
     float* Xc;                            // the wanted rows' residuals (last prefill layer)
+    float* attn_stats;                    // span max and sum per (row, head) of the rounded passes
     int* sel;                             // prompt rows whose logits are wanted (chunk-relative)
     int* selo;                            // and their output rows
     size_t ws_floats;
@@ -295,7 +300,10 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.ao = (float*)S.take((size_t)qd * 4);
     L.u = (float*)S.take((size_t)c->ffn * 4);
     L.logits = (float*)S.take((size_t)c->vocab * 4);
-    L.attn_part = (float*)S.take((size_t)kMaxSplit * c->n_kv_heads * G * (c->head_dim + 2) * 4);
+    // split partials: kMaxSplit splits of one decode query, or one split per
+    // prefill row (the rounded-probability passes write them for every row)
+    L.attn_part = (float*)S.take((size_t)(kMaxSplit > C ? kMaxSplit : C) * c->n_kv_heads * G * (c->head_dim + 2) * 4);
+    L.attn_stats = (float*)S.take((size_t)C * c->n_heads * 2 * 4);
     L.dlayers = (LayerW*)S.take((size_t)c->n_layers * sizeof(LayerW));
     auto pad64 = [](long long n) { return (n + 63) / 64 * 64; };
     L.qkv_stride = pad64(qd + 2 * kvd);
@@ -410,6 +418,7 @@ GemvArgs base_args(llm_ctx* c) {
     a.neox = c->cfg.rope_neox;
     a.n_ctx = c->cfg.n_ctx;
     a.rope = c->L.rope;
+    a.n3 = c->cfg.numerics;
     return a;
 }
 
@@ -465,6 +474,8 @@ hipError_t stage_attn(llm_ctx* c, int l, const float* q, float* out, hipStream_t
     t.n_split = L.n_split;
     t.scale_div = (float)sqrt((double)cf.head_dim);
     t.span = span_cfg(cf);
+    t.n3 = cf.numerics;
+    t.stats = L.attn_stats;
     return launch_attn(t, 1, s);
 }
 
@@ -755,7 +766,10 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
             same = same && w.qkv.dtype == dt && w.o.dtype == dt && w.gu.dtype == dt && w.down.dtype == dt;
         const char* sk = getenv("LLM_STEP");
         const bool want = !(sk && strcmp(sk, "graph") == 0);
-        c->step_grid = want && same ? step_grid(A, dt, &c->step_lds, &c->step_fn, &c->step_special) : 0;
+        // the step kernel computes with float activations only
+        c->step_grid = want && same && cfg->numerics == 0
+                           ? step_grid(A, dt, &c->step_lds, &c->step_fn, &c->step_special)
+                           : 0;
         c->use_step = c->step_grid > 0;
     }
 
@@ -830,6 +844,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
     hipStream_t s = c->stream;
     const int qd = c->qd, kvd = c->kvd, qkvd = qd + 2 * kvd;
     const int nr = (int)rows_out.size();
+    const bool n3 = cf.numerics != 0;  // llama.cpp's rounding of every product input
     // the wanted rows grouped by chunk, output order kept within a chunk:
     // c->sel_out[p] = output index, c->sel_row[p] = prompt row
     c->sel_out.clear();
@@ -860,6 +875,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             __half* kc = L.kc + (size_t)l * L.kv_layer;
             __half* vc = L.vc + (size_t)l * L.kv_layer;
             HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            if (n3) HIPCHK(c, launch_round_rows(L.Hf, m, cf.dim, W.qkv.dtype, L.Hh, L.Hl, s));
             HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, GemmA{L.Hf, L.Hh, L.Hl}, m, L.QKV, qkvd, W.bqkv, nullptr, nullptr,
                                   L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
@@ -881,7 +897,10 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             t.n_split = 1;
             t.scale_div = (float)sqrt((double)cf.head_dim);
             t.span = span_cfg(cf);
-            const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0;
+            t.n3 = cf.numerics;
+            t.stats = L.attn_stats;
+            // the matrix-core kernel computes with float probabilities only
+            const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0 && !cf.numerics;
             if (mfma_attn)
                 HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, L.Oh, L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
                                                    cf.head_dim, cf.n_ctx, t.scale_div, t.span, s));
@@ -899,12 +918,17 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 of = L.Q;
                 X = L.Xc;
             }
-            if (W.o.dtype == DT_F16 && (last || !mfma_attn)) HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
+            if (n3)
+                HIPCHK(c, launch_round_rows((float*)of, mr, qd, W.o.dtype, L.Oh, L.Ol, s));
+            else if (W.o.dtype == DT_F16 && (last || !mfma_attn))
+                HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
             HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, L.Ol}, mr, X, cf.dim, nullptr, nullptr, nullptr,
                                   L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            if (n3) HIPCHK(c, launch_round_rows(L.Hf, mr, cf.dim, W.gu.dtype, L.Hh, L.Hl, s));
             HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, L.Hl}, mr, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
                                   L.ws, L.ws_floats, s));
+            if (n3) HIPCHK(c, launch_round_rows(L.Uf, mr, cf.ffn, W.down.dtype, L.Uh, L.Ul, s));
             HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, L.Ul}, mr, X, cf.dim, nullptr, nullptr,
                                   nullptr, L.ws, L.ws_floats, s));
         }
@@ -913,6 +937,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             // final RMSNorm of the compact rows, then one vocabulary product
             // whose rows land at their output indices
             HIPCHK(c, launch_rmsnorm_rows(L.Xc, L.out_norm, k, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            if (n3) HIPCHK(c, launch_round_rows(L.Hf, k, cf.dim, L.out.dtype, L.Hh, L.Hl, s));
             HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, L.Hl}, k, d_rows, cf.vocab, nullptr, nullptr,
                                   nullptr, L.ws, L.ws_floats, s, L.selo + sb));
         } else if (k > 0) {

@@ -53,6 +53,10 @@ SMALL_SINKS = SMALL_F16.with_(name="small-sinks", attn_window=4, attn_sinks=2, s
 SMALL_TEMP = SMALL.with_(name="small-temp", attn_temp_scale=0.1, attn_temp_len=4, seed=20)
 SMALL_SPAN_ALL = SMALL_NEOX_BIAS.with_(name="small-window-sinks-temp", attn_window=6, attn_sinks=3,
                                       attn_temp_scale=0.5, attn_temp_len=3, seed=21)
+# llama.cpp's rounding points (numerics 1) on each weight type
+SMALL_N3 = SMALL.with_(name="small-f32-llamacpp", numerics=1, seed=23)
+SMALL_F16_N3 = SMALL_F16.with_(name="small-f16-llamacpp", numerics=1, seed=24)
+SMALL_Q8_N3 = SMALL_Q8.with_(name="small-q8_0-llamacpp", numerics=1, seed=25)
 # YaRN with a short original context, so that small heads have fast, ramped and slow pairs
 SMALL_YARN = SMALL.with_(name="small-yarn", yarn_factor=4.0, yarn_orig_ctx=400, rope_base=10000.0, seed=22)
 

@@ -130,6 +130,7 @@ def test_plan_rejects_bad_tensor_sets(case):
     ("attn_temp_scale", float("nan"), -1),
     ("yarn_factor", 0.5, -1),        # YaRN factors start at 1
     ("yarn_factor", 4.0, -1),        # ... and need the original context
+    ("numerics", 2, -1),
 ])
 def test_plan_rejects_bad_configs(field, value, want):
     ts = synth.make_tensor_set(SMALL)

@@ -98,6 +98,16 @@ def test_step_1b_q8_yarn_shape():
     run_decode(cfg, n_prompt=20, n_steps=4)
 
 
+def test_llamacpp_numerics_decode_on_the_launch_graph(monkeypatch):
+    # the persistent kernel computes with float activations only: with
+    # llama.cpp's rounding points the context decodes on the launch graph
+    monkeypatch.setenv("LLM_STEP", "persistent")
+    cfg = synth.C4.with_(n_ctx=160, numerics=1)
+    m = llm.Model(cfg, synth.make_tensor_set(cfg))
+    assert llm.llm_op_step_kind(m.ctx) == 0
+    m.close()
+
+
 def test_step_1b_f16_shape():
     cfg = synth.C3.with_(n_ctx=160)
     load(cfg, kind=2).close()
