@@ -85,7 +85,7 @@ def read_traffic():
     return None
 
 
-def cpu_baseline(cfg, budget_s=20.0):
+def cpu_baseline(cfg, budget_s=15.0):
     """The oracle, untuned, on a bounded sample of the decode workload: a short
     prompt prefill (not timed), then decode steps until the time budget."""
     import numpy as np
@@ -104,7 +104,7 @@ def cpu_baseline(cfg, budget_s=20.0):
         logits = m.forward(tok, pos)
         pos += 1
         n += 1
-        if time.perf_counter() - t0 > budget_s or n >= 64:
+        if time.perf_counter() - t0 > budget_s or n >= 1024:
             break
     dt = time.perf_counter() - t0
     m.close()
