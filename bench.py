@@ -181,7 +181,8 @@ def measure_prefill(llm, synth, np, torch, reps=5):
             "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
             "all_rows_ms": round(rt * 1e3, 3), "all_rows_gemm_tflop": round(rows_flop / 1e12, 4),
             "all_rows_mfma_frac": round(rows_flop / rt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
-            "llamacpp_numerics_ms": round(nt * 1e3, 3), "llamacpp_numerics_tok_s": round(512 / nt, 1)}
+            "llamacpp_numerics_ms": round(nt * 1e3, 3), "llamacpp_numerics_tok_s": round(512 / nt, 1),
+            "llamacpp_numerics_mfma_frac": round(gemm_flop / nt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
 
 
 def measure_decode_report(llm, synth, np, torch, cfg, ctx_len, steps=64, reps=3):

@@ -81,36 +81,35 @@ hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim
     return hipGetLastError();
 }
 
-__global__ void k_round_rows(float* X, int K, int dtype, __half* H, __half* L) {
-    const int row = blockIdx.x;
+// One element per thread; a Q8_0 block of 32 is 32 consecutive lanes, whose
+// maximum magnitude comes from a shuffle reduction within them.
+__global__ __launch_bounds__(256) void k_round_rows(float* X, int K, int dtype, __half* H, __half* L) {
+    const int row = blockIdx.x, i = blockIdx.y * 256 + threadIdx.x;
+    if (i >= K) return;  // K is a multiple of 32: whole 32-lane groups leave together
     float* x = X + (size_t)row * K;
-    for (int b = threadIdx.x; b < K / 32; b += blockDim.x) {
-        float v[32];
+    float v = x[i];
+    if (dtype == DT_Q8) {
+        float amax = fabsf(v);
 #pragma unroll
-        for (int j = 0; j < 32; j++) v[j] = x[32 * b + j];
-        if (dtype == DT_Q8) {
-            q8_round32(v);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 32; j++) v[j] = round16(v[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 32; j++) {
-            x[32 * b + j] = v[j];
-            if (H) {
-                const __half h = __float2half_rn(v[j]);
-                const size_t t = tile_off(row, 32 * b + j, K, kTileA);
-                H[t] = h;
-                L[t] = __float2half_rn(v[j] - __half2float(h));
-            }
-        }
+        for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f;
+        v = round16(d) * roundf(v * id);
+    } else {
+        v = round16(v);
+    }
+    x[i] = v;
+    if (H) {
+        const __half h = __float2half_rn(v);
+        const size_t t = tile_off(row, i, K, kTileA);
+        H[t] = h;
+        L[t] = __float2half_rn(v - __half2float(h));
     }
 }
 
 hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __half* L, hipStream_t s) {
     if (dtype == DT_F32 || n <= 0) return hipSuccess;
     if (K % 32) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_round_rows, dim3(n), dim3(64), 0, s, X, K, dtype, H, L);
+    hipLaunchKernelGGL(k_round_rows, dim3(n, (K + 255) / 256), dim3(256), 0, s, X, K, dtype, H, L);
     return hipGetLastError();
 }
 
@@ -452,7 +451,9 @@ __device__ __forceinline__ int hl_slot(int r, int c) { return 4 * r + (c ^ tile_
 #ifndef LLM_HL_WAVES
 #define LLM_HL_WAVES 8
 #endif
-template <int EPI, int NW>
+// LO = false: the activations are binary16 already (Al holds zeros and its
+// products are skipped).
+template <int EPI, int NW, bool LO>
 __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, const __half* Al, int M, int kz, int nm,
                                                      int nn, float* Y, int ldy, const float* bias, __half* Yh,
                                                      __half* Yl, float* P, const int* ymap) {
@@ -547,8 +548,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
             const char* a = st + (4 * wm + 2 * i) * 1024;
             F.ah[i][0] = *(const half8*)(a + fslot0);
             F.ah[i][1] = *(const half8*)(a + fslot1);
-            F.al[i][0] = *(const half8*)(a + 8192 + fslot0);
-            F.al[i][1] = *(const half8*)(a + 8192 + fslot1);
+            if constexpr (LO) {
+                F.al[i][0] = *(const half8*)(a + 8192 + fslot0);
+                F.al[i][1] = *(const half8*)(a + 8192 + fslot1);
+            }
         }
 #pragma unroll
         for (int j = 0; j < NJ; j++) {
@@ -565,7 +568,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
 #pragma unroll
                 for (int j = 0; j < NJ; j++) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.ah[i][kh], F.bf[j][kh], acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.al[i][kh], F.bf[j][kh], acc[i][j], 0, 0, 0);
+                    if constexpr (LO)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.al[i][kh], F.bf[j][kh], acc[i][j], 0, 0, 0);
                 }
     };
     // Stage s lives in ring slot s % HL_ST. The fragments of step ks are read
@@ -642,9 +646,13 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
     } else if (W.dtype == DT_F16 && W.wt && A.h && K % HL_K == 0) {
         S = gemm_splits(n, N, K, HL_M, HL_N, 8, ws_floats);
         const int nm = (n + HL_M - 1) / HL_M, nn = (N + HL_N - 1) / HL_N;
-        hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES), 0, s, W,
-                           (const __half*)A.h,
-                           (const __half*)A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr, ymap);
+        // without a lo plane the activations are binary16: one product per tile
+        if (A.l)
+            hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES, true>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES), 0, s,
+                               W, A.h, A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr, ymap);
+        else
+            hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES, false>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES), 0, s,
+                               W, A.h, A.h, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr, ymap);
     } else {
         S = gemm_splits(n, N, K, GB_M, GB_N, 4, ws_floats);
         dim3 grid((N + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M, S);
@@ -691,8 +699,14 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // With an attention span (a window plus sinks) each row masks the positions
 // outside its own span, and chunks outside every row's span are skipped; q
 // is scaled by its position's attention temperature before the split.
+// N3 (llama.cpp's rounding points, "What a Llama model computes, and why",
+// section 8): q is rounded to binary16 (one product per score tile), a first
+// pass over the chunks finds each row's span maximum M and sum L, and the
+// second weights V with the probabilities f16(e^(s - M) / L), which are the
+// binary16 operand of the P V product themselves.
 constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72, PA_PLD = 68;
 
+template <bool N3>
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc,
                                                            float* out, __half* out_h, __half* out_l, int n_q, int p0,
                                                            int n_heads, int n_kv_heads, int n_ctx, float scale_div,
@@ -722,7 +736,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         for (int j = 0; j < 8; j++) {
             const _Float16 h = (_Float16)v[j];
             qh[ks][j] = h;
-            ql[ks][j] = (_Float16)(v[j] - (float)h);
+            ql[ks][j] = N3 ? (_Float16)0.f : (_Float16)(v[j] - (float)h);
         }
     }
     // the four rows whose scores and outputs this lane holds: 4*lq + i
@@ -766,8 +780,17 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             vr[u] = ok ? *(const u32x4p*)(vbase + (size_t)t * hd + ld8) : z4;
         }
     };
-    load(chunk_of(0) * PA_CH);
     float* P = Ps[wave];
+    float Mrow[4], Lrow[4];  // N3: each row's span maximum and sum, from the first pass
+    for (int pass = N3 ? 0 : 1; pass < 2; pass++) {
+    if (N3 && pass == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            Mrow[i] = m_run[i];
+            Lrow[i] = l_run[i];
+        }
+    }
+    load(chunk_of(0) * PA_CH);
     for (int v = 0; v < nv; v++) {
         const int c0 = chunk_of(v) * PA_CH;
         __syncthreads();  // the previous chunk's K, V and P reads are done
@@ -791,8 +814,32 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             for (int ks = 0; ks < 2; ks++) {
                 const half8 kf = *(const half8*)(Ks + (16 * pt + lr) * PA_LD + 32 * ks + 8 * lq);
                 sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[ks], kf, sc[pt], 0, 0, 0);
-                sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], kf, sc[pt], 0, 0, 0);
+                if constexpr (!N3) sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], kf, sc[pt], 0, 0, 0);
             }
+        }
+        if (N3 && pass == 1) {
+            // the rounded probabilities of the whole span, the P V operand as is
+#pragma unroll
+            for (int pt = 0; pt < 4; pt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int t = c0 + 16 * pt + lr;
+                    const float e = span_has(span, t, rpos[i]) ? expf(sc[pt][i] / scale_div - Mrow[i]) / Lrow[i] : 0.f;
+                    P[(4 * lq + i) * PA_PLD + 16 * pt + lr] = round16(e);
+                }
+#pragma unroll
+            for (int ps = 0; ps < 2; ps++) {
+                const float4 p0v = *(const float4*)(P + lr * PA_PLD + 32 * ps + 8 * lq);
+                const float4 p1v = *(const float4*)(P + lr * PA_PLD + 32 * ps + 8 * lq + 4);
+                const half8 ph = {(_Float16)p0v.x, (_Float16)p0v.y, (_Float16)p0v.z, (_Float16)p0v.w,
+                                  (_Float16)p1v.x, (_Float16)p1v.y, (_Float16)p1v.z, (_Float16)p1v.w};
+#pragma unroll
+                for (int dt = 0; dt < 4; dt++) {
+                    const half8 vf = *(const half8*)(Vt + (16 * dt + lr) * PA_LD + 32 * ps + 8 * lq);
+                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vf, o[dt], 0, 0, 0);
+                }
+            }
+            continue;
         }
         // online softmax per row; a row's 64 scores sit in the 16 lanes with
         // the same lq, four tiles each
@@ -823,6 +870,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             l_run[i] = l_run[i] * alpha[i] + ls;
             m_run[i] = m_new;
         }
+        if (N3) continue;  // the first pass only finds M and L
 #pragma unroll
         for (int pt = 0; pt < 4; pt++)
 #pragma unroll
@@ -852,6 +900,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             }
         }
     }
+    }
     // out[z][h*64 + d] = o / l for the lane's rows 4 lq + i, dims 16 dt + lr
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -859,7 +908,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         if (z >= n_q) continue;
 #pragma unroll
         for (int dt = 0; dt < 4; dt++) {
-            const float v = o[dt][i] / l_run[i];
+            const float v = N3 ? o[dt][i] : o[dt][i] / l_run[i];
             const int col = h * hd + 16 * dt + lr;
             out[(size_t)z * qd + col] = v;
             const __half hh = __float2half_rn(v);
@@ -872,13 +921,17 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
 
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
-                                    int n_ctx, float scale_div, const SpanCfg& span, hipStream_t s) {
+                                    int n_ctx, float scale_div, const SpanCfg& span, bool n3, hipStream_t s) {
     const int G = n_kv_heads > 0 ? n_heads / n_kv_heads : 0;
     if (head_dim != 64 || G < 1 || G > PA_ROWS || PA_ROWS % G || n_heads % n_kv_heads || n_q <= 0)
         return hipErrorInvalidValue;
     const int TB = PA_ROWS / G;
-    hipLaunchKernelGGL(k_attn_prefill_mfma, dim3((n_q + TB - 1) / TB, n_kv_heads), dim3(256), 0, s, Q, kc, vc, out,
-                       out_h, out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div, span);
+    if (n3)
+        hipLaunchKernelGGL(k_attn_prefill_mfma<true>, dim3((n_q + TB - 1) / TB, n_kv_heads), dim3(256), 0, s, Q, kc, vc,
+                           out, out_h, out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div, span);
+    else
+        hipLaunchKernelGGL(k_attn_prefill_mfma<false>, dim3((n_q + TB - 1) / TB, n_kv_heads), dim3(256), 0, s, Q, kc,
+                           vc, out, out_h, out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div, span);
     return hipGetLastError();
 }
 

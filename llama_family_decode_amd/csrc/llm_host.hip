@@ -845,6 +845,8 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
     const int qd = c->qd, kvd = c->kvd, qkvd = qd + 2 * kvd;
     const int nr = (int)rows_out.size();
     const bool n3 = cf.numerics != 0;  // llama.cpp's rounding of every product input
+    // with rounded inputs an F16 product's lo plane is zero: one matrix-core pass
+    auto lo = [n3](const __half* l) { return n3 ? nullptr : l; };
     // the wanted rows grouped by chunk, output order kept within a chunk:
     // c->sel_out[p] = output index, c->sel_row[p] = prompt row
     c->sel_out.clear();
@@ -876,8 +878,8 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             __half* vc = L.vc + (size_t)l * L.kv_layer;
             HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
             if (n3) HIPCHK(c, launch_round_rows(L.Hf, m, cf.dim, W.qkv.dtype, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, GemmA{L.Hf, L.Hh, L.Hl}, m, L.QKV, qkvd, W.bqkv, nullptr, nullptr,
-                                  L.ws, L.ws_floats, s));
+            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, GemmA{L.Hf, L.Hh, lo(L.Hl)}, m, L.QKV, qkvd, W.bqkv, nullptr,
+                                  nullptr, L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
                                           cf.rope_neox, cf.n_ctx, L.rope, L.Q, kc, vc, s));
             AttnArgs t;
@@ -899,11 +901,10 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             t.span = span_cfg(cf);
             t.n3 = cf.numerics;
             t.stats = L.attn_stats;
-            // the matrix-core kernel computes with float probabilities only
-            const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0 && !cf.numerics;
+            const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0;
             if (mfma_attn)
                 HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, L.Oh, L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
-                                                   cf.head_dim, cf.n_ctx, t.scale_div, t.span, s));
+                                                   cf.head_dim, cf.n_ctx, t.scale_div, t.span, n3, s));
             else
                 HIPCHK(c, launch_attn(t, m, s));
             int mr = m;
@@ -922,14 +923,14 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 HIPCHK(c, launch_round_rows((float*)of, mr, qd, W.o.dtype, L.Oh, L.Ol, s));
             else if (W.o.dtype == DT_F16 && (last || !mfma_attn))
                 HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
-            HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, L.Ol}, mr, X, cf.dim, nullptr, nullptr, nullptr,
+            HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, lo(L.Ol)}, mr, X, cf.dim, nullptr, nullptr, nullptr,
                                   L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
             if (n3) HIPCHK(c, launch_round_rows(L.Hf, mr, cf.dim, W.gu.dtype, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, L.Hl}, mr, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
+            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, lo(L.Hl)}, mr, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
                                   L.ws, L.ws_floats, s));
             if (n3) HIPCHK(c, launch_round_rows(L.Uf, mr, cf.ffn, W.down.dtype, L.Uh, L.Ul, s));
-            HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, L.Ul}, mr, X, cf.dim, nullptr, nullptr,
+            HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, lo(L.Ul)}, mr, X, cf.dim, nullptr, nullptr,
                                   nullptr, L.ws, L.ws_floats, s));
         }
         c->len += m;
@@ -938,7 +939,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             // whose rows land at their output indices
             HIPCHK(c, launch_rmsnorm_rows(L.Xc, L.out_norm, k, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
             if (n3) HIPCHK(c, launch_round_rows(L.Hf, k, cf.dim, L.out.dtype, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, L.Hl}, k, d_rows, cf.vocab, nullptr, nullptr,
+            HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, lo(L.Hl)}, k, d_rows, cf.vocab, nullptr, nullptr,
                                   nullptr, L.ws, L.ws_floats, s, L.selo + sb));
         } else if (k > 0) {
             HIPCHK(c, launch_set_state(L.st, 0, c->len - 1, 0, s));
