@@ -276,9 +276,15 @@ struct GemmA {
 // F32 on the vector ALUs. SwiGLU also writes its output's hi/lo planes when
 // Yh is set. ws (ws_floats floats) holds split-K partials. A plain store may
 // scatter its rows: with ymap (device, n entries) row m goes to Y row ymap[m].
+// A residual product with defer set leaves a split-K product's S partials in
+// ws for the caller (*defer = S; 0 when it wrote Y itself).
 hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
                        __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s,
-                       const int* ymap = nullptr);
+                       const int* ymap = nullptr, int* defer = nullptr);
+// X[m] += the S split-K partials of ws (z order), then Y = rmsnorm(X[m]) * gain
+// as launch_rmsnorm_rows computes it.
+hipError_t launch_reduce_norm_rows(const float* P, int S, int n, float* X, int dim, const float* gain, float eps,
+                                   float* Yf, __half* Yh, __half* Yl, hipStream_t s);
 hipError_t launch_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int n_kv_heads, int head_dim, int n_rot,
                                int neox, int n_ctx, const float2* rope, float* Q, __half* kc, __half* vc,
                                hipStream_t s);

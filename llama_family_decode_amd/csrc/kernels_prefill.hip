@@ -50,34 +50,113 @@ hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, i
 // ------------------------------------------------------------ RMSNorm rows
 // y = (x * scale) * g with scale = (float)(1 / sqrt(sum(x^2)/n + eps)), the sum in
 // double ("The Forward Pass in Java", Example 4).
+// Block-wide sum of one double per thread (256 threads).
+__device__ __forceinline__ double rows_sum256(double v, double* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+
+// y = x * scale * g for the 8 values of x at column i0 of `row` (i0 % 8 == 0):
+// the fp32 row and, when Yh is set, the tiled hi/lo planes, one 16-byte slot
+// each (the tiled layout keeps 8 consecutive columns of a row together).
+__device__ __forceinline__ void norm_store8(const float (&x)[8], float scale, const float* gain, int row, int i0,
+                                           int dim, float* Yf, __half* Yh, __half* Yl) {
+    const float4 g0 = *(const float4*)(gain + i0), g1 = *(const float4*)(gain + i0 + 4);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) y[e] = x[e] * scale * g[e];
+    float* yf = Yf + (size_t)row * dim + i0;
+    *(float4*)yf = make_float4(y[0], y[1], y[2], y[3]);
+    *(float4*)(yf + 4) = make_float4(y[4], y[5], y[6], y[7]);
+    if (Yh) {
+        __half h[8], l[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            h[e] = __float2half_rn(y[e]);
+            l[e] = __float2half_rn(y[e] - __half2float(h[e]));
+        }
+        const size_t t = tile_off(row, i0, dim, kTileA);
+        *(uint4*)(Yh + t) = *(const uint4*)h;
+        *(uint4*)(Yl + t) = *(const uint4*)l;
+    }
+}
+
+// Y = rmsnorm(X) * gain per row ("The Forward Pass in Java", Example 4): the
+// sum of squares in double, the scale 1/sqrt(ss/dim + eps) rounded to float
+// once, y = (x * scale) * g. One block of 256 threads per row, 8 columns per
+// thread and step.
 __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const float* gain, int dim, float eps, float* Yf,
                                                       __half* Yh, __half* Yl) {
     __shared__ double red[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     const float* x = X + (size_t)row * dim;
     double ss = 0.0;
-    for (int i = tid; i < dim; i += 256) ss += (double)x[i] * (double)x[i];
+    for (int i0 = 8 * tid; i0 < dim; i0 += 8 * 256) {
+        const float4 a = *(const float4*)(x + i0), b = *(const float4*)(x + i0 + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
-    __syncthreads();
-    const double tot = red[0] + red[1] + red[2] + red[3];
+        for (int e = 0; e < 8; e++) ss += (double)v[e] * (double)v[e];
+    }
+    const double tot = rows_sum256(ss, red);
     const float scale = (float)(1.0 / sqrt(tot / (double)dim + (double)eps));
-    for (int i = tid; i < dim; i += 256) {
-        const float y = x[i] * scale * gain[i];
-        Yf[(size_t)row * dim + i] = y;
-        if (Yh) {
-            const __half h = __float2half_rn(y);
-            const size_t t = tile_off(row, i, dim, kTileA);
-            Yh[t] = h;
-            Yl[t] = __float2half_rn(y - __half2float(h));
-        }
+    for (int i0 = 8 * tid; i0 < dim; i0 += 8 * 256) {
+        const float4 a = *(const float4*)(x + i0), b = *(const float4*)(x + i0 + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        norm_store8(v, scale, gain, row, i0, dim, Yf, Yh, Yl);
     }
 }
 
 hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
                                __half* Yl, hipStream_t s) {
+    if (dim % 8) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_rmsnorm_rows, dim3(n), dim3(256), 0, s, X, gain, dim, eps, Yf, Yh, Yl);
+    return hipGetLastError();
+}
+
+// The split-K reduction of a residual product fused with the next RMSNorm:
+// X[m] += sum of the S partials P[z][m] in z order (as k_splitk_reduce adds
+// them), then Y = rmsnorm(X[m]) * gain as k_rmsnorm_rows computes it.
+__global__ __launch_bounds__(256) void k_reduce_norm_rows(const float* P, int S, int M, float* X, int dim,
+                                                          const float* gain, float eps, float* Yf, __half* Yh,
+                                                          __half* Yl) {
+    __shared__ double red[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    float* x = X + (size_t)row * dim;
+    const size_t MN = (size_t)M * dim;
+    double ss = 0.0;
+    for (int i0 = 8 * tid; i0 < dim; i0 += 8 * 256) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int z = 0; z < S; z++) {
+            const float* pz = P + z * MN + (size_t)row * dim + i0;
+            const float4 a = *(const float4*)pz, b = *(const float4*)(pz + 4);
+            acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+            acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+        }
+        const float4 a = *(const float4*)(x + i0), b = *(const float4*)(x + i0 + 4);
+        const float v[8] = {a.x + acc[0], a.y + acc[1], a.z + acc[2], a.w + acc[3],
+                            b.x + acc[4], b.y + acc[5], b.z + acc[6], b.w + acc[7]};
+        *(float4*)(x + i0) = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4*)(x + i0 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+        for (int e = 0; e < 8; e++) ss += (double)v[e] * (double)v[e];
+    }
+    const double tot = rows_sum256(ss, red);
+    const float scale = (float)(1.0 / sqrt(tot / (double)dim + (double)eps));
+    for (int i0 = 8 * tid; i0 < dim; i0 += 8 * 256) {  // this thread's own columns, written above
+        const float4 a = *(const float4*)(x + i0), b = *(const float4*)(x + i0 + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        norm_store8(v, scale, gain, row, i0, dim, Yf, Yh, Yl);
+    }
+}
+
+hipError_t launch_reduce_norm_rows(const float* P, int S, int n, float* X, int dim, const float* gain, float eps,
+                                   float* Yf, __half* Yh, __half* Yl, hipStream_t s) {
+    if (dim % 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_reduce_norm_rows, dim3(n), dim3(256), 0, s, P, S, n, X, dim, gain, eps, Yf, Yh, Yl);
     return hipGetLastError();
 }
 
@@ -637,7 +716,8 @@ static int gemm_splits(int M, int N, int K, int tm, int tn, int smax, size_t ws_
 
 template <int EPI>
 static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias, __half* Yh,
-                           __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap) {
+                           __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap, int* defer) {
+    if (defer) *defer = 0;
     const int N = W.rows, K = W.cols;
     int S = 1;
     if (W.dtype == DT_F32) {
@@ -666,6 +746,10 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
+    if (defer) {  // the caller reduces the S partials in ws itself
+        *defer = S;
+        return hipSuccess;
+    }
     const size_t items = EPI == EPI_SWIGLU ? (size_t)n * N / 2 : (size_t)n * N;
     hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, ws, S, n, N, Y,
                        ldy, bias, Yh, Yl, ymap);
@@ -673,12 +757,13 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
 }
 
 hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
-                       __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap) {
-    if (ymap && epi != EPI_STORE) return hipErrorInvalidValue;
+                       __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap,
+                       int* defer) {
+    if ((ymap && epi != EPI_STORE) || (defer && epi != EPI_RESID)) return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap);
-        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap);
-        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap);
+        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer);
+        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer);
+        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer);
     }
     return hipErrorInvalidValue;
 }

@@ -871,12 +871,14 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
         const int sb = chunk_begin[ci], k = chunk_begin[ci + 1] - sb;  // wanted rows of this chunk
         HIPCHK(c, hipMemcpyAsync(L.ptok, h_tokens + done, (size_t)m * 4, hipMemcpyHostToDevice, s));
         HIPCHK(c, launch_embed_rows(L.embd, L.ptok, m, L.X, cf.dim, s));
+        bool normed = false;  // Hf/Hh/Hl already hold this layer's attention-norm rows
         for (int l = 0; l < cf.n_layers; l++) {
             const LayerW& W = L.layers[l];
             const bool last = l == cf.n_layers - 1;
             __half* kc = L.kc + (size_t)l * L.kv_layer;
             __half* vc = L.vc + (size_t)l * L.kv_layer;
-            HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            if (!normed) HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            normed = false;
             if (n3) HIPCHK(c, launch_round_rows(L.Hf, m, cf.dim, W.qkv.dtype, L.Hh, L.Hl, s));
             HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, GemmA{L.Hf, L.Hh, lo(L.Hl)}, m, L.QKV, qkvd, W.bqkv, nullptr,
                                   nullptr, L.ws, L.ws_floats, s));
@@ -923,15 +925,28 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 HIPCHK(c, launch_round_rows((float*)of, mr, qd, W.o.dtype, L.Oh, L.Ol, s));
             else if (W.o.dtype == DT_F16 && (last || !mfma_attn))
                 HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
+            // output product + residual; a split-K product's reduction is fused
+            // with the FFN norm that follows
+            int S = 0;
             HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, lo(L.Ol)}, mr, X, cf.dim, nullptr, nullptr, nullptr,
-                                  L.ws, L.ws_floats, s));
-            HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+                                  L.ws, L.ws_floats, s, nullptr, &S));
+            if (S)
+                HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, W.ffn_norm, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            else
+                HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
             if (n3) HIPCHK(c, launch_round_rows(L.Hf, mr, cf.dim, W.gu.dtype, L.Hh, L.Hl, s));
             HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, lo(L.Hl)}, mr, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
                                   L.ws, L.ws_floats, s));
             if (n3) HIPCHK(c, launch_round_rows(L.Uf, mr, cf.ffn, W.down.dtype, L.Uh, L.Ul, s));
+            // down product + residual; before another layer a split-K
+            // reduction is fused with that layer's attention norm
             HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, lo(L.Ul)}, mr, X, cf.dim, nullptr, nullptr,
-                                  nullptr, L.ws, L.ws_floats, s));
+                                  nullptr, L.ws, L.ws_floats, s, nullptr, last ? nullptr : &S));
+            if (!last && S) {
+                HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, L.layers[l + 1].attn_norm, cf.eps, L.Hf,
+                                                  L.Hh, L.Hl, s));
+                normed = true;
+            }
         }
         c->len += m;
         if (k > 0 && d_rows) {
