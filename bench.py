@@ -267,6 +267,18 @@ def main():
     nxt = model.prefill(prompt)
     torch.cuda.synchronize()
     print(f"# loaded + prefilled {ctx_len} in {time.perf_counter() - t_load:.1f}s", file=sys.stderr, flush=True)
+    # the workload's own prompt pass (Q8_0 products on the matrix cores), median of 3
+    q8_times = []
+    for _ in range(3):
+        model.reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        nxt = model.prefill(prompt)
+        torch.cuda.synchronize()
+        q8_times.append(time.perf_counter() - t0)
+    q8_prefill = float(np.median(q8_times))
+    print(f"# prefill {ctx_len} (Q8_0): {q8_prefill * 1e3:.2f} ms, {ctx_len / q8_prefill:.0f} tok/s", file=sys.stderr,
+          flush=True)
 
     # warmup (then rewind to the prefilled length)
     if args.warmup > 0:
@@ -348,6 +360,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
                      "bytes_per_launch": step_bytes, "ms_per_launch": round(ms_step, 5), "position": mid_pos},
         "prefill": prefill,
+        "prefill_q8_0_2048": {"config": cfg.name, "tokens": ctx_len, "ms": round(q8_prefill * 1e3, 3),
+                              "tok_s": round(ctx_len / q8_prefill, 1)},
         "decode_reports": reports,
         "cpu_baseline": cpu,
     }

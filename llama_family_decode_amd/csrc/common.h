@@ -18,7 +18,8 @@ struct Mat {
     int rows, cols;
     const void* w;
     const uint16_t* s;
-    const void* wt;  // F16 only: the prefill products' tiled copy (or nullptr)
+    const void* wt;  // the prefill products' tiled binary16 copy (Q8_0: of the codes), or nullptr
+    const void* st;  // Q8_0 with wt: the block scales, [256-row tile][K step][256] binary16
 };
 
 // Tiled binary16 layout of the prefill products' operands: rows in tiles of
@@ -35,6 +36,9 @@ __host__ __device__ inline size_t tile_off(int m, int k, int K, int TM) {
     return (((size_t)t * nk + ks) * (TM >> 4) + g) * 512 + (size_t)(4 * r + (c ^ tile_swz(r))) * 8 + e;
 }
 inline size_t tiled_w_bytes(int rows, int cols) { return (size_t)((rows + kTileW - 1) / kTileW) * kTileW * cols * 2; }
+inline size_t tiled_s_bytes(int rows, int cols) {
+    return (size_t)((rows + kTileW - 1) / kTileW) * kTileW * (cols / 32) * 2;
+}
 
 // Attention span and temperature of the config: the query at position p
 // attends rows p-window+1..p plus rows 0..sinks-1 (window 0: rows 0..p), with
@@ -256,7 +260,8 @@ hipError_t launch_split_hl(const float* X, int n, int K, __half* H, __half* L, h
 // place; H, L (if set) get the rounded rows' tiled hi/lo planes.
 hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __half* L, hipStream_t s);
 // The tiled copy of an F16 matrix (rows padded with zeros to a multiple of 256).
-hipError_t launch_tile_w(const Mat& W, void* dst, hipStream_t s);
+// Fills W.wt (and for Q8_0 W.st) from W's stored rows.
+hipError_t launch_tile_w(const Mat& W, hipStream_t s);
 // Causal prefill attention of n_q queries at positions p0 .. p0+n_q-1 on the
 // matrix cores (head_dim 64 only; hipErrorInvalidValue otherwise): out as
 // fp32 rows [n_q][n_heads*64] and their tiled binary16 hi/lo planes.

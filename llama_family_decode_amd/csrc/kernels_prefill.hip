@@ -234,12 +234,44 @@ __global__ void k_tile_w(const __half* W, int rows, int cols, int rows_pad, __ha
     *(uint4*)(T + tile_off(n, k, cols, kTileW)) = v;
 }
 
-hipError_t launch_tile_w(const Mat& W, void* dst, hipStream_t s) {
-    if (W.dtype != DT_F16 || W.cols % 32) return hipErrorInvalidValue;
+// The same for Q8_0 codes (int8 rows; |code| <= 127 is exact in binary16).
+__global__ void k_tile_q8(const int8_t* W, int rows, int cols, int rows_pad, __half* T) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int cpr = cols >> 3;
+    if (i >= (size_t)rows_pad * cpr) return;
+    const int n = (int)(i / cpr), k = (int)(i % cpr) * 8;
+    __half h[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) h[e] = __float2half_rn(n < rows ? (float)W[(size_t)n * cols + k + e] : 0.f);
+    *(uint4*)(T + tile_off(n, k, cols, kTileW)) = *(const uint4*)h;
+}
+
+// Q8_0 block scales ([rows][cols/32] binary16 bits) as [tile][K step][256]:
+// the 256 scales a product tile needs for one 32-deep step are contiguous.
+__global__ void k_tile_scales(const uint16_t* S, int rows, int nkb, int rows_pad, uint16_t* T) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)rows_pad * nkb) return;
+    const int n = (int)(i % rows_pad), kb = (int)(i / rows_pad);
+    const int t = n / kTileW, r = n % kTileW;
+    T[((size_t)t * nkb + kb) * kTileW + r] = n < rows ? S[(size_t)n * nkb + kb] : (uint16_t)0;
+}
+
+hipError_t launch_tile_w(const Mat& W, hipStream_t s) {
+    if ((W.dtype != DT_F16 && W.dtype != DT_Q8) || W.cols % 32 || !W.wt) return hipErrorInvalidValue;
     const int rows_pad = (W.rows + kTileW - 1) / kTileW * kTileW;
     const size_t total = (size_t)rows_pad * (W.cols / 8);
-    hipLaunchKernelGGL(k_tile_w, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, (const __half*)W.w, W.rows,
-                       W.cols, rows_pad, (__half*)dst);
+    const unsigned grid = (unsigned)((total + 255) / 256);
+    if (W.dtype == DT_F16) {
+        hipLaunchKernelGGL(k_tile_w, dim3(grid), dim3(256), 0, s, (const __half*)W.w, W.rows, W.cols, rows_pad,
+                           (__half*)W.wt);
+        return hipGetLastError();
+    }
+    if (!W.st) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_tile_q8, dim3(grid), dim3(256), 0, s, (const int8_t*)W.w, W.rows, W.cols, rows_pad,
+                       (__half*)W.wt);
+    const size_t ns = (size_t)rows_pad * (W.cols / 32);
+    hipLaunchKernelGGL(k_tile_scales, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s, W.s, W.rows, W.cols / 32,
+                       rows_pad, (uint16_t*)W.st);
     return hipGetLastError();
 }
 
@@ -531,8 +563,10 @@ __device__ __forceinline__ int hl_slot(int r, int c) { return 4 * r + (c ^ tile_
 #define LLM_HL_WAVES 8
 #endif
 // LO = false: the activations are binary16 already (Al holds zeros and its
-// products are skipped).
-template <int EPI, int NW, bool LO>
+// products are skipped). Q8: W's tiled copy holds Q8_0 codes; each 32-deep
+// step (one Q8_0 block) is multiplied into a fresh accumulator that joins the
+// sum scaled by its weight row's block scale, staged with the step.
+template <int EPI, int NW, bool LO, bool Q8>
 __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, const __half* Al, int M, int kz, int nm,
                                                      int nn, float* Y, int ldy, const float* bias, __half* Yh,
                                                      __half* Yl, float* P, const int* ymap) {
@@ -540,7 +574,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
     // 2 x NJ tiles of the 32x32x16 instruction (on gfx950 it moves twice the
     // operands per cycle of the 16x16x32 one)
     constexpr int WN = NW / 2, NJ = HL_N / WN / 32, ND = 32 / NW;
-    __shared__ __attribute__((aligned(1024))) char lds[HL_ST * HL_STAGE];
+    // a Q8_0 stage also holds the tile's 256 block scales (wave w moves rows
+    // 32w .. 32w+31 with a fifth, four-lane DMA)
+    constexpr int STAGE = Q8 ? HL_STAGE + 1024 : HL_STAGE;
+    static_assert(!Q8 || NW == 8, "each of 8 waves stages 32 scales");
+    __shared__ __attribute__((aligned(1024))) char lds[HL_ST * STAGE];
     const int N = W.rows, K = W.cols;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // tiles that share a weight tile are dealt to one XCD (block b runs on
@@ -557,10 +595,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
     // in the tiled layout each is one contiguous 1 KB piece, lane l's 16 bytes
     // at 16 l, already in LDS slot order
     const __half* src[ND];
+    const uint16_t* ssrc = nullptr;
     // a K step advances 8 (A) or 16 (W) pieces; a wave's groups are all of one kind
     const size_t kstep = wave * ND < 16 ? 8 * 512 : 16 * 512;
     {
         const int nkK = K / HL_K, kbs = kb / HL_K;
+        if constexpr (Q8) ssrc = (const uint16_t*)W.st + ((size_t)nt * nkK + kbs) * HL_N + wave * 32 + (lane & 3) * 8;
 #pragma unroll
         for (int i = 0; i < ND; i++) {
             const int grp = wave * ND + i;
@@ -572,11 +612,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
     }
     const int nk = kz / HL_K;
     auto issue = [&](int ks) {
-        char* dst = lds + (ks % HL_ST) * HL_STAGE + wave * ND * 1024;
+        char* dst = lds + (ks % HL_ST) * STAGE + wave * ND * 1024;
 #pragma unroll
         for (int i = 0; i < ND; i++)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[i] + kstep * ks),
                                              (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+        if constexpr (Q8) {
+            if (lane < 4)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(ssrc + (size_t)HL_N * ks),
+                    (__attribute__((address_space(3))) void*)(lds + (ks % HL_ST) * STAGE + HL_STAGE + wave * 64), 16, 0,
+                    0);
+        }
     };
 
     // For 32x32x16 lane l supplies A[l%32][8*(l/32) + j] and B[8*(l/32) + j][l%32]
@@ -600,16 +647,22 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
     auto wait_bar = [&](int pend) {
         // s_waitcnt immediates (vmcnt n, lgkmcnt 0, expcnt unconstrained); as
         // builtins the compiler's own wait bookkeeping sees them
-        const int n = pend * ND;
+        const int n = pend * (Q8 ? ND + 1 : ND);
         asm volatile("" ::: "memory");
         if (n >= 24)
             __builtin_amdgcn_s_waitcnt(0x4078);
         else if (n >= 16)
             __builtin_amdgcn_s_waitcnt(0x4070);
+        else if (n >= 15)
+            __builtin_amdgcn_s_waitcnt(0x007F);
         else if (n >= 12)
             __builtin_amdgcn_s_waitcnt(0x007C);
+        else if (n >= 10)
+            __builtin_amdgcn_s_waitcnt(0x007A);
         else if (n >= 8)
             __builtin_amdgcn_s_waitcnt(0x0078);
+        else if (n >= 5)
+            __builtin_amdgcn_s_waitcnt(0x0075);
         else if (n >= 4)
             __builtin_amdgcn_s_waitcnt(0x0074);
         else
@@ -619,9 +672,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
     };
     struct Frag {
         half8 ah[2][2], al[2][2], bf[NJ][2];  // [tile][K half]
+        float sc[NJ];                         // Q8: the block scales of this lane's columns
     };
     auto fread = [&](int ks, Frag& F) {
-        const char* st = lds + (ks % HL_ST) * HL_STAGE;
+        const char* st = lds + (ks % HL_ST) * STAGE;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             const char* a = st + (4 * wm + 2 * i) * 1024;
@@ -637,9 +691,32 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
             const char* b = st + 16384 + (2 * NJ * wn + 2 * j) * 1024;
             F.bf[j][0] = *(const half8*)(b + fslot0);
             F.bf[j][1] = *(const half8*)(b + fslot1);
+            if constexpr (Q8)
+                F.sc[j] = __half2float(*(const __half*)(st + HL_STAGE + 2 * (32 * NJ * wn + 32 * j + (lane & 31))));
         }
     };
     auto fmma = [&](const Frag& F) {
+        if constexpr (Q8) {
+            float16v t[2][NJ];
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < NJ; j++) {
+                    t[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.ah[i][0], F.bf[j][0], (float16v){}, 0, 0, 0);
+                    if constexpr (LO)
+                        t[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.al[i][0], F.bf[j][0], t[i][j], 0, 0, 0);
+                    t[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.ah[i][1], F.bf[j][1], t[i][j], 0, 0, 0);
+                    if constexpr (LO)
+                        t[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.al[i][1], F.bf[j][1], t[i][j], 0, 0, 0);
+                }
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < NJ; j++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) acc[i][j][e] += F.sc[j] * t[i][j][e];
+            return;
+        }
 #pragma unroll
         for (int kh = 0; kh < 2; kh++)
 #pragma unroll
@@ -723,16 +800,25 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
     if (W.dtype == DT_F32) {
         dim3 grid((N + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
         hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl, ymap);
-    } else if (W.dtype == DT_F16 && W.wt && A.h && K % HL_K == 0) {
+    } else if ((W.dtype == DT_F16 || (W.dtype == DT_Q8 && W.st)) && W.wt && A.h && K % HL_K == 0) {
         S = gemm_splits(n, N, K, HL_M, HL_N, 8, ws_floats);
         const int nm = (n + HL_M - 1) / HL_M, nn = (N + HL_N - 1) / HL_N;
+        float* Pw = S > 1 ? ws : nullptr;
         // without a lo plane the activations are binary16: one product per tile
-        if (A.l)
-            hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES, true>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES), 0, s,
-                               W, A.h, A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr, ymap);
-        else
-            hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES, false>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES), 0, s,
-                               W, A.h, A.h, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr, ymap);
+        if (W.dtype == DT_Q8) {
+            if (A.l)
+                hipLaunchKernelGGL((k_gemm_hl<EPI, 8, true, true>), dim3(nm * nn, S), dim3(512), 0, s, W, A.h, A.l, n,
+                                   K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap);
+            else
+                hipLaunchKernelGGL((k_gemm_hl<EPI, 8, false, true>), dim3(nm * nn, S), dim3(512), 0, s, W, A.h, A.h, n,
+                                   K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap);
+        } else if (A.l) {
+            hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES, true, false>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES), 0,
+                               s, W, A.h, A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap);
+        } else {
+            hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES, false, false>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES),
+                               0, s, W, A.h, A.h, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap);
+        }
     } else {
         S = gemm_splits(n, N, K, GB_M, GB_N, 4, ws_floats);
         dim3 grid((N + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M, S);

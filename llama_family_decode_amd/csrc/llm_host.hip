@@ -239,12 +239,15 @@ Mat place_mat(Arena& A, int dtype, int rows, int cols) {
     m.w = A.take(mat_bytes_w(dtype, rows, cols));
     m.s = dtype == DT_Q8 ? (const uint16_t*)A.take(mat_bytes_s(dtype, rows, cols)) : nullptr;
     m.wt = nullptr;
+    m.st = nullptr;
     return m;
 }
 
 // Layer matrices in F16 also get the tiled copy the prefill products read.
+// Q8_0 ones get binary16 codes (exact) plus their block scales per K step.
 void place_tiled(Arena& A, Mat& m) {
-    if (m.dtype == DT_F16 && m.cols % 32 == 0) m.wt = A.take(tiled_w_bytes(m.rows, m.cols));
+    if ((m.dtype == DT_F16 || m.dtype == DT_Q8) && m.cols % 32 == 0) m.wt = A.take(tiled_w_bytes(m.rows, m.cols));
+    if (m.dtype == DT_Q8 && m.wt) m.st = A.take(tiled_s_bytes(m.rows, m.cols));
 }
 
 int decode_splits(const llm_config* c) {
@@ -697,9 +700,9 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
     for (int l = 0; ok && l < cfg->n_layers; l++) {
         const LayerW& D = L.layers[l];
         for (const Mat* m : {&D.qkv, &D.o, &D.gu, &D.down})
-            if (m->wt) ok = ok && launch_tile_w(*m, (void*)m->wt, s) == hipSuccess;
+            if (m->wt) ok = ok && launch_tile_w(*m, s) == hipSuccess;
     }
-    if (ok && L.out.wt) ok = launch_tile_w(L.out, (void*)L.out.wt, s) == hipSuccess;
+    if (ok && L.out.wt) ok = launch_tile_w(L.out, s) == hipSuccess;
     if (!ok) return bail(LLM_ERR_DEVICE, "weight upload failed");
 
     // ---- RoPE table and zeroed state
@@ -846,7 +849,8 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
     const int nr = (int)rows_out.size();
     const bool n3 = cf.numerics != 0;  // llama.cpp's rounding of every product input
     // with rounded inputs an F16 product's lo plane is zero: one matrix-core pass
-    auto lo = [n3](const __half* l) { return n3 ? nullptr : l; };
+    // (a rounded Q8_0 input, f16(d) * code, still needs both planes)
+    auto lo = [n3](const Mat& w, const __half* l) { return n3 && w.dtype == DT_F16 ? nullptr : l; };
     // the wanted rows grouped by chunk, output order kept within a chunk:
     // c->sel_out[p] = output index, c->sel_row[p] = prompt row
     c->sel_out.clear();
@@ -880,7 +884,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             if (!normed) HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
             normed = false;
             if (n3) HIPCHK(c, launch_round_rows(L.Hf, m, cf.dim, W.qkv.dtype, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, GemmA{L.Hf, L.Hh, lo(L.Hl)}, m, L.QKV, qkvd, W.bqkv, nullptr,
+            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, GemmA{L.Hf, L.Hh, lo(W.qkv, L.Hl)}, m, L.QKV, qkvd, W.bqkv, nullptr,
                                   nullptr, L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
                                           cf.rope_neox, cf.n_ctx, L.rope, L.Q, kc, vc, s));
@@ -923,24 +927,24 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             }
             if (n3)
                 HIPCHK(c, launch_round_rows((float*)of, mr, qd, W.o.dtype, L.Oh, L.Ol, s));
-            else if (W.o.dtype == DT_F16 && (last || !mfma_attn))
+            else if (W.o.wt && (last || !mfma_attn))  // the planes the tiled product reads
                 HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
             // output product + residual; a split-K product's reduction is fused
             // with the FFN norm that follows
             int S = 0;
-            HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, lo(L.Ol)}, mr, X, cf.dim, nullptr, nullptr, nullptr,
+            HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, lo(W.o, L.Ol)}, mr, X, cf.dim, nullptr, nullptr, nullptr,
                                   L.ws, L.ws_floats, s, nullptr, &S));
             if (S)
                 HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, W.ffn_norm, cf.eps, L.Hf, L.Hh, L.Hl, s));
             else
                 HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
             if (n3) HIPCHK(c, launch_round_rows(L.Hf, mr, cf.dim, W.gu.dtype, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, lo(L.Hl)}, mr, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
+            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, lo(W.gu, L.Hl)}, mr, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
                                   L.ws, L.ws_floats, s));
             if (n3) HIPCHK(c, launch_round_rows(L.Uf, mr, cf.ffn, W.down.dtype, L.Uh, L.Ul, s));
             // down product + residual; before another layer a split-K
             // reduction is fused with that layer's attention norm
-            HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, lo(L.Ul)}, mr, X, cf.dim, nullptr, nullptr,
+            HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, lo(W.down, L.Ul)}, mr, X, cf.dim, nullptr, nullptr,
                                   nullptr, L.ws, L.ws_floats, s, nullptr, last ? nullptr : &S));
             if (!last && S) {
                 HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, L.layers[l + 1].attn_norm, cf.eps, L.Hf,
@@ -954,7 +958,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             // whose rows land at their output indices
             HIPCHK(c, launch_rmsnorm_rows(L.Xc, L.out_norm, k, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
             if (n3) HIPCHK(c, launch_round_rows(L.Hf, k, cf.dim, L.out.dtype, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, lo(L.Hl)}, k, d_rows, cf.vocab, nullptr, nullptr,
+            HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, lo(L.out, L.Hl)}, k, d_rows, cf.vocab, nullptr, nullptr,
                                   nullptr, L.ws, L.ws_floats, s, L.selo + sb));
         } else if (k > 0) {
             HIPCHK(c, launch_set_state(L.st, 0, c->len - 1, 0, s));

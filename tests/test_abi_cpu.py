@@ -52,6 +52,15 @@ def plan_rc(cfg, ts, config=None):
     return llm.lib().llm_plan(ctypes.byref(c), arr, len(ts), ctypes.byref(w), ctypes.byref(k), ctypes.byref(s))
 
 
+def tiled_bytes(cfg, q8):
+    """The prefill products' tiled binary16 copies of the layer matrices (rows
+    padded to 256), plus, for Q8_0, their block scales."""
+    pad = lambda r: (r + 255) // 256 * 256
+    mats = [(cfg.q_dim + 2 * cfg.kv_dim, cfg.dim), (cfg.dim, cfg.q_dim), (2 * cfg.ffn, cfg.dim), (cfg.dim, cfg.ffn)]
+    per = sum(pad(r) * c * 2 + (pad(r) * (c // 32) * 2 if q8 else 0) for r, c in mats)
+    return cfg.n_layers * per
+
+
 def test_plan_sizes():
     ts = synth.make_tensor_set(SMALL)
     w, k, s = plan(SMALL, ts)
@@ -59,10 +68,10 @@ def test_plan_sizes():
     assert k >= 2 * SMALL.n_layers * SMALL.n_ctx * kvd * 2
     raw = sum(t.nbytes for t in ts)
     assert raw <= w <= raw + 64 * 1024  # packing adds only alignment
-    # Q8_0 packing keeps every byte: 34 per 32 values
+    # Q8_0 packing keeps every byte (34 per 32 values) and adds the tiled copies
     ts8 = synth.make_tensor_set(SMALL_Q8)
     w8, _, _ = plan(SMALL_Q8, ts8)
-    raw8 = sum(t.nbytes for t in ts8)
+    raw8 = sum(t.nbytes for t in ts8) + tiled_bytes(SMALL_Q8, True)
     assert raw8 <= w8 <= raw8 + 64 * 1024
 
 
@@ -88,7 +97,8 @@ def test_plan_1b_q8_sizes():
     w, k, s = llm.llm_plan(c, arr, len(ts))
     layer_q8 = 16 * (2048 * 3072 + 2048 * 2048 + 2 * 8192 * 2048 + 8192 * 2048) * 34 // 32
     embd = 128256 * 2048 * 4
-    assert layer_q8 + embd <= w <= layer_q8 + embd + 1 << 20
+    want = layer_q8 + embd + tiled_bytes(cfg, True)
+    assert want <= w <= want + (1 << 20)
     assert k == 2 * 16 * 8 * 8320 * 64 * 2
 
 
