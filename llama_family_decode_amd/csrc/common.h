@@ -267,7 +267,8 @@ hipError_t launch_tile_w(const Mat& W, hipStream_t s);
 // fp32 rows [n_q][n_heads*64] and their tiled binary16 hi/lo planes.
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
-                                    int n_ctx, float scale_div, const SpanCfg& span, bool n3, hipStream_t s);
+                                    int n_ctx, float scale_div, const SpanCfg& span, bool n3, float* ws,
+                                    size_t ws_floats, hipStream_t s);
 // Activations of a prefill product: fp32 rows (ld K) and, for F16 weights,
 // their binary16 hi/lo planes (tiled layout); l = nullptr when the activations
 // are binary16 already (one matrix-core pass).

@@ -875,13 +875,16 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // pass over the chunks finds each row's span maximum M and sum L, and the
 // second weights V with the probabilities f16(e^(s - M) / L), which are the
 // binary16 operand of the P V product themselves.
+// Long contexts split a block's chunks over gridDim.z blocks (cps chunks
+// each) that write their rows' (m, l, unnormalised o) to part, [row][head]
+// [split][2 + 64]; k_attn_prefill_merge then combines the splits.
 constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72, PA_PLD = 68;
 
 template <bool N3>
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc,
                                                            float* out, __half* out_h, __half* out_l, int n_q, int p0,
                                                            int n_heads, int n_kv_heads, int n_ctx, float scale_div,
-                                                           SpanCfg span) {
+                                                           SpanCfg span, int cps, float* part) {
     constexpr int hd = 64;
     __shared__ __attribute__((aligned(16))) __half Ks[PA_CH * PA_LD];   // [position][dim]
     __shared__ __attribute__((aligned(16))) __half Vt[hd * PA_LD];      // [dim][position]
@@ -961,8 +964,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             Lrow[i] = l_run[i];
         }
     }
-    load(chunk_of(0) * PA_CH);
-    for (int v = 0; v < nv; v++) {
+    // this block's share of the chunks
+    const int v_begin = N3 ? 0 : min(nv, (int)blockIdx.z * cps), v_end = N3 ? nv : min(nv, v_begin + cps);
+    if (v_begin < v_end) load(chunk_of(v_begin) * PA_CH);
+    for (int v = v_begin; v < v_end; v++) {
         const int c0 = chunk_of(v) * PA_CH;
         __syncthreads();  // the previous chunk's K, V and P reads are done
 #pragma unroll
@@ -973,7 +978,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             for (int j = 0; j < 8; j++) Vt[(ld8 + j) * PA_LD + lp + 32 * u] = vh[j];
         }
         __syncthreads();
-        if (v + 1 < nv) load(chunk_of(v + 1) * PA_CH);
+        if (v + 1 < v_end) load(chunk_of(v + 1) * PA_CH);
 
         // scores of this wave's 16 rows over the chunk: tile pt covers
         // positions c0 + 16 pt .. +15
@@ -1072,6 +1077,22 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         }
     }
     }
+    if (gridDim.z > 1) {  // this split's (m, l, o) per row for the merge
+        const int S = gridDim.z, s = blockIdx.z;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = 16 * wave + 4 * lq + i, z = z0 + r / G, h = g * G + r % G;
+            if (z >= n_q) continue;
+            float* pr = part + (((size_t)z * n_heads + h) * S + s) * (hd + 2);
+            if (lr == 0) {
+                pr[0] = m_run[i];
+                pr[1] = l_run[i];
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) pr[2 + 16 * dt + lr] = o[dt][i];
+        }
+        return;
+    }
     // out[z][h*64 + d] = o / l for the lane's rows 4 lq + i, dims 16 dt + lr
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -1090,19 +1111,60 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
     }
 }
 
+// The splits of each (row, head): M = max m_s, L = sum l_s e^(m_s - M),
+// out = sum o_s e^(m_s - M) / L in split order, with the hi/lo planes. One
+// 64-lane wave per (row, head), a lane per dimension.
+__global__ __launch_bounds__(256) void k_attn_prefill_merge(const float* part, int S, int n_q, int n_heads, float* out,
+                                                            __half* out_h, __half* out_l) {
+    constexpr int hd = 64;
+    const int item = blockIdx.x * 4 + (threadIdx.x >> 6), d = threadIdx.x & 63;
+    if (item >= n_q * n_heads) return;
+    const int z = item / n_heads, h = item % n_heads;
+    const float* pr = part + (size_t)item * S * (hd + 2);
+    float M = -INFINITY;
+    for (int j = 0; j < S; j++) M = fmaxf(M, pr[(size_t)j * (hd + 2)]);
+    float L = 0.f, O = 0.f;
+    for (int j = 0; j < S; j++) {
+        const float* pj = pr + (size_t)j * (hd + 2);
+        const float f = pj[0] == -INFINITY ? 0.f : expf(pj[0] - M);
+        L += pj[1] * f;
+        O += pj[2 + d] * f;
+    }
+    const float v = O / L;
+    const int qd = n_heads * hd, col = h * hd + d;
+    out[(size_t)z * qd + col] = v;
+    const __half hh = __float2half_rn(v);
+    const size_t t = tile_off(z, col, qd, kTileA);
+    out_h[t] = hh;
+    out_l[t] = __float2half_rn(v - __half2float(hh));
+}
+
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
-                                    int n_ctx, float scale_div, const SpanCfg& span, bool n3, hipStream_t s) {
+                                    int n_ctx, float scale_div, const SpanCfg& span, bool n3, float* ws,
+                                    size_t ws_floats, hipStream_t s) {
     const int G = n_kv_heads > 0 ? n_heads / n_kv_heads : 0;
     if (head_dim != 64 || G < 1 || G > PA_ROWS || PA_ROWS % G || n_heads % n_kv_heads || n_q <= 0)
         return hipErrorInvalidValue;
     const int TB = PA_ROWS / G;
-    if (n3)
-        hipLaunchKernelGGL(k_attn_prefill_mfma<true>, dim3((n_q + TB - 1) / TB, n_kv_heads), dim3(256), 0, s, Q, kc, vc,
-                           out, out_h, out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div, span);
-    else
-        hipLaunchKernelGGL(k_attn_prefill_mfma<false>, dim3((n_q + TB - 1) / TB, n_kv_heads), dim3(256), 0, s, Q, kc,
-                           vc, out, out_h, out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div, span);
+    const dim3 grid((n_q + TB - 1) / TB, n_kv_heads);
+    if (n3) {
+        hipLaunchKernelGGL(k_attn_prefill_mfma<true>, grid, dim3(256), 0, s, Q, kc, vc, out, out_h, out_l, n_q, p0,
+                           n_heads, n_kv_heads, n_ctx, scale_div, span, 0, nullptr);
+        return hipGetLastError();
+    }
+    // at most 8 chunks of 64 positions per block: longer contexts split
+    const int nch = (p0 + n_q - 1) / PA_CH + 1;
+    int S = (nch + 7) / 8;
+    if (S > 8) S = 8;
+    while (S > 1 && (size_t)n_q * n_heads * S * (head_dim + 2) > ws_floats) S--;
+    const int cps = (nch + S - 1) / S;
+    hipLaunchKernelGGL(k_attn_prefill_mfma<false>, dim3(grid.x, grid.y, S), dim3(256), 0, s, Q, kc, vc, out, out_h,
+                       out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div, span, cps, S > 1 ? ws : nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    hipLaunchKernelGGL(k_attn_prefill_merge, dim3((unsigned)((n_q * n_heads + 3) / 4)), dim3(256), 0, s, ws, S, n_q,
+                       n_heads, out, out_h, out_l);
     return hipGetLastError();
 }
 

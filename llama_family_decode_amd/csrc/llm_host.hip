@@ -910,7 +910,8 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0;
             if (mfma_attn)
                 HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, L.Oh, L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
-                                                   cf.head_dim, cf.n_ctx, t.scale_div, t.span, n3, s));
+                                                   cf.head_dim, cf.n_ctx, t.scale_div, t.span, n3, L.ws, L.ws_floats,
+                                                   s));
             else
                 HIPCHK(c, launch_attn(t, m, s));
             int mr = m;

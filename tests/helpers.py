@@ -53,6 +53,8 @@ SMALL_SINKS = SMALL_F16.with_(name="small-sinks", attn_window=4, attn_sinks=2, s
 SMALL_TEMP = SMALL.with_(name="small-temp", attn_temp_scale=0.1, attn_temp_len=4, seed=20)
 SMALL_SPAN_ALL = SMALL_NEOX_BIAS.with_(name="small-window-sinks-temp", attn_window=6, attn_sinks=3,
                                       attn_temp_scale=0.5, attn_temp_len=3, seed=21)
+# head_dim 64, the matrix-core prefill attention's size, on a small model
+SMALL_HD64 = SMALL.with_(name="small-hd64", dim=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn=704, seed=26)
 # llama.cpp's rounding points (numerics 1) on each weight type
 SMALL_N3 = SMALL.with_(name="small-f32-llamacpp", numerics=1, seed=23)
 SMALL_F16_N3 = SMALL_F16.with_(name="small-f16-llamacpp", numerics=1, seed=24)

@@ -20,7 +20,7 @@ import oracle
 import synth
 from helpers import (SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8,
                      SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW, SMALL_YARN, SMALL_N3, SMALL_F16_N3,
-                     SMALL_Q8_N3)
+                     SMALL_Q8_N3, SMALL_HD64)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -154,9 +154,15 @@ def test_prefill_small(cfg):
     run_decode(cfg, n_prompt=13, n_steps=4, prefill_gpu=True, prefill_ref=True)
 
 
-@pytest.mark.parametrize("cfg", [SMALL_Q8, SMALL_SPAN_ALL.with_(attn_window=300, attn_temp_len=400)],
+@pytest.mark.parametrize("cfg", [SMALL_Q8, SMALL_SPAN_ALL.with_(attn_window=300, attn_temp_len=400),
+                                 SMALL_HD64.with_(mat_dtype="q8_0", name="small-hd64-q8_0"),
+                                 SMALL_HD64.with_(mat_dtype="f16", embd_dtype="f16", tied=True,
+                                                  name="small-hd64-f16", attn_window=700, attn_sinks=4)],
                          ids=lambda c: c.name)
 def test_prefill_spans_chunks_and_ragged_tail(cfg):
+    # 1100 rows: three chunks, the last ragged; with head_dim 64 the
+    # matrix-core attention of the later chunks splits each block's cache
+    # range over 2 and 3 blocks and merges them
     cfg = cfg.with_(n_ctx=1200)
     run_decode(cfg, n_prompt=1100, n_steps=3, prefill_gpu=True, prefill_ref=True)
 
