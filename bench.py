@@ -18,8 +18,8 @@ compiled for this shape). The line also reports
   - decode_reports: the same decode with F16 matrices at context 2048, with
     Q8_0 at context 8192 (attention a larger share of the bytes), with
     Llama 3's RoPE frequency factors (rope_freqs.weight), at context 8192
-    with a 1024-row sliding window plus 4 sink rows, and with llama.cpp's
-    rounding points (on the launch graph);
+    with a 1024-row sliding window plus 4 sink rows, with llama.cpp's
+    rounding points (on the launch graph), and with YaRN (factor 16);
   - cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 8]
@@ -331,7 +331,10 @@ def main():
                                          synth.C4_LONG.with_(name="llama-1b-q8_0-window1024-sinks4", attn_window=1024,
                                                              attn_sinks=4), 8192),
                    measure_decode_report(llm, synth, np, torch,
-                                         synth.C4.with_(name="llama-1b-q8_0-llamacpp-numerics", numerics=1), 2048)]
+                                         synth.C4.with_(name="llama-1b-q8_0-llamacpp-numerics", numerics=1), 2048),
+                   measure_decode_report(llm, synth, np, torch,
+                                         synth.C4.with_(name="llama-1b-q8_0-yarn16", yarn_factor=16.0,
+                                                        yarn_orig_ctx=16384), 2048)]
 
     cpu = None
     if not args.no_cpu:
