@@ -151,6 +151,7 @@ struct StepArgs {
 };
 
 constexpr int kStepGroups = 8;     // block groups of the persistent step kernel (one per XCD)
+constexpr int kMaxStepGrid = 4096;  // blocks of the persistent step kernel at most
 constexpr int kStepMaxSplit = 64;  // attention splits per KV head of the persistent step kernel
 constexpr int kStepPhases = 5;     // barriers per layer of the persistent step kernel
 constexpr int kBarSlots = 2 * kStepGroups;  // barrier counters
@@ -243,6 +244,10 @@ hipError_t launch_argmax_finalize(State* st, int* gen_out, int gen_cap, hipStrea
 // step.
 int step_grid(StepArgs& a, int dtype, int* lds_bytes, const void** fn, bool* special);
 hipError_t launch_step(const StepArgs& a, const void* fn, int grid, int lds_bytes, hipStream_t s);
+// Whether a cooperative grid of `grid` blocks puts the blocks with equal
+// b mod 8 on one XCD (the step kernel's groups share their L2). d_buf holds
+// grid ints.
+bool step_groups_share_l2(int grid, int* d_buf, hipStream_t s);
 
 struct PrefillBufs;
 hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s);

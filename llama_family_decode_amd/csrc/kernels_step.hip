@@ -60,9 +60,18 @@ struct Geo {
 };
 using GeoRT = Geo<0, 0>;
 
+// Stores of values other blocks read after a barrier. Values read only by
+// the writer's own group (q|k|v, the SwiGLU output, the attention splits)
+// stay in that group's L2: a group's blocks all run on one XCD (the blocks b
+// with equal b mod 8, checked at load by step_groups_share_l2), the store has
+// reached L2 once the writer's wait_mem returns, and the readers' L1 holds no
+// copy (each per-layer buffer is read once per launch, after its write).
+// Values every group reads (the output and down partial sums) are written
+// through to the device coherence point.
 __device__ __forceinline__ void stc(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void stl(float* p, float v) { *(__attribute__((address_space(1))) float*)p = v; }
 __device__ __forceinline__ u64 ldc(u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ void arrive(u64* p) {
     (void)__hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -479,8 +488,8 @@ __device__ __forceinline__ void emit_qkv(const EmitArgs& e, int ra, int rb, floa
         va = r.x;
         vb = r.y;
     }
-    stc(e.out + ra, va);
-    stc(e.out + rb, vb);
+    stl(e.out + ra, va);
+    stl(e.out + rb, vb);
     if (kind > 0) {
         __half* row = (kind == 1 ? e.kc : e.vc) + ((size_t)head * e.n_ctx + e.pos) * e.hd;
         row[d] = f2h(va);
@@ -520,7 +529,7 @@ __device__ __forceinline__ void wbatch(const WRows& w, const int* rmap, int roff
                         } else if constexpr (EM == EM_QKV) {
                             emit_qkv(ea, rmap[row - 1], rmap[row], pend, v);
                         } else {
-                            stc(ea.out + (row >> 1), silu(pend) * v);
+                            stl(ea.out + (row >> 1), silu(pend) * v);
                         }
                     }
                 } else {
@@ -529,7 +538,7 @@ __device__ __forceinline__ void wbatch(const WRows& w, const int* rmap, int roff
                         if constexpr (EM == EM_QKV)
                             emit_qkv(ea, rmap[row], rmap[row + 1], v, other);
                         else
-                            stc(ea.out + (row >> 1), silu(v) * other);
+                            stl(ea.out + (row >> 1), silu(v) * other);
                     }
                 }
             } else if (cl == 0 && (FULL || row < w.r1)) {
@@ -666,7 +675,7 @@ __device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int
             if constexpr (EM == EM_QKV)
                 emit_qkv(ea, rmap[row], rmap[row + 1], t, other);
             else
-                stc(ea.out + (row >> 1), silu(t) * other);
+                stl(ea.out + (row >> 1), silu(t) * other);
         }
     } else if (end) {
         if constexpr (EM == EM_PART) {
@@ -906,11 +915,11 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                 float o = 0.f;
 #pragma unroll
                 for (int w = 0; w < kSW; w++) o += wred[w * GH + e];
-                stc(mypart + (e / hd) * stride + 2 + (e % hd), o);
+                stl(mypart + (e / hd) * stride + 2 + (e % hd), o);
             }
             if (tid < GC) {
-                stc(mypart + tid * stride, m_run[tid]);
-                stc(mypart + tid * stride + 1, l_run[tid]);
+                stl(mypart + tid * stride, m_run[tid]);
+                stl(mypart + tid * stride + 1, l_run[tid]);
             }
             __syncthreads();
         }
@@ -1377,6 +1386,24 @@ int step_grid(StepArgs& a, int dtype, int* lds_bytes, const void** fn, bool* spe
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, *fn, kSB, *lds_bytes) != hipSuccess) return 0;
     const int grid = cus / kNG * kNG;
     return per_cu >= 1 && grid >= kNG ? grid : 0;
+}
+
+// The XCD (hardware register XCC_ID) each block of a cooperative grid runs on.
+__global__ void k_xcd_probe(int* out) {
+    if (threadIdx.x == 0) out[blockIdx.x] = (int)__builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));
+}
+
+bool step_groups_share_l2(int grid, int* d_buf, hipStream_t s) {
+    void* params[] = {&d_buf};
+    if (hipLaunchCooperativeKernel((const void*)k_xcd_probe, dim3(grid), dim3(kSB), params, 0, s) != hipSuccess)
+        return false;
+    std::vector<int> x(grid);
+    if (hipMemcpyAsync(x.data(), d_buf, (size_t)grid * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return false;
+    for (int b = 0; b < grid; b++)
+        if (x[b] != x[b % kNG]) return false;
+    return true;
 }
 
 hipError_t launch_step(const StepArgs& a, const void* fn, int grid, int lds, hipStream_t s) {

@@ -224,6 +224,7 @@ struct Layout {
     __half *Hh, *Hl, *Oh, *Ol, *Uh, *Ul;  // binary16 hi/lo planes of Hf, Of, Uf
     float* Xc;                            // the wanted rows' residuals (last prefill layer)
     float* attn_stats;                    // span max and sum per (row, head) of the rounded passes
+    int* xcd;                             // the XCD of each step-kernel block (load-time check)
     int* sel;                             // prompt rows whose logits are wanted (chunk-relative)
     int* selo;                            // and their output rows
     size_t ws_floats;
@@ -321,6 +322,7 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.sbar = (unsigned long long*)S.take((size_t)kBarSlots * kBarStride * 8);
     L.strace = (unsigned long long*)S.take((size_t)(kStepPhases * c->n_layers + 2) * 8);
     L.gen_out = (int*)S.take((size_t)c->n_ctx * 4);
+    L.xcd = (int*)S.take((size_t)kMaxStepGrid * 4);
     L.ptok = (int*)S.take((size_t)C * 4);
     L.X = (float*)S.take((size_t)C * c->dim * 4);
     L.Hf = (float*)S.take((size_t)C * c->dim * 4);
@@ -773,6 +775,11 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         c->step_grid = want && same && cfg->numerics == 0
                            ? step_grid(A, dt, &c->step_lds, &c->step_fn, &c->step_special)
                            : 0;
+        // its groups exchange values through their XCD's L2
+        if (c->step_grid > kMaxStepGrid || (c->step_grid > 0 && !step_groups_share_l2(c->step_grid, L.xcd, s))) {
+            (void)hipGetLastError();
+            c->step_grid = 0;
+        }
         c->use_step = c->step_grid > 0;
     }
 
