@@ -879,6 +879,10 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // each) that write their rows' (m, l, unnormalised o) to part, [row][head]
 // [split][2 + 64]; k_attn_prefill_merge then combines the splits.
 constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72, PA_PLD = 68;
+#ifndef LLM_PA_CHUNKS
+#define LLM_PA_CHUNKS 8
+#endif
+constexpr int kPaChunks = LLM_PA_CHUNKS;
 
 template <bool N3>
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc,
@@ -1153,9 +1157,9 @@ hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __ha
                            n_heads, n_kv_heads, n_ctx, scale_div, span, 0, nullptr);
         return hipGetLastError();
     }
-    // at most 8 chunks of 64 positions per block: longer contexts split
+    // at most kPaChunks chunks of 64 positions per block: longer contexts split
     const int nch = (p0 + n_q - 1) / PA_CH + 1;
-    int S = (nch + 7) / 8;
+    int S = (nch + kPaChunks - 1) / kPaChunks;
     if (S > 8) S = 8;
     while (S > 1 && (size_t)n_q * n_heads * S * (head_dim + 2) > ws_floats) S--;
     const int cps = (nch + S - 1) / S;
