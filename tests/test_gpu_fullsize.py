@@ -92,11 +92,14 @@ def check_layer0_kv(cfg, T, model, tokens_at, max_ulps):
     return worst
 
 
-def test_c4_decode_at_2048_in_the_benchmarked_kernel(monkeypatch):
-    cfg = synth.C4  # 1B shape, Q8_0 layers, tied F32 embedding, n_ctx 8320
+@pytest.mark.parametrize("cfg,ctx", [(synth.C4, 2048), (synth.C3, 2048), (synth.C4_LONG, 8192)],
+                         ids=["q8_0-ctx2048", "f16-ctx2048", "q8_0-ctx8192"])
+def test_decode_at_full_context_in_the_benchmarked_kernel(monkeypatch, cfg, ctx):
+    # the three decode workloads: 1B Q8_0 with the tied F32 embedding at 2048
+    # (the headline) and at 8192 positions, 1B F16 at 2048
     ts = synth.make_tensor_set(cfg)
     T = _tensors_by_name(ts)
-    toks = synth.prompt(cfg, 2048)
+    toks = synth.prompt(cfg, ctx)
     n_steps = 6
 
     def run(kind_env):
@@ -120,7 +123,7 @@ def test_c4_decode_at_2048_in_the_benchmarked_kernel(monkeypatch):
         assert np.all(np.isfinite(lg))
         assert nx == first_max(lg)
     w0 = check_layer0_kv(cfg, T, step, feed, 2.0)
-    wp = check_layer0_kv(cfg, T, step, [(0, toks[0]), (1024, toks[1024]), (2047, toks[2047])], None)
+    wp = check_layer0_kv(cfg, T, step, [(0, toks[0]), (ctx // 2, toks[ctx // 2]), (ctx - 1, toks[ctx - 1])], None)
 
     # the independent launch-graph path, teacher-forced with the same tokens
     monkeypatch.setenv("LLM_STEP", "graph")
@@ -141,8 +144,8 @@ def test_c4_decode_at_2048_in_the_benchmarked_kernel(monkeypatch):
     for a, b in zip(lg_step, lg2):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     again.close()
-    print(f"[C4 ctx 2048] layer-0 KV: decode rows {w0} ulps, prefill rows {wp:.2e} rms; persistent vs graph "
-          f"{worst:.3e}", flush=True)
+    print(f"[{cfg.name} ctx {ctx}] layer-0 KV: decode rows {w0} ulps, prefill rows {wp:.2e} rms; persistent vs "
+          f"graph {worst:.3e}", flush=True)
 
 
 def test_c5_prefill_512_against_decode_and_oracle(monkeypatch):
