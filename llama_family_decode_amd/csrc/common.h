@@ -135,19 +135,21 @@ struct StepArgs {
     unsigned long long* bar;  // barrier counters, kBarStride u64 apart
     float* qkv;     // q | k | v after bias and RoPE, per layer [n_layers][qkv_stride]
     float* part;    // attention split partials per layer [n_layers][part_stride]
+    float* pst;     // rounding mode: the splits' (max, sum) of the first attention pass [n_layers][pst_stride]
     float* po;      // output-product partial sums per layer and group [n_layers][kStepGroups][pstride]
     float* pd;      // down-product partial sums, same layout
     float* u;       // SwiGLU output per layer [n_layers][u_stride]
     float* logits;  // [vocab]
     int* gen_out;
     int gen_cap;
-    long long qkv_stride, part_stride, u_stride, pstride;
+    long long qkv_stride, part_stride, u_stride, pstride, pst_stride;
     unsigned long long* trace;  // nullptr, or wall-clock stamps of block 0 after each barrier
     int dim, n_heads, n_kv_heads, head_dim, n_rot, neox, n_ctx, ffn, vocab;
     int lds_xr, lds_xs, lds_wsp;  // LDS regions (floats)
     int lds_lw;                   // LDS offset (floats) of the copy of the layer table
     float eps, scale_div;
     SpanCfg span;
+    int rnd;  // 1: llama.cpp's rounding points (product inputs, q, probabilities)
 };
 
 constexpr int kStepGroups = 8;     // block groups of the persistent step kernel (one per XCD)
@@ -198,7 +200,7 @@ struct GemvArgs {
     // EPI_ARGMAX
     int* gen_out;
     int gen_cap;
-    int n3;  // llama.cpp's rounding points: round the staged input for W's type
+    int rnd;  // llama.cpp's rounding points: round the staged input for W's type
 };
 
 struct AttnArgs {
@@ -217,7 +219,7 @@ struct AttnArgs {
     // llama.cpp's rounding points (q and the probabilities to binary16) run as
     // passes: 1 = split maxima and sums only, 2 = the weighted sum of V with
     // probabilities f16(e^(s - M) / L) from stats ([n_q][n_heads][2]: M, L)
-    int n3;
+    int rnd;
     float* stats;
 };
 
@@ -272,7 +274,7 @@ hipError_t launch_tile_w(const Mat& W, hipStream_t s);
 // fp32 rows [n_q][n_heads*64] and their tiled binary16 hi/lo planes.
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
-                                    int n_ctx, float scale_div, const SpanCfg& span, bool n3, float* ws,
+                                    int n_ctx, float scale_div, const SpanCfg& span, bool rnd, float* ws,
                                     size_t ws_floats, hipStream_t s);
 // Activations of a prefill product: fp32 rows (ld K) and, for F16 weights,
 // their binary16 hi/lo planes (tiled layout); l = nullptr when the activations

@@ -53,7 +53,7 @@ __device__ void stage_input(const GemvArgs& a, float* xs, double* red) {
         }
     }
     if constexpr (DT != DT_F32) {
-        if (a.n3) {  // llama.cpp's rounding of the product's input for this weight type
+        if (a.rnd) {  // llama.cpp's rounding of the product's input for this weight type
             __syncthreads();
             for (int b = tid; b < K / 32; b += kBlock) {
                 float v[32];
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const float v = dim_ok ? tau * qz[(g * G + h) * hd + sub * 8 + i] : 0.f;
-            qv[h][i] = a.n3 ? round16(v) : v;
+            qv[h][i] = a.rnd ? round16(v) : v;
         }
     float acc[G][8];
 #pragma unroll
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
             }
         }
         __syncthreads();
-        if (a.n3 == 2) {
+        if (a.rnd == 2) {
             // probabilities from the whole span's max M and sum L, rounded
             // to binary16 before they weight V
             for (int h = wave; h < G; h += kWaves) {
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < kAttnSteps; i++) {
             const int t = pg + i * PPI;
-            if (dim_ok && t < cn && a.n3 != 1) {
+            if (dim_ok && t < cn && a.rnd != 1) {
                 float vf[8];
                 unpack8(vr[i], vf);
 #pragma unroll
@@ -558,12 +558,12 @@ __global__ __launch_bounds__(kBlock) void k_attn(AttnArgs a) {
     const int GH = G * hd;
     float* outz = a.out + (size_t)z * qd + (size_t)g * G * hd;
     __half* outhz = a.out_h ? a.out_h + (size_t)z * qd + (size_t)g * G * hd : nullptr;
-    if (n_active == 1 && a.n3 != 1) {
+    if (n_active == 1 && a.rnd != 1) {
         for (int e = tid; e < GH; e += kBlock) {
             float o = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; w++) o += wred[w * GH + e];
-            const float r = a.n3 == 2 ? o : o / l_run[e / hd];
+            const float r = a.rnd == 2 ? o : o / l_run[e / hd];
             outz[e] = r;
             if (outhz) outhz[e] = f2h(r);
         }
@@ -689,12 +689,12 @@ static hipError_t launch_attn_g(const AttnArgs& a, int n_q, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_done = true;
     }
-    if (a.n3) {
+    if (a.rnd) {
         AttnArgs p = a;
-        p.n3 = 1;  // split maxima and sums
+        p.rnd = 1;  // split maxima and sums
         hipLaunchKernelGGL((k_attn<G>), dim3(a.n_split, a.n_kv_heads, n_q), dim3(kBlock), lds, s, p);
         hipLaunchKernelGGL((k_attn_stats<G>), dim3(a.n_kv_heads, n_q), dim3(64 * G), 0, s, p);
-        p.n3 = 2;  // the weighted sum with the rounded probabilities
+        p.rnd = 2;  // the weighted sum with the rounded probabilities
         hipLaunchKernelGGL((k_attn<G>), dim3(a.n_split, a.n_kv_heads, n_q), dim3(kBlock), lds, s, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.n_split == 1) return e;

@@ -870,7 +870,7 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // With an attention span (a window plus sinks) each row masks the positions
 // outside its own span, and chunks outside every row's span are skipped; q
 // is scaled by its position's attention temperature before the split.
-// N3 (llama.cpp's rounding points, "What a Llama model computes, and why",
+// The rounding mode (llama.cpp's rounding points, "What a Llama model computes, and why",
 // section 8): q is rounded to binary16 (one product per score tile), a first
 // pass over the chunks finds each row's span maximum M and sum L, and the
 // second weights V with the probabilities f16(e^(s - M) / L), which are the
@@ -884,7 +884,7 @@ constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72, PA_PLD = 68;
 #endif
 constexpr int kPaChunks = LLM_PA_CHUNKS;
 
-template <bool N3>
+template <bool RND>
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc,
                                                            float* out, __half* out_h, __half* out_l, int n_q, int p0,
                                                            int n_heads, int n_kv_heads, int n_ctx, float scale_div,
@@ -914,7 +914,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         for (int j = 0; j < 8; j++) {
             const _Float16 h = (_Float16)v[j];
             qh[ks][j] = h;
-            ql[ks][j] = N3 ? (_Float16)0.f : (_Float16)(v[j] - (float)h);
+            ql[ks][j] = RND ? (_Float16)0.f : (_Float16)(v[j] - (float)h);
         }
     }
     // the four rows whose scores and outputs this lane holds: 4*lq + i
@@ -959,9 +959,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         }
     };
     float* P = Ps[wave];
-    float Mrow[4], Lrow[4];  // N3: each row's span maximum and sum, from the first pass
-    for (int pass = N3 ? 0 : 1; pass < 2; pass++) {
-    if (N3 && pass == 1) {
+    float Mrow[4], Lrow[4];  // rounding mode: each row's span maximum and sum, from the first pass
+    for (int pass = RND ? 0 : 1; pass < 2; pass++) {
+    if (RND && pass == 1) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             Mrow[i] = m_run[i];
@@ -969,7 +969,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         }
     }
     // this block's share of the chunks
-    const int v_begin = N3 ? 0 : min(nv, (int)blockIdx.z * cps), v_end = N3 ? nv : min(nv, v_begin + cps);
+    const int v_begin = RND ? 0 : min(nv, (int)blockIdx.z * cps), v_end = RND ? nv : min(nv, v_begin + cps);
     if (v_begin < v_end) load(chunk_of(v_begin) * PA_CH);
     for (int v = v_begin; v < v_end; v++) {
         const int c0 = chunk_of(v) * PA_CH;
@@ -994,10 +994,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             for (int ks = 0; ks < 2; ks++) {
                 const half8 kf = *(const half8*)(Ks + (16 * pt + lr) * PA_LD + 32 * ks + 8 * lq);
                 sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[ks], kf, sc[pt], 0, 0, 0);
-                if constexpr (!N3) sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], kf, sc[pt], 0, 0, 0);
+                if constexpr (!RND) sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], kf, sc[pt], 0, 0, 0);
             }
         }
-        if (N3 && pass == 1) {
+        if (RND && pass == 1) {
             // the rounded probabilities of the whole span, the P V operand as is
 #pragma unroll
             for (int pt = 0; pt < 4; pt++)
@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             l_run[i] = l_run[i] * alpha[i] + ls;
             m_run[i] = m_new;
         }
-        if (N3) continue;  // the first pass only finds M and L
+        if (RND) continue;  // the first pass only finds M and L
 #pragma unroll
         for (int pt = 0; pt < 4; pt++)
 #pragma unroll
@@ -1104,7 +1104,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         if (z >= n_q) continue;
 #pragma unroll
         for (int dt = 0; dt < 4; dt++) {
-            const float v = N3 ? o[dt][i] : o[dt][i] / l_run[i];
+            const float v = RND ? o[dt][i] : o[dt][i] / l_run[i];
             const int col = h * hd + 16 * dt + lr;
             out[(size_t)z * qd + col] = v;
             const __half hh = __float2half_rn(v);
@@ -1145,14 +1145,14 @@ __global__ __launch_bounds__(256) void k_attn_prefill_merge(const float* part, i
 
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
-                                    int n_ctx, float scale_div, const SpanCfg& span, bool n3, float* ws,
+                                    int n_ctx, float scale_div, const SpanCfg& span, bool rnd, float* ws,
                                     size_t ws_floats, hipStream_t s) {
     const int G = n_kv_heads > 0 ? n_heads / n_kv_heads : 0;
     if (head_dim != 64 || G < 1 || G > PA_ROWS || PA_ROWS % G || n_heads % n_kv_heads || n_q <= 0)
         return hipErrorInvalidValue;
     const int TB = PA_ROWS / G;
     const dim3 grid((n_q + TB - 1) / TB, n_kv_heads);
-    if (n3) {
+    if (rnd) {
         hipLaunchKernelGGL(k_attn_prefill_mfma<true>, grid, dim3(256), 0, s, Q, kc, vc, out, out_h, out_l, n_q, p0,
                            n_heads, n_kv_heads, n_ctx, scale_div, span, 0, nullptr);
         return hipGetLastError();

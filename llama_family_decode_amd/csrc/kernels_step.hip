@@ -326,6 +326,34 @@ __device__ __forceinline__ void stage_copy(const float* src, int K, float* xs) {
     __syncthreads();
 }
 
+// The rounding mode's product input (llama.cpp's rounding points, "What a
+// Llama model computes, and why", section 8, with the Q8_0 quantizer of
+// "Loading GGUF with the FFM API", Example 8):
+// for Q8_0 weights each 32-element block of the staged input becomes its Q8_0
+// encoding decoded again (scale max|x|/127 rounded to binary16 after the
+// codes are taken), for F16 weights each element its binary16 value; F32
+// weights take the input as it is. K is a multiple of 32 and the staged input
+// starts at a block boundary, so the 32 lanes of a half-wave hold one block.
+template <int DT>
+__device__ __forceinline__ void round_input(float* xs, int K) {
+    if constexpr (DT != DT_F32) {
+        for (int i = thread_id(); i < K; i += kSB) {
+            float v = xs[swz<DT>(i)];
+            if constexpr (DT == DT_Q8) {
+                float amax = fabsf(v);
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+                const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f;
+                v = round16(d) * roundf(v * id);
+            } else {
+                v = round16(v);
+            }
+            xs[swz<DT>(i)] = v;
+        }
+        __syncthreads();
+    }
+}
+
 // xr[i] += sum over the groups that contributed of P[g][i], groups in order.
 __device__ __forceinline__ void add_partials(float* xr, const float* P, long long pstride, int dim, unsigned gmask) {
     for (int i = 4 * thread_id(); i < dim; i += 4 * kSB) {
@@ -766,10 +794,18 @@ __device__ __forceinline__ void attn_kv_load(const StepArgs& a, int layer, int g
 // G query heads of g are taken GC at a time. Splits run over the span's
 // indices (span_row gives the cache row); q is scaled by the attention
 // temperature of pos.
+//
+// The rounding mode ("What a Llama model computes, and why", section 8: q in
+// binary16, and the normalised probabilities rounded to binary16 before they weight V) runs
+// two passes. Pass 1 keeps only each split's (m, l), written to
+// pst[((g*S + s)*G + h)*2]. After a group barrier, pass 2 takes the span's
+// M = max m_s and L = sum l_s e^(m_s - M), weights V with f16(e^(x - M)/L), and
+// writes each split's o with m = 0 and l = 1 for split 0 (0 for the others),
+// so the merge adds the splits' o with weight one.
 template <int GC>
 __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos, const Span& span, const float* qkv,
-                                           float* part, int hlo, int nh, int S, int CH, int rk, int bg,
-                                           u32x4 (&kr)[kStepAttn], u32x4 (&vr)[kStepAttn], float* sm,
+                                           float* part, float* pst, int pass, int hlo, int nh, int S, int CH, int rk,
+                                           int bg, u32x4 (&kr)[kStepAttn], u32x4 (&vr)[kStepAttn], float* sm,
                                            float* m_run, float* l_run, float* alpha) {
     const int hd = a.head_dim, P = span.n, G = a.n_heads / a.n_kv_heads;
     const float tau = attn_temp(a.span, pos);
@@ -781,7 +817,7 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
     const int sub8 = dim_ok ? sub * 8 : 0;
     float* sc = sm;                 // [GC][CHUNK]
     float* wred = sm + GC * CHUNK;  // [kSW][GC][hd]
-    bool have = true;               // the first chunk of the first item is prefetched
+    bool have = pass != 2;          // the first chunk of the first item is prefetched
 
     for (int item = rk; item < nh * S; item += bg) {
         const int g = hlo + item / S, s = item % S;
@@ -813,11 +849,30 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                 qv[h][5] = a1.y * f;
                 qv[h][6] = a1.z * f;
                 qv[h][7] = a1.w * f;
+                if (pass != 0)
+#pragma unroll
+                    for (int i = 0; i < 8; i++) qv[h][i] = round16(qv[h][i]);
 #pragma unroll
                 for (int i = 0; i < 8; i++) acc[h][i] = 0.f;
             }
             __syncthreads();
-            if (tid < GC) {
+            if (pass == 2) {
+                // the span's max and sum from pass 1's splits (lane = split)
+                for (int h = wave; h < GC; h += kSW) {
+                    float m = -INFINITY, l = 0.f;
+                    if (lane < S) {
+                        const float* pj = pst + (((size_t)g * S + lane) * G + h0 + h) * 2;
+                        m = ldf(pj);
+                        l = ldf(pj + 1);
+                    }
+                    const float M = xmax64(m);
+                    const float L = xsum64(lane < S ? l * expf(m - M) : 0.f);
+                    if (lane == 0) {
+                        m_run[h] = M;
+                        l_run[h] = L;
+                    }
+                }
+            } else if (tid < GC) {
                 m_run[tid] = -INFINITY;
                 l_run[tid] = 0.f;
             }
@@ -858,6 +913,13 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                         if (sub == 0 && t < cn) sc[h * CHUNK + t] = d[i][h] / a.scale_div;
                 }
                 __syncthreads();
+                if (pass == 2) {
+                    for (int h = wave; h < GC; h += kSW) {
+                        const float M = m_run[h], L = l_run[h];
+                        for (int t = lane; t < cn; t += 64) sc[h * CHUNK + t] = round16(expf(sc[h * CHUNK + t] - M) / L);
+                        if (lane == 0) alpha[h] = 1.f;
+                    }
+                } else
                 for (int h = wave; h < GC; h += kSW) {
                     float mx = -INFINITY;
                     for (int t = lane; t < cn; t += 64) mx = fmaxf(mx, sc[h * CHUNK + t]);
@@ -888,7 +950,7 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
 #pragma unroll
                 for (int i = 0; i < kStepAttn; i++) {
                     const int t = pg + i * PPI;
-                    if (dim_ok && t < cn) {
+                    if (dim_ok && t < cn && pass != 1) {
                         float vf[8];
                         unpack8(vr[i], vf);
 #pragma unroll
@@ -902,6 +964,15 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                 __syncthreads();
             }
             if (h0 + GC < G) have = false;  // the next pass reloads K and V
+            if (pass == 1) {
+                if (tid < GC) {
+                    float* myst = pst + (((size_t)g * S + s) * G + h0 + tid) * 2;
+                    stl(myst, m_run[tid]);
+                    stl(myst + 1, l_run[tid]);
+                }
+                __syncthreads();
+                continue;
+            }
             lanes_sum_all<GC * 8>(&acc[0][0], LPP, 64);
             if (lane < LPP && dim_ok)
 #pragma unroll
@@ -918,8 +989,8 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                 stl(mypart + (e / hd) * stride + 2 + (e % hd), o);
             }
             if (tid < GC) {
-                stl(mypart + tid * stride, m_run[tid]);
-                stl(mypart + tid * stride + 1, l_run[tid]);
+                stl(mypart + tid * stride, pass == 2 ? 0.f : m_run[tid]);
+                stl(mypart + tid * stride + 1, pass == 2 ? (s == 0 ? 1.f : 0.f) : l_run[tid]);
             }
             __syncthreads();
         }
@@ -999,10 +1070,11 @@ __device__ __forceinline__ void merge_splits(const StepArgs& a, const float* par
 }
 
 // --------------------------------------------------------------------- logits
-template <int DT, class GEO = GeoRT>
+template <int DT, class GEO = GeoRT, bool RND = false>
 __device__ __forceinline__ void logits_phase(const StepArgs& a, const float* xr, const GainPF& gp, float* xs,
                                              double* red, ArgPart* wbest) {
     stage_norm<DT>(xr, a.out_norm, gp, a.eps, a.dim, xs, red);
+    if constexpr (RND) round_input<DT>(xs, a.dim);
     const int lane = thread_id() & 63, wave = thread_id() >> 6;
     const int wv = __builtin_amdgcn_readfirstlane(blockIdx.x * kSW + wave);
     WRows w = wave_rows(a.out.rows, gridDim.x * kSW, wv, a.dim / VecW<DT>::VE, false);
@@ -1044,8 +1116,9 @@ __device__ __forceinline__ void logits_phase(const StepArgs& a, const float* xr,
 // DT: layer weight type. The remaining parameters specialise the kernel for
 // one shape (ODT: output matrix type, GA: query heads per attention pass, then
 // the geometry of the QKV, output, gate/up, down and vocabulary products);
-// ODT = -1, GA = 0 and GeoRT take everything from the run-time shape.
-template <int DT, int ODT, int GA, class GQ, class GO, class GG, class GD, class GL>
+// ODT = -1, GA = 0 and GeoRT take everything from the run-time shape. RND:
+// llama.cpp's rounding points (rounded product inputs, two attention passes).
+template <int DT, int ODT, int GA, class GQ, class GO, class GG, class GD, class GL, bool RND>
 __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     extern __shared__ float sm[];
     __shared__ double red[kSW];
@@ -1083,7 +1156,9 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     for (int i = tid; i < a.n_layers * (int)(sizeof(LayerW) / 8); i += kSB)
         ((unsigned long long*)lw)[i] = ((const unsigned long long*)a.layers)[i];
 
-    const unsigned long long nloc = 3ull * a.n_layers, ncro = 2ull * a.n_layers + 1;
+    // group barriers per layer: after QKV, (rounding mode: between the two
+    // attention passes,) after attention, after gate/up
+    const unsigned long long nloc = (RND ? 4ull : 3ull) * a.n_layers, ncro = 2ull * a.n_layers + 1;
     unsigned long long jl = (unsigned long long)epoch * nloc, jc = (unsigned long long)epoch * ncro;
     int phase = 0;
     const bool tr = a.trace && blockIdx.x == 0 && tid == 0;
@@ -1159,12 +1234,14 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     for (int l = 0; l < a.n_layers; l++) {
         float* qkv = a.qkv + (size_t)l * a.qkv_stride;
         float* part = a.part + (size_t)l * a.part_stride;
+        float* pst = a.pst + (size_t)l * a.pst_stride;
         float* u = a.u + (size_t)l * a.u_stride;
         float* po = a.po + (size_t)l * kNG * a.pstride;
         float* pd = a.pd + (size_t)l * kNG * a.pstride;
 
         // ---- QKV
         stage_norm<DT>(xr, lw[l].attn_norm, gp, a.eps, a.dim, xs, red);
+        if constexpr (RND) round_input<DT>(xs, a.dim);
         ea.out = qkv;
         ea.bias = lw[l].bqkv;
         ea.kc = a.kc + (size_t)l * a.kv_layer;
@@ -1175,15 +1252,31 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         group_wait(a, x, ++jl * bg);
         STAMP();
 
-        // ---- attention
-        if constexpr (GA > 0) {
-            attn_items<GA>(a, l, pos, span, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha);
-        } else {
-            switch (G) {
-                case 1: attn_items<1>(a, l, pos, span, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
-                case 2: attn_items<2>(a, l, pos, span, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
-                default: attn_items<4>(a, l, pos, span, qkv, part, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run, alpha); break;
+        // ---- attention (the rounding mode: pass 1, group barrier, pass 2)
+        for (int pass = RND ? 1 : 0;; pass = 2) {
+            if constexpr (GA > 0) {
+                attn_items<GA>(a, l, pos, span, qkv, part, pst, pass, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run, l_run,
+                               alpha);
+            } else {
+                switch (G) {
+                    case 1:
+                        attn_items<1>(a, l, pos, span, qkv, part, pst, pass, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run,
+                                      l_run, alpha);
+                        break;
+                    case 2:
+                        attn_items<2>(a, l, pos, span, qkv, part, pst, pass, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run,
+                                      l_run, alpha);
+                        break;
+                    default:
+                        attn_items<4>(a, l, pos, span, qkv, part, pst, pass, hlo, nh, S, CH, rk, bg, kr, vr, xs, m_run,
+                                      l_run, alpha);
+                        break;
+                }
             }
+            if (pass != 1) break;
+            wait_mem();
+            group_arrive(a, x);
+            group_wait(a, x, ++jl * bg);
         }
         wait_mem();
         group_arrive(a, x);
@@ -1196,6 +1289,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         // ---- split merge + output product (partial over the group's heads)
         if (nh > 0) {
             merge_splits<DT>(a, part, hlo, nh, S, xs, wsp, ored);
+            if constexpr (RND) round_input<DT>(xs, nh * G * hd);
             ea.out = po + (size_t)x * a.pstride;
             wrun<DT, EM_PART, GO>(wo, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
         }
@@ -1211,6 +1305,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         // ---- residual, RMSNorm, gate/up + SwiGLU
         add_partials(xr, po, a.pstride, a.dim, hmask);
         stage_norm<DT>(xr, lw[l].ffn_norm, gp, a.eps, a.dim, xs, red);
+        if constexpr (RND) round_input<DT>(xs, a.dim);
         ea.out = u + flo;
         wrun<DT, EM_SWIGLU, GG>(wg, nullptr, 2 * flo, xs, pf, true, ea, best, bi, nfin);
         wait_mem();
@@ -1224,6 +1319,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         // ---- down product (partial over the group's hidden units)
         if (nf > 0) {
             stage_copy<DT>(u + flo, nf, xs);
+            if constexpr (RND) round_input<DT>(xs, nf);
             ea.out = pd + (size_t)x * a.pstride;
             wrun<DT, EM_PART, GD>(wd, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
         }
@@ -1244,12 +1340,12 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     }
 
     if constexpr (ODT >= 0) {
-        logits_phase<ODT, GL>(a, xr, gp, xs, red, wbest);
+        logits_phase<ODT, GL, RND>(a, xr, gp, xs, red, wbest);
     } else {
         switch (a.out.dtype) {
-            case DT_F32: logits_phase<DT_F32>(a, xr, gp, xs, red, wbest); break;
-            case DT_F16: logits_phase<DT_F16>(a, xr, gp, xs, red, wbest); break;
-            default: logits_phase<DT_Q8>(a, xr, gp, xs, red, wbest); break;
+            case DT_F32: logits_phase<DT_F32, GeoRT, RND>(a, xr, gp, xs, red, wbest); break;
+            case DT_F16: logits_phase<DT_F16, GeoRT, RND>(a, xr, gp, xs, red, wbest); break;
+            default: logits_phase<DT_Q8, GeoRT, RND>(a, xr, gp, xs, red, wbest); break;
         }
     }
     wait_mem();
@@ -1311,16 +1407,19 @@ bool step_lds_plan(StepArgs& a, int dtype, int* lds_bytes) {
 // (lanes-per-row shift, column batches) of the five products.
 struct StepSpec {
     int dt, odt, ga, geo[5][2];
-    const void* fn;
+    const void* fn;      // float numerics
+    const void* fn_rnd;  // llama.cpp's rounding points
 };
 
 static const StepSpec kSpecs[] = {
     // 2048-wide Q8_0 layers, 4 query heads per KV head of 64, 8192 FFN units, F32 vocabulary rows
     {DT_Q8, DT_F32, 4, {{6, 2}, {4, 1}, {6, 2}, {6, 1}, {6, 8}},
-     (const void*)k_step<DT_Q8, DT_F32, 4, Geo<6, 2>, Geo<4, 1>, Geo<6, 2>, Geo<6, 1>, Geo<6, 8>>},
+     (const void*)k_step<DT_Q8, DT_F32, 4, Geo<6, 2>, Geo<4, 1>, Geo<6, 2>, Geo<6, 1>, Geo<6, 8>, false>,
+     (const void*)k_step<DT_Q8, DT_F32, 4, Geo<6, 2>, Geo<4, 1>, Geo<6, 2>, Geo<6, 1>, Geo<6, 8>, true>},
     // the same shape with F16 layers and F16 vocabulary rows
     {DT_F16, DT_F16, 4, {{6, 4}, {5, 1}, {6, 4}, {6, 2}, {6, 4}},
-     (const void*)k_step<DT_F16, DT_F16, 4, Geo<6, 4>, Geo<5, 1>, Geo<6, 4>, Geo<6, 2>, Geo<6, 4>>},
+     (const void*)k_step<DT_F16, DT_F16, 4, Geo<6, 4>, Geo<5, 1>, Geo<6, 4>, Geo<6, 2>, Geo<6, 4>, false>,
+     (const void*)k_step<DT_F16, DT_F16, 4, Geo<6, 4>, Geo<5, 1>, Geo<6, 4>, Geo<6, 2>, Geo<6, 4>, true>},
 };
 
 // The geometry wave_rows gives a product of n rows over a window of nch
@@ -1366,13 +1465,18 @@ static const void* pick_kernel(const StepArgs& a, int dtype, bool* special) {
             for (int i = 0; i < 5; i++) same = same && sp.geo[i][0] == g[i][0] && sp.geo[i][1] == g[i][1];
             if (same) {
                 *special = true;
-                return sp.fn;
+                return a.rnd ? sp.fn_rnd : sp.fn;
             }
         }
+    if (a.rnd) switch (dtype) {
+            case DT_F32: return (const void*)k_step<DT_F32, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT, true>;
+            case DT_F16: return (const void*)k_step<DT_F16, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT, true>;
+            default: return (const void*)k_step<DT_Q8, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT, true>;
+        }
     switch (dtype) {
-        case DT_F32: return (const void*)k_step<DT_F32, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT>;
-        case DT_F16: return (const void*)k_step<DT_F16, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT>;
-        default: return (const void*)k_step<DT_Q8, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT>;
+        case DT_F32: return (const void*)k_step<DT_F32, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT, false>;
+        case DT_F16: return (const void*)k_step<DT_F16, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT, false>;
+        default: return (const void*)k_step<DT_Q8, -1, 0, GeoRT, GeoRT, GeoRT, GeoRT, GeoRT, false>;
     }
 }
 

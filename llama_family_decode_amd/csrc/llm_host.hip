@@ -216,8 +216,8 @@ struct Layout {
     int *gen_out, *ptok;
     LayerW* dlayers;  // device copy of the layer table (persistent step kernel)
     // per-layer activations of the persistent step kernel (strides padded to 256 bytes)
-    float *sqkv, *spart, *spo, *spd, *su;
-    long long qkv_stride, part_stride, u_stride, pstride;
+    float *sqkv, *spart, *spst, *spo, *spd, *su;
+    long long qkv_stride, part_stride, u_stride, pstride, pst_stride;
     unsigned long long* sbar;
     unsigned long long* strace;
     float *X, *Hf, *QKV, *Q, *Of, *Uf, *ws;
@@ -312,10 +312,12 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     auto pad64 = [](long long n) { return (n + 63) / 64 * 64; };
     L.qkv_stride = pad64(qd + 2 * kvd);
     L.part_stride = pad64((long long)kStepMaxSplit * c->n_kv_heads * G * (c->head_dim + 2));
+    L.pst_stride = pad64((long long)kStepMaxSplit * c->n_kv_heads * G * 2);
     L.u_stride = pad64(c->ffn);
     L.pstride = pad64(c->dim);
     L.sqkv = (float*)S.take((size_t)c->n_layers * L.qkv_stride * 4);
     L.spart = (float*)S.take((size_t)c->n_layers * L.part_stride * 4);
+    L.spst = (float*)S.take((size_t)c->n_layers * L.pst_stride * 4);
     L.spo = (float*)S.take((size_t)c->n_layers * kStepGroups * L.pstride * 4);
     L.spd = (float*)S.take((size_t)c->n_layers * kStepGroups * L.pstride * 4);
     L.su = (float*)S.take((size_t)c->n_layers * L.u_stride * 4);
@@ -423,7 +425,7 @@ GemvArgs base_args(llm_ctx* c) {
     a.neox = c->cfg.rope_neox;
     a.n_ctx = c->cfg.n_ctx;
     a.rope = c->L.rope;
-    a.n3 = c->cfg.numerics;
+    a.rnd = c->cfg.numerics;
     return a;
 }
 
@@ -479,7 +481,7 @@ hipError_t stage_attn(llm_ctx* c, int l, const float* q, float* out, hipStream_t
     t.n_split = L.n_split;
     t.scale_div = (float)sqrt((double)cf.head_dim);
     t.span = span_cfg(cf);
-    t.n3 = cf.numerics;
+    t.rnd = cf.numerics;
     t.stats = L.attn_stats;
     return launch_attn(t, 1, s);
 }
@@ -738,11 +740,13 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         A.bar = L.sbar;
         A.qkv = L.sqkv;
         A.part = L.spart;
+        A.pst = L.spst;
         A.po = L.spo;
         A.pd = L.spd;
         A.u = L.su;
         A.qkv_stride = L.qkv_stride;
         A.part_stride = L.part_stride;
+        A.pst_stride = L.pst_stride;
         A.u_stride = L.u_stride;
         A.pstride = L.pstride;
         A.logits = L.logits;
@@ -762,6 +766,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         A.eps = cfg->eps;
         A.scale_div = (float)sqrt((double)cfg->head_dim);
         A.span = span_cfg(*cfg);
+        A.rnd = cfg->numerics;
         if (!upload(L.dlayers, L.layers.data(), L.layers.size() * sizeof(LayerW)))
             return bail(LLM_ERR_DEVICE, "layer table upload failed");
         // The persistent kernel needs one weight type for all layer matrices.
@@ -771,10 +776,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
             same = same && w.qkv.dtype == dt && w.o.dtype == dt && w.gu.dtype == dt && w.down.dtype == dt;
         const char* sk = getenv("LLM_STEP");
         const bool want = !(sk && strcmp(sk, "graph") == 0);
-        // the step kernel computes with float activations only
-        c->step_grid = want && same && cfg->numerics == 0
-                           ? step_grid(A, dt, &c->step_lds, &c->step_fn, &c->step_special)
-                           : 0;
+        c->step_grid = want && same ? step_grid(A, dt, &c->step_lds, &c->step_fn, &c->step_special) : 0;
         // its groups exchange values through their XCD's L2
         if (c->step_grid > kMaxStepGrid || (c->step_grid > 0 && !step_groups_share_l2(c->step_grid, L.xcd, s))) {
             (void)hipGetLastError();
@@ -854,10 +856,10 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
     hipStream_t s = c->stream;
     const int qd = c->qd, kvd = c->kvd, qkvd = qd + 2 * kvd;
     const int nr = (int)rows_out.size();
-    const bool n3 = cf.numerics != 0;  // llama.cpp's rounding of every product input
+    const bool rnd = cf.numerics != 0;  // llama.cpp's rounding of every product input
     // with rounded inputs an F16 product's lo plane is zero: one matrix-core pass
     // (a rounded Q8_0 input, f16(d) * code, still needs both planes)
-    auto lo = [n3](const Mat& w, const __half* l) { return n3 && w.dtype == DT_F16 ? nullptr : l; };
+    auto lo = [rnd](const Mat& w, const __half* l) { return rnd && w.dtype == DT_F16 ? nullptr : l; };
     // the wanted rows grouped by chunk, output order kept within a chunk:
     // c->sel_out[p] = output index, c->sel_row[p] = prompt row
     c->sel_out.clear();
@@ -890,7 +892,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             __half* vc = L.vc + (size_t)l * L.kv_layer;
             if (!normed) HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
             normed = false;
-            if (n3) HIPCHK(c, launch_round_rows(L.Hf, m, cf.dim, W.qkv.dtype, L.Hh, L.Hl, s));
+            if (rnd) HIPCHK(c, launch_round_rows(L.Hf, m, cf.dim, W.qkv.dtype, L.Hh, L.Hl, s));
             HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, GemmA{L.Hf, L.Hh, lo(W.qkv, L.Hl)}, m, L.QKV, qkvd, W.bqkv, nullptr,
                                   nullptr, L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
@@ -912,12 +914,12 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             t.n_split = 1;
             t.scale_div = (float)sqrt((double)cf.head_dim);
             t.span = span_cfg(cf);
-            t.n3 = cf.numerics;
+            t.rnd = cf.numerics;
             t.stats = L.attn_stats;
             const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0;
             if (mfma_attn)
                 HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, L.Oh, L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
-                                                   cf.head_dim, cf.n_ctx, t.scale_div, t.span, n3, L.ws, L.ws_floats,
+                                                   cf.head_dim, cf.n_ctx, t.scale_div, t.span, rnd, L.ws, L.ws_floats,
                                                    s));
             else
                 HIPCHK(c, launch_attn(t, m, s));
@@ -933,7 +935,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 of = L.Q;
                 X = L.Xc;
             }
-            if (n3)
+            if (rnd)
                 HIPCHK(c, launch_round_rows((float*)of, mr, qd, W.o.dtype, L.Oh, L.Ol, s));
             else if (W.o.wt && (last || !mfma_attn))  // the planes the tiled product reads
                 HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
@@ -946,10 +948,10 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, W.ffn_norm, cf.eps, L.Hf, L.Hh, L.Hl, s));
             else
                 HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
-            if (n3) HIPCHK(c, launch_round_rows(L.Hf, mr, cf.dim, W.gu.dtype, L.Hh, L.Hl, s));
+            if (rnd) HIPCHK(c, launch_round_rows(L.Hf, mr, cf.dim, W.gu.dtype, L.Hh, L.Hl, s));
             HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, lo(W.gu, L.Hl)}, mr, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
                                   L.ws, L.ws_floats, s));
-            if (n3) HIPCHK(c, launch_round_rows(L.Uf, mr, cf.ffn, W.down.dtype, L.Uh, L.Ul, s));
+            if (rnd) HIPCHK(c, launch_round_rows(L.Uf, mr, cf.ffn, W.down.dtype, L.Uh, L.Ul, s));
             // down product + residual; before another layer a split-K
             // reduction is fused with that layer's attention norm
             HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, lo(W.down, L.Ul)}, mr, X, cf.dim, nullptr, nullptr,
@@ -965,7 +967,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             // final RMSNorm of the compact rows, then one vocabulary product
             // whose rows land at their output indices
             HIPCHK(c, launch_rmsnorm_rows(L.Xc, L.out_norm, k, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
-            if (n3) HIPCHK(c, launch_round_rows(L.Hf, k, cf.dim, L.out.dtype, L.Hh, L.Hl, s));
+            if (rnd) HIPCHK(c, launch_round_rows(L.Hf, k, cf.dim, L.out.dtype, L.Hh, L.Hl, s));
             HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, lo(L.out, L.Hl)}, k, d_rows, cf.vocab, nullptr, nullptr,
                                   nullptr, L.ws, L.ws_floats, s, L.selo + sb));
         } else if (k > 0) {

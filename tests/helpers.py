@@ -56,9 +56,9 @@ SMALL_SPAN_ALL = SMALL_NEOX_BIAS.with_(name="small-window-sinks-temp", attn_wind
 # head_dim 64, the matrix-core prefill attention's size, on a small model
 SMALL_HD64 = SMALL.with_(name="small-hd64", dim=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn=704, seed=26)
 # llama.cpp's rounding points (numerics 1) on each weight type
-SMALL_N3 = SMALL.with_(name="small-f32-llamacpp", numerics=1, seed=23)
-SMALL_F16_N3 = SMALL_F16.with_(name="small-f16-llamacpp", numerics=1, seed=24)
-SMALL_Q8_N3 = SMALL_Q8.with_(name="small-q8_0-llamacpp", numerics=1, seed=25)
+SMALL_RND = SMALL.with_(name="small-f32-llamacpp", numerics=1, seed=23)
+SMALL_F16_RND = SMALL_F16.with_(name="small-f16-llamacpp", numerics=1, seed=24)
+SMALL_Q8_RND = SMALL_Q8.with_(name="small-q8_0-llamacpp", numerics=1, seed=25)
 # YaRN with a short original context, so that small heads have fast, ramped and slow pairs
 SMALL_YARN = SMALL.with_(name="small-yarn", yarn_factor=4.0, yarn_orig_ctx=400, rope_base=10000.0, seed=22)
 

@@ -19,8 +19,8 @@ import pytest
 import oracle
 import synth
 from helpers import (SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8,
-                     SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW, SMALL_YARN, SMALL_N3, SMALL_F16_N3,
-                     SMALL_Q8_N3, SMALL_HD64)
+                     SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW, SMALL_YARN, SMALL_RND, SMALL_F16_RND,
+                     SMALL_Q8_RND, SMALL_HD64)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -141,7 +141,7 @@ def run_decode(cfg, n_prompt, n_steps, prefill_gpu=False, prefill_ref=False):
 
 
 SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA, SMALL_FREQS, SMALL_WINDOW,
-          SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL, SMALL_YARN, SMALL_N3, SMALL_F16_N3, SMALL_Q8_N3]
+          SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL, SMALL_YARN, SMALL_RND, SMALL_F16_RND, SMALL_Q8_RND]
 
 
 @pytest.mark.parametrize("cfg", SMALLS, ids=lambda c: c.name)
@@ -201,6 +201,10 @@ def rel_rms(a, b):
 
 
 def test_llamacpp_numerics_1b_q8_agreement_level():
+    check_llamacpp_q8_agreement(synth.C4.with_(n_ctx=160, numerics=1))
+
+
+def check_llamacpp_q8_agreement(cfg):
     # With Q8_0 activations a last-bit difference in a product's input can move
     # its 8-bit code by one step; "What a Llama model computes, and why",
     # section 8, reports that from then on two correct implementations differ by
@@ -211,7 +215,6 @@ def test_llamacpp_numerics_1b_q8_agreement_level():
     # token-by-token decode, two summation orders of the same rounding) RMS of
     # the oracle's, the GPU's greedy token among the oracle's top 5, and layer
     # 0's K/V (computed before any code can differ) within 2 binary16 ulps.
-    cfg = synth.C4.with_(n_ctx=160, numerics=1)
     ts = synth.make_tensor_set(cfg)
     toks = synth.prompt(cfg, 40)
     gpu, ref, dec = llm.Model(cfg, ts), oracle.Model(cfg, ts), llm.Model(cfg, ts)

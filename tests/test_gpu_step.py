@@ -8,16 +8,18 @@ shapes cover every code path of that kernel: grouped-query heads with G = 1, 2,
 4 and 8 (G = 8 runs as two passes of four query heads), KV-head counts below,
 equal to and above the group count, short rows read by part of a wave, NEOX
 RoPE with bias, partial RoPE, all three weight types, splits long enough to need
-two attention chunks, and the 1B shape of the decode benchmark.
+two attention chunks, llama.cpp's rounding points (numerics 1: rounded product
+inputs and two attention passes), and the 1B shape of the decode benchmark.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from helpers import (SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8,
-                     SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW, SMALL_YARN)
-from test_gpu_parity import check_step, run_decode, tol
+from helpers import (SMALL, SMALL_F16, SMALL_F16_RND, SMALL_FREQS, SMALL_MHA, SMALL_RND, SMALL_NEOX_BIAS,
+                     SMALL_PARTIAL_ROPE, SMALL_Q8, SMALL_Q8_RND, SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW,
+                     SMALL_YARN)
+from test_gpu_parity import check_llamacpp_q8_agreement, check_step, run_decode, tol
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -42,7 +44,8 @@ G8 = SMALL.with_(name="small-g8", dim=256, n_heads=8, n_kv_heads=1, head_dim=32,
 KV16 = SMALL.with_(name="small-kv16", dim=512, n_heads=16, n_kv_heads=16, head_dim=32, ffn=320, seed=22)
 SHORT_ROWS_Q8 = SMALL_Q8.with_(name="small-q8-g1", n_heads=2, n_kv_heads=2, head_dim=64, seed=23)
 STEP_SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, G8, KV16, SHORT_ROWS_Q8, SMALL_FREQS,
-               SMALL_WINDOW, SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL, SMALL_YARN]
+               SMALL_WINDOW, SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL, SMALL_YARN, SMALL_RND, SMALL_F16_RND, SMALL_Q8_RND,
+               G8.with_(name="small-g8-q8_0-llamacpp", mat_dtype="q8_0", tied=True, numerics=1, seed=26)]
 
 
 @pytest.mark.parametrize("cfg", STEP_SMALLS, ids=lambda c: c.name)
@@ -98,14 +101,40 @@ def test_step_1b_q8_yarn_shape():
     run_decode(cfg, n_prompt=20, n_steps=4)
 
 
-def test_llamacpp_numerics_decode_on_the_launch_graph(monkeypatch):
-    # the persistent kernel computes with float activations only: with
-    # llama.cpp's rounding points the context decodes on the launch graph
-    monkeypatch.setenv("LLM_STEP", "persistent")
+def test_step_1b_f16_llamacpp_numerics():
+    # llama.cpp's rounding points in the F16 benchmark kernel (kind 2): binary16
+    # product inputs, q, and the two attention passes over 150 positions
+    cfg = synth.C3.with_(n_ctx=200, numerics=1)
+    load(cfg, kind=2).close()
+    run_decode(cfg, n_prompt=150, n_steps=4, prefill_gpu=True, prefill_ref=True)
+
+
+def test_step_1b_q8_llamacpp_numerics_agreement_level():
+    # the Q8_0 benchmark kernel (kind 2) with llama.cpp's rounding points, at
+    # the agreement level of Q8_0 activations (the launch-graph test explains it)
     cfg = synth.C4.with_(n_ctx=160, numerics=1)
-    m = llm.Model(cfg, synth.make_tensor_set(cfg))
-    assert llm.llm_op_step_kind(m.ctx) == 0
-    m.close()
+    load(cfg, kind=2).close()
+    check_llamacpp_q8_agreement(cfg)
+
+
+def test_step_llamacpp_numerics_generate_equals_decode_loop():
+    # an extra barrier per layer in this mode: the counters must stay in step
+    # over many launches, through llm_generate's device-side feedback as well
+    cfg = SMALL_Q8_RND
+    ts = synth.make_tensor_set(cfg)
+    toks = synth.prompt(cfg, 6)
+    a, b = load(cfg, ts), load(cfg, ts)
+    n1, n2 = a.prefill(toks), b.prefill(toks)
+    assert n1 == n2
+    gen = a.generate(n1, 40)
+    seq, t, pos = [], n2, len(toks)
+    for _ in range(40):
+        t = b.decode(t, pos)
+        seq.append(t)
+        pos += 1
+    assert gen.tolist() == seq
+    a.close()
+    b.close()
 
 
 def test_step_1b_f16_shape():
