@@ -84,6 +84,14 @@ int llm_op_time(llm_ctx* ctx, int32_t stage, int32_t layer, int32_t pos, int32_t
  * of 32. Returns the kind, or a negative LLM_ERR_* for a NULL context. */
 int llm_op_step_kind(llm_ctx* ctx);
 
+/* Rows per prefill batch: llm_prefill and llm_prefill_rows run a prompt
+ * through the layers in consecutive chunks of this many rows (the last one
+ * shorter), each chunk's rows attending to the cache rows before them and to
+ * the chunk's own rows up to themselves ("What a Llama model computes, and
+ * why", the prefill/decode section). A context's batch buffers hold this
+ * many rows. No context needed; never fails. */
+int llm_op_prefill_chunk(void);
+
 /* Wall-clock stamps (100 MHz device clock) that block 0 of the last decode-step
  * launch took at its start and after each of its 5*n_layers + 1 barriers:
  * stamp k+1 - stamp k is the time of phase k (per layer: QKV, attention,

@@ -30,7 +30,7 @@ ERRORS = {
 EXPORTS = ["llm_plan", "llm_load_weights", "llm_decode", "llm_prefill", "llm_prefill_rows", "llm_generate", "llm_reset", "llm_free",
            "llm_last_error", "llm_logits", "llm_kv_len", "llm_kv_read", "llm_op_qkv", "llm_op_attention", "llm_op_o",
            "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind", "llm_op_step_trace",
-           "llm_op_step_kind"]
+           "llm_op_step_kind", "llm_op_prefill_chunk"]
 STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_FFN_UP, STAGE_DOWN, STAGE_LOGITS, STAGE_STEP = range(7)
 
 
@@ -103,6 +103,8 @@ def lib():
         L.llm_op_step_trace.restype = ctypes.c_int
         L.llm_op_step_kind.argtypes = [vp]
         L.llm_op_step_kind.restype = ctypes.c_int
+        L.llm_op_prefill_chunk.argtypes = []
+        L.llm_op_prefill_chunk.restype = ctypes.c_int
         for f in ("llm_op_qkv", "llm_op_attention", "llm_op_o", "llm_op_ffn_up", "llm_op_down", "llm_op_logits",
                   "llm_op_kv_write", "llm_op_time", "llm_rewind"):
             getattr(L, f).restype = ctypes.c_int
@@ -280,6 +282,11 @@ def llm_op_step_kind(ctx) -> int:
     if r < 0:
         raise LlmError(r, "llm_op_step_kind")
     return r
+
+
+def llm_op_prefill_chunk() -> int:
+    """Rows per prefill batch."""
+    return int(lib().llm_op_prefill_chunk())
 
 
 def llm_op_step_trace(ctx, n_layers: int) -> np.ndarray:

@@ -165,7 +165,10 @@ constexpr int kMaxCols = 16384;
 constexpr int kMaxHeadDim = 256;
 constexpr int kMaxGroup = 8;  // n_heads / n_kv_heads must be 1, 2, 4 or 8
 constexpr int kMaxSplit = 256;      // position splits of the decode attention
-constexpr int kPrefillChunk = 512;  // tokens per prefill batch
+#ifndef LLM_PREFILL_CHUNK
+#define LLM_PREFILL_CHUNK 2048
+#endif
+constexpr int kPrefillChunk = LLM_PREFILL_CHUNK;  // tokens per prefill batch
 
 // Prologue of a vector product: where the input vector comes from.
 enum Pro : int {

@@ -295,7 +295,10 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     Arena S;
     S.base = (char*)sb;
     const int G = c->n_heads / c->n_kv_heads;
+    // rows of one prefill batch; the matrix-core products keep their binary16
+    // activation planes in whole tiles of kTileA rows
     const int C = kPrefillChunk;
+    static_assert(kPrefillChunk % kTileA == 0, "prefill batches hold whole activation tiles");
     L.n_split = decode_splits(c);
     L.st = (State*)S.take(sizeof(State));
     L.rope = (float2*)S.take((size_t)c->n_ctx * (c->rope_dims / 2) * sizeof(float2));
@@ -1171,6 +1174,8 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
     *h_ms = ms / (float)n_launch;
     return LLM_OK;
 }
+
+int llm_op_prefill_chunk(void) { return kPrefillChunk; }
 
 int llm_op_step_kind(llm_ctx* c) {
     int rc = check_ctx(c);

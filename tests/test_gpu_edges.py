@@ -17,6 +17,10 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import llama_family_decode_amd as llm
 
+    CHUNK = llm.llm_op_prefill_chunk()
+else:
+    CHUNK = 2048
+
 
 def prefill_both(cfg, ts, toks):
     g, r = llm.Model(cfg, ts), oracle.Model(cfg, ts)
@@ -24,11 +28,11 @@ def prefill_both(cfg, ts, toks):
     return g, r, nxt, g.logits(), r.prefill(toks)
 
 
-@pytest.mark.parametrize("n", [1, 512, 513])
+@pytest.mark.parametrize("n", [1, CHUNK, CHUNK + 1])
 def test_prompt_lengths_at_chunk_edges(monkeypatch, n):
-    # one token; exactly one 512-row chunk; one chunk plus a one-row chunk
+    # one token; exactly one full chunk; one chunk plus a one-row chunk
     monkeypatch.setenv("LLM_STEP", "graph")
-    cfg = SMALL_Q8.with_(n_ctx=520)
+    cfg = SMALL_Q8.with_(n_ctx=CHUNK + 8)
     ts = synth.make_tensor_set(cfg)
     g, r, nxt, got, want = prefill_both(cfg, ts, synth.prompt(cfg, n))
     check_step(cfg, got, want, nxt, f"prompt of {n}")

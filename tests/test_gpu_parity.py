@@ -160,11 +160,12 @@ def test_prefill_small(cfg):
                                                   name="small-hd64-f16", attn_window=700, attn_sinks=4)],
                          ids=lambda c: c.name)
 def test_prefill_spans_chunks_and_ragged_tail(cfg):
-    # 1100 rows: three chunks, the last ragged; with head_dim 64 the
-    # matrix-core attention of the later chunks splits each block's cache
-    # range over 2 and 3 blocks and merges them
-    cfg = cfg.with_(n_ctx=1200)
-    run_decode(cfg, n_prompt=1100, n_steps=3, prefill_gpu=True, prefill_ref=True)
+    # three chunks, the last one 76 rows; with head_dim 64 the matrix-core
+    # attention splits each block's cache range over several blocks and
+    # merges them
+    n = 2 * llm.llm_op_prefill_chunk() + 76
+    cfg = cfg.with_(n_ctx=n + 100)
+    run_decode(cfg, n_prompt=n, n_steps=3, prefill_gpu=True, prefill_ref=True)
 
 
 def test_prefill_1b_q8_shape():

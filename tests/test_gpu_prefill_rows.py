@@ -24,6 +24,8 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import llama_family_decode_amd as llm
 
+    CHUNK = llm.llm_op_prefill_chunk()
+
 
 @pytest.fixture(autouse=True)
 def graph_path(monkeypatch):
@@ -95,8 +97,10 @@ def test_rows_continue_a_sequence():
 
 
 def test_rows_across_chunks_and_ragged_tail():
-    cfg = SMALL_Q8.with_(n_ctx=1200)
-    run_rows(cfg, 1100, [1099, 0, 511, 512, 1023, 1024, 700, 700, 1098], n_steps=1)
+    # three chunks, the last one 76 rows; rows on both sides of each edge
+    n = 2 * CHUNK + 76
+    cfg = SMALL_Q8.with_(n_ctx=n + 24)
+    run_rows(cfg, n, [n - 1, 0, CHUNK - 1, CHUNK, 2 * CHUNK - 1, 2 * CHUNK, 700, 700, n - 2], n_steps=1)
 
 
 def test_rows_1b_q8_shape():
