@@ -880,7 +880,7 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // [split][2 + 64]; k_attn_prefill_merge then combines the splits.
 constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72, PA_PLD = 68;
 #ifndef LLM_PA_CHUNKS
-#define LLM_PA_CHUNKS 8
+#define LLM_PA_CHUNKS 32
 #endif
 constexpr int kPaChunks = LLM_PA_CHUNKS;
 
@@ -894,7 +894,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
     __shared__ __attribute__((aligned(16))) __half Vt[hd * PA_LD];      // [dim][position]
     __shared__ __attribute__((aligned(16))) float Ps[4][16 * PA_PLD];   // per wave [row][position]
     const int G = n_heads / n_kv_heads, TB = PA_ROWS / G;
-    const int g = blockIdx.y, z0 = blockIdx.x * TB;
+    // blocks are dealt out in index order, so the latest query rows (the most
+    // causal work) come first, for every KV head, and short blocks fill the tail
+    const int g = blockIdx.x, z0 = (gridDim.y - 1 - blockIdx.y) * TB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int qd = n_heads * hd;
     const int lr = lane & 15, lq = lane >> 4;
@@ -1151,7 +1153,7 @@ hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __ha
     if (head_dim != 64 || G < 1 || G > PA_ROWS || PA_ROWS % G || n_heads % n_kv_heads || n_q <= 0)
         return hipErrorInvalidValue;
     const int TB = PA_ROWS / G;
-    const dim3 grid((n_q + TB - 1) / TB, n_kv_heads);
+    const dim3 grid(n_kv_heads, (n_q + TB - 1) / TB);  // KV head, query-row block from the last
     if (rnd) {
         hipLaunchKernelGGL(k_attn_prefill_mfma<true>, grid, dim3(256), 0, s, Q, kc, vc, out, out_h, out_l, n_q, p0,
                            n_heads, n_kv_heads, n_ctx, scale_div, span, 0, nullptr);
