@@ -779,13 +779,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
     }
 }
 
-// Splits of K for an M x N product on tiles of tm x tn: enough blocks to cover
-// the compute units, each split at least 256 deep and a multiple of 32, the
-// partials within ws_floats.
+// Splits of K for an M x N product on tiles of tm x tn: K is halved until the
+// blocks fill three quarters of the 256 compute units (one block each; past
+// that a split adds a round of blocks plus the reduction and gains nothing),
+// each split at least 256 deep and a multiple of 32, the partials within
+// ws_floats.
+#ifndef LLM_SPLIT_FILL
+#define LLM_SPLIT_FILL 192
+#endif
 static int gemm_splits(int M, int N, int K, int tm, int tn, int smax, size_t ws_floats) {
     const int tiles = ((N + tn - 1) / tn) * ((M + tm - 1) / tm);
     int S = 1;
-    while (tiles * S < 256 && 2 * S <= smax && (K / (2 * S)) % 32 == 0 && K / (2 * S) >= 256 &&
+    while (tiles * S < LLM_SPLIT_FILL && 2 * S <= smax && (K / (2 * S)) % 32 == 0 && K / (2 * S) >= 256 &&
            (size_t)2 * S * M * N <= ws_floats)
         S *= 2;
     return S;

@@ -196,3 +196,9 @@ def test_null_context_calls():
     assert L.llm_reset(None) == -1
     assert L.llm_decode(None, 0, 0, None, None) == -1
     L.llm_free(None)
+
+
+def test_prefill_batches_hold_whole_activation_tiles():
+    # the batch buffers hold the products' binary16 input planes in 128-row tiles
+    c = llm.llm_op_prefill_chunk()
+    assert c >= 128 and c % 128 == 0
