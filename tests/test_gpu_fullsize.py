@@ -57,7 +57,9 @@ def layer0_kv_oracle(cfg, T, token, pos):
     for name, bias_name in (("blk.0.attn_k.weight", "blk.0.attn_k.bias"), ("blk.0.attn_v.weight", "blk.0.attn_v.bias")):
         t = T[name]
         w = oracle.dequantize(t.dtype, t.data, kvd * cfg.dim)
-        v = oracle.matvec(w, h, kvd, cfg.dim)
+        # the rounding mode rounds the product's input for the weight type
+        hx = oracle.round_input(h, t.dtype) if cfg.numerics else h
+        v = oracle.matvec(w, hx, kvd, cfg.dim)
         if bias_name in T:
             v = v + oracle.dequantize(0, T[bias_name].data, kvd)
         if name.endswith("attn_k.weight"):
@@ -92,11 +94,14 @@ def check_layer0_kv(cfg, T, model, tokens_at, max_ulps):
     return worst
 
 
-@pytest.mark.parametrize("cfg,ctx", [(synth.C4, 2048), (synth.C3, 2048), (synth.C4_LONG, 8192)],
-                         ids=["q8_0-ctx2048", "f16-ctx2048", "q8_0-ctx8192"])
+@pytest.mark.parametrize("cfg,ctx", [(synth.C4, 2048), (synth.C3, 2048), (synth.C4_LONG, 8192),
+                                     (synth.C3.with_(name="llama-1b-f16-llamacpp", numerics=1), 2048)],
+                         ids=["q8_0-ctx2048", "f16-ctx2048", "q8_0-ctx8192", "f16-llamacpp-ctx2048"])
 def test_decode_at_full_context_in_the_benchmarked_kernel(monkeypatch, cfg, ctx):
     # the three decode workloads: 1B Q8_0 with the tied F32 embedding at 2048
-    # (the headline) and at 8192 positions, 1B F16 at 2048
+    # (the headline) and at 8192 positions, 1B F16 at 2048; and the F16 one
+    # with llama.cpp's rounding points (the benchmark kernel's rounding
+    # variant: binary16 product inputs, two attention passes over 2048 rows)
     ts = synth.make_tensor_set(cfg)
     T = _tensors_by_name(ts)
     toks = synth.prompt(cfg, ctx)
