@@ -19,7 +19,8 @@ compiled for this shape). The line also reports
     Q8_0 at context 8192 (attention a larger share of the bytes), with
     Llama 3's RoPE frequency factors (rope_freqs.weight), at context 8192
     with a 1024-row sliding window plus 4 sink rows, with llama.cpp's
-    rounding points (on the launch graph), and with YaRN (factor 16);
+    rounding points (the step kernel's rounding variant), and with YaRN
+    (factor 16);
   - cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps 128] [--warmup 8]

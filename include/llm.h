@@ -100,8 +100,9 @@ typedef struct {
  * 1 rounds where llama.cpp rounds ("What a Llama model computes, and why",
  * section 8): a Q8_0 product's input to Q8_0 blocks (Example 8's quantizer),
  * an F16 product's input to binary16, q to binary16 before q.k, and the
- * softmax probabilities to binary16 before they weight V. Mode 1 decodes on
- * the launch graph (the persistent step kernel computes mode 0 only). */
+ * softmax probabilities to binary16 before they weight V. Both decode paths
+ * and prefill implement both modes (the persistent step kernel as a variant
+ * compiled for mode 1, with a second attention pass). */
 typedef struct {
     int32_t dim, n_layers, n_heads, n_kv_heads, head_dim, ffn, vocab, n_ctx, rope_dims, rope_neox;
     float eps, rope_base;
