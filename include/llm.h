@@ -98,7 +98,8 @@ typedef struct {
  *
  * numerics: 0 computes with float activations (the Java engine's numerics);
  * 1 rounds where llama.cpp rounds ("What a Llama model computes, and why",
- * section 8): a Q8_0 product's input to Q8_0 blocks (Example 8's quantizer),
+ * section 8): a Q8_0 product's input to Q8_0 blocks (the quantizer of
+ * "Loading GGUF with the FFM API", Example 8),
  * an F16 product's input to binary16, q to binary16 before q.k, and the
  * softmax probabilities to binary16 before they weight V. Both decode paths
  * and prefill implement both modes (the persistent step kernel as a variant
