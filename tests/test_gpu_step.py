@@ -45,7 +45,10 @@ KV16 = SMALL.with_(name="small-kv16", dim=512, n_heads=16, n_kv_heads=16, head_d
 SHORT_ROWS_Q8 = SMALL_Q8.with_(name="small-q8-g1", n_heads=2, n_kv_heads=2, head_dim=64, seed=23)
 STEP_SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, G8, KV16, SHORT_ROWS_Q8, SMALL_FREQS,
                SMALL_WINDOW, SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL, SMALL_YARN, SMALL_RND, SMALL_F16_RND, SMALL_Q8_RND,
-               G8.with_(name="small-g8-q8_0-llamacpp", mat_dtype="q8_0", tied=True, numerics=1, seed=26)]
+               G8.with_(name="small-g8-q8_0-llamacpp", mat_dtype="q8_0", tied=True, numerics=1, seed=26),
+               KV16.with_(name="small-kv16-f16-llamacpp", mat_dtype="f16", embd_dtype="f16", tied=True, numerics=1,
+                          seed=27),
+               SHORT_ROWS_Q8.with_(name="small-q8-g1-llamacpp", numerics=1, seed=28)]
 
 
 @pytest.mark.parametrize("cfg", STEP_SMALLS, ids=lambda c: c.name)
