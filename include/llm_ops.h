@@ -95,7 +95,9 @@ int llm_op_prefill_chunk(void);
 /* Wall-clock stamps (100 MHz device clock) that block 0 of the last decode-step
  * launch took at its start and after each of its 5*n_layers + 1 barriers:
  * stamp k+1 - stamp k is the time of phase k (per layer: QKV, attention,
- * split merge + output, gate/up, down; then the logits). h_out receives
+ * split merge + output, gate/up, down; then the logits; with numerics = 1 the
+ * barrier between the two attention passes takes no stamp, so both passes
+ * count as the attention phase). h_out receives
  * 5*n_layers + 2 values. Available only when the context was loaded with the
  * environment variable LLM_STEP_TRACE=1 and runs the persistent step kernel;
  * otherwise LLM_ERR_ARG. Waits. */
