@@ -59,6 +59,9 @@ SMALL_HD64 = SMALL.with_(name="small-hd64", dim=256, n_heads=4, n_kv_heads=2, he
 SMALL_RND = SMALL.with_(name="small-f32-llamacpp", numerics=1, seed=23)
 SMALL_F16_RND = SMALL_F16.with_(name="small-f16-llamacpp", numerics=1, seed=24)
 SMALL_Q8_RND = SMALL_Q8.with_(name="small-q8_0-llamacpp", numerics=1, seed=25)
+# the rounding mode with a window, sinks and the temperature on Q8_0 weights
+SMALL_SPAN_RND = SMALL_SPAN_ALL.with_(name="small-span-q8_0-llamacpp", mat_dtype="q8_0", tied=True, numerics=1,
+                                      seed=29)
 # YaRN with a short original context, so that small heads have fast, ramped and slow pairs
 SMALL_YARN = SMALL.with_(name="small-yarn", yarn_factor=4.0, yarn_orig_ctx=400, rope_base=10000.0, seed=22)
 

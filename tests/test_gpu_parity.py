@@ -20,7 +20,7 @@ import oracle
 import synth
 from helpers import (SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8,
                      SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW, SMALL_YARN, SMALL_RND, SMALL_F16_RND,
-                     SMALL_Q8_RND, SMALL_HD64)
+                     SMALL_Q8_RND, SMALL_HD64, SMALL_SPAN_RND)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -141,7 +141,7 @@ def run_decode(cfg, n_prompt, n_steps, prefill_gpu=False, prefill_ref=False):
 
 
 SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA, SMALL_FREQS, SMALL_WINDOW,
-          SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL, SMALL_YARN, SMALL_RND, SMALL_F16_RND, SMALL_Q8_RND]
+          SMALL_SINKS, SMALL_TEMP, SMALL_SPAN_ALL, SMALL_YARN, SMALL_RND, SMALL_F16_RND, SMALL_Q8_RND, SMALL_SPAN_RND]
 
 
 @pytest.mark.parametrize("cfg", SMALLS, ids=lambda c: c.name)
@@ -157,7 +157,10 @@ def test_prefill_small(cfg):
 @pytest.mark.parametrize("cfg", [SMALL_Q8, SMALL_SPAN_ALL.with_(attn_window=300, attn_temp_len=400),
                                  SMALL_HD64.with_(mat_dtype="q8_0", name="small-hd64-q8_0"),
                                  SMALL_HD64.with_(mat_dtype="f16", embd_dtype="f16", tied=True,
-                                                  name="small-hd64-f16", attn_window=700, attn_sinks=4)],
+                                                  name="small-hd64-f16", attn_window=700, attn_sinks=4),
+                                 SMALL_HD64.with_(mat_dtype="f16", embd_dtype="f16", tied=True, numerics=1,
+                                                  name="small-hd64-f16-llamacpp", attn_window=700, attn_sinks=4,
+                                                  attn_temp_scale=0.1, attn_temp_len=1000)],
                          ids=lambda c: c.name)
 def test_prefill_spans_chunks_and_ragged_tail(cfg):
     # three chunks, the last one 76 rows; with head_dim 64 the matrix-core

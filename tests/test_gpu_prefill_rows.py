@@ -15,7 +15,7 @@ import pytest
 import oracle
 import synth
 from helpers import (SMALL, SMALL_F16, SMALL_FREQS, SMALL_MHA, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_Q8,
-                     SMALL_F16_RND, SMALL_Q8_RND, SMALL_SPAN_ALL)
+                     SMALL_F16_RND, SMALL_Q8_RND, SMALL_SPAN_ALL, SMALL_SPAN_RND)
 from test_gpu_parity import check_kv, check_step, first_max, tol, top2_gap
 
 torch = pytest.importorskip("torch")
@@ -78,7 +78,7 @@ def run_rows(cfg, n_prompt, rows, n_steps=2, split=None):
 
 
 SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, SMALL_MHA, SMALL_FREQS, SMALL_SPAN_ALL,
-          SMALL_F16_RND, SMALL_Q8_RND]
+          SMALL_F16_RND, SMALL_Q8_RND, SMALL_SPAN_RND]
 
 
 @pytest.mark.parametrize("cfg", SMALLS, ids=lambda c: c.name)

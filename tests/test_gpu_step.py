@@ -18,7 +18,7 @@ import oracle
 import synth
 from helpers import (SMALL, SMALL_F16, SMALL_F16_RND, SMALL_FREQS, SMALL_MHA, SMALL_RND, SMALL_NEOX_BIAS,
                      SMALL_PARTIAL_ROPE, SMALL_Q8, SMALL_Q8_RND, SMALL_SINKS, SMALL_SPAN_ALL, SMALL_TEMP, SMALL_WINDOW,
-                     SMALL_YARN)
+                     SMALL_YARN, SMALL_SPAN_RND)
 from test_gpu_parity import check_llamacpp_q8_agreement, check_step, run_decode, tol
 
 torch = pytest.importorskip("torch")
@@ -48,7 +48,7 @@ STEP_SMALLS = [SMALL, SMALL_F16, SMALL_Q8, SMALL_NEOX_BIAS, SMALL_PARTIAL_ROPE, 
                G8.with_(name="small-g8-q8_0-llamacpp", mat_dtype="q8_0", tied=True, numerics=1, seed=26),
                KV16.with_(name="small-kv16-f16-llamacpp", mat_dtype="f16", embd_dtype="f16", tied=True, numerics=1,
                           seed=27),
-               SHORT_ROWS_Q8.with_(name="small-q8-g1-llamacpp", numerics=1, seed=28)]
+               SHORT_ROWS_Q8.with_(name="small-q8-g1-llamacpp", numerics=1, seed=28), SMALL_SPAN_RND]
 
 
 @pytest.mark.parametrize("cfg", STEP_SMALLS, ids=lambda c: c.name)
