@@ -235,7 +235,7 @@ def main():
                          "the HBM counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the decode path has no multi-GPU sharding in this build "
+        print("bench.py measures one GPU only: the decode path is not sharded across GPUs "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
