@@ -818,6 +818,12 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
     float* sc = sm;                 // [GC][CHUNK]
     float* wred = sm + GC * CHUNK;  // [kSW][GC][hd]
     bool have = pass != 2;          // the first chunk of the first item is prefetched
+    // Pass 2 of a block with one item, one chunk and one group of query heads
+    // (at most one item per block always holds) still has pass 1's V rows in
+    // vr and its e^(s - m) in sc: it reweights those instead of reloading K/V
+    // and recomputing the scores.
+    const bool reuse = pass == 2 && CH <= CHUNK && G <= GC;
+    if (reuse) have = true;
 
     for (int item = rk; item < nh * S; item += bg) {
         const int g = hlo + item / S, s = item % S;
@@ -868,6 +874,7 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                     const float M = xmax64(m);
                     const float L = xsum64(lane < S ? l * expf(m - M) : 0.f);
                     if (lane == 0) {
+                        alpha[h] = m_run[h];  // this split's max from pass 1, for the reuse
                         m_run[h] = M;
                         l_run[h] = L;
                     }
@@ -888,32 +895,42 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                         vr[i] = vpos;
                     }
                 }
-                // scores: each lane's partial dot over its 8 dimensions, then
-                // the sums over the LPP lanes of a position, every step
-                // applied to all of the block's values at once
-                float d[kStepAttn][GC];
+                if (!reuse) {
+                    // scores: each lane's partial dot over its 8 dimensions, then
+                    // the sums over the LPP lanes of a position, every step
+                    // applied to all of the block's values at once
+                    float d[kStepAttn][GC];
 #pragma unroll
-                for (int i = 0; i < kStepAttn; i++) {
-                    float kf[8];
-                    unpack8(kr[i], kf);
+                    for (int i = 0; i < kStepAttn; i++) {
+                        float kf[8];
+                        unpack8(kr[i], kf);
 #pragma unroll
-                    for (int h = 0; h < GC; h++) {
-                        float v = 0.f;
+                        for (int h = 0; h < GC; h++) {
+                            float v = 0.f;
 #pragma unroll
-                        for (int j = 0; j < 8; j++) v += qv[h][j] * kf[j];
-                        d[i][h] = v;
+                            for (int j = 0; j < 8; j++) v += qv[h][j] * kf[j];
+                            d[i][h] = v;
+                        }
+                    }
+                    lanes_sum_all<kStepAttn * GC>(&d[0][0], 1, LPP);
+#pragma unroll
+                    for (int i = 0; i < kStepAttn; i++) {
+                        const int t = pg + i * PPI;
+#pragma unroll
+                        for (int h = 0; h < GC; h++)
+                            if (sub == 0 && t < cn) sc[h * CHUNK + t] = d[i][h] / a.scale_div;
                     }
                 }
-                lanes_sum_all<kStepAttn * GC>(&d[0][0], 1, LPP);
-#pragma unroll
-                for (int i = 0; i < kStepAttn; i++) {
-                    const int t = pg + i * PPI;
-#pragma unroll
-                    for (int h = 0; h < GC; h++)
-                        if (sub == 0 && t < cn) sc[h * CHUNK + t] = d[i][h] / a.scale_div;
-                }
                 __syncthreads();
-                if (pass == 2) {
+                if (reuse) {
+                    // sc holds e^(s - m1) of pass 1: e^(s - M) / L = that * e^(m1 - M) / L
+                    for (int h = wave; h < GC; h += kSW) {
+                        const float f = expf(alpha[h] - m_run[h]) / l_run[h];
+                        for (int t = lane; t < cn; t += 64) sc[h * CHUNK + t] = round16(sc[h * CHUNK + t] * f);
+                    }
+                    __syncthreads();
+                    if (tid < GC) alpha[tid] = 1.f;
+                } else if (pass == 2) {
                     for (int h = wave; h < GC; h += kSW) {
                         const float M = m_run[h], L = l_run[h];
                         for (int t = lane; t < cn; t += 64) sc[h * CHUNK + t] = round16(expf(sc[h * CHUNK + t] - M) / L);
