@@ -149,31 +149,36 @@ int orc_dequantize(int32_t dtype, const void* data, int64_t n, float* out) {
     return ORC_ERR_DTYPE;
 }
 
-/* C roundf: halves away from zero ("The Forward Pass in Java", Example 2). */
-static int round_half_away(float v) { return (int)copysign(floor(fabs((double)v) + 0.5), (double)v); }
-
 /*
- * The reference Q8_0 quantiser of "The Forward Pass in Java", Example 2 and
- * "Loading GGUF with the FFM API", Example 8: per block of 32, d = amax / 127 in
- * float, id = 1/d (0 when d = 0), qs = roundf(x * id), d stored as fp16.
- * Used only to check the pages' worked Q8_0 examples; the workloads draw their
- * Q8_0 blocks directly.
+ * Q8_0 encoding of 32-value blocks ("Loading GGUF with the FFM API", the Q8_0
+ * section and Example 8's quantizer; "The Forward Pass in Java", Example 2).
+ * The block's scale is its largest magnitude divided by 127, in float. Each
+ * code is the value times the scale's float reciprocal, rounded to the nearest
+ * integer with halves away from zero (C's roundf is that rule); an all-zero
+ * block has scale 0 and codes 0. The stored scale is the binary16 rounding of
+ * the float scale. Used for the pages' worked Q8_0 examples and for the
+ * rounding mode's product inputs; the workloads draw their Q8_0 blocks
+ * directly.
  */
+static float q8_block_scale(const float* x) {
+    float amax = 0.0f;
+    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(x[j]));
+    return amax / 127.0f;
+}
+
+static void q8_encode_block(const float* x, uint8_t* blk) {
+    const float d = q8_block_scale(x);
+    const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+    int8_t* codes = (int8_t*)(blk + 2);
+    for (int j = 0; j < 32; j++) codes[j] = (int8_t)roundf(x[j] * inv);
+    const uint16_t dh = orc_f32_to_f16(d);
+    blk[0] = (uint8_t)dh;
+    blk[1] = (uint8_t)(dh >> 8);
+}
+
 int orc_quantize_q8_0(const float* x, int64_t n, uint8_t* out) {
     if (n % 32) return ORC_ERR_SHAPE;
-    for (int64_t b = 0; b < n / 32; b++) {
-        float amax = 0.0f;
-        for (int j = 0; j < 32; j++) {
-            float a = fabsf(x[32 * b + j]);
-            if (a > amax) amax = a;
-        }
-        float d = amax / 127.0f;
-        float id = d != 0.0f ? 1.0f / d : 0.0f;
-        uint16_t dh = orc_f32_to_f16(d);
-        out[34 * b] = (uint8_t)(dh & 0xff);
-        out[34 * b + 1] = (uint8_t)(dh >> 8);
-        for (int j = 0; j < 32; j++) out[34 * b + 2 + j] = (uint8_t)(int8_t)round_half_away(x[32 * b + j] * id);
-    }
+    for (int64_t b = 0; b < n / 32; b++) q8_encode_block(x + 32 * b, out + 34 * b);
     return ORC_OK;
 }
 
@@ -184,7 +189,7 @@ int orc_quantize_q8_0(const float* x, int64_t n, uint8_t* out) {
  * rounded to binary16; F32 weights see it unchanged. In place, n values. */
 int orc_round_input(float* x, int64_t n, int32_t dtype) {
     if (dtype == ORC_F16) {
-        for (int64_t i = 0; i < n; i++) x[i] = orc_f16_to_f32(orc_f32_to_f16(x[i]));
+        for (int64_t i = 0; i < n; i++) x[i] = orc_f16_to_f32(orc_f32_to_f16(x[i])); /* binary16 RNE */
         return ORC_OK;
     }
     if (dtype != ORC_Q8_0) return ORC_OK;
@@ -203,13 +208,20 @@ int orc_round_input(float* x, int64_t n, int32_t dtype) {
  * section 2).
  * ---------------------------------------------------------------------- */
 
-/* RMSNorm, Example 4: y = x / sqrt(mean(x^2) + eps) * w, with the sum of squares
- * accumulated in double and the scale rounded to float once. */
+/* RMSNorm ("The Forward Pass in Java", Example 4; "What a Llama model computes,
+ * and why", section 2): out = x * r * w with r = 1 / sqrt(mean(x^2) + eps). The
+ * mean square is accumulated in double over i ascending, r is evaluated in
+ * double and rounded to float once, and each output is (x_i * r) * w_i in
+ * float. */
+static double mean_square(const float* x, int32_t n) {
+    double acc = 0.0;
+    for (int32_t i = 0; i < n; i++) acc += (double)x[i] * (double)x[i];
+    return acc / (double)n;
+}
+
 void orc_rmsnorm(float* out, const float* x, const float* w, int32_t n, float eps) {
-    double ss = 0.0;
-    for (int32_t i = 0; i < n; i++) ss += (double)x[i] * x[i];
-    float scale = (float)(1.0 / sqrt(ss / (double)n + (double)eps));
-    for (int32_t i = 0; i < n; i++) out[i] = x[i] * scale * w[i];
+    const float r = (float)(1.0 / sqrt(mean_square(x, n) + (double)eps));
+    for (int32_t i = 0; i < n; i++) out[i] = x[i] * r * w[i];
 }
 
 /* One sequential fp32 dot product over i ascending (Example 5). */
@@ -325,12 +337,17 @@ void orc_rope(float* vec, int32_t n_heads, int32_t head_dim, int32_t rope_dims, 
 /* silu(z) = z / (1 + e^-z), Example 8. */
 float orc_silu(float z) { return z / (1.0f + (float)exp(-(double)z)); }
 
-/* Greedy choice, Example 9: the first index of the strict maximum. */
+/* Greedy choice, Example 9: the first index of the strict maximum (a later
+ * equal value never replaces the one found first). */
 int32_t orc_argmax(const float* v, int32_t n) {
-    int32_t best = 0;
+    int32_t at = 0;
+    float top = v[0];
     for (int32_t i = 1; i < n; i++)
-        if (v[i] > v[best]) best = i;
-    return best;
+        if (v[i] > top) {
+            top = v[i];
+            at = i;
+        }
+    return at;
 }
 
 /*
@@ -362,54 +379,86 @@ int orc_attends(int32_t t, int32_t pos, int32_t window, int32_t sinks) {
 }
 
 /* Scaled dot-product attention of one token over the F16 cache ("The Forward
- * Pass in Java", Example 7): q scaled by the temperature, scores q.k /
- * sqrt(head_dim) over the attended rows, softmax, weighted sum of V. Query
- * head h reads KV head h / (n_heads / n_kv_heads). weights (optional) gets
- * [n_heads][pos + 1] probabilities, 0 for rows not attended. */
-/* round16 (llama.cpp's rounding points, "What a Llama model computes, and
- * why", section 8): the scaled query is rounded to binary16 before q.k, and
- * each probability, after the softmax's division, before it weights V; weights
- * then receives the rounded probabilities. */
+ * Pass in Java", Example 7; "What a Llama model computes, and why", section 2):
+ * for query head h, reading KV head h / (n_heads / n_kv_heads),
+ *   s_t = (q_h . K_t) / sqrt(head_dim) over the attended rows t,
+ *   p_t = exp(s_t - max s) / sum exp(s_t - max s),
+ *   out_h = sum_t p_t V_t.
+ * q is first scaled by the temperature of pos (float). Each dot product is a
+ * float sum over the dimensions in order; sqrt(head_dim) is taken in double
+ * and rounded to float, and the score is divided by it; exp is taken in double
+ * and rounded to float; the sum of the exponentials is a float sum over t
+ * ascending; p_t is one float division; out_h accumulates p_t V_t over t
+ * ascending. weights (optional) gets [n_heads][pos + 1] probabilities, 0 for
+ * rows not attended.
+ *
+ * round16 (llama.cpp's rounding points, "What a Llama model computes, and
+ * why", section 8): the temperature-scaled query is rounded to binary16 before
+ * the dot products, and each p_t, after the division, before it weights V;
+ * weights then receives the rounded probabilities. */
+static float f16_round(float x) { return orc_f16_to_f32(orc_f32_to_f16(x)); }
+
+/* s_t for the attended rows of 0..pos (others untouched); returns max s_t. */
+static float attn_scores(float* s, const float* q, const uint16_t* kc, int32_t kv_dim, int32_t kv_off, int32_t hd,
+                         int32_t pos, int32_t window, int32_t sinks) {
+    const float root = (float)sqrt((double)hd);
+    float top = -INFINITY;
+    for (int32_t t = 0; t <= pos; t++) {
+        if (!orc_attends(t, pos, window, sinks)) continue;
+        const uint16_t* k = kc + (int64_t)t * kv_dim + kv_off;
+        float acc = 0.0f;
+        for (int32_t i = 0; i < hd; i++) acc += q[i] * orc_f16_to_f32(k[i]);
+        s[t] = acc / root;
+        top = fmaxf(top, s[t]);
+    }
+    return top;
+}
+
+/* s_t -> p_t in place over the attended rows; rows not attended get 0. */
+static void attn_softmax(float* s, float top, int32_t pos, int32_t window, int32_t sinks, int32_t round16) {
+    float total = 0.0f;
+    for (int32_t t = 0; t <= pos; t++)
+        if (orc_attends(t, pos, window, sinks)) {
+            s[t] = (float)exp((double)(s[t] - top));
+            total += s[t];
+        }
+    for (int32_t t = 0; t <= pos; t++) {
+        float p = orc_attends(t, pos, window, sinks) ? s[t] / total : 0.0f;
+        s[t] = round16 ? f16_round(p) : p;
+    }
+}
+
+/* out += p_t V_t over the attended rows, t ascending. */
+static void attn_weighted_sum(float* out, const float* p, const uint16_t* vc, int32_t kv_dim, int32_t kv_off,
+                              int32_t hd, int32_t pos, int32_t window, int32_t sinks) {
+    for (int32_t t = 0; t <= pos; t++) {
+        if (!orc_attends(t, pos, window, sinks)) continue;
+        const uint16_t* v = vc + (int64_t)t * kv_dim + kv_off;
+        for (int32_t i = 0; i < hd; i++) out[i] += p[t] * orc_f16_to_f32(v[i]);
+    }
+}
+
 void orc_attention_nx(float* out, const float* q, const uint16_t* kcache, const uint16_t* vcache, int32_t n_heads,
                       int32_t n_kv_heads, int32_t head_dim, int32_t pos, int32_t window, int32_t sinks,
                       float temp_scale, int32_t temp_len, int32_t round16, float* weights) {
-    int32_t kv_dim = n_kv_heads * head_dim, group = n_heads / n_kv_heads;
-    float denom = (float)sqrt((double)head_dim);
-    float tau = orc_attn_temp(pos, temp_scale, temp_len);
+    const int32_t kv_dim = n_kv_heads * head_dim, group = n_heads / n_kv_heads;
+    const float tau = orc_attn_temp(pos, temp_scale, temp_len);
     for (int32_t i = 0; i < n_heads * head_dim; i++) out[i] = 0.0f;
 #pragma omp parallel for schedule(static)
     for (int32_t h = 0; h < n_heads; h++) {
-        float* att = (float*)malloc(sizeof(float) * (size_t)(pos + 1));
-        float* qs = (float*)malloc(sizeof(float) * (size_t)head_dim);
-        int32_t kv_off = (h / group) * head_dim;
-        for (int32_t i = 0; i < head_dim; i++) qs[i] = tau * q[h * head_dim + i];
-        if (round16)
-            for (int32_t i = 0; i < head_dim; i++) qs[i] = orc_f16_to_f32(orc_f32_to_f16(qs[i]));
-        float mx = -INFINITY;
-        for (int32_t t = 0; t <= pos; t++) {
-            if (!orc_attends(t, pos, window, sinks)) continue;
-            float s = 0.0f;
-            for (int32_t i = 0; i < head_dim; i++) s += qs[i] * orc_f16_to_f32(kcache[(int64_t)t * kv_dim + kv_off + i]);
-            att[t] = s / denom;
-            if (att[t] > mx) mx = att[t];
+        float* s = (float*)malloc(sizeof(float) * (size_t)(pos + 1));
+        float* qh = (float*)malloc(sizeof(float) * (size_t)head_dim);
+        const int32_t kv_off = (h / group) * head_dim;
+        for (int32_t i = 0; i < head_dim; i++) {
+            qh[i] = tau * q[h * head_dim + i];
+            if (round16) qh[i] = f16_round(qh[i]);
         }
-        float sum = 0.0f;
-        for (int32_t t = 0; t <= pos; t++) {
-            if (!orc_attends(t, pos, window, sinks)) continue;
-            att[t] = (float)exp((double)(att[t] - mx));
-            sum += att[t];
-        }
-        for (int32_t t = 0; t <= pos; t++) {
-            int on = orc_attends(t, pos, window, sinks);
-            float a = on ? att[t] / sum : 0.0f;
-            if (round16) a = orc_f16_to_f32(orc_f32_to_f16(a));
-            if (weights) weights[(int64_t)h * (pos + 1) + t] = a;
-            if (!on) continue;
-            for (int32_t i = 0; i < head_dim; i++)
-                out[h * head_dim + i] += a * orc_f16_to_f32(vcache[(int64_t)t * kv_dim + kv_off + i]);
-        }
-        free(qs);
-        free(att);
+        const float top = attn_scores(s, qh, kcache, kv_dim, kv_off, head_dim, pos, window, sinks);
+        attn_softmax(s, top, pos, window, sinks, round16);
+        if (weights) memcpy(weights + (int64_t)h * (pos + 1), s, sizeof(float) * (size_t)(pos + 1));
+        attn_weighted_sum(out + h * head_dim, s, vcache, kv_dim, kv_off, head_dim, pos, window, sinks);
+        free(qh);
+        free(s);
     }
 }
 
