@@ -859,6 +859,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
     hipStream_t s = c->stream;
     const int qd = c->qd, kvd = c->kvd, qkvd = qd + 2 * kvd;
     const int nr = (int)rows_out.size();
+    int rc = LLM_OK;
     const bool rnd = cf.numerics != 0;  // llama.cpp's rounding of every product input
     // with rounded inputs an F16 product's lo plane is zero: one matrix-core pass
     // (a rounded Q8_0 input, f16(d) * code, still needs both planes)
@@ -926,57 +927,64 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                                                    s));
             else
                 HIPCHK(c, launch_attn(t, m, s));
-            int mr = m;
-            const float* of = L.Of;
-            float* X = L.X;
-            if (last) {
-                if (k == 0) break;  // no wanted row here: the K/V rows were all the last layer owed
-                // gather the wanted rows' attention outputs and residuals
-                HIPCHK(c, launch_gather_rows(L.Of, qd, L.sel + sb, k, L.Q, s));
-                HIPCHK(c, launch_gather_rows(L.X, cf.dim, L.sel + sb, k, L.Xc, s));
-                mr = k;
-                of = L.Q;
-                X = L.Xc;
+            // output product + residual, RMSNorm, gate/up + SwiGLU, down +
+            // residual over mr rows (attention outputs `of`, residuals X)
+            auto post_attention = [&](const float* of, float* X, int mr) -> int {
+                if (rnd)
+                    HIPCHK(c, launch_round_rows((float*)of, mr, qd, W.o.dtype, L.Oh, L.Ol, s));
+                else if (W.o.wt && (last || !mfma_attn))  // the planes the tiled product reads
+                    HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
+                // a split-K output product's reduction is fused with the FFN norm
+                int S = 0;
+                HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, lo(W.o, L.Ol)}, mr, X, cf.dim, nullptr, nullptr,
+                                      nullptr, L.ws, L.ws_floats, s, nullptr, &S));
+                if (S)
+                    HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, W.ffn_norm, cf.eps, L.Hf, L.Hh, L.Hl, s));
+                else
+                    HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+                if (rnd) HIPCHK(c, launch_round_rows(L.Hf, mr, cf.dim, W.gu.dtype, L.Hh, L.Hl, s));
+                HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, lo(W.gu, L.Hl)}, mr, L.Uf, cf.ffn, nullptr, L.Uh,
+                                      L.Ul, L.ws, L.ws_floats, s));
+                if (rnd) HIPCHK(c, launch_round_rows(L.Uf, mr, cf.ffn, W.down.dtype, L.Uh, L.Ul, s));
+                // before another layer a split-K down product's reduction is
+                // fused with that layer's attention norm
+                HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, lo(W.down, L.Ul)}, mr, X, cf.dim, nullptr,
+                                      nullptr, nullptr, L.ws, L.ws_floats, s, nullptr, last ? nullptr : &S));
+                if (!last && S) {
+                    HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, L.layers[l + 1].attn_norm, cf.eps, L.Hf,
+                                                      L.Hh, L.Hl, s));
+                    normed = true;
+                }
+                return LLM_OK;
+            };
+            if (!last) {
+                if ((rc = post_attention(L.Of, L.X, m))) return rc;
+                continue;
             }
-            if (rnd)
-                HIPCHK(c, launch_round_rows((float*)of, mr, qd, W.o.dtype, L.Oh, L.Ol, s));
-            else if (W.o.wt && (last || !mfma_attn))  // the planes the tiled product reads
-                HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
-            // output product + residual; a split-K product's reduction is fused
-            // with the FFN norm that follows
-            int S = 0;
-            HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, lo(W.o, L.Ol)}, mr, X, cf.dim, nullptr, nullptr, nullptr,
-                                  L.ws, L.ws_floats, s, nullptr, &S));
-            if (S)
-                HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, W.ffn_norm, cf.eps, L.Hf, L.Hh, L.Hl, s));
-            else
-                HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
-            if (rnd) HIPCHK(c, launch_round_rows(L.Hf, mr, cf.dim, W.gu.dtype, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, lo(W.gu, L.Hl)}, mr, L.Uf, cf.ffn, nullptr, L.Uh, L.Ul,
-                                  L.ws, L.ws_floats, s));
-            if (rnd) HIPCHK(c, launch_round_rows(L.Uf, mr, cf.ffn, W.down.dtype, L.Uh, L.Ul, s));
-            // down product + residual; before another layer a split-K
-            // reduction is fused with that layer's attention norm
-            HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, lo(W.down, L.Ul)}, mr, X, cf.dim, nullptr, nullptr,
-                                  nullptr, L.ws, L.ws_floats, s, nullptr, last ? nullptr : &S));
-            if (!last && S) {
-                HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, L.layers[l + 1].attn_norm, cf.eps, L.Hf,
-                                                  L.Hh, L.Hl, s));
-                normed = true;
+            // The last layer: only the wanted rows go on, gathered into compact
+            // batches of at most one chunk's rows (repeated rows can make a
+            // chunk want more rows than it holds); each batch then gets the
+            // final RMSNorm and the vocabulary product.
+            for (int b0 = 0; b0 < k; b0 += kPrefillChunk) {
+                const int kb = k - b0 < kPrefillChunk ? k - b0 : kPrefillChunk;
+                HIPCHK(c, launch_gather_rows(L.Of, qd, L.sel + sb + b0, kb, L.Q, s));
+                HIPCHK(c, launch_gather_rows(L.X, cf.dim, L.sel + sb + b0, kb, L.Xc, s));
+                if ((rc = post_attention(L.Q, L.Xc, kb))) return rc;
+                if (d_rows) {
+                    // product rows land at their output indices
+                    HIPCHK(c, launch_rmsnorm_rows(L.Xc, L.out_norm, kb, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+                    if (rnd) HIPCHK(c, launch_round_rows(L.Hf, kb, cf.dim, L.out.dtype, L.Hh, L.Hl, s));
+                    HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, lo(L.out, L.Hl)}, kb, d_rows, cf.vocab,
+                                          nullptr, nullptr, nullptr, L.ws, L.ws_floats, s, L.selo + sb + b0));
+                } else {
+                    // the one wanted row (the prompt's last) through the decode
+                    // vocabulary kernel and argmax
+                    HIPCHK(c, launch_set_state(L.st, 0, p0 + m - 1, 0, s));
+                    HIPCHK(c, enqueue_logits(c, L.Xc, s));
+                }
             }
         }
         c->len += m;
-        if (k > 0 && d_rows) {
-            // final RMSNorm of the compact rows, then one vocabulary product
-            // whose rows land at their output indices
-            HIPCHK(c, launch_rmsnorm_rows(L.Xc, L.out_norm, k, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
-            if (rnd) HIPCHK(c, launch_round_rows(L.Hf, k, cf.dim, L.out.dtype, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, lo(L.out, L.Hl)}, k, d_rows, cf.vocab, nullptr, nullptr,
-                                  nullptr, L.ws, L.ws_floats, s, L.selo + sb));
-        } else if (k > 0) {
-            HIPCHK(c, launch_set_state(L.st, 0, c->len - 1, 0, s));
-            HIPCHK(c, enqueue_logits(c, L.Xc, s));
-        }
     }
     return LLM_OK;
 }
@@ -1201,5 +1209,6 @@ int llm_rewind(llm_ctx* c, int32_t len) {
     c->len = len;
     return LLM_OK;
 }
+
 
 }  // extern "C"

@@ -103,6 +103,16 @@ def test_rows_across_chunks_and_ragged_tail():
     run_rows(cfg, n, [n - 1, 0, CHUNK - 1, CHUNK, 2 * CHUNK - 1, 2 * CHUNK, 700, 700, n - 2], n_steps=1)
 
 
+def test_rows_repeated_past_one_chunk():
+    # more wanted rows in one chunk than the chunk holds (repeats): the last
+    # layer runs them in batches of at most one chunk
+    n = CHUNK + 52
+    rows = [5, CHUNK - 1, 0] * ((CHUNK + 600) // 3) + [CHUNK, n - 1]
+    cfg = SMALL_Q8.with_(n_ctx=len(rows) + 8)
+    assert cfg.n_ctx > CHUNK + 600
+    run_rows(cfg, n, rows, n_steps=1)
+
+
 def test_rows_1b_q8_shape():
     cfg = synth.C4.with_(n_ctx=160)
     run_rows(cfg, 40, [39, 0, 17, 38], n_steps=1)
