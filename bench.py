@@ -86,33 +86,83 @@ def read_traffic():
     return None
 
 
-def cpu_baseline(cfg, budget_s=15.0):
-    """The oracle, untuned, on a bounded sample of the decode workload: a short
-    prompt prefill (not timed), then decode steps until the time budget."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, ctx_len, budget_s=8.0):
+    """The oracle, untuned, on bounded samples of the same workloads:
+      - decode steps of the headline model at positions ctx_len.. over a
+        ctx_len-row cache (seeded binary16 rows written into the oracle's
+        cache: the oracle's step time does not depend on the cached values,
+        and its own 2048-row prompt pass takes minutes), with every thread
+        the process may use and with one thread;
+      - the prompt pass of the Qwen2-style F16 model on the first rows of its
+        512-id prompt, with every thread and with one thread.
+    Each sample runs about budget_s seconds (at least one step)."""
     import numpy as np
 
     import oracle
     import synth
 
+    def timed(fn, budget, cap):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn(n)
+            n += 1
+            if time.perf_counter() - t0 > budget or n >= cap:
+                return n, time.perf_counter() - t0
+
+    all_threads = oracle.max_threads()
     ts = synth.make_tensor_set(cfg)
     m = oracle.Model(cfg, ts)
     del ts
-    toks = synth.prompt(cfg, 16)
-    logits = m.prefill(toks)
-    pos, n, t0 = 16, 0, time.perf_counter()
-    while True:
-        tok = oracle.argmax(logits)
-        logits = m.forward(tok, pos)
-        pos += 1
-        n += 1
-        if time.perf_counter() - t0 > budget_s or n >= 1024:
-            break
-    dt = time.perf_counter() - t0
+    kvd = cfg.kv_dim
+    for l in range(cfg.n_layers):
+        k = synth.normal_f16_bits(cfg.seed, f"cpu-baseline-k{l}", ctx_len * kvd, std=1.0).reshape(ctx_len, kvd)
+        v = synth.normal_f16_bits(cfg.seed, f"cpu-baseline-v{l}", ctx_len * kvd, std=1.0).reshape(ctx_len, kvd)
+        for p in range(ctx_len):
+            m.kv_write(l, p, k[p], v[p])
+    toks = synth.prompt(cfg, 64, stream="cpu-baseline")
+    decode = {}
+    for threads in (all_threads, 1):
+        oracle.set_threads(threads)
+        m.set_len(ctx_len)
+        n, dt = timed(lambda i: m.forward(int(toks[i % 64]), ctx_len + i), budget_s, 64)
+        decode[threads] = (n, dt)
     m.close()
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    return {"value": round(n / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} greedy decode steps of the same 1B Q8_0 model at positions 16..{15 + n} after a 16-id "
-                      f"oracle prefill (cache 16 positions instead of 2048; attention is under 3% of the bytes)"}
+    c5 = synth.C5
+    ts = synth.make_tensor_set(c5)
+    pm = oracle.Model(c5, ts)
+    del ts
+    p5 = synth.prompt(c5, 512)
+    prefill = {}
+    for threads, rows in ((all_threads, 32), (1, 4)):
+        oracle.set_threads(threads)
+        pm.reset()
+        t0 = time.perf_counter()
+        pm.prefill(p5[:rows])
+        prefill[threads] = (rows, time.perf_counter() - t0)
+    pm.close()
+    oracle.set_threads(all_threads)
+    n_all, dt_all = decode[all_threads]
+    n_one, dt_one = decode[1]
+    return {"value": round(n_all / dt_all, 4), "unit": "tok/s", "cores": all_threads, "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "one_thread_tok_s": round(n_one / dt_one, 4),
+            "prefill_tok_s": round(prefill[all_threads][0] / prefill[all_threads][1], 3),
+            "prefill_one_thread_tok_s": round(prefill[1][0] / prefill[1][1], 3),
+            "sample": f"decode: {n_all} steps on {all_threads} threads and {n_one} on 1 thread of the same 1B Q8_0 "
+                      f"model at positions {ctx_len}.. over a {ctx_len}-row cache (seeded binary16 rows written "
+                      f"into the oracle's cache); prefill: the first {prefill[all_threads][0]} rows "
+                      f"({all_threads} threads) and {prefill[1][0]} rows (1 thread) of the 512-id prompt of the "
+                      f"Qwen2-style F16 1B model, as one prompt pass"}
 
 
 def measure_prefill(llm, synth, np, torch, reps=5):
@@ -339,8 +389,9 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg)
-        print(f"# cpu oracle {cpu['value']} tok/s on {cpu['cores']} threads", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, ctx_len)
+        print(f"# cpu oracle {cpu['value']} tok/s on {cpu['cores']} threads ({cpu['one_thread_tok_s']} on 1), "
+              f"prefill {cpu['prefill_tok_s']} tok/s; {cpu['cpu_model']}", file=sys.stderr, flush=True)
 
     line = {
         "metric": "decode tok/s (1B-shape Q8_0, tied F32 embedding, KV cache prefilled to 2048)",

@@ -97,6 +97,12 @@ def lib():
         L.orc_kv_read.argtypes = [vp, i32, i32, vp, vp]
         L.orc_free.argtypes = [vp]
         L.orc_free.restype = None
+        L.orc_kv_write.argtypes = [vp, i32, i32, vp, vp]
+        L.orc_set_len.argtypes = [vp, i32]
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_set_threads.restype = None
+        L.orc_max_threads.argtypes = []
+        L.orc_max_threads.restype = i32
         L.orc_weights_per_layer.argtypes = [i64, i64, i64]
         L.orc_weights_per_layer.restype = i64
         _lib = L
@@ -244,6 +250,15 @@ def attends(t: int, pos: int, window: int, sinks: int) -> bool:
     return bool(lib().orc_attends(t, pos, window, sinks))
 
 
+def set_threads(n: int):
+    """Threads of the oracle's OpenMP loops (its results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
 def weights_per_layer(dim: int, kv_dim: int, ffn: int) -> int:
     return int(lib().orc_weights_per_layer(dim, kv_dim, ffn))
 
@@ -336,6 +351,22 @@ class Model:
 
     def kv_len(self) -> int:
         return int(lib().orc_kv_len(self.h))
+
+    def kv_write(self, layer: int, pos: int, k_bits: np.ndarray, v_bits: np.ndarray):
+        """Write binary16 K and V bits of one layer at one position."""
+        k = np.ascontiguousarray(k_bits, np.uint16)
+        v = np.ascontiguousarray(v_bits, np.uint16)
+        kvd = self.config.n_kv_heads * self.config.head_dim
+        assert k.size == kvd and v.size == kvd
+        rc = lib().orc_kv_write(self.h, int(layer), int(pos), _p(k), _p(v))
+        if rc:
+            raise ValueError(f"orc_kv_write: {rc}")
+
+    def set_len(self, n: int):
+        """Declare cache rows 0..n-1 valid."""
+        rc = lib().orc_set_len(self.h, int(n))
+        if rc:
+            raise ValueError(f"orc_set_len: {rc}")
 
     def kv_read(self, layer: int, pos: int):
         kvd = self.config.n_kv_heads * self.config.head_dim

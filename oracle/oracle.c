@@ -21,6 +21,7 @@
  * against values the pages print, closed forms, invariants and brute force.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -811,6 +812,31 @@ int orc_kv_read(const orc_model* m, int32_t layer, int32_t pos, uint16_t* k, uin
     memcpy(v, m->vcache + base, (size_t)kvd * 2);
     return ORC_OK;
 }
+
+/* Binary16 bits of K and V written to one layer at one position (kv_dim
+ * values each): a cache filled from outside, for timing decode steps at a
+ * given cache length without running the prompt first. */
+int orc_kv_write(orc_model* m, int32_t layer, int32_t pos, const uint16_t* k, const uint16_t* v) {
+    if (layer < 0 || layer >= m->c.n_layers || pos < 0 || pos >= m->c.n_ctx) return ORC_ERR_ARG;
+    int32_t kvd = m->c.n_kv_heads * m->c.head_dim;
+    size_t base = ((size_t)layer * (size_t)m->c.n_ctx + (size_t)pos) * (size_t)kvd;
+    memcpy(m->kcache + base, k, (size_t)kvd * 2);
+    memcpy(m->vcache + base, v, (size_t)kvd * 2);
+    return ORC_OK;
+}
+
+/* Declares cache rows 0..len-1 valid (0 <= len <= n_ctx). */
+int orc_set_len(orc_model* m, int32_t len) {
+    if (len < 0 || len > m->c.n_ctx) return ORC_ERR_ARG;
+    m->len = len;
+    return ORC_OK;
+}
+
+/* Threads of the OpenMP loops (the results do not depend on it). */
+void orc_set_threads(int32_t n) {
+    if (n > 0) omp_set_num_threads(n);
+}
+int32_t orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* Size of one layer in weights ("The Forward Pass in Java", Example 1):
  * 2 d^2 + 2 d kv_dim + 3 d ffn + 2 d (biases not counted). */
