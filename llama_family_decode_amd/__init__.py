@@ -299,6 +299,19 @@ def llm_rewind(ctx, length: int):
     _check(lib().llm_rewind(ctx, int(length)), ctx)
 
 
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime torch has loaded (for copies out of library-owned buffers)."""
+    global _hip_rt
+    if _hip_rt is None:
+        _hip_rt = ctypes.CDLL("libamdhip64.so")
+        _hip_rt.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _hip_rt.hipMemcpy.restype = ctypes.c_int
+    return _hip_rt
+
+
 class Model:
     """A loaded model on one GPU. `tensors` are objects with name/dtype/ne/data."""
 
@@ -354,8 +367,20 @@ class Model:
         return llm_generate(self.ctx, token, n_steps)
 
     def logits(self) -> np.ndarray:
+        """The copy of the logits the last decode/prefill call made (d_logits)."""
         torch.cuda.synchronize(self.device)
         return self.logits_buf.cpu().numpy()
+
+    def ctx_logits(self) -> np.ndarray:
+        """The context's own logits buffer (llm_logits): the last decode,
+        prefill or generate step's logits."""
+        torch.cuda.synchronize(self.device)
+        out = np.empty(self.vocab, np.float32)
+        rc = _hip().hipMemcpy(ctypes.c_void_p(out.ctypes.data), ctypes.c_void_p(llm_logits(self.ctx)),
+                              ctypes.c_size_t(out.nbytes), 2)  # hipMemcpyDeviceToHost
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpy failed: {rc}")
+        return out
 
     def reset(self):
         llm_reset(self.ctx)

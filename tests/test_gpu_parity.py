@@ -299,8 +299,10 @@ def test_generate_equals_decode_loop():
         pos += 1
     assert gen.tolist() == seq
     assert a.kv_len() == b.kv_len() == len(toks) + 20
-    # the last step's logits of both loops, bit for bit
-    assert np.array_equal(a.logits().view(np.uint32), b.logits().view(np.uint32))
+    # the last step's logits of both loops (the context's own buffers), bit for bit
+    la, lb = a.ctx_logits(), b.ctx_logits()
+    assert np.array_equal(lb.view(np.uint32), b.logits().view(np.uint32))
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
 
 
 def test_determinism_bit_exact():
