@@ -40,6 +40,26 @@ int llm_op_qkv(llm_ctx* ctx, int32_t layer, int32_t pos, const float* d_x, float
  * (Example 7); writes n_heads*head_dim floats to d_out. */
 int llm_op_attention(llm_ctx* ctx, int32_t layer, int32_t pos, const float* d_q, float* d_out);
 
+/* Allocation-free variant of llm_op_attention, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, kernels and result as
+ * llm_op_attention; what those kernels write besides d_out (the position
+ * state, the per-split partials (m, l, o) and, with numerics = 1, the span
+ * maxima and sums) goes to a file-scope device array of
+ * LLM_NOALLOC_SCRATCH_BYTES bytes that each device holds until the process
+ * ends, instead of the context's scratch arena. Nothing is allocated: no
+ * hipMalloc, hipFree or allocating library call. Nothing in the array needs
+ * to start at zero (every value a call reads, the call writes first).
+ * Requires the context's device to be the current device (else LLM_ERR_ARG);
+ * returns LLM_ERR_LIMIT when the context's shape needs more than the array:
+ * 256 + n_split * n_kv_heads * (n_heads / n_kv_heads) * (head_dim + 2) * 4
+ * + n_heads * 8 bytes (each part rounded up to 256 bytes), n_split = 512 /
+ * n_kv_heads position splits. Every call on one device shares that device's
+ * array, so calls that overlap on one device (from other streams or threads)
+ * race; calls in order on one stream do not. */
+#define LLM_NOALLOC_SCRATCH_BYTES (4u << 20)
+int llm_op_attention_noalloc(llm_ctx* ctx, int32_t layer, int32_t pos, const float* d_q, float* d_out);
+
 /* Output stage: d_x (dim floats) += W_o d_in (d_in: n_heads*head_dim floats). */
 int llm_op_o(llm_ctx* ctx, int32_t layer, const float* d_in, float* d_x);
 

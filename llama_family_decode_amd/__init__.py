@@ -30,7 +30,7 @@ ERRORS = {
 EXPORTS = ["llm_plan", "llm_load_weights", "llm_decode", "llm_prefill", "llm_prefill_rows", "llm_generate", "llm_reset", "llm_free",
            "llm_last_error", "llm_logits", "llm_kv_len", "llm_kv_read", "llm_op_qkv", "llm_op_attention", "llm_op_o",
            "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind", "llm_op_step_trace",
-           "llm_op_step_kind", "llm_op_prefill_chunk"]
+           "llm_op_step_kind", "llm_op_prefill_chunk", "llm_op_attention_noalloc"]
 STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_FFN_UP, STAGE_DOWN, STAGE_LOGITS, STAGE_STEP = range(7)
 
 
@@ -92,6 +92,7 @@ def lib():
         L.llm_kv_read.restype = ctypes.c_int
         L.llm_op_qkv.argtypes = [vp, i32, i32, vp, vp]
         L.llm_op_attention.argtypes = [vp, i32, i32, vp, vp]
+        L.llm_op_attention_noalloc.argtypes = [vp, i32, i32, vp, vp]
         L.llm_op_o.argtypes = [vp, i32, vp, vp]
         L.llm_op_ffn_up.argtypes = [vp, i32, vp, vp]
         L.llm_op_down.argtypes = [vp, i32, vp, vp]
@@ -105,7 +106,7 @@ def lib():
         L.llm_op_step_kind.restype = ctypes.c_int
         L.llm_op_prefill_chunk.argtypes = []
         L.llm_op_prefill_chunk.restype = ctypes.c_int
-        for f in ("llm_op_qkv", "llm_op_attention", "llm_op_o", "llm_op_ffn_up", "llm_op_down", "llm_op_logits",
+        for f in ("llm_op_qkv", "llm_op_attention", "llm_op_attention_noalloc", "llm_op_o", "llm_op_ffn_up", "llm_op_down", "llm_op_logits",
                   "llm_op_kv_write", "llm_op_time", "llm_rewind"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -243,6 +244,10 @@ def llm_op_qkv(ctx, layer: int, pos: int, d_x: int, d_q: int):
 
 def llm_op_attention(ctx, layer: int, pos: int, d_q: int, d_out: int):
     _check(lib().llm_op_attention(ctx, layer, pos, d_q, d_out), ctx)
+
+
+def llm_op_attention_noalloc(ctx, layer: int, pos: int, d_q: int, d_out: int):
+    _check(lib().llm_op_attention_noalloc(ctx, layer, pos, d_q, d_out), ctx)
 
 
 def llm_op_o(ctx, layer: int, d_in: int, d_x: int):

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -387,6 +388,7 @@ struct llm_ctx {
     Layout L;
     int32_t len = 0;
     bool poisoned = false;
+    int device = -1;  // the device current at load
     std::string err;
     int g_qkv, g_o, g_gu, g_down, g_vocab;
     bool use_step = false;  // persistent step kernel (else the launch graph)
@@ -635,6 +637,11 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
     c->kvd = cfg->n_kv_heads * cfg->head_dim;
     c->G = cfg->n_heads / cfg->n_kv_heads;
     c->stream = (hipStream_t)hip_stream;
+    if (hipGetDevice(&c->device) != hipSuccess) {
+        release(c);
+        g_load_error = "hipGetDevice failed";
+        return LLM_ERR_DEVICE;
+    }
     const char* ng = getenv("LLM_NO_GRAPH");
     c->use_graph = !(ng && ng[0] == '1');
     auto bail = [&](int code, const std::string& msg) {
@@ -1210,5 +1217,81 @@ int llm_rewind(llm_ctx* c, int32_t len) {
     return LLM_OK;
 }
 
+// ------------------------------------------------- allocation-free attention
+// llm_op_attention_noalloc keeps everything its kernels write besides the
+// output in this array (each device holds its own copy until the process
+// ends): the position state, the split partials (m, l, o) and, with the
+// rounding mode, the span maxima and sums.
+}  // extern "C"
+
+static __device__ __align__(256) unsigned char scratch[LLM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};  // the array's device address on each device
+
+// The array's address on `dev` (which must be current): looked up once per
+// device with hipGetSymbolAddress. Host code never uses the array's own name
+// as an address.
+hipError_t noalloc_scratch(int dev, char** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_dev[dev] = p;
+    }
+    *out = (char*)g_scratch_dev[dev];
+    return hipSuccess;
+}
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+}  // namespace
+
+extern "C" {
+
+int llm_op_attention_noalloc(llm_ctx* c, int32_t layer, int32_t pos, const float* d_q, float* d_out) {
+    int rc = check_layer(c, layer);
+    if (rc) return rc;
+    if (pos < 0 || pos >= c->cfg.n_ctx || !d_q || !d_out) return fail(c, LLM_ERR_ARG, "bad position or pointer");
+    const llm_config& cf = c->cfg;
+    const int n_split = c->L.n_split;
+    // the state, the split partials of one query, the span statistics of one query
+    const size_t st_bytes = round256(sizeof(State));
+    const size_t part_bytes = round256((size_t)n_split * cf.n_kv_heads * c->G * (cf.head_dim + 2) * sizeof(float));
+    const size_t stats_bytes = round256((size_t)cf.n_heads * 2 * sizeof(float));
+    if (st_bytes + part_bytes + stats_bytes > (size_t)LLM_NOALLOC_SCRATCH_BYTES)
+        return fail(c, LLM_ERR_LIMIT, "the attention's split partials exceed the allocation-free scratch");
+    int dev = -1;
+    HIPCHK(c, hipGetDevice(&dev));
+    if (dev != c->device) return fail(c, LLM_ERR_ARG, "the context's device must be the current device");
+    char* base = nullptr;
+    HIPCHK(c, noalloc_scratch(dev, &base));
+    State* st = (State*)base;
+    HIPCHK(c, launch_set_state(st, 0, pos, 0, c->stream));
+    const Layout& L = c->L;
+    AttnArgs t;
+    memset(&t, 0, sizeof t);
+    t.q = d_q;
+    t.kc = L.kc + (size_t)layer * L.kv_layer;
+    t.vc = L.vc + (size_t)layer * L.kv_layer;
+    t.out = d_out;
+    t.part = (float*)(base + st_bytes);
+    t.st = st;
+    t.n_heads = cf.n_heads;
+    t.n_kv_heads = cf.n_kv_heads;
+    t.head_dim = cf.head_dim;
+    t.n_ctx = cf.n_ctx;
+    t.n_split = n_split;
+    t.scale_div = (float)sqrt((double)cf.head_dim);
+    t.span = span_cfg(cf);
+    t.rnd = cf.numerics;
+    t.stats = (float*)(base + st_bytes + part_bytes);
+    HIPCHK(c, launch_attn(t, 1, c->stream));
+    return LLM_OK;
+}
 
 }  // extern "C"
