@@ -285,17 +285,33 @@ __device__ __forceinline__ double block_sum_s(double v, double* red) {
 
 // xs (swizzled for weight type DT) = rmsnorm(xr) * gain over K elements
 // ("The Forward Pass in Java", Example 4: sum of squares in double, the scale
-// rounded to float once, then x * scale * gain).
-// The gain elements tid + j*kSB (j < kGainPF) of the next RMSNorm, loaded
-// ahead of the barrier that precedes it.
-constexpr int kGainPF = 4;
+// rounded to float once, then x * scale * gain). Thread t owns the elements
+// 4t .. 4t+3 (+ multiples of 4 * kSB): it sums their squares and writes their
+// outputs.
+// The gain elements 4t .. 4t+3 of the next RMSNorm, loaded ahead of the
+// barrier that precedes it.
 struct GainPF {
-    float g[kGainPF];
+    float4 g;
 };
 __device__ __forceinline__ void gain_load(GainPF& gp, const float* gain, int K) {
-    const int tid = thread_id();
-#pragma unroll
-    for (int j = 0; j < kGainPF; j++) gp.g[j] = tid + j * kSB < K ? ldf(gain + tid + j * kSB) : 0.f;
+    const int i = 4 * thread_id();
+    gp.g = i < K ? ldf4(gain + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// xs[swz(i .. i+3)] = v * scale * g
+template <int DT>
+__device__ __forceinline__ void norm_store4(float* xs, int i, float4 v, float scale, float4 g) {
+    float4 o;
+    o.x = v.x * scale * g.x;
+    o.y = v.y * scale * g.y;
+    o.z = v.z * scale * g.z;
+    o.w = v.w * scale * g.w;
+    *(float4*)(xs + swz<DT>(i)) = o;
+}
+
+__device__ __forceinline__ double sq4(float4 v) {
+    return (double)v.x * (double)v.x + (double)v.y * (double)v.y + (double)v.z * (double)v.z +
+           (double)v.w * (double)v.w;
 }
 
 template <int DT>
@@ -303,19 +319,11 @@ __device__ __forceinline__ void stage_norm(const float* xr, const float* gain, c
                                            float* xs, double* red) {
     const int tid = thread_id();
     double ss = 0.0;
-    for (int i = 4 * tid; i < K; i += 4 * kSB) {
-        const float4 v = *(const float4*)(xr + i);
-        ss += (double)v.x * (double)v.x + (double)v.y * (double)v.y + (double)v.z * (double)v.z +
-              (double)v.w * (double)v.w;
-    }
+    for (int i = 4 * tid; i < K; i += 4 * kSB) ss += sq4(*(const float4*)(xr + i));
     const double tot = block_sum_s(ss, red);
     const float scale = (float)(1.0 / sqrt(tot / (double)K + (double)eps));
-#pragma unroll
-    for (int j = 0; j < kGainPF; j++) {
-        const int i = tid + j * kSB;
-        if (i < K) xs[swz<DT>(i)] = xr[i] * scale * gp.g[j];
-    }
-    for (int i = tid + kGainPF * kSB; i < K; i += kSB) xs[swz<DT>(i)] = xr[i] * scale * ldf(gain + i);
+    for (int i = 4 * tid; i < K; i += 4 * kSB)
+        norm_store4<DT>(xs, i, *(const float4*)(xr + i), scale, i == 4 * tid ? gp.g : ldf4(gain + i));
     __syncthreads();
 }
 
@@ -354,24 +362,50 @@ __device__ __forceinline__ void round_input(float* xs, int K) {
     }
 }
 
+// v += the contributing groups' partial sums P[g][i .. i+3], groups in order.
+__device__ __forceinline__ float4 add4_partials(float4 v, const float* P, long long pstride, int i, unsigned gmask) {
+    float4 p[kNG];
+#pragma unroll
+    for (int g = 0; g < kNG; g++)
+        p[g] = (gmask >> g) & 1 ? ldf4(P + g * pstride + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int g = 0; g < kNG; g++)
+        if ((gmask >> g) & 1) {
+            v.x += p[g].x;
+            v.y += p[g].y;
+            v.z += p[g].z;
+            v.w += p[g].w;
+        }
+    return v;
+}
+
 // xr[i] += sum over the groups that contributed of P[g][i], groups in order.
 __device__ __forceinline__ void add_partials(float* xr, const float* P, long long pstride, int dim, unsigned gmask) {
-    for (int i = 4 * thread_id(); i < dim; i += 4 * kSB) {
-        float4 p[kNG];
-#pragma unroll
-        for (int g = 0; g < kNG; g++)
-            p[g] = (gmask >> g) & 1 ? ldf4(P + g * pstride + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-        float4 v = *(const float4*)(xr + i);
-#pragma unroll
-        for (int g = 0; g < kNG; g++)
-            if ((gmask >> g) & 1) {
-                v.x += p[g].x;
-                v.y += p[g].y;
-                v.z += p[g].z;
-                v.w += p[g].w;
-            }
+    for (int i = 4 * thread_id(); i < dim; i += 4 * kSB)
+        *(float4*)(xr + i) = add4_partials(*(const float4*)(xr + i), P, pstride, i, gmask);
+    __syncthreads();
+}
+
+// add_partials, then stage_norm with `gain`, in one pass: each thread keeps the
+// residual elements it updates and normalises them itself.
+template <int DT>
+__device__ __forceinline__ void add_partials_norm(float* xr, const float* P, long long pstride, int dim, unsigned gmask,
+                                                  const float* gain, const GainPF& gp, float eps, float* xs,
+                                                  double* red) {
+    const int tid = thread_id();
+    double ss = 0.0;
+    float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 4 * tid; i < dim; i += 4 * kSB) {
+        const float4 v = add4_partials(*(const float4*)(xr + i), P, pstride, i, gmask);
         *(float4*)(xr + i) = v;
+        if (i == 4 * tid) v0 = v;
+        ss += sq4(v);
     }
+    const double tot = block_sum_s(ss, red);
+    const float scale = (float)(1.0 / sqrt(tot / (double)dim + (double)eps));
+    for (int i = 4 * tid; i < dim; i += 4 * kSB)
+        norm_store4<DT>(xs, i, i == 4 * tid ? v0 : *(const float4*)(xr + i), scale,
+                        i == 4 * tid ? gp.g : ldf4(gain + i));
     __syncthreads();
 }
 
@@ -1087,10 +1121,11 @@ __device__ __forceinline__ void merge_splits(const StepArgs& a, const float* par
 }
 
 // --------------------------------------------------------------------- logits
+// xs holds rmsnorm(xr) * output_norm already when `normed` (for DT's swizzle).
 template <int DT, class GEO = GeoRT, bool RND = false>
 __device__ __forceinline__ void logits_phase(const StepArgs& a, const float* xr, const GainPF& gp, float* xs,
-                                             double* red, ArgPart* wbest) {
-    stage_norm<DT>(xr, a.out_norm, gp, a.eps, a.dim, xs, red);
+                                             double* red, ArgPart* wbest, bool normed) {
+    if (!normed) stage_norm<DT>(xr, a.out_norm, gp, a.eps, a.dim, xs, red);
     if constexpr (RND) round_input<DT>(xs, a.dim);
     const int lane = thread_id() & 63, wave = thread_id() >> 6;
     const int wv = __builtin_amdgcn_readfirstlane(blockIdx.x * kSW + wave);
@@ -1256,8 +1291,8 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         float* po = a.po + (size_t)l * kNG * a.pstride;
         float* pd = a.pd + (size_t)l * kNG * a.pstride;
 
-        // ---- QKV
-        stage_norm<DT>(xr, lw[l].attn_norm, gp, a.eps, a.dim, xs, red);
+        // ---- QKV (the previous layer's end left rmsnorm(x) * attn_norm in xs)
+        if (l == 0) stage_norm<DT>(xr, lw[0].attn_norm, gp, a.eps, a.dim, xs, red);
         if constexpr (RND) round_input<DT>(xs, a.dim);
         ea.out = qkv;
         ea.bias = lw[l].bqkv;
@@ -1320,8 +1355,7 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         STAMP();
 
         // ---- residual, RMSNorm, gate/up + SwiGLU
-        add_partials(xr, po, a.pstride, a.dim, hmask);
-        stage_norm<DT>(xr, lw[l].ffn_norm, gp, a.eps, a.dim, xs, red);
+        add_partials_norm<DT>(xr, po, a.pstride, a.dim, hmask, lw[l].ffn_norm, gp, a.eps, xs, red);
         if constexpr (RND) round_input<DT>(xs, a.dim);
         ea.out = u + flo;
         wrun<DT, EM_SWIGLU, GG>(wg, nullptr, 2 * flo, xs, pf, true, ea, best, bi, nfin);
@@ -1353,16 +1387,24 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         pin();
         all_wait(a, ++jc * bg);
         STAMP();
-        add_partials(xr, pd, a.pstride, a.dim, fmask);
+        // the residual, and the next RMSNorm: the next layer's attention norm,
+        // or after the last layer the output norm (for the output matrix's
+        // swizzle, known here in a kernel compiled for the shape)
+        if (l + 1 < a.n_layers)
+            add_partials_norm<DT>(xr, pd, a.pstride, a.dim, fmask, lw[l + 1].attn_norm, gp, a.eps, xs, red);
+        else if constexpr (ODT >= 0)
+            add_partials_norm<ODT>(xr, pd, a.pstride, a.dim, fmask, a.out_norm, gp, a.eps, xs, red);
+        else
+            add_partials(xr, pd, a.pstride, a.dim, fmask);
     }
 
     if constexpr (ODT >= 0) {
-        logits_phase<ODT, GL, RND>(a, xr, gp, xs, red, wbest);
+        logits_phase<ODT, GL, RND>(a, xr, gp, xs, red, wbest, true);
     } else {
         switch (a.out.dtype) {
-            case DT_F32: logits_phase<DT_F32, GeoRT, RND>(a, xr, gp, xs, red, wbest); break;
-            case DT_F16: logits_phase<DT_F16, GeoRT, RND>(a, xr, gp, xs, red, wbest); break;
-            default: logits_phase<DT_Q8, GeoRT, RND>(a, xr, gp, xs, red, wbest); break;
+            case DT_F32: logits_phase<DT_F32, GeoRT, RND>(a, xr, gp, xs, red, wbest, false); break;
+            case DT_F16: logits_phase<DT_F16, GeoRT, RND>(a, xr, gp, xs, red, wbest, false); break;
+            default: logits_phase<DT_Q8, GeoRT, RND>(a, xr, gp, xs, red, wbest, false); break;
         }
     }
     wait_mem();
