@@ -15,7 +15,7 @@ import numpy as np
 from . import build as _build
 
 F32, F16, Q8_0 = 0, 1, 8
-_lib = None
+_libs = {}
 
 
 class OrcConfig(ctypes.Structure):
@@ -37,12 +37,15 @@ class OrcTensor(ctypes.Structure):
                 ("ne", ctypes.c_int64 * 2), ("data", ctypes.c_void_p), ("nbytes", ctypes.c_size_t)]
 
 
-def lib():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_build.LIB):
+def lib(descending: bool = False):
+    """liboracle.so, or with descending=True its build that sums every dot
+    product over the input index descending (a second valid evaluation of the
+    same definition, used only to measure sensitivity to summation order)."""
+    if descending not in _libs:
+        path = _build.LIB_DESC if descending else _build.LIB
+        if not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
         L.orc_f16_to_f32.restype = f32
@@ -105,8 +108,8 @@ def lib():
         L.orc_max_threads.restype = i32
         L.orc_weights_per_layer.argtypes = [i64, i64, i64]
         L.orc_weights_per_layer.restype = i64
-        _lib = L
-    return _lib
+        _libs[descending] = L
+    return _libs[descending]
 
 
 def _p(a: np.ndarray):
@@ -287,8 +290,9 @@ def make_config(cfg) -> OrcConfig:
 class Model:
     """The oracle's forward pass over a tensor set (a list of synth.Tensor)."""
 
-    def __init__(self, cfg, tensors: Sequence, config: Optional[OrcConfig] = None):
+    def __init__(self, cfg, tensors: Sequence, config: Optional[OrcConfig] = None, descending: bool = False):
         self.cfg = cfg
+        self.L = lib(descending)
         self._keep = list(tensors)
         arr = (OrcTensor * len(tensors))()
         self._names = []
@@ -304,7 +308,7 @@ class Model:
             arr[i].nbytes = t.nbytes
         self.config = config if config is not None else make_config(cfg)
         h = ctypes.c_void_p()
-        rc = lib().orc_load(ctypes.byref(self.config), arr, len(tensors), ctypes.byref(h))
+        rc = self.L.orc_load(ctypes.byref(self.config), arr, len(tensors), ctypes.byref(h))
         if rc:
             raise ValueError(f"orc_load failed: {rc}")
         self.h = h
@@ -312,7 +316,7 @@ class Model:
 
     def close(self):
         if getattr(self, "h", None):
-            lib().orc_free(self.h)
+            self.L.orc_free(self.h)
             self.h = None
 
     def __del__(self):
@@ -323,7 +327,7 @@ class Model:
 
     def forward(self, token: int, pos: int) -> np.ndarray:
         out = np.empty(self.vocab, np.float32)
-        rc = lib().orc_forward(self.h, int(token), int(pos), _p(out))
+        rc = self.L.orc_forward(self.h, int(token), int(pos), _p(out))
         if rc:
             raise ValueError(f"orc_forward: {rc}")
         return out
@@ -331,7 +335,7 @@ class Model:
     def prefill(self, tokens) -> np.ndarray:
         tk = np.ascontiguousarray(tokens, np.int32)
         out = np.empty(self.vocab, np.float32)
-        rc = lib().orc_prefill(self.h, _p(tk), tk.size, _p(out))
+        rc = self.L.orc_prefill(self.h, _p(tk), tk.size, _p(out))
         if rc:
             raise ValueError(f"orc_prefill: {rc}")
         return out
@@ -341,16 +345,16 @@ class Model:
         tk = np.ascontiguousarray(tokens, np.int32)
         rw = np.ascontiguousarray(rows, np.int32)
         out = np.empty((rw.size, self.vocab), np.float32)
-        rc = lib().orc_prefill_rows(self.h, _p(tk), tk.size, _p(rw), rw.size, _p(out))
+        rc = self.L.orc_prefill_rows(self.h, _p(tk), tk.size, _p(rw), rw.size, _p(out))
         if rc:
             raise ValueError(f"orc_prefill_rows: {rc}")
         return out
 
     def reset(self):
-        lib().orc_reset(self.h)
+        self.L.orc_reset(self.h)
 
     def kv_len(self) -> int:
-        return int(lib().orc_kv_len(self.h))
+        return int(self.L.orc_kv_len(self.h))
 
     def kv_write(self, layer: int, pos: int, k_bits: np.ndarray, v_bits: np.ndarray):
         """Write binary16 K and V bits of one layer at one position."""
@@ -358,13 +362,13 @@ class Model:
         v = np.ascontiguousarray(v_bits, np.uint16)
         kvd = self.config.n_kv_heads * self.config.head_dim
         assert k.size == kvd and v.size == kvd
-        rc = lib().orc_kv_write(self.h, int(layer), int(pos), _p(k), _p(v))
+        rc = self.L.orc_kv_write(self.h, int(layer), int(pos), _p(k), _p(v))
         if rc:
             raise ValueError(f"orc_kv_write: {rc}")
 
     def set_len(self, n: int):
         """Declare cache rows 0..n-1 valid."""
-        rc = lib().orc_set_len(self.h, int(n))
+        rc = self.L.orc_set_len(self.h, int(n))
         if rc:
             raise ValueError(f"orc_set_len: {rc}")
 
@@ -372,7 +376,7 @@ class Model:
         kvd = self.config.n_kv_heads * self.config.head_dim
         k = np.empty(kvd, np.uint16)
         v = np.empty(kvd, np.uint16)
-        rc = lib().orc_kv_read(self.h, layer, pos, _p(k), _p(v))
+        rc = self.L.orc_kv_read(self.h, layer, pos, _p(k), _p(v))
         if rc:
             raise ValueError(f"orc_kv_read: {rc}")
         return k, v

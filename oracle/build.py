@@ -8,18 +8,26 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "liboracle.so")
+# the same source with every dot product summed over i descending (used only to
+# measure a workload's sensitivity to the summation order)
+LIB_DESC = os.path.join(HERE, "liboracle_desc.so")
 CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-std=c11", "-Wall", "-Wno-unused-function"]
 
 
-def build(verbose: bool = False) -> str:
+def _build_one(out: str, extra, verbose: bool) -> str:
     src = os.path.join(HERE, "oracle.c")
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, "-shared", "-fPIC", "-o", tmp, src, "-lm"]
+    tmp = out + ".tmp"
+    cmd = ["gcc", *CFLAGS, *extra, "-shared", "-fPIC", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    _build_one(LIB_DESC, ["-DORC_DOT_DESCENDING"], verbose)
+    return _build_one(LIB, [], verbose)
 
 
 if __name__ == "__main__":

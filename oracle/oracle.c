@@ -225,10 +225,19 @@ void orc_rmsnorm(float* out, const float* x, const float* w, int32_t n, float ep
     for (int32_t i = 0; i < n; i++) out[i] = x[i] * r * w[i];
 }
 
-/* One sequential fp32 dot product over i ascending (Example 5). */
+/* One sequential fp32 dot product over i ascending (Example 5). The build
+ * with ORC_DOT_DESCENDING (liboracle_desc.so) sums the same products over i
+ * descending: an equally valid evaluation of the definition, used only to
+ * measure how far the fp32 summation order alone moves a workload's logits
+ * ("What a Llama model computes, and why", section 8, names summation order as
+ * a source of divergence between implementations). */
 static float dot(const float* w, const float* x, int64_t n) {
     float s = 0.0f;
+#ifdef ORC_DOT_DESCENDING
+    for (int64_t i = n - 1; i >= 0; i--) s += w[i] * x[i];
+#else
     for (int64_t i = 0; i < n; i++) s += w[i] * x[i];
+#endif
     return s;
 }
 
