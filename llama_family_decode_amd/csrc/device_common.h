@@ -183,6 +183,35 @@ __device__ __forceinline__ float chunk_dot(u32x4 raw, const float* xs, int c) {
     return chunk_dot_x<DT>(raw, xchunk_load<DT>(xs, c));
 }
 
+// llama.cpp's rounding points on Q8_0 weights ("What a Llama model computes,
+// and why", section 8: the activations are rounded to 8 bits and the product
+// is an integer dot per block): the staged input as K int8 codes in element
+// order followed by one float scale (binary16-rounded) per 32-block. One
+// 16-byte weight chunk c meets the 16 codes at byte 16c and the scale of block
+// c / 2.
+struct XChunkI8 {
+    u32x4 q;
+    float d;
+};
+
+__device__ __forceinline__ XChunkI8 xchunk_load_i8(const float* xs, int K, int c) {
+    XChunkI8 x;
+    x.q = *(const u32x4*)((const char*)xs + 16 * c);
+    x.d = (xs + K / 4)[c >> 1];
+    return x;
+}
+
+// Weight codes . input codes as one exact int32 (four 4-way int8 dot
+// products), times the input block's scale; the caller applies the weight
+// row's block scale.
+__device__ __forceinline__ float chunk_dot_i8(u32x4 raw, const XChunkI8& x) {
+    int s = __builtin_amdgcn_sdot4((int)raw.x, (int)x.q.x, 0, false);
+    s = __builtin_amdgcn_sdot4((int)raw.y, (int)x.q.y, s, false);
+    s = __builtin_amdgcn_sdot4((int)raw.z, (int)x.q.z, s, false);
+    s = __builtin_amdgcn_sdot4((int)raw.w, (int)x.q.w, s, false);
+    return (float)s * x.d;
+}
+
 // Order-preserving 64-bit key of (value, index): a larger value wins, and for
 // equal values the smaller index wins, so the maximum key is the first index of
 // the strict maximum ("The Forward Pass in Java", Example 9). -0 is taken as +0.

@@ -379,6 +379,42 @@ __device__ __forceinline__ float4 add4_partials(float4 v, const float* P, long l
     return v;
 }
 
+// The rounding mode's Q8_0 product input for the integer products: each
+// 32-element block of the staged input quantized as round_input does (the
+// same codes and binary16 scale), kept as codes and scales (XChunkI8's
+// layout) instead of their decoded values. Thread t takes elements
+// t + j * kSB, j < 4, so K <= 4 * kSB (the kernels compiled for one shape).
+__device__ __forceinline__ void round_input_i8(float* xs, int K) {
+    const int tid = thread_id();
+    int code[4];
+    float dsc[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int i = tid + j * kSB;
+        code[j] = 0;
+        dsc[j] = 0.f;
+        if (i < K) {  // whole half-waves: K is a multiple of 32
+            const float v = xs[swz<DT_Q8>(i)];
+            float amax = fabsf(v);
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f;
+            code[j] = (int)roundf(v * id);
+            dsc[j] = round16(d);
+        }
+    }
+    __syncthreads();  // every float of the staged input has been read
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int i = tid + j * kSB;
+        if (i < K) {
+            ((int8_t*)xs)[i] = (int8_t)code[j];
+            if ((i & 31) == 0) (xs + K / 4)[i >> 5] = dsc[j];
+        }
+    }
+    __syncthreads();
+}
+
 // xr[i] += sum over the groups that contributed of P[g][i], groups in order.
 __device__ __forceinline__ void add_partials(float* xr, const float* P, long long pstride, int dim, unsigned gmask) {
     for (int i = 4 * thread_id(); i < dim; i += 4 * kSB)
@@ -669,7 +705,7 @@ __device__ __forceinline__ float seg_reduce16(const float (&v)[16], int lane) {
 // batch holds whole rows (an even number). Lane partials of each row
 // accumulate over its ncb slots, one transposed butterfly sums all rows over
 // their lanes, and the lanes emit the rows in parallel.
-template <int DT, int EM, int LSH, int NCB>
+template <int DT, int EM, int LSH, int NCB, bool I8 = false>
 __device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int roff, const float* xs, const PF& pf,
                                             int k0, int lane, const EmitArgs& ea, float& best, int& best_i,
                                             int& nonfinite) {
@@ -688,12 +724,17 @@ __device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int
         for (int r = 0; r < NR; r++) acc[r] = 0.f;
 #pragma unroll
         for (int cb = 0; cb < NCB; cb++) {
-            const XChunk<DT> xc = xchunk_load<DT>(xs, cl + (cb << LSH));
+            XChunk<DT> xc;
+            XChunkI8 xi;
+            if constexpr (I8)
+                xi = xchunk_load_i8(xs, w.W.nch * VecW<DT>::VE, cl + (cb << LSH));
+            else
+                xc = xchunk_load<DT>(xs, cl + (cb << LSH));
 #pragma unroll
             for (int r = 0; r < NR; r++) {
                 const int k = r * NCB + cb;
                 if (k0 + k < w.nslots) {
-                    const float p = chunk_dot_x<DT>(pf.q[k], xc);
+                    const float p = I8 ? chunk_dot_i8(pf.q[k], xi) : chunk_dot_x<DT>(pf.q[k], xc);
                     if constexpr (DT == DT_Q8)
                         acc[r] += h2f((uint16_t)pf.s[k]) * p;
                     else
@@ -711,7 +752,8 @@ __device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int
             rv[k] = 0.f;
             if (k0 + k < w.nslots) {
                 const int c = cl + (cb << LSH);
-                const float p = chunk_dot<DT>(pf.q[k], xs, c);
+                const float p = I8 ? chunk_dot_i8(pf.q[k], xchunk_load_i8(xs, w.W.nch * VecW<DT>::VE, c))
+                                   : chunk_dot<DT>(pf.q[k], xs, c);
                 if constexpr (DT == DT_Q8)
                     acc += h2f((uint16_t)pf.s[k]) * p;
                 else
@@ -757,7 +799,7 @@ __device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int
 // The wave's rows. If `prefetched`, pf already holds the first kPF slots
 // (issued by wload before the barrier). For pairs, wave ranges start at even
 // rows.
-template <int DT, int EM, class GEO = GeoRT>
+template <int DT, int EM, class GEO = GeoRT, bool I8 = false>
 __device__ __forceinline__ void wrun(const WRows& w, const int* rmap, int roff, const float* xs, PF& pf,
                                      bool prefetched, const EmitArgs& ea, float& best, int& best_i, int& nonfinite) {
     if (w.nslots == 0) return;
@@ -765,11 +807,11 @@ __device__ __forceinline__ void wrun(const WRows& w, const int* rmap, int roff, 
         const int lane = lane_id();
         for (int k0 = 0; k0 < w.nslots; k0 += kPF) {
             if (!prefetched || k0 > 0) wload<DT>(w, rmap, roff, k0, pf);
-            wbatch_fast<DT, EM, GEO::L, GEO::N>(w, rmap, roff, xs, pf, opaque_s(k0), lane, ea, best, best_i,
-                                                nonfinite);
+            wbatch_fast<DT, EM, GEO::L, GEO::N, I8>(w, rmap, roff, xs, pf, opaque_s(k0), lane, ea, best, best_i,
+                                                    nonfinite);
         }
-        return;
-    }
+    } else {
+    static_assert(!I8, "integer products run in the kernels compiled for one shape");
     const int lane = lane_id(), sub = lane >> w.lsh, cl = lane & (w.lpr - 1);
     const bool dense = w.lsh >= 4 && (w.W.nch & (w.lpr - 1)) == 0 && (w.r1 - w.r0) % w.rpi == 0 && w.ncb <= 8 &&
                        (w.ncb & (w.ncb - 1)) == 0;
@@ -785,6 +827,7 @@ __device__ __forceinline__ void wrun(const WRows& w, const int* rmap, int roff, 
             wbatch_fast<DT, EM, 4, 0>(w, rmap, roff, xs, pf, k0s, lane, ea, best, best_i, nonfinite);
         else
             wbatch<DT, EM, false>(w, rmap, roff, xs, pf, k0s, lane, sub, cl, ea, acc, pend, best, best_i, nonfinite);
+    }
     }
 }
 
@@ -1201,6 +1244,16 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
     float* wsp = xs + a.lds_xs;            // split weights of the merge
     float* ored = wsp + a.lds_wsp;         // merge partial sums [kSB]
     float2* cs = (float2*)(ored + kSB);    // RoPE (cos, sin) of this position, kMaxHeadDim/2 pairs
+    // llama.cpp's rounding points on Q8_0 layers in a kernel compiled for the
+    // shape: the products' inputs stay Q8_0 codes and the products are integer
+    // dot products
+    constexpr bool I8 = RND && DT == DT_Q8 && GA > 0;
+    auto round_in = [&](int K) {
+        if constexpr (I8)
+            round_input_i8(xs, K);
+        else if constexpr (RND)
+            round_input<DT>(xs, K);
+    };
     int* qmap = (int*)(cs + kMaxHeadDim / 2);  // the group's q/k/v rows in RoPE-pair order
     // the layer descriptors, copied once, so that the address of a phase's
     // weights is an LDS read rather than a dependent load from device memory
@@ -1293,12 +1346,12 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
 
         // ---- QKV (the previous layer's end left rmsnorm(x) * attn_norm in xs)
         if (l == 0) stage_norm<DT>(xr, lw[0].attn_norm, gp, a.eps, a.dim, xs, red);
-        if constexpr (RND) round_input<DT>(xs, a.dim);
+        round_in(a.dim);
         ea.out = qkv;
         ea.bias = lw[l].bqkv;
         ea.kc = a.kc + (size_t)l * a.kv_layer;
         ea.vc = a.vc + (size_t)l * a.kv_layer;
-        wrun<DT, EM_QKV, GQ>(wq, qmap, 0, xs, pf, true, ea, best, bi, nfin);
+        wrun<DT, EM_QKV, GQ, I8>(wq, qmap, 0, xs, pf, true, ea, best, bi, nfin);
         wait_mem();
         group_arrive(a, x);
         group_wait(a, x, ++jl * bg);
@@ -1341,9 +1394,9 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         // ---- split merge + output product (partial over the group's heads)
         if (nh > 0) {
             merge_splits<DT>(a, part, hlo, nh, S, xs, wsp, ored);
-            if constexpr (RND) round_input<DT>(xs, nh * G * hd);
+            round_in(nh * G * hd);
             ea.out = po + (size_t)x * a.pstride;
-            wrun<DT, EM_PART, GO>(wo, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
+            wrun<DT, EM_PART, GO, I8>(wo, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
         }
         wait_mem();
         all_arrive(a, x);
@@ -1356,9 +1409,9 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
 
         // ---- residual, RMSNorm, gate/up + SwiGLU
         add_partials_norm<DT>(xr, po, a.pstride, a.dim, hmask, lw[l].ffn_norm, gp, a.eps, xs, red);
-        if constexpr (RND) round_input<DT>(xs, a.dim);
+        round_in(a.dim);
         ea.out = u + flo;
-        wrun<DT, EM_SWIGLU, GG>(wg, nullptr, 2 * flo, xs, pf, true, ea, best, bi, nfin);
+        wrun<DT, EM_SWIGLU, GG, I8>(wg, nullptr, 2 * flo, xs, pf, true, ea, best, bi, nfin);
         wait_mem();
         group_arrive(a, x);
         wd.W = make_win<DT>(lw[l].down, flo, nf);
@@ -1370,9 +1423,9 @@ __global__ __launch_bounds__(kSB, 1) void k_step(StepArgs a) {
         // ---- down product (partial over the group's hidden units)
         if (nf > 0) {
             stage_copy<DT>(u + flo, nf, xs);
-            if constexpr (RND) round_input<DT>(xs, nf);
+            round_in(nf);
             ea.out = pd + (size_t)x * a.pstride;
-            wrun<DT, EM_PART, GD>(wd, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
+            wrun<DT, EM_PART, GD, I8>(wd, nullptr, 0, xs, pf, true, ea, best, bi, nfin);
         }
         wait_mem();
         all_arrive(a, x);

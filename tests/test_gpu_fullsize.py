@@ -153,6 +153,42 @@ def test_decode_at_full_context_in_the_benchmarked_kernel(monkeypatch, cfg, ctx)
           f"graph {worst:.3e}", flush=True)
 
 
+def test_q8_llamacpp_integer_products_layer0_against_the_oracle(monkeypatch):
+    # llama.cpp's rounding points on the 1B Q8_0 model in the benchmarked
+    # kernel: its products are integer dot products of the weight codes with
+    # the input's Q8_0 codes ("What a Llama model computes, and why", section
+    # 8). Layer 0's K and V rows of the decode steps depend only on each
+    # step's token, and the oracle computes them as the product of the
+    # dequantized weights with the rounded input: the two agree within
+    # binary16 rounding flips. Two runs repeat bit for bit.
+    cfg = synth.C4.with_(name="llama-1b-q8_0-llamacpp", numerics=1)
+    ts = synth.make_tensor_set(cfg)
+    T = _tensors_by_name(ts)
+    toks = synth.prompt(cfg, 2048)
+    monkeypatch.setenv("LLM_STEP", "persistent")
+    runs = []
+    for _ in range(2):
+        m = llm.Model(cfg, ts)
+        assert llm.llm_op_step_kind(m.ctx) == 2
+        t, pos = int(m.prefill(toks)), len(toks)
+        feed, logits, nexts = [], [], []
+        for _ in range(6):
+            feed.append((pos, t))
+            t = m.decode(t, pos)
+            logits.append(m.logits())
+            nexts.append(t)
+            pos += 1
+        for lg, nx in zip(logits, nexts):
+            assert np.all(np.isfinite(lg)) and nx == first_max(lg)
+        w0 = check_layer0_kv(cfg, T, m, feed, 2.0)
+        runs.append((nexts, logits))
+        m.close()
+    assert runs[0][0] == runs[1][0]
+    for a, b in zip(runs[0][1], runs[1][1]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    print(f"[{cfg.name}] layer-0 K/V of the integer products within {w0} binary16 ulps", flush=True)
+
+
 def test_c5_prefill_512_against_decode_and_oracle(monkeypatch):
     cfg = synth.C5  # Qwen2-style 1B, F16, NEOX RoPE, QKV bias
     ts = synth.make_tensor_set(cfg)
