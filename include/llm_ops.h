@@ -94,7 +94,7 @@ int llm_op_time(llm_ctx* ctx, int32_t stage, int32_t layer, int32_t pos, int32_t
 
 /* Which kernel runs the context's decode steps: 0 for the captured launch
  * graph (six launches per layer plus the logits), 1 for the persistent step
- * kernel (one cooperative launch per token), 2 for a persistent step kernel
+ * kernel (one launch per token), 2 for a persistent step kernel
  * compiled for the model's shape (the 2048-wide, 64-dim-head, 4-query-heads-
  * per-KV-head shape with 8192 FFN units: Q8_0 layers with F32 vocabulary
  * rows, or F16 layers with F16 vocabulary rows). The persistent kernel is used

@@ -249,7 +249,7 @@ hipError_t launch_argmax_finalize(State* st, int* gen_out, int gen_cap, hipStrea
 // step.
 int step_grid(StepArgs& a, int dtype, int* lds_bytes, const void** fn, bool* special);
 hipError_t launch_step(const StepArgs& a, const void* fn, int grid, int lds_bytes, hipStream_t s);
-// Whether a cooperative grid of `grid` blocks puts the blocks with equal
+// Whether a grid of `grid` blocks puts the blocks with equal
 // b mod 8 on one XCD (the step kernel's groups share their L2). d_buf holds
 // grid ints.
 bool step_groups_share_l2(int grid, int* d_buf, hipStream_t s);

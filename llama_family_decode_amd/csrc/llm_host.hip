@@ -806,7 +806,7 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
         if (launch_set_state(L.st, 0, 0, 0, s) != hipSuccess ||
             launch_step(c->step, c->step_fn, c->step_grid, c->step_lds, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
             (void)hipGetLastError();
-            c->use_step = false;  // cooperative launch unavailable: the launch graph runs the steps
+            c->use_step = false;  // the step kernel did not launch: the launch graph runs the steps
         } else {
             State st;
             if (hipMemcpy(&st, L.st, sizeof st, hipMemcpyDeviceToHost) != hipSuccess || st.abort)
