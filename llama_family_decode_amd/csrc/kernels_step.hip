@@ -892,14 +892,17 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
     const int sub = tid % LPP, pg = tid / LPP;
     const bool dim_ok = sub * 8 < hd;
     const int sub8 = dim_ok ? sub * 8 : 0;
-    float* sc = sm;                 // [GC][CHUNK]
-    float* wred = sm + GC * CHUNK;  // [kSW][GC][hd]
-    bool have = pass != 2;          // the first chunk of the first item is prefetched
+    float* sc = sm;                     // [GC][CHUNK]
+    float* wred = sm + GC * CHUNK;      // [kSW][GC][hd]
+    float* raw = wred + kSW * GC * hd;  // [GC][CHUNK]: pass 1's scaled scores
+    bool have = pass != 2;              // the first chunk of the first item is prefetched
     // Pass 2 of a block with one item, one chunk and one group of query heads
     // (at most one item per block always holds) still has pass 1's V rows in
-    // vr and its e^(s - m) in sc: it reweights those instead of reloading K/V
-    // and recomputing the scores.
-    const bool reuse = pass == 2 && CH <= CHUNK && G <= GC;
+    // vr and its scores in raw: it takes f16(e^(s - M)/L) from those instead of
+    // reloading K/V and recomputing the dot products (the same values, so the
+    // same result as the reloading path).
+    const bool single = CH <= CHUNK && G <= GC;
+    const bool reuse = pass == 2 && single;
     if (reuse) have = true;
 
     for (int item = rk; item < nh * S; item += bg) {
@@ -951,7 +954,6 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                     const float M = xmax64(m);
                     const float L = xsum64(lane < S ? l * expf(m - M) : 0.f);
                     if (lane == 0) {
-                        alpha[h] = m_run[h];  // this split's max from pass 1, for the reuse
                         m_run[h] = M;
                         l_run[h] = L;
                     }
@@ -999,18 +1001,11 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                     }
                 }
                 __syncthreads();
-                if (reuse) {
-                    // sc holds e^(s - m1) of pass 1: e^(s - M) / L = that * e^(m1 - M) / L
-                    for (int h = wave; h < GC; h += kSW) {
-                        const float f = expf(alpha[h] - m_run[h]) / l_run[h];
-                        for (int t = lane; t < cn; t += 64) sc[h * CHUNK + t] = round16(sc[h * CHUNK + t] * f);
-                    }
-                    __syncthreads();
-                    if (tid < GC) alpha[tid] = 1.f;
-                } else if (pass == 2) {
+                if (pass == 2) {
+                    const float* sv = reuse ? raw : sc;
                     for (int h = wave; h < GC; h += kSW) {
                         const float M = m_run[h], L = l_run[h];
-                        for (int t = lane; t < cn; t += 64) sc[h * CHUNK + t] = round16(expf(sc[h * CHUNK + t] - M) / L);
+                        for (int t = lane; t < cn; t += 64) sc[h * CHUNK + t] = round16(expf(sv[h * CHUNK + t] - M) / L);
                         if (lane == 0) alpha[h] = 1.f;
                     }
                 } else
@@ -1022,7 +1017,9 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
                     const float m_new = fmaxf(m_old, mx);
                     float ls = 0.f;
                     for (int t = lane; t < cn; t += 64) {
-                        const float e = expf(sc[h * CHUNK + t] - m_new);
+                        const float x = sc[h * CHUNK + t];
+                        if (pass == 1 && single) raw[h * CHUNK + t] = x;
+                        const float e = expf(x - m_new);
                         sc[h * CHUNK + t] = e;
                         ls += e;
                     }
@@ -1501,7 +1498,8 @@ bool step_lds_plan(StepArgs& a, int dtype, int* lds_bytes) {
     if (lds_any(nh_max * G * hd) > xs) xs = lds_any(nh_max * G * hd);
     if (lds_any(nf_max) > xs) xs = lds_any(nf_max);
     const int GC = G < 4 ? G : 4;
-    const int att = GC * (kSB / attn_lpp(hd)) * kStepAttn + kSW * GC * hd;
+    // scores, per-wave sums, and the rounding mode's copy of pass 1's scores
+    const int att = 2 * GC * (kSB / attn_lpp(hd)) * kStepAttn + kSW * GC * hd;
     if (att > xs) xs = att;
     a.lds_xr = (a.dim + 63) / 64 * 64;
     a.lds_xs = (xs + 63) / 64 * 64;
