@@ -37,12 +37,13 @@ class OrcTensor(ctypes.Structure):
                 ("ne", ctypes.c_int64 * 2), ("data", ctypes.c_void_p), ("nbytes", ctypes.c_size_t)]
 
 
-def lib(descending: bool = False):
-    """liboracle.so, or with descending=True its build that sums every dot
-    product over the input index descending (a second valid evaluation of the
-    same definition, used only to measure sensitivity to summation order)."""
-    if descending not in _libs:
-        path = _build.LIB_DESC if descending else _build.LIB
+def lib(variant: str = ""):
+    """liboracle.so, or one of its builds that evaluate the same definition in
+    another valid way, used only to measure a workload's sensitivity to the
+    rounding of its sums: variant "desc" sums every dot product over the input
+    index descending, "f64" accumulates every sum in double and rounds it once."""
+    if variant not in _libs:
+        path = _build.VARIANTS[variant][0]
         if not os.path.exists(path):
             _build.build()
         L = ctypes.CDLL(path)
@@ -108,8 +109,8 @@ def lib(descending: bool = False):
         L.orc_max_threads.restype = i32
         L.orc_weights_per_layer.argtypes = [i64, i64, i64]
         L.orc_weights_per_layer.restype = i64
-        _libs[descending] = L
-    return _libs[descending]
+        _libs[variant] = L
+    return _libs[variant]
 
 
 def _p(a: np.ndarray):
@@ -290,9 +291,9 @@ def make_config(cfg) -> OrcConfig:
 class Model:
     """The oracle's forward pass over a tensor set (a list of synth.Tensor)."""
 
-    def __init__(self, cfg, tensors: Sequence, config: Optional[OrcConfig] = None, descending: bool = False):
+    def __init__(self, cfg, tensors: Sequence, config: Optional[OrcConfig] = None, variant: str = ""):
         self.cfg = cfg
-        self.L = lib(descending)
+        self.L = lib(variant)
         self._keep = list(tensors)
         arr = (OrcTensor * len(tensors))()
         self._names = []

@@ -8,9 +8,12 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "liboracle.so")
-# the same source with every dot product summed over i descending (used only to
-# measure a workload's sensitivity to the summation order)
+# the same source evaluated in two other valid ways (used only to measure a
+# workload's sensitivity to the rounding of its sums): every dot product summed
+# over i descending, and every sum accumulated in double and rounded once
 LIB_DESC = os.path.join(HERE, "liboracle_desc.so")
+LIB_F64 = os.path.join(HERE, "liboracle_f64.so")
+VARIANTS = {"": (LIB, []), "desc": (LIB_DESC, ["-DORC_DOT_DESCENDING"]), "f64": (LIB_F64, ["-DORC_SUM_F64"])}
 CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-std=c11", "-Wall", "-Wno-unused-function"]
 
 
@@ -26,7 +29,9 @@ def _build_one(out: str, extra, verbose: bool) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    _build_one(LIB_DESC, ["-DORC_DOT_DESCENDING"], verbose)
+    for name, (out, extra) in VARIANTS.items():
+        if name:
+            _build_one(out, extra, verbose)
     return _build_one(LIB, [], verbose)
 
 

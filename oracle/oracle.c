@@ -225,20 +225,30 @@ void orc_rmsnorm(float* out, const float* x, const float* w, int32_t n, float ep
     for (int32_t i = 0; i < n; i++) out[i] = x[i] * r * w[i];
 }
 
-/* One sequential fp32 dot product over i ascending (Example 5). The build
- * with ORC_DOT_DESCENDING (liboracle_desc.so) sums the same products over i
- * descending: an equally valid evaluation of the definition, used only to
- * measure how far the fp32 summation order alone moves a workload's logits
- * ("What a Llama model computes, and why", section 8, names summation order as
- * a source of divergence between implementations). */
-static float dot(const float* w, const float* x, int64_t n) {
-    float s = 0.0f;
-#ifdef ORC_DOT_DESCENDING
-    for (int64_t i = n - 1; i >= 0; i--) s += w[i] * x[i];
+/* One sequential fp32 dot product over i ascending (Example 5). Two other
+ * builds of this file evaluate the same definition in another valid way, used
+ * only to measure how far the rounding of the sums alone moves a workload's
+ * logits ("What a Llama model computes, and why", section 8, names summation
+ * order as a source of divergence between implementations):
+ *  - ORC_DOT_DESCENDING (liboracle_desc.so) sums the same fp32 products over i
+ *    descending;
+ *  - ORC_SUM_F64 (liboracle_f64.so) accumulates every sum of the layer and the
+ *    attention (these dot products, the attention scores, the softmax total
+ *    and the weighted sum of V) in double and rounds it to float once: the
+ *    definition summed almost exactly. */
+#ifdef ORC_SUM_F64
+typedef double acc_t;
 #else
-    for (int64_t i = 0; i < n; i++) s += w[i] * x[i];
+typedef float acc_t;
 #endif
-    return s;
+static float dot(const float* w, const float* x, int64_t n) {
+    acc_t s = 0;
+#ifdef ORC_DOT_DESCENDING
+    for (int64_t i = n - 1; i >= 0; i--) s += (acc_t)w[i] * x[i];
+#else
+    for (int64_t i = 0; i < n; i++) s += (acc_t)w[i] * x[i];
+#endif
+    return (float)s;
 }
 
 /* Matrix-vector product in GGUF order, Example 5: a tensor with dims
@@ -416,9 +426,9 @@ static float attn_scores(float* s, const float* q, const uint16_t* kc, int32_t k
     for (int32_t t = 0; t <= pos; t++) {
         if (!orc_attends(t, pos, window, sinks)) continue;
         const uint16_t* k = kc + (int64_t)t * kv_dim + kv_off;
-        float acc = 0.0f;
-        for (int32_t i = 0; i < hd; i++) acc += q[i] * orc_f16_to_f32(k[i]);
-        s[t] = acc / root;
+        acc_t acc = 0;
+        for (int32_t i = 0; i < hd; i++) acc += (acc_t)q[i] * orc_f16_to_f32(k[i]);
+        s[t] = (float)acc / root;
         top = fmaxf(top, s[t]);
     }
     return top;
@@ -426,26 +436,30 @@ static float attn_scores(float* s, const float* q, const uint16_t* kc, int32_t k
 
 /* s_t -> p_t in place over the attended rows; rows not attended get 0. */
 static void attn_softmax(float* s, float top, int32_t pos, int32_t window, int32_t sinks, int32_t round16) {
-    float total = 0.0f;
+    acc_t sum = 0;
     for (int32_t t = 0; t <= pos; t++)
         if (orc_attends(t, pos, window, sinks)) {
             s[t] = (float)exp((double)(s[t] - top));
-            total += s[t];
+            sum += s[t];
         }
+    const float total = (float)sum;
     for (int32_t t = 0; t <= pos; t++) {
         float p = orc_attends(t, pos, window, sinks) ? s[t] / total : 0.0f;
         s[t] = round16 ? f16_round(p) : p;
     }
 }
 
-/* out += p_t V_t over the attended rows, t ascending. */
+/* out = sum of p_t V_t over the attended rows, t ascending. */
 static void attn_weighted_sum(float* out, const float* p, const uint16_t* vc, int32_t kv_dim, int32_t kv_off,
                               int32_t hd, int32_t pos, int32_t window, int32_t sinks) {
+    acc_t* acc = (acc_t*)calloc((size_t)hd, sizeof(acc_t));
     for (int32_t t = 0; t <= pos; t++) {
         if (!orc_attends(t, pos, window, sinks)) continue;
         const uint16_t* v = vc + (int64_t)t * kv_dim + kv_off;
-        for (int32_t i = 0; i < hd; i++) out[i] += p[t] * orc_f16_to_f32(v[i]);
+        for (int32_t i = 0; i < hd; i++) acc[i] += (acc_t)p[t] * orc_f16_to_f32(v[i]);
     }
+    for (int32_t i = 0; i < hd; i++) out[i] = (float)acc[i];
+    free(acc);
 }
 
 void orc_attention_nx(float* out, const float* q, const uint16_t* kcache, const uint16_t* vcache, int32_t n_heads,

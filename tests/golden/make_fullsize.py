@@ -17,17 +17,18 @@ workload (``fullsize_<name>.npz``):
 * for the prompt-only workload, the logits of chosen prompt rows
   (``row_idx`` / ``row_logits``).
 
-With --descending the script runs a workload again on the oracle built to sum
-every dot product over the input index descending (liboracle_desc.so: the same
-definition, another valid fp32 summation order), teacher-forced with the
-stored tokens, and writes ``fullsize_<name>_desc.npz``: at every step the
-largest |difference| of its logits from the stored ones over the sample
-(``sample_dist``) and over the whole vector at the stored steps
-(``full_dist``). That is how far the summation order alone moves this
+With --variant V the script runs a workload again on another build of the
+oracle that evaluates the same definition in another valid way (V = desc:
+every dot product summed over the input index descending, liboracle_desc.so;
+V = f64: every sum accumulated in double and rounded once, liboracle_f64.so),
+teacher-forced with the stored tokens, and writes ``fullsize_<name>_<V>.npz``:
+at every step the largest |difference| of its logits from the stored ones over
+the sample (``sample_dist``) and over the whole vector at the stored steps
+(``full_dist``). That is how far the rounding of the sums alone moves this
 workload's logits.
 
-Usage: python tests/golden/make_fullsize.py [--descending] [workload ...]   (default: all)
-The 8192-position prompt takes the oracle about 20 minutes on 8 cores.
+Usage: python tests/golden/make_fullsize.py [--variant desc|f64] [workload ...]   (default: all)
+The 8192-position prompt takes the oracle about 70 minutes on 8 cores.
 """
 import hashlib
 import os
@@ -58,8 +59,11 @@ def out_path(name: str) -> str:
     return os.path.join(HERE, f"fullsize_{name}.npz")
 
 
-def desc_path(name: str) -> str:
-    return os.path.join(HERE, f"fullsize_{name}_desc.npz")
+VARIANTS = ("desc", "f64")
+
+
+def variant_path(name: str, variant: str) -> str:
+    return os.path.join(HERE, f"fullsize_{name}_{variant}.npz")
 
 
 def sample_indices(vocab: int) -> np.ndarray:
@@ -134,8 +138,8 @@ def make(name: str):
     print(f"[{name}] written in {time.time() - t0:.1f}s total", flush=True)
 
 
-def make_descending(name: str):
-    """The workload on the descending-order oracle, against the stored values."""
+def make_variant(name: str, variant: str):
+    """The workload on another build of the oracle, against the stored values."""
     cfg, steps, full_steps, rows = WORKLOADS[name]
     with np.load(out_path(name), allow_pickle=False) as z:
         g = {k: z[k] for k in z.files}
@@ -143,7 +147,7 @@ def make_descending(name: str):
     t0 = time.time()
     toks = synth.prompt(cfg, P)
     assert hashlib.sha256(toks.tobytes()).hexdigest() == str(g["prompt_sha256"])
-    m = oracle.Model(cfg, synth.make_tensor_set(cfg), descending=True)
+    m = oracle.Model(cfg, synth.make_tensor_set(cfg), variant=variant)
     sidx = g["sample_idx"]
     full = {int(s_): g["full_logits"][i] for i, s_ in enumerate(g["full_steps"])}
     sd = np.zeros(steps + 1, np.float32)
@@ -154,22 +158,29 @@ def make_descending(name: str):
         if step in full:
             fd[list(full_steps).index(step)] = np.max(np.abs(v.astype(np.float64) - full[step]))
 
-    print(f"[{name} descending] prefill of {P} rows", flush=True)
+    print(f"[{name} {variant}] prefill of {P} rows", flush=True)
     record(0, m.prefill(toks))
     for s_ in range(1, steps + 1):
         record(s_, m.forward(int(g["tokens"][s_ - 1]), P + s_ - 1))
         if s_ % 16 == 0:
-            print(f"[{name} descending] decode step {s_}/{steps}", flush=True)
-    np.savez_compressed(desc_path(name), config=np.array(cfg.name), sample_dist=sd,
+            print(f"[{name} {variant}] decode step {s_}/{steps}", flush=True)
+    np.savez_compressed(variant_path(name, variant), config=np.array(cfg.name), sample_dist=sd,
                         full_steps=np.array(full_steps, np.int32), full_dist=fd)
     m.close()
-    print(f"[{name} descending] median {np.median(sd):.2e} max {sd.max():.2e}; written in {time.time() - t0:.1f}s",
+    print(f"[{name} {variant}] median {np.median(sd):.2e} max {sd.max():.2e}; written in {time.time() - t0:.1f}s",
           flush=True)
 
 
 if __name__ == "__main__":
     args = sys.argv[1:]
-    desc = "--descending" in args
-    names = [a for a in args if a != "--descending"] or list(WORKLOADS)
-    for n in names:
-        (make_descending if desc else make)(n)
+    variant = None
+    if "--variant" in args:
+        i = args.index("--variant")
+        variant = args[i + 1]
+        assert variant in VARIANTS, f"--variant takes one of {VARIANTS}"
+        del args[i:i + 2]
+    for n in args or list(WORKLOADS):
+        if variant:
+            make_variant(n, variant)
+        else:
+            make(n)

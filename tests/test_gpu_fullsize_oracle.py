@@ -18,15 +18,17 @@ compute the same function). Checked at every step:
   - max |dlogit| over a fixed sample of 1024 vocabulary entries, and over the
     whole vector at the prompt's last row and the first and last decode steps,
     within the tolerance of the weight type (2e-2 for F16 and Q8_0). For the
-    Q8_0 workloads the bar at each step is max(tolerance, 1.5 d), d being how
-    far the oracle itself moves at that step when it sums every dot product
-    in the other order (tests/golden/make_fullsize.py --descending): with
-    these weights (code uniform in [-127, 127] times a scale of |N(0, 0.002)|,
-    an effective standard deviation of about 0.15) the attention scores have a
-    standard deviation of about 40, the softmax is nearly one-hot, and the
-    fp32 summation order alone moves some steps' logits by more than 2e-2
-    ("What a Llama model computes, and why", section 8: implementations that
-    differ only in summation order drift apart);
+    Q8_0 workloads the bar at each step is max(tolerance, 1.5 d), d being the
+    larger of how far the oracle itself moves at that step when it sums every
+    dot product in the other order and when it accumulates every sum in
+    double (tests/golden/make_fullsize.py --variant desc / f64: the same
+    definition evaluated in two other valid ways): with these weights (code
+    uniform in [-127, 127] times a scale of |N(0, 0.002)|, an effective
+    standard deviation of about 0.15) the attention scores have a standard
+    deviation of about 40, the softmax is nearly one-hot, and the rounding of
+    the fp32 sums alone moves some steps' logits by more than 2e-2 ("What a
+    Llama model computes, and why", section 8: implementations that differ
+    only in summation order drift apart);
   - the GPU token is the first strict maximum of the GPU logits, and equals the
     oracle's wherever the oracle's top-2 gap exceeds that step's bar;
   - the KV length; every layer's K and V at sampled positions within the logit
@@ -63,12 +65,21 @@ def _load(name):
         return {k: z[k] for k in z.files}
 
 
-def _load_desc(name):
-    path = make_fullsize.desc_path(name)
-    if not os.path.exists(path):
-        return None
-    with np.load(path, allow_pickle=False) as z:
-        return {k: z[k] for k in z.files}
+def _variant_dist(name, steps, full_steps):
+    """Per step, the larger distance of the oracle's two other builds from it:
+    (over the sample, {step: over the whole vector}). Skips while a variant's
+    file is not generated."""
+    sample, full = np.zeros(steps + 1), {int(s): 0.0 for s in full_steps}
+    for v in make_fullsize.VARIANTS:
+        path = make_fullsize.variant_path(name, v)
+        if not os.path.exists(path):
+            pytest.skip(f"{os.path.basename(path)} not generated "
+                        f"(python tests/golden/make_fullsize.py --variant {v} {name})")
+        with np.load(path, allow_pickle=False) as z:
+            sample = np.maximum(sample, z["sample_dist"].astype(np.float64))
+            for i, s in enumerate(z["full_steps"]):
+                full[int(s)] = max(full[int(s)], float(z["full_dist"][i]))
+    return sample, full
 
 
 def _check_logits(bar, got, want, where):
@@ -109,6 +120,13 @@ def test_decode_workload_against_the_oracle(name):
     cfg, steps, full_steps, _ = make_fullsize.WORKLOADS[name]
     P = int(g["prompt_len"])
     assert P == cfg.prompt_len and int(g["steps"]) == steps
+    full = {int(s): g["full_logits"][i] for i, s in enumerate(g["full_steps"])}
+    t = tol(cfg)
+    sample_bar, full_bar = np.full(steps + 1, t), {s: t for s in full}
+    if cfg.mat_dtype == "q8_0":
+        ds, df = _variant_dist(name, steps, full_steps)
+        sample_bar = np.maximum(t, 1.5 * ds)
+        full_bar = {s: max(t, 1.5 * df[s]) for s in full}
     toks = synth.prompt(cfg, P)
     assert hashlib.sha256(toks.tobytes()).hexdigest() == str(g["prompt_sha256"]), "prompt generator changed"
     ts = synth.make_tensor_set(cfg)
@@ -116,14 +134,6 @@ def test_decode_workload_against_the_oracle(name):
     gpu = llm.Model(cfg, ts)
     assert llm.llm_op_step_kind(gpu.ctx) == 2, "the shape-compiled step kernel bench.py times"
     sidx = g["sample_idx"]
-    full = {int(s): g["full_logits"][i] for i, s in enumerate(g["full_steps"])}
-    t = tol(cfg)
-    d = _load_desc(name)
-    if cfg.mat_dtype == "q8_0":
-        assert d is not None, f"{os.path.basename(make_fullsize.desc_path(name))} not generated"
-    sample_bar = np.full(steps + 1, t) if d is None else np.maximum(t, 1.5 * d["sample_dist"])
-    full_bar = {s: t for s in full} if d is None else \
-        {int(s): max(t, 1.5 * float(d["full_dist"][i])) for i, s in enumerate(d["full_steps"])}
     worst, worst_ratio = 0.0, 0.0
     nxt = gpu.prefill(toks)
     for s in range(steps + 1):
