@@ -642,31 +642,20 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
 
-    // Waits until at most `pend` later stages of this wave's DMAs are in
-    // flight and its LDS reads have returned, then for every wave.
-    auto wait_bar = [&](int pend) {
-        // s_waitcnt immediates (vmcnt n, lgkmcnt 0, expcnt unconstrained); as
-        // builtins the compiler's own wait bookkeeping sees them
-        const int n = pend * (Q8 ? ND + 1 : ND);
+    // Waits until at most PEND later stages of this wave's DMAs are in flight
+    // and its LDS reads have returned, then for every wave. The s_waitcnt
+    // immediate (vmcnt n, lgkmcnt 0, expcnt unconstrained) is a compile-time
+    // constant, so a loop built from these waits has no branch in it and the
+    // compiler's own wait bookkeeping sees each one on every path.
+    auto wait_c = [&](auto pend_c) {
+        constexpr int n = decltype(pend_c)::value * (Q8 ? ND + 1 : ND);
+        static_assert(n >= 0 && n < 64, "vmcnt holds 6 bits");
+        constexpr int imm = (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14);
+        // the previous step's products stay before the wait: moved past the
+        // barrier they would leave that step with reads and no products
+        __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        if (n >= 24)
-            __builtin_amdgcn_s_waitcnt(0x4078);
-        else if (n >= 16)
-            __builtin_amdgcn_s_waitcnt(0x4070);
-        else if (n >= 15)
-            __builtin_amdgcn_s_waitcnt(0x007F);
-        else if (n >= 12)
-            __builtin_amdgcn_s_waitcnt(0x007C);
-        else if (n >= 10)
-            __builtin_amdgcn_s_waitcnt(0x007A);
-        else if (n >= 8)
-            __builtin_amdgcn_s_waitcnt(0x0078);
-        else if (n >= 5)
-            __builtin_amdgcn_s_waitcnt(0x0075);
-        else if (n >= 4)
-            __builtin_amdgcn_s_waitcnt(0x0074);
-        else
-            __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_waitcnt(imm);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
@@ -731,28 +720,76 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
     // Stage s lives in ring slot s % HL_ST. The fragments of step ks are read
     // during step ks - 1, so while step ks multiplies, the slots hold steps
     // ks+1 (landed) .. ks+HL_ST (in flight).
+    using std::integral_constant;
+    static_assert(HL_ST == 4, "the prologue and the last steps below are written for a four-stage ring");
     for (int p = 0; p < HL_ST && p < nk; p++) issue(p);
-    wait_bar(min(HL_ST - 1, nk - 1));
+    // stage 0 has landed once at most min(HL_ST, nk) - 1 later stages remain
+    if (nk >= 4)
+        wait_c(integral_constant<int, 3>{});
+    else if (nk == 3)
+        wait_c(integral_constant<int, 2>{});
+    else if (nk == 2)
+        wait_c(integral_constant<int, 1>{});
+    else
+        wait_c(integral_constant<int, 0>{});
     Frag F0, F1;
     fread(0, F0);
     // One K step: wait for the next step's stage (the last step re-reads its
     // own), refill the slot this step was read from, read the next fragments,
     // multiply the current ones. No branch guards the reads or the products,
     // so the compiler keeps one register assignment and a partial LDS wait.
-    auto step = [&](int ks, Frag& cur, Frag& nxt) {
-        wait_bar(min(HL_ST - 2, max(nk - 2 - ks, 0)));
-        if (ks + HL_ST < nk) issue(ks + HL_ST);
+    // With HL_ST - 1 stages issued ahead, step ks needs stage ks + 1 with at
+    // most min(HL_ST - 2, nk - 2 - ks) later stages still in flight: the
+    // steady steps (a refill each) wait with HL_ST - 2 in flight, the last
+    // min(nk, HL_ST) steps (no refills) with none. (Exact counts there, 2, 1,
+    // 0, 0, made the compiler spill the fragments in every instance.)
+    auto step = [&](int ks, Frag& cur, Frag& nxt, auto pend_c, auto refill_c) {
+        wait_c(pend_c);
+        if constexpr (decltype(refill_c)::value) issue(ks + HL_ST);
         fread(min(ks + 1, nk - 1), nxt);
-        // keep the reads ahead of the products, so LDS and the matrix cores
-        // work at the same time
-        __builtin_amdgcn_sched_barrier(0);
-        fmma(cur);
+        if constexpr (Q8) {
+            // reads first, then the products and their scale folds (the
+            // interleaved order below needs more registers than a Q8_0 step
+            // has left)
+            __builtin_amdgcn_sched_barrier(0);
+            fmma(cur);
+        } else {
+            fmma(cur);
+            // the next step's fragment reads interleaved with this step's
+            // products, a few at a time: a wave that issued all its reads
+            // first would stall on the full LDS queue before its first
+            // product (mask 0x100: LDS reads, 0x008: MFMA)
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
     };
-    for (int ks = 0; ks + 1 < nk; ks += 2) {
-        step(ks, F0, F1);
-        step(ks + 1, F1, F0);
+    using P0 = integral_constant<int, 0>;
+    using P1 = integral_constant<int, 1>;
+    using P2 = integral_constant<int, 2>;
+    using Refill = std::true_type;
+    using NoRefill = std::false_type;
+    const int nsteady = nk > HL_ST ? nk - HL_ST : 0;
+    int ks = 0;
+    for (; ks + 1 < nsteady; ks += 2) {
+        step(ks, F0, F1, P2{}, Refill{});
+        step(ks + 1, F1, F0, P2{}, Refill{});
     }
-    if (nk & 1) step(nk - 1, F0, F1);
+    if (ks < nsteady) {
+        step(ks, F0, F1, P2{}, Refill{});
+        ks++;
+        F0 = F1;
+    }
+    for (; ks + 1 < nk; ks += 2) {
+        step(ks, F0, F1, P0{}, NoRefill{});
+        step(ks + 1, F1, F0, P0{}, NoRefill{});
+    }
+    if (ks < nk) step(ks, F0, F1, P0{}, NoRefill{});
 
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
