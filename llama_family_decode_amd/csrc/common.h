@@ -305,4 +305,33 @@ hipError_t launch_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int
                                int neox, int n_ctx, const float2* rope, float* Q, __half* kc, __half* vc,
                                hipStream_t s);
 
+// Value of lane l ^ M, for a compile-time M: DPP quad permutes for 1 and 2,
+// swizzles (within 32 lanes) for 4, 8 and 16, the gfx950 half swap for 32.
+// None of them goes through an LDS address computation as a bpermute does.
+template <int M>
+__device__ __forceinline__ uint32_t xshfl_u(uint32_t v) {
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    } else if constexpr (M == 4 || M == 8 || M == 16) {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));    // bitmask mode, xor M
+    } else {
+        static_assert(M == 32, "xor offset");
+        // swaps lanes 32..63 of the first operand with lanes 0..31 of the second
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (threadIdx.x & 32) ? r[0] : r[1];
+    }
+}
+template <int M>
+__device__ __forceinline__ float xshfl(float v) { return __uint_as_float(xshfl_u<M>(__float_as_uint(v))); }
+template <int M>
+__device__ __forceinline__ int xshfl(int v) { return (int)xshfl_u<M>((uint32_t)v); }
+template <int M>
+__device__ __forceinline__ double xshfl(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const uint32_t lo = xshfl_u<M>((uint32_t)b), hi = xshfl_u<M>((uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
 }  // namespace llm

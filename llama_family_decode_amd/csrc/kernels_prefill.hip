@@ -921,6 +921,7 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // each) that write their rows' (m, l, unnormalised o) to part, [row][head]
 // [split][2 + 64]; k_attn_prefill_merge then combines the splits.
 constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72, PA_PLD = 68;
+constexpr float kPaInvDiv = 0.125f;  // 1 / (float)sqrt(64), exact
 #ifndef LLM_PA_CHUNKS
 #define LLM_PA_CHUNKS 32
 #endif
@@ -932,6 +933,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                                                            int n_heads, int n_kv_heads, int n_ctx, float scale_div,
                                                            SpanCfg span, int cps, float* part) {
     constexpr int hd = 64;
+    (void)scale_div;  // always 8 here (checked at launch): the scores are multiplied by kPaInvDiv
     __shared__ __attribute__((aligned(16))) __half Ks[PA_CH * PA_LD];   // [position][dim]
     __shared__ __attribute__((aligned(16))) __half Vt[hd * PA_LD];      // [dim][position]
     __shared__ __attribute__((aligned(16))) float Ps[4][16 * PA_PLD];   // per wave [row][position]
@@ -965,6 +967,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
     int rpos[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) rpos[i] = p0 + z0 + (16 * wave + 4 * lq + i) / G;
+
     float m_run[4], l_run[4];
     float4v o[4];
 #pragma unroll
@@ -975,6 +978,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
     }
 
     const int last = p0 + min(z0 + TB, n_q) - 1;  // the block's last position
+    const int rfirst = p0 + z0;                     // and its first
     const int nch = last / PA_CH + 1;
     // chunks in use: with a window, the sink chunks (below the first row's
     // window) and then the chunks from the first row's window start on;
@@ -1048,7 +1052,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const int t = c0 + 16 * pt + lr;
-                    const float e = span_has(span, t, rpos[i]) ? expf(sc[pt][i] / scale_div - Mrow[i]) / Lrow[i] : 0.f;
+                    const float e = span_has(span, t, rpos[i]) ? expf(sc[pt][i] * kPaInvDiv - Mrow[i]) / Lrow[i] : 0.f;
                     P[(4 * lq + i) * PA_PLD + 16 * pt + lr] = round16(e);
                 }
 #pragma unroll
@@ -1066,7 +1070,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             continue;
         }
         // online softmax per row; a row's 64 scores sit in the 16 lanes with
-        // the same lq, four tiles each
+        // the same lq, four tiles each. A chunk every row of the block
+        // attends in full needs no mask: all of it at or before the block's
+        // first position (causal) and, with a window, after the window start
+        // of its last position (rows past the last position are padding,
+        // never stored).
+        const bool full = c0 + PA_CH - 1 <= rfirst && (span.window <= 0 || c0 > last - span.window);
         float alpha[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -1074,12 +1083,15 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
 #pragma unroll
             for (int pt = 0; pt < 4; pt++) {
                 const int t = c0 + 16 * pt + lr;
-                const float s = span_has(span, t, rpos[i]) ? sc[pt][i] / scale_div : -INFINITY;
+                const float s = full || span_has(span, t, rpos[i]) ? sc[pt][i] * kPaInvDiv : -INFINITY;
                 sc[pt][i] = s;
                 mx = fmaxf(mx, s);
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            // over the 16 lanes of the row (offsets 1, 2, 4, 8: DPP and swizzles)
+            mx = fmaxf(mx, xshfl<1>(mx));
+            mx = fmaxf(mx, xshfl<2>(mx));
+            mx = fmaxf(mx, xshfl<4>(mx));
+            mx = fmaxf(mx, xshfl<8>(mx));
             const float m_new = fmaxf(m_run[i], mx);
             alpha[i] = m_run[i] == -INFINITY ? 0.f : expf(m_run[i] - m_new);
             float ls = 0.f;
@@ -1089,8 +1101,10 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                 sc[pt][i] = e;
                 ls += e;
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) ls += __shfl_xor(ls, off, 64);
+            ls += xshfl<1>(ls);
+            ls += xshfl<2>(ls);
+            ls += xshfl<4>(ls);
+            ls += xshfl<8>(ls);
             l_run[i] = l_run[i] * alpha[i] + ls;
             m_run[i] = m_new;
         }
@@ -1192,7 +1206,10 @@ hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __ha
                                     int n_ctx, float scale_div, const SpanCfg& span, bool rnd, float* ws,
                                     size_t ws_floats, hipStream_t s) {
     const int G = n_kv_heads > 0 ? n_heads / n_kv_heads : 0;
-    if (head_dim != 64 || G < 1 || G > PA_ROWS || PA_ROWS % G || n_heads % n_kv_heads || n_q <= 0)
+    // the kernel multiplies the scores by 1/8: exactly the division by
+    // (float)sqrt(64) = 8, a power of two
+    if (head_dim != 64 || scale_div != 8.0f || G < 1 || G > PA_ROWS || PA_ROWS % G || n_heads % n_kv_heads ||
+        n_q <= 0)
         return hipErrorInvalidValue;
     const int TB = PA_ROWS / G;
     const dim3 grid(n_kv_heads, (n_q + TB - 1) / TB);  // KV head, query-row block from the last
