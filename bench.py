@@ -355,6 +355,20 @@ def main():
     print(f"# decode {tok_s:.1f} tok/s ({1e3 * dt / args.steps:.3f} ms/token), step bytes {step_bytes / 1e6:.1f} MB "
           f"-> {step_bytes * tok_s / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # ABI-level decode: one llm_decode call per token, each returning the next
+    # token to the host (a 4-byte copy and a stream synchronisation), logits
+    # left on the device
+    abi_steps = min(64, args.steps)
+    t = nxt
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(abi_steps):
+        t = model.decode(int(t), ctx_len + i, want_next=True, copy_logits=False)
+    abi_dt = time.perf_counter() - t0
+    model.rewind(ctx_len)
+    print(f"# llm_decode per token (host round trip each): {abi_steps / abi_dt:.1f} tok/s", file=sys.stderr,
+          flush=True)
+
     # the dominant (only) decode kernel, timed with HIP events on its stream
     kind = llm.llm_op_step_kind(model.ctx)
     ms_step = model.time_stage(llm.STAGE_STEP, 0, mid_pos, 50)
@@ -366,6 +380,21 @@ def main():
     model.rewind(ctx_len)
     model.close()
     del model
+    torch.cuda.empty_cache()
+
+    # device-to-device copy of 1 GiB (reads and writes it): the chip's measured
+    # streaming rate beside the 8 TB/s specification
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    ev1.record()
+    ev1.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 10 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
     torch.cuda.empty_cache()
 
     prefill = None
@@ -414,6 +443,9 @@ def main():
         "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
                      "bytes_per_launch": step_bytes, "ms_per_launch": round(ms_step, 5), "position": mid_pos},
+        "abi_decode": {"tok_s": round(abi_steps / abi_dt, 1), "steps": abi_steps,
+                       "note": "llm_decode once per token, next token returned to the host each call"},
+        "device_copy_GBs": round(copy_gbs, 1),
         "prefill": prefill,
         "prefill_q8_0_2048": {"config": cfg.name, "tokens": ctx_len, "ms": round(q8_prefill * 1e3, 3),
                               "tok_s": round(ctx_len / q8_prefill, 1)},
