@@ -24,8 +24,9 @@ V = f64: every sum accumulated in double and rounded once, liboracle_f64.so),
 teacher-forced with the stored tokens, and writes ``fullsize_<name>_<V>.npz``:
 at every step the largest |difference| of its logits from the stored ones over
 the sample (``sample_dist``) and over the whole vector at the stored steps
-(``full_dist``). That is how far the rounding of the sums alone moves this
-workload's logits.
+(``full_dist``), and its own binary16 K and V of every layer at the stored
+positions (``kv_k`` / ``kv_v``). That is how far the rounding of the sums alone
+moves this workload's logits and cache.
 
 Usage: python tests/golden/make_fullsize.py [--variant desc|f64] [workload ...]   (default: all)
 The 8192-position prompt takes the oracle about 70 minutes on 8 cores.
@@ -164,8 +165,15 @@ def make_variant(name: str, variant: str):
         record(s_, m.forward(int(g["tokens"][s_ - 1]), P + s_ - 1))
         if s_ % 16 == 0:
             print(f"[{name} {variant}] decode step {s_}/{steps}", flush=True)
+    kvp = [int(p) for p in g["kv_pos"]]
+    kk = np.zeros_like(g["kv_k"])
+    vv = np.zeros_like(g["kv_v"])
+    for i, p in enumerate(kvp):
+        for l in range(cfg.n_layers):
+            kk[i, l], vv[i, l] = m.kv_read(l, p)
     np.savez_compressed(variant_path(name, variant), config=np.array(cfg.name), sample_dist=sd,
-                        full_steps=np.array(full_steps, np.int32), full_dist=fd)
+                        full_steps=np.array(full_steps, np.int32), full_dist=fd, kv_pos=np.array(kvp, np.int32),
+                        kv_k=kk, kv_v=vv)
     m.close()
     print(f"[{name} {variant}] median {np.median(sd):.2e} max {sd.max():.2e}; written in {time.time() - t0:.1f}s",
           flush=True)
