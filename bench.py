@@ -267,6 +267,33 @@ def measure_decode_report(llm, synth, np, torch, cfg, ctx_len, steps=64, reps=3)
             "hbm_frac": round(b * tok_s / 1e9 / HBM_PEAK_GBS, 4), "step_kind": kind}
 
 
+def measure_prefill_q8_llamacpp(llm, synth, np, torch, n=2048, reps=3):
+    """llm_prefill of the headline workload's 2048 ids with llama.cpp's
+    rounding points: the Q8_0 products on the integer matrix cores."""
+    cfg = synth.C4.with_(name="llama-1b-q8_0-llamacpp", numerics=1)
+    m = llm.Model(cfg, synth.make_tensor_set(cfg))
+    int8 = llm.llm_op_prefill_int8(m.ctx)
+    toks = synth.prompt(cfg, n)
+    m.prefill(toks)
+    m.reset()
+    times = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        m.prefill(toks)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        m.reset()
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    dt = float(np.median(times))
+    print(f"# prefill {n} (Q8_0, llama.cpp rounding points, integer products {int8}): {dt * 1e3:.2f} ms",
+          file=sys.stderr, flush=True)
+    return {"config": cfg.name, "tokens": n, "ms": round(dt * 1e3, 3), "tok_s": round(n / dt, 1),
+            "integer_products": int8}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +307,9 @@ def main():
                          "Q8_0 1B with RoPE frequency factors)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill measurement (512 ids, Qwen2-style F16 1B) and print it as JSON")
+    ap.add_argument("--prefill-llamacpp", action="store_true",
+                    help="only run the 2048-id prompt pass of the Q8_0 1B model with llama.cpp's rounding points "
+                         "(integer matrix-core products) and print it as JSON")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 5 device-to-device copies of this many bytes (the reference kernel that scales "
                          "the HBM counters) and exit")
@@ -304,6 +334,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(f"# copied {args.copy_bytes} bytes 5 times", file=sys.stderr)
+        return
+    if args.prefill_llamacpp:
+        print(json.dumps({"prefill_q8_0_2048_llamacpp": measure_prefill_q8_llamacpp(llm, synth, np, torch)}))
         return
     if args.prefill_only:
         print(json.dumps({"prefill": measure_prefill(llm, synth, np, torch)}))
@@ -415,6 +448,7 @@ def main():
                    measure_decode_report(llm, synth, np, torch,
                                          synth.C4.with_(name="llama-1b-q8_0-yarn16", yarn_factor=16.0,
                                                         yarn_orig_ctx=16384), 2048)]
+        reports.append({"prefill_q8_0_2048_llamacpp": measure_prefill_q8_llamacpp(llm, synth, np, torch)})
 
     cpu = None
     if not args.no_cpu:

@@ -112,6 +112,16 @@ int llm_op_step_kind(llm_ctx* ctx);
  * many rows. No context needed; never fails. */
 int llm_op_prefill_chunk(void);
 
+/* Whether the context's prefill runs its Q8_0 layer products as integer
+ * matrix-core products ("What a Llama model computes, and why", sections 5 and
+ * 8: activations rounded to 8-bit Q8_0 blocks and dotted with the 8-bit
+ * weights as integers): 1 when the model has Q8_0 layer matrices and
+ * numerics = 1 (each 32-deep block's exact int32 sum times the two block
+ * scales, from the int8 codes), 0 otherwise (the float numerics' products on
+ * the binary16 codes, or F16/F32 layers). Returns a negative LLM_ERR_* for a
+ * NULL context. */
+int llm_op_prefill_int8(llm_ctx* ctx);
+
 /* Wall-clock stamps (100 MHz device clock) that block 0 of the last decode-step
  * launch took at its start and after each of its 5*n_layers + 1 barriers:
  * stamp k+1 - stamp k is the time of phase k (per layer: QKV, attention,

@@ -30,7 +30,7 @@ ERRORS = {
 EXPORTS = ["llm_plan", "llm_load_weights", "llm_decode", "llm_prefill", "llm_prefill_rows", "llm_generate", "llm_reset", "llm_free",
            "llm_last_error", "llm_logits", "llm_kv_len", "llm_kv_read", "llm_op_qkv", "llm_op_attention", "llm_op_o",
            "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind", "llm_op_step_trace",
-           "llm_op_step_kind", "llm_op_prefill_chunk", "llm_op_attention_noalloc"]
+           "llm_op_step_kind", "llm_op_prefill_chunk", "llm_op_prefill_int8", "llm_op_attention_noalloc"]
 STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_FFN_UP, STAGE_DOWN, STAGE_LOGITS, STAGE_STEP = range(7)
 
 
@@ -106,6 +106,8 @@ def lib():
         L.llm_op_step_kind.restype = ctypes.c_int
         L.llm_op_prefill_chunk.argtypes = []
         L.llm_op_prefill_chunk.restype = ctypes.c_int
+        L.llm_op_prefill_int8.argtypes = [vp]
+        L.llm_op_prefill_int8.restype = ctypes.c_int
         for f in ("llm_op_qkv", "llm_op_attention", "llm_op_attention_noalloc", "llm_op_o", "llm_op_ffn_up", "llm_op_down", "llm_op_logits",
                   "llm_op_kv_write", "llm_op_time", "llm_rewind"):
             getattr(L, f).restype = ctypes.c_int
@@ -292,6 +294,14 @@ def llm_op_step_kind(ctx) -> int:
 def llm_op_prefill_chunk() -> int:
     """Rows per prefill batch."""
     return int(lib().llm_op_prefill_chunk())
+
+
+def llm_op_prefill_int8(ctx) -> int:
+    """1 when the context's prefill runs its Q8_0 products as integer matrix-core products."""
+    r = lib().llm_op_prefill_int8(ctx)
+    if r < 0:
+        raise LlmError(r, "llm_op_prefill_int8")
+    return r
 
 
 def llm_op_step_trace(ctx, n_layers: int) -> np.ndarray:

@@ -20,6 +20,8 @@ struct Mat {
     const uint16_t* s;
     const void* wt;  // the prefill products' tiled binary16 copy (Q8_0: of the codes), or nullptr
     const void* st;  // Q8_0 with wt: the block scales, [256-row tile][K step][256] binary16
+    const void* wi;  // Q8_0 under llama.cpp's rounding points: the tiled int8 codes, or nullptr
+    const float* si; // with wi: the block scales as fp32, [256-row tile][K step][256]
 };
 
 // Tiled binary16 layout of the prefill products' operands: rows in tiles of
@@ -38,6 +40,22 @@ __host__ __device__ inline size_t tile_off(int m, int k, int K, int TM) {
 inline size_t tiled_w_bytes(int rows, int cols) { return (size_t)((rows + kTileW - 1) / kTileW) * kTileW * cols * 2; }
 inline size_t tiled_s_bytes(int rows, int cols) {
     return (size_t)((rows + kTileW - 1) / kTileW) * kTileW * (cols / 32) * 2;
+}
+// Tiled int8 layout of Q8_0 codes (the integer products of llama.cpp's
+// rounding points): rows in tiles of TM, K in steps of 32; tile t, step ks is
+// one contiguous TM x 32-byte piece, row-major (row r's 32 codes at 32 r).
+// The block scales of activation rows: [128-row tile][K step][128] fp32.
+__host__ __device__ inline size_t tile_off_i8(int m, int k, int K, int TM) {
+    const int nk = K >> 5, t = m / TM;
+    return (((size_t)t * nk + (k >> 5)) * TM + (m - t * TM)) * 32 + (k & 31);
+}
+__host__ __device__ inline size_t tile_off_s(int m, int kb, int K, int TM) {
+    const int t = m / TM;
+    return ((size_t)t * (K >> 5) + kb) * TM + (m - t * TM);
+}
+inline size_t tiled_i8_bytes(int rows, int cols) { return (size_t)((rows + kTileW - 1) / kTileW) * kTileW * cols; }
+inline size_t tiled_sf_bytes(int rows, int cols) {
+    return (size_t)((rows + kTileW - 1) / kTileW) * kTileW * (cols / 32) * 4;
 }
 
 // Attention span and temperature of the config: the query at position p
@@ -268,7 +286,11 @@ hipError_t launch_split_hl(const float* X, int n, int K, __half* H, __half* L, h
 // llama.cpp's rounding of the n x K fp32 product inputs X for weights of type
 // dtype (Q8_0: each 32-block to its quantized values; F16: to binary16), in
 // place; H, L (if set) get the rounded rows' tiled hi/lo planes.
-hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __half* L, hipStream_t s);
+// With C and CS (Q8_0 only) the rounded rows' codes and block scales go to the
+// tiled int8 layout instead, and X is left as it was (the integer product
+// reads only the codes).
+hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __half* L, hipStream_t s,
+                             int8_t* C = nullptr, float* CS = nullptr);
 // The tiled copy of an F16 matrix (rows padded with zeros to a multiple of 256).
 // Fills W.wt (and for Q8_0 W.st) from W's stored rows.
 hipError_t launch_tile_w(const Mat& W, hipStream_t s);
@@ -286,6 +308,11 @@ struct GemmA {
     const float* f;
     const __half* h;
     const __half* l;
+    // llama.cpp's rounding points with Q8_0 weights: the rows' Q8_0 codes
+    // (tiled int8, kTileA rows) and block scales (the binary16 scale as fp32),
+    // or nullptr
+    const int8_t* c;
+    const float* cs;
 };
 // Y[n][rows] op= A[n][K] * W^T: F16 weights on the matrix cores with the
 // hi/lo activation planes, Q8_0 on the matrix cores splitting the fp32 rows,

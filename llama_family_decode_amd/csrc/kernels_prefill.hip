@@ -160,35 +160,65 @@ hipError_t launch_reduce_norm_rows(const float* P, int S, int n, float* X, int d
     return hipGetLastError();
 }
 
-// One element per thread; a Q8_0 block of 32 is 32 consecutive lanes, whose
-// maximum magnitude comes from a shuffle reduction within them.
-__global__ __launch_bounds__(256) void k_round_rows(float* X, int K, int dtype, __half* H, __half* L) {
-    const int row = blockIdx.x, i = blockIdx.y * 256 + threadIdx.x;
-    if (i >= K) return;  // K is a multiple of 32: whole 32-lane groups leave together
-    float* x = X + (size_t)row * K;
-    float v = x[i];
+// Eight consecutive elements of one row per thread (two 16-byte loads); a
+// Q8_0 block of 32 is one DPP quad of lanes, whose maximum magnitude comes from
+// two quad permutes. The rounded values go back to X when keep_x is set; with
+// C (Q8_0) the codes go to the tiled int8 layout (8 bytes per thread) and each
+// block's scale (its binary16 rounding, as fp32) to CS; H, L get the rounded
+// rows' tiled hi/lo planes (one 16-byte slot each per thread).
+__global__ __launch_bounds__(256) void k_round_rows(float* X, int K, int dtype, int keep_x, __half* H, __half* L,
+                                                    int8_t* C, float* CS) {
+    const int row = blockIdx.y, i = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= K) return;  // K is a multiple of 32: a block's quad leaves together
+    float* x = X + (size_t)row * K + i;
+    const float4 a = *(const float4*)x, b = *(const float4*)(x + 4);
+    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     if (dtype == DT_Q8) {
-        float amax = fabsf(v);
+        float amax = 0.f;
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-        const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f;
-        v = round16(d) * roundf(v * id);
+        for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(v[e]));
+        amax = fmaxf(amax, xshfl<1>(amax));
+        amax = fmaxf(amax, xshfl<2>(amax));
+        const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f, dh = round16(d);
+        uint32_t q[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            const float code = roundf(v[e] * id);
+            q[e >> 2] |= (uint32_t)(uint8_t)(int8_t)code << (8 * (e & 3));
+            v[e] = dh * code;
+        }
+        if (C) {
+            *(uint2*)(C + tile_off_i8(row, i, K, kTileA)) = make_uint2(q[0], q[1]);
+            if ((i & 31) == 0) CS[tile_off_s(row, i >> 5, K, kTileA)] = dh;
+        }
     } else {
-        v = round16(v);
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] = round16(v[e]);
     }
-    x[i] = v;
+    if (keep_x) {
+        *(float4*)x = make_float4(v[0], v[1], v[2], v[3]);
+        *(float4*)(x + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
     if (H) {
-        const __half h = __float2half_rn(v);
+        __half h[8], l[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            h[e] = __float2half_rn(v[e]);
+            l[e] = __float2half_rn(v[e] - __half2float(h[e]));
+        }
         const size_t t = tile_off(row, i, K, kTileA);
-        H[t] = h;
-        L[t] = __float2half_rn(v - __half2float(h));
+        *(uint4*)(H + t) = *(const uint4*)h;
+        *(uint4*)(L + t) = *(const uint4*)l;
     }
 }
 
-hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __half* L, hipStream_t s) {
+hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __half* L, hipStream_t s, int8_t* C,
+                             float* CS) {
     if (dtype == DT_F32 || n <= 0) return hipSuccess;
-    if (K % 32) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_round_rows, dim3(n, (K + 255) / 256), dim3(256), 0, s, X, K, dtype, H, L);
+    if (K % 32 || (C && (dtype != DT_Q8 || !CS))) return hipErrorInvalidValue;
+    // with codes the product reads only them (its K steps are the 32-blocks)
+    const int keep_x = C ? 0 : 1;
+    hipLaunchKernelGGL(k_round_rows, dim3((K + 2047) / 2048, n), dim3(256), 0, s, X, K, dtype, keep_x, H, L, C, CS);
     return hipGetLastError();
 }
 
@@ -246,6 +276,18 @@ __global__ void k_tile_q8(const int8_t* W, int rows, int cols, int rows_pad, __h
     *(uint4*)(T + tile_off(n, k, cols, kTileW)) = *(const uint4*)h;
 }
 
+// The same codes as int8 in the tiled int8 layout: one 16-byte piece (half a
+// row's 32-code step) per thread; rows past the matrix become zeros.
+__global__ void k_tile_i8(const int8_t* W, int rows, int cols, int rows_pad, int8_t* T) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int cpr = cols >> 4;
+    if (i >= (size_t)rows_pad * cpr) return;
+    const int n = (int)(i / cpr), k = (int)(i % cpr) * 16;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (n < rows) v = *(const uint4*)(W + (size_t)n * cols + k);
+    *(uint4*)(T + tile_off_i8(n, k, cols, kTileW)) = v;
+}
+
 // Q8_0 block scales ([rows][cols/32] binary16 bits) as [tile][K step][256]:
 // the 256 scales a product tile needs for one 32-deep step are contiguous.
 __global__ void k_tile_scales(const uint16_t* S, int rows, int nkb, int rows_pad, uint16_t* T) {
@@ -256,22 +298,42 @@ __global__ void k_tile_scales(const uint16_t* S, int rows, int nkb, int rows_pad
     T[((size_t)t * nkb + kb) * kTileW + r] = n < rows ? S[(size_t)n * nkb + kb] : (uint16_t)0;
 }
 
+// The same scales as fp32 (the integer products' copy).
+__global__ void k_tile_scales_f32(const uint16_t* S, int rows, int nkb, int rows_pad, float* T) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)rows_pad * nkb) return;
+    const int n = (int)(i % rows_pad), kb = (int)(i / rows_pad);
+    const int t = n / kTileW, r = n % kTileW;
+    T[((size_t)t * nkb + kb) * kTileW + r] = n < rows ? __half2float(__ushort_as_half(S[(size_t)n * nkb + kb])) : 0.f;
+}
+
 hipError_t launch_tile_w(const Mat& W, hipStream_t s) {
-    if ((W.dtype != DT_F16 && W.dtype != DT_Q8) || W.cols % 32 || !W.wt) return hipErrorInvalidValue;
+    if ((W.dtype != DT_F16 && W.dtype != DT_Q8) || W.cols % 32 || (!W.wt && !W.wi)) return hipErrorInvalidValue;
     const int rows_pad = (W.rows + kTileW - 1) / kTileW * kTileW;
     const size_t total = (size_t)rows_pad * (W.cols / 8);
     const unsigned grid = (unsigned)((total + 255) / 256);
     if (W.dtype == DT_F16) {
+        if (!W.wt) return hipErrorInvalidValue;
         hipLaunchKernelGGL(k_tile_w, dim3(grid), dim3(256), 0, s, (const __half*)W.w, W.rows, W.cols, rows_pad,
                            (__half*)W.wt);
         return hipGetLastError();
     }
-    if (!W.st) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_tile_q8, dim3(grid), dim3(256), 0, s, (const int8_t*)W.w, W.rows, W.cols, rows_pad,
-                       (__half*)W.wt);
     const size_t ns = (size_t)rows_pad * (W.cols / 32);
-    hipLaunchKernelGGL(k_tile_scales, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s, W.s, W.rows, W.cols / 32,
-                       rows_pad, (uint16_t*)W.st);
+    if (W.wt) {  // binary16 codes and scales (the float numerics' products)
+        if (!W.st) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_tile_q8, dim3(grid), dim3(256), 0, s, (const int8_t*)W.w, W.rows, W.cols, rows_pad,
+                           (__half*)W.wt);
+        hipLaunchKernelGGL(k_tile_scales, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s, W.s, W.rows,
+                           W.cols / 32, rows_pad, (uint16_t*)W.st);
+    }
+    if (W.wi) {  // int8 codes and fp32 scales (the integer products)
+        if (!W.si) return hipErrorInvalidValue;
+        const size_t n16 = (size_t)rows_pad * (W.cols / 16);
+        hipLaunchKernelGGL(k_tile_i8, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s, (const int8_t*)W.w, W.rows,
+                           W.cols, rows_pad, (int8_t*)W.wi);
+        hipLaunchKernelGGL(k_tile_scales_f32, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, s, W.s, W.rows,
+                           W.cols / 32, rows_pad, (float*)W.si);
+    }
     return hipGetLastError();
 }
 
@@ -816,6 +878,205 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
     }
 }
 
+// ------------------------------------------------------------ MFMA GEMM, int8
+// The Q8_0 products under llama.cpp's rounding points ("What a Llama model
+// computes, and why", sections 5 and 8: the activations rounded to 8-bit
+// blocks and dotted with the 8-bit weights as integers): both operands are
+// Q8_0 codes in the tiled int8 layout, one 32-deep K step is one Q8_0 block on
+// both sides, and each step's int32 sums (exact, below 2^24 in magnitude)
+// join the fp32 accumulator times d_w * d_x (two binary16 scales: their
+// product is exact in fp32). Block tile 128 (m) x 256 (n), eight waves in a
+// 2 x 4 arrangement, each 64 x 64 = 2 x 2 tiles of v_mfma_i32_32x32x32_i8
+// (lane l supplies row l%32's codes 16(l/32) .. +15 of the step; the result
+// has the f32 32x32 layout). A stage holds the step's activation codes (4 KB),
+// weight codes (8 KB), then the 128 activation and 256 weight scales as fp32
+// (1.5 KB); an eight-stage DMA ring moves it, two DMAs per wave (a step is
+// consumed faster than one of the binary16 kernel, so the ring holds more).
+constexpr int I8_SW = 4096, I8_SS = 12288, I8_STAGE = 13824, I8_ST = 8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+template <int EPI>
+__global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const float* As, int M, int kz, int nm,
+                                                 int nn, float* Y, int ldy, const float* bias, __half* Yh, __half* Yl,
+                                                 float* P, const int* ymap) {
+    __shared__ __attribute__((aligned(1024))) char lds[I8_ST * I8_STAGE];
+    const int N = W.rows, K = W.cols;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // tiles that share a weight tile are dealt to one XCD and start together
+    int q = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) q = (q & 7) * (nb >> 3) + (q >> 3);
+    const int mt = q % nm, nt = (q / nm) % nn;
+    const int z = blockIdx.y;
+    const int m0 = mt * HL_M, n0 = nt * HL_N, kb = z * kz;
+    const int nkK = K / HL_K, kbs = kb / HL_K;
+
+    // this wave's two DMAs per stage: waves 0-3 activation rows 32w .. 32w+31
+    // and weight rows 32w .. +31; waves 4-7 weight rows 32w .. +31 and 384
+    // bytes of the scales (lanes 0-23)
+    const char* src0;
+    const char* src1 = nullptr;
+    size_t adv0, adv1 = 0;
+    int dst0, dst1;
+    const size_t wtile = ((size_t)nt * nkK + kbs) * HL_N * 32;  // weight codes of step kbs, tile nt
+    if (wave < 4) {
+        src0 = (const char*)Ac + (((size_t)mt * nkK + kbs) * HL_M + 32 * wave) * 32 + lane * 16;
+        adv0 = (size_t)HL_M * 32;
+        dst0 = 1024 * wave;
+        src1 = (const char*)W.wi + wtile + (size_t)(32 * wave) * 32 + lane * 16;
+        adv1 = (size_t)HL_N * 32;
+        dst1 = I8_SW + 1024 * wave;
+    } else {
+        src0 = (const char*)W.wi + wtile + (size_t)(32 * wave) * 32 + lane * 16;
+        adv0 = (size_t)HL_N * 32;
+        dst0 = I8_SW + 1024 * wave;
+        const int b = 384 * (wave - 4) + 16 * lane;  // byte of the stage's scales this lane moves
+        dst1 = I8_SS + 384 * (wave - 4);
+        if (lane < 24) {
+            if (b < 4 * HL_M) {
+                src1 = (const char*)(As + ((size_t)mt * nkK + kbs) * HL_M) + b;
+                adv1 = (size_t)HL_M * 4;
+            } else {
+                src1 = (const char*)(W.si + ((size_t)nt * nkK + kbs) * HL_N) + (b - 4 * HL_M);
+                adv1 = (size_t)HL_N * 4;
+            }
+        }
+    }
+    const int nk = kz / HL_K;
+    auto issue = [&](int ks) {
+        char* st = lds + (ks % I8_ST) * I8_STAGE;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src0 + adv0 * ks),
+                                         (__attribute__((address_space(3))) void*)(st + dst0), 16, 0, 0);
+        if (src1)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src1 + adv1 * ks),
+                                             (__attribute__((address_space(3))) void*)(st + dst1), 16, 0, 0);
+    };
+    // waits until at most PEND later stages of this wave's DMAs are in
+    // flight and its LDS reads have returned, then for every wave
+    auto wait_c = [&](auto pend_c) {
+        constexpr int n = decltype(pend_c)::value * 2;
+        constexpr int imm = (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(imm);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
+    struct Frag {
+        i32x4 a[2], b[2];  // [tile]
+        float dw[2];       // the weight scale of this lane's column, per tile
+        float4 dx[2][4];   // the activation scales of this lane's 16 rows, per tile
+    };
+    auto fread = [&](int ks, Frag& F) {
+        const char* st = lds + (ks % I8_ST) * I8_STAGE;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int r = 64 * wm + 32 * i;
+            F.a[i] = *(const i32x4*)(st + (r + r32) * 32 + 16 * h);
+#pragma unroll
+            for (int g = 0; g < 4; g++) F.dx[i][g] = *(const float4*)(st + I8_SS + 4 * (r + 8 * g + 4 * h));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int c = 64 * wn + 32 * j + r32;
+            F.b[j] = *(const i32x4*)(st + I8_SW + c * 32 + 16 * h);
+            F.dw[j] = *(const float*)(st + I8_SS + 4 * HL_M + 4 * c);
+        }
+    };
+    float16v acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+    auto fmma = [&](const Frag& F) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            float dx[16];
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                dx[4 * g] = F.dx[i][g].x;
+                dx[4 * g + 1] = F.dx[i][g].y;
+                dx[4 * g + 2] = F.dx[i][g].z;
+                dx[4 * g + 3] = F.dx[i][g].w;
+            }
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const i32x16 t = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.a[i], F.b[j], (i32x16){}, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 16; e++) acc[i][j][e] += (float)t[e] * (F.dw[j] * dx[e]);
+            }
+        }
+    };
+    using std::integral_constant;
+    for (int p = 0; p < I8_ST && p < nk; p++) issue(p);
+    // stage 0 has landed once at most I8_ST - 1 later stages remain (a K
+    // shorter than the ring waits for all of them)
+    if (nk >= I8_ST)
+        wait_c(integral_constant<int, I8_ST - 1>{});
+    else
+        wait_c(integral_constant<int, 0>{});
+    Frag F0, F1;
+    fread(0, F0);
+    // one K step: wait for the next step's stage, refill the slot this step
+    // was read from, read the next fragments, multiply the current ones (the
+    // steady steps with I8_ST - 2 later stages in flight, the last ones with
+    // none)
+    auto step = [&](int ks, Frag& cur, Frag& nxt, auto pend_c, auto refill_c) {
+        wait_c(pend_c);
+        if constexpr (decltype(refill_c)::value) issue(ks + I8_ST);
+        fread(min(ks + 1, nk - 1), nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        fmma(cur);
+    };
+    using P0 = integral_constant<int, 0>;
+    using PS = integral_constant<int, I8_ST - 2>;
+    const int nsteady = nk > I8_ST ? nk - I8_ST : 0;
+    int ks = 0;
+    for (; ks + 1 < nsteady; ks += 2) {
+        step(ks, F0, F1, PS{}, std::true_type{});
+        step(ks + 1, F1, F0, PS{}, std::true_type{});
+    }
+    if (ks < nsteady) {
+        step(ks, F0, F1, PS{}, std::true_type{});
+        ks++;
+        F0 = F1;
+    }
+    for (; ks + 1 < nk; ks += 2) {
+        step(ks, F0, F1, P0{}, std::false_type{});
+        step(ks + 1, F1, F0, P0{}, std::false_type{});
+    }
+    if (ks < nk) step(ks, F0, F1, P0{}, std::false_type{});
+
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int n = n0 + 64 * wn + 32 * j + r32;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+                const float v = acc[i][j][e];
+                if (P) {
+                    if (m < M && n < N) P[((size_t)z * M + m) * N + n] = v;
+                } else if constexpr (EPI == EPI_SWIGLU) {
+                    const float up = __shfl_xor(v, 1, 64);
+                    if ((lane & 1) == 0 && m < M && n < N) store_swiglu(Y, Yh, Yl, m, n / 2, ldy, v, up);
+                } else if (m < M && n < N) {
+                    if constexpr (EPI == EPI_RESID)
+                        Y[(size_t)m * ldy + n] += v;
+                    else
+                        Y[(size_t)out_row(ymap, m) * ldy + n] = bias ? v + bias[n] : v;
+                }
+            }
+        }
+    }
+}
+
 // Splits of K for an M x N product on tiles of tm x tn: K is halved until the
 // blocks fill three quarters of the 256 compute units (one block each; past
 // that a split adds a round of blocks plus the reduction and gains nothing),
@@ -839,7 +1100,12 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
     if (defer) *defer = 0;
     const int N = W.rows, K = W.cols;
     int S = 1;
-    if (W.dtype == DT_F32) {
+    if (W.dtype == DT_Q8 && W.wi && W.si && A.c && A.cs && K % HL_K == 0) {
+        S = gemm_splits(n, N, K, HL_M, HL_N, 8, ws_floats);
+        const int nm = (n + HL_M - 1) / HL_M, nn = (N + HL_N - 1) / HL_N;
+        hipLaunchKernelGGL((k_gemm_i8<EPI>), dim3(nm * nn, S), dim3(512), 0, s, W, A.c, A.cs, n, K / S, nm, nn, Y, ldy,
+                           bias, Yh, Yl, S > 1 ? ws : nullptr, ymap);
+    } else if (W.dtype == DT_F32) {
         dim3 grid((N + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
         hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl, ymap);
     } else if ((W.dtype == DT_F16 || (W.dtype == DT_Q8 && W.st)) && W.wt && A.h && K % HL_K == 0) {

@@ -223,6 +223,8 @@ struct Layout {
     unsigned long long* strace;
     float *X, *Hf, *QKV, *Q, *Of, *Uf, *ws;
     __half *Hh, *Hl, *Oh, *Ol, *Uh, *Ul;  // binary16 hi/lo planes of Hf, Of, Uf
+    int8_t* Ci;                           // rounding mode: Q8_0 codes of a product's input rows (tiled int8)
+    float* Cs;                            // and their block scales (fp32), or nullptr
     float* Xc;                            // the wanted rows' residuals (last prefill layer)
     float* attn_stats;                    // span max and sum per (row, head) of the rounded passes
     int* xcd;                             // the XCD of each step-kernel block (load-time check)
@@ -242,14 +244,26 @@ Mat place_mat(Arena& A, int dtype, int rows, int cols) {
     m.s = dtype == DT_Q8 ? (const uint16_t*)A.take(mat_bytes_s(dtype, rows, cols)) : nullptr;
     m.wt = nullptr;
     m.st = nullptr;
+    m.wi = nullptr;
+    m.si = nullptr;
     return m;
 }
 
 // Layer matrices in F16 also get the tiled copy the prefill products read.
-// Q8_0 ones get binary16 codes (exact) plus their block scales per K step.
-void place_tiled(Arena& A, Mat& m) {
-    if ((m.dtype == DT_F16 || m.dtype == DT_Q8) && m.cols % 32 == 0) m.wt = A.take(tiled_w_bytes(m.rows, m.cols));
-    if (m.dtype == DT_Q8 && m.wt) m.st = A.take(tiled_s_bytes(m.rows, m.cols));
+// Q8_0 ones get binary16 codes (exact) plus their block scales per K step, or
+// under llama.cpp's rounding points (numerics 1), whose products are integer,
+// the tiled int8 codes plus their scales as fp32.
+void place_tiled(Arena& A, Mat& m, int numerics) {
+    if (m.cols % 32) return;
+    if (m.dtype == DT_F16) {
+        m.wt = A.take(tiled_w_bytes(m.rows, m.cols));
+    } else if (m.dtype == DT_Q8 && !numerics) {
+        m.wt = A.take(tiled_w_bytes(m.rows, m.cols));
+        m.st = A.take(tiled_s_bytes(m.rows, m.cols));
+    } else if (m.dtype == DT_Q8) {
+        m.wi = A.take(tiled_i8_bytes(m.rows, m.cols));
+        m.si = (const float*)A.take(tiled_sf_bytes(m.rows, m.cols));
+    }
 }
 
 int decode_splits(const llm_config* c) {
@@ -266,7 +280,7 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.embd = place_mat(W, V.embd->dtype, c->vocab, c->dim);
     L.out_norm = (const float*)W.take((size_t)c->dim * 4);
     L.out = V.out ? place_mat(W, V.out->dtype, c->vocab, c->dim) : L.embd;
-    place_tiled(W, L.out);  // for the batched vocabulary product of chosen prompt rows
+    place_tiled(W, L.out, c->numerics);  // for the batched vocabulary product of chosen prompt rows
     L.rope_freqs = V.rope_freqs ? (const float*)W.take((size_t)(c->rope_dims / 2) * 4) : nullptr;
     L.layers.resize(c->n_layers);
     for (int l = 0; l < c->n_layers; l++) {
@@ -279,10 +293,10 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
         D.ffn_norm = (const float*)W.take((size_t)c->dim * 4);
         D.gu = place_mat(W, S.gate->dtype, 2 * c->ffn, c->dim);
         D.down = place_mat(W, S.down->dtype, c->dim, c->ffn);
-        place_tiled(W, D.qkv);
-        place_tiled(W, D.o);
-        place_tiled(W, D.gu);
-        place_tiled(W, D.down);
+        place_tiled(W, D.qkv, c->numerics);
+        place_tiled(W, D.o, c->numerics);
+        place_tiled(W, D.gu, c->numerics);
+        place_tiled(W, D.down, c->numerics);
     }
     L.wbytes = W.off;
 
@@ -345,6 +359,16 @@ void make_layout(const llm_config* c, const Validated& V, void* wb, void* kb, vo
     L.sel = (int*)S.take((size_t)c->n_ctx * 4);
     L.selo = (int*)S.take((size_t)c->n_ctx * 4);
     L.Ul = (__half*)S.take((size_t)C * c->ffn * 2);
+    // the rounding mode's Q8_0 codes and scales of one product's input rows
+    // (the widest input: dim, q or ffn columns)
+    L.Ci = nullptr;
+    L.Cs = nullptr;
+    if (c->numerics) {
+        int kmax = c->dim > qd ? c->dim : qd;
+        if (c->ffn > kmax) kmax = c->ffn;
+        L.Ci = (int8_t*)S.take((size_t)C * kmax);
+        L.Cs = (float*)S.take((size_t)C * (kmax / 32) * 4);
+    }
     // split-K partials (up to 8 splits) of the prefill products with at most
     // max(q|k|v, dim) rows
     L.ws_floats = (size_t)8 * C * (qd + 2 * kvd > c->dim ? qd + 2 * kvd : c->dim);
@@ -714,9 +738,9 @@ int llm_load_weights(const llm_config* cfg, const llm_tensor* tensors, int32_t n
     for (int l = 0; ok && l < cfg->n_layers; l++) {
         const LayerW& D = L.layers[l];
         for (const Mat* m : {&D.qkv, &D.o, &D.gu, &D.down})
-            if (m->wt) ok = ok && launch_tile_w(*m, s) == hipSuccess;
+            if (m->wt || m->wi) ok = ok && launch_tile_w(*m, s) == hipSuccess;
     }
-    if (ok && L.out.wt) ok = launch_tile_w(L.out, s) == hipSuccess;
+    if (ok && (L.out.wt || L.out.wi)) ok = launch_tile_w(L.out, s) == hipSuccess;
     if (!ok) return bail(LLM_ERR_DEVICE, "weight upload failed");
 
     // ---- RoPE table and zeroed state
@@ -871,6 +895,16 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
     // with rounded inputs an F16 product's lo plane is zero: one matrix-core pass
     // (a rounded Q8_0 input, f16(d) * code, still needs both planes)
     auto lo = [rnd](const Mat& w, const __half* l) { return rnd && w.dtype == DT_F16 ? nullptr : l; };
+    // with rounded inputs a Q8_0 product takes them as Q8_0 codes and runs on
+    // the integer matrix cores (int8 codes times int8 codes per block)
+    auto codes = [&](const Mat& w) { return rnd && w.dtype == DT_Q8 && w.wi && L.Ci; };
+    auto ga = [&](const Mat& w, const float* f, const __half* h, const __half* l) {
+        return codes(w) ? GemmA{f, h, lo(w, l), L.Ci, L.Cs} : GemmA{f, h, lo(w, l), nullptr, nullptr};
+    };
+    auto round_rows = [&](float* X, int rows, int K, const Mat& w, __half* H, __half* Lp) {
+        return codes(w) ? launch_round_rows(X, rows, K, w.dtype, nullptr, nullptr, s, L.Ci, L.Cs)
+                        : launch_round_rows(X, rows, K, w.dtype, H, Lp, s);
+    };
     // the wanted rows grouped by chunk, output order kept within a chunk:
     // c->sel_out[p] = output index, c->sel_row[p] = prompt row
     c->sel_out.clear();
@@ -903,8 +937,8 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             __half* vc = L.vc + (size_t)l * L.kv_layer;
             if (!normed) HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
             normed = false;
-            if (rnd) HIPCHK(c, launch_round_rows(L.Hf, m, cf.dim, W.qkv.dtype, L.Hh, L.Hl, s));
-            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, GemmA{L.Hf, L.Hh, lo(W.qkv, L.Hl)}, m, L.QKV, qkvd, W.bqkv, nullptr,
+            if (rnd) HIPCHK(c, round_rows(L.Hf, m, cf.dim, W.qkv, L.Hh, L.Hl));
+            HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, ga(W.qkv, L.Hf, L.Hh, L.Hl), m, L.QKV, qkvd, W.bqkv, nullptr,
                                   nullptr, L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
                                           cf.rope_neox, cf.n_ctx, L.rope, L.Q, kc, vc, s));
@@ -938,24 +972,24 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             // residual over mr rows (attention outputs `of`, residuals X)
             auto post_attention = [&](const float* of, float* X, int mr) -> int {
                 if (rnd)
-                    HIPCHK(c, launch_round_rows((float*)of, mr, qd, W.o.dtype, L.Oh, L.Ol, s));
+                    HIPCHK(c, round_rows((float*)of, mr, qd, W.o, L.Oh, L.Ol));
                 else if (W.o.wt && (last || !mfma_attn))  // the planes the tiled product reads
                     HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
                 // a split-K output product's reduction is fused with the FFN norm
                 int S = 0;
-                HIPCHK(c, launch_gemm(EPI_RESID, W.o, GemmA{of, L.Oh, lo(W.o, L.Ol)}, mr, X, cf.dim, nullptr, nullptr,
+                HIPCHK(c, launch_gemm(EPI_RESID, W.o, ga(W.o, of, L.Oh, L.Ol), mr, X, cf.dim, nullptr, nullptr,
                                       nullptr, L.ws, L.ws_floats, s, nullptr, &S));
                 if (S)
                     HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, W.ffn_norm, cf.eps, L.Hf, L.Hh, L.Hl, s));
                 else
                     HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
-                if (rnd) HIPCHK(c, launch_round_rows(L.Hf, mr, cf.dim, W.gu.dtype, L.Hh, L.Hl, s));
-                HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, GemmA{L.Hf, L.Hh, lo(W.gu, L.Hl)}, mr, L.Uf, cf.ffn, nullptr, L.Uh,
+                if (rnd) HIPCHK(c, round_rows(L.Hf, mr, cf.dim, W.gu, L.Hh, L.Hl));
+                HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, ga(W.gu, L.Hf, L.Hh, L.Hl), mr, L.Uf, cf.ffn, nullptr, L.Uh,
                                       L.Ul, L.ws, L.ws_floats, s));
-                if (rnd) HIPCHK(c, launch_round_rows(L.Uf, mr, cf.ffn, W.down.dtype, L.Uh, L.Ul, s));
+                if (rnd) HIPCHK(c, round_rows(L.Uf, mr, cf.ffn, W.down, L.Uh, L.Ul));
                 // before another layer a split-K down product's reduction is
                 // fused with that layer's attention norm
-                HIPCHK(c, launch_gemm(EPI_RESID, W.down, GemmA{L.Uf, L.Uh, lo(W.down, L.Ul)}, mr, X, cf.dim, nullptr,
+                HIPCHK(c, launch_gemm(EPI_RESID, W.down, ga(W.down, L.Uf, L.Uh, L.Ul), mr, X, cf.dim, nullptr,
                                       nullptr, nullptr, L.ws, L.ws_floats, s, nullptr, last ? nullptr : &S));
                 if (!last && S) {
                     HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, L.layers[l + 1].attn_norm, cf.eps, L.Hf,
@@ -980,9 +1014,9 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 if (d_rows) {
                     // product rows land at their output indices
                     HIPCHK(c, launch_rmsnorm_rows(L.Xc, L.out_norm, kb, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
-                    if (rnd) HIPCHK(c, launch_round_rows(L.Hf, kb, cf.dim, L.out.dtype, L.Hh, L.Hl, s));
-                    HIPCHK(c, launch_gemm(EPI_STORE, L.out, GemmA{L.Hf, L.Hh, lo(L.out, L.Hl)}, kb, d_rows, cf.vocab,
-                                          nullptr, nullptr, nullptr, L.ws, L.ws_floats, s, L.selo + sb + b0));
+                    if (rnd) HIPCHK(c, round_rows(L.Hf, kb, cf.dim, L.out, L.Hh, L.Hl));
+                    HIPCHK(c, launch_gemm(EPI_STORE, L.out, ga(L.out, L.Hf, L.Hh, L.Hl), kb, d_rows, cf.vocab, nullptr,
+                                          nullptr, nullptr, L.ws, L.ws_floats, s, L.selo + sb + b0));
                 } else {
                     // the one wanted row (the prompt's last) through the decode
                     // vocabulary kernel and argmax
@@ -1191,6 +1225,12 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
 }
 
 int llm_op_prefill_chunk(void) { return kPrefillChunk; }
+
+int llm_op_prefill_int8(llm_ctx* c) {
+    int rc = check_ctx(c);
+    if (rc) return rc;
+    return c->cfg.numerics && c->L.Ci && !c->L.layers.empty() && c->L.layers[0].qkv.wi ? 1 : 0;
+}
 
 int llm_op_step_kind(llm_ctx* c) {
     int rc = check_ctx(c);

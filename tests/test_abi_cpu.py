@@ -10,7 +10,7 @@ import pytest
 
 import synth
 from conftest import ROOT
-from helpers import SMALL, SMALL_Q8, drop, f32_tensor
+from helpers import SMALL, SMALL_Q8, SMALL_Q8_RND, drop, f32_tensor
 
 llm = pytest.importorskip("llama_family_decode_amd")
 
@@ -73,6 +73,25 @@ def test_plan_sizes():
     w8, _, _ = plan(SMALL_Q8, ts8)
     raw8 = sum(t.nbytes for t in ts8) + tiled_bytes(SMALL_Q8, True)
     assert raw8 <= w8 <= raw8 + 64 * 1024
+
+
+def test_plan_q8_llamacpp_sizes():
+    # under llama.cpp's rounding points a Q8_0 layer matrix gets the tiled int8
+    # codes and fp32 block scales of the integer prefill products instead of
+    # the binary16 copy, and the scratch arena holds one batch's input codes
+    # (int8) and scales (fp32) for the widest product input
+    cfg, cfg0 = SMALL_Q8_RND, SMALL_Q8
+    ts = synth.make_tensor_set(cfg)
+    w, _, s = plan(cfg, ts)
+    pad = lambda r: (r + 255) // 256 * 256
+    mats = [(cfg.q_dim + 2 * cfg.kv_dim, cfg.dim), (cfg.dim, cfg.q_dim), (2 * cfg.ffn, cfg.dim), (cfg.dim, cfg.ffn)]
+    tiled = cfg.n_layers * sum(pad(r) * c + pad(r) * (c // 32) * 4 for r, c in mats)
+    raw = sum(t.nbytes for t in ts) + tiled
+    assert raw <= w <= raw + 64 * 1024
+    _, _, s0 = plan(cfg0, synth.make_tensor_set(cfg0))
+    C, kmax = llm.llm_op_prefill_chunk(), max(cfg.dim, cfg.q_dim, cfg.ffn)
+    a256 = lambda b: (b + 255) // 256 * 256
+    assert s - s0 == a256(C * kmax) + a256(C * (kmax // 32) * 4)
 
 
 def test_plan_1b_q8_sizes():
