@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+INT8_MFMA_PEAK_TOPS = 5000.0  # dense
 
 
 def span_rows(cfg, pos):
@@ -165,6 +166,23 @@ def cpu_baseline(cfg, ctx_len, budget_s=8.0):
                       f"Qwen2-style F16 1B model, as one prompt pass"}
 
 
+def product_fractions(llm, model, cfg, n_rows, peak, n_launch=20):
+    """Each prefill product of layer 0 over n_rows rows, timed with HIP events
+    on the context's stream (llm_op_time_prefill_product): average us per
+    launch, algorithmic TFLOP/s (2 * rows * outputs * inputs, the lo pass not
+    counted) and its fraction of the dense matrix-core peak."""
+    shapes = {"qkv": (llm.PRODUCT_QKV, cfg.q_dim + 2 * cfg.kv_dim, cfg.dim),
+              "o": (llm.PRODUCT_O, cfg.dim, cfg.q_dim),
+              "gate_up": (llm.PRODUCT_GATE_UP, 2 * cfg.ffn, cfg.dim),
+              "down": (llm.PRODUCT_DOWN, cfg.dim, cfg.ffn)}
+    out = {}
+    for name, (prod, n_out, n_in) in shapes.items():
+        ms = model.time_product(prod, n_rows, 0, n_launch)
+        tf = 2.0 * n_rows * n_out * n_in / (ms * 1e-3) / 1e12
+        out[name] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac": round(tf / peak, 4)}
+    return out
+
+
 def measure_prefill(llm, synth, np, torch, reps=5):
     """llm_prefill of 512 seeded ids on the Qwen2-style F16 1B model from an
     empty cache, median of `reps`, and llm_prefill_rows of the same ids with
@@ -197,6 +215,7 @@ def measure_prefill(llm, synth, np, torch, reps=5):
         rtimes.append(time.perf_counter() - t0)
         pm.reset()
     rt = float(np.median(rtimes))
+    products = product_fractions(llm, pm, c5, 512, F16_MFMA_PEAK_TFLOPS)
     # GEMM FLOPs the pass needs: the last layer's output product and FFN run
     # on the one row whose logits are read (on all 512 for every row's logits)
     qkv = c5.dim * (c5.q_dim + 2 * c5.kv_dim)
@@ -226,9 +245,10 @@ def measure_prefill(llm, synth, np, torch, reps=5):
     del pn
     torch.cuda.empty_cache()
     print(f"# prefill 512: {pt * 1e3:.2f} ms, {512 / pt:.0f} tok/s; with all 512 logit rows {rt * 1e3:.2f} ms; "
-          f"with llama.cpp's rounding points {nt * 1e3:.2f} ms", file=sys.stderr, flush=True)
+          f"with llama.cpp's rounding points {nt * 1e3:.2f} ms; products at 512 rows: "
+          + ", ".join(f"{k} {v['us']} us ({v['frac']:.3f})" for k, v in products.items()), file=sys.stderr, flush=True)
     return {"config": c5.name, "tokens": 512, "ms": round(pt * 1e3, 3), "tok_s": round(512 / pt, 1),
-            "gemm_tflop": round(gemm_flop / 1e12, 4),
+            "gemm_tflop": round(gemm_flop / 1e12, 4), "products_512_rows": products,
             "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
             "all_rows_ms": round(rt * 1e3, 3), "all_rows_gemm_tflop": round(rows_flop / 1e12, 4),
             "all_rows_mfma_frac": round(rows_flop / rt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
@@ -284,14 +304,16 @@ def measure_prefill_q8_llamacpp(llm, synth, np, torch, n=2048, reps=3):
         torch.cuda.synchronize()
         times.append(time.perf_counter() - t0)
         m.reset()
+    products = product_fractions(llm, m, cfg, n, INT8_MFMA_PEAK_TOPS if int8 else F16_MFMA_PEAK_TFLOPS)
     m.close()
     del m
     torch.cuda.empty_cache()
     dt = float(np.median(times))
-    print(f"# prefill {n} (Q8_0, llama.cpp rounding points, integer products {int8}): {dt * 1e3:.2f} ms",
+    print(f"# prefill {n} (Q8_0, llama.cpp rounding points, integer products {int8}): {dt * 1e3:.2f} ms; products "
+          + ", ".join(f"{k} {v['us']} us ({v['frac']:.3f} of the int8 peak)" for k, v in products.items()),
           file=sys.stderr, flush=True)
     return {"config": cfg.name, "tokens": n, "ms": round(dt * 1e3, 3), "tok_s": round(n / dt, 1),
-            "integer_products": int8}
+            "integer_products": int8, "products": products}
 
 
 def main():
@@ -363,6 +385,10 @@ def main():
     q8_prefill = float(np.median(q8_times))
     print(f"# prefill {ctx_len} (Q8_0): {q8_prefill * 1e3:.2f} ms, {ctx_len / q8_prefill:.0f} tok/s", file=sys.stderr,
           flush=True)
+    # each of its layer products alone (the batch buffers only; the cache is untouched)
+    q8_products = product_fractions(llm, model, cfg, ctx_len, F16_MFMA_PEAK_TFLOPS)
+    print("# prefill products at 2048 rows: " + ", ".join(f"{k} {v['us']} us ({v['frac']:.3f} of the f16 peak)"
+                                                           for k, v in q8_products.items()), file=sys.stderr, flush=True)
 
     # warmup (then rewind to the prefilled length)
     if args.warmup > 0:
@@ -482,7 +508,7 @@ def main():
         "device_copy_GBs": round(copy_gbs, 1),
         "prefill": prefill,
         "prefill_q8_0_2048": {"config": cfg.name, "tokens": ctx_len, "ms": round(q8_prefill * 1e3, 3),
-                              "tok_s": round(ctx_len / q8_prefill, 1)},
+                              "tok_s": round(ctx_len / q8_prefill, 1), "products": q8_products},
         "decode_reports": reports,
         "cpu_baseline": cpu,
     }

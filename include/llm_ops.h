@@ -92,6 +92,27 @@ int llm_op_kv_write(llm_ctx* ctx, int32_t layer, int32_t pos0, int32_t n_pos, co
  * pos of every layer. Waits. */
 int llm_op_time(llm_ctx* ctx, int32_t stage, int32_t layer, int32_t pos, int32_t n_launch, float* h_ms);
 
+/* The prompt pass's products of one layer ("What a Llama model computes, and
+ * why", section 5: prefill is the same products over a batch of rows). */
+#define LLM_PRODUCT_QKV 0     /* q|k|v rows (+ bias), stored */
+#define LLM_PRODUCT_O 1       /* output product, added to the residual */
+#define LLM_PRODUCT_GATE_UP 2 /* gate|up rows + SwiGLU */
+#define LLM_PRODUCT_DOWN 3    /* down product, added to the residual */
+
+/* Average device time in milliseconds of one launch of prefill product
+ * `product` (LLM_PRODUCT_*) of `layer` over n_rows rows (1 <= n_rows <=
+ * llm_op_prefill_chunk()), over n_launch back-to-back launches bracketed by
+ * HIP events on the context's stream: the matrix-core kernel the prompt pass
+ * runs for that product, with the same operands (the rounding mode's codes
+ * included) and epilogue, over the context's own batch buffers as inputs
+ * (their contents do not affect the time). A residual product split over K
+ * leaves its partial sums in the workspace, as in the prompt pass, whose next
+ * RMSNorm adds them; that reduction is not timed. The context's cache and
+ * kv_len are untouched, but the batch buffers are overwritten. Waits. Returns
+ * LLM_ERR_ARG for a bad product, layer, row count, launch count or pointer. */
+int llm_op_time_prefill_product(llm_ctx* ctx, int32_t product, int32_t layer, int32_t n_rows, int32_t n_launch,
+                                float* h_ms);
+
 /* Which kernel runs the context's decode steps: 0 for the captured launch
  * graph (six launches per layer plus the logits), 1 for the persistent step
  * kernel (one launch per token), 2 for a persistent step kernel

@@ -30,8 +30,10 @@ ERRORS = {
 EXPORTS = ["llm_plan", "llm_load_weights", "llm_decode", "llm_prefill", "llm_prefill_rows", "llm_generate", "llm_reset", "llm_free",
            "llm_last_error", "llm_logits", "llm_kv_len", "llm_kv_read", "llm_op_qkv", "llm_op_attention", "llm_op_o",
            "llm_op_ffn_up", "llm_op_down", "llm_op_logits", "llm_op_kv_write", "llm_op_time", "llm_rewind", "llm_op_step_trace",
-           "llm_op_step_kind", "llm_op_prefill_chunk", "llm_op_prefill_int8", "llm_op_attention_noalloc"]
+           "llm_op_step_kind", "llm_op_prefill_chunk", "llm_op_prefill_int8", "llm_op_attention_noalloc",
+           "llm_op_time_prefill_product"]
 STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_FFN_UP, STAGE_DOWN, STAGE_LOGITS, STAGE_STEP = range(7)
+PRODUCT_QKV, PRODUCT_O, PRODUCT_GATE_UP, PRODUCT_DOWN = range(4)
 
 
 class LlmError(RuntimeError):
@@ -99,6 +101,7 @@ def lib():
         L.llm_op_logits.argtypes = [vp, vp, vp, P(i32)]
         L.llm_op_kv_write.argtypes = [vp, i32, i32, i32, vp, vp]
         L.llm_op_time.argtypes = [vp, i32, i32, i32, i32, P(ctypes.c_float)]
+        L.llm_op_time_prefill_product.argtypes = [vp, i32, i32, i32, i32, P(ctypes.c_float)]
         L.llm_rewind.argtypes = [vp, i32]
         L.llm_op_step_trace.argtypes = [vp, vp, i32]
         L.llm_op_step_trace.restype = ctypes.c_int
@@ -109,7 +112,7 @@ def lib():
         L.llm_op_prefill_int8.argtypes = [vp]
         L.llm_op_prefill_int8.restype = ctypes.c_int
         for f in ("llm_op_qkv", "llm_op_attention", "llm_op_attention_noalloc", "llm_op_o", "llm_op_ffn_up", "llm_op_down", "llm_op_logits",
-                  "llm_op_kv_write", "llm_op_time", "llm_rewind"):
+                  "llm_op_kv_write", "llm_op_time", "llm_op_time_prefill_product", "llm_rewind"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -296,6 +299,12 @@ def llm_op_prefill_chunk() -> int:
     return int(lib().llm_op_prefill_chunk())
 
 
+def llm_op_time_prefill_product(ctx, product: int, layer: int = 0, n_rows: int = 512, n_launch: int = 20) -> float:
+    ms = ctypes.c_float()
+    _check(lib().llm_op_time_prefill_product(ctx, product, layer, n_rows, n_launch, ctypes.byref(ms)), ctx)
+    return float(ms.value)
+
+
 def llm_op_prefill_int8(ctx) -> int:
     """1 when the context's prefill runs its Q8_0 products as integer matrix-core products."""
     r = lib().llm_op_prefill_int8(ctx)
@@ -414,3 +423,6 @@ class Model:
 
     def time_stage(self, stage: int, layer: int = 0, pos: int = 0, n_launch: int = 20) -> float:
         return llm_op_time(self.ctx, stage, layer, pos, n_launch)
+
+    def time_product(self, product: int, n_rows: int, layer: int = 0, n_launch: int = 20) -> float:
+        return llm_op_time_prefill_product(self.ctx, product, layer, n_rows, n_launch)

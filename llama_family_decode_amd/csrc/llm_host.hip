@@ -883,6 +883,21 @@ int llm_generate(llm_ctx* c, int32_t token, int32_t n_steps, int32_t* h_tokens) 
 // with d_rows the logits of output j go to d_rows[j*vocab] (vocabulary
 // product over the compact batch), else exactly one row (the last) is wanted
 // and goes through the decode vocabulary kernel and argmax.
+// With llama.cpp's rounding points (numerics 1) a Q8_0 product takes its
+// rounded inputs as Q8_0 codes and runs on the integer matrix cores (int8
+// codes times int8 codes per block).
+static bool prefill_codes(const llm_ctx* c, const Mat& w) {
+    return c->cfg.numerics && w.dtype == DT_Q8 && w.wi && c->L.Ci;
+}
+// The operand of a prefill product with input rows f and their hi/lo planes h,
+// l. With rounded inputs an F16 product's lo plane is zero: one matrix-core
+// pass (a rounded Q8_0 input, f16(d) * code, still needs both planes, unless
+// the product runs on its codes).
+static GemmA prefill_operand(const llm_ctx* c, const Mat& w, const float* f, const __half* h, const __half* l) {
+    const __half* lo = c->cfg.numerics && w.dtype == DT_F16 ? nullptr : l;
+    return prefill_codes(c, w) ? GemmA{f, h, lo, c->L.Ci, c->L.Cs} : GemmA{f, h, lo, nullptr, nullptr};
+}
+
 static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const std::vector<int32_t>& rows_out,
                         float* d_rows) {
     const llm_config& cf = c->cfg;
@@ -892,18 +907,12 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
     const int nr = (int)rows_out.size();
     int rc = LLM_OK;
     const bool rnd = cf.numerics != 0;  // llama.cpp's rounding of every product input
-    // with rounded inputs an F16 product's lo plane is zero: one matrix-core pass
-    // (a rounded Q8_0 input, f16(d) * code, still needs both planes)
-    auto lo = [rnd](const Mat& w, const __half* l) { return rnd && w.dtype == DT_F16 ? nullptr : l; };
-    // with rounded inputs a Q8_0 product takes them as Q8_0 codes and runs on
-    // the integer matrix cores (int8 codes times int8 codes per block)
-    auto codes = [&](const Mat& w) { return rnd && w.dtype == DT_Q8 && w.wi && L.Ci; };
     auto ga = [&](const Mat& w, const float* f, const __half* h, const __half* l) {
-        return codes(w) ? GemmA{f, h, lo(w, l), L.Ci, L.Cs} : GemmA{f, h, lo(w, l), nullptr, nullptr};
+        return prefill_operand(c, w, f, h, l);
     };
     auto round_rows = [&](float* X, int rows, int K, const Mat& w, __half* H, __half* Lp) {
-        return codes(w) ? launch_round_rows(X, rows, K, w.dtype, nullptr, nullptr, s, L.Ci, L.Cs)
-                        : launch_round_rows(X, rows, K, w.dtype, H, Lp, s);
+        return prefill_codes(c, w) ? launch_round_rows(X, rows, K, w.dtype, nullptr, nullptr, s, L.Ci, L.Cs)
+                                   : launch_round_rows(X, rows, K, w.dtype, H, Lp, s);
     };
     // the wanted rows grouped by chunk, output order kept within a chunk:
     // c->sel_out[p] = output index, c->sel_row[p] = prompt row
@@ -1220,6 +1229,53 @@ int llm_op_time(llm_ctx* c, int32_t stage, int32_t layer, int32_t pos, int32_t n
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (e != hipSuccess) return dev_fail(c, e, "llm_op_time");
+    *h_ms = ms / (float)n_launch;
+    return LLM_OK;
+}
+
+int llm_op_time_prefill_product(llm_ctx* c, int32_t product, int32_t layer, int32_t n_rows, int32_t n_launch,
+                                float* h_ms) {
+    int rc = check_layer(c, layer);
+    if (rc) return rc;
+    if (product < LLM_PRODUCT_QKV || product > LLM_PRODUCT_DOWN || n_rows < 1 || n_rows > kPrefillChunk ||
+        n_launch <= 0 || !h_ms)
+        return fail(c, LLM_ERR_ARG, "bad product, row count, launch count or pointer");
+    Layout& L = c->L;
+    const LayerW& W = L.layers[layer];
+    hipStream_t s = c->stream;
+    const int qkvd = c->qd + 2 * c->kvd;
+    // the prompt pass's operands and epilogues; a residual product's split-K
+    // partials stay in the workspace (the pass adds them in its next RMSNorm)
+    auto one = [&]() -> hipError_t {
+        int S = 0;
+        switch (product) {
+            case LLM_PRODUCT_QKV:
+                return launch_gemm(EPI_STORE, W.qkv, prefill_operand(c, W.qkv, L.Hf, L.Hh, L.Hl), n_rows, L.QKV, qkvd,
+                                   W.bqkv, nullptr, nullptr, L.ws, L.ws_floats, s);
+            case LLM_PRODUCT_O:
+                return launch_gemm(EPI_RESID, W.o, prefill_operand(c, W.o, L.Of, L.Oh, L.Ol), n_rows, L.X, c->cfg.dim,
+                                   nullptr, nullptr, nullptr, L.ws, L.ws_floats, s, nullptr, &S);
+            case LLM_PRODUCT_GATE_UP:
+                return launch_gemm(EPI_SWIGLU, W.gu, prefill_operand(c, W.gu, L.Hf, L.Hh, L.Hl), n_rows, L.Uf,
+                                   c->cfg.ffn, nullptr, L.Uh, L.Ul, L.ws, L.ws_floats, s);
+            default:
+                return launch_gemm(EPI_RESID, W.down, prefill_operand(c, W.down, L.Uf, L.Uh, L.Ul), n_rows, L.X,
+                                   c->cfg.dim, nullptr, nullptr, nullptr, L.ws, L.ws_floats, s, nullptr, &S);
+        }
+    };
+    HIPCHK(c, one());  // warm
+    hipEvent_t e0, e1;
+    HIPCHK(c, hipEventCreate(&e0));
+    HIPCHK(c, hipEventCreate(&e1));
+    hipError_t e = hipEventRecord(e0, s);
+    for (int i = 0; e == hipSuccess && i < n_launch; i++) e = one();
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (e != hipSuccess) return dev_fail(c, e, "llm_op_time_prefill_product");
     *h_ms = ms / (float)n_launch;
     return LLM_OK;
 }

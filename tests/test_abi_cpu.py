@@ -214,6 +214,9 @@ def test_null_context_calls():
     assert L.llm_kv_len(None) == -1
     assert L.llm_reset(None) == -1
     assert L.llm_decode(None, 0, 0, None, None) == -1
+    ms = ctypes.c_float()
+    assert L.llm_op_time_prefill_product(None, 0, 0, 128, 1, ctypes.byref(ms)) == -1
+    assert L.llm_op_prefill_int8(None) == -1
     L.llm_free(None)
 
 

@@ -19,6 +19,8 @@ points both sides round the same float inputs; where an input is itself
 computed (an RMSNorm output) and differs by an ulp, its rounded value may sit
 one step away, which the bounds allow twice per output row.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -237,3 +239,32 @@ def test_stage_argument_errors():
     assert L.llm_op_logits(gpu.ctx, None, None, None) == -1
     assert gpu.kv_len() == 0
     gpu.close()
+
+
+@pytest.mark.parametrize("cfg", [SMALL_F16, SMALL_Q8_RND], ids=lambda c: c.name)
+def test_time_prefill_product(cfg):
+    # every prompt-pass product times over one row, a whole 128-row tile and a
+    # ragged 300 rows; the cache is untouched, and a prompt pass afterwards
+    # gives the logits of a context that never ran the timing
+    ts = synth.make_tensor_set(cfg)
+    toks = synth.prompt(cfg, 6)
+    gpu, ref = llm.Model(cfg, ts), llm.Model(cfg, ts)
+    ref.prefill(toks)
+    gpu.prefill(toks)
+    for prod in (llm.PRODUCT_QKV, llm.PRODUCT_O, llm.PRODUCT_GATE_UP, llm.PRODUCT_DOWN):
+        for n in (1, 128, 300):
+            ms = gpu.time_product(prod, n, cfg.n_layers - 1, 2)
+            assert 0.0 < ms < 100.0, (prod, n, ms)
+    assert gpu.kv_len() == len(toks)
+    gpu.reset()
+    gpu.prefill(toks)
+    assert np.array_equal(gpu.logits().view(np.uint32), ref.logits().view(np.uint32))
+    L = llm.lib()
+    ms = ctypes.c_float()
+    chunk = llm.llm_op_prefill_chunk()
+    for args in ((4, 0, 1, 1), (-1, 0, 1, 1), (0, cfg.n_layers, 1, 1), (0, 0, 0, 1), (0, 0, chunk + 1, 1),
+                 (0, 0, 1, 0)):
+        assert L.llm_op_time_prefill_product(gpu.ctx, *args, ctypes.byref(ms)) == -1, args
+    assert L.llm_op_time_prefill_product(gpu.ctx, 0, 0, 1, 1, None) == -1
+    gpu.close()
+    ref.close()
