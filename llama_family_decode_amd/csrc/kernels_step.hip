@@ -313,15 +313,23 @@ __device__ __forceinline__ void stage_copy(const float* src, int K, float* xs) {
 // codes are taken), for F16 weights each element its binary16 value; F32
 // weights take the input as it is. K is a multiple of 32 and the staged input
 // starts at a block boundary, so the 32 lanes of a half-wave hold one block.
+// Maximum over the 32 lanes of a half-wave (one Q8_0 block): DPP quad
+// permutes and swizzles, none of which computes an LDS address.
+__device__ __forceinline__ float half_wave_max(float v) {
+    v = fmaxf(v, xshfl<1>(v));
+    v = fmaxf(v, xshfl<2>(v));
+    v = fmaxf(v, xshfl<4>(v));
+    v = fmaxf(v, xshfl<8>(v));
+    return fmaxf(v, xshfl<16>(v));
+}
+
 template <int DT>
 __device__ __forceinline__ void round_input(float* xs, int K) {
     if constexpr (DT != DT_F32) {
         for (int i = thread_id(); i < K; i += kSB) {
             float v = xs[swz<DT>(i)];
             if constexpr (DT == DT_Q8) {
-                float amax = fabsf(v);
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+                const float amax = half_wave_max(fabsf(v));
                 const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f;
                 v = round16(d) * roundf(v * id);
             } else {
@@ -366,9 +374,7 @@ __device__ __forceinline__ void round_input_i8(float* xs, int K) {
         dsc[j] = 0.f;
         if (i < K) {  // whole half-waves: K is a multiple of 32
             const float v = xs[swz<DT_Q8>(i)];
-            float amax = fabsf(v);
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            const float amax = half_wave_max(fabsf(v));
             const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f;
             code[j] = (int)roundf(v * id);
             dsc[j] = round16(d);
@@ -587,9 +593,8 @@ __device__ __forceinline__ void wbatch(const WRows& w, const int* rmap, int roff
                 acc += p;
         }
         if (cb == w.ncb - 1 && (FULL || k0 + k < w.nslots)) {  // the group's rows are complete
-            float v = acc;
+            float v = lane_sum_down(acc, w.lpr);
             acc = 0.f;
-            for (int o = w.lpr >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
             if constexpr (EM == EM_QKV || EM == EM_SWIGLU) {
                 if (w.rpi == 1) {
                     if (lane == 0) {
@@ -641,14 +646,15 @@ __device__ __forceinline__ int slot_lane(int s) {
 
 // One halving step of the transposed butterfly: lanes with bit M set keep the
 // upper half of the values, the others the lower half; each sends the half it
-// drops to lane ^ M and adds what it receives.
+// drops to lane ^ M and adds what it receives. The exchange is xshfl's (half
+// swap, swizzle or DPP), not an LDS permute.
 template <int M, int N>
 __device__ __forceinline__ void halve(const float (&in)[2 * N], float (&out)[N], int lane) {
     const bool up = lane & M;
 #pragma unroll
     for (int i = 0; i < N; i++) {
         const float send = up ? in[i] : in[i + N], keep = up ? in[i + N] : in[i];
-        out[i] = keep + __shfl_xor(send, M, 64);
+        out[i] = keep + xshfl<M>(send);
     }
 }
 
@@ -665,8 +671,8 @@ __device__ __forceinline__ float seg_reduce16(const float (&v)[16], int lane) {
     halve<L / 8, 2>(t4, t2, lane);
     halve<L / 16, 1>(t2, t1, lane);
     float t = t1[0];
-    if constexpr (L / 32 >= 1) t += __shfl_xor(t, L / 32, 64);
-    if constexpr (L / 64 >= 1) t += __shfl_xor(t, L / 64, 64);
+    if constexpr (L / 32 >= 1) t += xshfl<(L / 32 >= 1 ? L / 32 : 1)>(t);
+    if constexpr (L / 64 >= 1) t += xshfl<(L / 64 >= 1 ? L / 64 : 1)>(t);
     return t;
 }
 
