@@ -329,6 +329,8 @@ def main():
                          "Q8_0 1B with RoPE frequency factors)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill measurement (512 ids, Qwen2-style F16 1B) and print it as JSON")
+    ap.add_argument("--no-products", action="store_true",
+                    help="skip timing the 2048-row prompt pass's products one by one")
     ap.add_argument("--prefill-llamacpp", action="store_true",
                     help="only run the 2048-id prompt pass of the Q8_0 1B model with llama.cpp's rounding points "
                          "(integer matrix-core products) and print it as JSON")
@@ -386,9 +388,12 @@ def main():
     print(f"# prefill {ctx_len} (Q8_0): {q8_prefill * 1e3:.2f} ms, {ctx_len / q8_prefill:.0f} tok/s", file=sys.stderr,
           flush=True)
     # each of its layer products alone (the batch buffers only; the cache is untouched)
-    q8_products = product_fractions(llm, model, cfg, ctx_len, F16_MFMA_PEAK_TFLOPS)
-    print("# prefill products at 2048 rows: " + ", ".join(f"{k} {v['us']} us ({v['frac']:.3f} of the f16 peak)"
-                                                           for k, v in q8_products.items()), file=sys.stderr, flush=True)
+    q8_products = None
+    if not args.no_products:
+        q8_products = product_fractions(llm, model, cfg, ctx_len, F16_MFMA_PEAK_TFLOPS)
+        print("# prefill products at 2048 rows: " + ", ".join(f"{k} {v['us']} us ({v['frac']:.3f} of the f16 peak)"
+                                                               for k, v in q8_products.items()), file=sys.stderr,
+              flush=True)
 
     # warmup (then rewind to the prefilled length)
     if args.warmup > 0:
