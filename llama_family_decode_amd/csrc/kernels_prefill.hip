@@ -1263,13 +1263,14 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
     const int lp = tid >> 3, ld8 = (tid & 7) * 8;
     const u32x4p z4 = {0u, 0u, 0u, 0u};
     u32x4p kr[2], vr[2];
-    auto load = [&](int c0) {
+    // (V only where the pass weights it: the rounding mode's first pass reads K alone)
+    auto load = [&](int c0, bool with_v) {
 #pragma unroll
         for (int u = 0; u < 2; u++) {
             const int t = c0 + lp + 32 * u;
             const bool ok = t <= last;  // rows past the block's last position are never written yet
             kr[u] = ok ? *(const u32x4p*)(kbase + (size_t)t * hd + ld8) : z4;
-            vr[u] = ok ? *(const u32x4p*)(vbase + (size_t)t * hd + ld8) : z4;
+            if (with_v) vr[u] = ok ? *(const u32x4p*)(vbase + (size_t)t * hd + ld8) : z4;
         }
     };
     float* P = Ps[wave];
@@ -1284,19 +1285,22 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
     }
     // this block's share of the chunks
     const int v_begin = RND ? 0 : min(nv, (int)blockIdx.z * cps), v_end = RND ? nv : min(nv, v_begin + cps);
-    if (v_begin < v_end) load(chunk_of(v_begin) * PA_CH);
+    const bool with_v = !RND || pass == 1;
+    if (v_begin < v_end) load(chunk_of(v_begin) * PA_CH, with_v);
     for (int v = v_begin; v < v_end; v++) {
         const int c0 = chunk_of(v) * PA_CH;
         __syncthreads();  // the previous chunk's K, V and P reads are done
 #pragma unroll
         for (int u = 0; u < 2; u++) {
             *(u32x4p*)(Ks + (lp + 32 * u) * PA_LD + ld8) = kr[u];
-            const __half* vh = (const __half*)&vr[u];
+            if (with_v) {
+                const __half* vh = (const __half*)&vr[u];
 #pragma unroll
-            for (int j = 0; j < 8; j++) Vt[(ld8 + j) * PA_LD + lp + 32 * u] = vh[j];
+                for (int j = 0; j < 8; j++) Vt[(ld8 + j) * PA_LD + lp + 32 * u] = vh[j];
+            }
         }
         __syncthreads();
-        if (v + 1 < v_end) load(chunk_of(v + 1) * PA_CH);
+        if (v + 1 < v_end) load(chunk_of(v + 1) * PA_CH, with_v);
 
         // scores of this wave's 16 rows over the chunk: tile pt covers
         // positions c0 + 16 pt .. +15
@@ -1311,6 +1315,11 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                 if constexpr (!RND) sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], kf, sc[pt], 0, 0, 0);
             }
         }
+        // A chunk every row of the block attends in full needs no mask: all of
+        // it at or before the block's first position (causal) and, with a
+        // window, after the window start of its last position (rows past the
+        // last position are padding, never stored).
+        const bool full = c0 + PA_CH - 1 <= rfirst && (span.window <= 0 || c0 > last - span.window);
         if (RND && pass == 1) {
             // the rounded probabilities of the whole span, the P V operand as is
 #pragma unroll
@@ -1318,7 +1327,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const int t = c0 + 16 * pt + lr;
-                    const float e = span_has(span, t, rpos[i]) ? expf(sc[pt][i] * kPaInvDiv - Mrow[i]) / Lrow[i] : 0.f;
+                    const float e =
+                        full || span_has(span, t, rpos[i]) ? expf(sc[pt][i] * kPaInvDiv - Mrow[i]) / Lrow[i] : 0.f;
                     P[(4 * lq + i) * PA_PLD + 16 * pt + lr] = round16(e);
                 }
 #pragma unroll
@@ -1336,12 +1346,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             continue;
         }
         // online softmax per row; a row's 64 scores sit in the 16 lanes with
-        // the same lq, four tiles each. A chunk every row of the block
-        // attends in full needs no mask: all of it at or before the block's
-        // first position (causal) and, with a window, after the window start
-        // of its last position (rows past the last position are padding,
-        // never stored).
-        const bool full = c0 + PA_CH - 1 <= rfirst && (span.window <= 0 || c0 > last - span.window);
+        // the same lq, four tiles each
         float alpha[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
