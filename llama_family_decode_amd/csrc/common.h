@@ -276,9 +276,11 @@ struct PrefillBufs;
 hipError_t launch_embed_rows(const Mat& E, const int* tokens, int n, float* X, int dim, hipStream_t s);
 // Yf = rmsnorm(X) * gain per row; with Yh set also the binary16 hi/lo pair of
 // each output (Yh = f16(y), Yl = f16(y - Yh)) in the tiled layout, the
-// matrix-core input form.
+// matrix-core input form; with C and CS (dim a multiple of 32) the outputs'
+// Q8_0 codes and block scales in the tiled int8 layout, as launch_round_rows
+// writes them (the integer products' input). Yf and Yh may be nullptr.
 hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
-                               __half* Yl, hipStream_t s);
+                               __half* Yl, hipStream_t s, int8_t* C = nullptr, float* CS = nullptr);
 // dst[j][0..K) = src[idx[j]][0..K) for j < k (fp32 rows).
 hipError_t launch_gather_rows(const float* src, int K, const int* idx, int k, float* dst, hipStream_t s);
 // H, L = the tiled binary16 hi/lo planes of the n x K fp32 rows X.
@@ -296,7 +298,8 @@ hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __hal
 hipError_t launch_tile_w(const Mat& W, hipStream_t s);
 // Causal prefill attention of n_q queries at positions p0 .. p0+n_q-1 on the
 // matrix cores (head_dim 64 only; hipErrorInvalidValue otherwise): out as
-// fp32 rows [n_q][n_heads*64] and their tiled binary16 hi/lo planes.
+// fp32 rows [n_q][n_heads*64] and, when out_h is set, their tiled binary16
+// hi/lo planes.
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
                                     int n_ctx, float scale_div, const SpanCfg& span, bool rnd, float* ws,
@@ -327,7 +330,8 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // X[m] += the S split-K partials of ws (z order), then Y = rmsnorm(X[m]) * gain
 // as launch_rmsnorm_rows computes it.
 hipError_t launch_reduce_norm_rows(const float* P, int S, int n, float* X, int dim, const float* gain, float eps,
-                                   float* Yf, __half* Yh, __half* Yl, hipStream_t s);
+                                   float* Yf, __half* Yh, __half* Yl, hipStream_t s, int8_t* C = nullptr,
+                                   float* CS = nullptr);
 hipError_t launch_rope_kv_rows(const float* QKV, int n, int p0, int n_heads, int n_kv_heads, int head_dim, int n_rot,
                                int neox, int n_ctx, const float2* rope, float* Q, __half* kc, __half* vc,
                                hipStream_t s);

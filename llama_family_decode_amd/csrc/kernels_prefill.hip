@@ -59,19 +59,42 @@ __device__ __forceinline__ double rows_sum256(double v, double* red) {
     return red[0] + red[1] + red[2] + red[3];
 }
 
+// The Q8_0 codes of 8 consecutive values of a row (a quarter of a block, the
+// block's four quarters in one DPP quad of lanes), as k_round_rows takes them:
+// d = max|y| / 127, codes roundf(y / d) through the float reciprocal, the
+// scale d rounded to binary16, to the tiled int8 layout (and the scale, as
+// fp32, from the block's first quarter).
+__device__ __forceinline__ void q8_codes8(const float (&y)[8], int row, int i0, int K, int8_t* C, float* CS) {
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(y[e]));
+    amax = fmaxf(amax, xshfl<1>(amax));
+    amax = fmaxf(amax, xshfl<2>(amax));
+    const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f;
+    uint32_t q[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; e++) q[e >> 2] |= (uint32_t)(uint8_t)(int8_t)roundf(y[e] * id) << (8 * (e & 3));
+    *(uint2*)(C + tile_off_i8(row, i0, K, kTileA)) = make_uint2(q[0], q[1]);
+    if ((i0 & 31) == 0) CS[tile_off_s(row, i0 >> 5, K, kTileA)] = round16(d);
+}
+
 // y = x * scale * g for the 8 values of x at column i0 of `row` (i0 % 8 == 0):
-// the fp32 row and, when Yh is set, the tiled hi/lo planes, one 16-byte slot
-// each (the tiled layout keeps 8 consecutive columns of a row together).
+// the fp32 row when Yf is set, the tiled hi/lo planes when Yh is set, one
+// 16-byte slot each (the tiled layout keeps 8 consecutive columns of a row
+// together), and y's Q8_0 codes and block scales when C is set.
 __device__ __forceinline__ void norm_store8(const float (&x)[8], float scale, const float* gain, int row, int i0,
-                                           int dim, float* Yf, __half* Yh, __half* Yl) {
+                                           int dim, float* Yf, __half* Yh, __half* Yl, int8_t* C, float* CS) {
     const float4 g0 = *(const float4*)(gain + i0), g1 = *(const float4*)(gain + i0 + 4);
     const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) y[e] = x[e] * scale * g[e];
-    float* yf = Yf + (size_t)row * dim + i0;
-    *(float4*)yf = make_float4(y[0], y[1], y[2], y[3]);
-    *(float4*)(yf + 4) = make_float4(y[4], y[5], y[6], y[7]);
+    if (C) q8_codes8(y, row, i0, dim, C, CS);
+    if (Yf) {
+        float* yf = Yf + (size_t)row * dim + i0;
+        *(float4*)yf = make_float4(y[0], y[1], y[2], y[3]);
+        *(float4*)(yf + 4) = make_float4(y[4], y[5], y[6], y[7]);
+    }
     if (Yh) {
         __half h[8], l[8];
 #pragma unroll
@@ -90,7 +113,7 @@ __device__ __forceinline__ void norm_store8(const float (&x)[8], float scale, co
 // once, y = (x * scale) * g. One block of 256 threads per row, 8 columns per
 // thread and step.
 __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const float* gain, int dim, float eps, float* Yf,
-                                                      __half* Yh, __half* Yl) {
+                                                      __half* Yh, __half* Yl, int8_t* C, float* CS) {
     __shared__ double red[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     const float* x = X + (size_t)row * dim;
@@ -106,14 +129,15 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const float* X, const floa
     for (int i0 = 8 * tid; i0 < dim; i0 += 8 * 256) {
         const float4 a = *(const float4*)(x + i0), b = *(const float4*)(x + i0 + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        norm_store8(v, scale, gain, row, i0, dim, Yf, Yh, Yl);
+        norm_store8(v, scale, gain, row, i0, dim, Yf, Yh, Yl, C, CS);
     }
 }
 
 hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim, float eps, float* Yf, __half* Yh,
-                               __half* Yl, hipStream_t s) {
-    if (dim % 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_rmsnorm_rows, dim3(n), dim3(256), 0, s, X, gain, dim, eps, Yf, Yh, Yl);
+                               __half* Yl, hipStream_t s, int8_t* C, float* CS) {
+    // with codes a block's four quarters must be one quad of lanes: whole blocks
+    if (dim % 8 || (C && (dim % 32 || !CS))) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_rmsnorm_rows, dim3(n), dim3(256), 0, s, X, gain, dim, eps, Yf, Yh, Yl, C, CS);
     return hipGetLastError();
 }
 
@@ -122,7 +146,7 @@ hipError_t launch_rmsnorm_rows(const float* X, const float* gain, int n, int dim
 // them), then Y = rmsnorm(X[m]) * gain as k_rmsnorm_rows computes it.
 __global__ __launch_bounds__(256) void k_reduce_norm_rows(const float* P, int S, int M, float* X, int dim,
                                                           const float* gain, float eps, float* Yf, __half* Yh,
-                                                          __half* Yl) {
+                                                          __half* Yl, int8_t* C, float* CS) {
     __shared__ double red[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     float* x = X + (size_t)row * dim;
@@ -149,14 +173,14 @@ __global__ __launch_bounds__(256) void k_reduce_norm_rows(const float* P, int S,
     for (int i0 = 8 * tid; i0 < dim; i0 += 8 * 256) {  // this thread's own columns, written above
         const float4 a = *(const float4*)(x + i0), b = *(const float4*)(x + i0 + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        norm_store8(v, scale, gain, row, i0, dim, Yf, Yh, Yl);
+        norm_store8(v, scale, gain, row, i0, dim, Yf, Yh, Yl, C, CS);
     }
 }
 
 hipError_t launch_reduce_norm_rows(const float* P, int S, int n, float* X, int dim, const float* gain, float eps,
-                                   float* Yf, __half* Yh, __half* Yl, hipStream_t s) {
-    if (dim % 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_reduce_norm_rows, dim3(n), dim3(256), 0, s, P, S, n, X, dim, gain, eps, Yf, Yh, Yl);
+                                   float* Yf, __half* Yh, __half* Yl, hipStream_t s, int8_t* C, float* CS) {
+    if (dim % 8 || (C && (dim % 32 || !CS))) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_reduce_norm_rows, dim3(n), dim3(256), 0, s, P, S, n, X, dim, gain, eps, Yf, Yh, Yl, C, CS);
     return hipGetLastError();
 }
 
@@ -1436,10 +1460,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             const float v = RND ? o[dt][i] : o[dt][i] / l_run[i];
             const int col = h * hd + 16 * dt + lr;
             out[(size_t)z * qd + col] = v;
-            const __half hh = __float2half_rn(v);
-            const size_t t = tile_off(z, col, qd, kTileA);
-            out_h[t] = hh;
-            out_l[t] = __float2half_rn(v - __half2float(hh));
+            if (out_h) {
+                const __half hh = __float2half_rn(v);
+                const size_t t = tile_off(z, col, qd, kTileA);
+                out_h[t] = hh;
+                out_l[t] = __float2half_rn(v - __half2float(hh));
+            }
         }
     }
 }
@@ -1466,10 +1492,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill_merge(const float* part, i
     const float v = O / L;
     const int qd = n_heads * hd, col = h * hd + d;
     out[(size_t)z * qd + col] = v;
-    const __half hh = __float2half_rn(v);
-    const size_t t = tile_off(z, col, qd, kTileA);
-    out_h[t] = hh;
-    out_l[t] = __float2half_rn(v - __half2float(hh));
+    if (out_h) {
+        const __half hh = __float2half_rn(v);
+        const size_t t = tile_off(z, col, qd, kTileA);
+        out_h[t] = hh;
+        out_l[t] = __float2half_rn(v - __half2float(hh));
+    }
 }
 
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,

@@ -914,6 +914,23 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
         return prefill_codes(c, w) ? launch_round_rows(X, rows, K, w.dtype, nullptr, nullptr, s, L.Ci, L.Cs)
                                    : launch_round_rows(X, rows, K, w.dtype, H, Lp, s);
     };
+    // RMSNorm of the residual rows X (after adding the S split-K partials of
+    // the workspace, if S > 0) as the input of product w: its Q8_0 codes when
+    // w runs on them, else the fp32 rows and their hi/lo planes
+    auto norm_rows = [&](const float* P, int S, float* X, int rows, const float* gain, const Mat& w) {
+        float* Yf = L.Hf;
+        __half *Yh = L.Hh, *Yl = L.Hl;
+        int8_t* C = nullptr;
+        float* CS = nullptr;
+        if (prefill_codes(c, w)) {
+            Yf = nullptr;
+            Yh = Yl = nullptr;
+            C = L.Ci;
+            CS = L.Cs;
+        }
+        return S ? launch_reduce_norm_rows(P, S, rows, X, cf.dim, gain, cf.eps, Yf, Yh, Yl, s, C, CS)
+                 : launch_rmsnorm_rows(X, gain, rows, cf.dim, cf.eps, Yf, Yh, Yl, s, C, CS);
+    };
     // the wanted rows grouped by chunk, output order kept within a chunk:
     // c->sel_out[p] = output index, c->sel_row[p] = prompt row
     c->sel_out.clear();
@@ -944,9 +961,10 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             const bool last = l == cf.n_layers - 1;
             __half* kc = L.kc + (size_t)l * L.kv_layer;
             __half* vc = L.vc + (size_t)l * L.kv_layer;
-            if (!normed) HIPCHK(c, launch_rmsnorm_rows(L.X, W.attn_norm, m, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
+            // (an integer product's codes come from the norm itself)
+            if (!normed) HIPCHK(c, norm_rows(nullptr, 0, L.X, m, W.attn_norm, W.qkv));
             normed = false;
-            if (rnd) HIPCHK(c, round_rows(L.Hf, m, cf.dim, W.qkv, L.Hh, L.Hl));
+            if (rnd && !prefill_codes(c, W.qkv)) HIPCHK(c, round_rows(L.Hf, m, cf.dim, W.qkv, L.Hh, L.Hl));
             HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, ga(W.qkv, L.Hf, L.Hh, L.Hl), m, L.QKV, qkvd, W.bqkv, nullptr,
                                   nullptr, L.ws, L.ws_floats, s));
             HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
@@ -971,8 +989,11 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             t.rnd = cf.numerics;
             t.stats = L.attn_stats;
             const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0;
+            // (no hi/lo planes where the output product runs on the codes)
+            const bool o_codes = prefill_codes(c, W.o);
             if (mfma_attn)
-                HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, L.Oh, L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
+                HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, o_codes ? nullptr : L.Oh,
+                                                   o_codes ? nullptr : L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
                                                    cf.head_dim, cf.n_ctx, t.scale_div, t.span, rnd, L.ws, L.ws_floats,
                                                    s));
             else
@@ -988,21 +1009,19 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 int S = 0;
                 HIPCHK(c, launch_gemm(EPI_RESID, W.o, ga(W.o, of, L.Oh, L.Ol), mr, X, cf.dim, nullptr, nullptr,
                                       nullptr, L.ws, L.ws_floats, s, nullptr, &S));
-                if (S)
-                    HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, W.ffn_norm, cf.eps, L.Hf, L.Hh, L.Hl, s));
-                else
-                    HIPCHK(c, launch_rmsnorm_rows(X, W.ffn_norm, mr, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
-                if (rnd) HIPCHK(c, round_rows(L.Hf, mr, cf.dim, W.gu, L.Hh, L.Hl));
-                HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, ga(W.gu, L.Hf, L.Hh, L.Hl), mr, L.Uf, cf.ffn, nullptr, L.Uh,
-                                      L.Ul, L.ws, L.ws_floats, s));
+                HIPCHK(c, norm_rows(L.ws, S, X, mr, W.ffn_norm, W.gu));
+                if (rnd && !prefill_codes(c, W.gu)) HIPCHK(c, round_rows(L.Hf, mr, cf.dim, W.gu, L.Hh, L.Hl));
+                // (no hi/lo planes of the SwiGLU output where down runs on the codes)
+                const bool d_codes = prefill_codes(c, W.down);
+                HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, ga(W.gu, L.Hf, L.Hh, L.Hl), mr, L.Uf, cf.ffn, nullptr,
+                                      d_codes ? nullptr : L.Uh, d_codes ? nullptr : L.Ul, L.ws, L.ws_floats, s));
                 if (rnd) HIPCHK(c, round_rows(L.Uf, mr, cf.ffn, W.down, L.Uh, L.Ul));
                 // before another layer a split-K down product's reduction is
                 // fused with that layer's attention norm
                 HIPCHK(c, launch_gemm(EPI_RESID, W.down, ga(W.down, L.Uf, L.Uh, L.Ul), mr, X, cf.dim, nullptr,
                                       nullptr, nullptr, L.ws, L.ws_floats, s, nullptr, last ? nullptr : &S));
                 if (!last && S) {
-                    HIPCHK(c, launch_reduce_norm_rows(L.ws, S, mr, X, cf.dim, L.layers[l + 1].attn_norm, cf.eps, L.Hf,
-                                                      L.Hh, L.Hl, s));
+                    HIPCHK(c, norm_rows(L.ws, S, X, mr, L.layers[l + 1].attn_norm, L.layers[l + 1].qkv));
                     normed = true;
                 }
                 return LLM_OK;
@@ -1255,9 +1274,12 @@ int llm_op_time_prefill_product(llm_ctx* c, int32_t product, int32_t layer, int3
             case LLM_PRODUCT_O:
                 return launch_gemm(EPI_RESID, W.o, prefill_operand(c, W.o, L.Of, L.Oh, L.Ol), n_rows, L.X, c->cfg.dim,
                                    nullptr, nullptr, nullptr, L.ws, L.ws_floats, s, nullptr, &S);
-            case LLM_PRODUCT_GATE_UP:
+            case LLM_PRODUCT_GATE_UP: {
+                const bool d_codes = prefill_codes(c, W.down);
                 return launch_gemm(EPI_SWIGLU, W.gu, prefill_operand(c, W.gu, L.Hf, L.Hh, L.Hl), n_rows, L.Uf,
-                                   c->cfg.ffn, nullptr, L.Uh, L.Ul, L.ws, L.ws_floats, s);
+                                   c->cfg.ffn, nullptr, d_codes ? nullptr : L.Uh, d_codes ? nullptr : L.Ul, L.ws,
+                                   L.ws_floats, s);
+            }
             default:
                 return launch_gemm(EPI_RESID, W.down, prefill_operand(c, W.down, L.Uf, L.Uh, L.Ul), n_rows, L.X,
                                    c->cfg.dim, nullptr, nullptr, nullptr, L.ws, L.ws_floats, s, nullptr, &S);
