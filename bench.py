@@ -287,7 +287,7 @@ def measure_decode_report(llm, synth, np, torch, cfg, ctx_len, steps=64, reps=3)
             "hbm_frac": round(b * tok_s / 1e9 / HBM_PEAK_GBS, 4), "step_kind": kind}
 
 
-def measure_prefill_q8_llamacpp(llm, synth, np, torch, n=2048, reps=3):
+def measure_prefill_q8_llamacpp(llm, synth, np, torch, n=2048, reps=3, products=True):
     """llm_prefill of the headline workload's 2048 ids with llama.cpp's
     rounding points: the Q8_0 products on the integer matrix cores."""
     cfg = synth.C4.with_(name="llama-1b-q8_0-llamacpp", numerics=1)
@@ -304,7 +304,7 @@ def measure_prefill_q8_llamacpp(llm, synth, np, torch, n=2048, reps=3):
         torch.cuda.synchronize()
         times.append(time.perf_counter() - t0)
         m.reset()
-    products = product_fractions(llm, m, cfg, n, INT8_MFMA_PEAK_TOPS if int8 else F16_MFMA_PEAK_TFLOPS)
+    products = product_fractions(llm, m, cfg, n, INT8_MFMA_PEAK_TOPS if int8 else F16_MFMA_PEAK_TFLOPS) if products else {}
     m.close()
     del m
     torch.cuda.empty_cache()
@@ -330,7 +330,7 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill measurement (512 ids, Qwen2-style F16 1B) and print it as JSON")
     ap.add_argument("--no-products", action="store_true",
-                    help="skip timing the 2048-row prompt pass's products one by one")
+                    help="skip timing the 2048-row prompt passes' products one by one")
     ap.add_argument("--prefill-llamacpp", action="store_true",
                     help="only run the 2048-id prompt pass of the Q8_0 1B model with llama.cpp's rounding points "
                          "(integer matrix-core products) and print it as JSON")
@@ -360,7 +360,8 @@ def main():
         print(f"# copied {args.copy_bytes} bytes 5 times", file=sys.stderr)
         return
     if args.prefill_llamacpp:
-        print(json.dumps({"prefill_q8_0_2048_llamacpp": measure_prefill_q8_llamacpp(llm, synth, np, torch)}))
+        print(json.dumps({"prefill_q8_0_2048_llamacpp": measure_prefill_q8_llamacpp(llm, synth, np, torch,
+                                                                                     products=not args.no_products)}))
         return
     if args.prefill_only:
         print(json.dumps({"prefill": measure_prefill(llm, synth, np, torch)}))

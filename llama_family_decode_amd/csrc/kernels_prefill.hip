@@ -1345,7 +1345,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         // last position are padding, never stored).
         const bool full = c0 + PA_CH - 1 <= rfirst && (span.window <= 0 || c0 > last - span.window);
         if (RND && pass == 1) {
-            // the rounded probabilities of the whole span, the P V operand as is
+            // the rounded probabilities of the whole span, the P V operand as
+            // is, staged as binary16 (rows 2 * PA_PLD halves apart)
+            _Float16* Ph = (_Float16*)P;
 #pragma unroll
             for (int pt = 0; pt < 4; pt++)
 #pragma unroll
@@ -1353,14 +1355,11 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                     const int t = c0 + 16 * pt + lr;
                     const float e =
                         full || span_has(span, t, rpos[i]) ? expf(sc[pt][i] * kPaInvDiv - Mrow[i]) / Lrow[i] : 0.f;
-                    P[(4 * lq + i) * PA_PLD + 16 * pt + lr] = round16(e);
+                    Ph[(4 * lq + i) * 2 * PA_PLD + 16 * pt + lr] = (_Float16)e;
                 }
 #pragma unroll
             for (int ps = 0; ps < 2; ps++) {
-                const float4 p0v = *(const float4*)(P + lr * PA_PLD + 32 * ps + 8 * lq);
-                const float4 p1v = *(const float4*)(P + lr * PA_PLD + 32 * ps + 8 * lq + 4);
-                const half8 ph = {(_Float16)p0v.x, (_Float16)p0v.y, (_Float16)p0v.z, (_Float16)p0v.w,
-                                  (_Float16)p1v.x, (_Float16)p1v.y, (_Float16)p1v.z, (_Float16)p1v.w};
+                const half8 ph = *(const half8*)(Ph + lr * 2 * PA_PLD + 32 * ps + 8 * lq);
 #pragma unroll
                 for (int dt = 0; dt < 4; dt++) {
                     const half8 vf = *(const half8*)(Vt + (16 * dt + lr) * PA_LD + 32 * ps + 8 * lq);
