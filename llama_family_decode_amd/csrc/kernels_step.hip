@@ -749,9 +749,17 @@ __device__ __forceinline__ void wbatch_fast(const WRows& w, const int* rmap, int
     const bool end = (cl & (L / 16 - 1)) == 0 && (s & (ncb - 1)) == ncb - 1 && k0 + s < w.nslots;
     if constexpr (EM == EM_QKV || EM == EM_SWIGLU) {
         // rows 2i and 2i+1: the odd row ends ncb slots later (whole-wave rows)
-        // or sits in the next group of lanes (shorter rows)
-        const int src = RPI == 1 ? slot_lane<LSH>((s + ncb) & 15) : (lane + L) & 63;
-        const float other = __shfl(t, src, 64);
+        // or sits in the next group of lanes (shorter rows). For an even row
+        // that is slot s ^ ncb (a batch starts at an even row), so lane ^ 4 ncb,
+        // or lane ^ L (its group index is even): one xshfl exchange. Only even
+        // rows use the value.
+        float other;
+        if constexpr (RPI == 1 && NCB > 0)
+            other = xshfl<(1 << (LSH - 4)) * (NCB > 0 ? NCB : 1)>(t);
+        else if constexpr (RPI > 1)
+            other = xshfl<(RPI > 1 ? L : 1)>(t);
+        else
+            other = __shfl(t, slot_lane<LSH>((s + ncb) & 15), 64);
         if (end && ((row - w.r0) & 1) == 0) {
             if constexpr (EM == EM_QKV)
                 emit_qkv(ea, rmap[row], rmap[row + 1], t, other);

@@ -17,6 +17,10 @@ workload (``fullsize_<name>.npz``):
 * for the prompt-only workload, the logits of chosen prompt rows
   (``row_idx`` / ``row_logits``).
 
+The rounding-mode workload (c4_q8_0_llamacpp_ctx2048: the headline model with
+llama.cpp's rounding points, "What a Llama model computes, and why", section 8)
+runs 16 decode steps.
+
 With --variant V the script runs a workload again on another build of the
 oracle that evaluates the same definition in another valid way (V = desc:
 every dot product summed over the input index descending, liboracle_desc.so;
@@ -53,6 +57,8 @@ WORKLOADS = {
     "c4_q8_0_ctx2048": (synth.C4, 128, (0, 1, 128), None),
     "c4_q8_0_ctx8192": (synth.C4_LONG, 128, (0, 1, 128), None),
     "c5_qwen2_prefill512": (synth.C5, 0, (0,), (0, 255, 511)),
+    # the headline workload with llama.cpp's rounding points (numerics 1)
+    "c4_q8_0_llamacpp_ctx2048": (synth.C4.with_(name="llama-1b-q8_0-llamacpp", numerics=1), 16, (0, 1, 16), None),
 }
 
 
