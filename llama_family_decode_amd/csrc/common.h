@@ -297,9 +297,9 @@ hipError_t launch_round_rows(float* X, int n, int K, int dtype, __half* H, __hal
 // Fills W.wt (and for Q8_0 W.st) from W's stored rows.
 hipError_t launch_tile_w(const Mat& W, hipStream_t s);
 // Causal prefill attention of n_q queries at positions p0 .. p0+n_q-1 on the
-// matrix cores (head_dim 64 only; hipErrorInvalidValue otherwise): out as
-// fp32 rows [n_q][n_heads*64] and, when out_h is set, their tiled binary16
-// hi/lo planes.
+// matrix cores (head_dim 64 only; hipErrorInvalidValue otherwise): out (if
+// set) as fp32 rows [n_q][n_heads*64] and, when out_h is set, their tiled
+// binary16 hi/lo planes.
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
                                     int n_ctx, float scale_div, const SpanCfg& span, bool rnd, float* ws,

@@ -364,12 +364,12 @@ hipError_t launch_tile_w(const Mat& W, hipStream_t s) {
 // Output row of product row m: ymap[m] when a row map is given (stores only).
 __device__ __forceinline__ int out_row(const int* ymap, int m) { return ymap ? ymap[m] : m; }
 
-// u = silu(gate) * up at Y[m*ldy + j], and its hi/lo pair (tiled, K = ldy)
-// when Yh is set.
+// u = silu(gate) * up at Y[m*ldy + j] when Y is set, and its hi/lo pair
+// (tiled, K = ldy) when Yh is set.
 __device__ __forceinline__ void store_swiglu(float* Y, __half* Yh, __half* Yl, int m, int j, int ldy, float gate,
                                              float up) {
     const float u = pf_silu(gate) * up;
-    Y[(size_t)m * ldy + j] = u;
+    if (Y) Y[(size_t)m * ldy + j] = u;
     if (Yh) {
         const __half h = __float2half_rn(u);
         const size_t t = tile_off(m, j, ldy, kTileA);
@@ -1458,7 +1458,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         for (int dt = 0; dt < 4; dt++) {
             const float v = RND ? o[dt][i] : o[dt][i] / l_run[i];
             const int col = h * hd + 16 * dt + lr;
-            out[(size_t)z * qd + col] = v;
+            if (out) out[(size_t)z * qd + col] = v;
             if (out_h) {
                 const __half hh = __float2half_rn(v);
                 const size_t t = tile_off(z, col, qd, kTileA);
@@ -1490,7 +1490,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_merge(const float* part, i
     }
     const float v = O / L;
     const int qd = n_heads * hd, col = h * hd + d;
-    out[(size_t)z * qd + col] = v;
+    if (out) out[(size_t)z * qd + col] = v;
     if (out_h) {
         const __half hh = __float2half_rn(v);
         const size_t t = tile_off(z, col, qd, kTileA);

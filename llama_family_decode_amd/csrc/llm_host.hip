@@ -897,6 +897,13 @@ static GemmA prefill_operand(const llm_ctx* c, const Mat& w, const float* f, con
     const __half* lo = c->cfg.numerics && w.dtype == DT_F16 ? nullptr : l;
     return prefill_codes(c, w) ? GemmA{f, h, lo, c->L.Ci, c->L.Cs} : GemmA{f, h, lo, nullptr, nullptr};
 }
+// Whether product w reads only its input's binary16 hi/lo planes (the tiled
+// matrix-core product in float numerics), so that no kernel needs the input's
+// fp32 rows: the rounding mode rounds those rows, and the other product
+// kernels read them.
+static bool prefill_planes_only(const llm_ctx* c, const Mat& w) {
+    return !c->cfg.numerics && w.wt && (w.dtype == DT_F16 || (w.dtype == DT_Q8 && w.st)) && w.cols % 32 == 0;
+}
 
 static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const std::vector<int32_t>& rows_out,
                         float* d_rows) {
@@ -918,7 +925,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
     // the workspace, if S > 0) as the input of product w: its Q8_0 codes when
     // w runs on them, else the fp32 rows and their hi/lo planes
     auto norm_rows = [&](const float* P, int S, float* X, int rows, const float* gain, const Mat& w) {
-        float* Yf = L.Hf;
+        float* Yf = prefill_planes_only(c, w) ? nullptr : L.Hf;
         __half *Yh = L.Hh, *Yl = L.Hl;
         int8_t* C = nullptr;
         float* CS = nullptr;
@@ -989,10 +996,12 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             t.rnd = cf.numerics;
             t.stats = L.attn_stats;
             const bool mfma_attn = cf.head_dim == 64 && (64 % (cf.n_heads / cf.n_kv_heads)) == 0;
-            // (no hi/lo planes where the output product runs on the codes)
-            const bool o_codes = prefill_codes(c, W.o);
+            // (no hi/lo planes where the output product runs on the codes, no
+            // fp32 rows where it reads only the planes, except in the last
+            // layer, whose rows are gathered)
+            const bool o_codes = prefill_codes(c, W.o), o_rows = last || !prefill_planes_only(c, W.o);
             if (mfma_attn)
-                HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, L.Of, o_codes ? nullptr : L.Oh,
+                HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, o_rows ? L.Of : nullptr, o_codes ? nullptr : L.Oh,
                                                    o_codes ? nullptr : L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
                                                    cf.head_dim, cf.n_ctx, t.scale_div, t.span, rnd, L.ws, L.ws_floats,
                                                    s));
@@ -1013,7 +1022,8 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 if (rnd && !prefill_codes(c, W.gu)) HIPCHK(c, round_rows(L.Hf, mr, cf.dim, W.gu, L.Hh, L.Hl));
                 // (no hi/lo planes of the SwiGLU output where down runs on the codes)
                 const bool d_codes = prefill_codes(c, W.down);
-                HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, ga(W.gu, L.Hf, L.Hh, L.Hl), mr, L.Uf, cf.ffn, nullptr,
+                HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, ga(W.gu, L.Hf, L.Hh, L.Hl), mr,
+                                      prefill_planes_only(c, W.down) ? nullptr : L.Uf, cf.ffn, nullptr,
                                       d_codes ? nullptr : L.Uh, d_codes ? nullptr : L.Ul, L.ws, L.ws_floats, s));
                 if (rnd) HIPCHK(c, round_rows(L.Uf, mr, cf.ffn, W.down, L.Uh, L.Ul));
                 // before another layer a split-K down product's reduction is
@@ -1276,8 +1286,8 @@ int llm_op_time_prefill_product(llm_ctx* c, int32_t product, int32_t layer, int3
                                    nullptr, nullptr, nullptr, L.ws, L.ws_floats, s, nullptr, &S);
             case LLM_PRODUCT_GATE_UP: {
                 const bool d_codes = prefill_codes(c, W.down);
-                return launch_gemm(EPI_SWIGLU, W.gu, prefill_operand(c, W.gu, L.Hf, L.Hh, L.Hl), n_rows, L.Uf,
-                                   c->cfg.ffn, nullptr, d_codes ? nullptr : L.Uh, d_codes ? nullptr : L.Ul, L.ws,
+                return launch_gemm(EPI_SWIGLU, W.gu, prefill_operand(c, W.gu, L.Hf, L.Hh, L.Hl), n_rows,
+                                   prefill_planes_only(c, W.down) ? nullptr : L.Uf, c->cfg.ffn, nullptr, d_codes ? nullptr : L.Uh, d_codes ? nullptr : L.Ul, L.ws,
                                    L.ws_floats, s);
             }
             default:
