@@ -909,8 +909,10 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int layer, int pos
             float qv[GC][8], acc[GC][8];
 #pragma unroll
             for (int h = 0; h < GC; h++) {
-                const float4 a0 = ldf4(qkv + ((g * G + h0 + h) * hd + sub8));
-                const float4 a1 = ldf4(qkv + ((g * G + h0 + h) * hd + sub8 + 4));
+                // (a pass 2 that reuses pass 1's scores needs no q)
+                const float4 a0 = reuse ? make_float4(0.f, 0.f, 0.f, 0.f) : ldf4(qkv + ((g * G + h0 + h) * hd + sub8));
+                const float4 a1 =
+                    reuse ? make_float4(0.f, 0.f, 0.f, 0.f) : ldf4(qkv + ((g * G + h0 + h) * hd + sub8 + 4));
                 const float f = dim_ok ? tau : 0.f;
                 qv[h][0] = a0.x * f;
                 qv[h][1] = a0.y * f;
