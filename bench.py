@@ -183,7 +183,7 @@ def product_fractions(llm, model, cfg, n_rows, peak, n_launch=20):
     return out
 
 
-def measure_prefill(llm, synth, np, torch, reps=5):
+def measure_prefill(llm, synth, np, torch, reps=5, products=True):
     """llm_prefill of 512 seeded ids on the Qwen2-style F16 1B model from an
     empty cache, median of `reps`, and llm_prefill_rows of the same ids with
     every row's logits; MFMA fraction = algorithmic GEMM FLOPs / time / F16
@@ -215,7 +215,7 @@ def measure_prefill(llm, synth, np, torch, reps=5):
         rtimes.append(time.perf_counter() - t0)
         pm.reset()
     rt = float(np.median(rtimes))
-    products = product_fractions(llm, pm, c5, 512, F16_MFMA_PEAK_TFLOPS)
+    products = product_fractions(llm, pm, c5, 512, F16_MFMA_PEAK_TFLOPS) if products else {}
     # GEMM FLOPs the pass needs: the last layer's output product and FFN run
     # on the one row whose logits are read (on all 512 for every row's logits)
     qkv = c5.dim * (c5.q_dim + 2 * c5.kv_dim)
@@ -245,8 +245,9 @@ def measure_prefill(llm, synth, np, torch, reps=5):
     del pn
     torch.cuda.empty_cache()
     print(f"# prefill 512: {pt * 1e3:.2f} ms, {512 / pt:.0f} tok/s; with all 512 logit rows {rt * 1e3:.2f} ms; "
-          f"with llama.cpp's rounding points {nt * 1e3:.2f} ms; products at 512 rows: "
-          + ", ".join(f"{k} {v['us']} us ({v['frac']:.3f})" for k, v in products.items()), file=sys.stderr, flush=True)
+          f"with llama.cpp's rounding points {nt * 1e3:.2f} ms"
+          + ("; products at 512 rows: " + ", ".join(f"{k} {v['us']} us ({v['frac']:.3f})" for k, v in products.items())
+             if products else ""), file=sys.stderr, flush=True)
     return {"config": c5.name, "tokens": 512, "ms": round(pt * 1e3, 3), "tok_s": round(512 / pt, 1),
             "gemm_tflop": round(gemm_flop / 1e12, 4), "products_512_rows": products,
             "whole_prefill_mfma_frac": round(gemm_flop / pt / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
@@ -330,7 +331,7 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill measurement (512 ids, Qwen2-style F16 1B) and print it as JSON")
     ap.add_argument("--no-products", action="store_true",
-                    help="skip timing the 2048-row prompt passes' products one by one")
+                    help="skip timing the prompt passes' products one by one")
     ap.add_argument("--prefill-llamacpp", action="store_true",
                     help="only run the 2048-id prompt pass of the Q8_0 1B model with llama.cpp's rounding points "
                          "(integer matrix-core products) and print it as JSON")
@@ -364,7 +365,7 @@ def main():
                                                                                      products=not args.no_products)}))
         return
     if args.prefill_only:
-        print(json.dumps({"prefill": measure_prefill(llm, synth, np, torch)}))
+        print(json.dumps({"prefill": measure_prefill(llm, synth, np, torch, products=not args.no_products)}))
         return
     cfg = synth.C4  # 1B shape, Q8_0 matrices, tied F32 embedding
     ctx_len = 2048
@@ -464,7 +465,7 @@ def main():
 
     prefill = None
     if not args.no_prefill:
-        prefill = measure_prefill(llm, synth, np, torch)
+        prefill = measure_prefill(llm, synth, np, torch, products=not args.no_products)
 
     reports = None
     if not args.no_reports:
