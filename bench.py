@@ -310,8 +310,9 @@ def measure_prefill_q8_llamacpp(llm, synth, np, torch, n=2048, reps=3, products=
     del m
     torch.cuda.empty_cache()
     dt = float(np.median(times))
-    print(f"# prefill {n} (Q8_0, llama.cpp rounding points, integer products {int8}): {dt * 1e3:.2f} ms; products "
-          + ", ".join(f"{k} {v['us']} us ({v['frac']:.3f} of the int8 peak)" for k, v in products.items()),
+    print(f"# prefill {n} (Q8_0, llama.cpp rounding points, integer products {int8}): {dt * 1e3:.2f} ms"
+          + ("; products " + ", ".join(f"{k} {v['us']} us ({v['frac']:.3f} of the int8 peak)"
+                                        for k, v in products.items()) if products else ""),
           file=sys.stderr, flush=True)
     return {"config": cfg.name, "tokens": n, "ms": round(dt * 1e3, 3), "tok_s": round(n / dt, 1),
             "integer_products": int8, "products": products}
