@@ -69,9 +69,9 @@ def test_int8_prefill_layer0_rows_1b():
     print(f"[{cfg.name}] layer-0 K/V of prompt rows within {w0} binary16 ulps", flush=True)
 
 
-def _oracle_rows(cfg, ts, toks, positions, variant=""):
+def _oracle_rows(cfg, ts, toks, positions, variant="", rows=None):
     m = oracle.Model(cfg, ts, variant=variant)
-    lg = m.prefill_rows(toks, list(range(len(toks)))).astype(np.float64)
+    lg = m.prefill_rows(toks, list(range(len(toks))) if rows is None else rows).astype(np.float64)
     kv = {(l, p): m.kv_read(l, p) for l in range(cfg.n_layers) for p in positions}
     m.close()
     return lg, kv
@@ -116,4 +116,46 @@ def test_int8_prefill_medium_against_the_oracle():
     m.close()
     print(f"[{cfg.name}] layer-0 K/V within {w0:.0f} ulps; row |dlogit| median {np.median(err):.3e} "
           f"(oracle builds {stats[:, 0].max():.3e}), max {err.max():.3e} (builds {stats[:, 2].max():.3e}); "
+          f"K/V {ratio:.2f} of the bar", flush=True)
+
+
+def test_int8_prefill_across_chunks():
+    # A prompt of one whole prefill chunk plus a ragged 52 rows: the second
+    # chunk's products reuse the codes buffers and attend the first chunk's
+    # cache. Layer-0 K/V on both sides of the boundary within 2 binary16 ulps of
+    # the oracle's; the logits of rows on both sides, and every layer's K/V
+    # there, within max(tolerance, 1.5 times the largest distance of the
+    # oracle's two other builds) as above.
+    cfg = MEDIUM_Q8_RND.with_(name="medium-q8_0-llamacpp-2chunks", n_ctx=2200)
+    chunk = llm.llm_op_prefill_chunk()
+    n = chunk + 52
+    ts = synth.make_tensor_set(cfg)
+    toks = synth.prompt(cfg, n)
+    rows = [0, 1000, chunk - 1, chunk, n - 1]
+    positions = (0, chunk - 2, chunk - 1, chunk, chunk + 1, n - 1)
+    m = llm.Model(cfg, ts)
+    assert llm.llm_op_prefill_int8(m.ctx) == 1
+    got = m.prefill_rows(toks, rows).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    w0 = check_layer0_kv(cfg, _tensors_by_name(ts), m, [(p, int(toks[p])) for p in positions], 2.0)
+    want, wkv = _oracle_rows(cfg, ts, toks, positions, rows=rows)
+    spread, kv_spread = 0.0, {k: 0.0 for k in wkv}
+    for v in ("desc", "f64"):
+        lg, kv = _oracle_rows(cfg, ts, toks, positions, v, rows=rows)
+        spread = max(spread, float(np.abs(lg - want).max()))
+        for k in kv:
+            kv_spread[k] = max([kv_spread[k]] + [_kv_dist(a, b, cfg.head_dim) for a, b in zip(kv[k], wkv[k])])
+    t = tol(cfg)
+    bar = max(t, 1.5 * spread)
+    err = np.abs(got - want).max(axis=1)
+    assert np.all(err <= bar), f"rows {rows}: max |dlogit| {err.tolist()} > {bar:.3e}"
+    ratio = 0.0
+    for (l, p), (ko, vo) in wkv.items():
+        kb = max(t, 1.5 * max(v for (l2, _), v in kv_spread.items() if l2 == l))
+        for a_bits, b_bits in zip(m.kv_read(l, p), (ko, vo)):
+            d = _kv_dist(a_bits, b_bits, cfg.head_dim, slack_ulps=2)
+            assert d <= kb, f"K/V of layer {l} at position {p} differ from the oracle by {d:.3e} > {kb:.3e}"
+            ratio = max(ratio, d / kb)
+    m.close()
+    print(f"[{cfg.name}] layer-0 K/V within {w0:.0f} ulps; max |dlogit| {err.max():.3e} (bar {bar:.3e}); "
           f"K/V {ratio:.2f} of the bar", flush=True)
