@@ -1318,9 +1318,30 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         for (int u = 0; u < 2; u++) {
             *(u32x4p*)(Ks + (lp + 32 * u) * PA_LD + ld8) = kr[u];
             if (with_v) {
-                const __half* vh = (const __half*)&vr[u];
+                // V transposed: half j of this thread goes to row ld8 + j. Store
+                // step s writes half (s + a) & 7, a = ld8 / 8, so that the lanes
+                // of one store reach rows of eight different residues mod 8
+                // (the same residue for all would put every lane in one group of
+                // banks): the eight halves are first rotated left by a.
+                const int a = ld8 >> 3;
+                uint32_t w[4] = {vr[u][0], vr[u][1], vr[u][2], vr[u][3]};
+                uint32_t t[4];
 #pragma unroll
-                for (int j = 0; j < 8; j++) Vt[(ld8 + j) * PA_LD + lp + 32 * u] = vh[j];
+                for (int k = 0; k < 4; k++) t[k] = __builtin_amdgcn_alignbit(w[(k + 1) & 3], w[k], 16);
+#pragma unroll
+                for (int k = 0; k < 4; k++) w[k] = (a & 1) ? t[k] : w[k];
+#pragma unroll
+                for (int k = 0; k < 4; k++) t[k] = w[(k + 1) & 3];
+#pragma unroll
+                for (int k = 0; k < 4; k++) w[k] = (a & 2) ? t[k] : w[k];
+#pragma unroll
+                for (int k = 0; k < 4; k++) t[k] = w[(k + 2) & 3];
+#pragma unroll
+                for (int k = 0; k < 4; k++) w[k] = (a & 4) ? t[k] : w[k];
+                uint16_t* vt16 = (uint16_t*)Vt + lp + 32 * u;
+#pragma unroll
+                for (int st = 0; st < 8; st++)
+                    vt16[(ld8 + ((st + a) & 7)) * PA_LD] = (uint16_t)(w[st >> 1] >> (16 * (st & 1)));
             }
         }
         __syncthreads();
