@@ -43,11 +43,15 @@ inline size_t tiled_s_bytes(int rows, int cols) {
 }
 // Tiled int8 layout of Q8_0 codes (the integer products of llama.cpp's
 // rounding points): rows in tiles of TM, K in steps of 32; tile t, step ks is
-// one contiguous TM x 32-byte piece, row-major (row r's 32 codes at 32 r).
+// one contiguous TM x 32-byte piece, row r's 32 codes at 32 r with their two
+// 16-byte halves swapped when i8_swz(r) is set. A fragment read takes one half
+// of 32 consecutive rows; the swap puts the rows of any 8 (or 16) consecutive
+// lanes in distinct 16-byte bank groups.
 // The block scales of activation rows: [128-row tile][K step][128] fp32.
+__host__ __device__ inline int i8_swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 __host__ __device__ inline size_t tile_off_i8(int m, int k, int K, int TM) {
-    const int nk = K >> 5, t = m / TM;
-    return (((size_t)t * nk + (k >> 5)) * TM + (m - t * TM)) * 32 + (k & 31);
+    const int nk = K >> 5, t = m / TM, r = m - t * TM;
+    return (((size_t)t * nk + (k >> 5)) * TM + r) * 32 + ((((k >> 4) & 1) ^ i8_swz(r)) << 4) + (k & 15);
 }
 __host__ __device__ inline size_t tile_off_s(int m, int kb, int K, int TM) {
     const int t = m / TM;

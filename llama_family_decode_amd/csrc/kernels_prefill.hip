@@ -994,19 +994,22 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
         float dw[2];       // the weight scale of this lane's column, per tile
         float4 dx[2][4];   // the activation scales of this lane's 16 rows, per tile
     };
+    // this lane's half of its row (rows are 32-aligned but for r32, whose
+    // bits 2 and 3 pick the half swap of the layout)
+    const int hs = 16 * (h ^ i8_swz(r32));
     auto fread = [&](int ks, Frag& F) {
         const char* st = lds + (ks % I8_ST) * I8_STAGE;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             const int r = 64 * wm + 32 * i;
-            F.a[i] = *(const i32x4*)(st + (r + r32) * 32 + 16 * h);
+            F.a[i] = *(const i32x4*)(st + (r + r32) * 32 + hs);
 #pragma unroll
             for (int g = 0; g < 4; g++) F.dx[i][g] = *(const float4*)(st + I8_SS + 4 * (r + 8 * g + 4 * h));
         }
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int c = 64 * wn + 32 * j + r32;
-            F.b[j] = *(const i32x4*)(st + I8_SW + c * 32 + 16 * h);
+            F.b[j] = *(const i32x4*)(st + I8_SW + c * 32 + hs);
             F.dw[j] = *(const float*)(st + I8_SS + 4 * HL_M + 4 * c);
         }
     };
