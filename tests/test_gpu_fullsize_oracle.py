@@ -225,17 +225,24 @@ def test_llamacpp_rounding_workload_against_the_oracle():
     # stored sample and over the whole vector where it is stored, there the
     # GPU's greedy token among the oracle's top 5, and layer 0's K/V (computed
     # before any code can differ) within 2 binary16 ulps at the stored positions.
+    # Element by element as well, as for the float-numerics Q8_0 workloads: the
+    # logits at each step within max(tolerance, 1.5 d) of the oracle's, d the
+    # larger distance of the oracle's two other builds at that step, and every
+    # layer's K/V within max(tolerance, 1.5 e) of the head rms (+ 2 ulps), e the
+    # builds' own K/V distance at that position and layer.
     name = "c4_q8_0_llamacpp_ctx2048"
     g = _load(name)
     cfg, steps, full_steps, _ = make_fullsize.WORKLOADS[name]
+    t = tol(cfg)
+    ds, df, kv_var = _variant_dist(name, g, cfg, steps, full_steps)
     P = int(g["prompt_len"])
     toks = synth.prompt(cfg, P)
     assert hashlib.sha256(toks.tobytes()).hexdigest() == str(g["prompt_sha256"]), "prompt generator changed"
     ts = synth.make_tensor_set(cfg)
     print(f"[{name}] prefill {P}, {steps} teacher-forced steps", flush=True)
     dec = llm.Model(cfg, ts)
-    for p, t in enumerate(toks):
-        dec.decode(int(t), p)
+    for p, tok in enumerate(toks):
+        dec.decode(int(tok), p)
     gpu = llm.Model(cfg, ts)
     assert llm.llm_op_step_kind(gpu.ctx) == 2 and llm.llm_op_prefill_int8(gpu.ctx) == 1
     nxt = gpu.prefill(toks)
@@ -244,7 +251,7 @@ def test_llamacpp_rounding_workload_against_the_oracle():
     bar = max(0.07, 2 * self_dist)
     full = {int(s): g["full_logits"][i] for i, s in enumerate(g["full_steps"])}
     sidx = g["sample_idx"]
-    worst = 0.0
+    worst, worst_el = 0.0, 0.0
     for s in range(steps + 1):
         if s > 0:
             nxt = gpu.decode(int(g["tokens"][s - 1]), P + s - 1)
@@ -252,13 +259,18 @@ def test_llamacpp_rounding_workload_against_the_oracle():
         assert np.all(np.isfinite(got)), f"step {s}: non-finite logits"
         assert nxt == first_max(got)
         d = _rel_rms(got[sidx], g["sample_logits"][s])
+        e = _check_logits(max(t, 1.5 * ds[s]), got[sidx], g["sample_logits"][s], f"{name} step {s} (sample)")
+        worst_el = max(worst_el, e / max(t, 1.5 * ds[s]))
         if s in full:
             d = max(d, _rel_rms(got, full[s]))
+            e = _check_logits(max(t, 1.5 * df[s]), got, full[s], f"{name} step {s} (whole vector)")
+            worst_el = max(worst_el, e / max(t, 1.5 * df[s]))
             top5 = np.argsort(-full[s].astype(np.float64), kind="stable")[:5]
             assert nxt in top5, f"step {s}: GPU token {nxt} not in the oracle's top 5 {top5.tolist()}"
         assert d <= bar, f"step {s}: logits {d:.3f} RMS from the oracle's > {bar:.3f}"
         worst = max(worst, d)
     assert gpu.kv_len() == P + steps
+    _, wkv, rkv = _check_kv(cfg, gpu, g, decode_from=P, kv_var=kv_var)
     w0 = 0.0
     for i, p in enumerate(g["kv_pos"]):
         kg, vg = gpu.kv_read(0, int(p))
@@ -267,4 +279,5 @@ def test_llamacpp_rounding_workload_against_the_oracle():
     assert w0 <= 2, f"layer-0 K/V differ from the oracle by {w0} binary16 ulps"
     gpu.close()
     print(f"[{name}] logits at most {worst:.3f} RMS from the oracle's (bar {bar:.3f}; GPU prefill vs its own "
-          f"decode {self_dist:.3f}); layer-0 K/V within {w0:.0f} ulps", flush=True)
+          f"decode {self_dist:.3f}), element-wise at most {worst_el:.2f} of the step's bar; layer-0 K/V within "
+          f"{w0:.0f} ulps; K/V {wkv:.3e} of head rms ({rkv:.2f} of the bar)", flush=True)
