@@ -1220,6 +1220,10 @@ constexpr float kPaInvDiv = 0.125f;  // 1 / (float)sqrt(64), exact
 #endif
 constexpr int kPaChunks = LLM_PA_CHUNKS;
 
+// e^x through the hardware base-2 exponential: x * log2(e) rounded once, then
+// v_exp_f32 (within a few ulps of expf over the softmax's range; e^-inf = 0).
+__device__ __forceinline__ float pa_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+
 template <bool RND>
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc,
                                                            float* out, __half* out_h, __half* out_l, int n_q, int p0,
@@ -1378,7 +1382,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                 for (int i = 0; i < 4; i++) {
                     const int t = c0 + 16 * pt + lr;
                     const float e =
-                        full || span_has(span, t, rpos[i]) ? expf(sc[pt][i] * kPaInvDiv - Mrow[i]) / Lrow[i] : 0.f;
+                        full || span_has(span, t, rpos[i]) ? pa_exp(sc[pt][i] * kPaInvDiv - Mrow[i]) / Lrow[i] : 0.f;
                     Ph[(4 * lq + i) * 2 * PA_PLD + 16 * pt + lr] = (_Float16)e;
                 }
 #pragma unroll
@@ -1411,11 +1415,11 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             mx = fmaxf(mx, xshfl<4>(mx));
             mx = fmaxf(mx, xshfl<8>(mx));
             const float m_new = fmaxf(m_run[i], mx);
-            alpha[i] = m_run[i] == -INFINITY ? 0.f : expf(m_run[i] - m_new);
+            alpha[i] = m_run[i] == -INFINITY ? 0.f : pa_exp(m_run[i] - m_new);
             float ls = 0.f;
 #pragma unroll
             for (int pt = 0; pt < 4; pt++) {
-                const float e = sc[pt][i] == -INFINITY ? 0.f : expf(sc[pt][i] - m_new);
+                const float e = sc[pt][i] == -INFINITY ? 0.f : pa_exp(sc[pt][i] - m_new);
                 sc[pt][i] = e;
                 ls += e;
             }
