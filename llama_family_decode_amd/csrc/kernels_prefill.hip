@@ -991,8 +991,8 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
     const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r32 = lane & 31;
     struct Frag {
         i32x4 a[2], b[2];  // [tile]
-        float dw[2];       // the weight scale of this lane's column, per tile
-        float4 dx[2][4];   // the activation scales of this lane's 16 rows, per tile
+        float sx[2];       // the activation scale of row r32 of each tile
+        float sw[2];       // the weight scale of column r32 of each tile (lanes 32-63: zero)
     };
     // this lane's half of its row (rows are 32-aligned but for r32, whose
     // bits 2 and 3 pick the half swap of the layout)
@@ -1003,14 +1003,14 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
         for (int i = 0; i < 2; i++) {
             const int r = 64 * wm + 32 * i;
             F.a[i] = *(const i32x4*)(st + (r + r32) * 32 + hs);
-#pragma unroll
-            for (int g = 0; g < 4; g++) F.dx[i][g] = *(const float4*)(st + I8_SS + 4 * (r + 8 * g + 4 * h));
+            F.sx[i] = *(const float*)(st + I8_SS + 4 * (r + r32));
         }
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int c = 64 * wn + 32 * j + r32;
             F.b[j] = *(const i32x4*)(st + I8_SW + c * 32 + hs);
-            F.dw[j] = *(const float*)(st + I8_SS + 4 * HL_M + 4 * c);
+            const float d = *(const float*)(st + I8_SS + 4 * HL_M + 4 * c);
+            F.sw[j] = h ? 0.f : d;
         }
     };
     float16v acc[2][2];
@@ -1020,22 +1020,20 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+    // The tile's 32 x 32 scale products d_x * d_w come from the fp32 matrix
+    // cores as a rank-1 product (A[i][k] = d_x of row i for k = 0, 1;
+    // B[0][j] = d_w of column j, B[1][j] = 0), which lands in the int8 result's
+    // layout and is exact, as each product is: it takes them off the VALU,
+    // which the fold saturates.
     auto fmma = [&](const Frag& F) {
 #pragma unroll
         for (int i = 0; i < 2; i++) {
-            float dx[16];
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                dx[4 * g] = F.dx[i][g].x;
-                dx[4 * g + 1] = F.dx[i][g].y;
-                dx[4 * g + 2] = F.dx[i][g].z;
-                dx[4 * g + 3] = F.dx[i][g].w;
-            }
 #pragma unroll
             for (int j = 0; j < 2; j++) {
                 const i32x16 t = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.a[i], F.b[j], (i32x16){}, 0, 0, 0);
+                const float16v d = __builtin_amdgcn_mfma_f32_32x32x2f32(F.sx[i], F.sw[j], (float16v){}, 0, 0, 0);
 #pragma unroll
-                for (int e = 0; e < 16; e++) acc[i][j][e] += (float)t[e] * (F.dw[j] * dx[e]);
+                for (int e = 0; e < 16; e++) acc[i][j][e] += (float)t[e] * d[e];
             }
         }
     };
