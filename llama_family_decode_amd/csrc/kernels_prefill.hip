@@ -992,7 +992,7 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
     struct Frag {
         i32x4 a[2], b[2];  // [tile]
         float sx[2];       // the activation scale of row r32 of each tile
-        float sw[2];       // the weight scale of column r32 of each tile (lanes 32-63: zero)
+        float sw[2];       // the weight scale of column r32 of each tile
     };
     // this lane's half of its row (rows are 32-aligned but for r32, whose
     // bits 2 and 3 pick the half swap of the layout)
@@ -1009,8 +1009,7 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
         for (int j = 0; j < 2; j++) {
             const int c = 64 * wn + 32 * j + r32;
             F.b[j] = *(const i32x4*)(st + I8_SW + c * 32 + hs);
-            const float d = *(const float*)(st + I8_SS + 4 * HL_M + 4 * c);
-            F.sw[j] = h ? 0.f : d;
+            F.sw[j] = *(const float*)(st + I8_SS + 4 * HL_M + 4 * c);
         }
     };
     float16v acc[2][2];
@@ -1020,21 +1019,47 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
-    // The tile's 32 x 32 scale products d_x * d_w come from the fp32 matrix
-    // cores as a rank-1 product (A[i][k] = d_x of row i for k = 0, 1;
-    // B[0][j] = d_w of column j, B[1][j] = 0), which lands in the int8 result's
-    // layout and is exact, as each product is: it takes them off the VALU,
-    // which the fold saturates.
+    // The tile's 32 x 32 scale products d_x * d_w come from the f16 matrix
+    // cores as a rank-1 product: lane l supplies element 0 of its 8-deep K
+    // slice, so A[i][0] = A[i][8] = d_x of row i, B[0][j] = d_w of column j,
+    // B[8][j] = 0 and every other element is 0. Both scales are binary16
+    // values (the weight's stored scale, the input's rounded one), so their
+    // conversion (toward zero) is exact, the matrix cores keep binary16
+    // subnormals, and each product is exact in fp32, in the int8 result's
+    // layout. That takes 64 multiplies per lane and step off the VALU, which
+    // the fold saturates (the fp32 matrix form of the product costs as much
+    // VALU time as the multiplies: its peak is the vector fp32 peak).
+    //
+    // The four tiles of a step are software-pipelined one tile deep: the
+    // matrix cores take tile n's products while the VALU folds tile n - 1's
+    // (a step's last tile is folded behind the next step's first products,
+    // and once more after the last step). pt/pd hold the products of two
+    // tiles; slot 1 starts as an empty tile, whose fold adds +0. The empty asm
+    // after each fold keeps it ahead of the next step's barrier, past which
+    // instruction selection would otherwise sink it.
+    i32x16 pt[2];
+    float16v pd[2];
+#pragma unroll
+    for (int e = 0; e < 16; e++) pt[1][e] = 0, pd[1][e] = 0.f;
+    auto fold = [&](int n) {
+#pragma unroll
+        for (int e = 0; e < 16; e++) acc[n >> 1][n & 1][e] += (float)pt[n & 1][e] * pd[n & 1][e];
+    };
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 xq = {0u, 0u, 0u, 0u}, wq = {0u, 0u, 0u, 0u};
     auto fmma = [&](const Frag& F) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const i32x16 t = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.a[i], F.b[j], (i32x16){}, 0, 0, 0);
-                const float16v d = __builtin_amdgcn_mfma_f32_32x32x2f32(F.sx[i], F.sw[j], (float16v){}, 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < 16; e++) acc[i][j][e] += (float)t[e] * d[e];
-            }
+        for (int n = 0; n < 4; n++) {
+            const int i = n >> 1, j = n & 1;
+            pt[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.a[i], F.b[j], (i32x16){}, 0, 0, 0);
+            xq.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(F.sx[i], 0.f));
+            wq.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(h ? 0.f : F.sw[j], 0.f));
+            pd[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, xq), __builtin_bit_cast(half8, wq),
+                                                           (float16v){}, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            fold((n + 3) & 3);
+            asm volatile("" : "+v"(acc[((n + 3) & 3) >> 1][(n + 3) & 1]));
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     using std::integral_constant;
@@ -1076,6 +1101,7 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
         step(ks + 1, F1, F0, P0{}, std::false_type{});
     }
     if (ks < nk) step(ks, F0, F1, P0{}, std::false_type{});
+    fold(3);
 
 #pragma unroll
     for (int j = 0; j < 2; j++) {

@@ -34,7 +34,7 @@ import pytest
 import oracle
 import synth
 from helpers import SMALL_F16_RND, SMALL_Q8, SMALL_Q8_RND
-from test_gpu_fullsize import _tensors_by_name, check_layer0_kv
+from test_gpu_fullsize import _row, _tensors_by_name, check_layer0_kv
 from test_gpu_fullsize_oracle import _kv_dist
 from test_gpu_parity import tol
 
@@ -159,3 +159,57 @@ def test_int8_prefill_across_chunks():
     m.close()
     print(f"[{cfg.name}] layer-0 K/V within {w0:.0f} ulps; max |dlogit| {err.max():.3e} (bar {bar:.3e}); "
           f"K/V {ratio:.2f} of the bar", flush=True)
+
+
+def _scaled(ts, gain_scale, kv_scale):
+    """The tensor set with layer 0's norm gain times gain_scale and the binary16
+    block scales of its K and V matrices times kv_scale (powers of two)."""
+    out = []
+    for t in ts:
+        if t.name == "blk.0.attn_norm.weight":
+            t = synth.Tensor(t.name, t.dtype, t.ne, (t.data.view(np.float32) * np.float32(gain_scale)).view(np.uint8))
+        elif t.name in ("blk.0.attn_k.weight", "blk.0.attn_v.weight"):
+            assert t.dtype == synth.Q8_0
+            b = t.data.copy().reshape(-1, 34)
+            d = b[:, :2].copy().view(np.float16).astype(np.float32) * np.float32(kv_scale)
+            b[:, :2] = d.astype(np.float16).view(np.uint8).reshape(-1, 2)
+            t = synth.Tensor(t.name, t.dtype, t.ne, b.reshape(-1))
+        out.append(t)
+    return out
+
+
+@pytest.mark.parametrize("gain_scale,kv_scale,which", [(2.0 ** -16, 2.0 ** 12, "input"), (2.0 ** 6, 2.0 ** -8, "weight")],
+                         ids=["subnormal-input-scales", "subnormal-weight-scales"])
+def test_int8_prefill_subnormal_block_scales(gain_scale, kv_scale, which):
+    # Q8_0 block scales below binary16's normal range on one side of layer 0's
+    # K and V products (all input scales, from a norm gain shrunk by 2^-16; or
+    # all K/V weight scales, shrunk by 2^-8), the other side scaled up so the
+    # rows stay normal. The product of the two scales must stay exact ("What a
+    # Llama model computes, and why", section 5: a Q8_0 value is its code times
+    # the block's binary16 scale, subnormals included): layer-0 K/V of all
+    # prompt rows within 2 binary16 ulps of the oracle's. A scale flushed to
+    # zero would zero whole rows.
+    cfg = MEDIUM_Q8_RND.with_(name=f"medium-q8_0-llamacpp-{which}-subnormal")
+    ts = _scaled(synth.make_tensor_set(cfg), gain_scale, kv_scale)
+    T = _tensors_by_name(ts)
+    n = 300
+    toks = synth.prompt(cfg, n)
+    # the premise: the chosen side's block scales are binary16 subnormals
+    tiny = 2.0 ** -14
+    if which == "input":
+        g = oracle.dequantize(0, T["blk.0.attn_norm.weight"].data, cfg.dim)
+        for tok in toks[:8]:
+            h = oracle.rmsnorm(_row(T["token_embd.weight"], cfg.dim, int(tok)), g, cfg.eps)
+            assert np.abs(h).max() / 127 < tiny
+    else:
+        for name in ("blk.0.attn_k.weight", "blk.0.attn_v.weight"):
+            d = T[name].data.reshape(-1, 34)[:, :2].copy().view(np.float16).astype(np.float64)
+            assert np.abs(d).max() < tiny
+    m = llm.Model(cfg, ts)
+    assert llm.llm_op_prefill_int8(m.ctx) == 1
+    m.prefill(toks)
+    w0 = check_layer0_kv(cfg, T, m, [(p, int(toks[p])) for p in range(n)], 2.0)
+    k, v = m.kv_read(0, n - 1)
+    assert np.count_nonzero(k.view(np.float16)) > k.size // 2 and np.count_nonzero(v.view(np.float16)) > v.size // 2
+    m.close()
+    print(f"[{cfg.name}] layer-0 K/V of {n} prompt rows within {w0:.0f} binary16 ulps", flush=True)
