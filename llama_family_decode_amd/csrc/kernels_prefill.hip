@@ -889,8 +889,17 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
                 if (P) {
                     if (m < M && n < N) P[((size_t)z * M + m) * N + n] = v;
                 } else if constexpr (EPI == EPI_SWIGLU) {
-                    const float up = __shfl_xor(v, 1, 64);
-                    if ((lane & 1) == 0 && m < M && n < N) store_swiglu(Y, Yh, Yl, m, n / 2, ldy, v, up);
+                    // lanes 2c and 2c + 1 hold the gate and up columns of one
+                    // hidden unit for rows m (element e) and m + 1 (e + 1):
+                    // one exchange gives the even lane row m's pair and the
+                    // odd lane row m + 1's, so every lane computes a unit
+                    if ((e & 1) == 0) {
+                        const bool odd = lane & 1;
+                        const float w = acc[i][j][e + 1];
+                        const float r = xshfl<1>(odd ? v : w);
+                        const int mr = m + (odd ? 1 : 0);
+                        if (mr < M && n < N) store_swiglu(Y, Yh, Yl, mr, n / 2, ldy, odd ? r : v, odd ? w : r);
+                    }
                 } else if (m < M && n < N) {
                     if constexpr (EPI == EPI_RESID)
                         Y[(size_t)m * ldy + n] += v;
@@ -1115,8 +1124,17 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
                 if (P) {
                     if (m < M && n < N) P[((size_t)z * M + m) * N + n] = v;
                 } else if constexpr (EPI == EPI_SWIGLU) {
-                    const float up = __shfl_xor(v, 1, 64);
-                    if ((lane & 1) == 0 && m < M && n < N) store_swiglu(Y, Yh, Yl, m, n / 2, ldy, v, up);
+                    // lanes 2c and 2c + 1 hold the gate and up columns of one
+                    // hidden unit for rows m (element e) and m + 1 (e + 1):
+                    // one exchange gives the even lane row m's pair and the
+                    // odd lane row m + 1's, so every lane computes a unit
+                    if ((e & 1) == 0) {
+                        const bool odd = lane & 1;
+                        const float w = acc[i][j][e + 1];
+                        const float r = xshfl<1>(odd ? v : w);
+                        const int mr = m + (odd ? 1 : 0);
+                        if (mr < M && n < N) store_swiglu(Y, Yh, Yl, mr, n / 2, ldy, odd ? r : v, odd ? w : r);
+                    }
                 } else if (m < M && n < N) {
                     if constexpr (EPI == EPI_RESID)
                         Y[(size_t)m * ldy + n] += v;
