@@ -774,16 +774,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
         if constexpr (Q8) {
             float16v t[2][NJ];
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int kh = 0; kh < 2; kh++)
 #pragma unroll
-                for (int j = 0; j < NJ; j++) {
-                    t[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.ah[i][0], F.bf[j][0], (float16v){}, 0, 0, 0);
-                    if constexpr (LO)
-                        t[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.al[i][0], F.bf[j][0], t[i][j], 0, 0, 0);
-                    t[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.ah[i][1], F.bf[j][1], t[i][j], 0, 0, 0);
-                    if constexpr (LO)
-                        t[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.al[i][1], F.bf[j][1], t[i][j], 0, 0, 0);
-                }
+                for (int pl = 0; pl < (LO ? 2 : 1); pl++)
+#pragma unroll
+                    for (int i = 0; i < 2; i++)
+#pragma unroll
+                        for (int j = 0; j < NJ; j++)
+                            t[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                pl ? F.al[i][kh] : F.ah[i][kh], F.bf[j][kh], kh || pl ? t[i][j] : (float16v){}, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
@@ -795,13 +794,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
 #pragma unroll
         for (int kh = 0; kh < 2; kh++)
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int pl = 0; pl < (LO ? 2 : 1); pl++)
 #pragma unroll
-                for (int j = 0; j < NJ; j++) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.ah[i][kh], F.bf[j][kh], acc[i][j], 0, 0, 0);
-                    if constexpr (LO)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.al[i][kh], F.bf[j][kh], acc[i][j], 0, 0, 0);
-                }
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int j = 0; j < NJ; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pl ? F.al[i][kh] : F.ah[i][kh], F.bf[j][kh],
+                                                                           acc[i][j], 0, 0, 0);
     };
     // Stage s lives in ring slot s % HL_ST. The fragments of step ks are read
     // during step ks - 1, so while step ks multiplies, the slots hold steps
