@@ -922,9 +922,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
 // (lane l supplies row l%32's codes 16(l/32) .. +15 of the step; the result
 // has the f32 32x32 layout). A stage holds the step's activation codes (4 KB),
 // weight codes (8 KB), then the 128 activation and 256 weight scales as fp32
-// (1.5 KB); an eight-stage DMA ring moves it, two DMAs per wave (a step is
-// consumed faster than one of the binary16 kernel, so the ring holds more).
-constexpr int I8_SW = 4096, I8_SS = 12288, I8_STAGE = 13824, I8_ST = 8;
+// (1.5 KB), then a zero word that no DMA touches (read by the lanes that supply
+// a zero weight scale); an eight-stage DMA ring moves it, two DMAs per wave (a
+// step is consumed faster than one of the binary16 kernel, so the ring holds
+// more).
+constexpr int I8_SW = 4096, I8_SS = 12288, I8_ZERO = 13824, I8_STAGE = 13840, I8_ST = 8;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
@@ -1017,7 +1019,8 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
         for (int j = 0; j < 2; j++) {
             const int c = 64 * wn + 32 * j + r32;
             F.b[j] = *(const i32x4*)(st + I8_SW + c * 32 + hs);
-            F.sw[j] = *(const float*)(st + I8_SS + 4 * HL_M + 4 * c);
+            // lanes 32-63 read the stage's zero word: their B[8][j] is 0
+            F.sw[j] = *(const float*)(st + (h ? I8_ZERO : I8_SS + 4 * HL_M + 4 * c));
         }
     };
     float16v acc[2][2];
@@ -1054,16 +1057,20 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
         for (int e = 0; e < 16; e++) acc[n >> 1][n & 1][e] += (float)pt[n & 1][e] * pd[n & 1][e];
     };
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 xq = {0u, 0u, 0u, 0u}, wq = {0u, 0u, 0u, 0u};
+    u32x4 xq[2], wq[2];
+#pragma unroll
+    for (int t = 0; t < 2; t++) xq[t] = wq[t] = (u32x4){0u, 0u, 0u, 0u};
     auto fmma = [&](const Frag& F) {
 #pragma unroll
         for (int n = 0; n < 4; n++) {
             const int i = n >> 1, j = n & 1;
             pt[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(F.a[i], F.b[j], (i32x16){}, 0, 0, 0);
-            xq.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(F.sx[i], 0.f));
-            wq.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(h ? 0.f : F.sw[j], 0.f));
-            pd[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, xq), __builtin_bit_cast(half8, wq),
-                                                           (float16v){}, 0, 0, 0);
+            if (n < 2) {
+                xq[n].x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(F.sx[n], 0.f));
+                wq[n].x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(F.sw[n], 0.f));
+            }
+            pd[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, xq[i]),
+                                                           __builtin_bit_cast(half8, wq[j]), (float16v){}, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             fold((n + 3) & 3);
             asm volatile("" : "+v"(acc[((n + 3) & 3) >> 1][(n + 3) & 1]));
@@ -1071,6 +1078,9 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
         }
     };
     using std::integral_constant;
+    // the stages' zero words (the first wait below, an LDS count of 0 and a
+    // barrier, orders these stores before every fragment read)
+    if (threadIdx.x < I8_ST) *(float*)(lds + threadIdx.x * I8_STAGE + I8_ZERO) = 0.f;
     for (int p = 0; p < I8_ST && p < nk; p++) issue(p);
     // stage 0 has landed once at most I8_ST - 1 later stages remain (a K
     // shorter than the ring waits for all of them)
