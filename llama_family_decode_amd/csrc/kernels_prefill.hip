@@ -855,7 +855,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
         }
     };
     using P0 = integral_constant<int, 0>;
-    using P1 = integral_constant<int, 1>;
     using P2 = integral_constant<int, 2>;
     using Refill = std::true_type;
     using NoRefill = std::false_type;
@@ -1251,7 +1250,10 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // (q as a hi/lo binary16 pair, K exact), divides them by sqrt(head_dim),
 // masks positions past each row's own, updates the running max m and sum l
 // of the online softmax, and adds P V (P as a hi/lo pair, V exact) to its
-// 16 x 64 output, rescaled by e^(m_old - m_new). The result o / l goes out
+// 16 x 64 output, rescaled by e^(m_old - m_new). Both products run
+// transposed (S^T = K Q^T, O^T = V^T P^T): a lane then holds 16 scores and
+// 16 outputs of one row, its softmax state is its own (two exchanges per
+// reduction), and P^T is the lane's own registers, with no LDS round trip. The result o / l goes out
 // as fp32 rows and as their hi/lo planes (the output product's input).
 // With an attention span (a window plus sinks) each row masks the positions
 // outside its own span, and chunks outside every row's span are skipped; q
@@ -1264,7 +1266,7 @@ hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, i
 // Long contexts split a block's chunks over gridDim.z blocks (cps chunks
 // each) that write their rows' (m, l, unnormalised o) to part, [row][head]
 // [split][2 + 64]; k_attn_prefill_merge then combines the splits.
-constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72, PA_PLD = 68;
+constexpr int PA_ROWS = 64, PA_CH = 64, PA_LD = 72;
 constexpr float kPaInvDiv = 0.125f;  // 1 / (float)sqrt(64), exact
 #ifndef LLM_PA_CHUNKS
 #define LLM_PA_CHUNKS 32
@@ -1284,7 +1286,6 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
     (void)scale_div;  // always 8 here (checked at launch): the scores are multiplied by kPaInvDiv
     __shared__ __attribute__((aligned(16))) __half Ks[PA_CH * PA_LD];   // [position][dim]
     __shared__ __attribute__((aligned(16))) __half Vt[hd * PA_LD];      // [dim][position]
-    __shared__ __attribute__((aligned(16))) float Ps[4][16 * PA_PLD];   // per wave [row][position]
     const int G = n_heads / n_kv_heads, TB = PA_ROWS / G;
     // blocks are dealt out in index order, so the latest query rows (the most
     // causal work) come first, for every KV head, and short blocks fill the tail
@@ -1311,19 +1312,15 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             ql[ks][j] = RND ? (_Float16)0.f : (_Float16)(v[j] - (float)h);
         }
     }
-    // the four rows whose scores and outputs this lane holds: 4*lq + i
-    int rpos[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) rpos[i] = p0 + z0 + (16 * wave + 4 * lq + i) / G;
-
-    float m_run[4], l_run[4];
+    // the lane's row is ra (the row of its q fragments): the products run
+    // transposed, S^T = K Q^T and O^T = V^T P^T, so the lane holds 16 of its
+    // row's scores and 16 of its row's outputs, and the row's softmax state
+    // is the lane's own
+    const int rp = p0 + z0 + ra / G;
+    float m_run = -INFINITY, l_run = 0.f;
     float4v o[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        m_run[i] = -INFINITY;
-        l_run[i] = 0.f;
-        o[i] = (float4v){0.f, 0.f, 0.f, 0.f};
-    }
+    for (int i = 0; i < 4; i++) o[i] = (float4v){0.f, 0.f, 0.f, 0.f};
 
     const int last = p0 + min(z0 + TB, n_q) - 1;  // the block's last position
     const int rfirst = p0 + z0;                     // and its first
@@ -1355,15 +1352,11 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             if (with_v) vr[u] = ok ? *(const u32x4p*)(vbase + (size_t)t * hd + ld8) : z4;
         }
     };
-    float* P = Ps[wave];
-    float Mrow[4], Lrow[4];  // rounding mode: each row's span maximum and sum, from the first pass
+    float Mrow = 0.f, Lrow = 1.f;  // rounding mode: the row's span maximum and sum, from the first pass
     for (int pass = RND ? 0 : 1; pass < 2; pass++) {
     if (RND && pass == 1) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            Mrow[i] = m_run[i];
-            Lrow[i] = l_run[i];
-        }
+        Mrow = m_run;
+        Lrow = l_run;
     }
     // this block's share of the chunks
     const int v_begin = RND ? 0 : min(nv, (int)blockIdx.z * cps), v_end = RND ? nv : min(nv, v_begin + cps);
@@ -1405,8 +1398,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         __syncthreads();
         if (v + 1 < v_end) load(chunk_of(v + 1) * PA_CH, with_v);
 
-        // scores of this wave's 16 rows over the chunk: tile pt covers
-        // positions c0 + 16 pt .. +15
+        // scores over the chunk, transposed: tile pt covers positions
+        // c0 + 16 pt .. +15, and the lane gets its row's scores at positions
+        // c0 + 16 pt + 4 lq + i in sc[pt][i]
         float4v sc[4];
 #pragma unroll
         for (int pt = 0; pt < 4; pt++) {
@@ -1414,8 +1408,8 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
 #pragma unroll
             for (int ks = 0; ks < 2; ks++) {
                 const half8 kf = *(const half8*)(Ks + (16 * pt + lr) * PA_LD + 32 * ks + 8 * lq);
-                sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[ks], kf, sc[pt], 0, 0, 0);
-                if constexpr (!RND) sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], kf, sc[pt], 0, 0, 0);
+                sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qh[ks], sc[pt], 0, 0, 0);
+                if constexpr (!RND) sc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, ql[ks], sc[pt], 0, 0, 0);
             }
         }
         // A chunk every row of the block attends in full needs no mask: all of
@@ -1423,120 +1417,109 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         // window, after the window start of its last position (rows past the
         // last position are padding, never stored).
         const bool full = c0 + PA_CH - 1 <= rfirst && (span.window <= 0 || c0 > last - span.window);
+        // o^T += V^T P^T over the chunk's 64 positions, two 32-deep steps. The
+        // K index of a step may map to positions in any order that P^T and
+        // V^T share: k = 8 lq + j is position 32 ps + 16 (j / 4) + 4 lq + j % 4,
+        // which is the lane's own score sc[2 ps + j / 4][j % 4], and V^T's
+        // row d supplies it as two runs of four positions from Vt.
+        auto pv = [&](int ps, const half8& ph, bool lo_too, const half8& pl) {
+#pragma unroll
+            for (int dt = 0; dt < 4; dt++) {
+                const __half* vrow = Vt + (16 * dt + lr) * PA_LD + 32 * ps + 4 * lq;
+                const uint2 v0 = *(const uint2*)vrow, v1 = *(const uint2*)(vrow + 16);
+                const half8 vf = __builtin_bit_cast(half8, (u32x4p){v0.x, v0.y, v1.x, v1.y});
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph, o[dt], 0, 0, 0);
+                if (lo_too) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl, o[dt], 0, 0, 0);
+            }
+        };
         if (RND && pass == 1) {
-            // the rounded probabilities of the whole span, the P V operand as
-            // is, staged as binary16 (rows 2 * PA_PLD halves apart)
-            _Float16* Ph = (_Float16*)P;
-#pragma unroll
-            for (int pt = 0; pt < 4; pt++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int t = c0 + 16 * pt + lr;
-                    const float e =
-                        full || span_has(span, t, rpos[i]) ? pa_exp(sc[pt][i] * kPaInvDiv - Mrow[i]) / Lrow[i] : 0.f;
-                    Ph[(4 * lq + i) * 2 * PA_PLD + 16 * pt + lr] = (_Float16)e;
-                }
+            // the rounded probabilities of the whole span, the P V operand as is
 #pragma unroll
             for (int ps = 0; ps < 2; ps++) {
-                const half8 ph = *(const half8*)(Ph + lr * 2 * PA_PLD + 32 * ps + 8 * lq);
+                half8 ph;
 #pragma unroll
-                for (int dt = 0; dt < 4; dt++) {
-                    const half8 vf = *(const half8*)(Vt + (16 * dt + lr) * PA_LD + 32 * ps + 8 * lq);
-                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vf, o[dt], 0, 0, 0);
+                for (int j = 0; j < 8; j++) {
+                    const int pt = 2 * ps + (j >> 2), i = j & 3;
+                    const int t = c0 + 16 * pt + 4 * lq + i;
+                    const float e = full || span_has(span, t, rp) ? pa_exp(sc[pt][i] * kPaInvDiv - Mrow) / Lrow : 0.f;
+                    ph[j] = (_Float16)e;
                 }
+                pv(ps, ph, false, ph);
             }
             continue;
         }
-        // online softmax per row; a row's 64 scores sit in the 16 lanes with
-        // the same lq, four tiles each
-        float alpha[4];
+        // online softmax of the lane's row: its 64 scores sit in the four
+        // lanes with the same lr, 16 each
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            float mx = -INFINITY;
+        for (int pt = 0; pt < 4; pt++)
 #pragma unroll
-            for (int pt = 0; pt < 4; pt++) {
-                const int t = c0 + 16 * pt + lr;
-                const float s = full || span_has(span, t, rpos[i]) ? sc[pt][i] * kPaInvDiv : -INFINITY;
-                sc[pt][i] = s;
-                mx = fmaxf(mx, s);
+            for (int i = 0; i < 4; i++) {
+                const int t = c0 + 16 * pt + 4 * lq + i;
+                const float sv = full || span_has(span, t, rp) ? sc[pt][i] * kPaInvDiv : -INFINITY;
+                sc[pt][i] = sv;
+                mx = fmaxf(mx, sv);
             }
-            // over the 16 lanes of the row (offsets 1, 2, 4, 8: DPP and swizzles)
-            mx = fmaxf(mx, xshfl<1>(mx));
-            mx = fmaxf(mx, xshfl<2>(mx));
-            mx = fmaxf(mx, xshfl<4>(mx));
-            mx = fmaxf(mx, xshfl<8>(mx));
-            const float m_new = fmaxf(m_run[i], mx);
-            alpha[i] = m_run[i] == -INFINITY ? 0.f : pa_exp(m_run[i] - m_new);
-            float ls = 0.f;
+        mx = fmaxf(mx, xshfl<16>(mx));
+        mx = fmaxf(mx, xshfl<32>(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.f : pa_exp(m_run - m_new);
+        float ls = 0.f;
 #pragma unroll
-            for (int pt = 0; pt < 4; pt++) {
+        for (int pt = 0; pt < 4; pt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
                 const float e = sc[pt][i] == -INFINITY ? 0.f : pa_exp(sc[pt][i] - m_new);
                 sc[pt][i] = e;
                 ls += e;
             }
-            ls += xshfl<1>(ls);
-            ls += xshfl<2>(ls);
-            ls += xshfl<4>(ls);
-            ls += xshfl<8>(ls);
-            l_run[i] = l_run[i] * alpha[i] + ls;
-            m_run[i] = m_new;
-        }
+        ls += xshfl<16>(ls);
+        ls += xshfl<32>(ls);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
         if (RND) continue;  // the first pass only finds M and L
-#pragma unroll
-        for (int pt = 0; pt < 4; pt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) P[(4 * lq + i) * PA_PLD + 16 * pt + lr] = sc[pt][i];
 #pragma unroll
         for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) o[dt][i] *= alpha[i];
-        // o += P V over the chunk's 64 positions (two 32-deep steps)
+            for (int i = 0; i < 4; i++) o[dt][i] *= alpha;
 #pragma unroll
         for (int ps = 0; ps < 2; ps++) {
-            const float4 p0v = *(const float4*)(P + lr * PA_PLD + 32 * ps + 8 * lq);
-            const float4 p1v = *(const float4*)(P + lr * PA_PLD + 32 * ps + 8 * lq + 4);
-            const float pv[8] = {p0v.x, p0v.y, p0v.z, p0v.w, p1v.x, p1v.y, p1v.z, p1v.w};
             half8 ph, pl;
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                const _Float16 h = (_Float16)pv[j];
+                const float pj = sc[2 * ps + (j >> 2)][j & 3];
+                const _Float16 h = (_Float16)pj;
                 ph[j] = h;
-                pl[j] = (_Float16)(pv[j] - (float)h);
+                pl[j] = (_Float16)(pj - (float)h);
             }
-#pragma unroll
-            for (int dt = 0; dt < 4; dt++) {
-                const half8 vf = *(const half8*)(Vt + (16 * dt + lr) * PA_LD + 32 * ps + 8 * lq);
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vf, o[dt], 0, 0, 0);
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vf, o[dt], 0, 0, 0);
-            }
+            pv(ps, ph, true, pl);
         }
     }
     }
-    if (gridDim.z > 1) {  // this split's (m, l, o) per row for the merge
-        const int S = gridDim.z, s = blockIdx.z;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int r = 16 * wave + 4 * lq + i, z = z0 + r / G, h = g * G + r % G;
-            if (z >= n_q) continue;
-            float* pr = part + (((size_t)z * n_heads + h) * S + s) * (hd + 2);
-            if (lr == 0) {
-                pr[0] = m_run[i];
-                pr[1] = l_run[i];
+    const int z = z0 + ra / G, h = g * G + ra % G;
+    if (gridDim.z > 1) {  // this split's (m, l, o) of the lane's row for the merge
+        const int S = gridDim.z, sp = blockIdx.z;
+        if (z < n_q) {
+            float* pr = part + (((size_t)z * n_heads + h) * S + sp) * (hd + 2);
+            if (lq == 0) {
+                pr[0] = m_run;
+                pr[1] = l_run;
             }
 #pragma unroll
-            for (int dt = 0; dt < 4; dt++) pr[2 + 16 * dt + lr] = o[dt][i];
+            for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) pr[2 + 16 * dt + 4 * lq + i] = o[dt][i];
         }
         return;
     }
-    // out[z][h*64 + d] = o / l for the lane's rows 4 lq + i, dims 16 dt + lr
+    // out[z][h*64 + d] = o / l for the lane's row, dims 16 dt + 4 lq + i
+    if (z >= n_q) return;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int r = 16 * wave + 4 * lq + i, z = z0 + r / G, h = g * G + r % G;
-        if (z >= n_q) continue;
+    for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++) {
-            const float v = RND ? o[dt][i] : o[dt][i] / l_run[i];
-            const int col = h * hd + 16 * dt + lr;
+        for (int i = 0; i < 4; i++) {
+            const float v = RND ? o[dt][i] : o[dt][i] / l_run;
+            const int col = h * hd + 16 * dt + 4 * lq + i;
             if (out) out[(size_t)z * qd + col] = v;
             if (out_h) {
                 const __half hh = __float2half_rn(v);
@@ -1545,7 +1528,6 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                 out_l[t] = __float2half_rn(v - __half2float(hh));
             }
         }
-    }
 }
 
 // The splits of each (row, head): M = max m_s, L = sum l_s e^(m_s - M),
