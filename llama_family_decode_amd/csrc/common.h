@@ -303,11 +303,13 @@ hipError_t launch_tile_w(const Mat& W, hipStream_t s);
 // Causal prefill attention of n_q queries at positions p0 .. p0+n_q-1 on the
 // matrix cores (head_dim 64 only; hipErrorInvalidValue otherwise): out (if
 // set) as fp32 rows [n_q][n_heads*64] and, when out_h is set, their tiled
-// binary16 hi/lo planes.
+// binary16 hi/lo planes. With rnd, oc/ocs (if set) receive the rows' Q8_0
+// codes and block scales in the tiled int8 layout, as launch_round_rows
+// writes them (rnd only: hipErrorInvalidValue otherwise).
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
                                     int n_ctx, float scale_div, const SpanCfg& span, bool rnd, float* ws,
-                                    size_t ws_floats, hipStream_t s);
+                                    size_t ws_floats, hipStream_t s, int8_t* oc = nullptr, float* ocs = nullptr);
 // Activations of a prefill product: fp32 rows (ld K) and, for F16 weights,
 // their binary16 hi/lo planes (tiled layout); l = nullptr when the activations
 // are binary16 already (one matrix-core pass).

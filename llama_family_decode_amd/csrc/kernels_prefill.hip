@@ -1281,7 +1281,8 @@ template <bool RND>
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc,
                                                            float* out, __half* out_h, __half* out_l, int n_q, int p0,
                                                            int n_heads, int n_kv_heads, int n_ctx, float scale_div,
-                                                           SpanCfg span, int cps, float* part) {
+                                                           SpanCfg span, int cps, float* part, int8_t* oc,
+                                                           float* ocs) {
     constexpr int hd = 64;
     (void)scale_div;  // always 8 here (checked at launch): the scores are multiplied by kPaInvDiv
     __shared__ __attribute__((aligned(16))) __half Ks[PA_CH * PA_LD];   // [position][dim]
@@ -1514,6 +1515,33 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
     }
     // out[z][h*64 + d] = o / l for the lane's row, dims 16 dt + 4 lq + i
     if (z >= n_q) return;
+    if constexpr (RND) {
+        if (oc) {
+            // the output product's input as Q8_0 codes, as the row rounding
+            // computes them: block bh of the head (dims 32 bh .. +31) is dt
+            // 2 bh and 2 bh + 1 of the row's four lanes (same lr)
+#pragma unroll
+            for (int bh = 0; bh < 2; bh++) {
+                float amax = 0.f;
+#pragma unroll
+                for (int u = 0; u < 2; u++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) amax = fmaxf(amax, fabsf(o[2 * bh + u][i]));
+                amax = fmaxf(amax, xshfl<16>(amax));
+                amax = fmaxf(amax, xshfl<32>(amax));
+                const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f;
+#pragma unroll
+                for (int u = 0; u < 2; u++) {
+                    uint32_t q = 0u;
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        q |= (uint32_t)(uint8_t)(int8_t)roundf(o[2 * bh + u][i] * id) << (8 * i);
+                    *(uint32_t*)(oc + tile_off_i8(z, h * hd + 32 * bh + 16 * u + 4 * lq, qd, kTileA)) = q;
+                }
+                if (lq == 0) ocs[tile_off_s(z, (h * hd + 32 * bh) >> 5, qd, kTileA)] = round16(d);
+            }
+        }
+    }
 #pragma unroll
     for (int dt = 0; dt < 4; dt++)
 #pragma unroll
@@ -1563,18 +1591,18 @@ __global__ __launch_bounds__(256) void k_attn_prefill_merge(const float* part, i
 hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc, float* out, __half* out_h,
                                     __half* out_l, int n_q, int p0, int n_heads, int n_kv_heads, int head_dim,
                                     int n_ctx, float scale_div, const SpanCfg& span, bool rnd, float* ws,
-                                    size_t ws_floats, hipStream_t s) {
+                                    size_t ws_floats, hipStream_t s, int8_t* oc, float* ocs) {
     const int G = n_kv_heads > 0 ? n_heads / n_kv_heads : 0;
     // the kernel multiplies the scores by 1/8: exactly the division by
     // (float)sqrt(64) = 8, a power of two
     if (head_dim != 64 || scale_div != 8.0f || G < 1 || G > PA_ROWS || PA_ROWS % G || n_heads % n_kv_heads ||
-        n_q <= 0)
+        n_q <= 0 || (oc && (!rnd || !ocs)))
         return hipErrorInvalidValue;
     const int TB = PA_ROWS / G;
     const dim3 grid(n_kv_heads, (n_q + TB - 1) / TB);  // KV head, query-row block from the last
     if (rnd) {
         hipLaunchKernelGGL(k_attn_prefill_mfma<true>, grid, dim3(256), 0, s, Q, kc, vc, out, out_h, out_l, n_q, p0,
-                           n_heads, n_kv_heads, n_ctx, scale_div, span, 0, nullptr);
+                           n_heads, n_kv_heads, n_ctx, scale_div, span, 0, nullptr, oc, ocs);
         return hipGetLastError();
     }
     // at most kPaChunks chunks of 64 positions per block: longer contexts split
@@ -1584,7 +1612,8 @@ hipError_t launch_attn_prefill_mfma(const float* Q, const __half* kc, const __ha
     while (S > 1 && (size_t)n_q * n_heads * S * (head_dim + 2) > ws_floats) S--;
     const int cps = (nch + S - 1) / S;
     hipLaunchKernelGGL(k_attn_prefill_mfma<false>, dim3(grid.x, grid.y, S), dim3(256), 0, s, Q, kc, vc, out, out_h,
-                       out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div, span, cps, S > 1 ? ws : nullptr);
+                       out_l, n_q, p0, n_heads, n_kv_heads, n_ctx, scale_div, span, cps, S > 1 ? ws : nullptr, nullptr,
+                       nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     hipLaunchKernelGGL(k_attn_prefill_merge, dim3((unsigned)((n_q * n_heads + 3) / 4)), dim3(256), 0, s, ws, S, n_q,

@@ -999,18 +999,22 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             // (no hi/lo planes where the output product runs on the codes, no
             // fp32 rows where it reads only the planes, except in the last
             // layer, whose rows are gathered)
-            const bool o_codes = prefill_codes(c, W.o), o_rows = last || !prefill_planes_only(c, W.o);
+            // (in the rounding mode the attention writes the output product's
+            // Q8_0 codes itself, except in the last layer, whose rows are
+            // gathered first)
+            const bool o_codes = prefill_codes(c, W.o), o_fused = rnd && o_codes && mfma_attn && !last;
+            const bool o_rows = last || (!prefill_planes_only(c, W.o) && !o_fused);
             if (mfma_attn)
                 HIPCHK(c, launch_attn_prefill_mfma(L.Q, kc, vc, o_rows ? L.Of : nullptr, o_codes ? nullptr : L.Oh,
                                                    o_codes ? nullptr : L.Ol, m, p0, cf.n_heads, cf.n_kv_heads,
                                                    cf.head_dim, cf.n_ctx, t.scale_div, t.span, rnd, L.ws, L.ws_floats,
-                                                   s));
+                                                   s, o_fused ? L.Ci : nullptr, o_fused ? L.Cs : nullptr));
             else
                 HIPCHK(c, launch_attn(t, m, s));
             // output product + residual, RMSNorm, gate/up + SwiGLU, down +
             // residual over mr rows (attention outputs `of`, residuals X)
-            auto post_attention = [&](const float* of, float* X, int mr) -> int {
-                if (rnd)
+            auto post_attention = [&](const float* of, float* X, int mr, bool o_done) -> int {
+                if (rnd && !o_done)
                     HIPCHK(c, round_rows((float*)of, mr, qd, W.o, L.Oh, L.Ol));
                 else if (W.o.wt && (last || !mfma_attn))  // the planes the tiled product reads
                     HIPCHK(c, launch_split_hl(of, mr, qd, L.Oh, L.Ol, s));
@@ -1037,7 +1041,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 return LLM_OK;
             };
             if (!last) {
-                if ((rc = post_attention(L.Of, L.X, m))) return rc;
+                if ((rc = post_attention(L.Of, L.X, m, o_fused))) return rc;
                 continue;
             }
             // The last layer: only the wanted rows go on, gathered into compact
@@ -1048,7 +1052,7 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                 const int kb = k - b0 < kPrefillChunk ? k - b0 : kPrefillChunk;
                 HIPCHK(c, launch_gather_rows(L.Of, qd, L.sel + sb + b0, kb, L.Q, s));
                 HIPCHK(c, launch_gather_rows(L.X, cf.dim, L.sel + sb + b0, kb, L.Xc, s));
-                if ((rc = post_attention(L.Q, L.Xc, kb))) return rc;
+                if ((rc = post_attention(L.Q, L.Xc, kb, false))) return rc;
                 if (d_rows) {
                     // product rows land at their output indices
                     HIPCHK(c, launch_rmsnorm_rows(L.Xc, L.out_norm, kb, cf.dim, cf.eps, L.Hf, L.Hh, L.Hl, s));
