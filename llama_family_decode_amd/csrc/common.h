@@ -329,10 +329,15 @@ struct GemmA {
 // Yh is set. ws (ws_floats floats) holds split-K partials. A plain store may
 // scatter its rows: with ymap (device, n entries) row m goes to Y row ymap[m].
 // A residual product with defer set leaves a split-K product's S partials in
-// ws for the caller (*defer = S; 0 when it wrote Y itself).
+// ws for the caller (*defer = S; 0 when it wrote Y itself). A SwiGLU product
+// given yc/ycs (and no Yh) may write its output as Q8_0 codes and block scales
+// in the tiled int8 layout (K = ldy), as launch_round_rows writes them, instead
+// of the fp32 rows Y: it does so when its integer path runs over one K split,
+// and then sets *yc_done to 1 (else 0, and Y holds the rows).
 hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
                        __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s,
-                       const int* ymap = nullptr, int* defer = nullptr);
+                       const int* ymap = nullptr, int* defer = nullptr, int8_t* yc = nullptr, float* ycs = nullptr,
+                       int* yc_done = nullptr);
 // X[m] += the S split-K partials of ws (z order), then Y = rmsnorm(X[m]) * gain
 // as launch_rmsnorm_rows computes it.
 hipError_t launch_reduce_norm_rows(const float* P, int S, int n, float* X, int dim, const float* gain, float eps,

@@ -932,7 +932,7 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 template <int EPI>
 __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const float* As, int M, int kz, int nm,
                                                  int nn, float* Y, int ldy, const float* bias, __half* Yh, __half* Yl,
-                                                 float* P, const int* ymap) {
+                                                 float* P, const int* ymap, int8_t* yc, float* ycs) {
     __shared__ __attribute__((aligned(1024))) char lds[I8_ST * I8_STAGE];
     const int N = W.rows, K = W.cols;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1120,6 +1120,44 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
     if (ks < nk) step(ks, F0, F1, P0{}, std::false_type{});
     fold(3);
 
+    if constexpr (EPI == EPI_SWIGLU) {
+        if (yc && !P) {
+            // The down product's input as Q8_0 codes, computed as the row
+            // rounding computes them. One block of 32 hidden units of a row is
+            // this wave's 64 interleaved columns: units ub + 16 j + k from
+            // tile j, unit ub + 16 j + k of row m in lane 2k and of row m + 1
+            // in lane 2k + 1 after the pair exchange, so the block's maximum
+            // is a reduction over the 16 lanes of one parity.
+            const int ub = (n0 + 64 * wn) / 2, k = r32 >> 1;
+            const bool odd = lane & 1;
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int e = 0; e < 16; e += 2) {
+                    const int mr = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3) + (odd ? 1 : 0);
+                    float u[2];
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        const float v = acc[i][j][e], w = acc[i][j][e + 1];
+                        const float r = xshfl<1>(odd ? v : w);
+                        u[j] = pf_silu(odd ? r : v) * (odd ? w : r);
+                    }
+                    float amax = fmaxf(fabsf(u[0]), fabsf(u[1]));
+                    amax = fmaxf(amax, xshfl<2>(amax));
+                    amax = fmaxf(amax, xshfl<4>(amax));
+                    amax = fmaxf(amax, xshfl<8>(amax));
+                    amax = fmaxf(amax, xshfl<16>(amax));
+                    const float d = amax / 127.f, id = d != 0.f ? 1.f / d : 0.f;
+                    if (mr < M && 2 * ub < N) {
+#pragma unroll
+                        for (int j = 0; j < 2; j++)
+                            yc[tile_off_i8(mr, ub + 16 * j + k, ldy, kTileA)] = (int8_t)roundf(u[j] * id);
+                        if (k == 0) ycs[tile_off_s(mr, ub >> 5, ldy, kTileA)] = round16(d);
+                    }
+                }
+            return;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int n = n0 + 64 * wn + 32 * j + r32;
@@ -1173,15 +1211,21 @@ static int gemm_splits(int M, int N, int K, int tm, int tn, int smax, size_t ws_
 
 template <int EPI>
 static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias, __half* Yh,
-                           __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap, int* defer) {
+                           __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap, int* defer,
+                           int8_t* yc, float* ycs, int* yc_done) {
     if (defer) *defer = 0;
+    if (yc_done) *yc_done = 0;
     const int N = W.rows, K = W.cols;
     int S = 1;
     if (W.dtype == DT_Q8 && W.wi && W.si && A.c && A.cs && K % HL_K == 0) {
         S = gemm_splits(n, N, K, HL_M, HL_N, 8, ws_floats);
         const int nm = (n + HL_M - 1) / HL_M, nn = (N + HL_N - 1) / HL_N;
-        hipLaunchKernelGGL((k_gemm_i8<EPI>), dim3(nm * nn, S), dim3(512), 0, s, W, A.c, A.cs, n, K / S, nm, nn, Y, ldy,
-                           bias, Yh, Yl, S > 1 ? ws : nullptr, ymap);
+        // a SwiGLU product over one K split may write its output as codes
+        const bool fuse = EPI == EPI_SWIGLU && yc && S == 1 && ldy % 32 == 0;
+        hipLaunchKernelGGL((k_gemm_i8<EPI>), dim3(nm * nn, S), dim3(512), 0, s, W, A.c, A.cs, n, K / S, nm, nn,
+                           fuse ? nullptr : Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr, ymap, fuse ? yc : nullptr,
+                           fuse ? ycs : nullptr);
+        if (yc_done) *yc_done = fuse;
     } else if (W.dtype == DT_F32) {
         dim3 grid((N + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
         hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl, ymap);
@@ -1229,12 +1273,17 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
 
 hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
                        __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap,
-                       int* defer) {
-    if ((ymap && epi != EPI_STORE) || (defer && epi != EPI_RESID)) return hipErrorInvalidValue;
+                       int* defer, int8_t* yc, float* ycs, int* yc_done) {
+    if ((ymap && epi != EPI_STORE) || (defer && epi != EPI_RESID) || (yc && (epi != EPI_SWIGLU || !ycs || Yh)))
+        return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_STORE: return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer);
-        case EPI_RESID: return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer);
-        case EPI_SWIGLU: return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer);
+        case EPI_STORE:
+            return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer, yc, ycs, yc_done);
+        case EPI_RESID:
+            return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer, yc, ycs, yc_done);
+        case EPI_SWIGLU:
+            return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer, yc, ycs,
+                                        yc_done);
     }
     return hipErrorInvalidValue;
 }

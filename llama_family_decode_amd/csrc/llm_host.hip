@@ -1024,16 +1024,25 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
                                       nullptr, L.ws, L.ws_floats, s, nullptr, &S));
                 HIPCHK(c, norm_rows(L.ws, S, X, mr, W.ffn_norm, W.gu));
                 if (rnd && !prefill_codes(c, W.gu)) HIPCHK(c, round_rows(L.Hf, mr, cf.dim, W.gu, L.Hh, L.Hl));
-                // (no hi/lo planes of the SwiGLU output where down runs on the codes)
+                // (no hi/lo planes of the SwiGLU output where down runs on the
+                // codes; in the rounding mode the gate/up product may write
+                // those codes itself, into the fp32 rows' buffer, which it then
+                // leaves unused: kPrefillChunk x ffn bytes of codes, then the
+                // block scales)
                 const bool d_codes = prefill_codes(c, W.down);
+                int8_t* uc = (int8_t*)L.Uf;
+                float* ucs = (float*)(uc + (size_t)kPrefillChunk * cf.ffn);
+                int u_done = 0;
                 HIPCHK(c, launch_gemm(EPI_SWIGLU, W.gu, ga(W.gu, L.Hf, L.Hh, L.Hl), mr,
                                       prefill_planes_only(c, W.down) ? nullptr : L.Uf, cf.ffn, nullptr,
-                                      d_codes ? nullptr : L.Uh, d_codes ? nullptr : L.Ul, L.ws, L.ws_floats, s));
-                if (rnd) HIPCHK(c, round_rows(L.Uf, mr, cf.ffn, W.down, L.Uh, L.Ul));
+                                      d_codes ? nullptr : L.Uh, d_codes ? nullptr : L.Ul, L.ws, L.ws_floats, s,
+                                      nullptr, nullptr, d_codes ? uc : nullptr, ucs, &u_done));
+                if (rnd && !u_done) HIPCHK(c, round_rows(L.Uf, mr, cf.ffn, W.down, L.Uh, L.Ul));
+                const GemmA da = u_done ? GemmA{nullptr, nullptr, nullptr, uc, ucs} : ga(W.down, L.Uf, L.Uh, L.Ul);
                 // before another layer a split-K down product's reduction is
                 // fused with that layer's attention norm
-                HIPCHK(c, launch_gemm(EPI_RESID, W.down, ga(W.down, L.Uf, L.Uh, L.Ul), mr, X, cf.dim, nullptr,
-                                      nullptr, nullptr, L.ws, L.ws_floats, s, nullptr, last ? nullptr : &S));
+                HIPCHK(c, launch_gemm(EPI_RESID, W.down, da, mr, X, cf.dim, nullptr, nullptr, nullptr, L.ws,
+                                      L.ws_floats, s, nullptr, last ? nullptr : &S));
                 if (!last && S) {
                     HIPCHK(c, norm_rows(L.ws, S, X, mr, L.layers[l + 1].attn_norm, L.layers[l + 1].qkv));
                     normed = true;
