@@ -1402,11 +1402,12 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             if (with_v) vr[u] = ok ? *(const u32x4p*)(vbase + (size_t)t * hd + ld8) : z4;
         }
     };
-    float Mrow = 0.f, Lrow = 1.f;  // rounding mode: the row's span maximum and sum, from the first pass
+    float Mrow = 0.f, Lrow = 1.f, Rrow = 1.f;  // rounding mode: the row's span maximum and sum, and 1 / sum
     for (int pass = RND ? 0 : 1; pass < 2; pass++) {
     if (RND && pass == 1) {
         Mrow = m_run;
         Lrow = l_run;
+        Rrow = 1.f / Lrow;
     }
     // this block's share of the chunks
     const int v_begin = RND ? 0 : min(nv, (int)blockIdx.z * cps), v_end = RND ? nv : min(nv, v_begin + cps);
@@ -1491,7 +1492,15 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                 for (int j = 0; j < 8; j++) {
                     const int pt = 2 * ps + (j >> 2), i = j & 3;
                     const int t = c0 + 16 * pt + 4 * lq + i;
-                    const float e = full || span_has(span, t, rp) ? pa_exp(sc[pt][i] * kPaInvDiv - Mrow) / Lrow : 0.f;
+                    // e / L, correctly rounded, from the correctly rounded 1 / L:
+                    // q = e r is within an ulp of e / L, its residual e - q L is
+                    // exact (an FMA), and q + (e - q L) r rounds to e / L
+                    // (Markstein's division step)
+                    const float ex = full || span_has(span, t, rp) ? pa_exp(sc[pt][i] * kPaInvDiv - Mrow) : 0.f;
+                    const float q0 = ex * Rrow;
+                    float e = fmaf(fmaf(-q0, Lrow, ex), Rrow, q0);
+                    // (rounded to fp32 first, as the quotient is, before binary16)
+                    asm volatile("" : "+v"(e));
                     ph[j] = (_Float16)e;
                 }
                 pv(ps, ph, false, ph);
