@@ -1495,7 +1495,9 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                     // e / L, correctly rounded, from the correctly rounded 1 / L:
                     // q = e r is within an ulp of e / L, its residual e - q L is
                     // exact (an FMA), and q + (e - q L) r rounds to e / L
-                    // (Markstein's division step)
+                    // (Markstein's division step) unless the residual
+                    // underflows, for quotients below about 2^-120, which are
+                    // 0 in binary16 either way
                     const float ex = full || span_has(span, t, rp) ? pa_exp(sc[pt][i] * kPaInvDiv - Mrow) : 0.f;
                     const float q0 = ex * Rrow;
                     float e = fmaf(fmaf(-q0, Lrow, ex), Rrow, q0);
