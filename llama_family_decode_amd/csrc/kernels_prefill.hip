@@ -1325,6 +1325,11 @@ constexpr int kPaChunks = LLM_PA_CHUNKS;
 // e^x through the hardware base-2 exponential: x * log2(e) rounded once, then
 // v_exp_f32 (within a few ulps of expf over the softmax's range; e^-inf = 0).
 __device__ __forceinline__ float pa_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+// e^(x/8) for an unscaled score difference x: the same as pa_exp(x/8), since
+// scaling by 1/8 is exact and moves into the constant (log2(e)/8 is exact too)
+__device__ __forceinline__ float pa_exp8(float x) {
+    return __builtin_amdgcn_exp2f(x * (1.44269504088896341f * 0.125f));
+}
 
 template <bool RND>
 __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const __half* kc, const __half* vc,
@@ -1333,7 +1338,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                                                            SpanCfg span, int cps, float* part, int8_t* oc,
                                                            float* ocs) {
     constexpr int hd = 64;
-    (void)scale_div;  // always 8 here (checked at launch): the scores are multiplied by kPaInvDiv
+    (void)scale_div;  // always 8 here (checked at launch): the scores are scaled by kPaInvDiv = 1/8
     __shared__ __attribute__((aligned(16))) __half Ks[PA_CH * PA_LD];   // [position][dim]
     __shared__ __attribute__((aligned(16))) __half Vt[hd * PA_LD];      // [dim][position]
     const int G = n_heads / n_kv_heads, TB = PA_ROWS / G;
@@ -1498,7 +1503,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
                     // (Markstein's division step) unless the residual
                     // underflows, for quotients below about 2^-120, which are
                     // 0 in binary16 either way
-                    const float ex = full || span_has(span, t, rp) ? pa_exp(sc[pt][i] * kPaInvDiv - Mrow) : 0.f;
+                    const float ex = full || span_has(span, t, rp) ? pa_exp8(sc[pt][i] - Mrow) : 0.f;
                     const float q0 = ex * Rrow;
                     float e = fmaf(fmaf(-q0, Lrow, ex), Rrow, q0);
                     // (rounded to fp32 first, as the quotient is, before binary16)
@@ -1510,30 +1515,44 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
             continue;
         }
         // online softmax of the lane's row: its 64 scores sit in the four
-        // lanes with the same lr, 16 each
+        // lanes with the same lr, 16 each. The scores and the running maximum
+        // stay unscaled (the 1/8 goes into the exponentials, pa_exp8); a chunk
+        // the row attends in full has only finite scores, so its maximum is
+        // finite and its exponentials need no test for masked positions.
         float mx = -INFINITY;
 #pragma unroll
         for (int pt = 0; pt < 4; pt++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int t = c0 + 16 * pt + 4 * lq + i;
-                const float sv = full || span_has(span, t, rp) ? sc[pt][i] * kPaInvDiv : -INFINITY;
+                const float sv = full || span_has(span, t, rp) ? sc[pt][i] : -INFINITY;
                 sc[pt][i] = sv;
                 mx = fmaxf(mx, sv);
             }
         mx = fmaxf(mx, xshfl<16>(mx));
         mx = fmaxf(mx, xshfl<32>(mx));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_run == -INFINITY ? 0.f : pa_exp(m_run - m_new);
+        const float alpha = m_run == -INFINITY ? 0.f : pa_exp8(m_run - m_new);
         float ls = 0.f;
+        if (full) {
 #pragma unroll
-        for (int pt = 0; pt < 4; pt++)
+            for (int pt = 0; pt < 4; pt++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float e = sc[pt][i] == -INFINITY ? 0.f : pa_exp(sc[pt][i] - m_new);
-                sc[pt][i] = e;
-                ls += e;
-            }
+                for (int i = 0; i < 4; i++) {
+                    const float e = pa_exp8(sc[pt][i] - m_new);
+                    sc[pt][i] = e;
+                    ls += e;
+                }
+        } else {
+#pragma unroll
+            for (int pt = 0; pt < 4; pt++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const float e = sc[pt][i] == -INFINITY ? 0.f : pa_exp8(sc[pt][i] - m_new);
+                    sc[pt][i] = e;
+                    ls += e;
+                }
+        }
         ls += xshfl<16>(ls);
         ls += xshfl<32>(ls);
         l_run = l_run * alpha + ls;
@@ -1563,7 +1582,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(const float* Q, const
         if (z < n_q) {
             float* pr = part + (((size_t)z * n_heads + h) * S + sp) * (hd + 2);
             if (lq == 0) {
-                pr[0] = m_run;
+                pr[0] = m_run * kPaInvDiv;  // the maximum in scaled units (exact)
                 pr[1] = l_run;
             }
 #pragma unroll
