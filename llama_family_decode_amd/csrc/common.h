@@ -334,10 +334,21 @@ struct GemmA {
 // in the tiled int8 layout (K = ldy), as launch_round_rows writes them, instead
 // of the fp32 rows Y: it does so when its integer path runs over one K split,
 // and then sets *yc_done to 1 (else 0, and Y holds the rows).
+// A q|k|v product given ro (head_dim 64, every pair rotated) may instead apply
+// RoPE to its rows and write q to ro.Q and k, v to this layer's F16 cache, as
+// launch_rope_kv_rows does from Y: it does so over one K split on the tiled
+// and integer paths, and then sets *ro_done to 1 (else 0, and Y holds the rows).
+struct RopeArgs {
+    const float2* rope;  // [pos][32] (cos, sin)
+    float* Q;            // [n][n_heads * 64]
+    __half* kc;          // [n_kv_heads][n_ctx][64]
+    __half* vc;
+    int p0, n_heads, n_kv_heads, n_ctx, neox;
+};
 hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
                        __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s,
                        const int* ymap = nullptr, int* defer = nullptr, int8_t* yc = nullptr, float* ycs = nullptr,
-                       int* yc_done = nullptr);
+                       int* yc_done = nullptr, const RopeArgs* ro = nullptr, int* ro_done = nullptr);
 // X[m] += the S split-K partials of ws (z order), then Y = rmsnorm(X[m]) * gain
 // as launch_rmsnorm_rows computes it.
 hipError_t launch_reduce_norm_rows(const float* P, int S, int n, float* X, int dim, const float* gain, float eps,

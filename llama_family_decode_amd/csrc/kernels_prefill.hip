@@ -26,6 +26,48 @@ __device__ __forceinline__ float2 pf_rope_rotate(float x0, float x1, float2 cs) 
 __device__ __forceinline__ float pf_h2f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
 __device__ __forceinline__ float pf_silu(float z) { return z / (1.0f + expf(-z)); }
 
+// One wave's 64 q|k|v columns hc .. hc + 63 (one head: hc % 64 == 0) of row
+// m, v0 / v1 the columns hc + r32 and hc + 32 + r32 with the bias added: RoPE
+// as k_rope_kv_rows applies it (head_dim 64, every pair rotated; NEOX pairs
+// (d, d + 32) in one lane, normal pairs (2p, 2p + 1) in lanes r32 and r32 ^ 1),
+// then the Q row or the F16 cache row. Every lane of the wave calls it (the
+// pair exchange); rows m >= M write nothing.
+__device__ __forceinline__ void rope_store2(const RopeArgs& ro, int m, int M, int hc, int r32, float v0, float v1) {
+    const int qd = ro.n_heads * 64, kvd = ro.n_kv_heads * 64, pos = ro.p0 + m;
+    float o0 = v0, o1 = v1;
+    if (hc < qd + kvd) {
+        if (ro.neox) {
+            if (m < M) {
+                const float2 rv = pf_rope_rotate(v0, v1, ro.rope[(size_t)pos * 32 + r32]);
+                o0 = rv.x;
+                o1 = rv.y;
+            }
+        } else {
+            const float w0 = xshfl<1>(v0), w1 = xshfl<1>(v1);
+            const bool odd = r32 & 1;
+            if (m < M) {
+                const float2 r0 = pf_rope_rotate(odd ? w0 : v0, odd ? v0 : w0, ro.rope[(size_t)pos * 32 + (r32 >> 1)]);
+                const float2 r1 =
+                    pf_rope_rotate(odd ? w1 : v1, odd ? v1 : w1, ro.rope[(size_t)pos * 32 + 16 + (r32 >> 1)]);
+                o0 = odd ? r0.y : r0.x;
+                o1 = odd ? r1.y : r1.x;
+            }
+        }
+    }
+    if (m >= M) return;
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int n = hc + 32 * j + r32;
+        const float o = j ? o1 : o0;
+        if (n < qd)
+            ro.Q[(size_t)m * qd + n] = o;
+        else if (n < qd + kvd)
+            ro.kc[((size_t)((n - qd) >> 6) * ro.n_ctx + pos) * 64 + (n & 63)] = __float2half_rn(o);
+        else
+            ro.vc[((size_t)((n - qd - kvd) >> 6) * ro.n_ctx + pos) * 64 + (n & 63)] = __float2half_rn(o);
+    }
+}
+
 // ------------------------------------------------------------ embedding rows
 __global__ void k_embed_rows(Mat E, const int* tokens, int n, float* X, int dim) {
     const int row = blockIdx.x;
@@ -655,7 +697,7 @@ __device__ __forceinline__ int hl_slot(int r, int c) { return 4 * r + (c ^ tile_
 template <int EPI, int NW, bool LO, bool Q8>
 __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, const __half* Al, int M, int kz, int nm,
                                                      int nn, float* Y, int ldy, const float* bias, __half* Yh,
-                                                     __half* Yl, float* P, const int* ymap) {
+                                                     __half* Yl, float* P, const int* ymap, RopeArgs ro) {
     // NW waves in a 2 x NW/2 arrangement; wave tile 64 x (256 / (NW/2)) as
     // 2 x NJ tiles of the 32x32x16 instruction (on gfx950 it moves twice the
     // operands per cycle of the 16x16x32 one)
@@ -875,6 +917,26 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_hl(Mat W, const __half* Ah, co
     }
     if (ks < nk) step(ks, F0, F1, P0{}, NoRefill{});
 
+    if constexpr (EPI == EPI_STORE && NJ == 2) {
+        if (ro.Q && !P) {  // q|k|v with RoPE and the K/V rows (one head per wave)
+            const int hc = n0 + 64 * wn, r32 = lane & 31;
+            if (hc < N) {
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        float v0 = acc[i][0][e], v1 = acc[i][1][e];
+                        if (bias) {
+                            v0 = v0 + bias[hc + r32];
+                            v1 = v1 + bias[hc + 32 + r32];
+                        }
+                        rope_store2(ro, m, M, hc, r32, v0, v1);
+                    }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < NJ; j++) {
         const int n = n0 + 32 * NJ * wn + 32 * j + (lane & 31);
@@ -932,7 +994,7 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 template <int EPI>
 __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const float* As, int M, int kz, int nm,
                                                  int nn, float* Y, int ldy, const float* bias, __half* Yh, __half* Yl,
-                                                 float* P, const int* ymap, int8_t* yc, float* ycs) {
+                                                 float* P, const int* ymap, int8_t* yc, float* ycs, RopeArgs ro) {
     __shared__ __attribute__((aligned(1024))) char lds[I8_ST * I8_STAGE];
     const int N = W.rows, K = W.cols;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1120,6 +1182,26 @@ __global__ __launch_bounds__(512) void k_gemm_i8(Mat W, const int8_t* Ac, const 
     if (ks < nk) step(ks, F0, F1, P0{}, std::false_type{});
     fold(3);
 
+    if constexpr (EPI == EPI_STORE) {
+        if (ro.Q && !P) {  // q|k|v with RoPE and the K/V rows (one head per wave)
+            const int hc = n0 + 64 * wn;
+            if (hc < N) {
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const int m = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+                        float v0 = acc[i][0][e], v1 = acc[i][1][e];
+                        if (bias) {
+                            v0 = v0 + bias[hc + r32];
+                            v1 = v1 + bias[hc + 32 + r32];
+                        }
+                        rope_store2(ro, m, M, hc, r32, v0, v1);
+                    }
+            }
+            return;
+        }
+    }
     if constexpr (EPI == EPI_SWIGLU) {
         if (yc && !P) {
             // The down product's input as Q8_0 codes, computed as the row
@@ -1212,9 +1294,11 @@ static int gemm_splits(int M, int N, int K, int tm, int tn, int smax, size_t ws_
 template <int EPI>
 static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias, __half* Yh,
                            __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap, int* defer,
-                           int8_t* yc, float* ycs, int* yc_done) {
+                           int8_t* yc, float* ycs, int* yc_done, const RopeArgs* ro, int* ro_done) {
     if (defer) *defer = 0;
     if (yc_done) *yc_done = 0;
+    if (ro_done) *ro_done = 0;
+    const RopeArgs ro_off{};
     const int N = W.rows, K = W.cols;
     int S = 1;
     if (W.dtype == DT_Q8 && W.wi && W.si && A.c && A.cs && K % HL_K == 0) {
@@ -1222,10 +1306,13 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
         const int nm = (n + HL_M - 1) / HL_M, nn = (N + HL_N - 1) / HL_N;
         // a SwiGLU product over one K split may write its output as codes
         const bool fuse = EPI == EPI_SWIGLU && yc && S == 1 && ldy % 32 == 0;
+        // a q|k|v product over one K split may apply RoPE and write Q and the cache rows
+        const bool rfuse = EPI == EPI_STORE && ro && S == 1 && !ymap;
         hipLaunchKernelGGL((k_gemm_i8<EPI>), dim3(nm * nn, S), dim3(512), 0, s, W, A.c, A.cs, n, K / S, nm, nn,
                            fuse ? nullptr : Y, ldy, bias, Yh, Yl, S > 1 ? ws : nullptr, ymap, fuse ? yc : nullptr,
-                           fuse ? ycs : nullptr);
+                           fuse ? ycs : nullptr, rfuse ? *ro : ro_off);
         if (yc_done) *yc_done = fuse;
+        if (ro_done) *ro_done = rfuse;
     } else if (W.dtype == DT_F32) {
         dim3 grid((N + GF_T - 1) / GF_T, (n + GF_T - 1) / GF_T);
         hipLaunchKernelGGL((k_gemm_f32<EPI>), grid, dim3(256), 0, s, W, A.f, n, Y, ldy, bias, Yh, Yl, ymap);
@@ -1233,21 +1320,25 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
         S = gemm_splits(n, N, K, HL_M, HL_N, 8, ws_floats);
         const int nm = (n + HL_M - 1) / HL_M, nn = (N + HL_N - 1) / HL_N;
         float* Pw = S > 1 ? ws : nullptr;
+        // (the fused q|k|v epilogue needs 64-column wave tiles: eight waves)
+        const bool rfuse = EPI == EPI_STORE && ro && S == 1 && !ymap && (W.dtype == DT_Q8 || LLM_HL_WAVES == 8);
+        const RopeArgs& rk = rfuse ? *ro : ro_off;
         // without a lo plane the activations are binary16: one product per tile
         if (W.dtype == DT_Q8) {
             if (A.l)
                 hipLaunchKernelGGL((k_gemm_hl<EPI, 8, true, true>), dim3(nm * nn, S), dim3(512), 0, s, W, A.h, A.l, n,
-                                   K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap);
+                                   K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap, rk);
             else
                 hipLaunchKernelGGL((k_gemm_hl<EPI, 8, false, true>), dim3(nm * nn, S), dim3(512), 0, s, W, A.h, A.h, n,
-                                   K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap);
+                                   K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap, rk);
         } else if (A.l) {
             hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES, true, false>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES), 0,
-                               s, W, A.h, A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap);
+                               s, W, A.h, A.l, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap, rk);
         } else {
             hipLaunchKernelGGL((k_gemm_hl<EPI, LLM_HL_WAVES, false, false>), dim3(nm * nn, S), dim3(64 * LLM_HL_WAVES),
-                               0, s, W, A.h, A.h, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap);
+                               0, s, W, A.h, A.h, n, K / S, nm, nn, Y, ldy, bias, Yh, Yl, Pw, ymap, rk);
         }
+        if (ro_done) *ro_done = rfuse;
     } else {
         S = gemm_splits(n, N, K, GB_M, GB_N, 4, ws_floats);
         dim3 grid((N + GB_N - 1) / GB_N, (n + GB_M - 1) / GB_M, S);
@@ -1273,17 +1364,20 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
 
 hipError_t launch_gemm(int epi, const Mat& W, const GemmA& A, int n, float* Y, int ldy, const float* bias,
                        __half* Yh, __half* Yl, float* ws, size_t ws_floats, hipStream_t s, const int* ymap,
-                       int* defer, int8_t* yc, float* ycs, int* yc_done) {
-    if ((ymap && epi != EPI_STORE) || (defer && epi != EPI_RESID) || (yc && (epi != EPI_SWIGLU || !ycs || Yh)))
+                       int* defer, int8_t* yc, float* ycs, int* yc_done, const RopeArgs* ro, int* ro_done) {
+    if ((ymap && epi != EPI_STORE) || (defer && epi != EPI_RESID) || (yc && (epi != EPI_SWIGLU || !ycs || Yh)) ||
+        (ro && (epi != EPI_STORE || ymap || !ro->Q || !ro->kc || !ro->vc || !ro->rope || Yh || ldy % 64)))
         return hipErrorInvalidValue;
     switch (epi) {
         case EPI_STORE:
-            return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer, yc, ycs, yc_done);
+            return gemm_epi<EPI_STORE>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer, yc, ycs, yc_done,
+                                       ro, ro_done);
         case EPI_RESID:
-            return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer, yc, ycs, yc_done);
+            return gemm_epi<EPI_RESID>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer, yc, ycs, yc_done,
+                                       ro, ro_done);
         case EPI_SWIGLU:
             return gemm_epi<EPI_SWIGLU>(W, A, n, Y, ldy, bias, Yh, Yl, ws, ws_floats, s, ymap, defer, yc, ycs,
-                                        yc_done);
+                                        yc_done, ro, ro_done);
     }
     return hipErrorInvalidValue;
 }

@@ -972,10 +972,16 @@ static int prefill_pass(llm_ctx* c, const int32_t* h_tokens, int32_t n, const st
             if (!normed) HIPCHK(c, norm_rows(nullptr, 0, L.X, m, W.attn_norm, W.qkv));
             normed = false;
             if (rnd && !prefill_codes(c, W.qkv)) HIPCHK(c, round_rows(L.Hf, m, cf.dim, W.qkv, L.Hh, L.Hl));
+            // (with head_dim 64 and every pair rotated, the product applies RoPE
+            // and writes q and the cache rows itself where it can)
+            const RopeArgs ro{L.rope, L.Q, kc, vc, p0, cf.n_heads, cf.n_kv_heads, cf.n_ctx, cf.rope_neox};
+            int ro_done = 0;
             HIPCHK(c, launch_gemm(EPI_STORE, W.qkv, ga(W.qkv, L.Hf, L.Hh, L.Hl), m, L.QKV, qkvd, W.bqkv, nullptr,
-                                  nullptr, L.ws, L.ws_floats, s));
-            HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
-                                          cf.rope_neox, cf.n_ctx, L.rope, L.Q, kc, vc, s));
+                                  nullptr, L.ws, L.ws_floats, s, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                  cf.head_dim == 64 && cf.rope_dims == 64 ? &ro : nullptr, &ro_done));
+            if (!ro_done)
+                HIPCHK(c, launch_rope_kv_rows(L.QKV, m, p0, cf.n_heads, cf.n_kv_heads, cf.head_dim, cf.rope_dims,
+                                              cf.rope_neox, cf.n_ctx, L.rope, L.Q, kc, vc, s));
             AttnArgs t;
             memset(&t, 0, sizeof t);
             t.q = L.Q;
