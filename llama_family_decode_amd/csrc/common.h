@@ -336,8 +336,9 @@ struct GemmA {
 // and then sets *yc_done to 1 (else 0, and Y holds the rows).
 // A q|k|v product given ro (head_dim 64, every pair rotated) may instead apply
 // RoPE to its rows and write q to ro.Q and k, v to this layer's F16 cache, as
-// launch_rope_kv_rows does from Y: it does so over one K split on the tiled
-// and integer paths, and then sets *ro_done to 1 (else 0, and Y holds the rows).
+// launch_rope_kv_rows does from Y: it does so in its epilogue over one K split
+// on the tiled and integer paths, and in the reduction of split-K partials,
+// and then sets *ro_done to 1 (else 0, and Y holds the rows).
 struct RopeArgs {
     const float2* rope;  // [pos][32] (cos, sin)
     float* Q;            // [n][n_heads * 64]

@@ -671,6 +671,47 @@ __global__ void k_splitk_reduce(const float* P, int S, int M, int N, float* Y, i
     }
 }
 
+// The q|k|v rows of the S split-K partials with RoPE and the K/V rows: one
+// thread per rotation pair, each value the sum of its partials in z order plus
+// the bias (as k_splitk_reduce forms it), then rotated and stored as
+// k_rope_kv_rows does (head_dim 64, every pair rotated).
+__global__ void k_splitk_rope(const float* P, int S, int n, const float* bias, RopeArgs ro) {
+    constexpr int hd = 64, half = 32;
+    const int qd = ro.n_heads * hd, kvd = ro.n_kv_heads * hd, W = qd + 2 * kvd;
+    const int pairs = W / 2;
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n * pairs) return;
+    const int row = idx / pairs, pi = idx % pairs;
+    const int head = pi / half, j = pi % half;
+    const int ra = head * hd + (ro.neox ? j : 2 * j), rb = ro.neox ? ra + half : ra + 1;
+    const size_t MN = (size_t)n * W, o = (size_t)row * W;
+    float va = 0.f, vb = 0.f;
+    for (int z = 0; z < S; z++) {
+        va += P[z * MN + o + ra];
+        vb += P[z * MN + o + rb];
+    }
+    if (bias) {
+        va = va + bias[ra];
+        vb = vb + bias[rb];
+    }
+    const int pos = ro.p0 + row;
+    if (head < ro.n_heads + ro.n_kv_heads) {
+        const float2 rv = pf_rope_rotate(va, vb, ro.rope[(size_t)pos * half + j]);
+        va = rv.x;
+        vb = rv.y;
+    }
+    if (ra < qd) {
+        ro.Q[(size_t)row * qd + ra] = va;
+        ro.Q[(size_t)row * qd + rb] = vb;
+    } else {
+        const bool k = ra < qd + kvd;
+        const int c0 = ra - qd - (k ? 0 : kvd);
+        __half* r = (k ? ro.kc : ro.vc) + ((size_t)(c0 / hd) * ro.n_ctx + pos) * hd;
+        r[c0 % hd] = __float2half_rn(va);
+        r[(rb - qd - (k ? 0 : kvd)) % hd] = __float2half_rn(vb);
+    }
+}
+
 // ------------------------------------------------------------ MFMA GEMM, F16 weights
 // The same product with the activations' hi/lo planes read from memory (made
 // once by the kernel that produces the activations) and every operand tile
@@ -1355,6 +1396,15 @@ static hipError_t gemm_epi(const Mat& W, const GemmA& A, int n, float* Y, int ld
     if (defer) {  // the caller reduces the S partials in ws itself
         *defer = S;
         return hipSuccess;
+    }
+    if constexpr (EPI == EPI_STORE) {
+        if (ro && !ymap) {  // the q|k|v partials go straight to RoPE and the K/V rows
+            const int pairs = n * (N / 2);
+            hipLaunchKernelGGL(k_splitk_rope, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, ws, S, n, bias,
+                               *ro);
+            if (ro_done) *ro_done = 1;
+            return hipGetLastError();
+        }
     }
     const size_t items = EPI == EPI_SWIGLU ? (size_t)n * N / 2 : (size_t)n * N;
     hipLaunchKernelGGL((k_splitk_reduce<EPI>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, ws, S, n, N, Y,
